@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark of the Simple GLA hot path on one MI355X.
+
+One step = one chunked prefill of a lightning layer (B=1, H=32, T=8192,
+Dk=Dv=128, bf16 in, fp32 state out) through ``sgla_chunk_fwd``. K timed steps
+run back to back after W warm-up steps, bracketed by device synchronisation;
+``value`` is prefill tokens/s. Each call is also bracketed by HIP events on the
+stream it runs on, which gives the per-call duration used for the roofline.
+
+The fused decode step (256 sequences x 32 heads, Dk=Dv=128, fp32 state in HBM,
+64 successive steps) is timed the same way and reported in ``decode``.
+
+``cpu_baseline`` times the oracle (plain C, fp64, OpenMP over (sequence, head)
+units) on the same prefill workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Simple GLA prefill tokens/s @H=32,D=128 bf16 (MFMA %) + decode HBM GB/s"
+PREFILL = "prefill_bf16_h32_t8192_d128"
+DECODE = "decode_bf16_n256_h32_d128_x64"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+
+
+def prefill_bytes(B, T, H, Dk, Dv, elem=2, with_s0=False):
+    """Algorithmic HBM bytes of one chunked-forward call: q, k, v read, o
+    written, g read (1,028 B per token and head at D=128 bf16), the final
+    state written and the initial state read when present."""
+    tok = B * T * H * (2 * Dk * elem + Dv * elem + Dv * elem + 4)
+    st = B * H * Dk * Dv * 4 * (2 if with_s0 else 1)
+    return tok + st
+
+
+def prefill_flops(B, T, H, Dk, Dv, C=64):
+    """Dense-tile flops: QK^T and A.V on 64x64 tiles, Q.S and K^T.V."""
+    per_tok = 2 * C * Dk + 2 * C * Dv + 2 * Dk * Dv + 2 * Dk * Dv
+    return B * T * H * per_tok
+
+
+def decode_bytes(N, H, Dk, Dv, elem=2):
+    """One decode step: the fp32 state read and written, q, k, v read, g read,
+    o written."""
+    return N * H * (2 * Dk * Dv * 4 + (2 * Dk + Dv) * elem + 4 + Dv * elem)
+
+
+def time_calls(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    region = starts[0].elapsed_time(ends[-1])
+    return wall, region, per
+
+
+def cpu_baseline(inp, W):
+    import numpy as np
+    import oracle
+    q, k, v, g = (W.to_numpy_f32(inp[x]) for x in ("q", "k", "v", "g"))
+    threads = oracle.default_threads()
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, g, inp["scale"], nthreads=threads)
+    dt = time.perf_counter() - t0
+    B, T, H, _ = q.shape
+    try:
+        model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
+                     if l.startswith("model name"))
+    except Exception:  # pragma: no cover
+        model = "unknown"
+    return {"value": B * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole prefill workload (B=1, T=8192, all 32 heads, 262,144 "
+                      "head-tokens), fp64 C oracle, OpenMP over (sequence, head) units; %.2f s; "
+                      "host CPU %s" % (dt, model)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--decode-passes", type=int, default=3,
+                    help="timed passes of 64 decode steps")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--seed", type=int, default=2)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d (WORLD_SIZE %d) is not "
+              "supported. A sequence shards by (sequence, head) units, with a carried-state "
+              "exchange for context parallelism; neither is built here." % (args.gpus, world),
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import linear_attention_hybrid_amd as sgla
+    import sgla_inputs as W
+
+    sgla.library()  # fail loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+              "data": "synthetic (seeded; q,k unit-RMS + RoPE, v ~ N(0,1), g = log sigmoid(N(4,1)))"}
+
+    if args.only in ("all", "prefill"):
+        inp = W.make_workload(PREFILL, seed=args.seed, device=dev)
+        B, T, H, Dk = inp["q"].shape
+        Dv = inp["v"].shape[-1]
+        out = torch.empty_like(inp["v"])
+        fs = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+
+        def step():
+            sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], None, None, inp["scale"],
+                           out=out, final_state=fs)
+
+        wall, region, per = time_calls(step, args.steps, args.warmup, torch)
+        ms_step = region / args.steps
+        per_avg = sum(per) / len(per)
+        nbytes = prefill_bytes(B, T, H, Dk, Dv)
+        flops = prefill_flops(B, T, H, Dk, Dv)
+        achieved = nbytes / (per_avg * 1e-3) / 1e9
+        result.update({
+            "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step,
+            "config": {"workload": PREFILL, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv,
+                       "chunk": 64, "scale": inp["scale"], "initial_state": "zero",
+                       "final_state": "fp32", "gpu": props.name},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "sgla_chunk_fwd (whole call: plan, segment-state, scan and "
+                                   "output kernels)",
+                         "algorithmic_bytes_per_launch": nbytes,
+                         "avg_launch_ms": per_avg},
+            "mfma": {"useful_tflops": flops / (per_avg * 1e-3) / 1e12,
+                     "useful_frac_of_bf16_peak": flops / (per_avg * 1e-3) / 1e12 /
+                     BF16_DENSE_PEAK_TFLOPS,
+                     "dense_tile_flops_per_launch": flops},
+            "wall_s_timed": wall,
+        })
+        if not args.no_cpu:
+            result["cpu_baseline"] = cpu_baseline(inp, W)
+        del inp, out, fs
+        torch.cuda.empty_cache()
+
+    if args.only in ("all", "decode"):
+        d = W.make_workload(DECODE, seed=4, device=dev)
+        steps, N, H, Dk = d["q"].shape
+        Dv = d["v"].shape[-1]
+        state = d["state"]
+        out = torch.empty((N, H, Dv), dtype=d["v"].dtype, device=dev)
+        counter = [0]
+
+        def dstep():
+            i = counter[0] % steps
+            counter[0] += 1
+            sgla.recurrent_step(d["q"][i], d["k"][i], d["v"][i], d["g"][i], state,
+                                scale=d["scale"], out=out)
+
+        n_timed = steps * args.decode_passes
+        wall, region, per = time_calls(dstep, n_timed, steps, torch)
+        per_avg = sum(per) / len(per)
+        nb = decode_bytes(N, H, Dk, Dv)
+        gbs = nb / (per_avg * 1e-3) / 1e9
+        dec = {"workload": DECODE, "steps_timed": n_timed, "ms_per_step": region / n_timed,
+               "tokens_per_s": N / (region / n_timed * 1e-3),
+               "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                            "kernel": "sgla_recurrent_step",
+                            "algorithmic_bytes_per_launch": nb, "avg_launch_ms": per_avg}}
+        result["decode"] = dec
+        if args.only == "decode":
+            result.update({"value": dec["tokens_per_s"], "unit": "tokens/s",
+                           "ms_per_step": dec["ms_per_step"],
+                           "config": {"workload": DECODE}, "roofline": dec["roofline"]})
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,152 @@
+/*
+ * sgla.h — C ABI of libsgla: Simple Gated Linear Attention on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (page "MiniCPM-SALA — Complete Blueprint", section
+ * "B2 lightning-attn (Simple GLA)"): every head of every sequence keeps a
+ * Dk x Dv state S. For each token t, in order,
+ *
+ *     S   <- exp(g_t) * S              (decay by a scalar log-decay g_t < 0)
+ *     S   <- S + k_t^T v_t             (rank-1 update, S[i][j] += k_t[i] v_t[j])
+ *     o_t  = scale * q_t S             (query after the update, sees token t)
+ *
+ * The chunked prefill computes the same thing 64 tokens at a time (page
+ * "Formulas and code for adapting inference to GDN/KDA linear modules",
+ * section 1.2 "Chunkwise Formulas": cumulative gate sums inside a chunk, a
+ * decay-masked intra-chunk score matrix, an inter-chunk term through the
+ * carried state and a state refresh, without the delta-rule terms). The decode
+ * step is one token of the recurrence applied in place to a stored state (same
+ * blueprint page: the state is loaded from the request's pool slot, updated,
+ * and saved back).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor arguments are DEVICE pointers to row-major, contiguous memory
+ *     owned by the caller. The library keeps no pointer after the call.
+ *   - dtype selects the element type of q, k, v and out (fp32 or bf16). g and
+ *     every state are always fp32.
+ *   - Supported head sizes: Dk, Dv in {64, 128}. Others give
+ *     SGLA_ERR_UNSUPPORTED.
+ *   - Base pointers of q, k, v, out and of every state must be 16-byte
+ *     aligned; g needs 4 bytes, cu_seqlens 8, state_indices 4
+ *     (SGLA_ERR_INVALID_ARG otherwise).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL means the default
+ *     stream) and the call returns without synchronising. Argument errors are
+ *     reported synchronously, before anything is enqueued. Launch failures map
+ *     to SGLA_ERR_HIP. Faults inside kernels surface at the caller's next
+ *     synchronisation, as usual in HIP.
+ *   - The library is re-entrant: it keeps no global mutable state.
+ */
+#ifndef SGLA_H_
+#define SGLA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SGLA_OK = 0,
+    SGLA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad enum      */
+    SGLA_ERR_UNSUPPORTED = 2, /* a size or combination this build does not handle */
+    SGLA_ERR_HIP = 3          /* a HIP runtime call or a launch failed              */
+} sgla_status;
+
+typedef enum {
+    SGLA_F32 = 0, /* q, k, v, out are float32                 */
+    SGLA_BF16 = 1 /* q, k, v, out are bfloat16 (fp32 compute) */
+} sgla_dtype;
+
+/*
+ * sgla_chunk_fwd — chunked prefill over whole sequences.
+ *
+ * Defined by the recurrence above (blueprint page, section "B2 lightning-attn
+ * (Simple GLA)"), evaluated chunk by chunk (GDN/KDA page, section 1.2). The
+ * interface follows the chunked call described on the GDN/KDA page, section
+ * 2.1 "Operator Implementation": an initial state gathered per sequence, an
+ * optional final state, and packed variable-length sequences given by
+ * cumulative start offsets.
+ *
+ * Arguments:
+ *   q, k          [B, T, H, Dk] dtype. With cu_seqlens: packed [T, H, Dk].
+ *   v             [B, T, H, Dv] dtype. With cu_seqlens: packed [T, H, Dv].
+ *   g             [B, T, H] fp32 log-decay per token and head (any real
+ *                 value; the decay factor is exp(g)).
+ *   initial_state [N, H, Dk, Dv] fp32, or NULL for zeros. N = B.
+ *   out           [B, T, H, Dv] dtype, written for every token.
+ *   final_state   [N, H, Dk, Dv] fp32, or NULL to skip. It may equal
+ *                 initial_state (in-place update); it must not overlap any
+ *                 other argument.
+ *   cu_seqlens    NULL: B sequences of T tokens each.
+ *                 Otherwise a device array of B + 1 int64 offsets with
+ *                 cu[0] = 0, cu[i] <= cu[i+1], cu[B] = T: sequence i is the
+ *                 packed tokens [cu[i], cu[i+1]). Chunks restart at every
+ *                 sequence start and tokens never mix across sequences. A
+ *                 zero-length sequence writes no output and its final state
+ *                 equals its initial state. The offsets are read on the
+ *                 device only; offsets that break the rule above are the
+ *                 caller's error (results are then undefined, but every
+ *                 access stays inside the buffers sized from B, T, H, Dk, Dv).
+ *   B             number of sequences (>= 0; 0 is a no-op).
+ *   T             tokens per sequence, or the packed total (>= 0).
+ *   H             heads (>= 1).
+ *   Dk, Dv        head sizes of q/k and v.
+ *   scale         output scale (normally 1/sqrt(Dk)).
+ *   dtype         element type of q, k, v, out.
+ *   stream        hipStream_t, or NULL.
+ *
+ * Memory: the call takes a temporary device workspace from HIP's
+ * stream-ordered allocator (hipMallocAsync/hipFreeAsync on `stream`) when a
+ * sequence is long enough to be split across workgroups; its size is at most
+ * (T / 256 + B + 1) * H * Dk * Dv * 4 bytes plus a small table.
+ * out must not alias q, k, v or g.
+ *
+ * Returns SGLA_OK, or SGLA_ERR_INVALID_ARG (null required pointer, negative
+ * size, misaligned pointer, B*T*H*max(Dk,Dv) beyond 2^62, bad dtype),
+ * SGLA_ERR_UNSUPPORTED (Dk or Dv not in {64, 128}), SGLA_ERR_HIP.
+ */
+sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                           const float *initial_state, void *out, float *final_state,
+                           const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv,
+                           float scale, sgla_dtype dtype, void *stream);
+
+/*
+ * sgla_recurrent_step — one decode token per row, state updated in place.
+ *
+ * Defined by one iteration of the recurrence above (blueprint page, section
+ * "B2 lightning-attn (Simple GLA)": decay, outer-product update, query), with
+ * the state read from and written back to the row's pool slot (same page,
+ * section "Memory Architecture": the request-to-state-slot mapping of the
+ * state pool).
+ *
+ * Arguments:
+ *   q, k          [N, H, Dk] dtype.
+ *   v             [N, H, Dv] dtype.
+ *   g             [N, H] fp32 log-decay.
+ *   state         [slots, H, Dk, Dv] fp32 pool, read and written in place.
+ *   state_indices [N] int32 row -> slot map, or NULL for slot = row. Slots
+ *                 must be distinct and inside [0, slots); the caller
+ *                 guarantees it (the library cannot see `slots`).
+ *   out           [N, H, Dv] dtype.
+ *   N, H, Dk, Dv  sizes (N >= 0; 0 is a no-op).
+ *   scale         output scale.
+ *   dtype, stream as above.
+ *
+ * Returns as sgla_chunk_fwd. Allocates nothing.
+ */
+sgla_status sgla_recurrent_step(const void *q, const void *k, const void *v, const float *g,
+                                float *state, const int32_t *state_indices, void *out, int N,
+                                int H, int Dk, int Dv, float scale, sgla_dtype dtype,
+                                void *stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *sgla_status_string(sgla_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int sgla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGLA_H_ */

@@ -1,0 +1,192 @@
+"""Simple Gated Linear Attention on AMD Instinct MI355X (gfx950).
+
+Python binding of ``libsgla.so`` (C ABI in ``include/sgla.h``). This module
+only checks and marshals arguments: every step of the computation runs in the
+library's HIP kernels. PyTorch is used for device memory and streams. If the
+library is not built, every call raises; there is no other code path.
+
+    o, S = chunk_fwd(q, k, v, g, initial_state=None, cu_seqlens=None)
+    o    = recurrent_step(q, k, v, g, state, state_indices=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import torch
+
+__all__ = ["chunk_fwd", "recurrent_step", "status_string", "library", "library_path",
+           "exported_symbols", "SglaError"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libsgla.so")
+header_path = os.path.join(os.path.dirname(_HERE), "include", "sgla.h")
+
+SGLA_OK, SGLA_ERR_INVALID_ARG, SGLA_ERR_UNSUPPORTED, SGLA_ERR_HIP = 0, 1, 2, 3
+SGLA_F32, SGLA_BF16 = 0, 1
+_DTYPE = {torch.float32: SGLA_F32, torch.bfloat16: SGLA_BF16}
+
+
+class SglaError(RuntimeError):
+    def __init__(self, func, status):
+        self.status = status
+        super().__init__("%s failed: %s" % (func, status_string(status)))
+
+
+_lib = None
+
+
+def library():
+    """Load libsgla.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(
+                "libsgla.so is not built (%s); run `python -m linear_attention_hybrid_amd.build`"
+                % library_path)
+        lib = ctypes.CDLL(library_path)
+        vp, ci, cf = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.sgla_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci,
+                                       vp]
+        lib.sgla_chunk_fwd.restype = ci
+        lib.sgla_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp]
+        lib.sgla_recurrent_step.restype = ci
+        lib.sgla_status_string.argtypes = [ci]
+        lib.sgla_status_string.restype = ctypes.c_char_p
+        lib.sgla_version.argtypes = []
+        lib.sgla_version.restype = ci
+        _lib = lib
+    return _lib
+
+
+def exported_symbols():
+    """Function names declared in include/sgla.h."""
+    with open(header_path) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(sgla_[a-z_]+)\s*\(", text,
+                                 re.M)))
+
+
+def status_string(status: int) -> str:
+    return library().sgla_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def chunk_fwd(q, k, v, g, initial_state=None, cu_seqlens=None, scale=None, out=None,
+              final_state=None, output_final_state=True):
+    """Chunked Simple GLA prefill.
+
+    q, k [B, T, H, Dk], v [B, T, H, Dv] (fp32 or bf16, same dtype, on one GPU),
+    g [B, T, H] fp32 log-decay. With ``cu_seqlens`` (int64 [N+1] on the same
+    device) B must be 1 and the N packed sequences are [cu[i], cu[i+1]).
+    initial_state [N, H, Dk, Dv] fp32 or None (zeros). scale defaults to
+    1/sqrt(Dk). Returns (o [B, T, H, Dv] in v's dtype, final_state [N, H, Dk,
+    Dv] fp32, or None when output_final_state is False and none was given).
+    ``final_state`` may be passed in (also the same tensor as initial_state).
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, T, H, Dk]")
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("chunk_fwd runs on a GPU; q is on %s" % device)
+    if q.dtype not in _DTYPE:
+        raise TypeError("q must be float32 or bfloat16")
+    _check(q, "q", q.dtype, (B, T, H, Dk), device)
+    _check(k, "k", q.dtype, (B, T, H, Dk), device)
+    _check(v, "v", q.dtype, (B, T, H, Dv), device)
+    _check(g, "g", torch.float32, (B, T, H), device)
+    N = B
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed sequences need B == 1")
+        if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+            raise ValueError("cu_seqlens must be 1-D with N+1 entries")
+        N = cu_seqlens.numel() - 1
+        _check(cu_seqlens, "cu_seqlens", torch.int64, (N + 1,), device)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", torch.float32, (N, H, Dk, Dv), device)
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=v.dtype, device=device)
+    else:
+        _check(out, "out", v.dtype, (B, T, H, Dv), device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=device)
+    elif final_state is not None:
+        _check(final_state, "final_state", torch.float32, (N, H, Dk, Dv), device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    # Packed input: the C ABI takes B = number of sequences and T = the total.
+    Barg = N if cu_seqlens is not None else B
+    with torch.cuda.device(device):
+        st = library().sgla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state),
+                                      _ptr(out), _ptr(final_state), _ptr(cu_seqlens), Barg, T,
+                                      H, Dk, Dv, float(scale), _DTYPE[q.dtype], _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_chunk_fwd", st)
+    return out, final_state
+
+
+def recurrent_step(q, k, v, g, state, state_indices=None, scale=None, out=None):
+    """One fused decode step, updating ``state`` in place.
+
+    q, k [N, H, Dk], v [N, H, Dv] (fp32 or bf16), g [N, H] fp32,
+    state [slots, H, Dk, Dv] fp32, state_indices [N] int32 (distinct slots) or
+    None for slot = row. Returns o [N, H, Dv] in v's dtype.
+    """
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, Dk]")
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    device = q.device
+    if device.type != "cuda":
+        raise ValueError("recurrent_step runs on a GPU; q is on %s" % device)
+    if q.dtype not in _DTYPE:
+        raise TypeError("q must be float32 or bfloat16")
+    _check(q, "q", q.dtype, (N, H, Dk), device)
+    _check(k, "k", q.dtype, (N, H, Dk), device)
+    _check(v, "v", q.dtype, (N, H, Dv), device)
+    _check(g, "g", torch.float32, (N, H), device)
+    if state.dim() != 4:
+        raise ValueError("state must be [slots, H, Dk, Dv]")
+    _check(state, "state", torch.float32, (state.shape[0], H, Dk, Dv), device)
+    if state_indices is not None:
+        _check(state_indices, "state_indices", torch.int32, (N,), device)
+    elif state.shape[0] < N:
+        raise ValueError("state has fewer slots than rows")
+    if out is None:
+        out = torch.empty((N, H, Dv), dtype=v.dtype, device=device)
+    else:
+        _check(out, "out", v.dtype, (N, H, Dv), device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    with torch.cuda.device(device):
+        st = library().sgla_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state),
+                                           _ptr(state_indices), _ptr(out), N, H, Dk, Dv,
+                                           float(scale), _DTYPE[q.dtype], _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_recurrent_step", st)
+    return out

@@ -1,0 +1,149 @@
+// Segment planning and the carried-state scan of the chunked forward.
+//
+// A long sequence is cut into segments of whole chunks so that many
+// workgroups can work on it at once. Each segment's state contribution is
+// computed from a zero state (the chunk state refresh of page "Formulas and
+// code for adapting inference to GDN/KDA linear modules", section 1.2, applied
+// chunk after chunk), then a short sequential pass per (sequence, head)
+// combines them into the state each segment starts from:
+//
+//     S_in(0) = S0,    S_in(j+1) = exp(Gamma_j) * S_in(j) + dS_j
+//
+// where Gamma_j is the sum of g over segment j and dS_j its zero-start state.
+// This is the recurrence itself, regrouped: unrolling it over a segment gives
+// exactly exp(Gamma_j) * S_in(j) plus the segment's own decayed outer products
+// (blueprint page, section "Why Linear Attention Loses Information": the state
+// is the decayed initial state plus the decayed sum of outer products).
+#include "sgla_internal.h"
+
+namespace sgla {
+
+__global__ __launch_bounds__(256) void plan_kernel(const int64_t *__restrict__ cu, int B, int T,
+                                                   int seg_len, int nseg_max,
+                                                   SegEntry *__restrict__ segs,
+                                                   SeqEntry *__restrict__ seqs) {
+    __shared__ int32_t sbuf[256];
+    __shared__ int32_t carry;
+    const int tid = threadIdx.x;
+    const int64_t ttot = cu ? (int64_t)T : (int64_t)B * T;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    // Pass 1: segments per sequence and the exclusive prefix sum of them.
+    for (int base = 0; base < B; base += 256) {
+        const int n = base + tid;
+        int32_t ns = 0;
+        if (n < B) {
+            int64_t len = cu ? cu[n + 1] - cu[n] : (int64_t)T;
+            if (len < 0) len = 0;
+            ns = len == 0 ? 1 : (int32_t)((len + seg_len - 1) / seg_len);
+        }
+        sbuf[tid] = ns;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int32_t add = tid >= off ? sbuf[tid - off] : 0;
+            __syncthreads();
+            sbuf[tid] += add;
+            __syncthreads();
+        }
+        const int32_t first = carry + sbuf[tid] - ns;
+        if (n < B) {
+            // Offsets that break the documented rule could ask for more rows
+            // than the table has; clamp so every later access stays inside.
+            int32_t room = nseg_max - first;
+            if (room < 0) room = 0;
+            seqs[n].first = first < nseg_max ? first : nseg_max;
+            seqs[n].nseg = ns < room ? ns : room;
+        }
+        __syncthreads();
+        if (tid == 255) carry += sbuf[255];
+        __syncthreads();
+    }
+    const int32_t total = carry;
+    // Pass 2: one table row per segment.
+    for (int s = tid; s < nseg_max; s += 256) {
+        SegEntry e;
+        e.pad0 = 0;
+        e.pad1 = 0;
+        if (s >= total || B == 0) {
+            e.tok0 = 0;
+            e.len = -1;
+            e.seq = 0;
+            e.p = 0;
+            e.nseg = 0;
+            segs[s] = e;
+            continue;
+        }
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (seqs[mid].first <= s) lo = mid; else hi = mid - 1;
+        }
+        const int n = lo;
+        const int32_t p = s - seqs[n].first;
+        const int64_t start = cu ? cu[n] : (int64_t)n * T;
+        const int64_t len = cu ? cu[n + 1] - cu[n] : (int64_t)T;
+        int64_t tok0 = start + (int64_t)p * seg_len;
+        int64_t l = len - (int64_t)p * seg_len;
+        if (l > seg_len) l = seg_len;
+        if (l < 0) l = 0;
+        if (tok0 < 0) { tok0 = 0; l = 0; }
+        if (tok0 > ttot) { tok0 = ttot; l = 0; }
+        if (tok0 + l > ttot) l = ttot - tok0;
+        e.tok0 = tok0;
+        e.len = (int32_t)l;
+        e.seq = n;
+        e.p = p;
+        e.nseg = seqs[n].nseg;
+        if (p >= e.nseg) e.len = -1;
+        segs[s] = e;
+    }
+}
+
+// One thread owns four consecutive state elements of one (sequence, head) and
+// walks the sequence's segments in order. In place: the slot of segment j
+// holds dS_j on entry and S_in(j) on exit.
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void scan_kernel(ChunkParams p) {
+    const int nh = blockIdx.x;
+    const int n = nh / p.H;
+    const int h = nh - n * p.H;
+    const SeqEntry se = p.seqs[n];
+    if (se.nseg <= 1) return;
+    const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
+    float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (p.s0) S = *reinterpret_cast<const float4 *>(p.s0 + ((int64_t)n * p.H + h) * DK * DV + e);
+    for (int j = 0; j < se.nseg; ++j) {
+        const int s = se.first + j;
+        float4 *slot = reinterpret_cast<float4 *>(p.buf + ((int64_t)s * p.H + h) * DK * DV + e);
+        float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
+        const bool more = j + 1 < se.nseg;
+        if (more) d = *slot;
+        *slot = S;
+        if (more) {
+            const float a = __expf(p.gam[(int64_t)s * p.H + h]);
+            S.x = fmaf(a, S.x, d.x);
+            S.y = fmaf(a, S.y, d.y);
+            S.z = fmaf(a, S.z, d.z);
+            S.w = fmaf(a, S.w, d.w);
+        }
+    }
+}
+
+hipError_t launch_plan(const int64_t *cu, int B, int T, int seg_len, int nseg_max,
+                       SegEntry *segs, SeqEntry *seqs, hipStream_t st) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, cu, B, T, seg_len, nseg_max, segs,
+                       seqs);
+    return hipGetLastError();
+}
+
+hipError_t launch_scan(const ChunkParams &p, int Dk, int Dv, hipStream_t st) {
+    if (p.N == 0) return hipSuccess;
+    const dim3 grid(p.N * p.H, (Dk * Dv) / 1024);
+    if (Dk == 128 && Dv == 128) hipLaunchKernelGGL((scan_kernel<128, 128>), grid, dim3(256), 0, st, p);
+    else if (Dk == 128 && Dv == 64) hipLaunchKernelGGL((scan_kernel<128, 64>), grid, dim3(256), 0, st, p);
+    else if (Dk == 64 && Dv == 128) hipLaunchKernelGGL((scan_kernel<64, 128>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((scan_kernel<64, 64>), grid, dim3(256), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace sgla

@@ -1,0 +1,135 @@
+// Host side of the libsgla C ABI: argument checks, planning, launches.
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/sgla.h"
+#include "sgla_internal.h"
+
+using namespace sgla;
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool misaligned(const void *p, uintptr_t a = 16) {
+    return p && (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
+}
+bool head_size_ok(int d) { return d == 64 || d == 128; }
+
+// Tokens per segment for the chunked forward: long enough that per-segment
+// state traffic (one Dk x Dv fp32 state written, scanned and re-read per
+// segment) stays small next to the token traffic, short enough that the number
+// of (segment, head) units keeps every compute unit busy.
+int choose_seg_len(int64_t ttot, int B, int H) {
+    const char *env = getenv("SGLA_SEG_LEN");
+    if (env) {
+        long v = strtol(env, nullptr, 10);
+        if (v >= kChunk && v % kChunk == 0 && v <= (1 << 24)) return (int)v;
+    }
+    const int64_t target_units = 2048;  // about 8 per compute unit
+    int64_t len = (ttot * H + target_units - 1) / target_units;
+    if (len < 512) len = 512;
+    if (len > 8192) len = 8192;
+    len = (len + kChunk - 1) / kChunk * kChunk;
+    (void)B;
+    return (int)len;
+}
+
+sgla_status hip_status(hipError_t e) { return e == hipSuccess ? SGLA_OK : SGLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *sgla_status_string(sgla_status s) {
+    switch (s) {
+        case SGLA_OK: return "SGLA_OK";
+        case SGLA_ERR_INVALID_ARG: return "SGLA_ERR_INVALID_ARG";
+        case SGLA_ERR_UNSUPPORTED: return "SGLA_ERR_UNSUPPORTED";
+        case SGLA_ERR_HIP: return "SGLA_ERR_HIP";
+    }
+    return "SGLA_ERR_UNKNOWN";
+}
+
+int sgla_version(void) { return kVersion; }
+
+sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                           const float *initial_state, void *out, float *final_state,
+                           const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv,
+                           float scale, sgla_dtype dtype, void *stream) {
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
+    if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
+    const int64_t ttot = cu_seqlens ? (int64_t)T : (int64_t)B * T;
+    if (ttot > ((int64_t)1 << 62) / ((int64_t)H * 128)) return SGLA_ERR_INVALID_ARG;
+    if ((int64_t)B * H > (int64_t)1 << 30) return SGLA_ERR_INVALID_ARG;
+    if (ttot > 0 && (!q || !k || !v || !g || !out)) return SGLA_ERR_INVALID_ARG;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) || misaligned(out) ||
+        misaligned(initial_state) || misaligned(final_state) || misaligned(cu_seqlens, 8))
+        return SGLA_ERR_INVALID_ARG;
+    if (B == 0) return SGLA_OK;
+    if (ttot == 0 && !final_state) return SGLA_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    const int seg_len = choose_seg_len(ttot, B, H);
+    const int64_t nseg_max64 = ttot / seg_len + B + 1;
+    if (nseg_max64 * H > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+    const int nseg_max = (int)nseg_max64;
+
+    // Workspace: segment table, sequence table, per-segment log-decays, states.
+    const size_t segs_b = (size_t)nseg_max * sizeof(SegEntry);
+    const size_t seqs_b = ((size_t)B * sizeof(SeqEntry) + 255) / 256 * 256;
+    const size_t gam_b = ((size_t)nseg_max * H * sizeof(float) + 255) / 256 * 256;
+    const size_t buf_b = (size_t)nseg_max * H * Dk * Dv * sizeof(float);
+    const size_t ws_b = segs_b + seqs_b + gam_b + buf_b;
+    char *ws = nullptr;
+    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&ws), ws_b, st);
+    if (e != hipSuccess) return SGLA_ERR_HIP;
+
+    ChunkParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.s0 = initial_state;
+    p.out = out;
+    p.sfin = final_state;
+    p.segs = reinterpret_cast<SegEntry *>(ws);
+    p.seqs = reinterpret_cast<SeqEntry *>(ws + segs_b);
+    p.gam = reinterpret_cast<float *>(ws + segs_b + seqs_b);
+    p.buf = reinterpret_cast<float *>(ws + segs_b + seqs_b + gam_b);
+    p.H = H;
+    p.nseg_max = nseg_max;
+    p.N = B;
+    p.scale = scale;
+    const bool bf16 = dtype == SGLA_BF16;
+
+    e = launch_plan(cu_seqlens, B, T, seg_len, nseg_max, const_cast<SegEntry *>(p.segs),
+                    const_cast<SeqEntry *>(p.seqs), st);
+    if (e == hipSuccess) e = launch_chunk_valu(p, bf16, Dk, Dv, /*phase_state=*/true, st);
+    if (e == hipSuccess) e = launch_scan(p, Dk, Dv, st);
+    if (e == hipSuccess) e = launch_chunk_valu(p, bf16, Dk, Dv, /*phase_state=*/false, st);
+    const hipError_t ef = hipFreeAsync(ws, st);
+    if (e == hipSuccess) e = ef;
+    return hip_status(e);
+}
+
+sgla_status sgla_recurrent_step(const void *q, const void *k, const void *v, const float *g,
+                                float *state, const int32_t *state_indices, void *out, int N,
+                                int H, int Dk, int Dv, float scale, sgla_dtype dtype,
+                                void *stream) {
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (N < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
+    if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > ((int64_t)1 << 31) - 1) return SGLA_ERR_INVALID_ARG;
+    if (N == 0) return SGLA_OK;
+    if (!q || !k || !v || !g || !state || !out) return SGLA_ERR_INVALID_ARG;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) ||
+        misaligned(state) || misaligned(out) || misaligned(state_indices, 4))
+        return SGLA_ERR_INVALID_ARG;
+    return hip_status(launch_recurrent_step(q, k, v, g, state, state_indices, out, N, H, Dk, Dv,
+                                            scale, dtype == SGLA_BF16,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

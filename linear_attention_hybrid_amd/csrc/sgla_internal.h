@@ -1,0 +1,96 @@
+// Internal declarations shared by the libsgla HIP sources. Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgla {
+
+constexpr int kChunk = 64;  // tokens per chunk (the chunk size the pages use)
+
+// One segment of one sequence: a run of whole chunks handled by one
+// workgroup column. Built on the device from cu_seqlens (or from B x T).
+struct SegEntry {
+    int64_t tok0;  // packed index of the segment's first token
+    int32_t len;   // tokens in the segment; -1 marks an unused table row
+    int32_t seq;   // sequence index
+    int32_t p;     // segment index inside its sequence
+    int32_t nseg;  // number of segments of that sequence
+    int32_t pad0;
+    int32_t pad1;
+};
+static_assert(sizeof(SegEntry) == 32, "SegEntry layout");
+
+struct SeqEntry {
+    int32_t first;  // table row of the sequence's first segment
+    int32_t nseg;   // number of segments (>= 1, also for empty sequences)
+};
+
+// Arguments of the chunked-forward kernels.
+struct ChunkParams {
+    const void *q;
+    const void *k;
+    const void *v;
+    const float *g;
+    const float *s0;      // [N,H,Dk,Dv] or nullptr
+    void *out;
+    float *sfin;          // [N,H,Dk,Dv] or nullptr
+    float *buf;           // [nseg_max,H,Dk,Dv]: segment states, then carried-in states
+    float *gam;           // [nseg_max,H]: total log-decay of each segment
+    const SegEntry *segs;  // [nseg_max]
+    const SeqEntry *seqs;  // [N]
+    int H;
+    int nseg_max;
+    int N;
+    float scale;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_plan(const int64_t *cu, int B, int T, int seg_len, int nseg_max,
+                       SegEntry *segs, SeqEntry *seqs, hipStream_t st);
+hipError_t launch_scan(const ChunkParams &p, int Dk, int Dv, hipStream_t st);
+hipError_t launch_chunk_valu(const ChunkParams &p, bool bf16, int Dk, int Dv, bool phase_state,
+                             hipStream_t st);
+hipError_t launch_recurrent_step(const void *q, const void *k, const void *v, const float *g,
+                                 float *state, const int32_t *idx, void *out, int N, int H,
+                                 int Dk, int Dv, float scale, bool bf16, hipStream_t st);
+
+// Map a linear workgroup id onto (unit, sub) so that the `nsub` workgroups of
+// one unit land on the same XCD (ids are dealt to the 8 XCDs round-robin) and
+// are dispatched close together, so they share that XCD's L2.
+__device__ __forceinline__ void xcd_unit_map(int id, int nsub, int &unit, int &sub) {
+    const int xcd = id & 7;
+    const int j = id >> 3;
+    unit = (j / nsub) * 8 + xcd;
+    sub = j % nsub;
+}
+
+// bf16 <-> fp32 (round to nearest even on the way down; NaN kept quiet).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const T *p, int64_t i);
+template <>
+__device__ __forceinline__ float load_elem<float>(const float *p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_elem<uint16_t>(const uint16_t *p, int64_t i) {
+    return bf16_to_f32(p[i]);
+}
+template <typename T>
+__device__ __forceinline__ void store_elem(T *p, int64_t i, float x);
+template <>
+__device__ __forceinline__ void store_elem<float>(float *p, int64_t i, float x) { p[i] = x; }
+template <>
+__device__ __forceinline__ void store_elem<uint16_t>(uint16_t *p, int64_t i, float x) {
+    p[i] = f32_to_bf16(x);
+}
+
+}  // namespace sgla

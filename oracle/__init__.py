@@ -26,10 +26,10 @@ LIBRARY = os.path.join(_HERE, "libsgla_oracle.so")
 
 
 def compile_source(src: str, out: str) -> str:
-    """gcc -O2 a C oracle source into a shared library (atomic replace)."""
+    """gcc -O3 a C oracle source into a shared library (atomic replace)."""
     tmp = out + ".tmp%d" % os.getpid()
     subprocess.check_call(
-        ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", src, "-o", tmp, "-lm"]
+        ["gcc", "-O3", "-std=c11", "-fPIC", "-shared", "-fopenmp", src, "-o", tmp, "-lm"]
     )
     os.replace(tmp, out)
     return out

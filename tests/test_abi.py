@@ -1,0 +1,117 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments synchronously, before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import linear_attention_hybrid_amd as sgla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sgla.library_path):
+        from linear_attention_hybrid_amd import build
+        build.build()
+    return sgla.library()
+
+
+def _no_gpu():
+    import torch
+    return not torch.cuda.is_available()
+
+
+def test_header_declares_the_entry_points():
+    names = sgla.exported_symbols()
+    for n in ("sgla_chunk_fwd", "sgla_recurrent_step", "sgla_status_string", "sgla_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", sgla.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in sgla.exported_symbols():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings_and_version(lib):
+    assert sgla.status_string(0) == "SGLA_OK"
+    assert sgla.status_string(1) == "SGLA_ERR_INVALID_ARG"
+    assert sgla.status_string(2) == "SGLA_ERR_UNSUPPORTED"
+    assert sgla.status_string(3) == "SGLA_ERR_HIP"
+    assert sgla.status_string(77) == "SGLA_ERR_UNKNOWN"
+    assert lib.sgla_version() >= 100
+
+
+A = 0x10000  # a 16-byte aligned address that is never dereferenced
+
+
+def chunk(lib, q=A, k=A, v=A, g=A, s0=None, out=A, sf=None, cu=None, B=0, T=0, H=1, Dk=64,
+          Dv=64, scale=1.0, dtype=0):
+    return lib.sgla_chunk_fwd(q, k, v, g, s0, out, sf, cu, B, T, H, Dk, Dv, scale, dtype, None)
+
+
+def step(lib, q=A, k=A, v=A, g=A, state=A, idx=None, out=A, N=0, H=1, Dk=64, Dv=64, dtype=0):
+    return lib.sgla_recurrent_step(q, k, v, g, state, idx, out, N, H, Dk, Dv, 1.0, dtype, None)
+
+
+def test_chunk_fwd_validation(lib):
+    # B = 0 would be a no-op, so every rejection below happens before any launch.
+    assert chunk(lib) == 0
+    assert chunk(lib, dtype=2) == 1
+    assert chunk(lib, dtype=-1) == 1
+    assert chunk(lib, B=-1) == 1
+    assert chunk(lib, T=-1) == 1
+    assert chunk(lib, H=0) == 1
+    assert chunk(lib, Dk=32) == 2
+    assert chunk(lib, Dv=96) == 2
+    assert chunk(lib, Dk=0) == 1
+    assert chunk(lib, q=A + 2) == 1
+    assert chunk(lib, v=A + 8) == 1
+    assert chunk(lib, out=A + 4) == 1
+    assert chunk(lib, g=A + 2) == 1
+    assert chunk(lib, g=A + 4) == 0          # g only needs fp32 alignment
+    assert chunk(lib, s0=A + 4) == 1
+    assert chunk(lib, sf=A + 8) == 1
+    assert chunk(lib, cu=A + 4) == 1
+    assert chunk(lib, B=1, T=2**31 - 1, H=2**30, Dk=128, Dv=128) == 1
+
+
+@pytest.mark.skipif("not _no_gpu()", reason="could reach a launch if validation were wrong")
+def test_chunk_fwd_null_pointers(lib):
+    assert chunk(lib, q=None, B=1, T=1) == 1
+    assert chunk(lib, g=None, B=1, T=1) == 1
+    assert chunk(lib, out=None, B=1, T=1) == 1
+    # No tokens and no final state: nothing to do, no pointer needed.
+    assert chunk(lib, q=None, k=None, v=None, g=None, out=None, B=3, T=0) == 0
+
+
+def test_recurrent_step_validation(lib):
+    assert step(lib) == 0
+    assert step(lib, dtype=5) == 1
+    assert step(lib, N=-1) == 1
+    assert step(lib, H=0) == 1
+    assert step(lib, Dk=256) == 2
+    assert step(lib, N=2**20, H=2**12) == 1
+
+
+@pytest.mark.skipif("not _no_gpu()", reason="could reach a launch if validation were wrong")
+def test_recurrent_step_pointer_checks(lib):
+    assert step(lib, N=1, state=None) == 1
+    assert step(lib, N=1, q=A + 2) == 1
+    assert step(lib, N=1, idx=A + 2) == 1
+    assert step(lib, N=1, state=A + 4) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 64)
+    with pytest.raises(ValueError):
+        sgla.chunk_fwd(x, x, x, torch.zeros(1, 4, 1))
+    with pytest.raises(ValueError):
+        sgla.recurrent_step(x[0], x[0], x[0], torch.zeros(4, 1), torch.zeros(4, 1, 64, 64))

@@ -1,0 +1,224 @@
+"""GPU parity of sgla_chunk_fwd against the oracle (through the C ABI).
+
+Small cases compare every output and final-state element; the named full-size
+workloads compare a seeded sample of heads (every token and state element of
+those heads) with the oracle, in the launch configuration the benchmark times.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_hybrid_amd as sgla
+import sgla_inputs as W
+from tests.parity import check, check_windows, host, nan_like, oracle_prefill, say
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(autouse=True)
+def _seg_len_env():
+    old = os.environ.pop("SGLA_SEG_LEN", None)
+    yield
+    os.environ.pop("SGLA_SEG_LEN", None)
+    if old is not None:
+        os.environ["SGLA_SEG_LEN"] = old
+
+
+def run_gpu(inp, poison=True, final=True):
+    B, T, H, Dk = inp["q"].shape
+    Dv = inp["v"].shape[-1]
+    N = B if inp["cu_seqlens"] is None else inp["cu_seqlens"].numel() - 1
+    out = nan_like((B, T, H, Dv), inp["v"].dtype) if poison else None
+    fs = nan_like((N, H, Dk, Dv), torch.float32) if (poison and final) else None
+    o, S = sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"],
+                          initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"],
+                          scale=inp["scale"], out=out, final_state=fs, output_final_state=final)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def compare(inp, o, S, dtype, what, heads=None, starts=None):
+    ro, rS = oracle_prefill(inp, heads)
+    go = host(o if heads is None else o[:, :, heads])
+    check(go, ro, dtype, what + " o")
+    if S is not None:
+        gS = host(S if heads is None else S[:, heads])
+        check(gS, rS, dtype, what + " final state", bf16_out=False)
+    if starts:
+        check_windows(go[0], ro[0], starts, dtype, what + " o")
+    return ro, rS
+
+
+def test_tiny_fp32_workload():
+    say("chunk_fwd tiny fp32 B=1 H=4 T=256 D=64 seed=1")
+    inp = W.make_workload("tiny_fp32_h4_t256_d64", seed=1, device="cuda")
+    o, S = run_gpu(inp)
+    compare(inp, o, S, "f32", "tiny fp32")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 129, 300])
+def test_edge_lengths(dtype, T):
+    say("chunk_fwd edge", dtype, "B=2 H=3 T=%d D=128/64 S0" % T)
+    inp = W.make_prefill(2, T, 3, 128, 64, dtype, "lightning", seed=T, device="cuda",
+                         init="normal")
+    o, S = run_gpu(inp)
+    compare(inp, o, S, dtype, "edge T=%d" % T)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_head_sizes(dk, dv, dtype):
+    say("chunk_fwd head sizes", dtype, dk, dv)
+    inp = W.make_prefill(1, 200, 2, dk, dv, dtype, "gaussian", seed=dk + dv, device="cuda",
+                         init="normal")
+    o, S = run_gpu(inp)
+    compare(inp, o, S, dtype, "Dk=%d Dv=%d" % (dk, dv))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("seg_len", [64, 128, 512])
+def test_multi_segment_state_passing(dtype, seg_len):
+    """Force short segments so sequences span several workgroups and the
+    carried state goes through the segment scan."""
+    say("chunk_fwd segments", dtype, "seg_len", seg_len)
+    os.environ["SGLA_SEG_LEN"] = str(seg_len)
+    T = 1000
+    inp = W.make_prefill(2, T, 3, 128, 128, dtype, "lightning", seed=seg_len, device="cuda",
+                         init="normal")
+    o, S = run_gpu(inp)
+    starts = [0] + list(range(seg_len, T, seg_len))
+    ro, rS = compare(inp, o, S, dtype, "segments %d" % seg_len, starts=starts)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_varlen_packed_matches_oracle_and_separate_runs(dtype):
+    lengths = [0, 1, 63, 64, 65, 200, 0, 700, 129]
+    cu = W.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    say("chunk_fwd varlen", dtype, lengths)
+    inp = W.make_prefill(1, T, 4, 128, 128, dtype, "lightning", seed=3, device="cuda",
+                         cu_seqlens=cu, init="normal")
+    os.environ["SGLA_SEG_LEN"] = "128"
+    o, S = run_gpu(inp)
+    compare(inp, o, S, dtype, "varlen", starts=[int(c) for c in cu[:-1]])
+    # Packed equals separate runs, bit for bit (same segment length).
+    for n, L in enumerate(lengths):
+        a, b = int(cu[n]), int(cu[n + 1])
+        one = dict(inp)
+        one["q"], one["k"], one["v"], one["g"] = (inp[x][:, a:b].contiguous()
+                                                  for x in ("q", "k", "v", "g"))
+        one["initial_state"] = inp["initial_state"][n:n + 1].contiguous()
+        one["cu_seqlens"] = None
+        on, Sn = run_gpu(one)
+        assert torch.equal(on, o[:, a:b]), n
+        assert torch.equal(Sn[0], S[n]), n
+        if L == 0:
+            assert torch.equal(S[n], inp["initial_state"][n]), n
+
+
+def test_no_final_state_and_in_place_state():
+    say("chunk_fwd final_state None / in place")
+    os.environ["SGLA_SEG_LEN"] = "128"
+    inp = W.make_prefill(2, 700, 2, 64, 64, "bf16", "lightning", seed=9, device="cuda",
+                         init="normal")
+    o1, S1 = run_gpu(inp)
+    o2, none = sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["initial_state"],
+                              output_final_state=False)
+    assert none is None
+    assert torch.equal(o1, o2)
+    st = inp["initial_state"].clone()
+    o3, S3 = sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], st, final_state=st)
+    torch.cuda.synchronize()
+    assert S3.data_ptr() == st.data_ptr()
+    assert torch.equal(o3, o1) and torch.equal(S3, S1)
+
+
+def test_zero_tokens_copies_state():
+    say("chunk_fwd T=0")
+    S0 = torch.randn(3, 2, 64, 128, device="cuda")
+    z = torch.empty(3, 0, 2, 64, device="cuda", dtype=torch.bfloat16)
+    zv = torch.empty(3, 0, 2, 128, device="cuda", dtype=torch.bfloat16)
+    g = torch.empty(3, 0, 2, device="cuda")
+    o, S = sgla.chunk_fwd(z, z, zv, g, initial_state=S0)
+    torch.cuda.synchronize()
+    assert o.shape == (3, 0, 2, 128)
+    assert torch.equal(S, S0)
+
+
+def test_split_and_chain():
+    say("chunk_fwd split/chain T=1500 at 640 and 1000")
+    inp = W.make_prefill(1, 1500, 2, 128, 128, "bf16", "lightning", seed=4, device="cuda",
+                         init="normal")
+    o, S = run_gpu(inp)
+    ro, rS = oracle_prefill(inp)
+    for t in (640, 1000):
+        a = dict(inp)
+        b = dict(inp)
+        for x in ("q", "k", "v", "g"):
+            a[x] = inp[x][:, :t].contiguous()
+            b[x] = inp[x][:, t:].contiguous()
+        oa, Sa = run_gpu(a)
+        b["initial_state"] = Sa
+        ob, Sb = run_gpu(b)
+        oc = torch.cat([oa, ob], dim=1)
+        check(host(oc), ro, "bf16", "split %d o" % t)
+        check(host(Sb), rS, "bf16", "split %d state" % t, bf16_out=False)
+        check_windows(host(oc)[0], ro[0], [t], "bf16", "split %d" % t)
+
+
+def test_deterministic():
+    say("chunk_fwd determinism")
+    inp = W.make_prefill(1, 2000, 4, 128, 128, "bf16", "lightning", seed=11, device="cuda",
+                         init="normal")
+    o1, S1 = run_gpu(inp)
+    o2, S2 = run_gpu(inp)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def _sample_heads(H, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted(rng.choice(H, size=n, replace=False).tolist())
+
+
+def test_workload_prefill_8k():
+    say("chunk_fwd workload prefill bf16 H=32 T=8192 D=128 seed=2 (4 sampled heads)")
+    inp = W.make_workload("prefill_bf16_h32_t8192_d128", seed=2, device="cuda")
+    o, S = run_gpu(inp)
+    heads = _sample_heads(32, 4, 2)
+    compare(inp, o, S, "bf16", "prefill 8k", heads=heads)
+
+
+def test_workload_prefill_64k_continuation_and_split():
+    say("chunk_fwd workload prefill bf16 H=32 T=65536 D=128 S0 seed=3 (3 sampled heads)")
+    inp = W.make_workload("prefill_bf16_h32_t65536_d128_cont", seed=3, device="cuda")
+    o, S = run_gpu(inp)
+    heads = _sample_heads(32, 3, 3)
+    ro, rS = compare(inp, o, S, "bf16", "prefill 64k", heads=heads, starts=[0])
+    t = 32768
+    a = dict(inp)
+    b = dict(inp)
+    for x in ("q", "k", "v", "g"):
+        a[x] = inp[x][:, :t].contiguous()
+        b[x] = inp[x][:, t:].contiguous()
+    oa, Sa = run_gpu(a)
+    b["initial_state"] = Sa
+    ob, Sb = run_gpu(b)
+    oc = host(torch.cat([oa, ob], dim=1)[:, :, heads])
+    check(oc, ro, "bf16", "64k split o")
+    check(host(Sb[:, heads]), rS, "bf16", "64k split state", bf16_out=False)
+    check_windows(oc[0], ro[0], [t], "bf16", "64k split")
+
+
+def test_workload_varlen_512k():
+    say("chunk_fwd workload varlen bf16 8 seqs 524288 tokens H=32 D=128 seed=5 (4 heads)")
+    inp = W.make_workload("varlen_bf16_h32_d128_8seq_512k", seed=5, device="cuda")
+    o, S = run_gpu(inp)
+    heads = _sample_heads(32, 4, 5)
+    cu = inp["cu_seqlens"].cpu().numpy()
+    compare(inp, o, S, "bf16", "varlen 512k", heads=heads,
+            starts=[int(c) for c in cu[:-1]])
