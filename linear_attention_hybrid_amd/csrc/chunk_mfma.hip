@@ -1,0 +1,342 @@
+// Chunked Simple GLA on the matrix cores: bf16 operands, fp32 accumulation,
+// Dk = Dv = 128, chunks of 64 tokens.
+//
+// Per chunk with inclusive cumulative gate sums G (page "Formulas and code for
+// adapting inference to GDN/KDA linear modules", section 1.2, reduced to Simple
+// GLA: no delta-rule terms, new_v = v; the diagonal is included because the
+// query reads the state after the token's own update, blueprint page, section
+// "B2 lightning-attn (Simple GLA)"):
+//
+//   A^T = K Q^T, then A[i][j] = scale * exp(G_i - G_j) * (q_i . k_j) for j <= i, else 0
+//   O^T = S^T Q^T (rows scaled by scale * exp(G_i)) + V^T A^T
+//   S   = exp(G_last) * S + (K * exp(G_last - G))^T V
+//
+// Everything is written in transposed form so that each MFMA result is
+// already in the register layout the next MFMA consumes:
+//   * the fp32 state S lives in the accumulators of the state update
+//     (32x32 tiles: lane l holds S[dk rows 8(v/4)+4(l/32)+v%4][dv column l%32]);
+//     converted to bf16 in registers it is directly the A operand of S^T Q^T,
+//     with Q read in the matching order of its dk rows;
+//   * A^T = K Q^T leaves each lane one query column i and 16 key rows j, i.e.
+//     4 consecutive j per group, written to LDS as A[i][j] with 8-byte stores,
+//     and read back as the B operand of V^T A^T;
+//   * O^T leaves each lane one token column i and 4 consecutive value rows per
+//     group, written to LDS as O[i][dv] rows and stored to HBM 16 B per lane.
+//
+// A workgroup is 4 waves; wave w owns value columns [32w, 32w+32) of the state
+// and of the output. Per chunk the workgroup streams q, k, v (16 KiB each) and
+// g from HBM with 16-byte loads, one chunk ahead of the compute (registers),
+// and stages them in LDS: Q and K row-major with 16-byte chunks XOR-swizzled by
+// row, K*exp(G_last-G) and V transposed (token-contiguous) with a swizzle that
+// keeps both the transposing writes and the MFMA operand reads spread over the
+// banks. LDS: 72 KiB for the output phase, so two workgroups fit on a CU.
+#include "sgla_internal.h"
+
+namespace sgla {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;
+constexpr int NT = 256;
+// LDS map, bytes.
+constexpr int OFF_Q = 0;          // Q rows [64][256 B], chunk-swizzled
+constexpr int OFF_K = 16384;      // K rows [64][256 B]; later the O staging rows
+constexpr int OFF_KT = 32768;     // (K*exp(G_last-G))^T [128 dk][128 B]
+constexpr int OFF_VT = 49152;     // V^T [128 dv][128 B]
+constexpr int OFF_A = 65536;      // A[64 i][128 B]
+constexpr int OFF_G = 73728;      // G[64] fp32
+constexpr int LDS_OUT = OFF_G + 256;
+constexpr int LDS_STATE = 32768;  // KT and VT only (state phase, placed at 0)
+
+// Byte offset of 16-byte chunk c of row r in a 256-byte-row tile (Q, K, O).
+__device__ __forceinline__ int row_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+// Byte offset of 16-byte chunk c (8 tokens) of row d in a 128-byte-row tile (KT, VT, A).
+__device__ __forceinline__ int tr_off(int d, int c) {
+    return d * 128 + ((c ^ (((d >> 1) ^ (d >> 3)) & 7)) << 4);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+    return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+    return (a >> 16) | (b & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t pack_f32(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_ld(const char *lds, int off) {
+    return *reinterpret_cast<const T *>(lds + off);
+}
+template <typename T>
+__device__ __forceinline__ void lds_st(char *lds, int off, T v) {
+    *reinterpret_cast<T *>(lds + off) = v;
+}
+
+template <bool STATE_ONLY>
+__global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
+    const int s = blockIdx.x / p.H;
+    const int h = blockIdx.x - s * p.H;
+    if (s >= p.nseg_max) return;
+    const SegEntry se = p.segs[s];
+    if (se.len < 0) return;
+    const bool last = se.p == se.nseg - 1;
+    if (STATE_ONLY && last) return;
+
+    __shared__ __attribute__((aligned(16))) char lds[STATE_ONLY ? LDS_STATE : LDS_OUT];
+    const int offKT = STATE_ONLY ? 0 : OFF_KT;
+    const int offVT = STATE_ONLY ? 16384 : OFF_VT;
+
+    const int H = p.H;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int l = tid & 63;
+    const int ln = l & 31;
+    const int lh = l >> 5;
+    const uint16_t *__restrict__ qg = static_cast<const uint16_t *>(p.q);
+    const uint16_t *__restrict__ kg = static_cast<const uint16_t *>(p.k);
+    const uint16_t *__restrict__ vg = static_cast<const uint16_t *>(p.v);
+    uint16_t *__restrict__ og = static_cast<uint16_t *>(p.out);
+    const int64_t sl = (int64_t)D * D;
+
+    // The carried-in state in accumulator layout.
+    f32x16 S[4];
+    {
+        const float *src = nullptr;
+        if (!STATE_ONLY) {
+            if (se.nseg == 1) src = p.s0 ? p.s0 + ((int64_t)se.seq * H + h) * sl : nullptr;
+            else src = p.buf + ((int64_t)s * H + h) * sl;
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int dk = 32 * b + 8 * (v >> 2) + 4 * lh + (v & 3);
+                S[b][v] = src ? src[dk * D + 32 * w + ln] : 0.f;
+            }
+    }
+
+    // Each thread moves two row pairs of 16-byte chunks per tile:
+    // pair pr = (tid >> 4) + 16 * it, rows 2pr and 2pr+1, chunk cidx.
+    const int cidx = tid & 15;
+    u32x4 qr[2][2], kr[2][2], vr[2][2];
+    float gr = 0.f;
+    auto issue = [&](int64_t t0, int n) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int r = 2 * ((tid >> 4) + 16 * it) + rr;
+                const int64_t off = ((t0 + r) * H + h) * D + 8 * cidx;
+                const bool ok = r < n;
+                kr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(kg + off) : u32x4{0, 0, 0, 0};
+                vr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(vg + off) : u32x4{0, 0, 0, 0};
+                if (!STATE_ONLY)
+                    qr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(qg + off) : u32x4{0, 0, 0, 0};
+            }
+        gr = l < n ? p.g[(t0 + l) * H + h] : 0.f;
+    };
+
+    const int len = se.len;
+    if (len > 0) issue(se.tok0, min(64, len));
+    float gam_acc = 0.f;
+
+    for (int c0 = 0; c0 < len; c0 += 64) {
+        const int n = min(64, len - c0);
+        const int64_t t0 = se.tok0 + c0;
+
+        // Gate prefix sum, one lane per token, in every wave.
+        float G = gr;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float up = __shfl_up(G, off, 64);
+            if (l >= off) G += up;
+        }
+        const float Gl = __shfl(G, 63, 64);
+        gam_acc += Gl;
+        float fac[2][2];
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr)
+                fac[it][rr] = __expf(Gl - __shfl(G, 2 * ((tid >> 4) + 16 * it) + rr, 64));
+
+        __syncthreads();  // every reader of the previous chunk's tiles is done
+        if (!STATE_ONLY) {
+#pragma unroll
+            for (int it = 0; it < 2; ++it)
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int r = 2 * ((tid >> 4) + 16 * it) + rr;
+                    lds_st(lds, OFF_Q + row_off(r, cidx), qr[it][rr]);
+                    lds_st(lds, OFF_K + row_off(r, cidx), kr[it][rr]);
+                }
+            if (w == 0) lds_st(lds, OFF_G + 4 * l, G);
+        }
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int r0 = 2 * ((tid >> 4) + 16 * it);
+            const int cb = (r0 & 7) * 2;  // byte offset of the token pair inside its chunk
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const uint32_t a0 = vr[it][0][e2], a1 = vr[it][1][e2];
+                const int d = 8 * cidx + 2 * e2;
+                lds_st(lds, offVT + tr_off(d, r0 >> 3) + cb, pack_lo(a0, a1));
+                lds_st(lds, offVT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(a0, a1));
+                const uint32_t k0 = kr[it][0][e2], k1 = kr[it][1][e2];
+                lds_st(lds, offKT + tr_off(d, r0 >> 3) + cb,
+                       pack_f32(lo_bf16(k0) * fac[it][0], lo_bf16(k1) * fac[it][1]));
+                lds_st(lds, offKT + tr_off(d + 1, r0 >> 3) + cb,
+                       pack_f32(hi_bf16(k0) * fac[it][0], hi_bf16(k1) * fac[it][1]));
+            }
+        }
+        __syncthreads();  // tiles of this chunk are in LDS
+
+        if (c0 + 64 < len) issue(t0 + 64, min(64, len - c0 - 64));
+
+        // V operand (lane: value column 32w+ln, 8 tokens), shared by V^T A^T and the update.
+        bf16x8 vop[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) vop[st] = lds_ld<bf16x8>(lds, offVT + tr_off(32 * w + ln, 2 * st + lh));
+
+        if (!STATE_ONLY) {
+            // Scores: wave 0 -> (j 0-31, i 0-31), 1 -> (j 0-31, i 32-63), 2 -> (j 32-63, i 32-63).
+            if (w < 3) {
+                const int jb = w == 2 ? 1 : 0;
+                const int ib = w == 0 ? 0 : 1;
+                f32x16 acc = {};
+                const int j = 32 * jb + ln;
+                const int i = 32 * ib + ln;
+#pragma unroll
+                for (int st = 0; st < 8; ++st) {
+                    const bf16x8 a = lds_ld<bf16x8>(lds, OFF_K + row_off(j, 2 * st + lh));
+                    const bf16x8 bq = lds_ld<bf16x8>(lds, OFF_Q + row_off(i, 2 * st + lh));
+                    acc = mfma(a, bq, acc);
+                }
+                const float Gi = lds_ld<float>(lds, OFF_G + 4 * i);
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int jr = 32 * jb + 8 * g4 + 4 * lh;
+                    const float4 Gj = lds_ld<float4>(lds, OFF_G + 4 * jr);
+                    const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
+                    float val[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        val[r] = (jr + r <= i) ? p.scale * __expf(Gi - gj[r]) * acc[4 * g4 + r] : 0.f;
+                    u32x2 pk = {pack_f32(val[0], val[1]), pack_f32(val[2], val[3])};
+                    lds_st(lds, OFF_A + tr_off(i, 4 * jb + g4) + 8 * lh, pk);
+                }
+            }
+            // S^T as bf16 A operands (before the state moves on).
+            bf16x8 sop[4][2];
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sop[b][s2][e] = (__bf16)S[b][8 * s2 + e];
+            __syncthreads();  // A complete; K rows free for the O staging
+
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int i = 32 * nt + ln;
+                f32x16 acc = {};
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const int c = 4 * b + 2 * s2;
+                        const bf16x4 x0 = lds_ld<bf16x4>(lds, OFF_Q + row_off(i, c) + 8 * lh);
+                        const bf16x4 x1 = lds_ld<bf16x4>(lds, OFF_Q + row_off(i, c + 1) + 8 * lh);
+                        const bf16x8 bq = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+                        acc = mfma(sop[b][s2], bq, acc);
+                    }
+                const float f = p.scale * __expf(lds_ld<float>(lds, OFF_G + 4 * i));
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[v] *= f;
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    if (nt == 0 && st >= 2) break;
+                    const bf16x8 ba = lds_ld<bf16x8>(lds, OFF_A + tr_off(i, 2 * st + lh));
+                    acc = mfma(vop[st], ba, acc);
+                }
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    u32x2 pk = {pack_f32(acc[4 * g4], acc[4 * g4 + 1]),
+                                pack_f32(acc[4 * g4 + 2], acc[4 * g4 + 3])};
+                    lds_st(lds, OFF_K + row_off(i, 4 * w + g4) + 8 * lh, pk);
+                }
+            }
+        }
+
+        const bool need_update = STATE_ONLY || (c0 + 64 < len) || (last && p.sfin);
+        if (need_update) {
+            const float a = __expf(Gl);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[b][v] *= a;
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const bf16x8 ka = lds_ld<bf16x8>(lds, offKT + tr_off(32 * b + ln, 2 * st + lh));
+                    S[b] = mfma(ka, vop[st], S[b]);
+                }
+            }
+        }
+
+        if (!STATE_ONLY) {
+            __syncthreads();  // O staging rows complete
+#pragma unroll
+            for (int it = 0; it < 2; ++it)
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int r = 2 * ((tid >> 4) + 16 * it) + rr;
+                    if (r < n) {
+                        const u32x4 o = lds_ld<u32x4>(lds, OFF_K + row_off(r, cidx));
+                        *reinterpret_cast<u32x4 *>(og + ((t0 + r) * H + h) * D + 8 * cidx) = o;
+                    }
+                }
+        }
+    }
+
+    float *dst = nullptr;
+    if (STATE_ONLY) dst = p.buf + ((int64_t)s * H + h) * sl;
+    else if (last && p.sfin) dst = p.sfin + ((int64_t)se.seq * H + h) * sl;
+    if (dst) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int dk = 32 * b + 8 * (v >> 2) + 4 * lh + (v & 3);
+                dst[dk * D + 32 * w + ln] = S[b][v];
+            }
+    }
+    if (STATE_ONLY && tid == 0) p.gam[(int64_t)s * H + h] = gam_acc;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t st) {
+    if (p.nseg_max == 0) return hipSuccess;
+    const dim3 grid((unsigned)((int64_t)p.nseg_max * p.H));
+    if (phase_state) hipLaunchKernelGGL((chunk_mfma_kernel<true>), grid, dim3(NT), 0, st, p);
+    else hipLaunchKernelGGL((chunk_mfma_kernel<false>), grid, dim3(NT), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace sgla

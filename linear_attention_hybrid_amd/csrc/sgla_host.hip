@@ -104,11 +104,18 @@ sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const fl
     p.scale = scale;
     const bool bf16 = dtype == SGLA_BF16;
 
+    // bf16 with 128-wide heads runs on the matrix cores; every other
+    // combination on the vector ALUs.
+    const bool mfma = bf16 && Dk == 128 && Dv == 128 && !getenv("SGLA_FORCE_VALU");
+    auto phase = [&](bool state_phase) {
+        return mfma ? launch_chunk_mfma(p, state_phase, st)
+                    : launch_chunk_valu(p, bf16, Dk, Dv, state_phase, st);
+    };
     e = launch_plan(cu_seqlens, B, T, seg_len, nseg_max, const_cast<SegEntry *>(p.segs),
                     const_cast<SeqEntry *>(p.seqs), st);
-    if (e == hipSuccess) e = launch_chunk_valu(p, bf16, Dk, Dv, /*phase_state=*/true, st);
+    if (e == hipSuccess) e = phase(/*state_phase=*/true);
     if (e == hipSuccess) e = launch_scan(p, Dk, Dv, st);
-    if (e == hipSuccess) e = launch_chunk_valu(p, bf16, Dk, Dv, /*phase_state=*/false, st);
+    if (e == hipSuccess) e = phase(/*state_phase=*/false);
     const hipError_t ef = hipFreeAsync(ws, st);
     if (e == hipSuccess) e = ef;
     return hip_status(e);

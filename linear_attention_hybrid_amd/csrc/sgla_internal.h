@@ -51,6 +51,7 @@ hipError_t launch_plan(const int64_t *cu, int B, int T, int seg_len, int nseg_ma
 hipError_t launch_scan(const ChunkParams &p, int Dk, int Dv, hipStream_t st);
 hipError_t launch_chunk_valu(const ChunkParams &p, bool bf16, int Dk, int Dv, bool phase_state,
                              hipStream_t st);
+hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t st);
 hipError_t launch_recurrent_step(const void *q, const void *k, const void *v, const float *g,
                                  float *state, const int32_t *idx, void *out, int N, int H,
                                  int Dk, int Dv, float scale, bool bf16, hipStream_t st);

@@ -222,3 +222,18 @@ def test_workload_varlen_512k():
     cu = inp["cu_seqlens"].cpu().numpy()
     compare(inp, o, S, "bf16", "varlen 512k", heads=heads,
             starts=[int(c) for c in cu[:-1]])
+
+
+@pytest.mark.parametrize("T", [65, 700])
+def test_vector_alu_path_for_bf16_128(T):
+    """bf16 with 128-wide heads normally runs on the matrix cores; the vector
+    ALU kernels stay correct for it too (they serve every other shape)."""
+    say("chunk_fwd forced VALU bf16 T=%d" % T)
+    os.environ["SGLA_FORCE_VALU"] = "1"
+    try:
+        inp = W.make_prefill(1, T, 3, 128, 128, "bf16", "lightning", seed=T, device="cuda",
+                             init="normal")
+        o, S = run_gpu(inp)
+    finally:
+        os.environ.pop("SGLA_FORCE_VALU", None)
+    compare(inp, o, S, "bf16", "forced VALU T=%d" % T)
