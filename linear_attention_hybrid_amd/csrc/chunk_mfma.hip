@@ -89,11 +89,11 @@ __device__ __forceinline__ void lds_st(char *lds, int off, T v) {
 }
 
 template <bool STATE_ONLY>
-__global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void chunk_mfma_kernel(ChunkParams p) {
     const int s = blockIdx.x / p.H;
     const int h = blockIdx.x - s * p.H;
     if (s >= p.nseg_max) return;
-    const SegEntry se = p.segs[s];
+    const SegEntry se = seg_at(p, s);
     if (se.len < 0) return;
     const bool last = se.p == se.nseg - 1;
     if (STATE_ONLY && last) return;
@@ -106,8 +106,6 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int l = tid & 63;
-    const int ln = l & 31;
-    const int lh = l >> 5;
     const uint16_t *__restrict__ qg = static_cast<const uint16_t *>(p.q);
     const uint16_t *__restrict__ kg = static_cast<const uint16_t *>(p.k);
     const uint16_t *__restrict__ vg = static_cast<const uint16_t *>(p.v);
@@ -122,34 +120,52 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
             if (se.nseg == 1) src = p.s0 ? p.s0 + ((int64_t)se.seq * H + h) * sl : nullptr;
             else src = p.buf + ((int64_t)s * H + h) * sl;
         }
+        if (src) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * b + 8 * (v >> 2) + 4 * lh + (v & 3);
-                S[b][v] = src ? src[dk * D + 32 * w + ln] : 0.f;
-            }
+                for (int v = 0; v < 16; ++v) {
+                    const int dk = 32 * b + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+                    S[b][v] = src[dk * D + 32 * w + (l & 31)];
+                }
+        } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) S[b] = f32x16{};
+        }
     }
 
     // Each thread moves two row pairs of 16-byte chunks per tile:
     // pair pr = (tid >> 4) + 16 * it, rows 2pr and 2pr+1, chunk cidx.
-    const int cidx = tid & 15;
     u32x4 qr[2][2], kr[2][2], vr[2][2];
     float gr = 0.f;
+    // Byte offset of this thread's 16-byte piece of row r inside a chunk, the
+    // same for q, k, v and out ([T, H, 128] rows of 256 bytes): 32-bit per
+    // lane on top of a per-chunk uniform base.
+    auto piece = [&](int r, int tv) -> uint32_t {
+        return (uint32_t)(r * H) * (uint32_t)(D * 2) + (uint32_t)(tv & 15) * 16u;
+    };
     auto issue = [&](int64_t t0, int n) {
+        // Opaque copy of the thread index: the per-lane offsets are rebuilt
+        // here rather than kept as twelve 64-bit pointers across the loop.
+        int tv = tid;
+        asm volatile("" : "+v"(tv));
+        const int64_t base = (t0 * H + h) * D;
+        const char *qb = reinterpret_cast<const char *>(qg + base);
+        const char *kb = reinterpret_cast<const char *>(kg + base);
+        const char *vb = reinterpret_cast<const char *>(vg + base);
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
-                const int r = 2 * ((tid >> 4) + 16 * it) + rr;
-                const int64_t off = ((t0 + r) * H + h) * D + 8 * cidx;
+                const int r = 2 * (((tv >> 4) & 15) + 16 * it) + rr;
+                const uint32_t off = piece(r, tv);
                 const bool ok = r < n;
-                kr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(kg + off) : u32x4{0, 0, 0, 0};
-                vr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(vg + off) : u32x4{0, 0, 0, 0};
+                kr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(kb + off) : u32x4{0, 0, 0, 0};
+                vr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(vb + off) : u32x4{0, 0, 0, 0};
                 if (!STATE_ONLY)
-                    qr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(qg + off) : u32x4{0, 0, 0, 0};
+                    qr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(qb + off) : u32x4{0, 0, 0, 0};
             }
-        gr = l < n ? p.g[(t0 + l) * H + h] : 0.f;
+        gr = (tv & 63) < n ? p.g[(t0 + (tv & 63)) * H + h] : 0.f;
     };
 
     const int len = se.len;
@@ -159,6 +175,15 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
     for (int c0 = 0; c0 < len; c0 += 64) {
         const int n = min(64, len - c0);
         const int64_t t0 = se.tok0 + c0;
+        // The swizzled LDS addresses depend on the lane; rebuilding them from
+        // an opaque copy of the thread index each chunk keeps the compiler from
+        // holding ~80 of them in registers across the loop.
+        int tidv = tid;
+        asm volatile("" : "+v"(tidv));
+        const int ln = tidv & 31;
+        const int lh = (tidv >> 5) & 1;
+        const int cidx = tidv & 15;
+        const int prb = (tidv >> 4) & 15;
 
         // Gate prefix sum, one lane per token, in every wave.
         float G = gr;
@@ -174,7 +199,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
         for (int it = 0; it < 2; ++it)
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr)
-                fac[it][rr] = __expf(Gl - __shfl(G, 2 * ((tid >> 4) + 16 * it) + rr, 64));
+                fac[it][rr] = __expf(Gl - __shfl(G, 2 * (prb + 16 * it) + rr, 64));
 
         __syncthreads();  // every reader of the previous chunk's tiles is done
         if (!STATE_ONLY) {
@@ -182,7 +207,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
             for (int it = 0; it < 2; ++it)
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr) {
-                    const int r = 2 * ((tid >> 4) + 16 * it) + rr;
+                    const int r = 2 * (prb + 16 * it) + rr;
                     lds_st(lds, OFF_Q + row_off(r, cidx), qr[it][rr]);
                     lds_st(lds, OFF_K + row_off(r, cidx), kr[it][rr]);
                 }
@@ -190,7 +215,7 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
         }
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
-            const int r0 = 2 * ((tid >> 4) + 16 * it);
+            const int r0 = 2 * (prb + 16 * it);
             const int cb = (r0 & 7) * 2;  // byte offset of the token pair inside its chunk
 #pragma unroll
             for (int e2 = 0; e2 < 4; ++e2) {
@@ -242,14 +267,6 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
                     lds_st(lds, OFF_A + tr_off(i, 4 * jb + g4) + 8 * lh, pk);
                 }
             }
-            // S^T as bf16 A operands (before the state moves on).
-            bf16x8 sop[4][2];
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) sop[b][s2][e] = (__bf16)S[b][8 * s2 + e];
             __syncthreads();  // A complete; K rows free for the O staging
 
 #pragma unroll
@@ -264,7 +281,11 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
                         const bf16x4 x0 = lds_ld<bf16x4>(lds, OFF_Q + row_off(i, c) + 8 * lh);
                         const bf16x4 x1 = lds_ld<bf16x4>(lds, OFF_Q + row_off(i, c + 1) + 8 * lh);
                         const bf16x8 bq = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        acc = mfma(sop[b][s2], bq, acc);
+                        // S^T as the bf16 A operand, converted from the fp32 state.
+                        bf16x8 sa;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) sa[e] = (__bf16)S[b][8 * s2 + e];
+                        acc = mfma(sa, bq, acc);
                     }
                 const float f = p.scale * __expf(lds_ld<float>(lds, OFF_G + 4 * i));
 #pragma unroll
@@ -305,10 +326,11 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
             for (int it = 0; it < 2; ++it)
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr) {
-                    const int r = 2 * ((tid >> 4) + 16 * it) + rr;
+                    const int r = 2 * (prb + 16 * it) + rr;
                     if (r < n) {
                         const u32x4 o = lds_ld<u32x4>(lds, OFF_K + row_off(r, cidx));
-                        *reinterpret_cast<u32x4 *>(og + ((t0 + r) * H + h) * D + 8 * cidx) = o;
+                        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(og + (t0 * H + h) * D) +
+                                                   piece(r, tidv)) = o;
                     }
                 }
         }
@@ -322,8 +344,8 @@ __global__ __launch_bounds__(NT) void chunk_mfma_kernel(ChunkParams p) {
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * b + 8 * (v >> 2) + 4 * lh + (v & 3);
-                dst[dk * D + 32 * w + ln] = S[b][v];
+                const int dk = 32 * b + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+                dst[dk * D + 32 * w + (l & 31)] = S[b][v];
             }
     }
     if (STATE_ONLY && tid == 0) p.gam[(int64_t)s * H + h] = gam_acc;

@@ -101,30 +101,45 @@ __global__ __launch_bounds__(256) void plan_kernel(const int64_t *__restrict__ c
 
 // One thread owns four consecutive state elements of one (sequence, head) and
 // walks the sequence's segments in order. In place: the slot of segment j
-// holds dS_j on entry and S_in(j) on exit.
+// holds dS_j on entry and S_in(j) on exit. The segment states are fetched in
+// batches before they are combined, so a batch costs one memory latency
+// instead of one per segment.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void scan_kernel(ChunkParams p) {
+    constexpr int kBatch = 16;
     const int nh = blockIdx.x;
     const int n = nh / p.H;
     const int h = nh - n * p.H;
-    const SeqEntry se = p.seqs[n];
+    const SeqEntry se = seq_at(p, n);
     if (se.nseg <= 1) return;
     const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
     float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p.s0) S = *reinterpret_cast<const float4 *>(p.s0 + ((int64_t)n * p.H + h) * DK * DV + e);
-    for (int j = 0; j < se.nseg; ++j) {
-        const int s = se.first + j;
-        float4 *slot = reinterpret_cast<float4 *>(p.buf + ((int64_t)s * p.H + h) * DK * DV + e);
-        float4 d = make_float4(0.f, 0.f, 0.f, 0.f);
-        const bool more = j + 1 < se.nseg;
-        if (more) d = *slot;
-        *slot = S;
-        if (more) {
-            const float a = __expf(p.gam[(int64_t)s * p.H + h]);
-            S.x = fmaf(a, S.x, d.x);
-            S.y = fmaf(a, S.y, d.y);
-            S.z = fmaf(a, S.z, d.z);
-            S.w = fmaf(a, S.w, d.w);
+    for (int j0 = 0; j0 < se.nseg; j0 += kBatch) {
+        // Loads first, branch-free: slots past the last segment state are
+        // clamped to a valid one and their values ignored below.
+        float4 d[kBatch];
+        float lg[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int j = min(j0 + b, se.nseg - 2);
+            const int s = se.first + j;
+            d[b] = *reinterpret_cast<const float4 *>(p.buf + ((int64_t)s * p.H + h) * DK * DV + e);
+            lg[b] = p.gam[(int64_t)s * p.H + h];
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int j = j0 + b;
+            if (j >= se.nseg) break;
+            const int s = se.first + j;
+            *reinterpret_cast<float4 *>(p.buf + ((int64_t)s * p.H + h) * DK * DV + e) = S;
+            if (j + 1 < se.nseg) {
+                const float a = __expf(lg[b]);
+                S.x = fmaf(a, S.x, d[b].x);
+                S.y = fmaf(a, S.y, d[b].y);
+                S.z = fmaf(a, S.z, d[b].z);
+                S.w = fmaf(a, S.w, d[b].w);
+            }
         }
     }
 }

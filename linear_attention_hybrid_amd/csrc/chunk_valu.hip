@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void chunk_valu_kernel(ChunkParams p) {
     const int s = unit / p.H;
     const int h = unit - s * p.H;
     if (s >= p.nseg_max) return;
-    const SegEntry se = p.segs[s];
+    const SegEntry se = seg_at(p, s);
     if (se.len < 0) return;
     const bool last = se.p == se.nseg - 1;
     if (STATE_ONLY && last) return;

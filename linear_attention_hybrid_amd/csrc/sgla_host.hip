@@ -72,19 +72,29 @@ sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const fl
     hipStream_t st = static_cast<hipStream_t>(stream);
 
     const int seg_len = choose_seg_len(ttot, B, H);
-    const int64_t nseg_max64 = ttot / seg_len + B + 1;
+    // Without cu_seqlens every sequence has T tokens and the same number of
+    // segments, so no table is built; with it, a device-side plan kernel lays
+    // the segments out (the host never reads the offsets).
+    const bool table = cu_seqlens != nullptr;
+    const int64_t nps64 = T == 0 ? 1 : ((int64_t)T + seg_len - 1) / seg_len;
+    const int64_t nseg_max64 = table ? ttot / seg_len + B + 1 : (int64_t)B * nps64;
     if (nseg_max64 * H > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
     const int nseg_max = (int)nseg_max64;
+    // Sequences that fit in one segment need no segment states and no scan.
+    const bool split = table || nps64 > 1;
 
     // Workspace: segment table, sequence table, per-segment log-decays, states.
-    const size_t segs_b = (size_t)nseg_max * sizeof(SegEntry);
-    const size_t seqs_b = ((size_t)B * sizeof(SeqEntry) + 255) / 256 * 256;
-    const size_t gam_b = ((size_t)nseg_max * H * sizeof(float) + 255) / 256 * 256;
-    const size_t buf_b = (size_t)nseg_max * H * Dk * Dv * sizeof(float);
+    const size_t segs_b = table ? (size_t)nseg_max * sizeof(SegEntry) : 0;
+    const size_t seqs_b = table ? ((size_t)B * sizeof(SeqEntry) + 255) / 256 * 256 : 0;
+    const size_t gam_b = split ? ((size_t)nseg_max * H * sizeof(float) + 255) / 256 * 256 : 0;
+    const size_t buf_b = split ? (size_t)nseg_max * H * Dk * Dv * sizeof(float) : 0;
     const size_t ws_b = segs_b + seqs_b + gam_b + buf_b;
     char *ws = nullptr;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&ws), ws_b, st);
-    if (e != hipSuccess) return SGLA_ERR_HIP;
+    hipError_t e = hipSuccess;
+    if (ws_b) {
+        e = hipMallocAsync(reinterpret_cast<void **>(&ws), ws_b, st);
+        if (e != hipSuccess) return SGLA_ERR_HIP;
+    }
 
     ChunkParams p;
     p.q = q;
@@ -94,14 +104,17 @@ sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const fl
     p.s0 = initial_state;
     p.out = out;
     p.sfin = final_state;
-    p.segs = reinterpret_cast<SegEntry *>(ws);
-    p.seqs = reinterpret_cast<SeqEntry *>(ws + segs_b);
-    p.gam = reinterpret_cast<float *>(ws + segs_b + seqs_b);
-    p.buf = reinterpret_cast<float *>(ws + segs_b + seqs_b + gam_b);
+    p.segs = table ? reinterpret_cast<SegEntry *>(ws) : nullptr;
+    p.seqs = table ? reinterpret_cast<SeqEntry *>(ws + segs_b) : nullptr;
+    p.gam = split ? reinterpret_cast<float *>(ws + segs_b + seqs_b) : nullptr;
+    p.buf = split ? reinterpret_cast<float *>(ws + segs_b + seqs_b + gam_b) : nullptr;
     p.H = H;
     p.nseg_max = nseg_max;
     p.N = B;
     p.scale = scale;
+    p.T = T;
+    p.seg_len = seg_len;
+    p.nps = (int)nps64;
     const bool bf16 = dtype == SGLA_BF16;
 
     // bf16 with 128-wide heads runs on the matrix cores; every other
@@ -111,13 +124,16 @@ sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const fl
         return mfma ? launch_chunk_mfma(p, state_phase, st)
                     : launch_chunk_valu(p, bf16, Dk, Dv, state_phase, st);
     };
-    e = launch_plan(cu_seqlens, B, T, seg_len, nseg_max, const_cast<SegEntry *>(p.segs),
-                    const_cast<SeqEntry *>(p.seqs), st);
-    if (e == hipSuccess) e = phase(/*state_phase=*/true);
-    if (e == hipSuccess) e = launch_scan(p, Dk, Dv, st);
+    if (table)
+        e = launch_plan(cu_seqlens, B, T, seg_len, nseg_max, reinterpret_cast<SegEntry *>(ws),
+                        reinterpret_cast<SeqEntry *>(ws + segs_b), st);
+    if (e == hipSuccess && split) e = phase(/*state_phase=*/true);
+    if (e == hipSuccess && split) e = launch_scan(p, Dk, Dv, st);
     if (e == hipSuccess) e = phase(/*state_phase=*/false);
-    const hipError_t ef = hipFreeAsync(ws, st);
-    if (e == hipSuccess) e = ef;
+    if (ws) {
+        const hipError_t ef = hipFreeAsync(ws, st);
+        if (e == hipSuccess) e = ef;
+    }
     return hip_status(e);
 }
 

@@ -37,13 +37,42 @@ struct ChunkParams {
     float *sfin;          // [N,H,Dk,Dv] or nullptr
     float *buf;           // [nseg_max,H,Dk,Dv]: segment states, then carried-in states
     float *gam;           // [nseg_max,H]: total log-decay of each segment
-    const SegEntry *segs;  // [nseg_max]
-    const SeqEntry *seqs;  // [N]
+    const SegEntry *segs;  // [nseg_max], or nullptr for B equal rows (see seg_at)
+    const SeqEntry *seqs;  // [N], or nullptr likewise
     int H;
     int nseg_max;
     int N;
     float scale;
+    int T;        // tokens per sequence when segs == nullptr
+    int seg_len;  // tokens per segment (a multiple of the chunk size)
+    int nps;      // segments per sequence when segs == nullptr
 };
+
+// Segment s of the call. Without a table (no cu_seqlens) every sequence has
+// the same T tokens and nps segments, so the entry is arithmetic.
+__device__ __forceinline__ SegEntry seg_at(const ChunkParams &p, int s) {
+    if (p.segs) return p.segs[s];
+    SegEntry e;
+    const int n = s / p.nps;
+    const int j = s - n * p.nps;
+    e.seq = n;
+    e.p = j;
+    e.nseg = p.nps;
+    e.tok0 = (int64_t)n * p.T + (int64_t)j * p.seg_len;
+    const int rem = p.T - j * p.seg_len;
+    e.len = rem < p.seg_len ? rem : p.seg_len;
+    e.pad0 = 0;
+    e.pad1 = 0;
+    return e;
+}
+
+__device__ __forceinline__ SeqEntry seq_at(const ChunkParams &p, int n) {
+    if (p.seqs) return p.seqs[n];
+    SeqEntry e;
+    e.first = n * p.nps;
+    e.nseg = p.nps;
+    return e;
+}
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_plan(const int64_t *cu, int B, int T, int seg_len, int nseg_max,
