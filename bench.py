@@ -18,6 +18,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -32,6 +34,46 @@ PREFILL = "prefill_bf16_h32_t8192_d128"
 DECODE = "decode_bf16_n256_h32_d128_x64"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    """sha256 over the library's kernel sources, to tell whether a stored
+    counter record still describes the kernels that are built."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_hybrid_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per call from the committed FETCH_SIZE/WRITE_SIZE record,
+    or None when there is none or the kernels changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_call")
+
+
+def copy_calibration(torch, dev, nbytes=256 << 20, reps=3):
+    """A plain device copy of known size, so FETCH_SIZE/WRITE_SIZE can be
+    scaled to bytes (run under rocprofv3 --pmc)."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def prefill_bytes(B, T, H, Dk, Dv, elem=2, with_s0=False):
@@ -104,6 +146,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
     ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (for counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -120,6 +164,8 @@ def main():
     sgla.library()  # fail loudly when the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
     props = torch.cuda.get_device_properties(dev)
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -148,7 +194,8 @@ def main():
                        "chunk": 64, "scale": inp["scale"], "initial_state": "zero",
                        "final_state": "fp32", "gpu": props.name},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "traffic": recorded_traffic(PREFILL),
                          "kernel": "sgla_chunk_fwd (whole call: plan, segment-state, scan and "
                                    "output kernels)",
                          "algorithmic_bytes_per_launch": nbytes,
@@ -186,7 +233,8 @@ def main():
         dec = {"workload": DECODE, "steps_timed": n_timed, "ms_per_step": region / n_timed,
                "tokens_per_s": N / (region / n_timed * 1e-3),
                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                            "traffic": recorded_traffic(DECODE),
                             "kernel": "sgla_recurrent_step",
                             "algorithmic_bytes_per_launch": nb, "avg_launch_ms": per_avg}}
         result["decode"] = dec
