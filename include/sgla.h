@@ -89,7 +89,7 @@ typedef enum {
  *                 access stays inside the buffers sized from B, T, H, Dk, Dv).
  *   B             number of sequences (>= 0; 0 is a no-op).
  *   T             tokens per sequence, or the packed total (>= 0).
- *   H             heads (>= 1).
+ *   H             heads (1 .. 65536).
  *   Dk, Dv        head sizes of q/k and v.
  *   scale         output scale (normally 1/sqrt(Dk)).
  *   dtype         element type of q, k, v, out.
@@ -103,7 +103,7 @@ typedef enum {
  *
  * Returns SGLA_OK, or SGLA_ERR_INVALID_ARG (null required pointer, negative
  * size, misaligned pointer, B*T*H*max(Dk,Dv) beyond 2^62, bad dtype),
- * SGLA_ERR_UNSUPPORTED (Dk or Dv not in {64, 128}), SGLA_ERR_HIP.
+ * SGLA_ERR_UNSUPPORTED (Dk or Dv not in {64, 128}, or H > 65536), SGLA_ERR_HIP.
  */
 sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                            const float *initial_state, void *out, float *final_state,

@@ -88,6 +88,25 @@ __device__ __forceinline__ void lds_st(char *lds, int off, T v) {
     *reinterpret_cast<T *>(lds + off) = v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts inside
+// each 16-lane row, then the row totals carried by row broadcasts (lanes with
+// no source lane add zero).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    int v = __builtin_bit_cast(int, x);
+#define SGLA_DPP_ADD(ctrl, rmask)                                                          \
+    v = __builtin_bit_cast(int, __builtin_bit_cast(float, v) +                              \
+                                    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp( \
+                                        0, v, ctrl, rmask, 0xf, false)))
+    SGLA_DPP_ADD(0x111, 0xf);  // row_shr:1
+    SGLA_DPP_ADD(0x112, 0xf);  // row_shr:2
+    SGLA_DPP_ADD(0x114, 0xf);  // row_shr:4
+    SGLA_DPP_ADD(0x118, 0xf);  // row_shr:8
+    SGLA_DPP_ADD(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
+    SGLA_DPP_ADD(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
+#undef SGLA_DPP_ADD
+    return __builtin_bit_cast(float, v);
+}
+
 template <bool STATE_ONLY>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void chunk_mfma_kernel(ChunkParams p) {
     const int s = blockIdx.x / p.H;
@@ -186,13 +205,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
         const int prb = (tidv >> 4) & 15;
 
         // Gate prefix sum, one lane per token, in every wave.
-        float G = gr;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float up = __shfl_up(G, off, 64);
-            if (l >= off) G += up;
-        }
-        const float Gl = __shfl(G, 63, 64);
+        const float G = wave_prefix_sum(gr);
+        const float Gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
         gam_acc += Gl;
         float fac[2][2];
 #pragma unroll

@@ -10,6 +10,9 @@ using namespace sgla;
 namespace {
 
 constexpr int kVersion = 100;  // 0.1.0
+// Heads per call: keeps the byte offset of a token row inside a 64-token
+// chunk (64 * H * Dv * 2 bytes) within 32 bits.
+constexpr int kMaxHeads = 65536;
 
 bool misaligned(const void *p, uintptr_t a = 16) {
     return p && (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
@@ -60,6 +63,7 @@ sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const fl
     if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
     if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
+    if (H > kMaxHeads) return SGLA_ERR_UNSUPPORTED;
     const int64_t ttot = cu_seqlens ? (int64_t)T : (int64_t)B * T;
     if (ttot > ((int64_t)1 << 62) / ((int64_t)H * 128)) return SGLA_ERR_INVALID_ARG;
     if ((int64_t)B * H > (int64_t)1 << 30) return SGLA_ERR_INVALID_ARG;

@@ -79,7 +79,8 @@ def test_chunk_fwd_validation(lib):
     assert chunk(lib, s0=A + 4) == 1
     assert chunk(lib, sf=A + 8) == 1
     assert chunk(lib, cu=A + 4) == 1
-    assert chunk(lib, B=1, T=2**31 - 1, H=2**30, Dk=128, Dv=128) == 1
+    assert chunk(lib, B=2**28, T=2**31 - 1, H=1, Dk=128, Dv=128) == 1  # B*T*H*D past 2^62
+    assert chunk(lib, B=1, T=1, H=2**16 + 1) == 2                      # beyond the head limit
 
 
 @pytest.mark.skipif("not _no_gpu()", reason="could reach a launch if validation were wrong")
