@@ -66,14 +66,79 @@ def recorded_traffic(workload):
 
 
 def copy_calibration(torch, dev, nbytes=256 << 20, reps=3):
-    """A plain device copy of known size, so FETCH_SIZE/WRITE_SIZE can be
-    scaled to bytes (run under rocprofv3 --pmc)."""
-    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    """An elementwise pass of known size (fp32 negation: nbytes read, nbytes
+    written, kernel name containing ``neg_kernel``), so FETCH_SIZE/WRITE_SIZE
+    can be scaled to bytes when run under rocprofv3 --pmc."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(reps):
-        dst.copy_(src)
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
     del src, dst
+
+
+def _counter_rows(run_dir, counter):
+    """(kernel name, value) per dispatch from the counter CSVs rocprofv3
+    wrote under run_dir (--output-format csv)."""
+    import csv
+    rows = []
+    for path in sorted(glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"),
+                                 recursive=True)):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return [(name, val) for _, name, val in rows]
+
+
+def _per_kernel_avg(rows):
+    acc = {}
+    for name, val in rows:
+        acc.setdefault(name, []).append(val)
+    return {name: sum(v) / len(v) for name, v in acc.items()}
+
+
+def record_traffic(fetch_dir, write_dir, calib_bytes=256 << 20):
+    """Turn a FETCH_SIZE run and a WRITE_SIZE run of
+    ``bench.py --copy-calibration`` into HBM bytes per call.
+
+    Both counters are in KiB per dispatch. Each is scaled by what it reads
+    for the fp32 negation pass of known size (calib_bytes read and written),
+    and the per-kernel averages are summed over the kernels of one call:
+    plan/state/scan/output for the chunked forward, the step kernel for
+    decode. Writes profiles/traffic.json keyed by workload, with the hash of
+    the kernel sources the counters were taken on."""
+    fetch = _per_kernel_avg(_counter_rows(fetch_dir, "FETCH_SIZE"))
+    write = _per_kernel_avg(_counter_rows(write_dir, "WRITE_SIZE"))
+    cal = [n for n in fetch if "neg_kernel" in n]
+    if not cal or not any("neg_kernel" in n for n in write):
+        raise SystemExit("record-traffic: no calibration pass (neg_kernel) in the counter runs")
+    f_scale = calib_bytes / (fetch[cal[0]] * 1024.0)
+    w_scale = calib_bytes / (write[[n for n in write if "neg_kernel" in n][0]] * 1024.0)
+
+    def kbytes(pred):
+        names = [n for n in fetch if pred(n)]
+        per = {n: (fetch[n] * 1024.0 * f_scale, write.get(n, 0.0) * 1024.0 * w_scale) for n in names}
+        return per, sum(a + b for a, b in per.values())
+
+    pre, pre_total = kbytes(lambda n: "sgla" in n and "recurrent" not in n)
+    dec, dec_total = kbytes(lambda n: "sgla" in n and "recurrent" in n)
+    src = kernel_source_hash()
+    rec = {"_calibration": {"fetch_scale": f_scale, "write_scale": w_scale,
+                            "pass": "fp32 negation, %d bytes read and written" % calib_bytes}}
+    if pre:
+        rec[PREFILL] = {"source_hash": src, "bytes_per_call": pre_total,
+                        "kernels": {n: {"fetch": a, "write": b} for n, (a, b) in pre.items()}}
+    if dec:
+        rec[DECODE] = {"source_hash": src, "bytes_per_call": dec_total,
+                       "kernels": {n: {"fetch": a, "write": b} for n, (a, b) in dec.items()}}
+    os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec, indent=1, sort_keys=True))
+    return 0
 
 
 def prefill_bytes(B, T, H, Dk, Dv, elem=2, with_s0=False):
@@ -115,6 +180,31 @@ def time_calls(fn, steps, warmup, torch):
     return wall, region, per
 
 
+def time_flushed(fn, reps, torch, dev, flush_bytes=1 << 30):
+    """Per-call times with the caches emptied before each call: a 1 GiB
+    buffer is overwritten between calls (outside the timed events), so the
+    call's inputs come from HBM rather than the 256 MB memory-side cache."""
+    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    per = []
+    for _ in range(reps):
+        flush.fill_(1.0)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b))
+    del flush
+    return per
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
 def cpu_baseline(inp, W):
     import numpy as np
     import oracle
@@ -147,8 +237,15 @@ def main():
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a 256 MiB device copy (for counter calibration)")
+                    help="also run a 256 MiB elementwise pass (for counter calibration)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: write profiles/traffic.json from two rocprofv3 --pmc "
+                         "runs (FETCH_SIZE, WRITE_SIZE) of this script with --copy-calibration")
+    ap.add_argument("--flushed-reps", type=int, default=20,
+                    help="calls timed one by one after a cache flush (0: skip)")
     args = ap.parse_args()
+    if args.record_traffic:
+        return record_traffic(*args.record_traffic)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d (WORLD_SIZE %d) is not "
@@ -205,7 +302,16 @@ def main():
                      BF16_DENSE_PEAK_TFLOPS,
                      "dense_tile_flops_per_launch": flops},
             "wall_s_timed": wall,
+            "per_call_ms": {"mean": per_avg, "median": median(per), "min": min(per)},
         })
+        if args.flushed_reps > 0:
+            fl = time_flushed(step, args.flushed_reps, torch, dev)
+            result["flushed"] = {
+                "note": "each call after a 1 GiB overwrite; inputs read from HBM",
+                "reps": len(fl), "median_ms": median(fl), "min_ms": min(fl),
+                "tokens_per_s": B * T / (median(fl) * 1e-3),
+                "achieved_GBs": nbytes / (median(fl) * 1e-3) / 1e9,
+                "frac": nbytes / (median(fl) * 1e-3) / 1e9 / HBM_PEAK_GBS}
         if not args.no_cpu:
             result["cpu_baseline"] = cpu_baseline(inp, W)
         del inp, out, fs
