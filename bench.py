@@ -109,13 +109,22 @@ def record_traffic(fetch_dir, write_dir, calib_bytes=256 << 20):
     plan/state/scan/output for the chunked forward, the step kernel for
     decode. Writes profiles/traffic.json keyed by workload, with the hash of
     the kernel sources the counters were taken on."""
-    fetch = _per_kernel_avg(_counter_rows(fetch_dir, "FETCH_SIZE"))
-    write = _per_kernel_avg(_counter_rows(write_dir, "WRITE_SIZE"))
-    cal = [n for n in fetch if "neg_kernel" in n]
-    if not cal or not any("neg_kernel" in n for n in write):
-        raise SystemExit("record-traffic: no calibration pass (neg_kernel) in the counter runs")
-    f_scale = calib_bytes / (fetch[cal[0]] * 1024.0)
-    w_scale = calib_bytes / (write[[n for n in write if "neg_kernel" in n][0]] * 1024.0)
+    fetch_rows = _counter_rows(fetch_dir, "FETCH_SIZE")
+    write_rows = _counter_rows(write_dir, "WRITE_SIZE")
+
+    def calibration(rows):
+        # The input generators negate small tensors too; the calibration
+        # dispatches are the large ones.
+        vals = [v for n, v in rows if "neg_kernel" in n]
+        if not vals:
+            raise SystemExit("record-traffic: no calibration pass (neg_kernel) in the counter runs")
+        big = [v for v in vals if v >= 0.25 * max(vals)]
+        return calib_bytes / (sum(big) / len(big) * 1024.0)
+
+    f_scale = calibration(fetch_rows)
+    w_scale = calibration(write_rows)
+    fetch = _per_kernel_avg(fetch_rows)
+    write = _per_kernel_avg(write_rows)
 
     def kbytes(pred):
         names = [n for n in fetch if pred(n)]
