@@ -9,6 +9,8 @@ stream it runs on, which gives the per-call duration used for the roofline.
 
 The fused decode step (256 sequences x 32 heads, Dk=Dv=128, fp32 state in HBM,
 64 successive steps) is timed the same way and reported in ``decode``.
+``prologue`` reports both again through the entry points that take q and k
+before the per-head RMSNorm and RoPE and apply them as the tiles load.
 
 ``cpu_baseline`` times the oracle (plain C, fp64, OpenMP over (sequence, head)
 units) on the same prefill workload on the host cores.
@@ -243,7 +245,7 @@ def main():
     ap.add_argument("--decode-passes", type=int, default=3,
                     help="timed passes of 64 decode steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue"], default="all")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB elementwise pass (for counter calibration)")
@@ -357,8 +359,70 @@ def main():
             result.update({"value": dec["tokens_per_s"], "unit": "tokens/s",
                            "ms_per_step": dec["ms_per_step"],
                            "config": {"workload": DECODE}, "roofline": dec["roofline"]})
+    if args.only in ("all", "prologue"):
+        result["prologue"] = bench_prologue(args, torch, sgla, W, dev)
+        if args.only == "prologue":
+            pf = result["prologue"]["prefill"]
+            result.update({"value": pf["tokens_per_s"], "unit": "tokens/s",
+                           "ms_per_step": pf["ms_per_call"],
+                           "config": {"workload": PREFILL + " (raw q/k, RMSNorm + RoPE in-kernel)"},
+                           "roofline": pf["roofline"]})
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_prologue(args, torch, sgla, W, dev):
+    """Prefill and decode through the q/k-prologue entry points: same shapes
+    as the plain lines, q and k drawn before normalisation (the "raw"
+    preset), RMSNorm weights 1 + N(0, 0.1^2), RoPE base 10000."""
+    out = {}
+    inp = W.make_prefill(1, 8192, 32, 128, 128, "bf16", "raw", seed=args.seed, device=dev)
+    qw, kw = W.norm_weights(128, seed=args.seed, device=dev)
+    o = torch.empty_like(inp["v"])
+    fs = torch.empty((1, 32, 128, 128), dtype=torch.float32, device=dev)
+
+    def step():
+        sgla.chunk_fwd_qk_norm_rope(inp["q"], inp["k"], inp["v"], inp["g"], qw, kw,
+                                    scale=inp["scale"], out=o, final_state=fs)
+
+    _, region, per = time_calls(step, args.steps, args.warmup, torch)
+    per_avg = sum(per) / len(per)
+    nbytes = prefill_bytes(1, 8192, 32, 128, 128) + 2 * 128 * 4
+    gbs = nbytes / (per_avg * 1e-3) / 1e9
+    out["prefill"] = {"workload": PREFILL + " with raw q/k", "ms_per_call": region / args.steps,
+                      "tokens_per_s": 8192 / (region / args.steps * 1e-3),
+                      "per_call_ms": {"mean": per_avg, "median": median(per), "min": min(per)},
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                   "kernel": "sgla_chunk_fwd_qk_norm_rope (whole call)",
+                                   "algorithmic_bytes_per_launch": nbytes,
+                                   "avg_launch_ms": per_avg}}
+    del inp, o, fs
+    d = W.make_decode(256, 32, 128, 128, 64, "bf16", "raw", seed=4, device=dev)
+    dqw, dkw = W.norm_weights(128, seed=4, device=dev)
+    dout = torch.empty((256, 32, 128), dtype=torch.bfloat16, device=dev)
+    counter = [0]
+
+    def dstep():
+        i = counter[0] % 64
+        counter[0] += 1
+        sgla.recurrent_step_qk_norm_rope(d["q"][i], d["k"][i], d["v"][i], d["g"][i], d["state"],
+                                         dqw, dkw, d["pos"][i], scale=d["scale"], out=dout)
+
+    n_timed = 64 * args.decode_passes
+    _, region, per = time_calls(dstep, n_timed, 64, torch)
+    per_avg = sum(per) / len(per)
+    nb = decode_bytes(256, 32, 128, 128) + 256 * 4 + 2 * 128 * 4
+    gbs = nb / (per_avg * 1e-3) / 1e9
+    out["decode"] = {"workload": DECODE + " with raw q/k", "ms_per_step": region / n_timed,
+                     "tokens_per_s": 256 / (region / n_timed * 1e-3),
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                  "kernel": "sgla_recurrent_step_qk_norm_rope",
+                                  "algorithmic_bytes_per_launch": nb, "avg_launch_ms": per_avg}}
+    del d, dout
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

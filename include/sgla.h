@@ -139,6 +139,69 @@ sgla_status sgla_recurrent_step(const void *q, const void *k, const void *v, con
                                 int H, int Dk, int Dv, float scale, sgla_dtype dtype,
                                 void *stream);
 
+/*
+ * The q/k prologue variants: the same operations with q and k given BEFORE
+ * the lightning layer's per-head normalisation and rotary embedding, which
+ * the kernels apply as they load each tile (page "MiniCPM-SALA — Complete
+ * Blueprint", section "B2 lightning-attn (Simple GLA)", the steps "QK RMSNorm
+ * (per-head)" and "RoPE"). For each token and head, x being its q (or k)
+ * vector of Dk = 128 values:
+ *
+ *     y = bf16( x / sqrt(mean(x^2) + eps) * w )      w = q_weight (k_weight),
+ *                                                     one [128] vector for all heads
+ *     for i < 64, with a = pos * theta^(-2i/128) radians:
+ *       x'[i]      = bf16( y[i] cos a - y[i+64] sin a )
+ *       x'[i + 64] = bf16( y[i+64] cos a + y[i] sin a )
+ *
+ * and x' takes the place of q (k) in the recurrence. The arithmetic between
+ * the two bf16 roundings is fp32; the angle is reduced in fp64, so positions
+ * up to 2^31 keep their accuracy. The pairing of dimension i with i + 64
+ * ("rotate half"), the exact angle and eps as an argument are readings where
+ * the page is silent.
+ *
+ * Only dtype SGLA_BF16 with Dk = 128 (and, for the chunked forward, Dv = 128)
+ * is supported; other combinations return SGLA_ERR_UNSUPPORTED. theta must be
+ * finite and > 0, eps finite and >= 0 (SGLA_ERR_INVALID_ARG otherwise).
+ * q_weight and k_weight are device fp32 [128], 4-byte aligned, never NULL.
+ */
+
+/*
+ * sgla_chunk_fwd_qk_norm_rope — sgla_chunk_fwd with the prologue.
+ *
+ *   pos_offset  [N] int32 device, or NULL for zeros: the position of each
+ *               sequence's first token; token j of sequence n (j counted from
+ *               the sequence start) has position pos_offset[n] + j. A
+ *               sequence continued from an earlier call passes the number of
+ *               tokens already processed.
+ *   theta, eps  RoPE base (10000 on the page) and RMSNorm epsilon.
+ * All other arguments, the workspace and the return codes are those of
+ * sgla_chunk_fwd.
+ */
+sgla_status sgla_chunk_fwd_qk_norm_rope(const void *q, const void *k, const void *v,
+                                        const float *g, const float *initial_state, void *out,
+                                        float *final_state, const int64_t *cu_seqlens,
+                                        const float *q_weight, const float *k_weight,
+                                        const int32_t *pos_offset, float theta, float eps, int B,
+                                        int T, int H, int Dk, int Dv, float scale,
+                                        sgla_dtype dtype, void *stream);
+
+/*
+ * sgla_recurrent_step_qk_norm_rope — sgla_recurrent_step with the prologue.
+ *
+ *   positions   [N] int32 device, never NULL: the position of each row's
+ *               token.
+ *   theta, eps  as above.
+ * All other arguments and the return codes are those of sgla_recurrent_step.
+ * Allocates nothing.
+ */
+sgla_status sgla_recurrent_step_qk_norm_rope(const void *q, const void *k, const void *v,
+                                             const float *g, float *state,
+                                             const int32_t *state_indices, void *out,
+                                             const float *q_weight, const float *k_weight,
+                                             const int32_t *positions, float theta, float eps,
+                                             int N, int H, int Dk, int Dv, float scale,
+                                             sgla_dtype dtype, void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *sgla_status_string(sgla_status s);
 

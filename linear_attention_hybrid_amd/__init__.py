@@ -7,6 +7,12 @@ library is not built, every call raises; there is no other code path.
 
     o, S = chunk_fwd(q, k, v, g, initial_state=None, cu_seqlens=None)
     o    = recurrent_step(q, k, v, g, state, state_indices=None)
+
+and the variants that take q and k before the per-head RMSNorm and RoPE of a
+lightning layer and apply both as the tiles are loaded:
+
+    o, S = chunk_fwd_qk_norm_rope(q, k, v, g, q_weight, k_weight, pos_offset=None)
+    o    = recurrent_step_qk_norm_rope(q, k, v, g, state, q_weight, k_weight, positions)
 """
 from __future__ import annotations
 
@@ -17,8 +23,8 @@ import re
 
 import torch
 
-__all__ = ["chunk_fwd", "recurrent_step", "status_string", "library", "library_path",
-           "exported_symbols", "SglaError"]
+__all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_qk_norm_rope", "recurrent_step_qk_norm_rope",
+           "status_string", "library", "library_path", "exported_symbols", "SglaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libsgla.so")
@@ -53,6 +59,12 @@ def library():
         lib.sgla_chunk_fwd.restype = ci
         lib.sgla_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf, ci, vp]
         lib.sgla_recurrent_step.restype = ci
+        lib.sgla_chunk_fwd_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf,
+                                                    cf, ci, ci, ci, ci, ci, cf, ci, vp]
+        lib.sgla_chunk_fwd_qk_norm_rope.restype = ci
+        lib.sgla_recurrent_step_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                         cf, cf, ci, ci, ci, ci, cf, ci, vp]
+        lib.sgla_recurrent_step_qk_norm_rope.restype = ci
         lib.sgla_status_string.argtypes = [ci]
         lib.sgla_status_string.restype = ctypes.c_char_p
         lib.sgla_version.argtypes = []
@@ -94,18 +106,8 @@ def _check(t, name, dtype, shape, device):
         raise ValueError("%s must be contiguous" % name)
 
 
-def chunk_fwd(q, k, v, g, initial_state=None, cu_seqlens=None, scale=None, out=None,
-              final_state=None, output_final_state=True):
-    """Chunked Simple GLA prefill.
-
-    q, k [B, T, H, Dk], v [B, T, H, Dv] (fp32 or bf16, same dtype, on one GPU),
-    g [B, T, H] fp32 log-decay. With ``cu_seqlens`` (int64 [N+1] on the same
-    device) B must be 1 and the N packed sequences are [cu[i], cu[i+1]).
-    initial_state [N, H, Dk, Dv] fp32 or None (zeros). scale defaults to
-    1/sqrt(Dk). Returns (o [B, T, H, Dv] in v's dtype, final_state [N, H, Dk,
-    Dv] fp32, or None when output_final_state is False and none was given).
-    ``final_state`` may be passed in (also the same tensor as initial_state).
-    """
+def _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
+                output_final_state):
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, Dk]")
     B, T, H, Dk = q.shape
@@ -141,22 +143,66 @@ def chunk_fwd(q, k, v, g, initial_state=None, cu_seqlens=None, scale=None, out=N
         scale = 1.0 / math.sqrt(Dk)
     # Packed input: the C ABI takes B = number of sequences and T = the total.
     Barg = N if cu_seqlens is not None else B
+    return dict(device=device, N=N, out=out, final_state=final_state,
+                sizes=(Barg, T, H, Dk, Dv), scale=float(scale))
+
+
+def chunk_fwd(q, k, v, g, initial_state=None, cu_seqlens=None, scale=None, out=None,
+              final_state=None, output_final_state=True):
+    """Chunked Simple GLA prefill.
+
+    q, k [B, T, H, Dk], v [B, T, H, Dv] (fp32 or bf16, same dtype, on one GPU),
+    g [B, T, H] fp32 log-decay. With ``cu_seqlens`` (int64 [N+1] on the same
+    device) B must be 1 and the N packed sequences are [cu[i], cu[i+1]).
+    initial_state [N, H, Dk, Dv] fp32 or None (zeros). scale defaults to
+    1/sqrt(Dk). Returns (o [B, T, H, Dv] in v's dtype, final_state [N, H, Dk,
+    Dv] fp32, or None when output_final_state is False and none was given).
+    ``final_state`` may be passed in (also the same tensor as initial_state).
+    """
+    a = _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
+                    output_final_state)
+    device = a["device"]
     with torch.cuda.device(device):
         st = library().sgla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state),
-                                      _ptr(out), _ptr(final_state), _ptr(cu_seqlens), Barg, T,
-                                      H, Dk, Dv, float(scale), _DTYPE[q.dtype], _stream(device))
+                                      _ptr(a["out"]), _ptr(a["final_state"]), _ptr(cu_seqlens),
+                                      *a["sizes"], a["scale"], _DTYPE[q.dtype], _stream(device))
     if st != SGLA_OK:
         raise SglaError("sgla_chunk_fwd", st)
-    return out, final_state
+    return a["out"], a["final_state"]
 
 
-def recurrent_step(q, k, v, g, state, state_indices=None, scale=None, out=None):
-    """One fused decode step, updating ``state`` in place.
+def _prologue_args(q_weight, k_weight, Dk, device):
+    _check(q_weight, "q_weight", torch.float32, (Dk,), device)
+    _check(k_weight, "k_weight", torch.float32, (Dk,), device)
 
-    q, k [N, H, Dk], v [N, H, Dv] (fp32 or bf16), g [N, H] fp32,
-    state [slots, H, Dk, Dv] fp32, state_indices [N] int32 (distinct slots) or
-    None for slot = row. Returns o [N, H, Dv] in v's dtype.
+
+def chunk_fwd_qk_norm_rope(q, k, v, g, q_weight, k_weight, pos_offset=None, theta=10000.0,
+                           eps=1e-6, initial_state=None, cu_seqlens=None, scale=None, out=None,
+                           final_state=None, output_final_state=True):
+    """``chunk_fwd`` with q and k given before the per-head RMSNorm (weights
+    q_weight, k_weight: fp32 [Dk], shared by all heads) and the rotate-half
+    RoPE with base ``theta``, both applied inside the kernels (bf16, Dk = Dv =
+    128 only). ``pos_offset`` (int32 [N] or None for zeros) is the position of
+    each sequence's first token; the others follow one by one.
     """
+    a = _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
+                    output_final_state)
+    device = a["device"]
+    _prologue_args(q_weight, k_weight, q.shape[-1], device)
+    if pos_offset is not None:
+        _check(pos_offset, "pos_offset", torch.int32, (a["N"],), device)
+    with torch.cuda.device(device):
+        st = library().sgla_chunk_fwd_qk_norm_rope(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(a["out"]),
+            _ptr(a["final_state"]), _ptr(cu_seqlens), _ptr(q_weight), _ptr(k_weight),
+            _ptr(pos_offset), float(theta), float(eps), *a["sizes"], a["scale"],
+            _DTYPE[q.dtype], _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_chunk_fwd_qk_norm_rope", st)
+    return a["out"], a["final_state"]
+
+
+def _step_args(q, k, v, g, state, state_indices, scale, out):
     if q.dim() != 3:
         raise ValueError("q must be [N, H, Dk]")
     N, H, Dk = q.shape
@@ -183,10 +229,42 @@ def recurrent_step(q, k, v, g, state, state_indices=None, scale=None, out=None):
         _check(out, "out", v.dtype, (N, H, Dv), device)
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)
+    return dict(device=device, out=out, sizes=(N, H, Dk, Dv), scale=float(scale))
+
+
+def recurrent_step(q, k, v, g, state, state_indices=None, scale=None, out=None):
+    """One fused decode step, updating ``state`` in place.
+
+    q, k [N, H, Dk], v [N, H, Dv] (fp32 or bf16), g [N, H] fp32,
+    state [slots, H, Dk, Dv] fp32, state_indices [N] int32 (distinct slots) or
+    None for slot = row. Returns o [N, H, Dv] in v's dtype.
+    """
+    a = _step_args(q, k, v, g, state, state_indices, scale, out)
+    device = a["device"]
     with torch.cuda.device(device):
         st = library().sgla_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state),
-                                           _ptr(state_indices), _ptr(out), N, H, Dk, Dv,
-                                           float(scale), _DTYPE[q.dtype], _stream(device))
+                                           _ptr(state_indices), _ptr(a["out"]), *a["sizes"],
+                                           a["scale"], _DTYPE[q.dtype], _stream(device))
     if st != SGLA_OK:
         raise SglaError("sgla_recurrent_step", st)
-    return out
+    return a["out"]
+
+
+def recurrent_step_qk_norm_rope(q, k, v, g, state, q_weight, k_weight, positions,
+                                theta=10000.0, eps=1e-6, state_indices=None, scale=None,
+                                out=None):
+    """``recurrent_step`` with q and k given before the per-head RMSNorm and
+    RoPE (bf16, Dk = 128 only); ``positions`` (int32 [N]) is the position of
+    each row's token."""
+    a = _step_args(q, k, v, g, state, state_indices, scale, out)
+    device = a["device"]
+    _prologue_args(q_weight, k_weight, q.shape[-1], device)
+    _check(positions, "positions", torch.int32, (q.shape[0],), device)
+    with torch.cuda.device(device):
+        st = library().sgla_recurrent_step_qk_norm_rope(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state), _ptr(state_indices), _ptr(a["out"]),
+            _ptr(q_weight), _ptr(k_weight), _ptr(positions), float(theta), float(eps),
+            *a["sizes"], a["scale"], _DTYPE[q.dtype], _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_recurrent_step_qk_norm_rope", st)
+    return a["out"]

@@ -54,6 +54,14 @@ constexpr int OFF_A = 65536;      // A[64 i][128 B]
 constexpr int OFF_G = 73728;      // G[64] fp32
 constexpr int LDS_OUT = OFF_G + 256;
 constexpr int LDS_STATE = 32768;  // KT and VT only (state phase, placed at 0)
+// q/k prologue tables, after the kernel's own LDS: RMSNorm weights of q and
+// k (2 x 128 fp32), RoPE turns per position per frequency (64 fp64 and the
+// same as fp32), and each wave's base turns of the current chunk (4 x 64 fp32).
+constexpr int PRO_W = 0;
+constexpr int PRO_OM = 1024;
+constexpr int PRO_OREV = 1536;
+constexpr int PRO_BASE = 1792;
+constexpr int PRO_BYTES = 2816;
 
 // Byte offset of 16-byte chunk c of row r in a 256-byte-row tile (Q, K, O).
 __device__ __forceinline__ int row_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
@@ -107,7 +115,45 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     return __builtin_bit_cast(float, v);
 }
 
-template <bool STATE_ONLY>
+// The prologue of one 16-byte piece (8 consecutive dims 8c .. 8c+7 of a
+// 128-dim row, c = lane & 15) held by each of the 16 lanes of a DPP row:
+// RMSNorm over the row (sum of squares across the 16 lanes), weight, bf16;
+// then RoPE against the partner dims (c ^ 8, the other half of the row) with
+// the angles whose cos/sin are given, bf16. `ok` false (a row past the end of
+// the chunk) gives zeros.
+__device__ __forceinline__ u32x4 qk_prologue_piece(u32x4 raw, const char *lds, int w_off,
+                                                   const float cs[8], const float sn[8],
+                                                   bool upper, bool ok, float eps) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        x[2 * j] = lo_bf16(raw[j]);
+        x[2 * j + 1] = hi_bf16(raw[j]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    ss = row16_sum(ss);
+    const float rs = ok ? rsqrtf(ss * (1.f / D) + eps) : 0.f;
+    const float4 w0 = lds_ld<float4>(lds, w_off);
+    const float4 w1 = lds_ld<float4>(lds, w_off + 16);
+    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = round_bf16(x[e] * rs * w[e]);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float z = row16_swap8(y[e]);
+        o[e] = upper ? fmaf(y[e], cs[e], z * sn[e]) : fmaf(y[e], cs[e], -z * sn[e]);
+    }
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = pack_f32(o[2 * j], o[2 * j + 1]);
+    return r;
+}
+
+template <bool STATE_ONLY, bool PRO>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void chunk_mfma_kernel(ChunkParams p) {
     const int s = blockIdx.x / p.H;
     const int h = blockIdx.x - s * p.H;
@@ -117,7 +163,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
     const bool last = se.p == se.nseg - 1;
     if (STATE_ONLY && last) return;
 
-    __shared__ __attribute__((aligned(16))) char lds[STATE_ONLY ? LDS_STATE : LDS_OUT];
+    constexpr int kBase = STATE_ONLY ? LDS_STATE : LDS_OUT;
+    __shared__ __attribute__((aligned(16))) char lds[kBase + (PRO ? PRO_BYTES : 0)];
     const int offKT = STATE_ONLY ? 0 : OFF_KT;
     const int offVT = STATE_ONLY ? 16384 : OFF_VT;
 
@@ -187,6 +234,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
         gr = (tv & 63) < n ? p.g[(t0 + (tv & 63)) * H + h] : 0.f;
     };
 
+    // Prologue tables, and the position of the segment's first token.
+    int64_t pos0 = 0;
+    if (PRO) {
+        if (tid < D) {
+            if (!STATE_ONLY) lds_st(lds, kBase + PRO_W + 4 * tid, p.qw[tid]);
+            lds_st(lds, kBase + PRO_W + 512 + 4 * tid, p.kw[tid]);
+        }
+        if (tid < 64) {
+            const double om = rope_turns_per_pos(tid, D, p.theta);
+            lds_st(lds, kBase + PRO_OM + 8 * tid, om);
+            lds_st(lds, kBase + PRO_OREV + 4 * tid, (float)om);
+        }
+        pos0 = (p.pos_off ? (int64_t)p.pos_off[se.seq] : 0) + (int64_t)se.p * p.seg_len;
+        __syncthreads();
+    }
+
     const int len = se.len;
     if (len > 0) issue(se.tok0, min(64, len));
     float gam_acc = 0.f;
@@ -214,6 +277,40 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr)
                 fac[it][rr] = __expf(Gl - __shfl(G, 2 * (prb + 16 * it) + rr, 64));
+
+        if (PRO) {
+            // This wave's base turns of the chunk's first token, one lane per
+            // frequency; the wave reads them back right away (its LDS
+            // accesses complete in order).
+            const int base = kBase + PRO_BASE + 256 * w;
+            lds_st(lds, base + 4 * (tidv & 63),
+                   rope_base_turns(pos0 + c0, lds_ld<double>(lds, kBase + PRO_OM + 8 * (tidv & 63))));
+            const int fb = 4 * 8 * (cidx & 7);
+            const float4 b0 = lds_ld<float4>(lds, base + fb), b1 = lds_ld<float4>(lds, base + fb + 16);
+            const float4 f0 = lds_ld<float4>(lds, kBase + PRO_OREV + fb);
+            const float4 f1 = lds_ld<float4>(lds, kBase + PRO_OREV + fb + 16);
+            const float bt[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            const float om[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+            const bool upper = cidx >= 8;
+#pragma unroll
+            for (int it = 0; it < 2; ++it)
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int r = 2 * (prb + 16 * it) + rr;
+                    float cs[8], sn[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float a = fmaf((float)r, om[e], bt[e]);
+                        cs[e] = cos_turns(a);
+                        sn[e] = sin_turns(a);
+                    }
+                    kr[it][rr] = qk_prologue_piece(kr[it][rr], lds, kBase + PRO_W + 512 + 32 * cidx,
+                                                   cs, sn, upper, r < n, p.eps);
+                    if (!STATE_ONLY)
+                        qr[it][rr] = qk_prologue_piece(qr[it][rr], lds, kBase + PRO_W + 32 * cidx,
+                                                       cs, sn, upper, r < n, p.eps);
+                }
+        }
 
         __syncthreads();  // every reader of the previous chunk's tiles is done
         if (!STATE_ONLY) {
@@ -370,8 +467,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
 hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t st) {
     if (p.nseg_max == 0) return hipSuccess;
     const dim3 grid((unsigned)((int64_t)p.nseg_max * p.H));
-    if (phase_state) hipLaunchKernelGGL((chunk_mfma_kernel<true>), grid, dim3(NT), 0, st, p);
-    else hipLaunchKernelGGL((chunk_mfma_kernel<false>), grid, dim3(NT), 0, st, p);
+    if (p.qw) {
+        if (phase_state) hipLaunchKernelGGL((chunk_mfma_kernel<true, true>), grid, dim3(NT), 0, st, p);
+        else hipLaunchKernelGGL((chunk_mfma_kernel<false, true>), grid, dim3(NT), 0, st, p);
+    } else {
+        if (phase_state) hipLaunchKernelGGL((chunk_mfma_kernel<true, false>), grid, dim3(NT), 0, st, p);
+        else hipLaunchKernelGGL((chunk_mfma_kernel<false, false>), grid, dim3(NT), 0, st, p);
+    }
     return hipGetLastError();
 }
 

@@ -20,11 +20,37 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <typename Tin, int DK, int DV>
+// Sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row16_sum(x);
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+// The q/k prologue for one head's 128-vector (q in wave 0, k in wave 1): lane
+// l holds dims l and l + 64, the pair that RoPE turns together. RMSNorm over
+// the 128 dims, weight, bf16; then the turn by pos * theta^(-2l/128), bf16.
+// Writes the two results to dst[l] and dst[l + 64].
+__device__ __forceinline__ void step_prologue(float a, float b, const float *__restrict__ w,
+                                              int64_t pos, const StepPrologue &pro, int l,
+                                              float *dst) {
+    const float ss = wave_sum(a * a + b * b);
+    const float rs = rsqrtf(ss * (1.f / 128) + pro.eps);
+    a = round_bf16(a * rs * w[l]);
+    b = round_bf16(b * rs * w[l + 64]);
+    const float t = rope_base_turns(pos, rope_turns_per_pos(l, 128, pro.theta));
+    const float c = cos_turns(t), sn = sin_turns(t);
+    dst[l] = round_bf16(fmaf(a, c, -b * sn));
+    dst[l + 64] = round_bf16(fmaf(b, c, a * sn));
+}
+
+template <typename Tin, int DK, int DV, bool PRO>
 __global__ __launch_bounds__(256) void recurrent_step_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ g, float *__restrict__ state, const int32_t *__restrict__ idx,
-    Tin *__restrict__ out, int H, float scale) {
+    Tin *__restrict__ out, int H, float scale, StepPrologue pro) {
+    static_assert(!PRO || DK == 128, "the prologue is built for 128-dim heads");
     constexpr int CG = DV / 4;     // float4 column groups per state row
     constexpr int RG = 256 / CG;   // row groups
     constexpr int RPT = DK / RG;   // rows per thread
@@ -37,7 +63,15 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
 
     __shared__ float qs[DK], ks[DK], vs[DV];
     __shared__ f32x4 red[RG][CG];
-    if (tid < DK) {
+    if (PRO) {
+        if (tid < 128) {
+            const int l = tid & 63;
+            const bool isq = tid < 64;
+            const Tin *src = (isq ? q : k) + (int64_t)row * DK;
+            step_prologue(load_elem(src, l), load_elem(src, l + 64), isq ? pro.qw : pro.kw,
+                          (int64_t)pro.pos[n], pro, l, isq ? qs : ks);
+        }
+    } else if (tid < DK) {
         qs[tid] = load_elem(q, (int64_t)row * DK + tid);
         ks[tid] = load_elem(k, (int64_t)row * DK + tid);
     }
@@ -80,34 +114,48 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
     }
 }
 
+template <typename Tin, int DK, int DV, bool PRO>
+hipError_t launch_k(const void *q, const void *k, const void *v, const float *g, float *state,
+                    const int32_t *idx, void *out, int N, int H, float scale,
+                    const StepPrologue &pro, hipStream_t st) {
+    hipLaunchKernelGGL((recurrent_step_kernel<Tin, DK, DV, PRO>), dim3((unsigned)(N * H)),
+                       dim3(256), 0, st, static_cast<const Tin *>(q), static_cast<const Tin *>(k),
+                       static_cast<const Tin *>(v), g, state, idx, static_cast<Tin *>(out), H,
+                       scale, pro);
+    return hipGetLastError();
+}
+
 template <typename Tin, int DK, int DV>
 hipError_t launch_t(const void *q, const void *k, const void *v, const float *g, float *state,
-                    const int32_t *idx, void *out, int N, int H, float scale, hipStream_t st) {
-    hipLaunchKernelGGL((recurrent_step_kernel<Tin, DK, DV>), dim3((unsigned)(N * H)), dim3(256), 0,
-                       st, static_cast<const Tin *>(q), static_cast<const Tin *>(k),
-                       static_cast<const Tin *>(v), g, state, idx, static_cast<Tin *>(out), H,
-                       scale);
-    return hipGetLastError();
+                    const int32_t *idx, void *out, int N, int H, float scale,
+                    const StepPrologue &pro, hipStream_t st) {
+    if constexpr (DK == 128)
+        if (pro.qw) return launch_k<Tin, DK, DV, true>(q, k, v, g, state, idx, out, N, H, scale, pro, st);
+    return launch_k<Tin, DK, DV, false>(q, k, v, g, state, idx, out, N, H, scale, pro, st);
 }
 
 template <typename Tin>
 hipError_t launch_dims(const void *q, const void *k, const void *v, const float *g, float *state,
                        const int32_t *idx, void *out, int N, int H, int Dk, int Dv, float scale,
-                       hipStream_t st) {
-    if (Dk == 128 && Dv == 128) return launch_t<Tin, 128, 128>(q, k, v, g, state, idx, out, N, H, scale, st);
-    if (Dk == 128 && Dv == 64) return launch_t<Tin, 128, 64>(q, k, v, g, state, idx, out, N, H, scale, st);
-    if (Dk == 64 && Dv == 128) return launch_t<Tin, 64, 128>(q, k, v, g, state, idx, out, N, H, scale, st);
-    return launch_t<Tin, 64, 64>(q, k, v, g, state, idx, out, N, H, scale, st);
+                       const StepPrologue &pro, hipStream_t st) {
+    if (Dk == 128 && Dv == 128)
+        return launch_t<Tin, 128, 128>(q, k, v, g, state, idx, out, N, H, scale, pro, st);
+    if (Dk == 128 && Dv == 64)
+        return launch_t<Tin, 128, 64>(q, k, v, g, state, idx, out, N, H, scale, pro, st);
+    if (Dk == 64 && Dv == 128)
+        return launch_t<Tin, 64, 128>(q, k, v, g, state, idx, out, N, H, scale, pro, st);
+    return launch_t<Tin, 64, 64>(q, k, v, g, state, idx, out, N, H, scale, pro, st);
 }
 
 }  // namespace
 
 hipError_t launch_recurrent_step(const void *q, const void *k, const void *v, const float *g,
                                  float *state, const int32_t *idx, void *out, int N, int H,
-                                 int Dk, int Dv, float scale, bool bf16, hipStream_t st) {
+                                 int Dk, int Dv, float scale, bool bf16, const StepPrologue &pro,
+                                 hipStream_t st) {
     if (N == 0) return hipSuccess;
-    if (bf16) return launch_dims<uint16_t>(q, k, v, g, state, idx, out, N, H, Dk, Dv, scale, st);
-    return launch_dims<float>(q, k, v, g, state, idx, out, N, H, Dk, Dv, scale, st);
+    if (bf16) return launch_dims<uint16_t>(q, k, v, g, state, idx, out, N, H, Dk, Dv, scale, pro, st);
+    return launch_dims<float>(q, k, v, g, state, idx, out, N, H, Dk, Dv, scale, pro, st);
 }
 
 }  // namespace sgla

@@ -40,6 +40,30 @@ int choose_seg_len(int64_t ttot, int B, int H) {
 
 sgla_status hip_status(hipError_t e) { return e == hipSuccess ? SGLA_OK : SGLA_ERR_HIP; }
 
+// Arguments of the q/k prologue (RMSNorm, RoPE) as the entry points get them.
+struct ProArgs {
+    const float *qw;
+    const float *kw;
+    const int32_t *pos;  // chunked forward: per-sequence offsets (may be null); step: per row
+    float theta;
+    float eps;
+};
+
+bool finite(float x) { return x == x && x - x == 0.f; }
+
+sgla_status check_prologue(const ProArgs &a) {
+    if (!a.qw || !a.kw) return SGLA_ERR_INVALID_ARG;
+    if (misaligned(a.qw, 4) || misaligned(a.kw, 4) || misaligned(a.pos, 4)) return SGLA_ERR_INVALID_ARG;
+    if (!finite(a.theta) || !(a.theta > 0.f) || !finite(a.eps) || a.eps < 0.f)
+        return SGLA_ERR_INVALID_ARG;
+    return SGLA_OK;
+}
+
+sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                      const float *initial_state, void *out, float *final_state,
+                      const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv, float scale,
+                      sgla_dtype dtype, void *stream, const ProArgs *pro);
+
 }  // namespace
 
 extern "C" {
@@ -60,10 +84,40 @@ sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const fl
                            const float *initial_state, void *out, float *final_state,
                            const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv,
                            float scale, sgla_dtype dtype, void *stream) {
+    return chunk_fwd(q, k, v, g, initial_state, out, final_state, cu_seqlens, B, T, H, Dk, Dv,
+                     scale, dtype, stream, nullptr);
+}
+
+sgla_status sgla_chunk_fwd_qk_norm_rope(const void *q, const void *k, const void *v,
+                                        const float *g, const float *initial_state, void *out,
+                                        float *final_state, const int64_t *cu_seqlens,
+                                        const float *q_weight, const float *k_weight,
+                                        const int32_t *pos_offset, float theta, float eps, int B,
+                                        int T, int H, int Dk, int Dv, float scale,
+                                        sgla_dtype dtype, void *stream) {
+    const ProArgs pro{q_weight, k_weight, pos_offset, theta, eps};
+    return chunk_fwd(q, k, v, g, initial_state, out, final_state, cu_seqlens, B, T, H, Dk, Dv,
+                     scale, dtype, stream, &pro);
+}
+
+}  // extern "C"
+
+namespace {
+
+sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                      const float *initial_state, void *out, float *final_state,
+                      const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv, float scale,
+                      sgla_dtype dtype, void *stream, const ProArgs *pro) {
     if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
     if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
     if (H > kMaxHeads) return SGLA_ERR_UNSUPPORTED;
+    if (pro) {
+        // The prologue is built into the bf16 matrix-core kernels (128-wide heads).
+        if (dtype != SGLA_BF16 || Dk != 128 || Dv != 128) return SGLA_ERR_UNSUPPORTED;
+        const sgla_status ps = check_prologue(*pro);
+        if (ps != SGLA_OK) return ps;
+    }
     const int64_t ttot = cu_seqlens ? (int64_t)T : (int64_t)B * T;
     if (ttot > ((int64_t)1 << 62) / ((int64_t)H * 128)) return SGLA_ERR_INVALID_ARG;
     if ((int64_t)B * H > (int64_t)1 << 30) return SGLA_ERR_INVALID_ARG;
@@ -119,11 +173,16 @@ sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const fl
     p.T = T;
     p.seg_len = seg_len;
     p.nps = (int)nps64;
+    p.qw = pro ? pro->qw : nullptr;
+    p.kw = pro ? pro->kw : nullptr;
+    p.pos_off = pro ? pro->pos : nullptr;
+    p.theta = pro ? pro->theta : 0.f;
+    p.eps = pro ? pro->eps : 0.f;
     const bool bf16 = dtype == SGLA_BF16;
 
     // bf16 with 128-wide heads runs on the matrix cores; every other
     // combination on the vector ALUs.
-    const bool mfma = bf16 && Dk == 128 && Dv == 128 && !getenv("SGLA_FORCE_VALU");
+    const bool mfma = bf16 && Dk == 128 && Dv == 128 && (pro || !getenv("SGLA_FORCE_VALU"));
     auto phase = [&](bool state_phase) {
         return mfma ? launch_chunk_mfma(p, state_phase, st)
                     : launch_chunk_valu(p, bf16, Dk, Dv, state_phase, st);
@@ -141,22 +200,54 @@ sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const fl
     return hip_status(e);
 }
 
+sgla_status recurrent_step(const void *q, const void *k, const void *v, const float *g,
+                           float *state, const int32_t *state_indices, void *out, int N, int H,
+                           int Dk, int Dv, float scale, sgla_dtype dtype, void *stream,
+                           const ProArgs *pro) {
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (N < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
+    if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
+    if (pro) {
+        if (dtype != SGLA_BF16 || Dk != 128) return SGLA_ERR_UNSUPPORTED;
+        const sgla_status ps = check_prologue(*pro);
+        if (ps != SGLA_OK) return ps;
+    }
+    if ((int64_t)N * H > ((int64_t)1 << 31) - 1) return SGLA_ERR_INVALID_ARG;
+    if (N == 0) return SGLA_OK;
+    if (!q || !k || !v || !g || !state || !out) return SGLA_ERR_INVALID_ARG;
+    if (pro && !pro->pos) return SGLA_ERR_INVALID_ARG;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) ||
+        misaligned(state) || misaligned(out) || misaligned(state_indices, 4))
+        return SGLA_ERR_INVALID_ARG;
+    StepPrologue sp{};
+    if (pro) sp = StepPrologue{pro->qw, pro->kw, pro->pos, pro->theta, pro->eps};
+    return hip_status(launch_recurrent_step(q, k, v, g, state, state_indices, out, N, H, Dk, Dv,
+                                            scale, dtype == SGLA_BF16, sp,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
 sgla_status sgla_recurrent_step(const void *q, const void *k, const void *v, const float *g,
                                 float *state, const int32_t *state_indices, void *out, int N,
                                 int H, int Dk, int Dv, float scale, sgla_dtype dtype,
                                 void *stream) {
-    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
-    if (N < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
-    if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
-    if ((int64_t)N * H > ((int64_t)1 << 31) - 1) return SGLA_ERR_INVALID_ARG;
-    if (N == 0) return SGLA_OK;
-    if (!q || !k || !v || !g || !state || !out) return SGLA_ERR_INVALID_ARG;
-    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) ||
-        misaligned(state) || misaligned(out) || misaligned(state_indices, 4))
-        return SGLA_ERR_INVALID_ARG;
-    return hip_status(launch_recurrent_step(q, k, v, g, state, state_indices, out, N, H, Dk, Dv,
-                                            scale, dtype == SGLA_BF16,
-                                            static_cast<hipStream_t>(stream)));
+    return recurrent_step(q, k, v, g, state, state_indices, out, N, H, Dk, Dv, scale, dtype,
+                          stream, nullptr);
+}
+
+sgla_status sgla_recurrent_step_qk_norm_rope(const void *q, const void *k, const void *v,
+                                             const float *g, float *state,
+                                             const int32_t *state_indices, void *out,
+                                             const float *q_weight, const float *k_weight,
+                                             const int32_t *positions, float theta, float eps,
+                                             int N, int H, int Dk, int Dv, float scale,
+                                             sgla_dtype dtype, void *stream) {
+    const ProArgs pro{q_weight, k_weight, positions, theta, eps};
+    return recurrent_step(q, k, v, g, state, state_indices, out, N, H, Dk, Dv, scale, dtype,
+                          stream, &pro);
 }
 
 }  // extern "C"

@@ -46,6 +46,13 @@ struct ChunkParams {
     int T;        // tokens per sequence when segs == nullptr
     int seg_len;  // tokens per segment (a multiple of the chunk size)
     int nps;      // segments per sequence when segs == nullptr
+    // q/k prologue (per-head RMSNorm, then rotate-half RoPE) applied as the
+    // tiles are loaded; qw == nullptr: none.
+    const float *qw;         // [Dk] RMSNorm weight of q
+    const float *kw;         // [Dk] RMSNorm weight of k
+    const int32_t *pos_off;  // [N] position of each sequence's first token, or nullptr (0)
+    float theta;             // RoPE base
+    float eps;               // RMSNorm epsilon
 };
 
 // Segment s of the call. Without a table (no cu_seqlens) every sequence has
@@ -74,6 +81,51 @@ __device__ __forceinline__ SeqEntry seq_at(const ChunkParams &p, int n) {
     return e;
 }
 
+// ---- q/k prologue helpers (page "MiniCPM-SALA — Complete Blueprint",
+// section "B2 lightning-attn (Simple GLA)": per-head RMSNorm of q and k with
+// one weight vector of length Dk, stored in bf16; then RoPE with base theta
+// on the fp32 values, stored in bf16). RoPE turns the pair (i, i + Dk/2) by
+// pos * theta^(-2i/Dk) radians in the positive sense:
+// (a, b) -> (a cos - b sin, b cos + a sin).
+
+// Round to the nearest bf16 (ties to even) and back to fp32.
+__device__ __forceinline__ float round_bf16(float x) { return (float)(__bf16)x; }
+
+// Turns per position of frequency i: theta^(-2i/dk) / (2 pi), in fp64.
+__device__ __forceinline__ double rope_turns_per_pos(int i, int dk, float theta) {
+    return exp2(-(2.0 * i / dk) * log2((double)theta)) * 0.15915494309189533577;
+}
+
+// Fractional turns of pos * omega, reduced in fp64 so that positions up to
+// 2^31 keep about 1e-7 turn of accuracy; the result lies in [-0.5, 0.5].
+__device__ __forceinline__ float rope_base_turns(int64_t pos, double turns_per_pos) {
+    double t = (double)pos * turns_per_pos;
+    return (float)(t - rint(t));
+}
+
+// sin and cos of an angle given in turns (|x| < 256): the hardware
+// instructions take turns directly.
+__device__ __forceinline__ float sin_turns(float x) { return __builtin_amdgcn_sinf(x); }
+__device__ __forceinline__ float cos_turns(float x) { return __builtin_amdgcn_cosf(x); }
+
+// Sum over the 16 lanes of a DPP row (lanes 16a .. 16a+15), in every lane:
+// rotations by 8, 4, 2, 1 inside the row.
+__device__ __forceinline__ float row16_sum(float x) {
+#define SGLA_ROR_ADD(ctrl) \
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false))
+    SGLA_ROR_ADD(0x128);  // row_ror:8
+    SGLA_ROR_ADD(0x124);  // row_ror:4
+    SGLA_ROR_ADD(0x122);  // row_ror:2
+    SGLA_ROR_ADD(0x121);  // row_ror:1
+#undef SGLA_ROR_ADD
+    return x;
+}
+
+// The value lane (l ^ 8) holds, for lanes of one DPP row (rotation by 8).
+__device__ __forceinline__ float row16_swap8(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+}
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_plan(const int64_t *cu, int B, int T, int seg_len, int nseg_max,
                        SegEntry *segs, SeqEntry *seqs, hipStream_t st);
@@ -81,9 +133,18 @@ hipError_t launch_scan(const ChunkParams &p, int Dk, int Dv, hipStream_t st);
 hipError_t launch_chunk_valu(const ChunkParams &p, bool bf16, int Dk, int Dv, bool phase_state,
                              hipStream_t st);
 hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t st);
+// Decode-step prologue arguments; qw == nullptr: none.
+struct StepPrologue {
+    const float *qw;
+    const float *kw;
+    const int32_t *pos;  // [N] position of each row's token
+    float theta;
+    float eps;
+};
 hipError_t launch_recurrent_step(const void *q, const void *k, const void *v, const float *g,
                                  float *state, const int32_t *idx, void *out, int N, int H,
-                                 int Dk, int Dv, float scale, bool bf16, hipStream_t st);
+                                 int Dk, int Dv, float scale, bool bf16, const StepPrologue &pro,
+                                 hipStream_t st);
 
 // Map a linear workgroup id onto (unit, sub) so that the `nsub` workgroups of
 // one unit land on the same XCD (ids are dealt to the 8 XCDs round-robin) and

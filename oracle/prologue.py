@@ -85,15 +85,55 @@ def sequence_positions(n_tok, cu_seqlens=None):
     return pos
 
 
-def qk_prologue(x, w, pos, theta=10000.0, eps=1e-6):
+def bf16_spacing(x):
+    """Distance between consecutive bf16 numbers at |x| (8 significant bits)."""
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), np.finfo(np.float32).tiny)
+    return np.ldexp(1.0, np.floor(np.log2(a)).astype(np.int64) - 7)
+
+
+def near_rounding_tie(v, band):
+    """True where moving v by up to ``band`` (>= 0, absolute) either way
+    changes its bf16 rounding, i.e. v lies within band of a midpoint between
+    two bf16 numbers. The band must exceed the fp32 spacing at v (the rounding
+    goes through fp32), which every band used here does by far."""
+    v = np.asarray(v, dtype=np.float64)
+    return round_to_bf16(v + band) != round_to_bf16(v - band)
+
+
+def qk_prologue(x, w, pos, theta=10000.0, eps=1e-6, tie_eta=None):
     """The prologue of one of q or k.
 
     x: [B, T, H, d] raw values (bf16 values as floats); w: [d]; pos: [B*T]
     positions in token order (the rows of x flattened over B and T).
-    Returns the bf16 values (as fp64) that the recurrence consumes."""
+    Returns the bf16 values (as fp64) that the recurrence consumes.
+
+    With ``tie_eta`` it also returns, per element, the largest change that a
+    different decision at either bf16 rounding could make, for an
+    implementation whose values before rounding are off by at most tie_eta
+    times the size of what they are made from: tie_eta * |y| for the RMSNorm
+    output y, tie_eta * (|y_i| + |y_partner|) for a RoPE output (its angle and
+    sine/cosine errors scale with the pair it turns, even when the result is
+    near zero). An element within that distance of a midpoint may round the
+    other way: the bound is one spacing of the result for its own rounding,
+    plus, where the RMSNorm output of the element or of its RoPE partner was
+    near a midpoint, that output's spacing and one more spacing of the
+    result. Elsewhere it is 0."""
     x = np.asarray(x, dtype=np.float64)
     B, T, H, d = x.shape
-    y = round_to_bf16(rms_norm(x, w, eps))
+    y_pre = rms_norm(x, w, eps)
+    y = round_to_bf16(y_pre)
     y = y.reshape(B * T, H, d)
-    z = round_to_bf16(rope_rotate_half(y, np.asarray(pos).reshape(B * T), theta))
-    return z.reshape(B, T, H, d)
+    z_pre = rope_rotate_half(y, np.asarray(pos).reshape(B * T), theta)
+    z = round_to_bf16(z_pre)
+    if tie_eta is None:
+        return z.reshape(B, T, H, d)
+    half = d // 2
+    swap = lambda a: np.concatenate([a[..., half:], a[..., :half]], axis=-1)
+    y_pre = y_pre.reshape(B * T, H, d)
+    dy = np.where(near_rounding_tie(y_pre, tie_eta * np.abs(y_pre)), bf16_spacing(2.0 * y), 0.0)
+    dy_pair = dy + swap(dy)
+    sz = bf16_spacing(2.0 * np.maximum(np.abs(z), np.abs(z_pre)))
+    band = tie_eta * (np.abs(y) + np.abs(swap(y)))
+    bound = np.where(near_rounding_tie(z_pre, band), sz, 0.0)
+    bound = bound + np.where(dy_pair > 0, dy_pair + sz, 0.0)
+    return z.reshape(B, T, H, d), bound.reshape(B, T, H, d)

@@ -6,15 +6,19 @@ distributions below. It contains none of the gated-linear-attention arithmetic
 and imports neither the oracle nor the GPU library.
 
 Input recipes (the lightning-layer inputs described on the page "MiniCPM-SALA —
-Complete Blueprint", section "B2 lightning-attn (Simple GLA)": per-head QK
-RMSNorm with eps 1e-6, RoPE with theta 10000 on fp32 q and k, then a cast to
-bf16):
+Complete Blueprint", section "B2 lightning-attn (Simple GLA)": q and k after
+the per-head RMSNorm and RoPE, cast to bf16):
 
 * ``"gaussian"``  : q, k, v ~ N(0, 1) per element; gate input x ~ N(3, 1).
-* ``"lightning"`` : raw q, k rows ~ N(0, 1) scaled to unit RMS (eps 1e-6,
-  weight 1), rotated by RoPE (rotate-half pairing, theta 10000, angles in
-  fp64, at the token's position inside its own sequence); v ~ N(0, 1);
-  gate input x ~ N(4, 1).
+* ``"lightning"`` : q, k rows ~ N(0, 1) scaled to unit RMS (eps 1e-6, weight
+  1); v ~ N(0, 1); gate input x ~ N(4, 1). RoPE would turn each row by a fixed
+  rotation; a row whose direction is uniformly random (an isotropic Gaussian
+  row, scaled by a function of its length) has the same distribution after
+  any rotation, so the rows are not rotated here.
+* ``"raw"``       : q, k as they arrive before the RMSNorm and RoPE (for the
+  entry points that apply both): rows ~ N(0, 1) times a per-row factor
+  exp(N(0, 0.5^2)); v and the gates as in ``"lightning"``. ``norm_weights``
+  draws the two RMSNorm weight vectors, 1 + N(0, 0.1^2) per element.
 
 In both, the per-token per-head log-decay is g = log(sigmoid(x)) in fp32, so
 every decay factor exp(g) lies in (0, 1). Initial states, when present, are
@@ -31,7 +35,6 @@ import numpy as np
 import torch
 import torch.nn.functional as F
 
-ROPE_THETA = 10000.0
 RMS_EPS = 1e-6
 _BLOCK_TOKENS = 32768
 
@@ -98,27 +101,27 @@ def _unit_rms(x: torch.Tensor) -> torch.Tensor:
     return x * torch.rsqrt(x.pow(2).mean(dim=-1, keepdim=True) + RMS_EPS)
 
 
-def _rope(x: torch.Tensor, pos: torch.Tensor) -> torch.Tensor:
-    """Rotate-half RoPE. x [tokens, H, D] fp32, pos [tokens] int64."""
-    D = x.shape[-1]
-    half = D // 2
-    inv_freq = ROPE_THETA ** (-(torch.arange(half, dtype=torch.float64, device=x.device) * 2.0) / D)
-    ang = pos.to(torch.float64)[:, None] * inv_freq[None, :]
-    cos = torch.cos(ang).to(torch.float32)[:, None, :]
-    sin = torch.sin(ang).to(torch.float32)[:, None, :]
-    x1, x2 = x[..., :half], x[..., half:]
-    return torch.cat([x1 * cos - x2 * sin, x2 * cos + x1 * sin], dim=-1)
-
-
-def _draw_qk(shape_tokens, H, D, preset, pos, gen, device, out_dtype):
+def _draw_qk(shape_tokens, H, D, preset, gen, device, out_dtype):
     out = torch.empty((shape_tokens, H, D), dtype=out_dtype, device=device)
     for s in range(0, shape_tokens, _BLOCK_TOKENS):
         e = min(shape_tokens, s + _BLOCK_TOKENS)
         x = torch.randn((e - s, H, D), generator=gen, device=device, dtype=torch.float32)
         if preset == "lightning":
-            x = _rope(_unit_rms(x), pos[s:e])
+            x = _unit_rms(x)
+        elif preset == "raw":
+            f = torch.randn((e - s, H, 1), generator=gen, device=device, dtype=torch.float32)
+            x = x * torch.exp(0.5 * f)
         out[s:e] = x.to(out_dtype)
     return out
+
+
+def norm_weights(D: int, seed: int, device="cpu"):
+    """The q and k RMSNorm weights for the ``"raw"`` preset: fp32 [D] each,
+    1 + N(0, 0.1^2) per element."""
+    gen = generator(seed, device)
+    w = 1.0 + 0.1 * torch.randn((2, D), generator=gen, device=torch.device(device),
+                                dtype=torch.float32)
+    return w[0].contiguous(), w[1].contiguous()
 
 
 def _draw_plain(shape_tokens, inner, gen, device, out_dtype, mean=0.0, std=1.0):
@@ -133,11 +136,11 @@ def _draw_plain(shape_tokens, inner, gen, device, out_dtype, mean=0.0, std=1.0):
 
 
 def gate_mean(preset: str) -> float:
-    return {"gaussian": 3.0, "lightning": 4.0}[preset]
+    return {"gaussian": 3.0, "lightning": 4.0, "raw": 4.0}[preset]
 
 
 def make_prefill(B, T, H, Dk, Dv, dtype="bf16", preset="lightning", seed=0, device="cpu",
-                 cu_seqlens=None, init=None, pos_start=0):
+                 cu_seqlens=None, init=None):
     """Inputs for one chunked-forward call.
 
     Returns a dict with q, k [B, T, H, Dk]; v [B, T, H, Dv] (dtype); g [B, T, H]
@@ -157,13 +160,8 @@ def make_prefill(B, T, H, Dk, Dv, dtype="bf16", preset="lightning", seed=0, devi
         cu_np = None
         N = B
     BT = B * T
-    if cu_np is None:
-        pos = np.tile(np.arange(T, dtype=np.int64) + pos_start, B)
-    else:
-        pos = positions_for(T, cu_np, pos_start)
-    pos_t = torch.from_numpy(pos).to(device)
-    q = _draw_qk(BT, H, Dk, preset, pos_t, gen, device, tdt)
-    k = _draw_qk(BT, H, Dk, preset, pos_t, gen, device, tdt)
+    q = _draw_qk(BT, H, Dk, preset, gen, device, tdt)
+    k = _draw_qk(BT, H, Dk, preset, gen, device, tdt)
     v = _draw_plain(BT, (H, Dv), gen, device, tdt)
     x = _draw_plain(BT, (H,), gen, device, torch.float32, mean=gate_mean(preset))
     g = F.logsigmoid(x)
@@ -186,8 +184,8 @@ def make_decode(N, H, Dk, Dv, steps, dtype="bf16", preset="lightning", seed=0, d
     """Inputs for ``steps`` successive decode steps of N sequences.
 
     Returns q, k [steps, N, H, Dk]; v [steps, N, H, Dv]; g [steps, N, H] fp32;
-    state [slots or N, H, Dk, Dv] fp32 ~ N(0, 0.02^2); scale. Step i of every
-    sequence is at position pos0 + i.
+    state [slots or N, H, Dk, Dv] fp32 ~ N(0, 0.02^2); scale; pos [steps, N]
+    int32, step i of every sequence at position pos0 + i.
     """
     device = torch.device(device)
     tdt = TORCH_DTYPE[dtype]
@@ -199,14 +197,15 @@ def make_decode(N, H, Dk, Dv, steps, dtype="bf16", preset="lightning", seed=0, d
                             dtype=torch.float32) * 0.02
     qs, ks, vs, gs = [], [], [], []
     for i in range(steps):
-        pos = torch.full((N,), pos0 + i, dtype=torch.int64, device=device)
-        qs.append(_draw_qk(N, H, Dk, preset, pos, gen, device, tdt))
-        ks.append(_draw_qk(N, H, Dk, preset, pos, gen, device, tdt))
+        qs.append(_draw_qk(N, H, Dk, preset, gen, device, tdt))
+        ks.append(_draw_qk(N, H, Dk, preset, gen, device, tdt))
         vs.append(_draw_plain(N, (H, Dv), gen, device, tdt))
         x = _draw_plain(N, (H,), gen, device, torch.float32, mean=gate_mean(preset))
         gs.append(F.logsigmoid(x))
+    pos = (torch.arange(steps, dtype=torch.int32, device=device)[:, None] + pos0).expand(steps, N)
     return dict(q=torch.stack(qs), k=torch.stack(ks), v=torch.stack(vs), g=torch.stack(gs),
-                state=state, scale=1.0 / math.sqrt(Dk), dtype=dtype, preset=preset, seed=seed)
+                state=state, scale=1.0 / math.sqrt(Dk), dtype=dtype, preset=preset, seed=seed,
+                pos=pos.contiguous())
 
 
 def make_workload(name: str, seed: int = 0, device="cpu", preset=None):

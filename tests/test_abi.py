@@ -26,7 +26,8 @@ def _no_gpu():
 
 def test_header_declares_the_entry_points():
     names = sgla.exported_symbols()
-    for n in ("sgla_chunk_fwd", "sgla_recurrent_step", "sgla_status_string", "sgla_version"):
+    for n in ("sgla_chunk_fwd", "sgla_recurrent_step", "sgla_chunk_fwd_qk_norm_rope",
+              "sgla_recurrent_step_qk_norm_rope", "sgla_status_string", "sgla_version"):
         assert n in names
 
 
@@ -107,6 +108,50 @@ def test_recurrent_step_pointer_checks(lib):
     assert step(lib, N=1, q=A + 2) == 1
     assert step(lib, N=1, idx=A + 2) == 1
     assert step(lib, N=1, state=A + 4) == 1
+
+
+def chunk_pro(lib, q=A, k=A, v=A, g=A, s0=None, out=A, sf=None, cu=None, qw=A, kw=A, pos=None,
+              theta=1e4, eps=1e-6, B=0, T=0, H=1, Dk=128, Dv=128, dtype=1):
+    return lib.sgla_chunk_fwd_qk_norm_rope(q, k, v, g, s0, out, sf, cu, qw, kw, pos, theta, eps,
+                                           B, T, H, Dk, Dv, 1.0, dtype, None)
+
+
+def step_pro(lib, q=A, k=A, v=A, g=A, state=A, idx=None, out=A, qw=A, kw=A, pos=A, theta=1e4,
+             eps=1e-6, N=0, H=1, Dk=128, Dv=128, dtype=1):
+    return lib.sgla_recurrent_step_qk_norm_rope(q, k, v, g, state, idx, out, qw, kw, pos, theta,
+                                                eps, N, H, Dk, Dv, 1.0, dtype, None)
+
+
+def test_qk_norm_rope_validation(lib):
+    nan, inf = float("nan"), float("inf")
+    # B = 0 / N = 0: every check below still runs before the no-op return.
+    assert chunk_pro(lib) == 0
+    assert chunk_pro(lib, dtype=0) == 2        # the prologue is built for bf16
+    assert chunk_pro(lib, Dk=64, Dv=64) == 2
+    assert chunk_pro(lib, Dv=64) == 2
+    assert chunk_pro(lib, qw=None) == 1
+    assert chunk_pro(lib, kw=None) == 1
+    assert chunk_pro(lib, kw=A + 2) == 1
+    assert chunk_pro(lib, pos=A + 2) == 1
+    assert chunk_pro(lib, pos=A + 4) == 0      # int32 offsets need 4 bytes
+    for bad in (0.0, -1.0, inf, nan):
+        assert chunk_pro(lib, theta=bad) == 1, bad
+    for bad in (-1e-6, inf, nan):
+        assert chunk_pro(lib, eps=bad) == 1, bad
+    assert chunk_pro(lib, eps=0.0) == 0
+    assert step_pro(lib) == 0
+    assert step_pro(lib, Dv=64) == 0
+    assert step_pro(lib, dtype=0) == 2
+    assert step_pro(lib, Dk=64) == 2
+    assert step_pro(lib, qw=None) == 1
+    assert step_pro(lib, theta=nan) == 1
+    assert step_pro(lib, eps=-1.0) == 1
+
+
+@pytest.mark.skipif("not _no_gpu()", reason="could reach a launch if validation were wrong")
+def test_qk_norm_rope_pointer_checks(lib):
+    assert step_pro(lib, N=1, pos=None) == 1   # positions are required for a step
+    assert chunk_pro(lib, B=1, T=1, q=None) == 1
 
 
 def test_binding_refuses_cpu_tensors():

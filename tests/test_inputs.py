@@ -18,7 +18,6 @@ def test_same_seed_same_bytes():
 
 def test_lightning_rows_unit_rms_and_gates_negative():
     w = W.make_prefill(1, 512, 4, 128, 128, "f32", "lightning", seed=1)
-    # RoPE is a rotation, so rows keep the unit RMS of the normalisation.
     rms = w["q"].pow(2).mean(-1).sqrt()
     assert torch.allclose(rms, torch.ones_like(rms), atol=1e-4)
     g = w["g"]
@@ -34,11 +33,16 @@ def test_gaussian_preset_gate_mean():
     assert abs(float(w["v"].std()) - 1.0) < 0.05
 
 
-def test_rope_position_zero_is_identity_after_norm():
-    gen_a = W.generator(3)
-    x = torch.randn((5, 2, 8), generator=gen_a)
-    y = W._rope(x, torch.zeros(5, dtype=torch.int64))
-    assert torch.allclose(x, y)
+def test_raw_preset_rows_vary_in_scale_and_weights():
+    w = W.make_prefill(1, 2048, 4, 128, 128, "f32", "raw", seed=3)
+    log_rms = w["k"].pow(2).mean(-1).sqrt().log()
+    # per-row factor exp(N(0, 0.5^2)) on rows of unit expected RMS
+    assert abs(float(log_rms.std()) - 0.5) < 0.05
+    assert torch.all(w["g"] < 0)
+    qw, kw = W.norm_weights(128, seed=3)
+    assert qw.shape == (128,) and qw.dtype == torch.float32
+    assert abs(float(torch.cat([qw, kw]).mean()) - 1.0) < 0.03
+    assert not torch.equal(qw, kw)
 
 
 def test_varlen_lengths():

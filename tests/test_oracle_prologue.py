@@ -147,3 +147,17 @@ def test_planted_mistake_is_caught(tmp_path, name):
         except AssertionError:
             failed.append(pin.__name__)
     assert failed, "no pin caught the planted mistake %s" % name
+
+
+def test_rounding_tie_helpers():
+    # 1 + 2^-8 lies exactly between the bf16 numbers 1 and 1 + 2^-7
+    assert P.near_rounding_tie(np.array([1.0 + 2.0 ** -8]), 1e-6)[0]
+    assert not P.near_rounding_tie(np.array([1.0]), 1e-3)[0]
+    assert P.near_rounding_tie(np.array([1.0]), 2.0 ** -8 + 1e-12)[0]
+    np.testing.assert_array_equal(P.bf16_spacing(np.array([1.0, 1.5, 3.0, -0.25])),
+                                  [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -9])
+    # far from every midpoint, no element gets a bound
+    x = np.full((1, 1, 1, D), 1.0)
+    z, b = P.qk_prologue(x, np.ones(D), np.zeros(1), 10000.0, 0.0, tie_eta=2.0 ** -20)
+    np.testing.assert_array_equal(z, x)
+    assert not b.any()
