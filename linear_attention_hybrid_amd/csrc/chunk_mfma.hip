@@ -56,12 +56,14 @@ constexpr int LDS_OUT = OFF_G + 256;
 constexpr int LDS_STATE = 32768;  // KT and VT only (state phase, placed at 0)
 // q/k prologue tables, after the kernel's own LDS: RMSNorm weights of q and
 // k (2 x 128 fp32), RoPE turns per position per frequency (64 fp64 and the
-// same as fp32), and each wave's base turns of the current chunk (4 x 64 fp32).
+// same as fp32), cos and sin of one position's turn per frequency (64 x 2
+// fp32), and each wave's base turns of the current chunk (4 x 64 fp32).
 constexpr int PRO_W = 0;
 constexpr int PRO_OM = 1024;
 constexpr int PRO_OREV = 1536;
-constexpr int PRO_BASE = 1792;
-constexpr int PRO_BYTES = 2816;
+constexpr int PRO_ROT = 1792;
+constexpr int PRO_BASE = 2304;
+constexpr int PRO_BYTES = 3328;
 
 // Byte offset of 16-byte chunk c of row r in a 256-byte-row tile (Q, K, O).
 __device__ __forceinline__ int row_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
@@ -118,12 +120,13 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
 // The prologue of one 16-byte piece (8 consecutive dims 8c .. 8c+7 of a
 // 128-dim row, c = lane & 15) held by each of the 16 lanes of a DPP row:
 // RMSNorm over the row (sum of squares across the 16 lanes), weight, bf16;
-// then RoPE against the partner dims (c ^ 8, the other half of the row) with
-// the angles whose cos/sin are given, bf16. `ok` false (a row past the end of
-// the chunk) gives zeros.
+// then RoPE against the partner dims (c ^ 8, the other half of the row), bf16.
+// cs/sn are the cos and sin of each dim's angle, the sine already negated in
+// the lower half (c < 8), where the partner enters with a minus sign. `ok`
+// false (a row past the end of the chunk) gives zeros.
 __device__ __forceinline__ u32x4 qk_prologue_piece(u32x4 raw, const char *lds, int w_off,
-                                                   const float cs[8], const float sn[8],
-                                                   bool upper, bool ok, float eps) {
+                                                   const float cs[8], const float sn[8], bool ok,
+                                                   float eps) {
     float x[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -141,15 +144,18 @@ __device__ __forceinline__ u32x4 qk_prologue_piece(u32x4 raw, const char *lds, i
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = round_bf16(x[e] * rs * w[e]);
-    float o[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float z = row16_swap8(y[e]);
-        o[e] = upper ? fmaf(y[e], cs[e], z * sn[e]) : fmaf(y[e], cs[e], -z * sn[e]);
-    }
     u32x4 r;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = pack_f32(o[2 * j], o[2 * j + 1]);
+    for (int j = 0; j < 4; ++j) {
+        float o[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int e = 2 * j + h;
+            const float t = row16_swap8(y[e]) * sn[e];
+            o[h] = fmaf(y[e], cs[e], t);
+        }
+        r[j] = pack_f32(o[0], o[1]);
+    }
     return r;
 }
 
@@ -245,6 +251,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
             const double om = rope_turns_per_pos(tid, D, p.theta);
             lds_st(lds, kBase + PRO_OM + 8 * tid, om);
             lds_st(lds, kBase + PRO_OREV + 4 * tid, (float)om);
+            const double t = 6.283185307179586477 * (om - rint(om));
+            lds_st(lds, kBase + PRO_ROT + 8 * tid, make_float2((float)cos(t), (float)sin(t)));
         }
         pos0 = (p.pos_off ? (int64_t)p.pos_off[se.seq] : 0) + (int64_t)se.p * p.seg_len;
         __syncthreads();
@@ -289,26 +297,40 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
             const float4 b0 = lds_ld<float4>(lds, base + fb), b1 = lds_ld<float4>(lds, base + fb + 16);
             const float4 f0 = lds_ld<float4>(lds, kBase + PRO_OREV + fb);
             const float4 f1 = lds_ld<float4>(lds, kBase + PRO_OREV + fb + 16);
-            const float bt[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-            const float om[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-            const bool upper = cidx >= 8;
+            // The lower half of the row turns its partner in with a minus
+            // sign: there every sine is negated (the angle is).
+            const float sg = cidx >= 8 ? 1.f : -1.f;
+            const float bt[8] = {sg * b0.x, sg * b0.y, sg * b0.z, sg * b0.w,
+                                 sg * b1.x, sg * b1.y, sg * b1.z, sg * b1.w};
+            const float om[8] = {sg * f0.x, sg * f0.y, sg * f0.z, sg * f0.w,
+                                 sg * f1.x, sg * f1.y, sg * f1.z, sg * f1.w};
+            // Rows 2prb and 2prb + 32 from the hardware sine/cosine, rows
+            // 2prb + 1 and 2prb + 33 by one more position's turn.
+            float cs[2][2][8], sn[2][2][8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float2 rot = lds_ld<float2>(lds, kBase + PRO_ROT + 2 * fb + 8 * e);
+                const float r1s = sg * rot.y;
+#pragma unroll
+                for (int it = 0; it < 2; ++it) {
+                    const float a = fmaf((float)(2 * (prb + 16 * it)), om[e], bt[e]);
+                    const float c0 = cos_turns(a), s0 = sin_turns(a);
+                    cs[it][0][e] = c0;
+                    sn[it][0][e] = s0;
+                    cs[it][1][e] = fmaf(c0, rot.x, -s0 * r1s);
+                    sn[it][1][e] = fmaf(s0, rot.x, c0 * r1s);
+                }
+            }
 #pragma unroll
             for (int it = 0; it < 2; ++it)
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr) {
                     const int r = 2 * (prb + 16 * it) + rr;
-                    float cs[8], sn[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float a = fmaf((float)r, om[e], bt[e]);
-                        cs[e] = cos_turns(a);
-                        sn[e] = sin_turns(a);
-                    }
                     kr[it][rr] = qk_prologue_piece(kr[it][rr], lds, kBase + PRO_W + 512 + 32 * cidx,
-                                                   cs, sn, upper, r < n, p.eps);
+                                                   cs[it][rr], sn[it][rr], r < n, p.eps);
                     if (!STATE_ONLY)
                         qr[it][rr] = qk_prologue_piece(qr[it][rr], lds, kBase + PRO_W + 32 * cidx,
-                                                       cs, sn, upper, r < n, p.eps);
+                                                       cs[it][rr], sn[it][rr], r < n, p.eps);
                 }
         }
 

@@ -122,8 +122,9 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // The value lane (l ^ 8) holds, for lanes of one DPP row (rotation by 8).
+// No `old` operand, so the move can fold into the instruction that uses it.
 __device__ __forceinline__ float row16_swap8(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xf, 0xf, true));
 }
 
 // Launchers (return hipSuccess or the launch error).
