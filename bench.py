@@ -245,7 +245,8 @@ def main():
     ap.add_argument("--decode-passes", type=int, default=3,
                     help="timed passes of 64 decode steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "epilogue"],
+                    default="all")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB elementwise pass (for counter calibration)")
@@ -367,8 +368,38 @@ def main():
                            "ms_per_step": pf["ms_per_call"],
                            "config": {"workload": PREFILL + " (raw q/k, RMSNorm + RoPE in-kernel)"},
                            "roofline": pf["roofline"]})
+    if args.only in ("all", "epilogue"):
+        result["epilogue"] = bench_epilogue(args, torch, sgla, W, dev)
+        if args.only == "epilogue":
+            e = result["epilogue"]
+            result.update({"value": e["tokens_per_s"], "unit": "tokens/s",
+                           "ms_per_step": e["ms_per_call"],
+                           "config": {"workload": e["workload"]}, "roofline": e["roofline"]})
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_epilogue(args, torch, sgla, W, dev):
+    """The output epilogue (RMSNorm over all 32 heads of a token, sigmoid
+    gate) on the prefill's output shape: 8192 tokens x 4096, bf16."""
+    rows, width = 8192, 4096
+    inp = W.make_epilogue(rows, width, "bf16", seed=args.seed, device=dev)
+    out = torch.empty_like(inp["o"])
+
+    def step():
+        sgla.out_norm_gate(inp["o"], inp["z"], inp["weight"], out=out)
+
+    _, region, per = time_calls(step, args.steps, args.warmup, torch)
+    per_avg = sum(per) / len(per)
+    nbytes = 3 * rows * width * 2 + width * 4
+    gbs = nbytes / (per_avg * 1e-3) / 1e9
+    del inp, out
+    return {"workload": "out_norm_gate bf16 %d tokens x %d (32 heads x 128)" % (rows, width),
+            "ms_per_call": region / args.steps, "tokens_per_s": rows / (region / args.steps * 1e-3),
+            "per_call_ms": {"mean": per_avg, "median": median(per), "min": min(per)},
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "kernel": "sgla_out_norm_gate",
+                         "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": per_avg}}
 
 
 def bench_prologue(args, torch, sgla, W, dev):

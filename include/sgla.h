@@ -202,6 +202,40 @@ sgla_status sgla_recurrent_step_qk_norm_rope(const void *q, const void *k, const
                                              int N, int H, int Dk, int Dv, float scale,
                                              sgla_dtype dtype, void *stream);
 
+/*
+ * sgla_out_norm_gate — the output epilogue of a lightning layer.
+ *
+ * Defined by page "MiniCPM-SALA — Complete Blueprint", section
+ * "B2 lightning-attn (Simple GLA)", step "Output Norm + Gate + Projection"
+ * (without the projection). For every row r (one token, all heads
+ * concatenated: width = H * Dv, 4096 on the page):
+ *
+ *     y   = o[r] / sqrt(mean(o[r]^2) + eps) * weight
+ *     out = y * sigmoid(z[r])
+ *
+ * z holds the gate logits (the gate projection of the layer input, before
+ * the sigmoid). With dtype SGLA_BF16, y, the gate and the product are each
+ * stored in bf16 (the module outputs' dtype), the arithmetic between them is
+ * fp32; with SGLA_F32 nothing is rounded beyond fp32.
+ *
+ * Arguments:
+ *   o       [rows, width] dtype; the attention output ([B, T, H, Dv] is
+ *           [B*T, H*Dv]).
+ *   z       [rows, width] dtype, gate logits.
+ *   weight  [width] fp32 RMSNorm weight.
+ *   out     [rows, width] dtype. It may equal o (in place); it must not
+ *           overlap z or weight otherwise.
+ *   rows    >= 0 (0 is a no-op), < 2^31.
+ *   width   a multiple of 8, at most 16384 (SGLA_ERR_UNSUPPORTED otherwise).
+ *   eps     finite, >= 0.
+ * o, z, weight and out must be 16-byte aligned. Returns SGLA_OK,
+ * SGLA_ERR_INVALID_ARG, SGLA_ERR_UNSUPPORTED or SGLA_ERR_HIP; allocates
+ * nothing.
+ */
+sgla_status sgla_out_norm_gate(const void *o, const void *z, const float *weight, void *out,
+                               int64_t rows, int width, float eps, sgla_dtype dtype,
+                               void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *sgla_status_string(sgla_status s);
 

@@ -13,6 +13,11 @@ lightning layer and apply both as the tiles are loaded:
 
     o, S = chunk_fwd_qk_norm_rope(q, k, v, g, q_weight, k_weight, pos_offset=None)
     o    = recurrent_step_qk_norm_rope(q, k, v, g, state, q_weight, k_weight, positions)
+
+and the layer's output epilogue (RMSNorm over all heads of a token, sigmoid
+gate):
+
+    y    = out_norm_gate(o, z, weight)
 """
 from __future__ import annotations
 
@@ -24,7 +29,8 @@ import re
 import torch
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_qk_norm_rope", "recurrent_step_qk_norm_rope",
-           "status_string", "library", "library_path", "exported_symbols", "SglaError"]
+           "out_norm_gate", "status_string", "library", "library_path", "exported_symbols",
+           "SglaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libsgla.so")
@@ -65,6 +71,8 @@ def library():
         lib.sgla_recurrent_step_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                          cf, cf, ci, ci, ci, ci, cf, ci, vp]
         lib.sgla_recurrent_step_qk_norm_rope.restype = ci
+        lib.sgla_out_norm_gate.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ci, cf, ci, vp]
+        lib.sgla_out_norm_gate.restype = ci
         lib.sgla_status_string.argtypes = [ci]
         lib.sgla_status_string.restype = ctypes.c_char_p
         lib.sgla_version.argtypes = []
@@ -268,3 +276,35 @@ def recurrent_step_qk_norm_rope(q, k, v, g, state, q_weight, k_weight, positions
     if st != SGLA_OK:
         raise SglaError("sgla_recurrent_step_qk_norm_rope", st)
     return a["out"]
+
+
+def out_norm_gate(o, z, weight, eps=1e-6, out=None):
+    """The output epilogue: each row of ``width = weight.numel()`` elements of
+    o (the heads of one token, e.g. o [B, T, H, Dv] with width H * Dv) is
+    RMS-normalised with ``weight`` (fp32 [width]) and multiplied by
+    sigmoid(z); z has o's shape and dtype. ``out`` may be o itself. Returns
+    out (o's shape and dtype)."""
+    device = o.device
+    if device.type != "cuda":
+        raise ValueError("out_norm_gate runs on a GPU; o is on %s" % device)
+    if o.dtype not in _DTYPE:
+        raise TypeError("o must be float32 or bfloat16")
+    if weight.dim() != 1:
+        raise ValueError("weight must be 1-D")
+    width = weight.shape[0]
+    if o.numel() % width != 0:
+        raise ValueError("o's size is not a whole number of rows of %d" % width)
+    _check(o, "o", o.dtype, tuple(o.shape), device)
+    _check(z, "z", o.dtype, tuple(o.shape), device)
+    _check(weight, "weight", torch.float32, (width,), device)
+    if out is None:
+        out = torch.empty_like(o)
+    else:
+        _check(out, "out", o.dtype, tuple(o.shape), device)
+    rows = o.numel() // width
+    with torch.cuda.device(device):
+        st = library().sgla_out_norm_gate(_ptr(o), _ptr(z), _ptr(weight), _ptr(out), rows, width,
+                                          float(eps), _DTYPE[o.dtype], _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_out_norm_gate", st)
+    return out

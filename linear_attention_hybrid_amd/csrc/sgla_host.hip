@@ -13,6 +13,9 @@ constexpr int kVersion = 100;  // 0.1.0
 // Heads per call: keeps the byte offset of a token row inside a 64-token
 // chunk (64 * H * Dv * 2 bytes) within 32 bits.
 constexpr int kMaxHeads = 65536;
+// Widest row of the output epilogue: the kernel keeps a row in registers,
+// up to 8 pieces of 8 elements per thread of a 256-thread workgroup.
+constexpr int kMaxOutWidth = 16384;
 
 bool misaligned(const void *p, uintptr_t a = 16) {
     return p && (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
@@ -248,6 +251,21 @@ sgla_status sgla_recurrent_step_qk_norm_rope(const void *q, const void *k, const
     const ProArgs pro{q_weight, k_weight, positions, theta, eps};
     return recurrent_step(q, k, v, g, state, state_indices, out, N, H, Dk, Dv, scale, dtype,
                           stream, &pro);
+}
+
+sgla_status sgla_out_norm_gate(const void *o, const void *z, const float *weight, void *out,
+                               int64_t rows, int width, float eps, sgla_dtype dtype,
+                               void *stream) {
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (rows < 0 || width < 1 || rows > ((int64_t)1 << 31) - 1) return SGLA_ERR_INVALID_ARG;
+    if (!finite(eps) || eps < 0.f) return SGLA_ERR_INVALID_ARG;
+    if (width % 8 != 0 || width > kMaxOutWidth) return SGLA_ERR_UNSUPPORTED;
+    if (rows == 0) return SGLA_OK;
+    if (!o || !z || !weight || !out) return SGLA_ERR_INVALID_ARG;
+    if (misaligned(o) || misaligned(z) || misaligned(weight) || misaligned(out))
+        return SGLA_ERR_INVALID_ARG;
+    return hip_status(launch_out_norm_gate(o, z, weight, out, rows, width, eps,
+                                           dtype == SGLA_BF16, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

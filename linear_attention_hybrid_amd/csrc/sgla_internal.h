@@ -134,6 +134,8 @@ hipError_t launch_scan(const ChunkParams &p, int Dk, int Dv, hipStream_t st);
 hipError_t launch_chunk_valu(const ChunkParams &p, bool bf16, int Dk, int Dv, bool phase_state,
                              hipStream_t st);
 hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t st);
+hipError_t launch_out_norm_gate(const void *o, const void *z, const float *w, void *out,
+                                int64_t rows, int width, float eps, bool bf16, hipStream_t st);
 // Decode-step prologue arguments; qw == nullptr: none.
 struct StepPrologue {
     const float *qw;

@@ -225,6 +225,24 @@ def make_workload(name: str, seed: int = 0, device="cpu", preset=None):
                         device, init=w["init"])
 
 
+def make_epilogue(rows: int, width: int, dtype="bf16", seed=0, device="cpu"):
+    """Inputs of the output epilogue: o [rows, width] ~ N(0, 1) times a per-row
+    factor exp(N(0, 0.5^2)) (attention outputs vary in size from token to
+    token); gate logits z [rows, width] ~ N(0, 2^2), so the gate spans (0, 1);
+    weight [width] fp32 = 1 + N(0, 0.1^2). Draw order: o, the row factors, z,
+    weight."""
+    device = torch.device(device)
+    tdt = TORCH_DTYPE[dtype]
+    gen = generator(seed, device)
+    o = torch.randn((rows, width), generator=gen, device=device, dtype=torch.float32)
+    f = torch.randn((rows, 1), generator=gen, device=device, dtype=torch.float32)
+    o = (o * torch.exp(0.5 * f)).to(tdt)
+    z = (2.0 * torch.randn((rows, width), generator=gen, device=device,
+                           dtype=torch.float32)).to(tdt)
+    w = 1.0 + 0.1 * torch.randn((width,), generator=gen, device=device, dtype=torch.float32)
+    return dict(o=o, z=z, weight=w, dtype=dtype, seed=seed)
+
+
 def to_numpy_f32(t):
     """Exact host copy in fp32 (bf16 -> fp32 is exact)."""
     if t is None:

@@ -27,7 +27,8 @@ def _no_gpu():
 def test_header_declares_the_entry_points():
     names = sgla.exported_symbols()
     for n in ("sgla_chunk_fwd", "sgla_recurrent_step", "sgla_chunk_fwd_qk_norm_rope",
-              "sgla_recurrent_step_qk_norm_rope", "sgla_status_string", "sgla_version"):
+              "sgla_recurrent_step_qk_norm_rope", "sgla_out_norm_gate", "sgla_status_string",
+              "sgla_version"):
         assert n in names
 
 
@@ -152,6 +153,29 @@ def test_qk_norm_rope_validation(lib):
 def test_qk_norm_rope_pointer_checks(lib):
     assert step_pro(lib, N=1, pos=None) == 1   # positions are required for a step
     assert chunk_pro(lib, B=1, T=1, q=None) == 1
+
+
+def epi(lib, o=A, z=A, w=A, out=A, rows=0, width=4096, eps=1e-6, dtype=1):
+    return lib.sgla_out_norm_gate(o, z, w, out, rows, width, eps, dtype, None)
+
+
+def test_out_norm_gate_validation(lib):
+    assert epi(lib) == 0
+    assert epi(lib, dtype=3) == 1
+    assert epi(lib, rows=-1) == 1
+    assert epi(lib, rows=2**31) == 1
+    assert epi(lib, width=0) == 1
+    assert epi(lib, width=4100) == 2          # not a multiple of 8
+    assert epi(lib, width=16384 + 8) == 2     # wider than a row the kernel holds
+    assert epi(lib, eps=-1.0) == 1
+    assert epi(lib, eps=float("nan")) == 1
+
+
+@pytest.mark.skipif("not _no_gpu()", reason="could reach a launch if validation were wrong")
+def test_out_norm_gate_pointer_checks(lib):
+    assert epi(lib, rows=1, o=None) == 1
+    assert epi(lib, rows=1, w=A + 4) == 1
+    assert epi(lib, rows=1, out=A + 8) == 1
 
 
 def test_binding_refuses_cpu_tensors():
