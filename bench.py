@@ -167,10 +167,10 @@ def prefill_flops(B, T, H, Dk, Dv, C=64):
     return B * T * H * per_tok
 
 
-def decode_bytes(N, H, Dk, Dv, elem=2):
-    """One decode step: the fp32 state read and written, q, k, v read, g read,
-    o written."""
-    return N * H * (2 * Dk * Dv * 4 + (2 * Dk + Dv) * elem + 4 + Dv * elem)
+def decode_bytes(N, H, Dk, Dv, elem=2, state_elem=4):
+    """One decode step: the state read and written (fp32, or bf16 with
+    state_elem=2), q, k, v read, g read, o written."""
+    return N * H * (2 * Dk * Dv * state_elem + (2 * Dk + Dv) * elem + 4 + Dv * elem)
 
 
 def time_calls(fn, steps, warmup, torch):
@@ -245,8 +245,8 @@ def main():
     ap.add_argument("--decode-passes", type=int, default=3,
                     help="timed passes of 64 decode steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "epilogue"],
-                    default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "epilogue",
+                                       "bf16-state"], default="all")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB elementwise pass (for counter calibration)")
@@ -368,6 +368,13 @@ def main():
                            "ms_per_step": pf["ms_per_call"],
                            "config": {"workload": PREFILL + " (raw q/k, RMSNorm + RoPE in-kernel)"},
                            "roofline": pf["roofline"]})
+    if args.only in ("all", "bf16-state"):
+        result["decode_bf16_state"] = bench_bf16_state(args, torch, sgla, W, dev)
+        if args.only == "bf16-state":
+            e = result["decode_bf16_state"]
+            result.update({"value": e["tokens_per_s"], "unit": "tokens/s",
+                           "ms_per_step": e["ms_per_step"],
+                           "config": {"workload": e["workload"]}, "roofline": e["roofline"]})
     if args.only in ("all", "epilogue"):
         result["epilogue"] = bench_epilogue(args, torch, sgla, W, dev)
         if args.only == "epilogue":
@@ -377,6 +384,37 @@ def main():
                            "config": {"workload": e["workload"]}, "roofline": e["roofline"]})
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_bf16_state(args, torch, sgla, W, dev):
+    """The batched decode (256 x 32 heads, D=128, 64 successive steps) with
+    the state pool stored in bf16 (sgla_recurrent_step_ex)."""
+    d = W.make_workload(DECODE, seed=4, device=dev)
+    steps, N, H, Dk = d["q"].shape
+    Dv = d["v"].shape[-1]
+    state = d["state"].to(torch.bfloat16)
+    del d["state"]
+    out = torch.empty((N, H, Dv), dtype=d["v"].dtype, device=dev)
+    counter = [0]
+
+    def dstep():
+        i = counter[0] % steps
+        counter[0] += 1
+        sgla.recurrent_step_ex(d["q"][i], d["k"][i], d["v"][i], d["g"][i], state,
+                               scale=d["scale"], out=out)
+
+    n_timed = steps * args.decode_passes
+    _, region, per = time_calls(dstep, n_timed, steps, torch)
+    per_avg = sum(per) / len(per)
+    nb = decode_bytes(N, H, Dk, Dv, state_elem=2)
+    gbs = nb / (per_avg * 1e-3) / 1e9
+    del d, state, out
+    torch.cuda.empty_cache()
+    return {"workload": DECODE + " with a bf16 state pool", "steps_timed": n_timed,
+            "ms_per_step": region / n_timed, "tokens_per_s": N / (region / n_timed * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "kernel": "sgla_recurrent_step_ex (bf16 state)",
+                         "algorithmic_bytes_per_launch": nb, "avg_launch_ms": per_avg}}
 
 
 def bench_epilogue(args, torch, sgla, W, dev):

@@ -203,6 +203,30 @@ sgla_status sgla_recurrent_step_qk_norm_rope(const void *q, const void *k, const
                                              sgla_dtype dtype, void *stream);
 
 /*
+ * sgla_recurrent_step_ex — the decode step with every option: the state pool
+ * stored in fp32 or bf16, and the q/k prologue on or off.
+ *
+ *   state        [slots, H, Dk, Dv] in state_dtype, read and written in place.
+ *   state_dtype  SGLA_F32 or SGLA_BF16 (the pool's dtype on the blueprint
+ *                page, section "B2 lightning-attn (Simple GLA)"). A bf16
+ *                state is loaded, decayed, updated and read by the query in
+ *                fp32 (the query sees the updated state before rounding),
+ *                then stored rounded to nearest even; that halves the bytes a
+ *                step moves.
+ *   q_weight     NULL: no prologue (k_weight, positions, theta, eps are
+ *                ignored). Otherwise the prologue of
+ *                sgla_recurrent_step_qk_norm_rope, with the same conditions.
+ * All other arguments and the return codes are those of sgla_recurrent_step;
+ * the bf16 pool must be 16-byte aligned. Allocates nothing.
+ */
+sgla_status sgla_recurrent_step_ex(const void *q, const void *k, const void *v, const float *g,
+                                   void *state, sgla_dtype state_dtype,
+                                   const int32_t *state_indices, void *out,
+                                   const float *q_weight, const float *k_weight,
+                                   const int32_t *positions, float theta, float eps, int N, int H,
+                                   int Dk, int Dv, float scale, sgla_dtype dtype, void *stream);
+
+/*
  * sgla_out_norm_gate — the output epilogue of a lightning layer.
  *
  * Defined by page "MiniCPM-SALA — Complete Blueprint", section

@@ -18,6 +18,9 @@ and the layer's output epilogue (RMSNorm over all heads of a token, sigmoid
 gate):
 
     y    = out_norm_gate(o, z, weight)
+
+``recurrent_step_ex`` takes every decode option at once (a bf16 state pool,
+the prologue).
 """
 from __future__ import annotations
 
@@ -29,7 +32,7 @@ import re
 import torch
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_qk_norm_rope", "recurrent_step_qk_norm_rope",
-           "out_norm_gate", "status_string", "library", "library_path", "exported_symbols",
+           "recurrent_step_ex", "out_norm_gate", "status_string", "library", "library_path", "exported_symbols",
            "SglaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +74,9 @@ def library():
         lib.sgla_recurrent_step_qk_norm_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                          cf, cf, ci, ci, ci, ci, cf, ci, vp]
         lib.sgla_recurrent_step_qk_norm_rope.restype = ci
+        lib.sgla_recurrent_step_ex.argtypes = [vp, vp, vp, vp, vp, ci, vp, vp, vp, vp, vp, cf, cf,
+                                               ci, ci, ci, ci, cf, ci, vp]
+        lib.sgla_recurrent_step_ex.restype = ci
         lib.sgla_out_norm_gate.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ci, cf, ci, vp]
         lib.sgla_out_norm_gate.restype = ci
         lib.sgla_status_string.argtypes = [ci]
@@ -210,7 +216,7 @@ def chunk_fwd_qk_norm_rope(q, k, v, g, q_weight, k_weight, pos_offset=None, thet
     return a["out"], a["final_state"]
 
 
-def _step_args(q, k, v, g, state, state_indices, scale, out):
+def _step_args(q, k, v, g, state, state_indices, scale, out, allow_bf16_state=False):
     if q.dim() != 3:
         raise ValueError("q must be [N, H, Dk]")
     N, H, Dk = q.shape
@@ -226,7 +232,9 @@ def _step_args(q, k, v, g, state, state_indices, scale, out):
     _check(g, "g", torch.float32, (N, H), device)
     if state.dim() != 4:
         raise ValueError("state must be [slots, H, Dk, Dv]")
-    _check(state, "state", torch.float32, (state.shape[0], H, Dk, Dv), device)
+    if state.dtype not in _DTYPE or (state.dtype != torch.float32 and not allow_bf16_state):
+        raise TypeError("state must be float32%s" % (" or bfloat16" if allow_bf16_state else ""))
+    _check(state, "state", state.dtype, (state.shape[0], H, Dk, Dv), device)
     if state_indices is not None:
         _check(state_indices, "state_indices", torch.int32, (N,), device)
     elif state.shape[0] < N:
@@ -308,3 +316,26 @@ def out_norm_gate(o, z, weight, eps=1e-6, out=None):
     if st != SGLA_OK:
         raise SglaError("sgla_out_norm_gate", st)
     return out
+
+
+def recurrent_step_ex(q, k, v, g, state, state_indices=None, q_weight=None, k_weight=None,
+                      positions=None, theta=10000.0, eps=1e-6, scale=None, out=None):
+    """The decode step with every option: ``state`` may be float32 or
+    bfloat16 (a bf16 pool is updated in fp32 and stored rounded); with
+    ``q_weight`` given, q and k go through the per-head RMSNorm and RoPE
+    first (then ``k_weight`` and ``positions`` are required). Returns o."""
+    a = _step_args(q, k, v, g, state, state_indices, scale, out, allow_bf16_state=True)
+    device = a["device"]
+    if q_weight is not None:
+        if k_weight is None or positions is None:
+            raise ValueError("the prologue needs q_weight, k_weight and positions")
+        _prologue_args(q_weight, k_weight, q.shape[-1], device)
+        _check(positions, "positions", torch.int32, (q.shape[0],), device)
+    with torch.cuda.device(device):
+        st = library().sgla_recurrent_step_ex(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(state), _DTYPE[state.dtype],
+            _ptr(state_indices), _ptr(a["out"]), _ptr(q_weight), _ptr(k_weight), _ptr(positions),
+            float(theta), float(eps), *a["sizes"], a["scale"], _DTYPE[q.dtype], _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_recurrent_step_ex", st)
+    return a["out"]

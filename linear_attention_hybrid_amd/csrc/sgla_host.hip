@@ -204,10 +204,11 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
 }
 
 sgla_status recurrent_step(const void *q, const void *k, const void *v, const float *g,
-                           float *state, const int32_t *state_indices, void *out, int N, int H,
-                           int Dk, int Dv, float scale, sgla_dtype dtype, void *stream,
-                           const ProArgs *pro) {
+                           void *state, sgla_dtype state_dtype, const int32_t *state_indices,
+                           void *out, int N, int H, int Dk, int Dv, float scale, sgla_dtype dtype,
+                           void *stream, const ProArgs *pro) {
     if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (state_dtype != SGLA_F32 && state_dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
     if (N < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
     if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
     if (pro) {
@@ -224,8 +225,9 @@ sgla_status recurrent_step(const void *q, const void *k, const void *v, const fl
         return SGLA_ERR_INVALID_ARG;
     StepPrologue sp{};
     if (pro) sp = StepPrologue{pro->qw, pro->kw, pro->pos, pro->theta, pro->eps};
-    return hip_status(launch_recurrent_step(q, k, v, g, state, state_indices, out, N, H, Dk, Dv,
-                                            scale, dtype == SGLA_BF16, sp,
+    return hip_status(launch_recurrent_step(q, k, v, g, state, state_dtype == SGLA_BF16,
+                                            state_indices, out, N, H, Dk, Dv, scale,
+                                            dtype == SGLA_BF16, sp,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -237,8 +239,8 @@ sgla_status sgla_recurrent_step(const void *q, const void *k, const void *v, con
                                 float *state, const int32_t *state_indices, void *out, int N,
                                 int H, int Dk, int Dv, float scale, sgla_dtype dtype,
                                 void *stream) {
-    return recurrent_step(q, k, v, g, state, state_indices, out, N, H, Dk, Dv, scale, dtype,
-                          stream, nullptr);
+    return recurrent_step(q, k, v, g, state, SGLA_F32, state_indices, out, N, H, Dk, Dv, scale,
+                          dtype, stream, nullptr);
 }
 
 sgla_status sgla_recurrent_step_qk_norm_rope(const void *q, const void *k, const void *v,
@@ -249,8 +251,19 @@ sgla_status sgla_recurrent_step_qk_norm_rope(const void *q, const void *k, const
                                              int N, int H, int Dk, int Dv, float scale,
                                              sgla_dtype dtype, void *stream) {
     const ProArgs pro{q_weight, k_weight, positions, theta, eps};
-    return recurrent_step(q, k, v, g, state, state_indices, out, N, H, Dk, Dv, scale, dtype,
-                          stream, &pro);
+    return recurrent_step(q, k, v, g, state, SGLA_F32, state_indices, out, N, H, Dk, Dv, scale,
+                          dtype, stream, &pro);
+}
+
+sgla_status sgla_recurrent_step_ex(const void *q, const void *k, const void *v, const float *g,
+                                   void *state, sgla_dtype state_dtype,
+                                   const int32_t *state_indices, void *out,
+                                   const float *q_weight, const float *k_weight,
+                                   const int32_t *positions, float theta, float eps, int N, int H,
+                                   int Dk, int Dv, float scale, sgla_dtype dtype, void *stream) {
+    const ProArgs pro{q_weight, k_weight, positions, theta, eps};
+    return recurrent_step(q, k, v, g, state, state_dtype, state_indices, out, N, H, Dk, Dv, scale,
+                          dtype, stream, q_weight ? &pro : nullptr);
 }
 
 sgla_status sgla_out_norm_gate(const void *o, const void *z, const float *weight, void *out,

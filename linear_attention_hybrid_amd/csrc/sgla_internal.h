@@ -145,9 +145,9 @@ struct StepPrologue {
     float eps;
 };
 hipError_t launch_recurrent_step(const void *q, const void *k, const void *v, const float *g,
-                                 float *state, const int32_t *idx, void *out, int N, int H,
-                                 int Dk, int Dv, float scale, bool bf16, const StepPrologue &pro,
-                                 hipStream_t st);
+                                 void *state, bool state_bf16, const int32_t *idx, void *out,
+                                 int N, int H, int Dk, int Dv, float scale, bool bf16,
+                                 const StepPrologue &pro, hipStream_t st);
 
 // Map a linear workgroup id onto (unit, sub) so that the `nsub` workgroups of
 // one unit land on the same XCD (ids are dealt to the 8 XCDs round-robin) and

@@ -27,8 +27,8 @@ def _no_gpu():
 def test_header_declares_the_entry_points():
     names = sgla.exported_symbols()
     for n in ("sgla_chunk_fwd", "sgla_recurrent_step", "sgla_chunk_fwd_qk_norm_rope",
-              "sgla_recurrent_step_qk_norm_rope", "sgla_out_norm_gate", "sgla_status_string",
-              "sgla_version"):
+              "sgla_recurrent_step_qk_norm_rope", "sgla_recurrent_step_ex", "sgla_out_norm_gate",
+              "sgla_status_string", "sgla_version"):
         assert n in names
 
 
@@ -153,6 +153,29 @@ def test_qk_norm_rope_validation(lib):
 def test_qk_norm_rope_pointer_checks(lib):
     assert step_pro(lib, N=1, pos=None) == 1   # positions are required for a step
     assert chunk_pro(lib, B=1, T=1, q=None) == 1
+
+
+def step_ex(lib, state_dtype=1, qw=None, kw=None, pos=None, theta=1e4, eps=1e-6, N=0, H=1,
+            Dk=128, Dv=128, dtype=1, state=A):
+    return lib.sgla_recurrent_step_ex(A, A, A, A, state, state_dtype, None, A, qw, kw, pos, theta,
+                                      eps, N, H, Dk, Dv, 1.0, dtype, None)
+
+
+def test_recurrent_step_ex_validation(lib):
+    assert step_ex(lib) == 0
+    assert step_ex(lib, state_dtype=0) == 0
+    assert step_ex(lib, state_dtype=2) == 1
+    assert step_ex(lib, state_dtype=-1) == 1
+    assert step_ex(lib, Dk=64, Dv=64, dtype=0) == 0          # no prologue: any supported size
+    assert step_ex(lib, qw=A, kw=A, pos=A, Dk=64) == 2        # the prologue needs Dk = 128
+    assert step_ex(lib, qw=A, kw=None, pos=A) == 1
+    assert step_ex(lib, qw=A, kw=A, pos=A, theta=0.0) == 1
+
+
+@pytest.mark.skipif("not _no_gpu()", reason="could reach a launch if validation were wrong")
+def test_recurrent_step_ex_pointer_checks(lib):
+    assert step_ex(lib, N=1, state=A + 8) == 1                 # bf16 pool still needs 16 bytes
+    assert step_ex(lib, N=1, qw=A, kw=A, pos=None) == 1
 
 
 def epi(lib, o=A, z=A, w=A, out=A, rows=0, width=4096, eps=1e-6, dtype=1):
