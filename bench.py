@@ -40,6 +40,22 @@ BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
+PREFILL_PRO = PREFILL + "+qk_norm_rope"
+DECODE_PRO = DECODE + "+qk_norm_rope"
+DECODE_BF16 = DECODE + "+bf16_state"
+EPILOGUE = "out_norm_gate_bf16_8192x4096"
+# The kernels of one call of each workload, as rocprofv3 names them.
+CALL_KERNELS = {
+    PREFILL: ["chunk_mfma_kernel<true, false>", "scan_kernel<128, 128>",
+              "chunk_mfma_kernel<false, false>"],
+    PREFILL_PRO: ["chunk_mfma_kernel<true, true>", "scan_kernel<128, 128>",
+                  "chunk_mfma_kernel<false, true>"],
+    DECODE: ["recurrent_step_kernel<unsigned short, 128, 128, false, float>"],
+    DECODE_PRO: ["recurrent_step_kernel<unsigned short, 128, 128, true, float>"],
+    DECODE_BF16: ["recurrent_step_kernel<unsigned short, 128, 128, false, unsigned short>"],
+    EPILOGUE: ["out_norm_gate_kernel<unsigned short, 2>"],
+}
+
 
 def kernel_source_hash():
     """sha256 over the library's kernel sources, to tell whether a stored
@@ -107,10 +123,9 @@ def record_traffic(fetch_dir, write_dir, calib_bytes=256 << 20):
 
     Both counters are in KiB per dispatch. Each is scaled by what it reads
     for the fp32 negation pass of known size (calib_bytes read and written),
-    and the per-kernel averages are summed over the kernels of one call:
-    plan/state/scan/output for the chunked forward, the step kernel for
-    decode. Writes profiles/traffic.json keyed by workload, with the hash of
-    the kernel sources the counters were taken on."""
+    averaged per kernel, and summed over the kernels of one call of each
+    workload (CALL_KERNELS). Writes profiles/traffic.json keyed by workload,
+    with the hash of the kernel sources the counters were taken on."""
     fetch_rows = _counter_rows(fetch_dir, "FETCH_SIZE")
     write_rows = _counter_rows(write_dir, "WRITE_SIZE")
 
@@ -128,22 +143,24 @@ def record_traffic(fetch_dir, write_dir, calib_bytes=256 << 20):
     fetch = _per_kernel_avg(fetch_rows)
     write = _per_kernel_avg(write_rows)
 
-    def kbytes(pred):
-        names = [n for n in fetch if pred(n)]
-        per = {n: (fetch[n] * 1024.0 * f_scale, write.get(n, 0.0) * 1024.0 * w_scale) for n in names}
-        return per, sum(a + b for a, b in per.values())
+    def find(pattern, table):
+        names = [n for n in table if pattern in n]
+        return names[0] if len(names) == 1 else None
 
-    pre, pre_total = kbytes(lambda n: "sgla" in n and "recurrent" not in n)
-    dec, dec_total = kbytes(lambda n: "sgla" in n and "recurrent" in n)
     src = kernel_source_hash()
     rec = {"_calibration": {"fetch_scale": f_scale, "write_scale": w_scale,
                             "pass": "fp32 negation, %d bytes read and written" % calib_bytes}}
-    if pre:
-        rec[PREFILL] = {"source_hash": src, "bytes_per_call": pre_total,
-                        "kernels": {n: {"fetch": a, "write": b} for n, (a, b) in pre.items()}}
-    if dec:
-        rec[DECODE] = {"source_hash": src, "bytes_per_call": dec_total,
-                       "kernels": {n: {"fetch": a, "write": b} for n, (a, b) in dec.items()}}
+    for wl, parts in CALL_KERNELS.items():
+        kern = {}
+        for pat in parts:
+            nf, nw = find(pat, fetch), find(pat, write)
+            if nf is None or nw is None:
+                kern = None
+                break
+            kern[nf] = {"fetch": fetch[nf] * 1024.0 * f_scale, "write": write[nw] * 1024.0 * w_scale}
+        if kern:
+            rec[wl] = {"source_hash": src, "kernels": kern,
+                       "bytes_per_call": sum(v["fetch"] + v["write"] for v in kern.values())}
     os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
     with open(TRAFFIC_RECORD, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
@@ -216,25 +233,32 @@ def median(xs):
     return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
 
 
-def cpu_baseline(inp, W):
+def cpu_baseline(inp, W, min_seconds=10.0, max_reps=500):
+    """The oracle on the whole prefill workload, repeated until at least
+    ``min_seconds`` of host time have passed (one pass takes a fraction of a
+    second on many cores); reports the mean rate."""
     import numpy as np
     import oracle
     q, k, v, g = (W.to_numpy_f32(inp[x]) for x in ("q", "k", "v", "g"))
     threads = oracle.default_threads()
     oracle.build(force=False)
-    t0 = time.perf_counter()
-    oracle.forward(q, k, v, g, inp["scale"], nthreads=threads)
-    dt = time.perf_counter() - t0
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(q, k, v, g, inp["scale"], nthreads=threads)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
     B, T, H, _ = q.shape
     try:
         model = next(l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo")
                      if l.startswith("model name"))
     except Exception:  # pragma: no cover
         model = "unknown"
-    return {"value": B * T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": B * T * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "the whole prefill workload (B=1, T=8192, all 32 heads, 262,144 "
-                      "head-tokens), fp64 C oracle, OpenMP over (sequence, head) units; %.2f s; "
-                      "host CPU %s" % (dt, model)}
+                      "head-tokens), %d passes in %.1f s (%.3f s each), fp64 C oracle, OpenMP over "
+                      "(sequence, head) units; host CPU %s" % (reps, dt, dt / reps, model)}
 
 
 def main():
@@ -413,7 +437,8 @@ def bench_bf16_state(args, torch, sgla, W, dev):
     return {"workload": DECODE + " with a bf16 state pool", "steps_timed": n_timed,
             "ms_per_step": region / n_timed, "tokens_per_s": N / (region / n_timed * 1e-3),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "kernel": "sgla_recurrent_step_ex (bf16 state)",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(DECODE_BF16),
+                         "kernel": "sgla_recurrent_step_ex (bf16 state)",
                          "algorithmic_bytes_per_launch": nb, "avg_launch_ms": per_avg}}
 
 
@@ -436,7 +461,8 @@ def bench_epilogue(args, torch, sgla, W, dev):
             "ms_per_call": region / args.steps, "tokens_per_s": rows / (region / args.steps * 1e-3),
             "per_call_ms": {"mean": per_avg, "median": median(per), "min": min(per)},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "kernel": "sgla_out_norm_gate",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(EPILOGUE),
+                         "kernel": "sgla_out_norm_gate",
                          "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": per_avg}}
 
 
@@ -463,6 +489,7 @@ def bench_prologue(args, torch, sgla, W, dev):
                       "per_call_ms": {"mean": per_avg, "median": median(per), "min": min(per)},
                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                   "traffic": recorded_traffic(PREFILL_PRO),
                                    "kernel": "sgla_chunk_fwd_qk_norm_rope (whole call)",
                                    "algorithmic_bytes_per_launch": nbytes,
                                    "avg_launch_ms": per_avg}}
@@ -487,6 +514,7 @@ def bench_prologue(args, torch, sgla, W, dev):
                      "tokens_per_s": 256 / (region / n_timed * 1e-3),
                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                  "traffic": recorded_traffic(DECODE_PRO),
                                   "kernel": "sgla_recurrent_step_qk_norm_rope",
                                   "algorithmic_bytes_per_launch": nb, "avg_launch_ms": per_avg}}
     del d, dout
