@@ -260,6 +260,65 @@ sgla_status sgla_out_norm_gate(const void *o, const void *z, const float *weight
                                int64_t rows, int width, float eps, sgla_dtype dtype,
                                void *stream);
 
+/*
+ * The gated delta rule (GDN), the delta-rule family of linear attention that
+ * page "Formulas and code for adapting inference to GDN/KDA linear modules"
+ * adapts to chunked inference. Per sequence and head, with a Dk x Dv state S
+ * (zeros, or the initial state) and for every token t in order (section 1.1,
+ * the recursive formulas), alpha_t = exp(g[t]) and beta_t = beta[t]:
+ *
+ *     S   <- alpha_t S
+ *     u   =  k_t^T S                       what the state returns for k_t
+ *     S   <- S + beta_t k_t (v_t - u)^T    delta-rule write
+ *     o_t =  scale q_t^T S
+ *
+ * The decay comes before the memory read, as in the page's chunkwise form
+ * (section 1.2: W = T (K_beta * exp(G)) measures the correction against the
+ * decayed state); the page's token-by-token pseudocode reads before the decay,
+ * which the chunkwise form does not reproduce. beta is given per token and
+ * head in fp32 (the page computes it as a sigmoid; any real value is
+ * accepted). q and k are used as given: the page normalises keys before the
+ * layer, and the caller does the same.
+ */
+
+/*
+ * sgla_gdn_chunk_fwd — chunked GDN prefill over whole sequences (page
+ * "Formulas and code for adapting inference to GDN/KDA linear modules",
+ * section 1.2: UT transform T = (I + strictly_lower(diag(beta) K K^T *
+ * Gamma))^-1, W = T (K_beta * exp(G)), U = T V_beta, new_v = U - W S per
+ * chunk of 64 tokens; section 2.1 for the call: initial state per sequence,
+ * final state, packed sequences by cumulative offsets).
+ *
+ * Arguments: as sgla_chunk_fwd, plus
+ *   beta   [B, T, H] fp32 (packed [T, H] with cu_seqlens), 4-byte aligned.
+ * Only dtype SGLA_BF16 with Dk = Dv = 128 is supported (SGLA_ERR_UNSUPPORTED
+ * otherwise).
+ *
+ * Memory: the call takes a device workspace from HIP's stream-ordered
+ * allocator on `stream` of (T / 64 + B + 1) * H * 48 KiB (per chunk and head
+ * W in bf16 and U in fp32; B * ceil(T / 64) * H * 48 KiB without cu_seqlens)
+ * plus a small table, and frees it on the same stream. Returns as
+ * sgla_chunk_fwd.
+ */
+sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *initial_state, void *out,
+                               float *final_state, const int64_t *cu_seqlens, int B, int T, int H,
+                               int Dk, int Dv, float scale, sgla_dtype dtype, void *stream);
+
+/*
+ * sgla_gdn_recurrent_step — one GDN decode token per row, state updated in
+ * place through the row -> slot map (one iteration of the recurrence above).
+ *
+ * Arguments: as sgla_recurrent_step, plus
+ *   beta   [N, H] fp32, 4-byte aligned.
+ * dtype SGLA_F32 or SGLA_BF16; Dk, Dv in {64, 128}. The state pool is fp32.
+ * Returns as sgla_recurrent_step. Allocates nothing.
+ */
+sgla_status sgla_gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, float *state,
+                                    const int32_t *state_indices, void *out, int N, int H, int Dk,
+                                    int Dv, float scale, sgla_dtype dtype, void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *sgla_status_string(sgla_status s);
 

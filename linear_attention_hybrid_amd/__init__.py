@@ -21,6 +21,11 @@ gate):
 
 ``recurrent_step_ex`` takes every decode option at once (a bf16 state pool,
 the prologue).
+
+The gated delta rule (GDN), with a per-token write strength beta:
+
+    o, S = gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None)
+    o    = gdn_recurrent_step(q, k, v, g, beta, state, state_indices=None)
 """
 from __future__ import annotations
 
@@ -32,8 +37,8 @@ import re
 import torch
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_qk_norm_rope", "recurrent_step_qk_norm_rope",
-           "recurrent_step_ex", "out_norm_gate", "status_string", "library", "library_path", "exported_symbols",
-           "SglaError"]
+           "recurrent_step_ex", "out_norm_gate", "gdn_chunk_fwd", "gdn_recurrent_step",
+           "status_string", "library", "library_path", "exported_symbols", "SglaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libsgla.so")
@@ -79,6 +84,12 @@ def library():
         lib.sgla_recurrent_step_ex.restype = ci
         lib.sgla_out_norm_gate.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ci, cf, ci, vp]
         lib.sgla_out_norm_gate.restype = ci
+        lib.sgla_gdn_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
+                                           cf, ci, vp]
+        lib.sgla_gdn_chunk_fwd.restype = ci
+        lib.sgla_gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf,
+                                                ci, vp]
+        lib.sgla_gdn_recurrent_step.restype = ci
         lib.sgla_status_string.argtypes = [ci]
         lib.sgla_status_string.restype = ctypes.c_char_p
         lib.sgla_version.argtypes = []
@@ -338,4 +349,40 @@ def recurrent_step_ex(q, k, v, g, state, state_indices=None, q_weight=None, k_we
             float(theta), float(eps), *a["sizes"], a["scale"], _DTYPE[q.dtype], _stream(device))
     if st != SGLA_OK:
         raise SglaError("sgla_recurrent_step_ex", st)
+    return a["out"]
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None, out=None,
+                  final_state=None, output_final_state=True):
+    """Chunked prefill of the gated delta rule: arguments and results as
+    ``chunk_fwd``, plus ``beta`` [B, T, H] fp32, the write strength of each
+    token and head. bf16 with Dk = Dv = 128 only."""
+    a = _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
+                    output_final_state)
+    device = a["device"]
+    _check(beta, "beta", torch.float32, tuple(g.shape), device)
+    with torch.cuda.device(device):
+        st = library().sgla_gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                          _ptr(initial_state), _ptr(a["out"]),
+                                          _ptr(a["final_state"]), _ptr(cu_seqlens), *a["sizes"],
+                                          a["scale"], _DTYPE[q.dtype], _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_gdn_chunk_fwd", st)
+    return a["out"], a["final_state"]
+
+
+def gdn_recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=None, out=None):
+    """One decode step of the gated delta rule, updating the fp32 ``state``
+    pool in place: arguments as ``recurrent_step``, plus ``beta`` [N, H]
+    fp32. Returns o [N, H, Dv] in v's dtype."""
+    a = _step_args(q, k, v, g, state, state_indices, scale, out)
+    device = a["device"]
+    _check(beta, "beta", torch.float32, tuple(g.shape), device)
+    with torch.cuda.device(device):
+        st = library().sgla_gdn_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                               _ptr(state), _ptr(state_indices), _ptr(a["out"]),
+                                               *a["sizes"], a["scale"], _DTYPE[q.dtype],
+                                               _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_gdn_recurrent_step", st)
     return a["out"]

@@ -30,18 +30,11 @@
 // row, K*exp(G_last-G) and V transposed (token-contiguous) with a swizzle that
 // keeps both the transposing writes and the MFMA operand reads spread over the
 // banks. LDS: 72 KiB for the output phase, so two workgroups fit on a CU.
-#include "sgla_internal.h"
+#include "mfma_tile.h"
 
 namespace sgla {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
 constexpr int NT = 256;
@@ -64,58 +57,6 @@ constexpr int PRO_OREV = 1536;
 constexpr int PRO_ROT = 1792;
 constexpr int PRO_BASE = 2304;
 constexpr int PRO_BYTES = 3328;
-
-// Byte offset of 16-byte chunk c of row r in a 256-byte-row tile (Q, K, O).
-__device__ __forceinline__ int row_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
-// Byte offset of 16-byte chunk c (8 tokens) of row d in a 128-byte-row tile (KT, VT, A).
-__device__ __forceinline__ int tr_off(int d, int c) {
-    return d * 128 + ((c ^ (((d >> 1) ^ (d >> 3)) & 7)) << 4);
-}
-
-__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-    return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-    return (a >> 16) | (b & 0xffff0000u);
-}
-__device__ __forceinline__ uint32_t pack_f32(float a, float b) {
-    bf16x2 v = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-template <typename T>
-__device__ __forceinline__ T lds_ld(const char *lds, int off) {
-    return *reinterpret_cast<const T *>(lds + off);
-}
-template <typename T>
-__device__ __forceinline__ void lds_st(char *lds, int off, T v) {
-    *reinterpret_cast<T *>(lds + off) = v;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts inside
-// each 16-lane row, then the row totals carried by row broadcasts (lanes with
-// no source lane add zero).
-__device__ __forceinline__ float wave_prefix_sum(float x) {
-    int v = __builtin_bit_cast(int, x);
-#define SGLA_DPP_ADD(ctrl, rmask)                                                          \
-    v = __builtin_bit_cast(int, __builtin_bit_cast(float, v) +                              \
-                                    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp( \
-                                        0, v, ctrl, rmask, 0xf, false)))
-    SGLA_DPP_ADD(0x111, 0xf);  // row_shr:1
-    SGLA_DPP_ADD(0x112, 0xf);  // row_shr:2
-    SGLA_DPP_ADD(0x114, 0xf);  // row_shr:4
-    SGLA_DPP_ADD(0x118, 0xf);  // row_shr:8
-    SGLA_DPP_ADD(0x142, 0xa);  // row_bcast:15 into rows 1 and 3
-    SGLA_DPP_ADD(0x143, 0xc);  // row_bcast:31 into rows 2 and 3
-#undef SGLA_DPP_ADD
-    return __builtin_bit_cast(float, v);
-}
 
 // The prologue of one 16-byte piece (8 consecutive dims 8c .. 8c+7 of a
 // 128-dim row, c = lane & 15) held by each of the 16 lanes of a DPP row:

@@ -281,4 +281,88 @@ sgla_status sgla_out_norm_gate(const void *o, const void *z, const float *weight
                                            dtype == SGLA_BF16, static_cast<hipStream_t>(stream)));
 }
 
+sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *initial_state, void *out,
+                               float *final_state, const int64_t *cu_seqlens, int B, int T, int H,
+                               int Dk, int Dv, float scale, sgla_dtype dtype, void *stream) {
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
+    // The delta rule runs on the bf16 matrix-core kernels with 128-wide heads.
+    if (dtype != SGLA_BF16 || Dk != 128 || Dv != 128) return SGLA_ERR_UNSUPPORTED;
+    if (H > kMaxHeads) return SGLA_ERR_UNSUPPORTED;
+    const int64_t ttot = cu_seqlens ? (int64_t)T : (int64_t)B * T;
+    if (ttot > ((int64_t)1 << 62) / ((int64_t)H * 128)) return SGLA_ERR_INVALID_ARG;
+    if ((int64_t)B * H > (int64_t)1 << 30) return SGLA_ERR_INVALID_ARG;
+    if (ttot > 0 && (!q || !k || !v || !g || !beta || !out)) return SGLA_ERR_INVALID_ARG;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) ||
+        misaligned(beta, 4) || misaligned(out) || misaligned(initial_state) ||
+        misaligned(final_state) || misaligned(cu_seqlens, 8))
+        return SGLA_ERR_INVALID_ARG;
+    if (B == 0) return SGLA_OK;
+    if (ttot == 0 && !final_state) return SGLA_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    // One table row per chunk: without cu_seqlens the rows are arithmetic,
+    // with it the plan kernel lays them out on the device.
+    const bool table = cu_seqlens != nullptr;
+    const int64_t nps64 = T == 0 ? 1 : ((int64_t)T + kChunk - 1) / kChunk;
+    const int64_t nch64 = table ? ttot / kChunk + B + 1 : (int64_t)B * nps64;
+    if (nch64 * H > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+    const int nch = (int)nch64;
+
+    const size_t segs_b = table ? (size_t)nch * sizeof(SegEntry) : 0;
+    const size_t seqs_b = table ? ((size_t)B * sizeof(SeqEntry) + 255) / 256 * 256 : 0;
+    const size_t tile_b = (size_t)nch * H * kChunk * 128 * sizeof(uint16_t);  // W, bf16
+    const size_t ws_b = segs_b + seqs_b + 3 * tile_b;                           // + U, fp32
+    char *ws = nullptr;
+    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&ws), ws_b, st);
+    if (e != hipSuccess) return SGLA_ERR_HIP;
+
+    GdnParams p{};
+    p.c.q = q;
+    p.c.k = k;
+    p.c.v = v;
+    p.c.g = g;
+    p.c.s0 = initial_state;
+    p.c.out = out;
+    p.c.sfin = final_state;
+    p.c.segs = table ? reinterpret_cast<SegEntry *>(ws) : nullptr;
+    p.c.seqs = table ? reinterpret_cast<SeqEntry *>(ws + segs_b) : nullptr;
+    p.c.H = H;
+    p.c.nseg_max = nch;
+    p.c.N = B;
+    p.c.scale = scale;
+    p.c.T = T;
+    p.c.seg_len = kChunk;
+    p.c.nps = (int)nps64;
+    p.beta = beta;
+    p.w = reinterpret_cast<uint16_t *>(ws + segs_b + seqs_b);
+    p.u = reinterpret_cast<float *>(ws + segs_b + seqs_b + tile_b);
+    if (table)
+        e = launch_plan(cu_seqlens, B, T, kChunk, nch, reinterpret_cast<SegEntry *>(ws),
+                        reinterpret_cast<SeqEntry *>(ws + segs_b), st);
+    if (e == hipSuccess) e = launch_gdn_chunk(p, st);
+    const hipError_t ef = hipFreeAsync(ws, st);
+    if (e == hipSuccess) e = ef;
+    return hip_status(e);
+}
+
+sgla_status sgla_gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, float *state,
+                                    const int32_t *state_indices, void *out, int N, int H, int Dk,
+                                    int Dv, float scale, sgla_dtype dtype, void *stream) {
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (N < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
+    if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > ((int64_t)1 << 31) - 1) return SGLA_ERR_INVALID_ARG;
+    if (N == 0) return SGLA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !out) return SGLA_ERR_INVALID_ARG;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) ||
+        misaligned(beta, 4) || misaligned(state) || misaligned(out) ||
+        misaligned(state_indices, 4))
+        return SGLA_ERR_INVALID_ARG;
+    return hip_status(launch_gdn_step(q, k, v, g, beta, state, state_indices, out, N, H, Dk, Dv,
+                                      scale, dtype == SGLA_BF16, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -127,6 +127,15 @@ __device__ __forceinline__ float row16_swap8(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xf, 0xf, true));
 }
 
+// Arguments of the chunked gated-delta-rule kernels. The chunk table is the
+// segment table with one chunk per segment (seg_len = kChunk).
+struct GdnParams {
+    ChunkParams c;      // q, k, v, g, s0, out, sfin, segs, seqs, H, nseg_max, N, scale, T, nps
+    const float *beta;  // [tokens, H] write strength of each token
+    uint16_t *w;        // [nseg_max, H, 64, 128] W rows of each chunk (bf16)
+    float *u;           // [nseg_max, H, 128, 64] U of each chunk, value-major (fp32)
+};
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_plan(const int64_t *cu, int B, int T, int seg_len, int nseg_max,
                        SegEntry *segs, SeqEntry *seqs, hipStream_t st);
@@ -148,6 +157,11 @@ hipError_t launch_recurrent_step(const void *q, const void *k, const void *v, co
                                  void *state, bool state_bf16, const int32_t *idx, void *out,
                                  int N, int H, int Dk, int Dv, float scale, bool bf16,
                                  const StepPrologue &pro, hipStream_t st);
+
+hipError_t launch_gdn_chunk(const GdnParams &p, hipStream_t st);
+hipError_t launch_gdn_step(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, const int32_t *idx, void *out, int N,
+                           int H, int Dk, int Dv, float scale, bool bf16, hipStream_t st);
 
 // Map a linear workgroup id onto (unit, sub) so that the `nsub` workgroups of
 // one unit land on the same XCD (ids are dealt to the 8 XCDs round-robin) and

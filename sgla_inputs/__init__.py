@@ -20,7 +20,14 @@ the per-head RMSNorm and RoPE, cast to bf16):
   exp(N(0, 0.5^2)); v and the gates as in ``"lightning"``. ``norm_weights``
   draws the two RMSNorm weight vectors, 1 + N(0, 0.1^2) per element.
 
-In both, the per-token per-head log-decay is g = log(sigmoid(x)) in fp32, so
+* ``"gdn"``       : inputs of the gated delta rule (page "Formulas and code
+  for adapting inference to GDN/KDA linear modules", section 1.1: q and k
+  are L2-normalised per head with eps 1e-6 inside the square root, beta is a
+  sigmoid): q, k rows ~ N(0, 1) scaled to unit L2 norm; v ~ N(0, 1); gate
+  input x ~ N(4, 1); with ``with_beta`` a write strength beta = sigmoid(b),
+  b ~ N(0, 1), per token and head (fp32), drawn after everything else.
+
+In all of them, the per-token per-head log-decay is g = log(sigmoid(x)) in fp32, so
 every decay factor exp(g) lies in (0, 1). Initial states, when present, are
 fp32 ~ N(0, 0.02^2). bf16 tensors come from a round-to-nearest-even cast of the
 fp32 draws. Draw order from one ``torch.Generator`` seeded with ``seed``: q, k,
@@ -108,6 +115,8 @@ def _draw_qk(shape_tokens, H, D, preset, gen, device, out_dtype):
         x = torch.randn((e - s, H, D), generator=gen, device=device, dtype=torch.float32)
         if preset == "lightning":
             x = _unit_rms(x)
+        elif preset == "gdn":
+            x = x * torch.rsqrt(x.pow(2).sum(dim=-1, keepdim=True) + RMS_EPS)
         elif preset == "raw":
             f = torch.randn((e - s, H, 1), generator=gen, device=device, dtype=torch.float32)
             x = x * torch.exp(0.5 * f)
@@ -136,17 +145,18 @@ def _draw_plain(shape_tokens, inner, gen, device, out_dtype, mean=0.0, std=1.0):
 
 
 def gate_mean(preset: str) -> float:
-    return {"gaussian": 3.0, "lightning": 4.0, "raw": 4.0}[preset]
+    return {"gaussian": 3.0, "lightning": 4.0, "raw": 4.0, "gdn": 4.0}[preset]
 
 
 def make_prefill(B, T, H, Dk, Dv, dtype="bf16", preset="lightning", seed=0, device="cpu",
-                 cu_seqlens=None, init=None):
+                 cu_seqlens=None, init=None, with_beta=False):
     """Inputs for one chunked-forward call.
 
     Returns a dict with q, k [B, T, H, Dk]; v [B, T, H, Dv] (dtype); g [B, T, H]
     fp32; initial_state [N, H, Dk, Dv] fp32 or None; cu_seqlens int64 tensor or
     None; scale = 1/sqrt(Dk). With ``cu_seqlens`` B must be 1 and T the total.
-    ``init`` is None (zero state) or "normal" (N(0, 0.02^2)).
+    ``init`` is None (zero state) or "normal" (N(0, 0.02^2)). With
+    ``with_beta`` also beta [B, T, H] fp32 in (0, 1).
     """
     device = torch.device(device)
     tdt = TORCH_DTYPE[dtype]
@@ -171,21 +181,25 @@ def make_prefill(B, T, H, Dk, Dv, dtype="bf16", preset="lightning", seed=0, devi
               * 0.02)
     elif init is not None:
         raise ValueError(init)
+    beta = None
+    if with_beta:
+        beta = torch.sigmoid(_draw_plain(BT, (H,), gen, device, torch.float32)).view(B, T, H)
     return dict(
         q=q.view(B, T, H, Dk), k=k.view(B, T, H, Dk), v=v.view(B, T, H, Dv), g=g.view(B, T, H),
-        initial_state=S0,
+        initial_state=S0, beta=beta,
         cu_seqlens=None if cu_np is None else torch.from_numpy(cu_np).to(device),
         scale=1.0 / math.sqrt(Dk), dtype=dtype, preset=preset, seed=seed,
     )
 
 
 def make_decode(N, H, Dk, Dv, steps, dtype="bf16", preset="lightning", seed=0, device="cpu",
-                pos0=100000, slots=None, with_state=True):
+                pos0=100000, slots=None, with_state=True, with_beta=False):
     """Inputs for ``steps`` successive decode steps of N sequences.
 
     Returns q, k [steps, N, H, Dk]; v [steps, N, H, Dv]; g [steps, N, H] fp32;
     state [slots or N, H, Dk, Dv] fp32 ~ N(0, 0.02^2); scale; pos [steps, N]
-    int32, step i of every sequence at position pos0 + i.
+    int32, step i of every sequence at position pos0 + i. With ``with_beta``
+    also beta [steps, N, H] fp32 (drawn after each step's gate).
     """
     device = torch.device(device)
     tdt = TORCH_DTYPE[dtype]
@@ -195,16 +209,18 @@ def make_decode(N, H, Dk, Dv, steps, dtype="bf16", preset="lightning", seed=0, d
     if with_state:
         state = torch.randn((nslots, H, Dk, Dv), generator=gen, device=device,
                             dtype=torch.float32) * 0.02
-    qs, ks, vs, gs = [], [], [], []
+    qs, ks, vs, gs, bs = [], [], [], [], []
     for i in range(steps):
         qs.append(_draw_qk(N, H, Dk, preset, gen, device, tdt))
         ks.append(_draw_qk(N, H, Dk, preset, gen, device, tdt))
         vs.append(_draw_plain(N, (H, Dv), gen, device, tdt))
         x = _draw_plain(N, (H,), gen, device, torch.float32, mean=gate_mean(preset))
         gs.append(F.logsigmoid(x))
+        if with_beta:
+            bs.append(torch.sigmoid(_draw_plain(N, (H,), gen, device, torch.float32)))
     pos = (torch.arange(steps, dtype=torch.int32, device=device)[:, None] + pos0).expand(steps, N)
     return dict(q=torch.stack(qs), k=torch.stack(ks), v=torch.stack(vs), g=torch.stack(gs),
-                state=state, scale=1.0 / math.sqrt(Dk), dtype=dtype, preset=preset, seed=seed,
+                beta=torch.stack(bs) if with_beta else None, state=state, scale=1.0 / math.sqrt(Dk), dtype=dtype, preset=preset, seed=seed,
                 pos=pos.contiguous())
 
 

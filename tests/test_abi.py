@@ -28,7 +28,8 @@ def test_header_declares_the_entry_points():
     names = sgla.exported_symbols()
     for n in ("sgla_chunk_fwd", "sgla_recurrent_step", "sgla_chunk_fwd_qk_norm_rope",
               "sgla_recurrent_step_qk_norm_rope", "sgla_recurrent_step_ex", "sgla_out_norm_gate",
-              "sgla_status_string", "sgla_version"):
+              "sgla_gdn_chunk_fwd", "sgla_gdn_recurrent_step", "sgla_status_string",
+              "sgla_version"):
         assert n in names
 
 
@@ -208,3 +209,41 @@ def test_binding_refuses_cpu_tensors():
         sgla.chunk_fwd(x, x, x, torch.zeros(1, 4, 1))
     with pytest.raises(ValueError):
         sgla.recurrent_step(x[0], x[0], x[0], torch.zeros(4, 1), torch.zeros(4, 1, 64, 64))
+
+
+def gdn_chunk(lib, q=A, k=A, v=A, g=A, beta=A, s0=None, out=A, sf=None, cu=None, B=0, T=0, H=1,
+              Dk=128, Dv=128, dtype=1):
+    return lib.sgla_gdn_chunk_fwd(q, k, v, g, beta, s0, out, sf, cu, B, T, H, Dk, Dv, 1.0, dtype,
+                                  None)
+
+
+def gdn_step(lib, q=A, k=A, v=A, g=A, beta=A, state=A, idx=None, out=A, N=0, H=1, Dk=128,
+             Dv=128, dtype=1):
+    return lib.sgla_gdn_recurrent_step(q, k, v, g, beta, state, idx, out, N, H, Dk, Dv, 1.0,
+                                       dtype, None)
+
+
+def test_gdn_validation(lib):
+    assert gdn_chunk(lib) == 0
+    assert gdn_chunk(lib, dtype=0) == 2        # the chunked delta rule is built for bf16
+    assert gdn_chunk(lib, Dk=64, Dv=64) == 2
+    assert gdn_chunk(lib, dtype=4) == 1
+    assert gdn_chunk(lib, B=-1) == 1
+    assert gdn_chunk(lib, beta=A + 2) == 1
+    assert gdn_chunk(lib, beta=A + 4) == 0     # fp32 alignment is enough
+    assert gdn_chunk(lib, cu=A + 4) == 1
+    assert gdn_chunk(lib, B=1, T=1, H=2**16 + 1) == 2
+    assert gdn_step(lib) == 0
+    assert gdn_step(lib, Dk=64, Dv=64, dtype=0) == 0
+    assert gdn_step(lib, Dk=96) == 2
+    assert gdn_step(lib, N=-1) == 1
+    assert gdn_step(lib, dtype=2) == 1
+
+
+@pytest.mark.skipif("not _no_gpu()", reason="could reach a launch if validation were wrong")
+def test_gdn_pointer_checks(lib):
+    assert gdn_chunk(lib, B=1, T=1, beta=None) == 1
+    assert gdn_chunk(lib, B=1, T=1, q=None) == 1
+    assert gdn_step(lib, N=1, beta=None) == 1
+    assert gdn_step(lib, N=1, beta=A + 2) == 1
+    assert gdn_step(lib, N=1, state=A + 4) == 1

@@ -1,0 +1,176 @@
+"""GPU parity of the gated delta rule (sgla_gdn_recurrent_step, sgla_gdn_chunk_fwd)
+against the fp64 token-by-token oracle (oracle/gdn_oracle.c).
+
+Inputs follow the "gdn" recipe of sgla_inputs: L2-normalised q and k rows,
+v ~ N(0, 1), g = log(sigmoid(N(4, 1))) (long memory, so errors carried in
+the state are not hidden by fast forgetting), beta = sigmoid(N(0, 1)). The
+bars are those of the Simple GLA path: fp32 max |err| <= 1e-4 RMS; bf16
+rel-L2 <= 5e-3 and max |err| <= 2e-2 RMS (plus the final bf16 rounding of
+outputs), separately for outputs and final states.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_hybrid_amd as sgla
+import oracle.gdn as GDN
+import sgla_inputs as W
+from tests.parity import check as _check, check_windows, host, nan_like, say
+
+pytestmark = pytest.mark.gpu
+
+
+def check(got, ref, dtype, what, **kw):
+    """parity.check, printing the measured errors."""
+    m = _check(got, ref, dtype, what, **kw)
+    say("  %-28s rel-L2 %.2e  max/RMS %.2e" % (what, m["rel_l2"],
+                                               m["max_abs"] / max(m["rms_ref"], 1e-30)))
+    return m
+
+
+def oracle_gdn(inp, heads=None):
+    sel = (lambda t: t) if heads is None else (lambda t: t[:, :, heads])
+    S0 = inp["initial_state"]
+    if S0 is not None:
+        S0 = host(S0 if heads is None else S0[:, heads]).astype(np.float64)
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].cpu().numpy()
+    return GDN.forward(host(sel(inp["q"])), host(sel(inp["k"])), host(sel(inp["v"])),
+                       host(sel(inp["g"])), host(sel(inp["beta"])), inp["scale"],
+                       initial_state=S0, cu_seqlens=cu)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_gdn_step_with_slot_map(dtype, dk, dv):
+    say("gdn_recurrent_step", dtype, dk, dv, "N=5 H=3 slots=9, 4 steps")
+    N, H, slots, steps = 5, 3, 9, 4
+    d = W.make_decode(N, H, dk, dv, steps, dtype, "gdn", seed=dk * 5 + dv, device="cuda",
+                      slots=slots, with_beta=True)
+    idx = torch.tensor([7, 0, 3, 8, 2], dtype=torch.int32, device="cuda")
+    state = (d["state"] * 25).contiguous()          # unit-size states: the memory read matters
+    ref_state = host(state).astype(np.float64)
+    untouched = [s for s in range(slots) if s not in idx.tolist()]
+    before_untouched = state[untouched].clone()
+    for i in range(steps):
+        out = nan_like((N, H, dv), d["v"].dtype)
+        o = sgla.gdn_recurrent_step(d["q"][i], d["k"][i], d["v"][i], d["g"][i], d["beta"][i],
+                                    state, state_indices=idx, scale=d["scale"], out=out)
+        torch.cuda.synchronize()
+        ro = GDN.step(host(d["q"][i]), host(d["k"][i]), host(d["v"][i]), host(d["g"][i]),
+                      host(d["beta"][i]), ref_state, d["scale"], state_indices=idx.cpu().numpy())
+        check(host(o), ro, dtype, "gdn step %d o" % i)
+        check(host(state[idx.long()]), ref_state[idx.cpu().numpy()], dtype,
+              "gdn step %d state" % i, bf16_out=False)
+    assert torch.equal(state[untouched], before_untouched)
+
+
+def test_gdn_step_equals_one_token_chunk():
+    say("gdn_recurrent_step == gdn_chunk_fwd(T=1)")
+    N, H, D = 4, 2, 128
+    d = W.make_decode(N, H, D, D, 1, "bf16", "gdn", seed=23, device="cuda", with_beta=True)
+    S0 = (d["state"] * 25).contiguous()
+    state = S0.clone()
+    o_step = sgla.gdn_recurrent_step(d["q"][0], d["k"][0], d["v"][0], d["g"][0], d["beta"][0],
+                                     state)
+    one = lambda t: t[0][:, None].contiguous()
+    o_chunk, S_chunk = sgla.gdn_chunk_fwd(one(d["q"]), one(d["k"]), one(d["v"]), one(d["g"]),
+                                          one(d["beta"]), initial_state=S0)
+    torch.cuda.synchronize()
+    check(host(o_step), host(o_chunk[:, 0]), "bf16", "step vs chunk o")
+    check(host(state), host(S_chunk), "bf16", "step vs chunk state", bf16_out=False)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 200, 333])
+@pytest.mark.parametrize("init", [None, "normal"])
+def test_gdn_chunk_vs_oracle(T, init):
+    say("gdn_chunk_fwd B=2 H=3 T=%d init=%s" % (T, init))
+    inp = W.make_prefill(2, T, 3, 128, 128, "bf16", "gdn", seed=T + (init is not None),
+                         device="cuda", init=init, with_beta=True)
+    if init is not None:
+        inp["initial_state"] = inp["initial_state"] * 25
+    out = nan_like((2, T, 3, 128), torch.bfloat16)
+    o, S = sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                              initial_state=inp["initial_state"], out=out)
+    torch.cuda.synchronize()
+    ro, rS = oracle_gdn(inp)
+    check(host(o), ro, "bf16", "gdn o")
+    check(host(S), rS, "bf16", "gdn final state", bf16_out=False)
+    for b in range(2):
+        check_windows(host(o[b]), ro[b], [0], "bf16", "gdn o seq %d" % b)
+
+
+def test_gdn_chunk_varlen_packed_equals_separate():
+    lengths = [0, 1, 63, 64, 65, 130, 200, 7]
+    say("gdn_chunk_fwd varlen", lengths)
+    cu = W.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    H = 2
+    inp = W.make_prefill(1, T, H, 128, 128, "bf16", "gdn", seed=77, device="cuda",
+                         cu_seqlens=cu, init="normal", with_beta=True)
+    inp["initial_state"] = inp["initial_state"] * 25
+    o, S = sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                              initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    ro, rS = oracle_gdn(inp)
+    check(host(o), ro, "bf16", "gdn varlen o")
+    check(host(S), rS, "bf16", "gdn varlen states", bf16_out=False)
+    check_windows(host(o[0]), ro[0], [int(c) for c in cu[:-1]], "bf16", "gdn varlen o",
+                  ends=[int(c) for c in cu[1:]])
+    # Each sequence on its own: the same chunks, the same arithmetic, bit for bit.
+    for i, L in enumerate(lengths):
+        a, b = int(cu[i]), int(cu[i + 1])
+        part = lambda t: t[:, a:b].contiguous()
+        oi, Si = sgla.gdn_chunk_fwd(part(inp["q"]), part(inp["k"]), part(inp["v"]),
+                                    part(inp["g"]), part(inp["beta"]),
+                                    initial_state=inp["initial_state"][i:i + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(oi[0], o[0, a:b]), i
+        assert torch.equal(Si[0], S[i]), i
+    # An empty sequence keeps its initial state.
+    assert torch.equal(S[0], inp["initial_state"][0])
+
+
+def test_gdn_chunk_split_chain_and_in_place():
+    say("gdn_chunk_fwd split at 128 and chained, final_state in place")
+    T, H = 320, 2
+    inp = W.make_prefill(1, T, H, 128, 128, "bf16", "gdn", seed=91, device="cuda",
+                         init="normal", with_beta=True)
+    S0 = inp["initial_state"] * 25
+    o_all, S_all = sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                      initial_state=S0)
+    S = S0.clone()
+    part = lambda t, a, b: t[:, a:b].contiguous()
+    o1, _ = sgla.gdn_chunk_fwd(*(part(inp[x], 0, 128) for x in ("q", "k", "v", "g", "beta")),
+                               initial_state=S, final_state=S)
+    o2, _ = sgla.gdn_chunk_fwd(*(part(inp[x], 128, T) for x in ("q", "k", "v", "g", "beta")),
+                               initial_state=S, final_state=S)
+    torch.cuda.synchronize()
+    # A split on a chunk boundary sees the same chunks: identical results.
+    assert torch.equal(torch.cat([o1, o2], dim=1), o_all)
+    assert torch.equal(S, S_all)
+
+
+def test_gdn_chunk_no_tokens_copies_state():
+    say("gdn_chunk_fwd T=0 with a final state")
+    H = 3
+    S0 = torch.randn((2, H, 128, 128), device="cuda")
+    z = torch.empty((2, 0, H, 128), dtype=torch.bfloat16, device="cuda")
+    zg = torch.empty((2, 0, H), dtype=torch.float32, device="cuda")
+    o, S = sgla.gdn_chunk_fwd(z, z, z, zg, zg, initial_state=S0)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, H, 128)
+    assert torch.equal(S, S0)
+
+
+def test_gdn_chunk_prefill_workload_sampled():
+    """The lightning-prefill shape (B=1, T=8192, H=32, Dk=Dv=128) with GDN
+    inputs; the oracle runs 4 seeded heads in full."""
+    say("gdn_chunk_fwd B=1 T=8192 H=32 D=128 seed=5 (4 heads checked)")
+    inp = W.make_prefill(1, 8192, 32, 128, 128, "bf16", "gdn", seed=5, device="cuda",
+                         with_beta=True)
+    o, S = sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"])
+    torch.cuda.synchronize()
+    heads = np.sort(np.random.default_rng(5).choice(32, size=4, replace=False))
+    ro, rS = oracle_gdn(inp, heads=heads)
+    check(host(o[:, :, heads]), ro, "bf16", "gdn prefill o")
+    check(host(S[:, heads]), rS, "bf16", "gdn prefill state", bf16_out=False)
