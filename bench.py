@@ -44,6 +44,8 @@ PREFILL_PRO = PREFILL + "+qk_norm_rope"
 DECODE_PRO = DECODE + "+qk_norm_rope"
 DECODE_BF16 = DECODE + "+bf16_state"
 EPILOGUE = "out_norm_gate_bf16_8192x4096"
+GDN_PREFILL = "gdn_prefill_bf16_h32_t8192_d128"
+GDN_DECODE = "gdn_decode_bf16_n256_h32_d128_x64"
 # The kernels of one call of each workload, as rocprofv3 names them.
 CALL_KERNELS = {
     PREFILL: ["chunk_mfma_kernel<true, false>", "scan_kernel<128, 128>",
@@ -54,6 +56,8 @@ CALL_KERNELS = {
     DECODE_PRO: ["recurrent_step_kernel<unsigned short, 128, 128, true, float>"],
     DECODE_BF16: ["recurrent_step_kernel<unsigned short, 128, 128, false, unsigned short>"],
     EPILOGUE: ["out_norm_gate_kernel<unsigned short, 2>"],
+    GDN_PREFILL: ["gdn_prep_kernel", "gdn_chain_kernel", "gdn_output_kernel"],
+    GDN_DECODE: ["gdn_step_kernel<unsigned short, 128, 128>"],
 }
 
 
@@ -270,7 +274,7 @@ def main():
                     help="timed passes of 64 decode steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "epilogue",
-                                       "bf16-state"], default="all")
+                                       "bf16-state", "gdn"], default="all")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB elementwise pass (for counter calibration)")
@@ -406,8 +410,73 @@ def main():
             result.update({"value": e["tokens_per_s"], "unit": "tokens/s",
                            "ms_per_step": e["ms_per_call"],
                            "config": {"workload": e["workload"]}, "roofline": e["roofline"]})
+    if args.only in ("all", "gdn"):
+        result["gdn"] = bench_gdn(args, torch, sgla, W, dev)
+        if args.only == "gdn":
+            e = result["gdn"]["prefill"]
+            result.update({"value": e["tokens_per_s"], "unit": "tokens/s",
+                           "ms_per_step": e["ms_per_call"],
+                           "config": {"workload": e["workload"]}, "roofline": e["roofline"]})
     print(json.dumps(result), flush=True)
     return 0
+
+
+def bench_gdn(args, torch, sgla, W, dev):
+    """The gated delta rule on the same shapes: prefill B=1, T=8192, H=32,
+    Dk=Dv=128 (sgla_gdn_chunk_fwd) and the batched decode, 256 x 32 heads,
+    64 successive steps (sgla_gdn_recurrent_step); "gdn" inputs (L2-normalised
+    q and k, beta = sigmoid(N(0, 1)))."""
+    out = {}
+    inp = W.make_prefill(1, 8192, 32, 128, 128, "bf16", "gdn", seed=args.seed, device=dev,
+                         with_beta=True)
+    o = torch.empty_like(inp["v"])
+    fs = torch.empty((1, 32, 128, 128), dtype=torch.float32, device=dev)
+
+    def step():
+        sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                           scale=inp["scale"], out=o, final_state=fs)
+
+    _, region, per = time_calls(step, args.steps, args.warmup, torch)
+    per_avg = sum(per) / len(per)
+    nbytes = prefill_bytes(1, 8192, 32, 128, 128) + 8192 * 32 * 4
+    gbs = nbytes / (per_avg * 1e-3) / 1e9
+    out["prefill"] = {"workload": GDN_PREFILL, "ms_per_call": region / args.steps,
+                      "tokens_per_s": 8192 / (region / args.steps * 1e-3),
+                      "per_call_ms": {"mean": per_avg, "median": median(per), "min": min(per)},
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                   "traffic": recorded_traffic(GDN_PREFILL),
+                                   "kernel": "sgla_gdn_chunk_fwd (whole call: per-chunk UT "
+                                             "transform, state chain, per-chunk output)",
+                                   "algorithmic_bytes_per_launch": nbytes,
+                                   "avg_launch_ms": per_avg}}
+    del inp, o, fs
+    torch.cuda.empty_cache()
+    d = W.make_decode(256, 32, 128, 128, 64, "bf16", "gdn", seed=4, device=dev, with_beta=True)
+    dout = torch.empty((256, 32, 128), dtype=torch.bfloat16, device=dev)
+    counter = [0]
+
+    def dstep():
+        i = counter[0] % 64
+        counter[0] += 1
+        sgla.gdn_recurrent_step(d["q"][i], d["k"][i], d["v"][i], d["g"][i], d["beta"][i],
+                                d["state"], scale=d["scale"], out=dout)
+
+    n_timed = 64 * args.decode_passes
+    _, region, per = time_calls(dstep, n_timed, 64, torch)
+    per_avg = sum(per) / len(per)
+    nb = decode_bytes(256, 32, 128, 128) + 256 * 32 * 4
+    gbs = nb / (per_avg * 1e-3) / 1e9
+    out["decode"] = {"workload": GDN_DECODE, "ms_per_step": region / n_timed,
+                     "tokens_per_s": 256 / (region / n_timed * 1e-3),
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                  "traffic": recorded_traffic(GDN_DECODE),
+                                  "kernel": "sgla_gdn_recurrent_step",
+                                  "algorithmic_bytes_per_launch": nb, "avg_launch_ms": per_avg}}
+    del d, dout
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_bf16_state(args, torch, sgla, W, dev):

@@ -29,6 +29,9 @@
 // The inverse T is found in fp32 by back substitution on (I + A)^T, whose
 // solution for unit vector e_c is row c of T: lane c of one wave computes row
 // c and writes it contiguously, 64 lanes, 64 rows, no transposition. The
+// substitution is right-looking: as soon as y_j is final it is taken out of
+// every y_m, m < j, so the dependent chain is 64 steps long and each step's
+// updates are independent of one another. The
 // column scalings beta exp(G) and beta are folded into T, which is then split
 // into a bf16 high and low part, so W and U come from exact bf16 K and V
 // times a T accurate to about 2^-16.
@@ -45,15 +48,15 @@ constexpr int NT = 256;
 constexpr int P_K = 0;             // K rows [64][256 B]; then T' high and low parts
 constexpr int P_KT = 16384;        // K^T [128 dk][128 B]
 constexpr int P_VT = 32768;        // V^T [128 dv][128 B]
-constexpr int P_AT = 49152;        // A^T fp32 [64][68]; then T'' high and low parts
-constexpr int AT_ROW = 68 * 4;     // padded row (16-byte aligned, rows start 4 banks apart)
-constexpr int P_G = P_AT + 64 * AT_ROW;
+constexpr int P_A = 49152;         // A fp32 [64][68], row-major; then T'' high and low parts
+constexpr int A_ROW = 68 * 4;      // padded row (16-byte aligned, rows start 4 banks apart)
+constexpr int P_G = P_A + 64 * A_ROW;
 constexpr int P_B = P_G + 256;
 constexpr int P_BYTES = P_B + 256;
 constexpr int P_TPH = 0;           // T' = T diag(beta exp(G)), [64 rows][128 B] bf16, high part
 constexpr int P_TPL = 8192;        // low part
-constexpr int P_TQH = P_AT;        // T'' = T diag(beta), high part
-constexpr int P_TQL = P_AT + 8192; // low part
+constexpr int P_TQH = P_A;         // T'' = T diag(beta), high part
+constexpr int P_TQL = P_A + 8192;  // low part
 static_assert(P_TQL + 8192 <= P_G, "T'' parts overlap the gate tables");
 
 // ---- gdn_chunk_kernel LDS map (bytes).
@@ -64,6 +67,23 @@ constexpr int C_W = 49152;   // W rows [64][256 B]
 constexpr int C_A = 65536;   // scores A[64 i][128 B]
 constexpr int C_G = 73728;   // G[64] fp32
 constexpr int C_BYTES = C_G + 256;
+
+// Per chunk and head the workspace tile holds W (16 KiB bf16 rows) and U
+// (32 KiB fp32, value-major) from the prep kernel. Once the chain kernel has
+// taken a chunk's W and U it reuses the same tile for what the output kernel
+// needs: the bf16 state the chunk starts from and the chunk's bf16 new_v, both
+// stored as the register image of their MFMA operands (16 bytes per lane and
+// operand, lanes consecutive), so the output kernel loads them straight into
+// operand registers.
+constexpr int TILE_ELEMS = 64 * D;                 // bf16 elements of W; U is as many floats
+constexpr int TILE_BYTES = 3 * TILE_ELEMS * 2;      // W + U = 48 KiB
+constexpr int IMG_S = 0;                            // state image: [wave 4][8 operands][64 lanes] x 16 B
+constexpr int IMG_NV = 4 * 8 * 64 * 16;             // new_v image: [wave 4][4 operands][64 lanes] x 16 B
+static_assert(IMG_NV + 4 * 4 * 64 * 16 <= TILE_BYTES, "images exceed the tile");
+
+__device__ __forceinline__ char *tile_at(const GdnParams &p, int64_t s, int h) {
+    return p.tiles + ((int64_t)s * p.c.H + h) * TILE_BYTES;
+}
 
 __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -129,54 +149,56 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     }
     __syncthreads();
 
-    // A^T[m][i] = A[i][m] = beta_i (k_i . k_m) exp(G_i - G_m) for i > m, else 0.
-    // Waves 0-2 take the tiles (i block, m block) = (0,0), (1,0), (1,1); the
-    // tile with every i < m is never read.
+    // A[i][m] = beta_i (k_i . k_m) exp(G_i - G_m) for i > m, else 0, row-major.
+    // K K^T is symmetric; with the m block as the A operand each lane holds
+    // one row i and four consecutive m per group. Waves 0-2 take the tiles
+    // (i block, m block) = (0,0), (1,0), (1,1); the tile with every i < m is
+    // never read.
     if (w < 3) {
         const int ib = w == 0 ? 0 : 1;
         const int mb = w == 2 ? 1 : 0;
-        const int ir = 32 * ib + ln;
-        const int m = 32 * mb + ln;
+        const int i = 32 * ib + ln;
+        const int mr = 32 * mb + ln;
         f32x16 acc = {};
 #pragma unroll
         for (int st = 0; st < 8; ++st) {
-            const bf16x8 a = lds_ld<bf16x8>(lds, P_K + row_off(ir, 2 * st + lh));
-            const bf16x8 b = lds_ld<bf16x8>(lds, P_K + row_off(m, 2 * st + lh));
+            const bf16x8 a = lds_ld<bf16x8>(lds, P_K + row_off(mr, 2 * st + lh));
+            const bf16x8 b = lds_ld<bf16x8>(lds, P_K + row_off(i, 2 * st + lh));
             acc = mfma(a, b, acc);
         }
-        const float Gm = lds_ld<float>(lds, P_G + 4 * m);
+        const float Gi = lds_ld<float>(lds, P_G + 4 * i);
+        const float bi = lds_ld<float>(lds, P_B + 4 * i);
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-            const int i0 = 32 * ib + 8 * g4 + 4 * lh;
-            const float4 Gi = lds_ld<float4>(lds, P_G + 4 * i0);
-            const float4 Bi = lds_ld<float4>(lds, P_B + 4 * i0);
-            const float gi[4] = {Gi.x, Gi.y, Gi.z, Gi.w};
-            const float bi[4] = {Bi.x, Bi.y, Bi.z, Bi.w};
+            const int m0 = 32 * mb + 8 * g4 + 4 * lh;
+            const float4 Gm = lds_ld<float4>(lds, P_G + 4 * m0);
+            const float gm[4] = {Gm.x, Gm.y, Gm.z, Gm.w};
             float a[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                a[r] = (i0 + r > m) ? bi[r] * acc[4 * g4 + r] * __expf(gi[r] - Gm) : 0.f;
-            lds_st(lds, P_AT + m * AT_ROW + 4 * i0, make_float4(a[0], a[1], a[2], a[3]));
+                a[r] = (i > m0 + r) ? bi * acc[4 * g4 + r] * __expf(Gi - gm[r]) : 0.f;
+            lds_st(lds, P_A + i * A_ROW + 4 * m0, make_float4(a[0], a[1], a[2], a[3]));
         }
     }
     __syncthreads();
 
     // Row c = l of T = (I + A)^-1 by back substitution on (I + A)^T y = e_c:
-    // y_m = [m == c] - sum_{j > m} A[j][m] y_j, for m = 63 down to 0.
+    // y_m = [m == c] - sum_{j > m} A[j][m] y_j. Right-looking: for j = 63
+    // down to 1, y_j is final and leaves -A[j][m] y_j in every y_m, m < j.
     if (w == 0) {
         float y[64];
 #pragma unroll
-        for (int m = 63; m >= 0; --m) {
-            float acc = m == l ? 1.f : 0.f;
+        for (int m = 0; m < 64; ++m) y[m] = m == l ? 1.f : 0.f;
 #pragma unroll
-            for (int jq = (m + 1) & ~3; jq < 64; jq += 4) {
-                const float4 a = lds_ld<float4>(lds, P_AT + m * AT_ROW + 4 * jq);
-                if (jq + 0 > m) acc = fmaf(-a.x, y[jq + 0], acc);
-                if (jq + 1 > m) acc = fmaf(-a.y, y[jq + 1], acc);
-                if (jq + 2 > m) acc = fmaf(-a.z, y[jq + 2], acc);
-                if (jq + 3 > m) acc = fmaf(-a.w, y[jq + 3], acc);
+        for (int j = 63; j >= 1; --j) {
+#pragma unroll
+            for (int mq = 0; mq < j; mq += 4) {
+                const float4 a = lds_ld<float4>(lds, P_A + j * A_ROW + 4 * mq);
+                if (mq + 0 < j) y[mq + 0] = fmaf(-a.x, y[j], y[mq + 0]);
+                if (mq + 1 < j) y[mq + 1] = fmaf(-a.y, y[j], y[mq + 1]);
+                if (mq + 2 < j) y[mq + 2] = fmaf(-a.z, y[j], y[mq + 2]);
+                if (mq + 3 < j) y[mq + 3] = fmaf(-a.w, y[j], y[mq + 3]);
             }
-            y[m] = acc;
         }
         // T'[c][m] = y_m beta_m exp(G_m), T''[c][m] = y_m beta_m, each as a
         // bf16 high part and the bf16 rounding of the rest.
@@ -209,8 +231,8 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     // Wave w: W^T = K^T T'^T for dk rows [32w, 32w + 32) (stored as W rows,
     // token-major), and U = T'' V for value columns [32w, 32w + 32) (stored
     // as U^T rows, value-major, fp32). Rows past the chunk's end come out zero.
-    uint16_t *wt = p.w + ((int64_t)s * H + h) * (64 * D);
-    float *ut = p.u + ((int64_t)s * H + h) * (64 * D);
+    uint16_t *wt = reinterpret_cast<uint16_t *>(tile_at(p, s, h));
+    float *ut = reinterpret_cast<float *>(tile_at(p, s, h) + TILE_ELEMS * 2);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         f32x16 aw = {}, au = {};
@@ -236,29 +258,38 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     }
 }
 
-// One (sequence, head) per workgroup, through all its chunks. Wave w owns
-// value columns [32w, 32w + 32) of the state (lane l: column 32w + l % 32,
-// key rows 32b + 8(v/4) + 4(l/32) + v%4 of accumulator S[b], element v).
+// ---- gdn_chain_kernel LDS map (bytes).
+constexpr int H_W = 0;        // W rows [64][256 B]
+constexpr int H_KT = 16384;   // K^T [128 dk][128 B]
+constexpr int H_U = 32768;    // U pieces, lane-private: [wave 4][8 pieces][64 lanes] x 16 B
+constexpr int H_G = 65536;    // G[64] fp32
+constexpr int H_BYTES = H_G + 256;
+
+// One (sequence, head) per workgroup, through all its chunks: the state
+// recurrence alone. Wave w owns value columns [32w, 32w + 32) of the state
+// (lane l: column 32w + l % 32, key rows 32b + 8(v/4) + 4(l/32) + v%4 of
+// accumulator S[b], element v).
 //
 // new_v = U - W S comes out of the MFMA with each lane holding one value
 // column and, per group of four, four consecutive tokens: converted in
-// registers it is directly the token-indexed operand of the output product
-// (bf16) and of the state update (exp(G_last - G) new_v as bf16 high and low
-// parts), the other operand (scores, K^T) being read in the same token order.
-__global__ __launch_bounds__(NT) void gdn_chunk_kernel(GdnParams p) {
+// registers it is directly the token-indexed operand of the state update
+// (exp(G_last - G) new_v as bf16 high and low parts, K^T read in the same
+// token order) and, stored as its register image, of the output product.
+// The next chunk's k, W and U stream into registers while a chunk computes;
+// U then waits in lane-private LDS slots, so the registers are free for the
+// next prefetch.
+__global__ __launch_bounds__(NT) void gdn_chain_kernel(GdnParams p) {
     const int H = p.c.H;
     const int seq = blockIdx.x / H;
     const int h = blockIdx.x - seq * H;
     if (seq >= p.c.N) return;
     const SeqEntry sq = seq_at(p.c, seq);
-    __shared__ __attribute__((aligned(16))) char lds[C_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds[H_BYTES];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int l = tid & 63;
-    const uint16_t *__restrict__ qg = static_cast<const uint16_t *>(p.c.q);
     const uint16_t *__restrict__ kg = static_cast<const uint16_t *>(p.c.k);
-    uint16_t *__restrict__ og = static_cast<uint16_t *>(p.c.out);
     const int64_t sl = (int64_t)D * D;
 
     f32x16 S[4];
@@ -273,20 +304,18 @@ __global__ __launch_bounds__(NT) void gdn_chunk_kernel(GdnParams p) {
             }
     }
 
-    u32x4 qr[2][2], kr[2][2], wr[2][2];
-    float4 ur[2][4];
+    u32x4 kr[2][2], wr[2][2];
+    float4 ur[8];
     float gr = 0.f;
     auto issue = [&](int j) {
         const SegEntry e = seg_at(p.c, sq.first + j);
         const int n = e.len;
         int tv = tid;
         asm volatile("" : "+v"(tv));
-        const int64_t base = (e.tok0 * H + h) * D;
-        const uint16_t *qb = qg + base;
-        const uint16_t *kb = kg + base;
-        const int64_t tile = ((int64_t)(sq.first + j) * H + h) * (64 * D);
-        const uint16_t *wb = p.w + tile;
-        const float *ub = p.u + tile;
+        const uint16_t *kb = kg + (e.tok0 * H + h) * D;
+        const char *tb = tile_at(p, sq.first + j, h);
+        const uint16_t *wb = reinterpret_cast<const uint16_t *>(tb);
+        const float *ub = reinterpret_cast<const float *>(tb + TILE_ELEMS * 2);
         const int64_t rs = (int64_t)H * D;
 #pragma unroll
         for (int it = 0; it < 2; ++it)
@@ -294,19 +323,15 @@ __global__ __launch_bounds__(NT) void gdn_chunk_kernel(GdnParams p) {
             for (int rr = 0; rr < 2; ++rr) {
                 const int r = 2 * (((tv >> 4) & 15) + 16 * it) + rr;
                 const int c8 = 8 * (tv & 15);
-                const bool ok = r < n;
-                qr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(qb + r * rs + c8) : u32x4{0, 0, 0, 0};
-                kr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(kb + r * rs + c8) : u32x4{0, 0, 0, 0};
+                kr[it][rr] = r < n ? *reinterpret_cast<const u32x4 *>(kb + r * rs + c8) : u32x4{0, 0, 0, 0};
                 wr[it][rr] = *reinterpret_cast<const u32x4 *>(wb + r * D + c8);
             }
-        // U^T pieces in accumulator order: value column 32w + l%32, tokens
-        // 32nt + 8q + 4(l/32) .. + 3.
+        // U^T pieces in accumulator order: value column 32w + l%32, piece
+        // 4nt + q holds tokens 32nt + 8q + 4(l/32) .. + 3.
         const int dv = 32 * (tv >> 6) + (tv & 31);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                ur[nt][q] = *reinterpret_cast<const float4 *>(ub + dv * 64 + 32 * nt + 8 * q + 4 * ((tv >> 5) & 1));
+        for (int pc = 0; pc < 8; ++pc)
+            ur[pc] = *reinterpret_cast<const float4 *>(ub + dv * 64 + 8 * pc + 4 * ((tv >> 5) & 1));
         gr = (tv & 63) < n ? p.c.g[(e.tok0 + (tv & 63)) * H + h] : 0.f;
     };
 
@@ -316,42 +341,24 @@ __global__ __launch_bounds__(NT) void gdn_chunk_kernel(GdnParams p) {
     const bool any = nch > 1 || (nch == 1 && seg_at(p.c, sq.first).len > 0);
     if (any) issue(0);
 
+    const int ln = tid & 31;
+    const int lh = (tid >> 5) & 1;
+    const int cidx = tid & 15;
+    const int prb = (tid >> 4) & 15;
     for (int j = 0; any && j < nch; ++j) {
-        const SegEntry se = seg_at(p.c, sq.first + j);
-        const int n = se.len;
-        const int64_t t0 = se.tok0;
-        int tidv = tid;
-        asm volatile("" : "+v"(tidv));
-        const int ln = tidv & 31;
-        const int lh = (tidv >> 5) & 1;
-        const int cidx = tidv & 15;
-        const int prb = (tidv >> 4) & 15;
 
         const float G = wave_prefix_sum(gr);
         const float Gl = lane_value(G, 63);
-        // U of this chunk, before the next chunk's loads reuse the registers.
-        float uc[2][16];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uc[nt][4 * q + 0] = ur[nt][q].x;
-                uc[nt][4 * q + 1] = ur[nt][q].y;
-                uc[nt][4 * q + 2] = ur[nt][q].z;
-                uc[nt][4 * q + 3] = ur[nt][q].w;
-            }
 
         __syncthreads();  // every reader of the previous chunk's tiles is done
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const int r = 2 * (prb + 16 * it) + rr;
-                lds_st(lds, C_Q + row_off(r, cidx), qr[it][rr]);
-                lds_st(lds, C_K + row_off(r, cidx), kr[it][rr]);
-                lds_st(lds, C_W + row_off(r, cidx), wr[it][rr]);
-            }
-        if (w == 0) lds_st(lds, C_G + 4 * l, G);
+            for (int rr = 0; rr < 2; ++rr)
+                lds_st(lds, H_W + row_off(2 * (prb + 16 * it) + rr, cidx), wr[it][rr]);
+#pragma unroll
+        for (int pc = 0; pc < 8; ++pc) lds_st(lds, H_U + ((w * 8 + pc) * 64 + l) * 16, ur[pc]);
+        if (w == 0) lds_st(lds, H_G + 4 * l, G);
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
             const int r0 = 2 * (prb + 16 * it);
@@ -360,148 +367,86 @@ __global__ __launch_bounds__(NT) void gdn_chunk_kernel(GdnParams p) {
             for (int e2 = 0; e2 < 4; ++e2) {
                 const uint32_t k0 = kr[it][0][e2], k1 = kr[it][1][e2];
                 const int d = 8 * cidx + 2 * e2;
-                lds_st(lds, C_KT + tr_off(d, r0 >> 3) + cb, pack_lo(k0, k1));
-                lds_st(lds, C_KT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(k0, k1));
+                lds_st(lds, H_KT + tr_off(d, r0 >> 3) + cb, pack_lo(k0, k1));
+                lds_st(lds, H_KT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(k0, k1));
             }
         }
-        __syncthreads();  // tiles of this chunk are in LDS
+        __syncthreads();  // tiles of this chunk are in LDS; its W and U are all read
 
         if (j + 1 < nch) issue(j + 1);
 
-        // The state as bf16 operands: B of W S (columns = value columns) and
-        // A of S^T Q^T (rows = value columns), key rows in accumulator order.
-        bf16x8 sb[4][2];
+        // W S for both token halves in one pass over the state: each bf16
+        // operand of S (key rows in accumulator order) is made, stored in the
+        // chunk's tile for the output kernel, and used at once.
+        char *img = tile_at(p, sq.first + j, h);
+        f32x16 acc[2] = {{}, {}};
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
+            for (int s2 = 0; s2 < 2; ++s2) {
+                bf16x8 sb;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) sb[b][s2][e] = (__bf16)S[b][8 * s2 + e];
-
-        // Scores: wave 0 -> (j 0-31, i 0-31), 1 -> (j 0-31, i 32-63), 2 -> (j 32-63, i 32-63).
-        if (w < 3) {
-            const int jb = w == 2 ? 1 : 0;
-            const int ib = w == 0 ? 0 : 1;
-            f32x16 acc = {};
-            const int jj = 32 * jb + ln;
-            const int i = 32 * ib + ln;
+                for (int e = 0; e < 8; ++e) sb[e] = (__bf16)S[b][8 * s2 + e];
+                *reinterpret_cast<bf16x8 *>(img + IMG_S + ((w * 8 + 2 * b + s2) * 64 + l) * 16) = sb;
+                const int c = 4 * b + 2 * s2;
 #pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const bf16x8 a = lds_ld<bf16x8>(lds, C_K + row_off(jj, 2 * st + lh));
-                const bf16x8 bq = lds_ld<bf16x8>(lds, C_Q + row_off(i, 2 * st + lh));
-                acc = mfma(a, bq, acc);
+                for (int nt = 0; nt < 2; ++nt) {
+                    const int i = 32 * nt + ln;
+                    const bf16x4 x0 = lds_ld<bf16x4>(lds, H_W + row_off(i, c) + 8 * lh);
+                    const bf16x4 x1 = lds_ld<bf16x4>(lds, H_W + row_off(i, c + 1) + 8 * lh);
+                    acc[nt] = mfma(cat4(x0, x1), sb, acc[nt]);
+                }
             }
-            const float Gi = lds_ld<float>(lds, C_G + 4 * i);
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int jr = 32 * jb + 8 * g4 + 4 * lh;
-                const float4 Gj = lds_ld<float4>(lds, C_G + 4 * jr);
-                const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
-                float val[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    val[r] = (jr + r <= i) ? p.c.scale * __expf(Gi - gj[r]) * acc[4 * g4 + r] : 0.f;
-                const u32x2 pk = {pack_f32(val[0], val[1]), pack_f32(val[2], val[3])};
-                lds_st(lds, C_A + tr_off(i, 4 * jb + g4) + 8 * lh, pk);
-            }
-        }
 
-        // new_v = U - W S for this wave's value columns, both token halves:
-        // nvop in bf16 for the output; exp(G_last - G) new_v as high and low
-        // bf16 parts (nvh, nvl) for the state update.
-        bf16x8 nvop[4], nvh[4], nvl[4];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int i = 32 * nt + ln;
-            f32x16 acc = {};
+        const bool update = j + 1 < nch || p.c.sfin;
+        if (update) {
+            const float a = __expf(Gl);
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int c = 4 * b + 2 * s2;
-                    const bf16x4 x0 = lds_ld<bf16x4>(lds, C_W + row_off(i, c) + 8 * lh);
-                    const bf16x4 x1 = lds_ld<bf16x4>(lds, C_W + row_off(i, c + 1) + 8 * lh);
-                    acc = mfma(cat4(x0, x1), sb[b][s2], acc);
-                }
+                for (int v = 0; v < 16; ++v) S[b][v] *= a;
+        }
+        // Per token half: new_v = U - W S, its bf16 image for the output
+        // kernel, and its share of the update with exp(G_last - G) new_v as
+        // high and low bf16 parts.
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            bf16x8 nvo[2], nvh[2], nvl[2];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                const float4 u = lds_ld<float4>(lds, H_U + ((w * 8 + 4 * nt + q) * 64 + l) * 16);
+                const float uq[4] = {u.x, u.y, u.z, u.w};
                 // tokens 32nt + 8q + 4(l/32) + r of accumulator element 4q + r
-                const float4 Gt = lds_ld<float4>(lds, C_G + 4 * (32 * nt + 8 * q + 4 * lh));
+                const float4 Gt = lds_ld<float4>(lds, H_G + 4 * (32 * nt + 8 * q + 4 * lh));
                 const float gt[4] = {Gt.x, Gt.y, Gt.z, Gt.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int v = 4 * q + r;
-                    const float nv = uc[nt][v] - acc[v];
+                    const float nv = uq[r] - acc[nt][v];
                     const float x = nv * __expf(Gl - gt[r]);
                     const __bf16 xh = (__bf16)x;
-                    nvop[2 * nt + (v >> 3)][v & 7] = (__bf16)nv;
-                    nvh[2 * nt + (v >> 3)][v & 7] = xh;
-                    nvl[2 * nt + (v >> 3)][v & 7] = (__bf16)(x - (float)xh);
+                    nvo[v >> 3][v & 7] = (__bf16)nv;
+                    nvh[v >> 3][v & 7] = xh;
+                    nvl[v >> 3][v & 7] = (__bf16)(x - (float)xh);
                 }
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+                *reinterpret_cast<bf16x8 *>(img + IMG_NV + ((w * 4 + 2 * nt + s2) * 64 + l) * 16) = nvo[s2];
+            if (update) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const int st = 2 * nt + s2;
+                        const bf16x4 z0 = lds_ld<bf16x4>(lds, H_KT + tr_off(32 * b + ln, 2 * st) + 8 * lh);
+                        const bf16x4 z1 = lds_ld<bf16x4>(lds, H_KT + tr_off(32 * b + ln, 2 * st + 1) + 8 * lh);
+                        const bf16x8 kt = cat4(z0, z1);
+                        S[b] = mfma(kt, nvh[s2], S[b]);
+                        S[b] = mfma(kt, nvl[s2], S[b]);
+                    }
             }
         }
-        __syncthreads();  // scores complete; K rows free for the O staging
-
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            const int i = 32 * nt + ln;
-            f32x16 acc = {};
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int c = 4 * b + 2 * s2;
-                    const bf16x4 x0 = lds_ld<bf16x4>(lds, C_Q + row_off(i, c) + 8 * lh);
-                    const bf16x4 x1 = lds_ld<bf16x4>(lds, C_Q + row_off(i, c + 1) + 8 * lh);
-                    acc = mfma(sb[b][s2], cat4(x0, x1), acc);
-                }
-            const float f = p.c.scale * __expf(lds_ld<float>(lds, C_G + 4 * i));
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[v] *= f;
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                if (nt == 0 && st >= 2) break;
-                const bf16x4 y0 = lds_ld<bf16x4>(lds, C_A + tr_off(i, 2 * st) + 8 * lh);
-                const bf16x4 y1 = lds_ld<bf16x4>(lds, C_A + tr_off(i, 2 * st + 1) + 8 * lh);
-                acc = mfma(nvop[st], cat4(y0, y1), acc);
-            }
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const u32x2 pk = {pack_f32(acc[4 * g4], acc[4 * g4 + 1]),
-                                  pack_f32(acc[4 * g4 + 2], acc[4 * g4 + 3])};
-                lds_st(lds, C_K + row_off(i, 4 * w + g4) + 8 * lh, pk);
-            }
-        }
-
-        const bool last = j + 1 == nch;
-        if (!last || p.c.sfin) {
-            const float a = __expf(Gl);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) S[b][v] *= a;
-#pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const bf16x4 z0 = lds_ld<bf16x4>(lds, C_KT + tr_off(32 * b + ln, 2 * st) + 8 * lh);
-                    const bf16x4 z1 = lds_ld<bf16x4>(lds, C_KT + tr_off(32 * b + ln, 2 * st + 1) + 8 * lh);
-                    const bf16x8 kt = cat4(z0, z1);
-                    S[b] = mfma(kt, nvh[st], S[b]);
-                    S[b] = mfma(kt, nvl[st], S[b]);
-                }
-            }
-        }
-
-        __syncthreads();  // O staging rows complete
-#pragma unroll
-        for (int it = 0; it < 2; ++it)
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const int r = 2 * (prb + 16 * it) + rr;
-                if (r < n) {
-                    const u32x4 o = lds_ld<u32x4>(lds, C_K + row_off(r, cidx));
-                    *reinterpret_cast<u32x4 *>(og + (t0 + r) * H * D + h * D + 8 * cidx) = o;
-                }
-            }
     }
 
     if (p.c.sfin) {
@@ -516,15 +461,154 @@ __global__ __launch_bounds__(NT) void gdn_chunk_kernel(GdnParams p) {
     }
 }
 
+// ---- gdn_output_kernel LDS map (bytes).
+constexpr int O_Q = 0;       // Q rows [64][256 B]
+constexpr int O_K = 16384;   // K rows [64][256 B]; later the O staging rows
+constexpr int O_A = 32768;   // scores A[64 i][128 B]
+constexpr int O_G = 40960;   // G[64] fp32
+constexpr int O_BYTES = O_G + 256;
+
+// One (chunk, head) per workgroup, all chunks at once:
+// O = scale ((Q * exp(G)) S + lower(Q K^T * Gamma) new_v), with S (the state
+// the chunk starts from) and new_v taken in bf16 from the chain kernel's
+// images. Wave w computes value columns [32w, 32w + 32) of O.
+__global__ __launch_bounds__(NT) void gdn_output_kernel(GdnParams p) {
+    const int H = p.c.H;
+    const int s = blockIdx.x / H;
+    const int h = blockIdx.x - s * H;
+    if (s >= p.c.nseg_max) return;
+    const SegEntry se = seg_at(p.c, s);
+    if (se.len <= 0) return;
+    const int n = se.len;
+    __shared__ __attribute__((aligned(16))) char lds[O_BYTES];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int l = tid & 63;
+    const int ln = l & 31;
+    const int lh = l >> 5;
+    const int cidx = tid & 15;
+    const int prb = (tid >> 4) & 15;
+
+    const int64_t base = (se.tok0 * H + h) * D;
+    const uint16_t *qg = static_cast<const uint16_t *>(p.c.q) + base;
+    const uint16_t *kg = static_cast<const uint16_t *>(p.c.k) + base;
+    const int64_t rs = (int64_t)H * D;
+    u32x4 qr[2][2], kr[2][2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int r = 2 * (prb + 16 * it) + rr;
+            const bool ok = r < n;
+            qr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(qg + r * rs + 8 * cidx) : u32x4{0, 0, 0, 0};
+            kr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(kg + r * rs + 8 * cidx) : u32x4{0, 0, 0, 0};
+        }
+    const float gv = l < n ? p.c.g[(se.tok0 + l) * H + h] : 0.f;
+    const char *img = tile_at(p, s, h);
+    bf16x8 sb[8], nvop[4];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+        sb[k] = *reinterpret_cast<const bf16x8 *>(img + IMG_S + ((w * 8 + k) * 64 + l) * 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        nvop[k] = *reinterpret_cast<const bf16x8 *>(img + IMG_NV + ((w * 4 + k) * 64 + l) * 16);
+
+    const float G = wave_prefix_sum(gv);
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int r = 2 * (prb + 16 * it) + rr;
+            lds_st(lds, O_Q + row_off(r, cidx), qr[it][rr]);
+            lds_st(lds, O_K + row_off(r, cidx), kr[it][rr]);
+        }
+    if (w == 0) lds_st(lds, O_G + 4 * l, G);
+    __syncthreads();
+
+    // Scores: wave 0 -> (j 0-31, i 0-31), 1 -> (j 0-31, i 32-63), 2 -> (j 32-63, i 32-63).
+    if (w < 3) {
+        const int jb = w == 2 ? 1 : 0;
+        const int ib = w == 0 ? 0 : 1;
+        f32x16 acc = {};
+        const int jj = 32 * jb + ln;
+        const int i = 32 * ib + ln;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const bf16x8 a = lds_ld<bf16x8>(lds, O_K + row_off(jj, 2 * st + lh));
+            const bf16x8 bq = lds_ld<bf16x8>(lds, O_Q + row_off(i, 2 * st + lh));
+            acc = mfma(a, bq, acc);
+        }
+        const float Gi = lds_ld<float>(lds, O_G + 4 * i);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int jr = 32 * jb + 8 * g4 + 4 * lh;
+            const float4 Gj = lds_ld<float4>(lds, O_G + 4 * jr);
+            const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
+            float val[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                val[r] = (jr + r <= i) ? p.c.scale * __expf(Gi - gj[r]) * acc[4 * g4 + r] : 0.f;
+            const u32x2 pk = {pack_f32(val[0], val[1]), pack_f32(val[2], val[3])};
+            lds_st(lds, O_A + tr_off(i, 4 * jb + g4) + 8 * lh, pk);
+        }
+    }
+    __syncthreads();  // scores complete; K rows free for the O staging
+
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        const int i = 32 * nt + ln;
+        f32x16 acc = {};
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int c = 4 * b + 2 * s2;
+                const bf16x4 x0 = lds_ld<bf16x4>(lds, O_Q + row_off(i, c) + 8 * lh);
+                const bf16x4 x1 = lds_ld<bf16x4>(lds, O_Q + row_off(i, c + 1) + 8 * lh);
+                acc = mfma(sb[2 * b + s2], cat4(x0, x1), acc);
+            }
+        const float f = p.c.scale * __expf(lds_ld<float>(lds, O_G + 4 * i));
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] *= f;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            if (nt == 0 && st >= 2) break;
+            const bf16x4 y0 = lds_ld<bf16x4>(lds, O_A + tr_off(i, 2 * st) + 8 * lh);
+            const bf16x4 y1 = lds_ld<bf16x4>(lds, O_A + tr_off(i, 2 * st + 1) + 8 * lh);
+            acc = mfma(nvop[st], cat4(y0, y1), acc);
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const u32x2 pk = {pack_f32(acc[4 * g4], acc[4 * g4 + 1]),
+                              pack_f32(acc[4 * g4 + 2], acc[4 * g4 + 3])};
+            lds_st(lds, O_K + row_off(i, 4 * w + g4) + 8 * lh, pk);
+        }
+    }
+    __syncthreads();  // O staging rows complete
+    uint16_t *og = static_cast<uint16_t *>(p.c.out) + base;
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int r = 2 * (prb + 16 * it) + rr;
+            if (r < n)
+                *reinterpret_cast<u32x4 *>(og + r * rs + 8 * cidx) = lds_ld<u32x4>(lds, O_K + row_off(r, cidx));
+        }
+}
+
 }  // namespace
 
 hipError_t launch_gdn_chunk(const GdnParams &p, hipStream_t st) {
     if (p.c.N == 0) return hipSuccess;
-    if (p.c.nseg_max > 0)
-        hipLaunchKernelGGL(gdn_prep_kernel, dim3((unsigned)((int64_t)p.c.nseg_max * p.c.H)), dim3(NT), 0, st, p);
+    const dim3 chunks((unsigned)((int64_t)p.c.nseg_max * p.c.H));
+    if (p.c.nseg_max > 0) hipLaunchKernelGGL(gdn_prep_kernel, chunks, dim3(NT), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gdn_chunk_kernel, dim3((unsigned)((int64_t)p.c.N * p.c.H)), dim3(NT), 0, st, p);
+    hipLaunchKernelGGL(gdn_chain_kernel, dim3((unsigned)((int64_t)p.c.N * p.c.H)), dim3(NT), 0, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (p.c.nseg_max > 0) hipLaunchKernelGGL(gdn_output_kernel, chunks, dim3(NT), 0, st, p);
     return hipGetLastError();
 }
 

@@ -132,8 +132,8 @@ __device__ __forceinline__ float row16_swap8(float x) {
 struct GdnParams {
     ChunkParams c;      // q, k, v, g, s0, out, sfin, segs, seqs, H, nseg_max, N, scale, T, nps
     const float *beta;  // [tokens, H] write strength of each token
-    uint16_t *w;        // [nseg_max, H, 64, 128] W rows of each chunk (bf16)
-    float *u;           // [nseg_max, H, 128, 64] U of each chunk, value-major (fp32)
+    char *tiles;        // [nseg_max, H] tiles of 48 KiB: W rows (bf16) and U^T (fp32) of each
+                        // chunk, later the chunk's start state and new_v for the output
 };
 
 // Launchers (return hipSuccess or the launch error).
