@@ -85,9 +85,6 @@ __device__ __forceinline__ char *tile_at(const GdnParams &p, int64_t s, int h) {
     return p.tiles + ((int64_t)s * p.c.H + h) * TILE_BYTES;
 }
 
-__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 
 __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     const int H = p.c.H;

@@ -41,6 +41,10 @@ __device__ __forceinline__ uint32_t pack_f32(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
