@@ -295,9 +295,9 @@ sgla_status sgla_out_norm_gate(const void *o, const void *z, const float *weight
  * otherwise).
  *
  * Memory: the call takes a device workspace from HIP's stream-ordered
- * allocator on `stream` of (T / 64 + B + 1) * H * 48 KiB (per chunk and head
- * W in bf16 and U in fp32; B * ceil(T / 64) * H * 48 KiB without cu_seqlens)
- * plus a small table, and frees it on the same stream. Returns as
+ * allocator on `stream` of (T / 64 + B + 1) * H * 64 KiB (per chunk and head
+ * W and new_v in bf16, U in fp32; B * ceil(T / 64) * H * 64 KiB without
+ * cu_seqlens) plus a small table, and frees it on the same stream. Returns as
  * sgla_chunk_fwd.
  */
 sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,

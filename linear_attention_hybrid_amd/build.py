@@ -22,6 +22,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON_FLAGS = [
     "-O3", "-fPIC", "-std=c++17", "--offload-arch=" + ARCH,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Keep MFMA accumulators in ordinary VGPRs where they fit: kernels whose
+    # state lives in accumulators then do their elementwise work on them
+    # without copying through the accumulator registers.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
     "-I" + os.path.join(os.path.dirname(HERE), "include"),
 ]

@@ -16,9 +16,11 @@
 // W and U depend on the chunk alone, so they are computed for every chunk at
 // once by a first kernel (gdn_prep_kernel), one workgroup per (chunk, head),
 // and kept in a workspace (W in bf16, an MFMA operand; U in fp32). The state
-// recurrence is sequential over chunks: gdn_chunk_kernel walks one (sequence,
-// head) per workgroup through its chunks with the fp32 state in the MFMA
-// accumulators.
+// recurrence is sequential over chunks: gdn_chain_kernel walks each
+// (sequence, head, block of 32 value columns) through its chunks with the
+// fp32 state in the MFMA accumulators. A last kernel (gdn_output_kernel)
+// forms every chunk's output at once from the states and new_v the chain
+// leaves behind.
 //
 // Precision: the state is written through new_v, which is not a bf16 input
 // (beta v already is not), so the update takes exp(G_last - G) new_v in fp32
@@ -31,10 +33,10 @@
 // c and writes it contiguously, 64 lanes, 64 rows, no transposition. The
 // substitution is right-looking: as soon as y_j is final it is taken out of
 // every y_m, m < j, so the dependent chain is 64 steps long and each step's
-// updates are independent of one another. The
-// column scalings beta exp(G) and beta are folded into T, which is then split
-// into a bf16 high and low part, so W and U come from exact bf16 K and V
-// times a T accurate to about 2^-16.
+// updates are independent of one another. The column scalings beta exp(G)
+// and beta are folded into T, which is then split into a bf16 high and low
+// part, so W and U come from exact bf16 K and V times a T accurate to about
+// 2^-16.
 #include "mfma_tile.h"
 
 namespace sgla {
@@ -59,27 +61,18 @@ constexpr int P_TQH = P_A;         // T'' = T diag(beta), high part
 constexpr int P_TQL = P_A + 8192;  // low part
 static_assert(P_TQL + 8192 <= P_G, "T'' parts overlap the gate tables");
 
-// ---- gdn_chunk_kernel LDS map (bytes).
-constexpr int C_Q = 0;       // Q rows [64][256 B]
-constexpr int C_K = 16384;   // K rows [64][256 B]; later the O staging rows
-constexpr int C_KT = 32768;  // K^T [128 dk][128 B]
-constexpr int C_W = 49152;   // W rows [64][256 B]
-constexpr int C_A = 65536;   // scores A[64 i][128 B]
-constexpr int C_G = 73728;   // G[64] fp32
-constexpr int C_BYTES = C_G + 256;
-
 // Per chunk and head the workspace tile holds W (16 KiB bf16 rows) and U
-// (32 KiB fp32, value-major) from the prep kernel. Once the chain kernel has
-// taken a chunk's W and U it reuses the same tile for what the output kernel
-// needs: the bf16 state the chunk starts from and the chunk's bf16 new_v, both
-// stored as the register image of their MFMA operands (16 bytes per lane and
-// operand, lanes consecutive), so the output kernel loads them straight into
-// operand registers.
+// (32 KiB fp32, value-major: the 8 KiB of value columns 32b .. 32b + 31 are
+// read only by the chain workgroup of column block b). Once that workgroup
+// has taken its U slice it stores there the chunk's start state for its
+// columns, in bf16, as the register image of the output kernel's MFMA operand
+// (16 bytes per lane and operand, lanes consecutive). The chunk's bf16 new_v
+// goes, as an image too, to a separate 16 KiB per chunk and head.
 constexpr int TILE_ELEMS = 64 * D;                 // bf16 elements of W; U is as many floats
 constexpr int TILE_BYTES = 3 * TILE_ELEMS * 2;      // W + U = 48 KiB
-constexpr int IMG_S = 0;                            // state image: [wave 4][8 operands][64 lanes] x 16 B
-constexpr int IMG_NV = 4 * 8 * 64 * 16;             // new_v image: [wave 4][4 operands][64 lanes] x 16 B
-static_assert(IMG_NV + 4 * 4 * 64 * 16 <= TILE_BYTES, "images exceed the tile");
+constexpr int IMG_S = TILE_ELEMS * 2;               // state image: [block 4][8 operands][64 lanes] x 16 B
+constexpr int NV_BYTES = 4 * 4 * 64 * 16;           // new_v image: [block 4][4 operands][64 lanes] x 16 B
+static_assert(IMG_S + 4 * 8 * 64 * 16 == TILE_BYTES, "state image must fill the U slices");
 
 __device__ __forceinline__ char *tile_at(const GdnParams &p, int64_t s, int h) {
     return p.tiles + ((int64_t)s * p.c.H + h) * TILE_BYTES;
@@ -255,39 +248,46 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     }
 }
 
-// ---- gdn_chain_kernel LDS map (bytes).
-constexpr int H_W = 0;        // W rows [64][256 B]
-constexpr int H_KT = 16384;   // K^T [128 dk][128 B]
-constexpr int H_U = 32768;    // U pieces, lane-private: [wave 4][8 pieces][64 lanes] x 16 B
-constexpr int H_G = 65536;    // G[64] fp32
+// ---- gdn_chain_kernel: a ring of two chunk buffers in LDS (bytes).
+constexpr int HB_W = 0;        // W rows [64][256 B], swizzled as row_off
+constexpr int HB_K = 16384;    // k rows [64][256 B], swizzled as row_off
+constexpr int HB_U = 32768;    // this block's U pieces: [8][64 lanes] x 16 B
+constexpr int HB_G = 40960;    // g[64] fp32 (rows past the chunk's end: the last row's)
+constexpr int H_BUF = HB_G + 256;
+constexpr int H_G = 2 * H_BUF; // G[64] fp32 of the current chunk
 constexpr int H_BYTES = H_G + 256;
+constexpr int H_STORES = 8 + 4;  // image stores per chunk (state, new_v)
 
-// One (sequence, head) per workgroup, through all its chunks: the state
-// recurrence alone. Wave w owns value columns [32w, 32w + 32) of the state
-// (lane l: column 32w + l % 32, key rows 32b + 8(v/4) + 4(l/32) + v%4 of
-// accumulator S[b], element v).
+// The state recurrence, one wave per (sequence, head, block of 32 value
+// columns): W and k of a chunk are read by the four blocks of a head (the
+// four workgroups sit on one XCD and share its L2), U, the state and the
+// images are the block's own. Lane l holds column 32b + l % 32 of the state,
+// key rows 32r + 8(v/4) + 4(l/32) + v%4 of accumulator S[r], element v.
 //
-// new_v = U - W S comes out of the MFMA with each lane holding one value
-// column and, per group of four, four consecutive tokens: converted in
-// registers it is directly the token-indexed operand of the state update
-// (exp(G_last - G) new_v as bf16 high and low parts, K^T read in the same
-// token order) and, stored as its register image, of the output product.
-// The next chunk's k, W and U stream into registers while a chunk computes;
-// U then waits in lane-private LDS slots, so the registers are free for the
-// next prefetch.
-__global__ __launch_bounds__(NT) void gdn_chain_kernel(GdnParams p) {
+// Chunk j + 1's W rows, k rows and U pieces stream into the other ring buffer
+// by direct global -> LDS loads while chunk j computes. new_v = U - W S comes
+// out of the MFMA with each lane holding one value column and, per group of
+// four, four consecutive tokens: converted in registers it is directly the
+// token-indexed operand of the update (exp(G_last - G) new_v as bf16 high and
+// low parts), whose other operand, K^T, comes from the k rows through the
+// transposing read in the same token order.
+__global__ __launch_bounds__(64) void gdn_chain_kernel(GdnParams p) {
     const int H = p.c.H;
-    const int seq = blockIdx.x / H;
-    const int h = blockIdx.x - seq * H;
+    int unit, cb;
+    xcd_unit_map(blockIdx.x, 4, unit, cb);
+    const int seq = unit / H;
+    const int h = unit - seq * H;
     if (seq >= p.c.N) return;
     const SeqEntry sq = seq_at(p.c, seq);
     __shared__ __attribute__((aligned(16))) char lds[H_BYTES];
 
-    const int tid = threadIdx.x;
-    const int w = tid >> 6;
-    const int l = tid & 63;
-    const uint16_t *__restrict__ kg = static_cast<const uint16_t *>(p.c.k);
+    const int l = threadIdx.x;
+    const int ln = l & 31;
+    const int lh = l >> 5;
+    const int m16 = l & 15;
+    const int g16 = l >> 4;
     const int64_t sl = (int64_t)D * D;
+    const int64_t row_bytes = (int64_t)H * D * 2;
 
     f32x16 S[4];
     {
@@ -296,86 +296,80 @@ __global__ __launch_bounds__(NT) void gdn_chain_kernel(GdnParams p) {
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * b + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-                S[b][v] = src ? src[dk * D + 32 * w + (l & 31)] : 0.f;
+                const int dk = 32 * b + 8 * (v >> 2) + 4 * lh + (v & 3);
+                S[b][v] = src ? src[dk * D + 32 * cb + ln] : 0.f;
             }
+        // Take the loaded values here, once: otherwise the compiler keeps
+        // treating them as possibly in flight at the top of the chunk loop and
+        // waits there for every load and store of the wave, prefetches included.
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) asm volatile("" : "+v"(S[b][v]));
     }
 
-    u32x4 kr[2][2], wr[2][2];
-    float4 ur[8];
-    float gr = 0.f;
-    auto issue = [&](int j) {
-        const SegEntry e = seg_at(p.c, sq.first + j);
-        const int n = e.len;
-        int tv = tid;
-        asm volatile("" : "+v"(tv));
-        const uint16_t *kb = kg + (e.tok0 * H + h) * D;
-        const char *tb = tile_at(p, sq.first + j, h);
-        const uint16_t *wb = reinterpret_cast<const uint16_t *>(tb);
-        const float *ub = reinterpret_cast<const float *>(tb + TILE_ELEMS * 2);
-        const int64_t rs = (int64_t)H * D;
-#pragma unroll
-        for (int it = 0; it < 2; ++it)
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                const int r = 2 * (((tv >> 4) & 15) + 16 * it) + rr;
-                const int c8 = 8 * (tv & 15);
-                kr[it][rr] = r < n ? *reinterpret_cast<const u32x4 *>(kb + r * rs + c8) : u32x4{0, 0, 0, 0};
-                wr[it][rr] = *reinterpret_cast<const u32x4 *>(wb + r * D + c8);
-            }
-        // U^T pieces in accumulator order: value column 32w + l%32, piece
-        // 4nt + q holds tokens 32nt + 8q + 4(l/32) .. + 3.
-        const int dv = 32 * (tv >> 6) + (tv & 31);
-#pragma unroll
-        for (int pc = 0; pc < 8; ++pc)
-            ur[pc] = *reinterpret_cast<const float4 *>(ub + dv * 64 + 8 * pc + 4 * ((tv >> 5) & 1));
-        gr = (tv & 63) < n ? p.c.g[(e.tok0 + (tv & 63)) * H + h] : 0.f;
-    };
-
+    // The sequence's chunks are consecutive tokens: its start and length come
+    // from its first and last table rows, read once, so the loop itself reads
+    // no table entries (and the compiler adds no waits for them).
     // nseg is at least 1 for a valid table (an empty sequence has one empty
     // row); offsets that break the rules can leave 0, and then no row is read.
     const int nch = sq.nseg;
-    const bool any = nch > 1 || (nch == 1 && seg_at(p.c, sq.first).len > 0);
+    int64_t tok0 = 0;
+    int len = 0;
+    if (nch > 0) {
+        tok0 = seg_at(p.c, sq.first).tok0;
+        len = (nch - 1) * kChunk + max(seg_at(p.c, sq.first + nch - 1).len, 0);
+    }
+    auto issue = [&](int j) {
+        const int n = min(kChunk, len - kChunk * j);
+        const int64_t t0 = tok0 + (int64_t)kChunk * j;
+        const char *buf = lds + (j & 1) * H_BUF;
+        const char *tile = tile_at(p, sq.first + j, h);
+        const char *kb = static_cast<const char *>(p.c.k) + (t0 * H + h) * (D * 2);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = 4 * i + (l >> 4);
+            const int pc = (m16 ^ (r & 15)) << 4;
+            gll16(tile + r * 256 + pc, buf + HB_W + 1024 * i);
+            gll16(kb + min(r, n - 1) * row_bytes + pc, buf + HB_K + 1024 * i);
+        }
+        // U^T pieces in accumulator order: value column 32cb + l%32, piece
+        // 4nt + q holds tokens 32nt + 8q + 4(l/32) .. + 3.
+        const char *ub = tile + TILE_ELEMS * 2 + ((32 * cb + ln) * 64 + 4 * lh) * 4;
+#pragma unroll
+        for (int pc = 0; pc < 8; ++pc) gll16(ub + 32 * pc, buf + HB_U + 1024 * pc);
+        gll4(p.c.g + (t0 + min(l, n - 1)) * H + h, buf + HB_G);
+    };
+
+    // Lane-constant parts of the transposing reads of K^T (rows 32b + l%32;
+    // the two reads of an operand give tokens 4(l/32) + 0..3 and + 8 + 0..3
+    // of each 16-token step, the order new_v comes out in).
+    int trk[4][2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) trk[b][hf] = tr_src(4 * (g16 >> 1) + 8 * hf, 32 * b + 16 * (g16 & 1), m16);
+
+    const bool any = len > 0;
     if (any) issue(0);
 
-    const int ln = tid & 31;
-    const int lh = (tid >> 5) & 1;
-    const int cidx = tid & 15;
-    const int prb = (tid >> 4) & 15;
     for (int j = 0; any && j < nch; ++j) {
-
-        const float G = wave_prefix_sum(gr);
+        // Chunk j's loads are done once only the previous chunk's image
+        // stores, issued after them, may remain.
+        wait_vm_n(j > 0 ? H_STORES : 0);
+        const char *buf = lds + (j & 1) * H_BUF;
+        const int n = min(kChunk, len - kChunk * j);
+        const float G = wave_prefix_sum(l < n ? lds_ld<float>(buf, HB_G + 4 * l) : 0.f);
         const float Gl = lane_value(G, 63);
-
-        __syncthreads();  // every reader of the previous chunk's tiles is done
-#pragma unroll
-        for (int it = 0; it < 2; ++it)
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr)
-                lds_st(lds, H_W + row_off(2 * (prb + 16 * it) + rr, cidx), wr[it][rr]);
-#pragma unroll
-        for (int pc = 0; pc < 8; ++pc) lds_st(lds, H_U + ((w * 8 + pc) * 64 + l) * 16, ur[pc]);
-        if (w == 0) lds_st(lds, H_G + 4 * l, G);
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-            const int r0 = 2 * (prb + 16 * it);
-            const int cb = (r0 & 7) * 2;
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const uint32_t k0 = kr[it][0][e2], k1 = kr[it][1][e2];
-                const int d = 8 * cidx + 2 * e2;
-                lds_st(lds, H_KT + tr_off(d, r0 >> 3) + cb, pack_lo(k0, k1));
-                lds_st(lds, H_KT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(k0, k1));
-            }
-        }
-        __syncthreads();  // tiles of this chunk are in LDS; its W and U are all read
-
+        lds_st(lds, H_G + 4 * l, G);
         if (j + 1 < nch) issue(j + 1);
 
         // W S for both token halves in one pass over the state: each bf16
         // operand of S (key rows in accumulator order) is made, stored in the
         // chunk's tile for the output kernel, and used at once.
-        char *img = tile_at(p, sq.first + j, h);
+        const int64_t unit_chunk = (int64_t)(sq.first + j) * H + h;
+        char *simg = tile_at(p, sq.first + j, h) + IMG_S + cb * 8 * 64 * 16;
+        char *nimg = p.nvimg + unit_chunk * NV_BYTES + cb * 4 * 64 * 16;
         f32x16 acc[2] = {{}, {}};
 #pragma unroll
         for (int b = 0; b < 4; ++b)
@@ -384,13 +378,13 @@ __global__ __launch_bounds__(NT) void gdn_chain_kernel(GdnParams p) {
                 bf16x8 sb;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) sb[e] = (__bf16)S[b][8 * s2 + e];
-                *reinterpret_cast<bf16x8 *>(img + IMG_S + ((w * 8 + 2 * b + s2) * 64 + l) * 16) = sb;
+                *reinterpret_cast<bf16x8 *>(simg + ((2 * b + s2) * 64 + l) * 16) = sb;
                 const int c = 4 * b + 2 * s2;
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) {
                     const int i = 32 * nt + ln;
-                    const bf16x4 x0 = lds_ld<bf16x4>(lds, H_W + row_off(i, c) + 8 * lh);
-                    const bf16x4 x1 = lds_ld<bf16x4>(lds, H_W + row_off(i, c + 1) + 8 * lh);
+                    const bf16x4 x0 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c) + 8 * lh);
+                    const bf16x4 x1 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c + 1) + 8 * lh);
                     acc[nt] = mfma(cat4(x0, x1), sb, acc[nt]);
                 }
             }
@@ -411,7 +405,7 @@ __global__ __launch_bounds__(NT) void gdn_chain_kernel(GdnParams p) {
             bf16x8 nvo[2], nvh[2], nvl[2];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float4 u = lds_ld<float4>(lds, H_U + ((w * 8 + 4 * nt + q) * 64 + l) * 16);
+                const float4 u = lds_ld<float4>(buf, HB_U + (4 * nt + q) * 1024 + 16 * l);
                 const float uq[4] = {u.x, u.y, u.z, u.w};
                 // tokens 32nt + 8q + 4(l/32) + r of accumulator element 4q + r
                 const float4 Gt = lds_ld<float4>(lds, H_G + 4 * (32 * nt + 8 * q + 4 * lh));
@@ -429,16 +423,15 @@ __global__ __launch_bounds__(NT) void gdn_chain_kernel(GdnParams p) {
             }
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
-                *reinterpret_cast<bf16x8 *>(img + IMG_NV + ((w * 4 + 2 * nt + s2) * 64 + l) * 16) = nvo[s2];
+                *reinterpret_cast<bf16x8 *>(nimg + ((2 * nt + s2) * 64 + l) * 16) = nvo[s2];
             if (update) {
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2) {
                         const int st = 2 * nt + s2;
-                        const bf16x4 z0 = lds_ld<bf16x4>(lds, H_KT + tr_off(32 * b + ln, 2 * st) + 8 * lh);
-                        const bf16x4 z1 = lds_ld<bf16x4>(lds, H_KT + tr_off(32 * b + ln, 2 * st + 1) + 8 * lh);
-                        const bf16x8 kt = cat4(z0, z1);
+                        const bf16x8 kt = cat4(lds_tr(buf, HB_K + 4096 * st + trk[b][0]),
+                                               lds_tr(buf, HB_K + 4096 * st + trk[b][1]));
                         S[b] = mfma(kt, nvh[s2], S[b]);
                         S[b] = mfma(kt, nvl[s2], S[b]);
                     }
@@ -452,8 +445,8 @@ __global__ __launch_bounds__(NT) void gdn_chain_kernel(GdnParams p) {
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * b + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
-                dst[dk * D + 32 * w + (l & 31)] = S[b][v];
+                const int dk = 32 * b + 8 * (v >> 2) + 4 * lh + (v & 3);
+                dst[dk * D + 32 * cb + ln] = S[b][v];
             }
     }
 }
@@ -502,14 +495,15 @@ __global__ __launch_bounds__(NT) void gdn_output_kernel(GdnParams p) {
             kr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(kg + r * rs + 8 * cidx) : u32x4{0, 0, 0, 0};
         }
     const float gv = l < n ? p.c.g[(se.tok0 + l) * H + h] : 0.f;
-    const char *img = tile_at(p, s, h);
+    const char *img = tile_at(p, s, h) + IMG_S;
+    const char *nimg = p.nvimg + ((int64_t)s * H + h) * NV_BYTES;
     bf16x8 sb[8], nvop[4];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-        sb[k] = *reinterpret_cast<const bf16x8 *>(img + IMG_S + ((w * 8 + k) * 64 + l) * 16);
+        sb[k] = *reinterpret_cast<const bf16x8 *>(img + ((w * 8 + k) * 64 + l) * 16);
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        nvop[k] = *reinterpret_cast<const bf16x8 *>(img + IMG_NV + ((w * 4 + k) * 64 + l) * 16);
+        nvop[k] = *reinterpret_cast<const bf16x8 *>(nimg + ((w * 4 + k) * 64 + l) * 16);
 
     const float G = wave_prefix_sum(gv);
 #pragma unroll
@@ -602,7 +596,10 @@ hipError_t launch_gdn_chunk(const GdnParams &p, hipStream_t st) {
     if (p.c.nseg_max > 0) hipLaunchKernelGGL(gdn_prep_kernel, chunks, dim3(NT), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gdn_chain_kernel, dim3((unsigned)((int64_t)p.c.N * p.c.H)), dim3(NT), 0, st, p);
+    // Four column blocks per (sequence, head), the units rounded up to whole
+    // groups of eight so that xcd_unit_map covers them.
+    const int64_t units = ((int64_t)p.c.N * p.c.H + 7) / 8 * 8;
+    hipLaunchKernelGGL(gdn_chain_kernel, dim3((unsigned)(units * 4)), dim3(64), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.c.nseg_max > 0) hipLaunchKernelGGL(gdn_output_kernel, chunks, dim3(NT), 0, st, p);

@@ -81,4 +81,65 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
 
+
+// ---- Direct global -> LDS loads and the transposing LDS read (gfx950).
+//
+// global_load_lds_dwordx4: every lane names its own 16-byte global source;
+// lane t's data lands at the wave-uniform LDS base (M0) + 16 t (the dword
+// form: + 4 t). Written as inline assembly so that the compiler adds no waits
+// of its own before later LDS reads (it cannot tell the target buffers apart
+// and would wait for every load in flight); callers order them with wait_vm_n.
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+__device__ __forceinline__ void gll16(const void *src, const char *lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_dst))), "v"(src)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void gll4(const void *src, const char *lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_dst))), "v"(src)
+                 : "memory", "m0");
+}
+
+// Wait until at most n (0 .. 63) vector-memory operations of this wave are
+// outstanding; they complete in issue order. n must be wave-uniform.
+__device__ __forceinline__ void wait_vm_n(int n) {
+    switch (n) {
+#define SGLA_W(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+        SGLA_W(1) SGLA_W(2) SGLA_W(3) SGLA_W(4) SGLA_W(5) SGLA_W(6) SGLA_W(7)
+        SGLA_W(8) SGLA_W(9) SGLA_W(10) SGLA_W(11) SGLA_W(12) SGLA_W(13) SGLA_W(14) SGLA_W(15)
+        SGLA_W(16) SGLA_W(17) SGLA_W(18) SGLA_W(19) SGLA_W(20) SGLA_W(21) SGLA_W(22) SGLA_W(23)
+        SGLA_W(24) SGLA_W(25) SGLA_W(26) SGLA_W(27) SGLA_W(28) SGLA_W(29) SGLA_W(30) SGLA_W(31)
+        SGLA_W(32) SGLA_W(33) SGLA_W(34) SGLA_W(35) SGLA_W(36) SGLA_W(37) SGLA_W(38) SGLA_W(39)
+        SGLA_W(40) SGLA_W(41) SGLA_W(42) SGLA_W(43) SGLA_W(44) SGLA_W(45) SGLA_W(46) SGLA_W(47)
+        SGLA_W(48) SGLA_W(49) SGLA_W(50) SGLA_W(51) SGLA_W(52) SGLA_W(53) SGLA_W(54) SGLA_W(55)
+        SGLA_W(56) SGLA_W(57) SGLA_W(58) SGLA_W(59) SGLA_W(60) SGLA_W(61) SGLA_W(62) SGLA_W(63)
+#undef SGLA_W
+        default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 8 bytes named by lane 4k + i / 4, for k = 0..3. With lane m of
+// the group naming row r0 + m / 4, columns c0 + 4 (m % 4) .. + 3 of a
+// row-major bf16 tile, lane i gets column c0 + i of rows r0 .. r0 + 3: four
+// consecutive rows of one column, as an MFMA operand needs them.
+typedef short sgla_v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_tr(const char *lds, int off) {
+    const sgla_v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) sgla_v4s *)((__attribute__((address_space(3))) char *)(lds + off)));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Byte offset, in a 64 x 128 bf16 row tile swizzled as row_off, of the 8 bytes
+// lane m of a 16-lane group names for the transposing read of rows r0 .. r0+3,
+// columns c0 .. c0+15 (r0 a multiple of 4, c0 a multiple of 16).
+__device__ __forceinline__ int tr_src(int r0, int c0, int m) {
+    const int r = r0 + (m >> 2);
+    const int cc = (c0 >> 3) + ((m & 3) >> 1);
+    return r * 256 + ((cc ^ (r & 15)) << 4) + 8 * (m & 1);
+}
+
 }  // namespace sgla

@@ -312,9 +312,11 @@ sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
 
     const size_t segs_b = table ? (size_t)nch * sizeof(SegEntry) : 0;
     const size_t seqs_b = table ? ((size_t)B * sizeof(SeqEntry) + 255) / 256 * 256 : 0;
-    // Per chunk and head: W (64 x 128 bf16) and U (64 x 128 fp32).
+    // Per chunk and head: W (64 x 128 bf16) and U (64 x 128 fp32), then
+    // new_v (64 x 128 bf16) for the output kernel.
     const size_t tiles_b = (size_t)nch * H * kChunk * 128 * (sizeof(uint16_t) + sizeof(float));
-    const size_t ws_b = segs_b + seqs_b + tiles_b;
+    const size_t nv_b = (size_t)nch * H * kChunk * 128 * sizeof(uint16_t);
+    const size_t ws_b = segs_b + seqs_b + tiles_b + nv_b;
     char *ws = nullptr;
     hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&ws), ws_b, st);
     if (e != hipSuccess) return SGLA_ERR_HIP;
@@ -338,6 +340,7 @@ sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
     p.c.nps = (int)nps64;
     p.beta = beta;
     p.tiles = ws + segs_b + seqs_b;
+    p.nvimg = ws + segs_b + seqs_b + tiles_b;
     if (table)
         e = launch_plan(cu_seqlens, B, T, kChunk, nch, reinterpret_cast<SegEntry *>(ws),
                         reinterpret_cast<SeqEntry *>(ws + segs_b), st);

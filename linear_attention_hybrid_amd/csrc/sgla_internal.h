@@ -133,7 +133,8 @@ struct GdnParams {
     ChunkParams c;      // q, k, v, g, s0, out, sfin, segs, seqs, H, nseg_max, N, scale, T, nps
     const float *beta;  // [tokens, H] write strength of each token
     char *tiles;        // [nseg_max, H] tiles of 48 KiB: W rows (bf16) and U^T (fp32) of each
-                        // chunk, later the chunk's start state and new_v for the output
+                        // chunk; U's slices later hold the chunk's start state for the output
+    char *nvimg;        // [nseg_max, H] 16 KiB: each chunk's new_v for the output
 };
 
 // Launchers (return hipSuccess or the launch error).
