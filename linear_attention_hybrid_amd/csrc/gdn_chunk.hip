@@ -54,7 +54,15 @@ constexpr int P_A = 49152;         // A fp32 [64][68], row-major; then T'' high 
 constexpr int A_ROW = 68 * 4;      // padded row (16-byte aligned, rows start 4 banks apart)
 constexpr int P_G = P_A + 64 * A_ROW;
 constexpr int P_B = P_G + 256;
-constexpr int P_BYTES = P_B + 256;
+constexpr int P_X = P_B + 256;     // per-wave 16 x 16 fp32 scratch block (4 x 1280 B)
+constexpr int P_BYTES = P_X + 4 * 1280;
+// T in 16 x 16 fp32 blocks (I, J), I >= J, rows of 80 bytes (20 floats: the
+// 16 rows of a block start 4 banks apart), in the K rows region once K K^T
+// is done.
+constexpr int TB_ROW = 80;
+constexpr int TB_BYTES = 16 * TB_ROW;
+__host__ __device__ constexpr int tb_off(int I, int J) { return (I * (I + 1) / 2 + J) * TB_BYTES; }
+static_assert(tb_off(3, 3) + TB_BYTES <= 16384, "T blocks exceed the K rows region");
 constexpr int P_TPH = 0;           // T' = T diag(beta exp(G)), [64 rows][128 B] bf16, high part
 constexpr int P_TPL = 8192;        // low part
 constexpr int P_TQH = P_A;         // T'' = T diag(beta), high part
@@ -78,6 +86,25 @@ __device__ __forceinline__ char *tile_at(const GdnParams &p, int64_t s, int h) {
     return p.tiles + ((int64_t)s * p.c.H + h) * TILE_BYTES;
 }
 
+
+// acc += L R for 16 x 16 fp32 blocks in LDS (row strides in bytes): this lane
+// takes row r = l / 4, columns c0 .. c0 + 3 with c0 = 4 (l % 4).
+__device__ __forceinline__ void blk_mac(const char *lds, int lL, int sL, int lR, int sR, int r,
+                                        int c0, float acc[4]) {
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+        const float4 a = lds_ld<float4>(lds, lL + r * sL + 16 * k4);
+        const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const float4 b = lds_ld<float4>(lds, lR + (4 * k4 + kk) * sR + 4 * c0);
+            acc[0] = fmaf(av[kk], b.x, acc[0]);
+            acc[1] = fmaf(av[kk], b.y, acc[1]);
+            acc[2] = fmaf(av[kk], b.z, acc[2]);
+            acc[3] = fmaf(av[kk], b.w, acc[3]);
+        }
+    }
+}
 
 __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     const int H = p.c.H;
@@ -172,24 +199,71 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     }
     __syncthreads();
 
-    // Row c = l of T = (I + A)^-1 by back substitution on (I + A)^T y = e_c:
-    // y_m = [m == c] - sum_{j > m} A[j][m] y_j. Right-looking: for j = 63
-    // down to 1, y_j is final and leaves -A[j][m] y_j in every y_m, m < j.
-    if (w == 0) {
-        float y[64];
+    // T = (I + A)^-1 in 16 x 16 blocks. The diagonal blocks first, one per
+    // wave: row r of T_ww solves (I + A_ww)^T y = e_r by right-looking back
+    // substitution (once y_j is final it leaves -A[j][m] y_j in every y_m,
+    // m < j; 15 dependent steps).
+    if (l < 16) {
+        float y[16];
 #pragma unroll
-        for (int m = 0; m < 64; ++m) y[m] = m == l ? 1.f : 0.f;
+        for (int m = 0; m < 16; ++m) y[m] = m == l ? 1.f : 0.f;
 #pragma unroll
-        for (int j = 63; j >= 1; --j) {
+        for (int j = 15; j >= 1; --j) {
 #pragma unroll
             for (int mq = 0; mq < j; mq += 4) {
-                const float4 a = lds_ld<float4>(lds, P_A + j * A_ROW + 4 * mq);
+                const float4 a = lds_ld<float4>(lds, P_A + (16 * w + j) * A_ROW + 4 * (16 * w + mq));
                 if (mq + 0 < j) y[mq + 0] = fmaf(-a.x, y[j], y[mq + 0]);
                 if (mq + 1 < j) y[mq + 1] = fmaf(-a.y, y[j], y[mq + 1]);
                 if (mq + 2 < j) y[mq + 2] = fmaf(-a.z, y[j], y[mq + 2]);
                 if (mq + 3 < j) y[mq + 3] = fmaf(-a.w, y[j], y[mq + 3]);
             }
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            lds_st(lds, tb_off(w, w) + l * TB_ROW + 16 * q,
+                   make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]));
+    }
+    __syncthreads();
+    // Then block row by block row: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,
+    // wave J taking column block J (waves J >= I wait at this level).
+    {
+        const int r = l >> 2;
+        const int c0 = 4 * (l & 3);
+#pragma unroll
+        for (int I = 1; I < 4; ++I) {
+            if (w < I) {
+                const int J = w;
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                for (int K = J; K < I; ++K)
+                    blk_mac(lds, P_A + 16 * I * A_ROW + 64 * K, A_ROW, tb_off(K, J), TB_ROW, r, c0, acc);
+                // X_J for this wave's own lanes (LDS in order within a wave).
+                lds_st(lds, P_X + 1280 * w + r * TB_ROW + 4 * c0, make_float4(acc[0], acc[1], acc[2], acc[3]));
+                float t[4] = {0.f, 0.f, 0.f, 0.f};
+                blk_mac(lds, tb_off(I, I), TB_ROW, P_X + 1280 * w, TB_ROW, r, c0, t);
+                lds_st(lds, tb_off(I, J) + r * TB_ROW + 4 * c0, make_float4(-t[0], -t[1], -t[2], -t[3]));
+            }
+            __syncthreads();
+        }
+    }
+
+    // Row c = l of T, in wave 0.
+    if (w == 0) {
+        float y[64];
+        const int I = l >> 4;
+        const int r = l & 15;
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool ok = J <= I;
+                const float4 v = lds_ld<float4>(lds, (ok ? tb_off(I, J) : 0) + r * TB_ROW + 16 * q);
+                y[16 * J + 4 * q + 0] = ok ? v.x : 0.f;
+                y[16 * J + 4 * q + 1] = ok ? v.y : 0.f;
+                y[16 * J + 4 * q + 2] = ok ? v.z : 0.f;
+                y[16 * J + 4 * q + 3] = ok ? v.w : 0.f;
+            }
+        // Every lane holds its row before any T' row overwrites the blocks.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         // T'[c][m] = y_m beta_m exp(G_m), T''[c][m] = y_m beta_m, each as a
         // bf16 high part and the bf16 rounding of the rest.
 #pragma unroll
