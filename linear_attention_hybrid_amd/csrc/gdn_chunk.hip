@@ -328,34 +328,35 @@ constexpr int HB_K = 16384;    // k rows [64][256 B], swizzled as row_off
 constexpr int HB_U = 32768;    // this block's U pieces: [8][64 lanes] x 16 B
 constexpr int HB_G = 40960;    // g[64] fp32 (rows past the chunk's end: the last row's)
 constexpr int H_BUF = HB_G + 256;
-constexpr int H_G = 2 * H_BUF; // G[64] fp32 of the current chunk
-constexpr int H_BYTES = H_G + 256;
-constexpr int H_STORES = 8 + 4;  // image stores per chunk (state, new_v)
+constexpr int H_XS = 2 * H_BUF;       // state operands exchanged: [wave 2][4][64 lanes] x 16 B
+constexpr int H_XN = H_XS + 8192;     // new_v high/low operands exchanged: [wave 2][4][64 lanes] x 16 B
+constexpr int H_G = H_XN + 8192;      // G[64] fp32 of the current chunk, one copy per wave
+constexpr int H_BYTES = H_G + 2 * 256;
+constexpr int H_STORES = 4 + 2;       // image stores per wave and chunk (state, new_v)
 
-// The state recurrence, one wave per (sequence, head, block of 32 value
-// columns): W and k of a chunk are read by the four blocks of a head (the
-// four workgroups sit on one XCD and share its L2), U, the state and the
-// images are the block's own. Lane l holds column 32b + l % 32 of the state,
-// key rows 32r + 8(v/4) + 4(l/32) + v%4 of accumulator S[r], element v.
+// The state recurrence of one (sequence, head, block of 32 value columns)
+// per workgroup of two waves: W and k of a chunk are read by the four blocks
+// of a head (the four workgroups sit on one XCD and share its L2); U, the
+// state and the images are the block's own. Wave a holds key rows
+// 64a .. 64a + 63 of the block's state (lane l: column 32b + l % 32 of the
+// head's value columns, key rows 32(2a + r) + 8(v/4) + 4(l/32) + v%4 of
+// accumulator S[r], element v) and forms new_v for tokens 32a .. 32a + 31.
 //
-// Chunk j + 1's W rows, k rows and U pieces stream into the other ring buffer
-// by direct global -> LDS loads while chunk j computes. new_v = U - W S comes
-// out of the MFMA with each lane holding one value column and, per group of
-// four, four consecutive tokens: converted in registers it is directly the
-// token-indexed operand of the update (exp(G_last - G) new_v as bf16 high and
-// low parts), whose other operand, K^T, comes from the k rows through the
-// transposing read in the same token order.
-__global__ __launch_bounds__(64) void gdn_chain_kernel(GdnParams p) {
+// Per chunk: the waves swap their halves of the state as bf16 operands, so
+// each forms new_v = U - W S for its token half over all key rows; then they
+// swap exp(G_last - G) new_v as bf16 high and low parts, so each updates its
+// key rows with all 64 tokens (K^T from the k rows through the transposing
+// read, in the token order new_v comes out in). Chunk j + 1's W rows, k
+// rows, U pieces and g stream into the other ring buffer by direct
+// global -> LDS loads meanwhile.
+// The work of wave WA (a compile-time index, so that every register array is
+// indexed by constants); both waves pass the same barriers in the same order.
+template <int WA>
+__device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, int cb, char *lds) {
+    constexpr int wa = WA;
     const int H = p.c.H;
-    int unit, cb;
-    xcd_unit_map(blockIdx.x, 4, unit, cb);
-    const int seq = unit / H;
-    const int h = unit - seq * H;
-    if (seq >= p.c.N) return;
     const SeqEntry sq = seq_at(p.c, seq);
-    __shared__ __attribute__((aligned(16))) char lds[H_BYTES];
-
-    const int l = threadIdx.x;
+    const int l = threadIdx.x & 63;
     const int ln = l & 31;
     const int lh = l >> 5;
     const int m16 = l & 15;
@@ -363,23 +364,23 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(GdnParams p) {
     const int64_t sl = (int64_t)D * D;
     const int64_t row_bytes = (int64_t)H * D * 2;
 
-    f32x16 S[4];
+    f32x16 S[2];
     {
         const float *src = p.c.s0 ? p.c.s0 + ((int64_t)seq * H + h) * sl : nullptr;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * b + 8 * (v >> 2) + 4 * lh + (v & 3);
-                S[b][v] = src ? src[dk * D + 32 * cb + ln] : 0.f;
+                const int dk = 32 * (2 * wa + r) + 8 * (v >> 2) + 4 * lh + (v & 3);
+                S[r][v] = src ? src[dk * D + 32 * cb + ln] : 0.f;
             }
         // Take the loaded values here, once: otherwise the compiler keeps
         // treating them as possibly in flight at the top of the chunk loop and
         // waits there for every load and store of the wave, prefetches included.
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) asm volatile("" : "+v"(S[b][v]));
+            for (int v = 0; v < 16; ++v) asm volatile("" : "+v"(S[r][v]));
     }
 
     // The sequence's chunks are consecutive tokens: its start and length come
@@ -394,6 +395,8 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(GdnParams p) {
         tok0 = seg_at(p.c, sq.first).tok0;
         len = (nch - 1) * kChunk + max(seg_at(p.c, sq.first + nch - 1).len, 0);
     }
+    // Each wave loads half of every tile: W and k rows 32a .. 32a + 31, the U
+    // pieces of its token half, and (wave 0) g.
     auto issue = [&](int j) {
         const int n = min(kChunk, len - kChunk * j);
         const int64_t t0 = tok0 + (int64_t)kChunk * j;
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(GdnParams p) {
         const char *tile = tile_at(p, sq.first + j, h);
         const char *kb = static_cast<const char *>(p.c.k) + (t0 * H + h) * (D * 2);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 8 * wa; i < 8 * wa + 8; ++i) {
             const int r = 4 * i + (l >> 4);
             const int pc = (m16 ^ (r & 15)) << 4;
             gll16(tile + r * 256 + pc, buf + HB_W + 1024 * i);
@@ -411,104 +414,120 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(GdnParams p) {
         // 4nt + q holds tokens 32nt + 8q + 4(l/32) .. + 3.
         const char *ub = tile + TILE_ELEMS * 2 + ((32 * cb + ln) * 64 + 4 * lh) * 4;
 #pragma unroll
-        for (int pc = 0; pc < 8; ++pc) gll16(ub + 32 * pc, buf + HB_U + 1024 * pc);
-        gll4(p.c.g + (t0 + min(l, n - 1)) * H + h, buf + HB_G);
+        for (int pc = 4 * wa; pc < 4 * wa + 4; ++pc) gll16(ub + 32 * pc, buf + HB_U + 1024 * pc);
+        if (wa == 0) gll4(p.c.g + (t0 + min(l, n - 1)) * H + h, buf + HB_G);
     };
 
     // Lane-constant parts of the transposing reads of K^T (rows 32b + l%32;
     // the two reads of an operand give tokens 4(l/32) + 0..3 and + 8 + 0..3
     // of each 16-token step, the order new_v comes out in).
-    int trk[4][2];
+    int trk[2][2];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) trk[b][hf] = tr_src(4 * (g16 >> 1) + 8 * hf, 32 * b + 16 * (g16 & 1), m16);
+        for (int hf = 0; hf < 2; ++hf)
+            trk[r][hf] = tr_src(4 * (g16 >> 1) + 8 * hf, 32 * (2 * wa + r) + 16 * (g16 & 1), m16);
 
     const bool any = len > 0;
     if (any) issue(0);
 
     for (int j = 0; any && j < nch; ++j) {
-        // Chunk j's loads are done once only the previous chunk's image
-        // stores, issued after them, may remain.
+        // This wave's loads of chunk j are done once only its image stores of
+        // the previous chunk, issued after them, may remain; the barrier then
+        // publishes both waves' halves.
         wait_vm_n(j > 0 ? H_STORES : 0);
+        __syncthreads();
         const char *buf = lds + (j & 1) * H_BUF;
+        if (j + 1 < nch) issue(j + 1);
         const int n = min(kChunk, len - kChunk * j);
         const float G = wave_prefix_sum(l < n ? lds_ld<float>(buf, HB_G + 4 * l) : 0.f);
         const float Gl = lane_value(G, 63);
-        lds_st(lds, H_G + 4 * l, G);
-        if (j + 1 < nch) issue(j + 1);
+        lds_st(lds, H_G + 256 * wa + 4 * l, G);
 
-        // W S for both token halves in one pass over the state: each bf16
-        // operand of S (key rows in accumulator order) is made, stored in the
-        // chunk's tile for the output kernel, and used at once.
-        const int64_t unit_chunk = (int64_t)(sq.first + j) * H + h;
+        // This wave's half of the state as bf16 operands (key rows in
+        // accumulator order): to the partner, and to the chunk's tile for
+        // the output kernel.
         char *simg = tile_at(p, sq.first + j, h) + IMG_S + cb * 8 * 64 * 16;
-        char *nimg = p.nvimg + unit_chunk * NV_BYTES + cb * 4 * 64 * 16;
-        f32x16 acc[2] = {{}, {}};
+        char *nimg = p.nvimg + ((int64_t)(sq.first + j) * H + h) * NV_BYTES + cb * 4 * 64 * 16;
+        bf16x8 sb[8];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int op = 4 * wa + 2 * r + s2;   // operand index 2b + s2, b = 2wa + r
+                bf16x8 x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = (__bf16)S[r][8 * s2 + e];
+                sb[op] = x;
+                lds_st(lds, H_XS + ((wa * 4 + 2 * r + s2) * 64 + l) * 16, x);
+                *reinterpret_cast<bf16x8 *>(simg + (op * 64 + l) * 16) = x;
+            }
+        __syncthreads();  // both halves of the state are exchanged
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            sb[4 * (1 - wa) + k] = lds_ld<bf16x8>(lds, H_XS + (((1 - wa) * 4 + k) * 64 + l) * 16);
+
+        // new_v = U - W S for token half nt = wa over all key rows.
+        const int nt = wa;
+        f32x16 acc = {};
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                bf16x8 sb;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) sb[e] = (__bf16)S[b][8 * s2 + e];
-                *reinterpret_cast<bf16x8 *>(simg + ((2 * b + s2) * 64 + l) * 16) = sb;
                 const int c = 4 * b + 2 * s2;
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    const int i = 32 * nt + ln;
-                    const bf16x4 x0 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c) + 8 * lh);
-                    const bf16x4 x1 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c + 1) + 8 * lh);
-                    acc[nt] = mfma(cat4(x0, x1), sb, acc[nt]);
-                }
+                const int i = 32 * nt + ln;
+                const bf16x4 x0 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c) + 8 * lh);
+                const bf16x4 x1 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c + 1) + 8 * lh);
+                acc = mfma(cat4(x0, x1), sb[2 * b + s2], acc);
             }
+        // Its bf16 image for the output kernel, and exp(G_last - G) new_v as
+        // high and low bf16 parts for both waves' updates.
+        bf16x8 nvo[2], nvh[4], nvl[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 u = lds_ld<float4>(buf, HB_U + (4 * nt + q) * 1024 + 16 * l);
+            const float uq[4] = {u.x, u.y, u.z, u.w};
+            // tokens 32nt + 8q + 4(l/32) + r of accumulator element 4q + r
+            const float4 Gt = lds_ld<float4>(lds, H_G + 256 * wa + 4 * (32 * nt + 8 * q + 4 * lh));
+            const float gt[4] = {Gt.x, Gt.y, Gt.z, Gt.w};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int v = 4 * q + r;
+                const float nv = uq[r] - acc[v];
+                const float x = nv * __expf(Gl - gt[r]);
+                const __bf16 xh = (__bf16)x;
+                nvo[v >> 3][v & 7] = (__bf16)nv;
+                nvh[2 * nt + (v >> 3)][v & 7] = xh;
+                nvl[2 * nt + (v >> 3)][v & 7] = (__bf16)(x - (float)xh);
+            }
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            *reinterpret_cast<bf16x8 *>(nimg + ((2 * nt + s2) * 64 + l) * 16) = nvo[s2];
+            lds_st(lds, H_XN + ((wa * 4 + s2) * 64 + l) * 16, nvh[2 * nt + s2]);
+            lds_st(lds, H_XN + ((wa * 4 + 2 + s2) * 64 + l) * 16, nvl[2 * nt + s2]);
+        }
+        __syncthreads();  // both token halves of new_v are exchanged
+        const int ot = 1 - wa;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            nvh[2 * ot + s2] = lds_ld<bf16x8>(lds, H_XN + ((ot * 4 + s2) * 64 + l) * 16);
+            nvl[2 * ot + s2] = lds_ld<bf16x8>(lds, H_XN + ((ot * 4 + 2 + s2) * 64 + l) * 16);
+        }
 
-        const bool update = j + 1 < nch || p.c.sfin;
-        if (update) {
+        if (j + 1 < nch || p.c.sfin) {
             const float a = __expf(Gl);
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int r = 0; r < 2; ++r) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) S[b][v] *= a;
-        }
-        // Per token half: new_v = U - W S, its bf16 image for the output
-        // kernel, and its share of the update with exp(G_last - G) new_v as
-        // high and low bf16 parts.
+                for (int v = 0; v < 16; ++v) S[r][v] *= a;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            bf16x8 nvo[2], nvh[2], nvl[2];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 u = lds_ld<float4>(buf, HB_U + (4 * nt + q) * 1024 + 16 * l);
-                const float uq[4] = {u.x, u.y, u.z, u.w};
-                // tokens 32nt + 8q + 4(l/32) + r of accumulator element 4q + r
-                const float4 Gt = lds_ld<float4>(lds, H_G + 4 * (32 * nt + 8 * q + 4 * lh));
-                const float gt[4] = {Gt.x, Gt.y, Gt.z, Gt.w};
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int v = 4 * q + r;
-                    const float nv = uq[r] - acc[nt][v];
-                    const float x = nv * __expf(Gl - gt[r]);
-                    const __bf16 xh = (__bf16)x;
-                    nvo[v >> 3][v & 7] = (__bf16)nv;
-                    nvh[v >> 3][v & 7] = xh;
-                    nvl[v >> 3][v & 7] = (__bf16)(x - (float)xh);
+                for (int st = 0; st < 4; ++st) {
+                    const bf16x8 kt = cat4(lds_tr(buf, HB_K + 4096 * st + trk[r][0]),
+                                           lds_tr(buf, HB_K + 4096 * st + trk[r][1]));
+                    S[r] = mfma(kt, nvh[st], S[r]);
+                    S[r] = mfma(kt, nvl[st], S[r]);
                 }
-            }
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                *reinterpret_cast<bf16x8 *>(nimg + ((2 * nt + s2) * 64 + l) * 16) = nvo[s2];
-            if (update) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        const int st = 2 * nt + s2;
-                        const bf16x8 kt = cat4(lds_tr(buf, HB_K + 4096 * st + trk[b][0]),
-                                               lds_tr(buf, HB_K + 4096 * st + trk[b][1]));
-                        S[b] = mfma(kt, nvh[s2], S[b]);
-                        S[b] = mfma(kt, nvl[s2], S[b]);
-                    }
             }
         }
     }
@@ -516,13 +535,24 @@ __global__ __launch_bounds__(64) void gdn_chain_kernel(GdnParams p) {
     if (p.c.sfin) {
         float *dst = p.c.sfin + ((int64_t)seq * H + h) * sl;
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * b + 8 * (v >> 2) + 4 * lh + (v & 3);
-                dst[dk * D + 32 * cb + ln] = S[b][v];
+                const int dk = 32 * (2 * wa + r) + 8 * (v >> 2) + 4 * lh + (v & 3);
+                dst[dk * D + 32 * cb + ln] = S[r][v];
             }
     }
+}
+
+__global__ __launch_bounds__(128) void gdn_chain_kernel(GdnParams p) {
+    int unit, cb;
+    xcd_unit_map(blockIdx.x, 4, unit, cb);
+    const int seq = unit / p.c.H;
+    const int h = unit - seq * p.c.H;
+    if (seq >= p.c.N) return;
+    __shared__ __attribute__((aligned(16))) char lds[H_BYTES];
+    if (threadIdx.x >> 6) chain_wave<1>(p, seq, h, cb, lds);
+    else chain_wave<0>(p, seq, h, cb, lds);
 }
 
 // ---- gdn_output_kernel LDS map (bytes).
@@ -673,7 +703,7 @@ hipError_t launch_gdn_chunk(const GdnParams &p, hipStream_t st) {
     // Four column blocks per (sequence, head), the units rounded up to whole
     // groups of eight so that xcd_unit_map covers them.
     const int64_t units = ((int64_t)p.c.N * p.c.H + 7) / 8 * 8;
-    hipLaunchKernelGGL(gdn_chain_kernel, dim3((unsigned)(units * 4)), dim3(64), 0, st, p);
+    hipLaunchKernelGGL(gdn_chain_kernel, dim3((unsigned)(units * 4)), dim3(128), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.c.nseg_max > 0) hipLaunchKernelGGL(gdn_output_kernel, chunks, dim3(NT), 0, st, p);
