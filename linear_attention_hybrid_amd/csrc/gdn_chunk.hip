@@ -558,14 +558,17 @@ __global__ __launch_bounds__(128) void gdn_chain_kernel(GdnParams p) {
 // ---- gdn_output_kernel LDS map (bytes).
 constexpr int O_Q = 0;       // Q rows [64][256 B]
 constexpr int O_K = 16384;   // K rows [64][256 B]; later the O staging rows
-constexpr int O_A = 32768;   // scores A[64 i][128 B]
-constexpr int O_G = 40960;   // G[64] fp32
+constexpr int O_A = 32768;   // scores A[64 i][128 B], bf16 high part
+constexpr int O_AL = 40960;  // low part
+constexpr int O_G = 49152;   // G[64] fp32
 constexpr int O_BYTES = O_G + 256;
 
 // One (chunk, head) per workgroup, all chunks at once:
 // O = scale ((Q * exp(G)) S + lower(Q K^T * Gamma) new_v), with S (the state
 // the chunk starts from) and new_v taken in bf16 from the chain kernel's
-// images. Wave w computes value columns [32w, 32w + 32) of O.
+// images, and the scores split into bf16 high and low parts (the product of
+// rounded scores and rounded new_v is the largest part of the bf16 error).
+// Wave w computes value columns [32w, 32w + 32) of O.
 __global__ __launch_bounds__(NT) void gdn_output_kernel(GdnParams p) {
     const int H = p.c.H;
     const int s = blockIdx.x / H;
@@ -644,8 +647,14 @@ __global__ __launch_bounds__(NT) void gdn_output_kernel(GdnParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 val[r] = (jr + r <= i) ? p.c.scale * __expf(Gi - gj[r]) * acc[4 * g4 + r] : 0.f;
+            // bf16 high part and the bf16 rounding of the rest
+            float lo[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) lo[r] = val[r] - round_bf16(val[r]);
             const u32x2 pk = {pack_f32(val[0], val[1]), pack_f32(val[2], val[3])};
+            const u32x2 pl = {pack_f32(lo[0], lo[1]), pack_f32(lo[2], lo[3])};
             lds_st(lds, O_A + tr_off(i, 4 * jb + g4) + 8 * lh, pk);
+            lds_st(lds, O_AL + tr_off(i, 4 * jb + g4) + 8 * lh, pl);
         }
     }
     __syncthreads();  // scores complete; K rows free for the O staging
@@ -671,7 +680,10 @@ __global__ __launch_bounds__(NT) void gdn_output_kernel(GdnParams p) {
             if (nt == 0 && st >= 2) break;
             const bf16x4 y0 = lds_ld<bf16x4>(lds, O_A + tr_off(i, 2 * st) + 8 * lh);
             const bf16x4 y1 = lds_ld<bf16x4>(lds, O_A + tr_off(i, 2 * st + 1) + 8 * lh);
+            const bf16x4 z0 = lds_ld<bf16x4>(lds, O_AL + tr_off(i, 2 * st) + 8 * lh);
+            const bf16x4 z1 = lds_ld<bf16x4>(lds, O_AL + tr_off(i, 2 * st + 1) + 8 * lh);
             acc = mfma(nvop[st], cat4(y0, y1), acc);
+            acc = mfma(nvop[st], cat4(z0, z1), acc);
         }
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {

@@ -174,3 +174,56 @@ def test_gdn_chunk_prefill_workload_sampled():
     ro, rS = oracle_gdn(inp, heads=heads)
     check(host(o[:, :, heads]), ro, "bf16", "gdn prefill o")
     check(host(S[:, heads]), rS, "bf16", "gdn prefill state", bf16_out=False)
+
+
+def _sample_heads(H, n, seed):
+    return np.sort(np.random.default_rng(seed).choice(H, size=n, replace=False))
+
+
+def test_gdn_long_continuation_and_split():
+    """The long-continuation shape (B=1, T=65536, H=32, Dk=Dv=128) from a
+    nonzero initial state, 1,024 chunks per chain; the oracle runs 2 seeded
+    heads in full. Split at 32768 and chained, the result is bit for bit the
+    same (the split falls on a chunk boundary)."""
+    say("gdn_chunk_fwd B=1 T=65536 H=32 D=128 S0 seed=6 (2 heads checked), split at 32768")
+    inp = W.make_prefill(1, 65536, 32, 128, 128, "bf16", "gdn", seed=6, device="cuda",
+                         init="normal", with_beta=True)
+    inp["initial_state"] = inp["initial_state"] * 25
+    o, S = sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                              initial_state=inp["initial_state"])
+    torch.cuda.synchronize()
+    heads = _sample_heads(32, 2, 6)
+    ro, rS = oracle_gdn(inp, heads=heads)
+    check(host(o[:, :, heads]), ro, "bf16", "gdn 64k o")
+    check(host(S[:, heads]), rS, "bf16", "gdn 64k state", bf16_out=False)
+    check_windows(host(o[0][:, heads]), ro[0], [0], "bf16", "gdn 64k o")
+    t = 32768
+    part = lambda x, a, b: inp[x][:, a:b].contiguous()
+    oa, Sa = sgla.gdn_chunk_fwd(*(part(x, 0, t) for x in ("q", "k", "v", "g", "beta")),
+                                initial_state=inp["initial_state"])
+    ob, Sb = sgla.gdn_chunk_fwd(*(part(x, t, 65536) for x in ("q", "k", "v", "g", "beta")),
+                                initial_state=Sa)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([oa, ob], dim=1), o)
+    assert torch.equal(Sb, S)
+
+
+def test_gdn_varlen_sampled():
+    """Eight packed sequences of log-uniform lengths in [512, 16384] rescaled to
+    65,536 tokens, H=32, each with its own initial state; the oracle runs 3
+    seeded heads, every sequence start windowed."""
+    lengths = W.varlen_lengths(8, 65536, 512, 16384, seed=8)
+    say("gdn_chunk_fwd varlen 8 seqs 65536 tokens H=32 seed=8 (3 heads)", list(lengths))
+    cu = W.cu_from_lengths(lengths)
+    inp = W.make_prefill(1, 65536, 32, 128, 128, "bf16", "gdn", seed=8, device="cuda",
+                         cu_seqlens=cu, init="normal", with_beta=True)
+    inp["initial_state"] = inp["initial_state"] * 25
+    o, S = sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                              initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    heads = _sample_heads(32, 3, 8)
+    ro, rS = oracle_gdn(inp, heads=heads)
+    check(host(o[:, :, heads]), ro, "bf16", "gdn varlen 64k o")
+    check(host(S[:, heads]), rS, "bf16", "gdn varlen 64k states", bf16_out=False)
+    check_windows(host(o[0][:, heads]), ro[0], [int(c) for c in cu[:-1]], "bf16",
+                  "gdn varlen 64k o", ends=[int(c) for c in cu[1:]])
