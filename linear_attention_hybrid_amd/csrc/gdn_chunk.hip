@@ -322,47 +322,174 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     }
 }
 
-// ---- gdn_chain_kernel: a ring of two chunk buffers in LDS (bytes).
+// ---- gdn_chain_kernel: a ring of H_RING chunk buffers in LDS (bytes).
 constexpr int HB_W = 0;        // W rows [64][256 B], swizzled as row_off
 constexpr int HB_K = 16384;    // k rows [64][256 B], swizzled as row_off
 constexpr int HB_U = 32768;    // this block's U pieces: [8][64 lanes] x 16 B
 constexpr int HB_G = 40960;    // g[64] fp32 (rows past the chunk's end: the last row's)
 constexpr int H_BUF = HB_G + 256;
-constexpr int H_XS = 2 * H_BUF;       // state operands exchanged: [wave 2][4][64 lanes] x 16 B
+constexpr int H_RING = 3;             // chunk j + 2 loads while chunk j computes
+constexpr int H_XS = H_RING * H_BUF;  // state operands: [wave 2][4][64 lanes] x 16 B (the state image)
 constexpr int H_XN = H_XS + 8192;     // new_v high/low operands exchanged: [wave 2][4][64 lanes] x 16 B
-constexpr int H_G = H_XN + 8192;      // G[64] fp32 of the current chunk, one copy per wave
+constexpr int H_NV = H_XN + 8192;     // bf16 new_v: [wave 2][2][64 lanes] x 16 B (the new_v image)
+constexpr int H_G = H_NV + 4096;      // G[64] fp32 of the current chunk, one copy per wave
 constexpr int H_BYTES = H_G + 2 * 256;
-constexpr int H_STORES = 4 + 2;       // image stores per wave and chunk (state, new_v)
+constexpr int H_MOVERS = 4;           // waves that move data (after the two compute waves)
+// The most operations a mover may leave outstanding at a chunk's start must
+// fit the wait instruction's counter.
+static_assert(4 / H_MOVERS + (H_RING - 2) * (2 * (16 / H_MOVERS) + 8 / H_MOVERS + 1 + 12 / H_MOVERS) <= 63,
+              "wait counts must fit vmcnt");
+
+// A sequence's chunks are consecutive tokens: its start and length come from
+// its first and last table rows, read once, so the chunk loop itself reads no
+// table entries (and the compiler adds no waits for them). nseg is at least 1
+// for a valid table (an empty sequence has one empty row); offsets that break
+// the rules can leave 0, and then no row is read.
+struct ChainSeq {
+    int first, nch, len;
+    int64_t tok0;
+};
+__device__ __forceinline__ ChainSeq chain_seq(const GdnParams &p, int seq) {
+    const SeqEntry sq = seq_at(p.c, seq);
+    ChainSeq c{sq.first, sq.nseg, 0, 0};
+    if (c.nch > 0) {
+        c.tok0 = seg_at(p.c, sq.first).tok0;
+        c.len = (c.nch - 1) * kChunk + max(seg_at(p.c, sq.first + c.nch - 1).len, 0);
+    }
+    return c;
+}
+
+// The chain workgroup has 2 + H_MOVERS waves. Waves 0 and 1 hold the state
+// and compute; the mover waves move every byte between HBM and LDS: chunk
+// j + 1's W rows, k rows, U pieces and g into the other ring buffer by direct
+// global -> LDS loads, and chunk j's state and new_v images from LDS to the
+// workspace, each mover an equal share. A wave that issues a load waits while
+// the memory path takes it, and one wave moves only about 20 bytes per ns
+// here, so the compute waves issue none and the movers split the bytes.
+//
+// A mover's order of vector-memory operations in chunk j, all counted by
+// vmcnt and completed in issue order: g (mover 0) and its W rows of chunk
+// j + H_RING - 1 (after the first barrier), its part of chunk j's state image,
+// its k rows (after the second), its U pieces and its part of chunk j's new_v
+// image (after the third). A chunk's loads are therefore done once at most
+// the operations issued after them remain outstanding.
+__device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, int cb, int mv, char *lds) {
+    const int H = p.c.H;
+    const ChainSeq c = chain_seq(p, seq);
+    const int l = threadIdx.x & 63;
+    const int ln = l & 31;
+    const int lh = l >> 5;
+    const int m16 = l & 15;
+    const int64_t row_bytes = (int64_t)H * D * 2;
+
+    auto issue_w = [&](int j) {  // g and W rows
+        const int n = min(kChunk, c.len - kChunk * j);
+        const int64_t t0 = c.tok0 + (int64_t)kChunk * j;
+        const char *buf = lds + (j % H_RING) * H_BUF;
+        const char *tile = tile_at(p, c.first + j, h);
+        if (mv == 0) gll4(p.c.g + (t0 + min(l, n - 1)) * H + h, buf + HB_G);
+#pragma unroll
+        for (int i = mv * (16 / H_MOVERS); i < (mv + 1) * (16 / H_MOVERS); ++i) {
+            const int r = 4 * i + (l >> 4);
+            gll16(tile + r * 256 + ((m16 ^ (r & 15)) << 4), buf + HB_W + 1024 * i);
+        }
+    };
+    auto issue_k = [&](int j) {  // k rows; rows past the chunk's end repeat its last row
+        const int n = min(kChunk, c.len - kChunk * j);
+        const int64_t t0 = c.tok0 + (int64_t)kChunk * j;
+        const char *buf = lds + (j % H_RING) * H_BUF;
+        const char *kb = static_cast<const char *>(p.c.k) + (t0 * H + h) * (D * 2);
+#pragma unroll
+        for (int i = mv * (16 / H_MOVERS); i < (mv + 1) * (16 / H_MOVERS); ++i) {
+            const int r = 4 * i + (l >> 4);
+            gll16(kb + min(r, n - 1) * row_bytes + ((m16 ^ (r & 15)) << 4), buf + HB_K + 1024 * i);
+        }
+    };
+    auto issue_u = [&](int j) {
+        // U^T pieces in accumulator order: value column 32cb + l%32, piece
+        // 4nt + q holds tokens 32nt + 8q + 4(l/32) .. + 3.
+        const char *buf = lds + (j % H_RING) * H_BUF;
+        const char *ub = tile_at(p, c.first + j, h) + TILE_ELEMS * 2 + ((32 * cb + ln) * 64 + 4 * lh) * 4;
+#pragma unroll
+        for (int pc = mv * (8 / H_MOVERS); pc < (mv + 1) * (8 / H_MOVERS); ++pc)
+            gll16(ub + 32 * pc, buf + HB_U + 1024 * pc);
+    };
+
+    constexpr int SK = 8 / H_MOVERS, NK = 4 / H_MOVERS;  // image stores per chunk
+    const int nload = 2 * (16 / H_MOVERS) + 8 / H_MOVERS + (mv == 0 ? 1 : 0);
+    // Operations this mover issues in chunk i.
+    auto ops = [&](int i) { return (i + H_RING - 1 < c.nch ? nload : 0) + SK + NK; };
+
+    if (c.len <= 0) return;
+    for (int j = 0; j < H_RING - 1 && j < c.nch; ++j) {
+        issue_w(j);
+        issue_k(j);
+        issue_u(j);
+    }
+    for (int j = 0; j < c.nch; ++j) {
+        // Operations issued after chunk j's last load: for the first chunks
+        // the later prologue loads and the chunks since; after that chunk
+        // j - H_RING + 1's new_v stores and the chunks since.
+        int after = 0;
+        if (j <= H_RING - 2) {
+            for (int i = j + 1; i <= H_RING - 2; ++i) after += i < c.nch ? nload : 0;
+            for (int i = 0; i < j; ++i) after += ops(i);
+        } else {
+            after = NK;
+            for (int i = j - H_RING + 2; i < j; ++i) after += ops(i);
+        }
+        wait_vm_n(__builtin_amdgcn_readfirstlane(after));
+        __syncthreads();  // chunk j is in LDS; chunk j - 1's buffer is free
+        const int jn = j + H_RING - 1;
+        const bool more = jn < c.nch;
+        if (more) issue_w(jn);
+        __syncthreads();  // the state operands are in H_XS
+        char *simg = tile_at(p, c.first + j, h) + IMG_S + cb * 8 * 64 * 16;
+        bf16x8 x[SK];
+#pragma unroll
+        for (int k = 0; k < SK; ++k) x[k] = lds_ld<bf16x8>(lds, H_XS + ((mv * SK + k) * 64 + l) * 16);
+#pragma unroll
+        for (int k = 0; k < SK; ++k)
+            *reinterpret_cast<bf16x8 *>(simg + ((mv * SK + k) * 64 + l) * 16) = x[k];
+        if (more) issue_k(jn);
+        __syncthreads();  // new_v is in H_NV
+        if (more) issue_u(jn);
+        char *nimg = p.nvimg + ((int64_t)(c.first + j) * H + h) * NV_BYTES + cb * 4 * 64 * 16;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) x[k] = lds_ld<bf16x8>(lds, H_NV + ((mv * NK + k) * 64 + l) * 16);
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+            *reinterpret_cast<bf16x8 *>(nimg + ((mv * NK + k) * 64 + l) * 16) = x[k];
+    }
+}
 
 // The state recurrence of one (sequence, head, block of 32 value columns)
-// per workgroup of two waves: W and k of a chunk are read by the four blocks
-// of a head (the four workgroups sit on one XCD and share its L2); U, the
-// state and the images are the block's own. Wave a holds key rows
-// 64a .. 64a + 63 of the block's state (lane l: column 32b + l % 32 of the
-// head's value columns, key rows 32(2a + r) + 8(v/4) + 4(l/32) + v%4 of
-// accumulator S[r], element v) and forms new_v for tokens 32a .. 32a + 31.
+// per workgroup: W and k of a chunk are read by the four blocks of a head
+// (the four workgroups sit on one XCD and share its L2); U, the state and the
+// images are the block's own. Compute wave a holds key rows 64a .. 64a + 63
+// of the block's state (lane l: column 32b + l % 32 of the head's value
+// columns, key rows 32(2a + r) + 8(v/4) + 4(l/32) + v%4 of accumulator S[r],
+// element v) and forms new_v for tokens 32a .. 32a + 31.
 //
-// Per chunk: the waves swap their halves of the state as bf16 operands, so
-// each forms new_v = U - W S for its token half over all key rows; then they
-// swap exp(G_last - G) new_v as bf16 high and low parts, so each updates its
-// key rows with all 64 tokens (K^T from the k rows through the transposing
-// read, in the token order new_v comes out in). Chunk j + 1's W rows, k
-// rows, U pieces and g stream into the other ring buffer by direct
-// global -> LDS loads meanwhile.
-// The work of wave WA (a compile-time index, so that every register array is
-// indexed by constants); both waves pass the same barriers in the same order.
+// Per chunk: the compute waves swap their halves of the state as bf16
+// operands, so each forms new_v = U - W S for its token half over all key
+// rows; then they swap exp(G_last - G) new_v as bf16 high and low parts, so
+// each updates its key rows with all 64 tokens (K^T from the k rows through
+// the transposing read, in the token order new_v comes out in).
+// The work of compute wave WA (a compile-time index, so that every register
+// array is indexed by constants); all three waves pass the same barriers in
+// the same order.
 template <int WA>
 __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, int cb, char *lds) {
     constexpr int wa = WA;
     const int H = p.c.H;
-    const SeqEntry sq = seq_at(p.c, seq);
+    const ChainSeq c = chain_seq(p, seq);
     const int l = threadIdx.x & 63;
     const int ln = l & 31;
     const int lh = l >> 5;
     const int m16 = l & 15;
     const int g16 = l >> 4;
     const int64_t sl = (int64_t)D * D;
-    const int64_t row_bytes = (int64_t)H * D * 2;
 
     f32x16 S[2];
     {
@@ -374,49 +501,7 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
                 const int dk = 32 * (2 * wa + r) + 8 * (v >> 2) + 4 * lh + (v & 3);
                 S[r][v] = src ? src[dk * D + 32 * cb + ln] : 0.f;
             }
-        // Take the loaded values here, once: otherwise the compiler keeps
-        // treating them as possibly in flight at the top of the chunk loop and
-        // waits there for every load and store of the wave, prefetches included.
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) asm volatile("" : "+v"(S[r][v]));
     }
-
-    // The sequence's chunks are consecutive tokens: its start and length come
-    // from its first and last table rows, read once, so the loop itself reads
-    // no table entries (and the compiler adds no waits for them).
-    // nseg is at least 1 for a valid table (an empty sequence has one empty
-    // row); offsets that break the rules can leave 0, and then no row is read.
-    const int nch = sq.nseg;
-    int64_t tok0 = 0;
-    int len = 0;
-    if (nch > 0) {
-        tok0 = seg_at(p.c, sq.first).tok0;
-        len = (nch - 1) * kChunk + max(seg_at(p.c, sq.first + nch - 1).len, 0);
-    }
-    // Each wave loads half of every tile: W and k rows 32a .. 32a + 31, the U
-    // pieces of its token half, and (wave 0) g.
-    auto issue = [&](int j) {
-        const int n = min(kChunk, len - kChunk * j);
-        const int64_t t0 = tok0 + (int64_t)kChunk * j;
-        const char *buf = lds + (j & 1) * H_BUF;
-        const char *tile = tile_at(p, sq.first + j, h);
-        const char *kb = static_cast<const char *>(p.c.k) + (t0 * H + h) * (D * 2);
-#pragma unroll
-        for (int i = 8 * wa; i < 8 * wa + 8; ++i) {
-            const int r = 4 * i + (l >> 4);
-            const int pc = (m16 ^ (r & 15)) << 4;
-            gll16(tile + r * 256 + pc, buf + HB_W + 1024 * i);
-            gll16(kb + min(r, n - 1) * row_bytes + pc, buf + HB_K + 1024 * i);
-        }
-        // U^T pieces in accumulator order: value column 32cb + l%32, piece
-        // 4nt + q holds tokens 32nt + 8q + 4(l/32) .. + 3.
-        const char *ub = tile + TILE_ELEMS * 2 + ((32 * cb + ln) * 64 + 4 * lh) * 4;
-#pragma unroll
-        for (int pc = 4 * wa; pc < 4 * wa + 4; ++pc) gll16(ub + 32 * pc, buf + HB_U + 1024 * pc);
-        if (wa == 0) gll4(p.c.g + (t0 + min(l, n - 1)) * H + h, buf + HB_G);
-    };
 
     // Lane-constant parts of the transposing reads of K^T (rows 32b + l%32;
     // the two reads of an operand give tokens 4(l/32) + 0..3 and + 8 + 0..3
@@ -428,27 +513,17 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
         for (int hf = 0; hf < 2; ++hf)
             trk[r][hf] = tr_src(4 * (g16 >> 1) + 8 * hf, 32 * (2 * wa + r) + 16 * (g16 & 1), m16);
 
-    const bool any = len > 0;
-    if (any) issue(0);
-
-    for (int j = 0; any && j < nch; ++j) {
-        // This wave's loads of chunk j are done once only its image stores of
-        // the previous chunk, issued after them, may remain; the barrier then
-        // publishes both waves' halves.
-        wait_vm_n(j > 0 ? H_STORES : 0);
-        __syncthreads();
-        const char *buf = lds + (j & 1) * H_BUF;
-        if (j + 1 < nch) issue(j + 1);
-        const int n = min(kChunk, len - kChunk * j);
+    const int nch = c.len > 0 ? c.nch : 0;
+    for (int j = 0; j < nch; ++j) {
+        __syncthreads();  // chunk j is in LDS
+        const char *buf = lds + (j % H_RING) * H_BUF;
+        const int n = min(kChunk, c.len - kChunk * j);
         const float G = wave_prefix_sum(l < n ? lds_ld<float>(buf, HB_G + 4 * l) : 0.f);
         const float Gl = lane_value(G, 63);
         lds_st(lds, H_G + 256 * wa + 4 * l, G);
 
         // This wave's half of the state as bf16 operands (key rows in
-        // accumulator order): to the partner, and to the chunk's tile for
-        // the output kernel.
-        char *simg = tile_at(p, sq.first + j, h) + IMG_S + cb * 8 * 64 * 16;
-        char *nimg = p.nvimg + ((int64_t)(sq.first + j) * H + h) * NV_BYTES + cb * 4 * 64 * 16;
+        // accumulator order), for the partner and for the state image.
         bf16x8 sb[8];
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -459,27 +534,28 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
 #pragma unroll
                 for (int e = 0; e < 8; ++e) x[e] = (__bf16)S[r][8 * s2 + e];
                 sb[op] = x;
-                lds_st(lds, H_XS + ((wa * 4 + 2 * r + s2) * 64 + l) * 16, x);
-                *reinterpret_cast<bf16x8 *>(simg + (op * 64 + l) * 16) = x;
+                lds_st(lds, H_XS + (op * 64 + l) * 16, x);
             }
         __syncthreads();  // both halves of the state are exchanged
 #pragma unroll
         for (int k = 0; k < 4; ++k)
             sb[4 * (1 - wa) + k] = lds_ld<bf16x8>(lds, H_XS + (((1 - wa) * 4 + k) * 64 + l) * 16);
 
-        // new_v = U - W S for token half nt = wa over all key rows.
+        // new_v = U - W S for token half nt = wa over all key rows, as two
+        // independent accumulation chains (key rows 0..63 and 64..127).
         const int nt = wa;
-        f32x16 acc = {};
+        f32x16 acc2[2] = {};
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const int c = 4 * b + 2 * s2;
+                const int cc = 4 * b + 2 * s2;
                 const int i = 32 * nt + ln;
-                const bf16x4 x0 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c) + 8 * lh);
-                const bf16x4 x1 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c + 1) + 8 * lh);
-                acc = mfma(cat4(x0, x1), sb[2 * b + s2], acc);
+                const bf16x4 x0 = lds_ld<bf16x4>(buf, HB_W + row_off(i, cc) + 8 * lh);
+                const bf16x4 x1 = lds_ld<bf16x4>(buf, HB_W + row_off(i, cc + 1) + 8 * lh);
+                acc2[b >> 1] = mfma(cat4(x0, x1), sb[2 * b + s2], acc2[b >> 1]);
             }
+        const f32x16 acc = acc2[0] + acc2[1];
         // Its bf16 image for the output kernel, and exp(G_last - G) new_v as
         // high and low bf16 parts for both waves' updates.
         bf16x8 nvo[2], nvh[4], nvl[4];
@@ -503,7 +579,7 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            *reinterpret_cast<bf16x8 *>(nimg + ((2 * nt + s2) * 64 + l) * 16) = nvo[s2];
+            lds_st(lds, H_NV + ((2 * nt + s2) * 64 + l) * 16, nvo[s2]);
             lds_st(lds, H_XN + ((wa * 4 + s2) * 64 + l) * 16, nvh[2 * nt + s2]);
             lds_st(lds, H_XN + ((wa * 4 + 2 + s2) * 64 + l) * 16, nvl[2 * nt + s2]);
         }
@@ -517,6 +593,9 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
 
         if (j + 1 < nch || p.c.sfin) {
             const float a = __expf(Gl);
+            // The low parts accumulate apart from the state, so each key-row
+            // block runs two independent chains.
+            f32x16 lo[2] = {};
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
 #pragma unroll
@@ -526,9 +605,11 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
                     const bf16x8 kt = cat4(lds_tr(buf, HB_K + 4096 * st + trk[r][0]),
                                            lds_tr(buf, HB_K + 4096 * st + trk[r][1]));
                     S[r] = mfma(kt, nvh[st], S[r]);
-                    S[r] = mfma(kt, nvl[st], S[r]);
+                    lo[r] = mfma(kt, nvl[st], lo[r]);
                 }
             }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) S[r] += lo[r];
         }
     }
 
@@ -544,14 +625,19 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
     }
 }
 
-__global__ __launch_bounds__(128) void gdn_chain_kernel(GdnParams p) {
+constexpr int H_THREADS = 64 * (2 + H_MOVERS);
+static_assert(H_MOVERS == 1 || H_MOVERS == 2 || H_MOVERS == 4, "movers split 4, 8 and 16 pieces evenly");
+
+__global__ __launch_bounds__(H_THREADS) void gdn_chain_kernel(GdnParams p) {
     int unit, cb;
     xcd_unit_map(blockIdx.x, 4, unit, cb);
     const int seq = unit / p.c.H;
     const int h = unit - seq * p.c.H;
     if (seq >= p.c.N) return;
     __shared__ __attribute__((aligned(16))) char lds[H_BYTES];
-    if (threadIdx.x >> 6) chain_wave<1>(p, seq, h, cb, lds);
+    const int w = threadIdx.x >> 6;
+    if (w >= 2) chain_mover(p, seq, h, cb, w - 2, lds);
+    else if (w == 1) chain_wave<1>(p, seq, h, cb, lds);
     else chain_wave<0>(p, seq, h, cb, lds);
 }
 
@@ -715,7 +801,7 @@ hipError_t launch_gdn_chunk(const GdnParams &p, hipStream_t st) {
     // Four column blocks per (sequence, head), the units rounded up to whole
     // groups of eight so that xcd_unit_map covers them.
     const int64_t units = ((int64_t)p.c.N * p.c.H + 7) / 8 * 8;
-    hipLaunchKernelGGL(gdn_chain_kernel, dim3((unsigned)(units * 4)), dim3(128), 0, st, p);
+    hipLaunchKernelGGL(gdn_chain_kernel, dim3((unsigned)(units * 4)), dim3(H_THREADS), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.c.nseg_max > 0) hipLaunchKernelGGL(gdn_output_kernel, chunks, dim3(NT), 0, st, p);
