@@ -70,15 +70,19 @@ constexpr int P_TQL = P_A + 8192;  // low part
 static_assert(P_TQL + 8192 <= P_G, "T'' parts overlap the gate tables");
 
 // Per chunk and head the workspace tile holds W (16 KiB bf16 rows) and U
-// (32 KiB fp32, value-major: the 8 KiB of value columns 32b .. 32b + 31 are
-// read only by the chain workgroup of column block b). Once that workgroup
+// (32 KiB fp32, as [block b][piece p][lane l] x 16 B: lane l of piece p holds
+// tokens 8p + 4(l/32) .. + 3 of value column 32b + l % 32, the order the chain
+// kernel's accumulators use, so each 1 KiB piece is one contiguous load; the
+// 8 KiB of block b are read only by the chain workgroup of column block b).
+// Once that workgroup
 // has taken its U slice it stores there the chunk's start state for its
 // columns, in bf16, as the register image of the output kernel's MFMA operand
 // (16 bytes per lane and operand, lanes consecutive). The chunk's bf16 new_v
 // goes, as an image too, to a separate 16 KiB per chunk and head.
 constexpr int TILE_ELEMS = 64 * D;                 // bf16 elements of W; U is as many floats
+constexpr int T_U = TILE_ELEMS * 2;                 // byte offset of U
 constexpr int TILE_BYTES = 3 * TILE_ELEMS * 2;      // W + U = 48 KiB
-constexpr int IMG_S = TILE_ELEMS * 2;               // state image: [block 4][8 operands][64 lanes] x 16 B
+constexpr int IMG_S = T_U;                          // state image: [block 4][8 operands][64 lanes] x 16 B
 constexpr int NV_BYTES = 4 * 4 * 64 * 16;           // new_v image: [block 4][4 operands][64 lanes] x 16 B
 static_assert(IMG_S + 4 * 8 * 64 * 16 == TILE_BYTES, "state image must fill the U slices");
 
@@ -293,10 +297,10 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     __syncthreads();
 
     // Wave w: W^T = K^T T'^T for dk rows [32w, 32w + 32) (stored as W rows,
-    // token-major), and U = T'' V for value columns [32w, 32w + 32) (stored
-    // as U^T rows, value-major, fp32). Rows past the chunk's end come out zero.
+    // token-major), and U = T'' V for value columns [32w, 32w + 32) (fp32, in
+    // the pieces of column block w). Rows past the chunk's end come out zero.
     uint16_t *wt = reinterpret_cast<uint16_t *>(tile_at(p, s, h));
-    float *ut = reinterpret_cast<float *>(tile_at(p, s, h) + TILE_ELEMS * 2);
+    float *ut = reinterpret_cast<float *>(tile_at(p, s, h) + T_U);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
         f32x16 aw = {}, au = {};
@@ -311,12 +315,11 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
             au = mfma(lds_ld<bf16x8>(lds, P_TQL + tr_off(ti, 2 * st + lh)), vt, au);
         }
         const int i = 32 * nt + ln;
-        const int dv = 32 * w + ln;
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const u32x2 pw = {pack_f32(aw[4 * g4], aw[4 * g4 + 1]), pack_f32(aw[4 * g4 + 2], aw[4 * g4 + 3])};
             *reinterpret_cast<u32x2 *>(wt + i * D + 32 * w + 8 * g4 + 4 * lh) = pw;
-            *reinterpret_cast<float4 *>(ut + dv * 64 + 32 * nt + 8 * g4 + 4 * lh) =
+            *reinterpret_cast<float4 *>(ut + ((w * 8 + 4 * nt + g4) * 64 + l) * 4) =
                 make_float4(au[4 * g4], au[4 * g4 + 1], au[4 * g4 + 2], au[4 * g4 + 3]);
         }
     }
@@ -332,13 +335,9 @@ constexpr int H_RING = 3;             // chunk j + 2 loads while chunk j compute
 constexpr int H_XS = H_RING * H_BUF;  // state operands: [wave 2][4][64 lanes] x 16 B (the state image)
 constexpr int H_XN = H_XS + 8192;     // new_v high/low operands exchanged: [wave 2][4][64 lanes] x 16 B
 constexpr int H_NV = H_XN + 8192;     // bf16 new_v: [wave 2][2][64 lanes] x 16 B (the new_v image)
-constexpr int H_G = H_NV + 4096;      // G[64] fp32 of the current chunk, one copy per wave
+constexpr int H_G = H_NV + 4096;      // exp(G_last - G)[64] fp32 of the current chunk, one copy per wave
 constexpr int H_BYTES = H_G + 2 * 256;
 constexpr int H_MOVERS = 4;           // waves that move data (after the two compute waves)
-// The most operations a mover may leave outstanding at a chunk's start must
-// fit the wait instruction's counter.
-static_assert(4 / H_MOVERS + (H_RING - 2) * (2 * (16 / H_MOVERS) + 8 / H_MOVERS + 1 + 12 / H_MOVERS) <= 63,
-              "wait counts must fit vmcnt");
 
 // A sequence's chunks are consecutive tokens: its start and length come from
 // its first and last table rows, read once, so the chunk loop itself reads no
@@ -361,38 +360,40 @@ __device__ __forceinline__ ChainSeq chain_seq(const GdnParams &p, int seq) {
 
 // The chain workgroup has 2 + H_MOVERS waves. Waves 0 and 1 hold the state
 // and compute; the mover waves move every byte between HBM and LDS: chunk
-// j + 1's W rows, k rows, U pieces and g into the other ring buffer by direct
-// global -> LDS loads, and chunk j's state and new_v images from LDS to the
-// workspace, each mover an equal share. A wave that issues a load waits while
-// the memory path takes it, and one wave moves only about 20 bytes per ns
-// here, so the compute waves issue none and the movers split the bytes.
+// j + 2's W rows, k rows, U pieces and g into the ring by direct global ->
+// LDS loads, and chunk j's state and new_v images from LDS to the workspace,
+// each mover an equal share. A wave is held at each load it issues while the
+// memory path takes it (one wave moves about 20 bytes per ns this way), so
+// the compute waves issue none and the movers split the bytes.
 //
-// A mover's order of vector-memory operations in chunk j, all counted by
-// vmcnt and completed in issue order: g (mover 0) and its W rows of chunk
-// j + H_RING - 1 (after the first barrier), its part of chunk j's state image,
-// its k rows (after the second), its U pieces and its part of chunk j's new_v
-// image (after the third). A chunk's loads are therefore done once at most
-// the operations issued after them remain outstanding.
+// vmcnt counts every operation a wave issues and they complete in issue
+// order, so a chunk's loads are done once at most the operations issued
+// after its last load remain outstanding; each mover keeps that count.
 __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, int cb, int mv, char *lds) {
+    static_assert(H_RING == 3, "the mover keeps the counts of two chunks in flight");
+    constexpr int M = H_MOVERS;
     const int H = p.c.H;
     const ChainSeq c = chain_seq(p, seq);
     const int l = threadIdx.x & 63;
-    const int ln = l & 31;
-    const int lh = l >> 5;
     const int m16 = l & 15;
     const int64_t row_bytes = (int64_t)H * D * 2;
+    int issued = 0;  // vector-memory operations this wave has issued
 
     auto issue_w = [&](int j) {  // g and W rows
         const int n = min(kChunk, c.len - kChunk * j);
         const int64_t t0 = c.tok0 + (int64_t)kChunk * j;
         const char *buf = lds + (j % H_RING) * H_BUF;
         const char *tile = tile_at(p, c.first + j, h);
-        if (mv == 0) gll4(p.c.g + (t0 + min(l, n - 1)) * H + h, buf + HB_G);
+        if (mv == 0) {
+            gll4(p.c.g + (t0 + min(l, n - 1)) * H + h, buf + HB_G);
+            ++issued;
+        }
 #pragma unroll
-        for (int i = mv * (16 / H_MOVERS); i < (mv + 1) * (16 / H_MOVERS); ++i) {
+        for (int i = mv * (16 / M); i < (mv + 1) * (16 / M); ++i) {
             const int r = 4 * i + (l >> 4);
             gll16(tile + r * 256 + ((m16 ^ (r & 15)) << 4), buf + HB_W + 1024 * i);
         }
+        issued += 16 / M;
     };
     auto issue_k = [&](int j) {  // k rows; rows past the chunk's end repeat its last row
         const int n = min(kChunk, c.len - kChunk * j);
@@ -400,66 +401,66 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
         const char *buf = lds + (j % H_RING) * H_BUF;
         const char *kb = static_cast<const char *>(p.c.k) + (t0 * H + h) * (D * 2);
 #pragma unroll
-        for (int i = mv * (16 / H_MOVERS); i < (mv + 1) * (16 / H_MOVERS); ++i) {
+        for (int i = mv * (16 / M); i < (mv + 1) * (16 / M); ++i) {
             const int r = 4 * i + (l >> 4);
             gll16(kb + min(r, n - 1) * row_bytes + ((m16 ^ (r & 15)) << 4), buf + HB_K + 1024 * i);
         }
+        issued += 16 / M;
     };
     auto issue_u = [&](int j) {
-        // U^T pieces in accumulator order: value column 32cb + l%32, piece
+        // U pieces in accumulator order: value column 32cb + l%32, piece
         // 4nt + q holds tokens 32nt + 8q + 4(l/32) .. + 3.
         const char *buf = lds + (j % H_RING) * H_BUF;
-        const char *ub = tile_at(p, c.first + j, h) + TILE_ELEMS * 2 + ((32 * cb + ln) * 64 + 4 * lh) * 4;
+        const char *ub = tile_at(p, c.first + j, h) + T_U + cb * 8192 + 16 * l;
 #pragma unroll
-        for (int pc = mv * (8 / H_MOVERS); pc < (mv + 1) * (8 / H_MOVERS); ++pc)
-            gll16(ub + 32 * pc, buf + HB_U + 1024 * pc);
+        for (int pc = mv * (8 / M); pc < (mv + 1) * (8 / M); ++pc)
+            gll16(ub + 1024 * pc, buf + HB_U + 1024 * pc);
+        issued += 8 / M;
     };
-
-    constexpr int SK = 8 / H_MOVERS, NK = 4 / H_MOVERS;  // image stores per chunk
-    const int nload = 2 * (16 / H_MOVERS) + 8 / H_MOVERS + (mv == 0 ? 1 : 0);
-    // Operations this mover issues in chunk i.
-    auto ops = [&](int i) { return (i + H_RING - 1 < c.nch ? nload : 0) + SK + NK; };
-
     if (c.len <= 0) return;
-    for (int j = 0; j < H_RING - 1 && j < c.nch; ++j) {
-        issue_w(j);
-        issue_k(j);
-        issue_u(j);
+    // issued-counts after the last load of chunks j and j + 1
+    issue_w(0);
+    issue_k(0);
+    issue_u(0);
+    int mark0 = issued;
+    if (c.nch > 1) {
+        issue_w(1);
+        issue_k(1);
+        issue_u(1);
     }
+    int mark1 = issued;
+
     for (int j = 0; j < c.nch; ++j) {
-        // Operations issued after chunk j's last load: for the first chunks
-        // the later prologue loads and the chunks since; after that chunk
-        // j - H_RING + 1's new_v stores and the chunks since.
-        int after = 0;
-        if (j <= H_RING - 2) {
-            for (int i = j + 1; i <= H_RING - 2; ++i) after += i < c.nch ? nload : 0;
-            for (int i = 0; i < j; ++i) after += ops(i);
-        } else {
-            after = NK;
-            for (int i = j - H_RING + 2; i < j; ++i) after += ops(i);
-        }
-        wait_vm_n(__builtin_amdgcn_readfirstlane(after));
+        wait_vm_n(__builtin_amdgcn_readfirstlane(min(issued - mark0, 63)));
         __syncthreads();  // chunk j is in LDS; chunk j - 1's buffer is free
-        const int jn = j + H_RING - 1;
+        const int jn = j + 2;
         const bool more = jn < c.nch;
         if (more) issue_w(jn);
         __syncthreads();  // the state operands are in H_XS
         char *simg = tile_at(p, c.first + j, h) + IMG_S + cb * 8 * 64 * 16;
-        bf16x8 x[SK];
+        bf16x8 x[8 / M];
 #pragma unroll
-        for (int k = 0; k < SK; ++k) x[k] = lds_ld<bf16x8>(lds, H_XS + ((mv * SK + k) * 64 + l) * 16);
+        for (int t = 0; t < 8 / M; ++t) x[t] = lds_ld<bf16x8>(lds, H_XS + ((mv + M * t) * 64 + l) * 16);
 #pragma unroll
-        for (int k = 0; k < SK; ++k)
-            *reinterpret_cast<bf16x8 *>(simg + ((mv * SK + k) * 64 + l) * 16) = x[k];
+        for (int t = 0; t < 8 / M; ++t)
+            *reinterpret_cast<bf16x8 *>(simg + ((mv + M * t) * 64 + l) * 16) = x[t];
+        issued += 8 / M;
         if (more) issue_k(jn);
         __syncthreads();  // new_v is in H_NV
         if (more) issue_u(jn);
+        const int mark2 = issued;
         char *nimg = p.nvimg + ((int64_t)(c.first + j) * H + h) * NV_BYTES + cb * 4 * 64 * 16;
 #pragma unroll
-        for (int k = 0; k < NK; ++k) x[k] = lds_ld<bf16x8>(lds, H_NV + ((mv * NK + k) * 64 + l) * 16);
-#pragma unroll
-        for (int k = 0; k < NK; ++k)
-            *reinterpret_cast<bf16x8 *>(nimg + ((mv * NK + k) * 64 + l) * 16) = x[k];
+        for (int t = 0; t < (4 + M - 1) / M; ++t) {
+            const int k = mv + M * t;
+            if (k < 4) {
+                x[t] = lds_ld<bf16x8>(lds, H_NV + (k * 64 + l) * 16);
+                *reinterpret_cast<bf16x8 *>(nimg + (k * 64 + l) * 16) = x[t];
+                ++issued;
+            }
+        }
+        mark0 = mark1;
+        mark1 = mark2;
     }
 }
 
@@ -520,7 +521,9 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
         const int n = min(kChunk, c.len - kChunk * j);
         const float G = wave_prefix_sum(l < n ? lds_ld<float>(buf, HB_G + 4 * l) : 0.f);
         const float Gl = lane_value(G, 63);
-        lds_st(lds, H_G + 256 * wa + 4 * l, G);
+        // exp(G_last - G) of token l, once per token rather than once per
+        // element of new_v
+        lds_st(lds, H_G + 256 * wa + 4 * l, __expf(Gl - G));
 
         // This wave's half of the state as bf16 operands (key rows in
         // accumulator order), for the partner and for the state image.
@@ -564,13 +567,13 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
             const float4 u = lds_ld<float4>(buf, HB_U + (4 * nt + q) * 1024 + 16 * l);
             const float uq[4] = {u.x, u.y, u.z, u.w};
             // tokens 32nt + 8q + 4(l/32) + r of accumulator element 4q + r
-            const float4 Gt = lds_ld<float4>(lds, H_G + 256 * wa + 4 * (32 * nt + 8 * q + 4 * lh));
-            const float gt[4] = {Gt.x, Gt.y, Gt.z, Gt.w};
+            const float4 Et = lds_ld<float4>(lds, H_G + 256 * wa + 4 * (32 * nt + 8 * q + 4 * lh));
+            const float et[4] = {Et.x, Et.y, Et.z, Et.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int v = 4 * q + r;
                 const float nv = uq[r] - acc[v];
-                const float x = nv * __expf(Gl - gt[r]);
+                const float x = nv * et[r];
                 const __bf16 xh = (__bf16)x;
                 nvo[v >> 3][v & 7] = (__bf16)nv;
                 nvh[2 * nt + (v >> 3)][v & 7] = xh;
@@ -593,9 +596,6 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
 
         if (j + 1 < nch || p.c.sfin) {
             const float a = __expf(Gl);
-            // The low parts accumulate apart from the state, so each key-row
-            // block runs two independent chains.
-            f32x16 lo[2] = {};
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
 #pragma unroll
@@ -605,11 +605,9 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
                     const bf16x8 kt = cat4(lds_tr(buf, HB_K + 4096 * st + trk[r][0]),
                                            lds_tr(buf, HB_K + 4096 * st + trk[r][1]));
                     S[r] = mfma(kt, nvh[st], S[r]);
-                    lo[r] = mfma(kt, nvl[st], lo[r]);
+                    S[r] = mfma(kt, nvl[st], S[r]);
                 }
             }
-#pragma unroll
-            for (int r = 0; r < 2; ++r) S[r] += lo[r];
         }
     }
 
@@ -626,7 +624,8 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
 }
 
 constexpr int H_THREADS = 64 * (2 + H_MOVERS);
-static_assert(H_MOVERS == 1 || H_MOVERS == 2 || H_MOVERS == 4, "movers split 4, 8 and 16 pieces evenly");
+static_assert(H_MOVERS == 1 || H_MOVERS == 2 || H_MOVERS == 4 || H_MOVERS == 8,
+              "movers split 8 and 16 pieces evenly");
 
 __global__ __launch_bounds__(H_THREADS) void gdn_chain_kernel(GdnParams p) {
     int unit, cb;
