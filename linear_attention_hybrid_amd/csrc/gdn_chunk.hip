@@ -28,15 +28,15 @@
 // into the state keeps about 16 bits. The output products use bf16 operands
 // (state, scores, new_v) as the Simple GLA kernels do.
 //
-// The inverse T is found in fp32 by back substitution on (I + A)^T, whose
-// solution for unit vector e_c is row c of T: lane c of one wave computes row
-// c and writes it contiguously, 64 lanes, 64 rows, no transposition. The
-// substitution is right-looking: as soon as y_j is final it is taken out of
-// every y_m, m < j, so the dependent chain is 64 steps long and each step's
-// updates are independent of one another. The column scalings beta exp(G)
-// and beta are folded into T, which is then split into a bf16 high and low
-// part, so W and U come from exact bf16 K and V times a T accurate to about
-// 2^-16.
+// The inverse T is found in fp32 in 16 x 16 blocks. Each wave inverts one
+// diagonal block by back substitution on its transpose, whose solution for
+// unit vector e_r is row r of the block's inverse (right-looking: as soon as
+// y_j is final it is taken out of every y_m, m < j; 15 dependent steps).
+// The blocks below the diagonal follow block row by block row,
+// T_IJ = -T_II sum_K A_IK T_KJ, on fp32 16 x 16 x 4 MFMAs. The column
+// scalings beta exp(G) and beta are folded into T, which is then split into
+// a bf16 high and low part, so W and U come from exact bf16 K and V times a
+// T accurate to about 2^-16.
 #include "mfma_tile.h"
 
 namespace sgla {
@@ -45,6 +45,7 @@ namespace {
 
 constexpr int D = 128;
 constexpr int NT = 256;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // ---- gdn_prep_kernel LDS map (bytes).
 constexpr int P_K = 0;             // K rows [64][256 B]; then T' high and low parts
@@ -54,7 +55,8 @@ constexpr int P_A = 49152;         // A fp32 [64][68], row-major; then T'' high 
 constexpr int A_ROW = 68 * 4;      // padded row (16-byte aligned, rows start 4 banks apart)
 constexpr int P_G = P_A + 64 * A_ROW;
 constexpr int P_B = P_G + 256;
-constexpr int P_X = P_B + 256;     // per-wave 16 x 16 fp32 scratch block (4 x 1280 B)
+constexpr int P_E = P_B + 256;     // exp(G) per token
+constexpr int P_X = P_E + 256;     // per-wave 16 x 16 fp32 scratch block (4 x 1280 B)
 constexpr int P_BYTES = P_X + 4 * 1280;
 // T in 16 x 16 fp32 blocks (I, J), I >= J, rows of 80 bytes (20 floats: the
 // 16 rows of a block start 4 banks apart), in the K rows region once K K^T
@@ -91,33 +93,12 @@ __device__ __forceinline__ char *tile_at(const GdnParams &p, int64_t s, int h) {
 }
 
 
-// acc += L R for 16 x 16 fp32 blocks in LDS (row strides in bytes): this lane
-// takes row r = l / 4, columns c0 .. c0 + 3 with c0 = 4 (l % 4).
-__device__ __forceinline__ void blk_mac(const char *lds, int lL, int sL, int lR, int sR, int r,
-                                        int c0, float acc[4]) {
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-        const float4 a = lds_ld<float4>(lds, lL + r * sL + 16 * k4);
-        const float av[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const float4 b = lds_ld<float4>(lds, lR + (4 * k4 + kk) * sR + 4 * c0);
-            acc[0] = fmaf(av[kk], b.x, acc[0]);
-            acc[1] = fmaf(av[kk], b.y, acc[1]);
-            acc[2] = fmaf(av[kk], b.z, acc[2]);
-            acc[3] = fmaf(av[kk], b.w, acc[3]);
-        }
-    }
-}
-
-__global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
+// Persistent: workgroup b takes the (chunk, head) items b, b + gridDim.x, ...
+// in chunk-major order, and loads the next item's k and v rows, g and beta
+// into registers while it works on the current one, so that their latency is
+// hidden behind that work.
+__global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
     const int H = p.c.H;
-    const int s = blockIdx.x / H;
-    const int h = blockIdx.x - s * H;
-    if (s >= p.c.nseg_max) return;
-    const SegEntry se = seg_at(p.c, s);
-    if (se.len <= 0) return;
-    const int n = se.len;  // <= 64
     __shared__ __attribute__((aligned(16))) char lds[P_BYTES];
 
     const int tid = threadIdx.x;
@@ -127,47 +108,74 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     const int lh = l >> 5;
     const int cidx = tid & 15;
     const int prb = (tid >> 4) & 15;
-
-    // K and V rows: each thread moves two row pairs of 16-byte pieces.
-    const int64_t base = (se.tok0 * H + h) * D;
-    const uint16_t *kg = static_cast<const uint16_t *>(p.c.k) + base;
-    const uint16_t *vg = static_cast<const uint16_t *>(p.c.v) + base;
     const int64_t row_stride = (int64_t)H * D;
+
+    // An item's k and v rows (each thread two row pairs of 16-byte pieces;
+    // zero past the chunk's end), g and beta.
     u32x4 kr[2][2], vr[2][2];
-#pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int r = 2 * (prb + 16 * it) + rr;
-            const bool ok = r < n;
-            kr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(kg + r * row_stride + 8 * cidx) : u32x4{0, 0, 0, 0};
-            vr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(vg + r * row_stride + 8 * cidx) : u32x4{0, 0, 0, 0};
+    float gv, bv;
+    int fn;  // the fetched item's token count
+    auto fetch = [&](int item) {
+        int n = 0, hh = 0;
+        int64_t tok0 = 0;
+        if (item < nitems) {
+            const int s = item / H;
+            hh = item - s * H;
+            const SegEntry se = seg_at(p.c, s);
+            n = se.len;
+            tok0 = se.tok0;
         }
-    const float gv = l < n ? p.c.g[(se.tok0 + l) * H + h] : 0.f;
-    const float bv = l < n ? p.beta[(se.tok0 + l) * H + h] : 0.f;
-    const float G = wave_prefix_sum(gv);
-    if (w == 0) {
-        lds_st(lds, P_G + 4 * l, G);
-        lds_st(lds, P_B + 4 * l, bv);
-    }
+        const int64_t base = (tok0 * H + hh) * D;
+        const uint16_t *kg = static_cast<const uint16_t *>(p.c.k) + base;
+        const uint16_t *vg = static_cast<const uint16_t *>(p.c.v) + base;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+        for (int it = 0; it < 2; ++it)
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
-            lds_st(lds, P_K + row_off(2 * (prb + 16 * it) + rr, cidx), kr[it][rr]);
-        const int r0 = 2 * (prb + 16 * it);
-        const int cb = (r0 & 7) * 2;  // byte offset of the token pair inside its 8-token piece
+            for (int rr = 0; rr < 2; ++rr) {
+                const int r = 2 * (prb + 16 * it) + rr;
+                const bool ok = r < n;
+                kr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(kg + r * row_stride + 8 * cidx) : u32x4{0, 0, 0, 0};
+                vr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(vg + r * row_stride + 8 * cidx) : u32x4{0, 0, 0, 0};
+            }
+        gv = l < n ? p.c.g[(tok0 + l) * H + hh] : 0.f;
+        bv = l < n ? p.beta[(tok0 + l) * H + hh] : 0.f;
+        fn = __builtin_amdgcn_readfirstlane(n);
+    };
+
+    fetch(blockIdx.x);
+    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const int s = item / H;
+    const int h = item - s * H;
+    const int n = fn;  // <= 64
+    if (n > 0) {
+        const float G = wave_prefix_sum(gv);
+        if (w == 0) {
+            lds_st(lds, P_G + 4 * l, G);
+            lds_st(lds, P_B + 4 * l, bv);
+        } else if (w == 1) {
+            lds_st(lds, P_E + 4 * l, __expf(G));
+        }
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-            const int d = 8 * cidx + 2 * e2;
-            const uint32_t k0 = kr[it][0][e2], k1 = kr[it][1][e2];
-            const uint32_t v0 = vr[it][0][e2], v1 = vr[it][1][e2];
-            lds_st(lds, P_KT + tr_off(d, r0 >> 3) + cb, pack_lo(k0, k1));
-            lds_st(lds, P_KT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(k0, k1));
-            lds_st(lds, P_VT + tr_off(d, r0 >> 3) + cb, pack_lo(v0, v1));
-            lds_st(lds, P_VT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(v0, v1));
+        for (int it = 0; it < 2; ++it) {
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr)
+                lds_st(lds, P_K + row_off(2 * (prb + 16 * it) + rr, cidx), kr[it][rr]);
+            const int r0 = 2 * (prb + 16 * it);
+            const int cb = (r0 & 7) * 2;  // byte offset of the token pair inside its 8-token piece
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const int d = 8 * cidx + 2 * e2;
+                const uint32_t k0 = kr[it][0][e2], k1 = kr[it][1][e2];
+                const uint32_t v0 = vr[it][0][e2], v1 = vr[it][1][e2];
+                lds_st(lds, P_KT + tr_off(d, r0 >> 3) + cb, pack_lo(k0, k1));
+                lds_st(lds, P_KT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(k0, k1));
+                lds_st(lds, P_VT + tr_off(d, r0 >> 3) + cb, pack_lo(v0, v1));
+                lds_st(lds, P_VT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(v0, v1));
+            }
         }
     }
+    fetch(item + gridDim.x);
+    if (n <= 0) continue;
     __syncthreads();
 
     // A[i][m] = beta_i (k_i . k_m) exp(G_i - G_m) for i > m, else 0, row-major.
@@ -229,60 +237,74 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
     }
     __syncthreads();
     // Then block row by block row: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,
-    // wave J taking column block J (waves J >= I wait at this level).
+    // wave J taking column block J (waves J >= I wait at this level). Each
+    // 16 x 16 x 16 product is four fp32 16 x 16 x 4 MFMAs: lane l supplies
+    // L[l % 16][4k + l / 16] and R[4k + l / 16][l % 16] and receives
+    // D[4 (l / 16) + v][l % 16] in element v.
     {
-        const int r = l >> 2;
-        const int c0 = 4 * (l & 3);
+        const int lr = l & 15;
+        const int lk = l >> 4;
 #pragma unroll
         for (int I = 1; I < 4; ++I) {
             if (w < I) {
                 const int J = w;
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
                 for (int K = J; K < I; ++K)
-                    blk_mac(lds, P_A + 16 * I * A_ROW + 64 * K, A_ROW, tb_off(K, J), TB_ROW, r, c0, acc);
-                // X_J for this wave's own lanes (LDS in order within a wave).
-                lds_st(lds, P_X + 1280 * w + r * TB_ROW + 4 * c0, make_float4(acc[0], acc[1], acc[2], acc[3]));
-                float t[4] = {0.f, 0.f, 0.f, 0.f};
-                blk_mac(lds, tb_off(I, I), TB_ROW, P_X + 1280 * w, TB_ROW, r, c0, t);
-                lds_st(lds, tb_off(I, J) + r * TB_ROW + 4 * c0, make_float4(-t[0], -t[1], -t[2], -t[3]));
+#pragma unroll
+                    for (int k4 = 0; k4 < 4; ++k4) {
+                        const float a = lds_ld<float>(lds, P_A + (16 * I + lr) * A_ROW + 64 * K + 4 * (4 * k4 + lk));
+                        const float b = lds_ld<float>(lds, tb_off(K, J) + (4 * k4 + lk) * TB_ROW + 4 * lr);
+                        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
+                    }
+                // X to this wave's scratch block, row-major (a wave's LDS
+                // accesses take effect in order), then T_II X.
+#pragma unroll
+                for (int v = 0; v < 4; ++v) lds_st(lds, P_X + 1280 * w + (4 * lk + v) * TB_ROW + 4 * lr, x[v]);
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    const float a = lds_ld<float>(lds, tb_off(I, I) + lr * TB_ROW + 4 * (4 * k4 + lk));
+                    const float b = lds_ld<float>(lds, P_X + 1280 * w + (4 * k4 + lk) * TB_ROW + 4 * lr);
+                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t, 0, 0, 0);
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) lds_st(lds, tb_off(I, J) + (4 * lk + v) * TB_ROW + 4 * lr, -t[v]);
             }
             __syncthreads();
         }
     }
 
-    // Row c = l of T, in wave 0.
-    if (w == 0) {
-        float y[64];
+    // T'[c][m] = T[c][m] beta_m exp(G_m) and T''[c][m] = T[c][m] beta_m, each
+    // as a bf16 high part and the bf16 rounding of the rest: wave w forms
+    // columns 16w .. 16w + 15 (block column w) of every row c = l.
+    {
         const int I = l >> 4;
         const int r = l & 15;
+        const bool ok = w <= I;
+        float y[16];
 #pragma unroll
-        for (int J = 0; J < 4; ++J)
+        for (int q = 0; q < 4; ++q) {
+            const float4 v = lds_ld<float4>(lds, (ok ? tb_off(I, w) : 0) + r * TB_ROW + 16 * q);
+            y[4 * q + 0] = ok ? v.x : 0.f;
+            y[4 * q + 1] = ok ? v.y : 0.f;
+            y[4 * q + 2] = ok ? v.z : 0.f;
+            y[4 * q + 3] = ok ? v.w : 0.f;
+        }
+        __syncthreads();  // every block is read before the T' parts overwrite them
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const bool ok = J <= I;
-                const float4 v = lds_ld<float4>(lds, (ok ? tb_off(I, J) : 0) + r * TB_ROW + 16 * q);
-                y[16 * J + 4 * q + 0] = ok ? v.x : 0.f;
-                y[16 * J + 4 * q + 1] = ok ? v.y : 0.f;
-                y[16 * J + 4 * q + 2] = ok ? v.z : 0.f;
-                y[16 * J + 4 * q + 3] = ok ? v.w : 0.f;
-            }
-        // Every lane holds its row before any T' row overwrites the blocks.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // T'[c][m] = y_m beta_m exp(G_m), T''[c][m] = y_m beta_m, each as a
-        // bf16 high part and the bf16 rounding of the rest.
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float4 G0 = lds_ld<float4>(lds, P_G + 32 * q);
-            const float4 G1 = lds_ld<float4>(lds, P_G + 32 * q + 16);
+        for (int q2 = 0; q2 < 2; ++q2) {
+            const int q = 2 * w + q2;  // columns 8q .. 8q + 7
+            const float4 E0 = lds_ld<float4>(lds, P_E + 32 * q);
+            const float4 E1 = lds_ld<float4>(lds, P_E + 32 * q + 16);
             const float4 B0 = lds_ld<float4>(lds, P_B + 32 * q);
             const float4 B1 = lds_ld<float4>(lds, P_B + 32 * q + 16);
-            const float gq[8] = {G0.x, G0.y, G0.z, G0.w, G1.x, G1.y, G1.z, G1.w};
+            const float eq[8] = {E0.x, E0.y, E0.z, E0.w, E1.x, E1.y, E1.z, E1.w};
             const float bq[8] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
             bf16x8 ph, pl, qh, ql;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float tq = y[8 * q + e] * bq[e];
-                const float tp = tq * __expf(gq[e]);
+                const float tq = y[8 * q2 + e] * bq[e];
+                const float tp = tq * eq[e];
                 ph[e] = (__bf16)tp;
                 pl[e] = (__bf16)(tp - (float)ph[e]);
                 qh[e] = (__bf16)tq;
@@ -322,6 +344,8 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p) {
             *reinterpret_cast<float4 *>(ut + ((w * 8 + 4 * nt + g4) * 64 + l) * 4) =
                 make_float4(au[4 * g4], au[4 * g4 + 1], au[4 * g4 + 2], au[4 * g4 + 3]);
         }
+    }
+    __syncthreads();  // LDS is free for the next item
     }
 }
 
@@ -794,7 +818,16 @@ __global__ __launch_bounds__(NT) void gdn_output_kernel(GdnParams p) {
 hipError_t launch_gdn_chunk(const GdnParams &p, hipStream_t st) {
     if (p.c.N == 0) return hipSuccess;
     const dim3 chunks((unsigned)((int64_t)p.c.nseg_max * p.c.H));
-    if (p.c.nseg_max > 0) hipLaunchKernelGGL(gdn_prep_kernel, chunks, dim3(NT), 0, st, p);
+    if (p.c.nseg_max > 0) {
+        // Two workgroups fit on a CU (72 KiB of LDS each).
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        const int64_t nitems = (int64_t)p.c.nseg_max * p.c.H;
+        const unsigned wgs = (unsigned)std::min<int64_t>(nitems, 2 * (int64_t)cus);
+        hipLaunchKernelGGL(gdn_prep_kernel, dim3(wgs), dim3(NT), 0, st, p, (int)nitems);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // Four column blocks per (sequence, head), the units rounded up to whole
