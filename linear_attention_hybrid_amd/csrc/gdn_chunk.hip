@@ -17,7 +17,7 @@
 // once by a first kernel (gdn_prep_kernel), one workgroup per (chunk, head),
 // and kept in a workspace (W in bf16, an MFMA operand; U in fp32). The state
 // recurrence is sequential over chunks: gdn_chain_kernel walks each
-// (sequence, head, block of 32 value columns) through its chunks with the
+// (sequence, head, block of 16 value columns) through its chunks with the
 // fp32 state in the MFMA accumulators. A last kernel (gdn_output_kernel)
 // forms every chunk's output at once from the states and new_v the chain
 // leaves behind.
@@ -72,15 +72,14 @@ constexpr int P_TQL = P_A + 8192;  // low part
 static_assert(P_TQL + 8192 <= P_G, "T'' parts overlap the gate tables");
 
 // Per chunk and head the workspace tile holds W (16 KiB bf16 rows) and U
-// (32 KiB fp32, as [block b][piece p][lane l] x 16 B: lane l of piece p holds
-// tokens 8p + 4(l/32) .. + 3 of value column 32b + l % 32, the order the chain
-// kernel's accumulators use, so each 1 KiB piece is one contiguous load; the
-// 8 KiB of block b are read only by the chain workgroup of column block b).
-// Once that workgroup
-// has taken its U slice it stores there the chunk's start state for its
-// columns, in bf16, as the register image of the output kernel's MFMA operand
-// (16 bytes per lane and operand, lanes consecutive). The chunk's bf16 new_v
-// goes, as an image too, to a separate 16 KiB per chunk and head.
+// (32 KiB fp32, as [slice w][piece p][lane l] x 16 B: lane l of piece p of
+// slice w holds tokens 8p + 4(l/32) .. + 3 of value column 32w + l % 32).
+// Slice w has the layout of the output kernel's operand image for its wave w
+// (16 bytes per lane and operand, lanes consecutive), and the U of each chain
+// workgroup (16 value columns: half the lanes of one slice) sits in exactly
+// the bytes where that workgroup later stores its half of the chunk's start
+// state, in bf16, as that image; no other workgroup reads them. The chunk's
+// bf16 new_v goes, as an image too, to a separate 16 KiB per chunk and head.
 constexpr int TILE_ELEMS = 64 * D;                 // bf16 elements of W; U is as many floats
 constexpr int T_U = TILE_ELEMS * 2;                 // byte offset of U
 constexpr int TILE_BYTES = 3 * TILE_ELEMS * 2;      // W + U = 48 KiB
@@ -320,7 +319,7 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
 
     // Wave w: W^T = K^T T'^T for dk rows [32w, 32w + 32) (stored as W rows,
     // token-major), and U = T'' V for value columns [32w, 32w + 32) (fp32, in
-    // the pieces of column block w). Rows past the chunk's end come out zero.
+    // the pieces of slice w). Rows past the chunk's end come out zero.
     uint16_t *wt = reinterpret_cast<uint16_t *>(tile_at(p, s, h));
     float *ut = reinterpret_cast<float *>(tile_at(p, s, h) + T_U);
 #pragma unroll
@@ -349,19 +348,37 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
     }
 }
 
-// ---- gdn_chain_kernel: a ring of H_RING chunk buffers in LDS (bytes).
-constexpr int HB_W = 0;        // W rows [64][256 B], swizzled as row_off
-constexpr int HB_K = 16384;    // k rows [64][256 B], swizzled as row_off
-constexpr int HB_U = 32768;    // this block's U pieces: [8][64 lanes] x 16 B
-constexpr int HB_G = 40960;    // g[64] fp32 (rows past the chunk's end: the last row's)
+// ---- gdn_chain_kernel: one workgroup per (sequence, head, block of 16 value
+// columns); a ring of H_RING chunk buffers in LDS (bytes).
+constexpr int H_COLS = 16;            // value columns per chain workgroup
+constexpr int H_NB = D / H_COLS;      // column blocks per head
+constexpr int HB_W = 0;               // W rows [64][256 B], swizzled as row_off
+constexpr int HB_K = 16384;           // k rows [64][256 B], swizzled as row_off
+constexpr int HB_U = 32768;           // this block's U: [token tile 4][64 lanes] x 16 B
+constexpr int HB_G = 36864;           // g[64] fp32 (rows past the chunk's end: the last row's)
 constexpr int H_BUF = HB_G + 256;
 constexpr int H_RING = 3;             // chunk j + 2 loads while chunk j computes
-constexpr int H_XS = H_RING * H_BUF;  // state operands: [wave 2][4][64 lanes] x 16 B (the state image)
-constexpr int H_XN = H_XS + 8192;     // new_v high/low operands exchanged: [wave 2][4][64 lanes] x 16 B
-constexpr int H_NV = H_XN + 8192;     // bf16 new_v: [wave 2][2][64 lanes] x 16 B (the new_v image)
-constexpr int H_G = H_NV + 4096;      // exp(G_last - G)[64] fp32 of the current chunk, one copy per wave
-constexpr int H_BYTES = H_G + 2 * 256;
+// Operand stages, each in the order of the output kernel's operand images:
+// piece (op, lh, c) of 16 bytes at ((2 op + lh) 16 + c) 16 holds elements
+// 16 op + 4 lh + {0..3} and 16 op + 8 + 4 lh + {0..3} (keys or tokens) of
+// the block's column c.
+constexpr int H_SS = H_RING * H_BUF;  // the chunk's start state, bf16: 8 ops
+constexpr int H_SN = H_SS + 4096;     // new_v, bf16: 4 ops
+constexpr int H_XH = H_SN + 2048;     // exp(G_last - G) new_v, bf16 high part: 4 ops
+constexpr int H_XL = H_XH + 2048;     // low part
+constexpr int H_E = H_XL + 2048;      // exp(G_last - G)[64], one copy per compute wave
+constexpr int H_BYTES = H_E + 2 * 256;
 constexpr int H_MOVERS = 4;           // waves that move data (after the two compute waves)
+constexpr int H_THREADS = 64 * (2 + H_MOVERS);
+
+__device__ __forceinline__ int stage_off(int op, int lh, int c) { return ((2 * op + lh) * 16 + c) * 16; }
+
+// Byte offset, inside the 8 KiB image slice of output wave cb / 2, of piece
+// (op, lh, c) of column block cb: the output kernel's lane 32 lh + 16 (cb % 2)
+// + c of operand op.
+__device__ __forceinline__ int image_off(int cb, int op, int lh, int c) {
+    return (op * 64 + lh * 32 + 16 * (cb & 1) + c) * 16;
+}
 
 // A sequence's chunks are consecutive tokens: its start and length come from
 // its first and last table rows, read once, so the chunk loop itself reads no
@@ -385,22 +402,25 @@ __device__ __forceinline__ ChainSeq chain_seq(const GdnParams &p, int seq) {
 // The chain workgroup has 2 + H_MOVERS waves. Waves 0 and 1 hold the state
 // and compute; the mover waves move every byte between HBM and LDS: chunk
 // j + 2's W rows, k rows, U pieces and g into the ring by direct global ->
-// LDS loads, and chunk j's state and new_v images from LDS to the workspace,
-// each mover an equal share. A wave is held at each load it issues while the
-// memory path takes it (one wave moves about 20 bytes per ns this way), so
-// the compute waves issue none and the movers split the bytes.
+// LDS loads, and chunk j's state and new_v images from the LDS stages to the
+// workspace, each mover an equal share. A wave is held at each load it issues
+// while the memory path takes it (one wave moves about 20 bytes per ns this
+// way), so the compute waves issue none and the movers split the bytes.
 //
 // vmcnt counts every operation a wave issues and they complete in issue
 // order, so a chunk's loads are done once at most the operations issued
 // after its last load remain outstanding; each mover keeps that count.
 __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, int cb, int mv, char *lds) {
     static_assert(H_RING == 3, "the mover keeps the counts of two chunks in flight");
-    constexpr int M = H_MOVERS;
+    static_assert(H_MOVERS == 4, "the movers split 16 W and 16 k pieces, 4 U pieces and the images four ways");
     const int H = p.c.H;
     const ChainSeq c = chain_seq(p, seq);
     const int l = threadIdx.x & 63;
     const int m16 = l & 15;
     const int64_t row_bytes = (int64_t)H * D * 2;
+    // This block's U pieces and state image share the bytes of its half of
+    // the 8 KiB image slice of output wave cb / 2 (see gdn_prep_kernel).
+    const int slice = T_U + (cb >> 1) * 8192;
     int issued = 0;  // vector-memory operations this wave has issued
 
     auto issue_w = [&](int j) {  // g and W rows
@@ -413,11 +433,11 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
             ++issued;
         }
 #pragma unroll
-        for (int i = mv * (16 / M); i < (mv + 1) * (16 / M); ++i) {
+        for (int i = 4 * mv; i < 4 * mv + 4; ++i) {
             const int r = 4 * i + (l >> 4);
             gll16(tile + r * 256 + ((m16 ^ (r & 15)) << 4), buf + HB_W + 1024 * i);
         }
-        issued += 16 / M;
+        issued += 4;
     };
     auto issue_k = [&](int j) {  // k rows; rows past the chunk's end repeat its last row
         const int n = min(kChunk, c.len - kChunk * j);
@@ -425,22 +445,22 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
         const char *buf = lds + (j % H_RING) * H_BUF;
         const char *kb = static_cast<const char *>(p.c.k) + (t0 * H + h) * (D * 2);
 #pragma unroll
-        for (int i = mv * (16 / M); i < (mv + 1) * (16 / M); ++i) {
+        for (int i = 4 * mv; i < 4 * mv + 4; ++i) {
             const int r = 4 * i + (l >> 4);
             gll16(kb + min(r, n - 1) * row_bytes + ((m16 ^ (r & 15)) << 4), buf + HB_K + 1024 * i);
         }
-        issued += 16 / M;
+        issued += 4;
     };
     auto issue_u = [&](int j) {
-        // U pieces in accumulator order: value column 32cb + l%32, piece
-        // 4nt + q holds tokens 32nt + 8q + 4(l/32) .. + 3.
+        // Token tile mv: lane l holds tokens 16 mv + 4 (l / 16) .. + 3 of
+        // column l % 16, the piece (op, lh) = (2 mv + l / 32, (l / 16) % 2).
         const char *buf = lds + (j % H_RING) * H_BUF;
-        const char *ub = tile_at(p, c.first + j, h) + T_U + cb * 8192 + 16 * l;
-#pragma unroll
-        for (int pc = mv * (8 / M); pc < (mv + 1) * (8 / M); ++pc)
-            gll16(ub + 1024 * pc, buf + HB_U + 1024 * pc);
-        issued += 8 / M;
+        const int rho = 4 * mv + (l >> 4);
+        gll16(tile_at(p, c.first + j, h) + slice + image_off(cb, rho >> 1, rho & 1, m16),
+              buf + HB_U + 1024 * mv);
+        ++issued;
     };
+
     if (c.len <= 0) return;
     // issued-counts after the last load of chunks j and j + 1
     issue_w(0);
@@ -454,89 +474,87 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
     }
     int mark1 = issued;
 
+    // This mover's pieces of the stages: state piece 64 mv + l, new_v piece
+    // 64 mv + l for movers 0 and 1.
+    const int sp = 64 * mv + l;
+    const int s_img = image_off(cb, sp >> 5, (sp >> 4) & 1, sp & 15);
+    const int n_img = ((cb >> 1) * 4 * 64) * 16 + image_off(cb, sp >> 5, (sp >> 4) & 1, sp & 15);
+
     for (int j = 0; j < c.nch; ++j) {
         wait_vm_n(__builtin_amdgcn_readfirstlane(min(issued - mark0, 63)));
         __syncthreads();  // chunk j is in LDS; chunk j - 1's buffer is free
         const int jn = j + 2;
         const bool more = jn < c.nch;
         if (more) issue_w(jn);
-        __syncthreads();  // the state operands are in H_XS
-        char *simg = tile_at(p, c.first + j, h) + IMG_S + cb * 8 * 64 * 16;
-        bf16x8 x[8 / M];
-#pragma unroll
-        for (int t = 0; t < 8 / M; ++t) x[t] = lds_ld<bf16x8>(lds, H_XS + ((mv + M * t) * 64 + l) * 16);
-#pragma unroll
-        for (int t = 0; t < 8 / M; ++t)
-            *reinterpret_cast<bf16x8 *>(simg + ((mv + M * t) * 64 + l) * 16) = x[t];
-        issued += 8 / M;
+        __syncthreads();  // the state operands are staged
+        {
+            const bf16x8 x = lds_ld<bf16x8>(lds, H_SS + 16 * sp);
+            *reinterpret_cast<bf16x8 *>(tile_at(p, c.first + j, h) + slice + s_img) = x;
+            ++issued;
+        }
         if (more) issue_k(jn);
-        __syncthreads();  // new_v is in H_NV
+        __syncthreads();  // new_v is staged
         if (more) issue_u(jn);
         const int mark2 = issued;
-        char *nimg = p.nvimg + ((int64_t)(c.first + j) * H + h) * NV_BYTES + cb * 4 * 64 * 16;
-#pragma unroll
-        for (int t = 0; t < (4 + M - 1) / M; ++t) {
-            const int k = mv + M * t;
-            if (k < 4) {
-                x[t] = lds_ld<bf16x8>(lds, H_NV + (k * 64 + l) * 16);
-                *reinterpret_cast<bf16x8 *>(nimg + (k * 64 + l) * 16) = x[t];
-                ++issued;
-            }
+        if (mv < 2) {
+            const bf16x8 x = lds_ld<bf16x8>(lds, H_SN + 16 * sp);
+            *reinterpret_cast<bf16x8 *>(p.nvimg + ((int64_t)(c.first + j) * H + h) * NV_BYTES + n_img) = x;
+            ++issued;
         }
         mark0 = mark1;
         mark1 = mark2;
     }
 }
 
-// The state recurrence of one (sequence, head, block of 32 value columns)
-// per workgroup: W and k of a chunk are read by the four blocks of a head
-// (the four workgroups sit on one XCD and share its L2); U, the state and the
-// images are the block's own. Compute wave a holds key rows 64a .. 64a + 63
-// of the block's state (lane l: column 32b + l % 32 of the head's value
-// columns, key rows 32(2a + r) + 8(v/4) + 4(l/32) + v%4 of accumulator S[r],
-// element v) and forms new_v for tokens 32a .. 32a + 31.
+// The state recurrence of one (sequence, head, block of 16 value columns)
+// per workgroup: W and k of a chunk are read by the eight blocks of a head
+// (the eight workgroups sit on one XCD and share its L2); U, the state and
+// the images are the block's own. Compute wave a holds key rows
+// 64a .. 64a + 63 of the block's state as four 16 x 16 tiles (tile t: lane l
+// holds key 64a + 16t + 4(l/16) + v, column l % 16, in element v) and forms
+// new_v for tokens 32a .. 32a + 31.
 //
-// Per chunk: the compute waves swap their halves of the state as bf16
-// operands, so each forms new_v = U - W S for its token half over all key
-// rows; then they swap exp(G_last - G) new_v as bf16 high and low parts, so
-// each updates its key rows with all 64 tokens (K^T from the k rows through
-// the transposing read, in the token order new_v comes out in).
+// Per chunk, on 16 x 16 x 32 bf16 MFMAs: the compute waves stage their state
+// as bf16 operands, so each forms new_v = U - W S for its token half over all
+// key rows; then they stage exp(G_last - G) new_v as bf16 high and low parts,
+// so each updates its key rows with all 64 tokens (K^T from the k rows
+// through the transposing read). Inside one MFMA the order of the 32 k values
+// is free as long as both operands follow it; here it is the order of the
+// stage pieces, so the stages are at once the operands and the images.
 // The work of compute wave WA (a compile-time index, so that every register
-// array is indexed by constants); all three waves pass the same barriers in
-// the same order.
+// array is indexed by constants); all waves pass the same barriers in the
+// same order.
 template <int WA>
 __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, int cb, char *lds) {
     constexpr int wa = WA;
     const int H = p.c.H;
     const ChainSeq c = chain_seq(p, seq);
     const int l = threadIdx.x & 63;
-    const int ln = l & 31;
-    const int lh = l >> 5;
-    const int m16 = l & 15;
-    const int g16 = l >> 4;
+    const int lc = l & 15;   // column (state, new_v) or row (W, K^T) of a 16 x 16 tile
+    const int g = l >> 4;    // lane group
     const int64_t sl = (int64_t)D * D;
+    const int col = H_COLS * cb + lc;
 
-    f32x16 S[2];
+    f32x4 S[4];
     {
         const float *src = p.c.s0 ? p.c.s0 + ((int64_t)seq * H + h) * sl : nullptr;
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * (2 * wa + r) + 8 * (v >> 2) + 4 * lh + (v & 3);
-                S[r][v] = src ? src[dk * D + 32 * cb + ln] : 0.f;
-            }
+            for (int v = 0; v < 4; ++v)
+                S[t][v] = src ? src[(64 * wa + 16 * t + 4 * g + v) * D + col] : 0.f;
     }
 
-    // Lane-constant parts of the transposing reads of K^T (rows 32b + l%32;
-    // the two reads of an operand give tokens 4(l/32) + 0..3 and + 8 + 0..3
-    // of each 16-token step, the order new_v comes out in).
-    int trk[2][2];
+    // The k values lane group g supplies in step ks of 32: 32 ks + o(g) + {0..3}
+    // and + 8 + {0..3}, o(g) = 16 (g / 2) + 4 (g % 2): stage piece
+    // (2 ks + g / 2, g % 2). Lane-constant parts of the transposing reads of
+    // K^T (key tile t, the two 4-token halves).
+    const int og = 16 * (g >> 1) + 4 * (g & 1);
+    int trk[4][2];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-            trk[r][hf] = tr_src(4 * (g16 >> 1) + 8 * hf, 32 * (2 * wa + r) + 16 * (g16 & 1), m16);
+        for (int hf = 0; hf < 2; ++hf) trk[t][hf] = tr_src(og + 8 * hf, 64 * wa + 16 * t, lc);
 
     const int nch = c.len > 0 ? c.nch : 0;
     for (int j = 0; j < nch; ++j) {
@@ -545,91 +563,72 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
         const int n = min(kChunk, c.len - kChunk * j);
         const float G = wave_prefix_sum(l < n ? lds_ld<float>(buf, HB_G + 4 * l) : 0.f);
         const float Gl = lane_value(G, 63);
-        // exp(G_last - G) of token l, once per token rather than once per
-        // element of new_v
-        lds_st(lds, H_G + 256 * wa + 4 * l, __expf(Gl - G));
+        // exp(G_last - G) of token l, once per token
+        lds_st(lds, H_E + 256 * wa + 4 * l, __expf(Gl - G));
 
-        // This wave's half of the state as bf16 operands (key rows in
-        // accumulator order), for the partner and for the state image.
-        bf16x8 sb[8];
+        // This wave's state tiles as bf16 stage pieces: key tile 4wa + t,
+        // lane group g -> piece (4wa + t, g % 2), half g / 2.
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int op = 4 * wa + 2 * r + s2;   // operand index 2b + s2, b = 2wa + r
-                bf16x8 x;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = (__bf16)S[r][8 * s2 + e];
-                sb[op] = x;
-                lds_st(lds, H_XS + (op * 64 + l) * 16, x);
-            }
-        __syncthreads();  // both halves of the state are exchanged
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            sb[4 * (1 - wa) + k] = lds_ld<bf16x8>(lds, H_XS + (((1 - wa) * 4 + k) * 64 + l) * 16);
+        for (int t = 0; t < 4; ++t) {
+            const bf16x4 x = {(__bf16)S[t][0], (__bf16)S[t][1], (__bf16)S[t][2], (__bf16)S[t][3]};
+            lds_st(lds, H_SS + stage_off(4 * wa + t, g & 1, lc) + 8 * (g >> 1), x);
+        }
+        __syncthreads();  // both halves of the state are staged
 
-        // new_v = U - W S for token half nt = wa over all key rows, as two
-        // independent accumulation chains (key rows 0..63 and 64..127).
-        const int nt = wa;
-        f32x16 acc2[2] = {};
+        // new_v = U - W S for token tiles 2wa, 2wa + 1 over all key rows.
+        f32x4 acc[2] = {};
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 sb = lds_ld<bf16x8>(lds, H_SS + stage_off(2 * ks + (g >> 1), g & 1, lc));
+            const int c1 = 4 * ks + 2 * (g >> 1);
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int cc = 4 * b + 2 * s2;
-                const int i = 32 * nt + ln;
-                const bf16x4 x0 = lds_ld<bf16x4>(buf, HB_W + row_off(i, cc) + 8 * lh);
-                const bf16x4 x1 = lds_ld<bf16x4>(buf, HB_W + row_off(i, cc + 1) + 8 * lh);
-                acc2[b >> 1] = mfma(cat4(x0, x1), sb[2 * b + s2], acc2[b >> 1]);
+            for (int tt = 0; tt < 2; ++tt) {
+                const int i = 16 * (2 * wa + tt) + lc;
+                const bf16x4 x0 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c1) + 8 * (g & 1));
+                const bf16x4 x1 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c1 + 1) + 8 * (g & 1));
+                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat4(x0, x1), sb, acc[tt], 0, 0, 0);
             }
-        const f32x16 acc = acc2[0] + acc2[1];
+        }
         // Its bf16 image for the output kernel, and exp(G_last - G) new_v as
         // high and low bf16 parts for both waves' updates.
-        bf16x8 nvo[2], nvh[4], nvl[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 u = lds_ld<float4>(buf, HB_U + (4 * nt + q) * 1024 + 16 * l);
+        for (int tt = 0; tt < 2; ++tt) {
+            const int q = 2 * wa + tt;  // token tile
+            const float4 u = lds_ld<float4>(buf, HB_U + 1024 * q + 16 * l);
+            const float4 e = lds_ld<float4>(lds, H_E + 256 * wa + 4 * (16 * q + 4 * g));
             const float uq[4] = {u.x, u.y, u.z, u.w};
-            // tokens 32nt + 8q + 4(l/32) + r of accumulator element 4q + r
-            const float4 Et = lds_ld<float4>(lds, H_G + 256 * wa + 4 * (32 * nt + 8 * q + 4 * lh));
-            const float et[4] = {Et.x, Et.y, Et.z, Et.w};
+            const float eq[4] = {e.x, e.y, e.z, e.w};
+            bf16x4 nvo, xh, xl;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int v = 4 * q + r;
-                const float nv = uq[r] - acc[v];
-                const float x = nv * et[r];
-                const __bf16 xh = (__bf16)x;
-                nvo[v >> 3][v & 7] = (__bf16)nv;
-                nvh[2 * nt + (v >> 3)][v & 7] = xh;
-                nvl[2 * nt + (v >> 3)][v & 7] = (__bf16)(x - (float)xh);
+            for (int v = 0; v < 4; ++v) {
+                const float nv = uq[v] - acc[tt][v];
+                const float x = nv * eq[v];
+                nvo[v] = (__bf16)nv;
+                xh[v] = (__bf16)x;
+                xl[v] = (__bf16)(x - (float)xh[v]);
             }
+            const int so = stage_off(q, g & 1, lc) + 8 * (g >> 1);
+            lds_st(lds, H_SN + so, nvo);
+            lds_st(lds, H_XH + so, xh);
+            lds_st(lds, H_XL + so, xl);
         }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            lds_st(lds, H_NV + ((2 * nt + s2) * 64 + l) * 16, nvo[s2]);
-            lds_st(lds, H_XN + ((wa * 4 + s2) * 64 + l) * 16, nvh[2 * nt + s2]);
-            lds_st(lds, H_XN + ((wa * 4 + 2 + s2) * 64 + l) * 16, nvl[2 * nt + s2]);
-        }
-        __syncthreads();  // both token halves of new_v are exchanged
-        const int ot = 1 - wa;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            nvh[2 * ot + s2] = lds_ld<bf16x8>(lds, H_XN + ((ot * 4 + s2) * 64 + l) * 16);
-            nvl[2 * ot + s2] = lds_ld<bf16x8>(lds, H_XN + ((ot * 4 + 2 + s2) * 64 + l) * 16);
-        }
+        __syncthreads();  // both token halves of new_v are staged
 
         if (j + 1 < nch || p.c.sfin) {
             const float a = __expf(Gl);
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
+            for (int t = 0; t < 4; ++t) S[t] *= a;
 #pragma unroll
-                for (int v = 0; v < 16; ++v) S[r][v] *= a;
+            for (int ks = 0; ks < 2; ++ks) {
+                const int so = stage_off(2 * ks + (g >> 1), g & 1, lc);
+                const bf16x8 xh = lds_ld<bf16x8>(lds, H_XH + so);
+                const bf16x8 xl = lds_ld<bf16x8>(lds, H_XL + so);
 #pragma unroll
-                for (int st = 0; st < 4; ++st) {
-                    const bf16x8 kt = cat4(lds_tr(buf, HB_K + 4096 * st + trk[r][0]),
-                                           lds_tr(buf, HB_K + 4096 * st + trk[r][1]));
-                    S[r] = mfma(kt, nvh[st], S[r]);
-                    S[r] = mfma(kt, nvl[st], S[r]);
+                for (int t = 0; t < 4; ++t) {
+                    const bf16x8 kt = cat4(lds_tr(buf, HB_K + 8192 * ks + trk[t][0]),
+                                           lds_tr(buf, HB_K + 8192 * ks + trk[t][1]));
+                    S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, xh, S[t], 0, 0, 0);
+                    S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, xl, S[t], 0, 0, 0);
                 }
             }
         }
@@ -638,22 +637,15 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
     if (p.c.sfin) {
         float *dst = p.c.sfin + ((int64_t)seq * H + h) * sl;
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * (2 * wa + r) + 8 * (v >> 2) + 4 * lh + (v & 3);
-                dst[dk * D + 32 * cb + ln] = S[r][v];
-            }
+            for (int v = 0; v < 4; ++v) dst[(64 * wa + 16 * t + 4 * g + v) * D + col] = S[t][v];
     }
 }
 
-constexpr int H_THREADS = 64 * (2 + H_MOVERS);
-static_assert(H_MOVERS == 1 || H_MOVERS == 2 || H_MOVERS == 4 || H_MOVERS == 8,
-              "movers split 8 and 16 pieces evenly");
-
 __global__ __launch_bounds__(H_THREADS) void gdn_chain_kernel(GdnParams p) {
     int unit, cb;
-    xcd_unit_map(blockIdx.x, 4, unit, cb);
+    xcd_unit_map(blockIdx.x, H_NB, unit, cb);
     const int seq = unit / p.c.H;
     const int h = unit - seq * p.c.H;
     if (seq >= p.c.N) return;
@@ -830,10 +822,10 @@ hipError_t launch_gdn_chunk(const GdnParams &p, hipStream_t st) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // Four column blocks per (sequence, head), the units rounded up to whole
+    // H_NB column blocks per (sequence, head), the units rounded up to whole
     // groups of eight so that xcd_unit_map covers them.
     const int64_t units = ((int64_t)p.c.N * p.c.H + 7) / 8 * 8;
-    hipLaunchKernelGGL(gdn_chain_kernel, dim3((unsigned)(units * 4)), dim3(H_THREADS), 0, st, p);
+    hipLaunchKernelGGL(gdn_chain_kernel, dim3((unsigned)(units * H_NB)), dim3(H_THREADS), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.c.nseg_max > 0) hipLaunchKernelGGL(gdn_output_kernel, chunks, dim3(NT), 0, st, p);
