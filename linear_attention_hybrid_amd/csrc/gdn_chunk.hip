@@ -357,7 +357,7 @@ constexpr int HB_K = 16384;           // k rows [64][256 B], swizzled as row_off
 constexpr int HB_U = 32768;           // this block's U: [token tile 4][64 lanes] x 16 B
 constexpr int HB_G = 36864;           // g[64] fp32 (rows past the chunk's end: the last row's)
 constexpr int H_BUF = HB_G + 256;
-constexpr int H_RING = 3;             // chunk j + 2 loads while chunk j computes
+constexpr int H_RING = 4;             // chunk j + 3 loads while chunk j computes
 // Operand stages, each in the order of the output kernel's operand images:
 // piece (op, lh, c) of 16 bytes at ((2 op + lh) 16 + c) 16 holds elements
 // 16 op + 4 lh + {0..3} and 16 op + 8 + 4 lh + {0..3} (keys or tokens) of
@@ -370,6 +370,12 @@ constexpr int H_E = H_XL + 2048;      // exp(G_last - G)[64], one copy per compu
 constexpr int H_BYTES = H_E + 2 * 256;
 constexpr int H_MOVERS = 4;           // waves that move data (after the two compute waves)
 constexpr int H_THREADS = 64 * (2 + H_MOVERS);
+// Mover roles: every mover takes 16 / H_MOVERS of the W and of the k pieces;
+// movers 0..3 one U token tile each; H_SMOV.. H_SMOV + 3 one quarter of the
+// state image each; movers 0 and 1 half of the new_v image each; H_GMOV g.
+constexpr int H_WK = 16 / H_MOVERS;
+constexpr int H_SMOV = H_MOVERS == 8 ? 4 : 0;
+constexpr int H_GMOV = H_MOVERS == 8 ? 4 : 0;
 
 __device__ __forceinline__ int stage_off(int op, int lh, int c) { return ((2 * op + lh) * 16 + c) * 16; }
 
@@ -401,7 +407,7 @@ __device__ __forceinline__ ChainSeq chain_seq(const GdnParams &p, int seq) {
 
 // The chain workgroup has 2 + H_MOVERS waves. Waves 0 and 1 hold the state
 // and compute; the mover waves move every byte between HBM and LDS: chunk
-// j + 2's W rows, k rows, U pieces and g into the ring by direct global ->
+// j + 3's W rows, k rows, U pieces and g into the ring by direct global ->
 // LDS loads, and chunk j's state and new_v images from the LDS stages to the
 // workspace, each mover an equal share. A wave is held at each load it issues
 // while the memory path takes it (one wave moves about 20 bytes per ns this
@@ -411,8 +417,8 @@ __device__ __forceinline__ ChainSeq chain_seq(const GdnParams &p, int seq) {
 // order, so a chunk's loads are done once at most the operations issued
 // after its last load remain outstanding; each mover keeps that count.
 __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, int cb, int mv, char *lds) {
-    static_assert(H_RING == 3, "the mover keeps the counts of two chunks in flight");
-    static_assert(H_MOVERS == 4, "the movers split 16 W and 16 k pieces, 4 U pieces and the images four ways");
+    static_assert(H_RING == 4, "the mover keeps the counts of three chunks in flight");
+    static_assert(H_MOVERS == 4 || H_MOVERS == 8, "the mover roles are laid out for four or eight movers");
     const int H = p.c.H;
     const ChainSeq c = chain_seq(p, seq);
     const int l = threadIdx.x & 63;
@@ -428,16 +434,16 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
         const int64_t t0 = c.tok0 + (int64_t)kChunk * j;
         const char *buf = lds + (j % H_RING) * H_BUF;
         const char *tile = tile_at(p, c.first + j, h);
-        if (mv == 0) {
+        if (mv == H_GMOV) {
             gll4(p.c.g + (t0 + min(l, n - 1)) * H + h, buf + HB_G);
             ++issued;
         }
 #pragma unroll
-        for (int i = 4 * mv; i < 4 * mv + 4; ++i) {
+        for (int i = H_WK * mv; i < H_WK * mv + H_WK; ++i) {
             const int r = 4 * i + (l >> 4);
             gll16(tile + r * 256 + ((m16 ^ (r & 15)) << 4), buf + HB_W + 1024 * i);
         }
-        issued += 4;
+        issued += H_WK;
     };
     auto issue_k = [&](int j) {  // k rows; rows past the chunk's end repeat its last row
         const int n = min(kChunk, c.len - kChunk * j);
@@ -445,15 +451,16 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
         const char *buf = lds + (j % H_RING) * H_BUF;
         const char *kb = static_cast<const char *>(p.c.k) + (t0 * H + h) * (D * 2);
 #pragma unroll
-        for (int i = 4 * mv; i < 4 * mv + 4; ++i) {
+        for (int i = H_WK * mv; i < H_WK * mv + H_WK; ++i) {
             const int r = 4 * i + (l >> 4);
             gll16(kb + min(r, n - 1) * row_bytes + ((m16 ^ (r & 15)) << 4), buf + HB_K + 1024 * i);
         }
-        issued += 4;
+        issued += H_WK;
     };
     auto issue_u = [&](int j) {
         // Token tile mv: lane l holds tokens 16 mv + 4 (l / 16) .. + 3 of
         // column l % 16, the piece (op, lh) = (2 mv + l / 32, (l / 16) % 2).
+        if (mv >= 4) return;
         const char *buf = lds + (j % H_RING) * H_BUF;
         const int rho = 4 * mv + (l >> 4);
         gll16(tile_at(p, c.first + j, h) + slice + image_off(cb, rho >> 1, rho & 1, m16),
@@ -462,32 +469,35 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
     };
 
     if (c.len <= 0) return;
-    // issued-counts after the last load of chunks j and j + 1
-    issue_w(0);
-    issue_k(0);
-    issue_u(0);
-    int mark0 = issued;
-    if (c.nch > 1) {
-        issue_w(1);
-        issue_k(1);
-        issue_u(1);
+    // issued-counts after the last load of chunks j, j + 1 and j + 2
+    int mark[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        if (i < c.nch) {
+            issue_w(i);
+            issue_k(i);
+            issue_u(i);
+        }
+        mark[i] = issued;
     }
-    int mark1 = issued;
 
-    // This mover's pieces of the stages: state piece 64 mv + l, new_v piece
-    // 64 mv + l for movers 0 and 1.
-    const int sp = 64 * mv + l;
+    // This mover's pieces of the stages: state piece 64 (mv - H_SMOV) + l,
+    // new_v piece 64 mv + l for movers 0 and 1.
+    const int sm = mv - H_SMOV;
+    const bool s_copy = sm >= 0 && sm < 4;
+    const int sp = 64 * sm + l;
     const int s_img = image_off(cb, sp >> 5, (sp >> 4) & 1, sp & 15);
-    const int n_img = ((cb >> 1) * 4 * 64) * 16 + image_off(cb, sp >> 5, (sp >> 4) & 1, sp & 15);
+    const int np = 64 * mv + l;
+    const int n_img = ((cb >> 1) * 4 * 64) * 16 + image_off(cb, np >> 5, (np >> 4) & 1, np & 15);
 
     for (int j = 0; j < c.nch; ++j) {
-        wait_vm_n(__builtin_amdgcn_readfirstlane(min(issued - mark0, 63)));
+        wait_vm_n(__builtin_amdgcn_readfirstlane(min(issued - mark[0], 63)));
         __syncthreads();  // chunk j is in LDS; chunk j - 1's buffer is free
-        const int jn = j + 2;
+        const int jn = j + 3;
         const bool more = jn < c.nch;
         if (more) issue_w(jn);
         __syncthreads();  // the state operands are staged
-        {
+        if (s_copy) {
             const bf16x8 x = lds_ld<bf16x8>(lds, H_SS + 16 * sp);
             *reinterpret_cast<bf16x8 *>(tile_at(p, c.first + j, h) + slice + s_img) = x;
             ++issued;
@@ -497,12 +507,13 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
         if (more) issue_u(jn);
         const int mark2 = issued;
         if (mv < 2) {
-            const bf16x8 x = lds_ld<bf16x8>(lds, H_SN + 16 * sp);
+            const bf16x8 x = lds_ld<bf16x8>(lds, H_SN + 16 * np);
             *reinterpret_cast<bf16x8 *>(p.nvimg + ((int64_t)(c.first + j) * H + h) * NV_BYTES + n_img) = x;
             ++issued;
         }
-        mark0 = mark1;
-        mark1 = mark2;
+        mark[0] = mark[1];
+        mark[1] = mark[2];
+        mark[2] = mark2;
     }
 }
 
