@@ -99,6 +99,45 @@ def test_gdn_chunk_vs_oracle(T, init):
         check_windows(host(o[b]), ro[b], [0], "bf16", "gdn o seq %d" % b)
 
 
+def test_gdn_chunk_odd_batch_and_heads():
+    """B * H = 25 (the chain rounds its (sequence, head) units up to groups of
+    eight) and T = 100 (a ragged second chunk), with an initial state."""
+    say("gdn_chunk_fwd B=5 H=5 T=100 init")
+    inp = W.make_prefill(5, 100, 5, 128, 128, "bf16", "gdn", seed=55, device="cuda",
+                         init="normal", with_beta=True)
+    inp["initial_state"] = inp["initial_state"] * 25
+    o, S = sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                              initial_state=inp["initial_state"],
+                              out=nan_like((5, 100, 5, 128), torch.bfloat16))
+    torch.cuda.synchronize()
+    ro, rS = oracle_gdn(inp)
+    check(host(o), ro, "bf16", "gdn 5x5 o")
+    check(host(S), rS, "bf16", "gdn 5x5 final state", bf16_out=False)
+
+
+def test_gdn_chunk_many_short_sequences():
+    """40 packed sequences of 0 .. 130 tokens and 3 heads: many chains, most of
+    them one or two chunks long, each checked against the oracle."""
+    rng = np.random.default_rng(40)
+    lengths = [int(x) for x in rng.integers(0, 131, size=40)]
+    lengths[3] = 0
+    lengths[7] = 64
+    say("gdn_chunk_fwd varlen 40 sequences, %d tokens, H=3" % sum(lengths))
+    cu = W.cu_from_lengths(lengths)
+    T = int(cu[-1])
+    inp = W.make_prefill(1, T, 3, 128, 128, "bf16", "gdn", seed=41, device="cuda",
+                         cu_seqlens=cu, init="normal", with_beta=True)
+    inp["initial_state"] = inp["initial_state"] * 25
+    o, S = sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                              initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"],
+                              out=nan_like((1, T, 3, 128), torch.bfloat16))
+    torch.cuda.synchronize()
+    ro, rS = oracle_gdn(inp)
+    check(host(o), ro, "bf16", "gdn 40 seqs o")
+    check(host(S), rS, "bf16", "gdn 40 seqs states", bf16_out=False)
+    assert torch.equal(S[3], inp["initial_state"][3])
+
+
 def test_gdn_chunk_varlen_packed_equals_separate():
     lengths = [0, 1, 63, 64, 65, 130, 200, 7]
     say("gdn_chunk_fwd varlen", lengths)
