@@ -367,9 +367,10 @@ constexpr int H_SN = H_SS + 4096;     // new_v, bf16: 4 ops
 constexpr int H_XH = H_SN + 2048;     // exp(G_last - G) new_v, bf16 high part: 4 ops
 constexpr int H_XL = H_XH + 2048;     // low part
 constexpr int H_E = H_XL + 2048;      // exp(G_last - G)[64], one copy per compute wave
-constexpr int H_BYTES = H_E + 2 * 256;
+constexpr int H_CW = 2;               // compute waves
+constexpr int H_BYTES = H_E + H_CW * 256;
 constexpr int H_MOVERS = 4;           // waves that move data (after the two compute waves)
-constexpr int H_THREADS = 64 * (2 + H_MOVERS);
+constexpr int H_THREADS = 64 * (H_CW + H_MOVERS);
 // Mover roles: every mover takes 16 / H_MOVERS of the W and of the k pieces;
 // movers 0..3 one U token tile each; H_SMOV.. H_SMOV + 3 one quarter of the
 // state image each; movers 0 and 1 half of the new_v image each; H_GMOV g.
@@ -405,8 +406,8 @@ __device__ __forceinline__ ChainSeq chain_seq(const GdnParams &p, int seq) {
     return c;
 }
 
-// The chain workgroup has 2 + H_MOVERS waves. Waves 0 and 1 hold the state
-// and compute; the mover waves move every byte between HBM and LDS: chunk
+// The chain workgroup has H_CW + H_MOVERS waves. Waves 0 .. H_CW - 1 hold
+// the state and compute; the mover waves move every byte between HBM and LDS: chunk
 // j + 3's W rows, k rows, U pieces and g into the ring by direct global ->
 // LDS loads, and chunk j's state and new_v images from the LDS stages to the
 // workspace, each mover an equal share. A wave is held at each load it issues
@@ -520,10 +521,11 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
 // The state recurrence of one (sequence, head, block of 16 value columns)
 // per workgroup: W and k of a chunk are read by the eight blocks of a head
 // (the eight workgroups sit on one XCD and share its L2); U, the state and
-// the images are the block's own. Compute wave a holds key rows
-// 64a .. 64a + 63 of the block's state as four 16 x 16 tiles (tile t: lane l
-// holds key 64a + 16t + 4(l/16) + v, column l % 16, in element v) and forms
-// new_v for tokens 32a .. 32a + 31.
+// the images are the block's own. Compute wave a (of H_CW) holds key tiles
+// KT a .. KT a + KT - 1 of the block's state, KT = 8 / H_CW, as 16 x 16
+// tiles (tile t: lane l holds key 16t + 4(l/16) + v, column l % 16, in
+// element v), and forms new_v for token tiles TT a .. TT a + TT - 1,
+// TT = 4 / H_CW (16 tokens each).
 //
 // Per chunk, on 16 x 16 x 32 bf16 MFMAs: the compute waves stage their state
 // as bf16 operands, so each forms new_v = U - W S for its token half over all
@@ -537,7 +539,10 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
 // same order.
 template <int WA>
 __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, int cb, char *lds) {
+    static_assert(H_CW == 2 || H_CW == 4, "two or four compute waves");
     constexpr int wa = WA;
+    constexpr int KT = 8 / H_CW;  // key tiles of this wave
+    constexpr int TT = 4 / H_CW;  // token tiles of this wave
     const int H = p.c.H;
     const ChainSeq c = chain_seq(p, seq);
     const int l = threadIdx.x & 63;
@@ -546,14 +551,14 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
     const int64_t sl = (int64_t)D * D;
     const int col = H_COLS * cb + lc;
 
-    f32x4 S[4];
+    f32x4 S[KT];
     {
         const float *src = p.c.s0 ? p.c.s0 + ((int64_t)seq * H + h) * sl : nullptr;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < KT; ++t)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                S[t][v] = src ? src[(64 * wa + 16 * t + 4 * g + v) * D + col] : 0.f;
+                S[t][v] = src ? src[(16 * (KT * wa + t) + 4 * g + v) * D + col] : 0.f;
     }
 
     // The k values lane group g supplies in step ks of 32: 32 ks + o(g) + {0..3}
@@ -561,11 +566,11 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
     // (2 ks + g / 2, g % 2). Lane-constant parts of the transposing reads of
     // K^T (key tile t, the two 4-token halves).
     const int og = 16 * (g >> 1) + 4 * (g & 1);
-    int trk[4][2];
+    int trk[KT][2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < KT; ++t)
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) trk[t][hf] = tr_src(og + 8 * hf, 64 * wa + 16 * t, lc);
+        for (int hf = 0; hf < 2; ++hf) trk[t][hf] = tr_src(og + 8 * hf, 16 * (KT * wa + t), lc);
 
     const int nch = c.len > 0 ? c.nch : 0;
     for (int j = 0; j < nch; ++j) {
@@ -577,34 +582,34 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
         // exp(G_last - G) of token l, once per token
         lds_st(lds, H_E + 256 * wa + 4 * l, __expf(Gl - G));
 
-        // This wave's state tiles as bf16 stage pieces: key tile 4wa + t,
-        // lane group g -> piece (4wa + t, g % 2), half g / 2.
+        // This wave's state tiles as bf16 stage pieces: key tile KT wa + t,
+        // lane group g -> piece (KT wa + t, g % 2), half g / 2.
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < KT; ++t) {
             const bf16x4 x = {(__bf16)S[t][0], (__bf16)S[t][1], (__bf16)S[t][2], (__bf16)S[t][3]};
-            lds_st(lds, H_SS + stage_off(4 * wa + t, g & 1, lc) + 8 * (g >> 1), x);
+            lds_st(lds, H_SS + stage_off(KT * wa + t, g & 1, lc) + 8 * (g >> 1), x);
         }
-        __syncthreads();  // both halves of the state are staged
+        __syncthreads();  // the whole state is staged
 
-        // new_v = U - W S for token tiles 2wa, 2wa + 1 over all key rows.
-        f32x4 acc[2] = {};
+        // new_v = U - W S for this wave's token tiles over all key rows.
+        f32x4 acc[TT] = {};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const bf16x8 sb = lds_ld<bf16x8>(lds, H_SS + stage_off(2 * ks + (g >> 1), g & 1, lc));
             const int c1 = 4 * ks + 2 * (g >> 1);
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int i = 16 * (2 * wa + tt) + lc;
+            for (int tt = 0; tt < TT; ++tt) {
+                const int i = 16 * (TT * wa + tt) + lc;
                 const bf16x4 x0 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c1) + 8 * (g & 1));
                 const bf16x4 x1 = lds_ld<bf16x4>(buf, HB_W + row_off(i, c1 + 1) + 8 * (g & 1));
                 acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat4(x0, x1), sb, acc[tt], 0, 0, 0);
             }
         }
         // Its bf16 image for the output kernel, and exp(G_last - G) new_v as
-        // high and low bf16 parts for both waves' updates.
+        // high and low bf16 parts for every wave's update.
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const int q = 2 * wa + tt;  // token tile
+        for (int tt = 0; tt < TT; ++tt) {
+            const int q = TT * wa + tt;  // token tile
             const float4 u = lds_ld<float4>(buf, HB_U + 1024 * q + 16 * l);
             const float4 e = lds_ld<float4>(lds, H_E + 256 * wa + 4 * (16 * q + 4 * g));
             const float uq[4] = {u.x, u.y, u.z, u.w};
@@ -623,19 +628,19 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
             lds_st(lds, H_XH + so, xh);
             lds_st(lds, H_XL + so, xl);
         }
-        __syncthreads();  // both token halves of new_v are staged
+        __syncthreads();  // every token tile of new_v is staged
 
         if (j + 1 < nch || p.c.sfin) {
             const float a = __expf(Gl);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) S[t] *= a;
+            for (int t = 0; t < KT; ++t) S[t] *= a;
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int so = stage_off(2 * ks + (g >> 1), g & 1, lc);
                 const bf16x8 xh = lds_ld<bf16x8>(lds, H_XH + so);
                 const bf16x8 xl = lds_ld<bf16x8>(lds, H_XL + so);
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
+                for (int t = 0; t < KT; ++t) {
                     const bf16x8 kt = cat4(lds_tr(buf, HB_K + 8192 * ks + trk[t][0]),
                                            lds_tr(buf, HB_K + 8192 * ks + trk[t][1]));
                     S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt, xh, S[t], 0, 0, 0);
@@ -648,9 +653,9 @@ __device__ __forceinline__ void chain_wave(const GdnParams &p, int seq, int h, i
     if (p.c.sfin) {
         float *dst = p.c.sfin + ((int64_t)seq * H + h) * sl;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < KT; ++t)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) dst[(64 * wa + 16 * t + 4 * g + v) * D + col] = S[t][v];
+            for (int v = 0; v < 4; ++v) dst[(16 * (KT * wa + t) + 4 * g + v) * D + col] = S[t][v];
     }
 }
 
@@ -662,9 +667,11 @@ __global__ __launch_bounds__(H_THREADS) void gdn_chain_kernel(GdnParams p) {
     if (seq >= p.c.N) return;
     __shared__ __attribute__((aligned(16))) char lds[H_BYTES];
     const int w = threadIdx.x >> 6;
-    if (w >= 2) chain_mover(p, seq, h, cb, w - 2, lds);
+    if (w >= H_CW) chain_mover(p, seq, h, cb, w - H_CW, lds);
+    else if (w == 0) chain_wave<0>(p, seq, h, cb, lds);
     else if (w == 1) chain_wave<1>(p, seq, h, cb, lds);
-    else chain_wave<0>(p, seq, h, cb, lds);
+    else if (H_CW > 2 && w == 2) chain_wave<2 % H_CW>(p, seq, h, cb, lds);
+    else if (H_CW > 3) chain_wave<3 % H_CW>(p, seq, h, cb, lds);
 }
 
 // ---- gdn_output_kernel LDS map (bytes).
