@@ -61,14 +61,29 @@ CALL_KERNELS = {
 }
 
 
-def kernel_source_hash():
-    """sha256 over the library's kernel sources, to tell whether a stored
-    counter record still describes the kernels that are built."""
+# The sources each workload's kernels are built from, besides the shared ones
+# (headers, the host code that picks launch shapes, the build flags).
+WORKLOAD_SOURCES = {
+    PREFILL: ["chunk_mfma.hip", "chunk_plan.hip"],
+    PREFILL_PRO: ["chunk_mfma.hip", "chunk_plan.hip"],
+    DECODE: ["recurrent_step.hip"],
+    DECODE_PRO: ["recurrent_step.hip"],
+    DECODE_BF16: ["recurrent_step.hip"],
+    EPILOGUE: ["out_norm_gate.hip"],
+    GDN_PREFILL: ["gdn_chunk.hip"],
+    GDN_DECODE: ["gdn_step.hip"],
+}
+SHARED_SOURCES = ["sgla_internal.h", "mfma_tile.h", "sgla_host.hip", "../build.py"]
+
+
+def kernel_source_hash(workload):
+    """sha256 over the sources of one workload's kernels, to tell whether a
+    stored counter record still describes the kernels that are built."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_hybrid_amd", "csrc")
-    for path in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
-        h.update(os.path.basename(path).encode())
-        with open(path, "rb") as f:
+    for name in sorted(WORKLOAD_SOURCES[workload]) + SHARED_SOURCES:
+        h.update(name.encode())
+        with open(os.path.normpath(os.path.join(csrc, name)), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
@@ -82,7 +97,7 @@ def recorded_traffic(workload):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    if not entry or entry.get("source_hash") != kernel_source_hash():
+    if not entry or entry.get("source_hash") != kernel_source_hash(workload):
         return None
     return entry.get("bytes_per_call")
 
@@ -151,7 +166,6 @@ def record_traffic(fetch_dir, write_dir, calib_bytes=256 << 20):
         names = [n for n in table if pattern in n]
         return names[0] if len(names) == 1 else None
 
-    src = kernel_source_hash()
     rec = {"_calibration": {"fetch_scale": f_scale, "write_scale": w_scale,
                             "pass": "fp32 negation, %d bytes read and written" % calib_bytes}}
     for wl, parts in CALL_KERNELS.items():
@@ -163,7 +177,7 @@ def record_traffic(fetch_dir, write_dir, calib_bytes=256 << 20):
                 break
             kern[nf] = {"fetch": fetch[nf] * 1024.0 * f_scale, "write": write[nw] * 1024.0 * w_scale}
         if kern:
-            rec[wl] = {"source_hash": src, "kernels": kern,
+            rec[wl] = {"source_hash": kernel_source_hash(wl), "kernels": kern,
                        "bytes_per_call": sum(v["fetch"] + v["write"] for v in kern.values())}
     os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
     with open(TRAFFIC_RECORD, "w") as f:
