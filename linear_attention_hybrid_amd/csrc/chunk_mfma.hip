@@ -49,14 +49,16 @@ constexpr int LDS_OUT = OFF_G + 256;
 constexpr int LDS_STATE = 32768;  // KT and VT only (state phase, placed at 0)
 // q/k prologue tables, after the kernel's own LDS: RMSNorm weights of q and
 // k (2 x 128 fp32), RoPE turns per position per frequency (64 fp64 and the
-// same as fp32), cos and sin of one position's turn per frequency (64 x 2
-// fp32), and each wave's base turns of the current chunk (4 x 64 fp32).
+// same as fp32), cos and sin of one position's and of 32 positions' turn per
+// frequency (2 x 64 x 2 fp32), and each wave's base turns of the current
+// chunk (4 x 64 fp32).
 constexpr int PRO_W = 0;
 constexpr int PRO_OM = 1024;
 constexpr int PRO_OREV = 1536;
 constexpr int PRO_ROT = 1792;
-constexpr int PRO_BASE = 2304;
-constexpr int PRO_BYTES = 3328;
+constexpr int PRO_ROT32 = 2304;
+constexpr int PRO_BASE = 2816;
+constexpr int PRO_BYTES = 3840;
 
 // The prologue of one 16-byte piece (8 consecutive dims 8c .. 8c+7 of a
 // 128-dim row, c = lane & 15) held by each of the 16 lanes of a DPP row:
@@ -194,6 +196,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
             lds_st(lds, kBase + PRO_OREV + 4 * tid, (float)om);
             const double t = 6.283185307179586477 * (om - rint(om));
             lds_st(lds, kBase + PRO_ROT + 8 * tid, make_float2((float)cos(t), (float)sin(t)));
+            const double t32 = 6.283185307179586477 * (32.0 * om - rint(32.0 * om));
+            lds_st(lds, kBase + PRO_ROT32 + 8 * tid, make_float2((float)cos(t32), (float)sin(t32)));
         }
         pos0 = (p.pos_off ? (int64_t)p.pos_off[se.seq] : 0) + (int64_t)se.p * p.seg_len;
         __syncthreads();
@@ -245,33 +249,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
                                  sg * b1.x, sg * b1.y, sg * b1.z, sg * b1.w};
             const float om[8] = {sg * f0.x, sg * f0.y, sg * f0.z, sg * f0.w,
                                  sg * f1.x, sg * f1.y, sg * f1.z, sg * f1.w};
-            // Rows 2prb and 2prb + 32 from the hardware sine/cosine, rows
-            // 2prb + 1 and 2prb + 33 by one more position's turn.
-            float cs[2][2][8], sn[2][2][8];
+            // Row 2prb from the hardware sine/cosine; rows 2prb + 1, + 32 and
+            // + 33 by turning it one, 32 and 33 positions further. Each row's
+            // values are formed just before its pieces use them.
+            float c0[8], s0[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float2 rot = lds_ld<float2>(lds, kBase + PRO_ROT + 2 * fb + 8 * e);
-                const float r1s = sg * rot.y;
-#pragma unroll
-                for (int it = 0; it < 2; ++it) {
-                    const float a = fmaf((float)(2 * (prb + 16 * it)), om[e], bt[e]);
-                    const float c0 = cos_turns(a), s0 = sin_turns(a);
-                    cs[it][0][e] = c0;
-                    sn[it][0][e] = s0;
-                    cs[it][1][e] = fmaf(c0, rot.x, -s0 * r1s);
-                    sn[it][1][e] = fmaf(s0, rot.x, c0 * r1s);
-                }
+                const float a = fmaf((float)(2 * prb), om[e], bt[e]);
+                c0[e] = cos_turns(a);
+                s0[e] = sin_turns(a);
             }
 #pragma unroll
             for (int it = 0; it < 2; ++it)
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr) {
+                    float cs[8], sn[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float c = c0[e], sv = s0[e];
+                        if (it) {
+                            const float2 r32 = lds_ld<float2>(lds, kBase + PRO_ROT32 + 2 * fb + 8 * e);
+                            const float rs = sg * r32.y;
+                            const float cn = fmaf(c, r32.x, -sv * rs);
+                            sv = fmaf(sv, r32.x, c * rs);
+                            c = cn;
+                        }
+                        if (rr) {
+                            const float2 rot = lds_ld<float2>(lds, kBase + PRO_ROT + 2 * fb + 8 * e);
+                            const float rs = sg * rot.y;
+                            const float cn = fmaf(c, rot.x, -sv * rs);
+                            sv = fmaf(sv, rot.x, c * rs);
+                            c = cn;
+                        }
+                        cs[e] = c;
+                        sn[e] = sv;
+                    }
                     const int r = 2 * (prb + 16 * it) + rr;
                     kr[it][rr] = qk_prologue_piece(kr[it][rr], lds, kBase + PRO_W + 512 + 32 * cidx,
-                                                   cs[it][rr], sn[it][rr], r < n, p.eps);
+                                                   cs, sn, r < n, p.eps);
                     if (!STATE_ONLY)
                         qr[it][rr] = qk_prologue_piece(qr[it][rr], lds, kBase + PRO_W + 32 * cidx,
-                                                       cs[it][rr], sn[it][rr], r < n, p.eps);
+                                                       cs, sn, r < n, p.eps);
                 }
         }
 
