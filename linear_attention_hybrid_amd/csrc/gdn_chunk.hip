@@ -14,8 +14,8 @@
 //   S     = exp(G_last) S + (K * exp(G_last - G))^T new_v
 //
 // W and U depend on the chunk alone, so they are computed for every chunk at
-// once by a first kernel (gdn_prep_kernel), one workgroup per (chunk, head),
-// and kept in a workspace (W in bf16, an MFMA operand; U in fp32). The state
+// once by a first kernel (gdn_prep_kernel, persistent over the (chunk, head)
+// items) and kept in a workspace (W in bf16, an MFMA operand; U in fp32). The state
 // recurrence is sequential over chunks: gdn_chain_kernel walks each
 // (sequence, head, block of 16 value columns) through its chunks with the
 // fp32 state in the MFMA accumulators. A last kernel (gdn_output_kernel)
@@ -26,7 +26,8 @@
 // (beta v already is not), so the update takes exp(G_last - G) new_v in fp32
 // split into a bf16 high and low part against the exact bf16 K: the write
 // into the state keeps about 16 bits. The output products use bf16 operands
-// (state, scores, new_v) as the Simple GLA kernels do.
+// for the state and new_v, as the Simple GLA kernels do, and bf16 high and
+// low parts for the scores.
 //
 // The inverse T is found in fp32 in 16 x 16 blocks. Each wave inverts one
 // diagonal block by back substitution on its transpose, whose solution for
@@ -143,208 +144,208 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
 
     fetch(blockIdx.x);
     for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int s = item / H;
-    const int h = item - s * H;
-    const int n = fn;  // <= 64
-    if (n > 0) {
-        const float G = wave_prefix_sum(gv);
-        if (w == 0) {
-            lds_st(lds, P_G + 4 * l, G);
-            lds_st(lds, P_B + 4 * l, bv);
-        } else if (w == 1) {
-            lds_st(lds, P_E + 4 * l, __expf(G));
-        }
+        const int s = item / H;
+        const int h = item - s * H;
+        const int n = fn;  // <= 64
+        if (n > 0) {
+            const float G = wave_prefix_sum(gv);
+            if (w == 0) {
+                lds_st(lds, P_G + 4 * l, G);
+                lds_st(lds, P_B + 4 * l, bv);
+            } else if (w == 1) {
+                lds_st(lds, P_E + 4 * l, __expf(G));
+            }
 #pragma unroll
-        for (int it = 0; it < 2; ++it) {
+            for (int it = 0; it < 2; ++it) {
 #pragma unroll
-            for (int rr = 0; rr < 2; ++rr)
-                lds_st(lds, P_K + row_off(2 * (prb + 16 * it) + rr, cidx), kr[it][rr]);
-            const int r0 = 2 * (prb + 16 * it);
-            const int cb = (r0 & 7) * 2;  // byte offset of the token pair inside its 8-token piece
+                for (int rr = 0; rr < 2; ++rr)
+                    lds_st(lds, P_K + row_off(2 * (prb + 16 * it) + rr, cidx), kr[it][rr]);
+                const int r0 = 2 * (prb + 16 * it);
+                const int cb = (r0 & 7) * 2;  // byte offset of the token pair inside its 8-token piece
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const int d = 8 * cidx + 2 * e2;
-                const uint32_t k0 = kr[it][0][e2], k1 = kr[it][1][e2];
-                const uint32_t v0 = vr[it][0][e2], v1 = vr[it][1][e2];
-                lds_st(lds, P_KT + tr_off(d, r0 >> 3) + cb, pack_lo(k0, k1));
-                lds_st(lds, P_KT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(k0, k1));
-                lds_st(lds, P_VT + tr_off(d, r0 >> 3) + cb, pack_lo(v0, v1));
-                lds_st(lds, P_VT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(v0, v1));
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int d = 8 * cidx + 2 * e2;
+                    const uint32_t k0 = kr[it][0][e2], k1 = kr[it][1][e2];
+                    const uint32_t v0 = vr[it][0][e2], v1 = vr[it][1][e2];
+                    lds_st(lds, P_KT + tr_off(d, r0 >> 3) + cb, pack_lo(k0, k1));
+                    lds_st(lds, P_KT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(k0, k1));
+                    lds_st(lds, P_VT + tr_off(d, r0 >> 3) + cb, pack_lo(v0, v1));
+                    lds_st(lds, P_VT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(v0, v1));
+                }
             }
         }
-    }
-    fetch(item + gridDim.x);
-    if (n <= 0) continue;
-    __syncthreads();
+        fetch(item + gridDim.x);
+        if (n <= 0) continue;
+        __syncthreads();
 
-    // A[i][m] = beta_i (k_i . k_m) exp(G_i - G_m) for i > m, else 0, row-major.
-    // K K^T is symmetric; with the m block as the A operand each lane holds
-    // one row i and four consecutive m per group. Waves 0-2 take the tiles
-    // (i block, m block) = (0,0), (1,0), (1,1); the tile with every i < m is
-    // never read.
-    if (w < 3) {
-        const int ib = w == 0 ? 0 : 1;
-        const int mb = w == 2 ? 1 : 0;
-        const int i = 32 * ib + ln;
-        const int mr = 32 * mb + ln;
-        f32x16 acc = {};
+        // A[i][m] = beta_i (k_i . k_m) exp(G_i - G_m) for i > m, else 0, row-major.
+        // K K^T is symmetric; with the m block as the A operand each lane holds
+        // one row i and four consecutive m per group. Waves 0-2 take the tiles
+        // (i block, m block) = (0,0), (1,0), (1,1); the tile with every i < m is
+        // never read.
+        if (w < 3) {
+            const int ib = w == 0 ? 0 : 1;
+            const int mb = w == 2 ? 1 : 0;
+            const int i = 32 * ib + ln;
+            const int mr = 32 * mb + ln;
+            f32x16 acc = {};
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const bf16x8 a = lds_ld<bf16x8>(lds, P_K + row_off(mr, 2 * st + lh));
-            const bf16x8 b = lds_ld<bf16x8>(lds, P_K + row_off(i, 2 * st + lh));
-            acc = mfma(a, b, acc);
-        }
-        const float Gi = lds_ld<float>(lds, P_G + 4 * i);
-        const float bi = lds_ld<float>(lds, P_B + 4 * i);
+            for (int st = 0; st < 8; ++st) {
+                const bf16x8 a = lds_ld<bf16x8>(lds, P_K + row_off(mr, 2 * st + lh));
+                const bf16x8 b = lds_ld<bf16x8>(lds, P_K + row_off(i, 2 * st + lh));
+                acc = mfma(a, b, acc);
+            }
+            const float Gi = lds_ld<float>(lds, P_G + 4 * i);
+            const float bi = lds_ld<float>(lds, P_B + 4 * i);
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const int m0 = 32 * mb + 8 * g4 + 4 * lh;
-            const float4 Gm = lds_ld<float4>(lds, P_G + 4 * m0);
-            const float gm[4] = {Gm.x, Gm.y, Gm.z, Gm.w};
-            float a[4];
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int m0 = 32 * mb + 8 * g4 + 4 * lh;
+                const float4 Gm = lds_ld<float4>(lds, P_G + 4 * m0);
+                const float gm[4] = {Gm.x, Gm.y, Gm.z, Gm.w};
+                float a[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                a[r] = (i > m0 + r) ? bi * acc[4 * g4 + r] * __expf(Gi - gm[r]) : 0.f;
-            lds_st(lds, P_A + i * A_ROW + 4 * m0, make_float4(a[0], a[1], a[2], a[3]));
-        }
-    }
-    __syncthreads();
-
-    // T = (I + A)^-1 in 16 x 16 blocks. The diagonal blocks first, one per
-    // wave: row r of T_ww solves (I + A_ww)^T y = e_r by right-looking back
-    // substitution (once y_j is final it leaves -A[j][m] y_j in every y_m,
-    // m < j; 15 dependent steps).
-    if (l < 16) {
-        float y[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) y[m] = m == l ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 15; j >= 1; --j) {
-#pragma unroll
-            for (int mq = 0; mq < j; mq += 4) {
-                const float4 a = lds_ld<float4>(lds, P_A + (16 * w + j) * A_ROW + 4 * (16 * w + mq));
-                if (mq + 0 < j) y[mq + 0] = fmaf(-a.x, y[j], y[mq + 0]);
-                if (mq + 1 < j) y[mq + 1] = fmaf(-a.y, y[j], y[mq + 1]);
-                if (mq + 2 < j) y[mq + 2] = fmaf(-a.z, y[j], y[mq + 2]);
-                if (mq + 3 < j) y[mq + 3] = fmaf(-a.w, y[j], y[mq + 3]);
+                for (int r = 0; r < 4; ++r)
+                    a[r] = (i > m0 + r) ? bi * acc[4 * g4 + r] * __expf(Gi - gm[r]) : 0.f;
+                lds_st(lds, P_A + i * A_ROW + 4 * m0, make_float4(a[0], a[1], a[2], a[3]));
             }
         }
+        __syncthreads();
+
+        // T = (I + A)^-1 in 16 x 16 blocks. The diagonal blocks first, one per
+        // wave: row r of T_ww solves (I + A_ww)^T y = e_r by right-looking back
+        // substitution (once y_j is final it leaves -A[j][m] y_j in every y_m,
+        // m < j; 15 dependent steps).
+        if (l < 16) {
+            float y[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            lds_st(lds, tb_off(w, w) + l * TB_ROW + 16 * q,
-                   make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]));
-    }
-    __syncthreads();
-    // Then block row by block row: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,
-    // wave J taking column block J (waves J >= I wait at this level). Each
-    // 16 x 16 x 16 product is four fp32 16 x 16 x 4 MFMAs: lane l supplies
-    // L[l % 16][4k + l / 16] and R[4k + l / 16][l % 16] and receives
-    // D[4 (l / 16) + v][l % 16] in element v.
-    {
-        const int lr = l & 15;
-        const int lk = l >> 4;
+            for (int m = 0; m < 16; ++m) y[m] = m == l ? 1.f : 0.f;
 #pragma unroll
-        for (int I = 1; I < 4; ++I) {
-            if (w < I) {
-                const int J = w;
-                f32x4 x = {0.f, 0.f, 0.f, 0.f};
-                for (int K = J; K < I; ++K)
+            for (int j = 15; j >= 1; --j) {
+#pragma unroll
+                for (int mq = 0; mq < j; mq += 4) {
+                    const float4 a = lds_ld<float4>(lds, P_A + (16 * w + j) * A_ROW + 4 * (16 * w + mq));
+                    if (mq + 0 < j) y[mq + 0] = fmaf(-a.x, y[j], y[mq + 0]);
+                    if (mq + 1 < j) y[mq + 1] = fmaf(-a.y, y[j], y[mq + 1]);
+                    if (mq + 2 < j) y[mq + 2] = fmaf(-a.z, y[j], y[mq + 2]);
+                    if (mq + 3 < j) y[mq + 3] = fmaf(-a.w, y[j], y[mq + 3]);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                lds_st(lds, tb_off(w, w) + l * TB_ROW + 16 * q,
+                       make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]));
+        }
+        __syncthreads();
+        // Then block row by block row: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,
+        // wave J taking column block J (waves J >= I wait at this level). Each
+        // 16 x 16 x 16 product is four fp32 16 x 16 x 4 MFMAs: lane l supplies
+        // L[l % 16][4k + l / 16] and R[4k + l / 16][l % 16] and receives
+        // D[4 (l / 16) + v][l % 16] in element v.
+        {
+            const int lr = l & 15;
+            const int lk = l >> 4;
+#pragma unroll
+            for (int I = 1; I < 4; ++I) {
+                if (w < I) {
+                    const int J = w;
+                    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+                    for (int K = J; K < I; ++K)
+#pragma unroll
+                        for (int k4 = 0; k4 < 4; ++k4) {
+                            const float a = lds_ld<float>(lds, P_A + (16 * I + lr) * A_ROW + 64 * K + 4 * (4 * k4 + lk));
+                            const float b = lds_ld<float>(lds, tb_off(K, J) + (4 * k4 + lk) * TB_ROW + 4 * lr);
+                            x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
+                        }
+                    // X to this wave's scratch block, row-major (a wave's LDS
+                    // accesses take effect in order), then T_II X.
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) lds_st(lds, P_X + 1280 * w + (4 * lk + v) * TB_ROW + 4 * lr, x[v]);
+                    f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int k4 = 0; k4 < 4; ++k4) {
-                        const float a = lds_ld<float>(lds, P_A + (16 * I + lr) * A_ROW + 64 * K + 4 * (4 * k4 + lk));
-                        const float b = lds_ld<float>(lds, tb_off(K, J) + (4 * k4 + lk) * TB_ROW + 4 * lr);
-                        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
+                        const float a = lds_ld<float>(lds, tb_off(I, I) + lr * TB_ROW + 4 * (4 * k4 + lk));
+                        const float b = lds_ld<float>(lds, P_X + 1280 * w + (4 * k4 + lk) * TB_ROW + 4 * lr);
+                        t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t, 0, 0, 0);
                     }
-                // X to this wave's scratch block, row-major (a wave's LDS
-                // accesses take effect in order), then T_II X.
 #pragma unroll
-                for (int v = 0; v < 4; ++v) lds_st(lds, P_X + 1280 * w + (4 * lk + v) * TB_ROW + 4 * lr, x[v]);
-                f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) {
-                    const float a = lds_ld<float>(lds, tb_off(I, I) + lr * TB_ROW + 4 * (4 * k4 + lk));
-                    const float b = lds_ld<float>(lds, P_X + 1280 * w + (4 * k4 + lk) * TB_ROW + 4 * lr);
-                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t, 0, 0, 0);
+                    for (int v = 0; v < 4; ++v) lds_st(lds, tb_off(I, J) + (4 * lk + v) * TB_ROW + 4 * lr, -t[v]);
                 }
-#pragma unroll
-                for (int v = 0; v < 4; ++v) lds_st(lds, tb_off(I, J) + (4 * lk + v) * TB_ROW + 4 * lr, -t[v]);
+                __syncthreads();
             }
-            __syncthreads();
         }
-    }
 
-    // T'[c][m] = T[c][m] beta_m exp(G_m) and T''[c][m] = T[c][m] beta_m, each
-    // as a bf16 high part and the bf16 rounding of the rest: wave w forms
-    // columns 16w .. 16w + 15 (block column w) of every row c = l.
-    {
-        const int I = l >> 4;
-        const int r = l & 15;
-        const bool ok = w <= I;
-        float y[16];
+        // T'[c][m] = T[c][m] beta_m exp(G_m) and T''[c][m] = T[c][m] beta_m, each
+        // as a bf16 high part and the bf16 rounding of the rest: wave w forms
+        // columns 16w .. 16w + 15 (block column w) of every row c = l.
+        {
+            const int I = l >> 4;
+            const int r = l & 15;
+            const bool ok = w <= I;
+            float y[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 v = lds_ld<float4>(lds, (ok ? tb_off(I, w) : 0) + r * TB_ROW + 16 * q);
-            y[4 * q + 0] = ok ? v.x : 0.f;
-            y[4 * q + 1] = ok ? v.y : 0.f;
-            y[4 * q + 2] = ok ? v.z : 0.f;
-            y[4 * q + 3] = ok ? v.w : 0.f;
-        }
-        __syncthreads();  // every block is read before the T' parts overwrite them
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-            const int q = 2 * w + q2;  // columns 8q .. 8q + 7
-            const float4 E0 = lds_ld<float4>(lds, P_E + 32 * q);
-            const float4 E1 = lds_ld<float4>(lds, P_E + 32 * q + 16);
-            const float4 B0 = lds_ld<float4>(lds, P_B + 32 * q);
-            const float4 B1 = lds_ld<float4>(lds, P_B + 32 * q + 16);
-            const float eq[8] = {E0.x, E0.y, E0.z, E0.w, E1.x, E1.y, E1.z, E1.w};
-            const float bq[8] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
-            bf16x8 ph, pl, qh, ql;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float tq = y[8 * q2 + e] * bq[e];
-                const float tp = tq * eq[e];
-                ph[e] = (__bf16)tp;
-                pl[e] = (__bf16)(tp - (float)ph[e]);
-                qh[e] = (__bf16)tq;
-                ql[e] = (__bf16)(tq - (float)qh[e]);
+            for (int q = 0; q < 4; ++q) {
+                const float4 v = lds_ld<float4>(lds, (ok ? tb_off(I, w) : 0) + r * TB_ROW + 16 * q);
+                y[4 * q + 0] = ok ? v.x : 0.f;
+                y[4 * q + 1] = ok ? v.y : 0.f;
+                y[4 * q + 2] = ok ? v.z : 0.f;
+                y[4 * q + 3] = ok ? v.w : 0.f;
             }
-            lds_st(lds, P_TPH + tr_off(l, q), ph);
-            lds_st(lds, P_TPL + tr_off(l, q), pl);
-            lds_st(lds, P_TQH + tr_off(l, q), qh);
-            lds_st(lds, P_TQL + tr_off(l, q), ql);
+            __syncthreads();  // every block is read before the T' parts overwrite them
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int q = 2 * w + q2;  // columns 8q .. 8q + 7
+                const float4 E0 = lds_ld<float4>(lds, P_E + 32 * q);
+                const float4 E1 = lds_ld<float4>(lds, P_E + 32 * q + 16);
+                const float4 B0 = lds_ld<float4>(lds, P_B + 32 * q);
+                const float4 B1 = lds_ld<float4>(lds, P_B + 32 * q + 16);
+                const float eq[8] = {E0.x, E0.y, E0.z, E0.w, E1.x, E1.y, E1.z, E1.w};
+                const float bq[8] = {B0.x, B0.y, B0.z, B0.w, B1.x, B1.y, B1.z, B1.w};
+                bf16x8 ph, pl, qh, ql;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float tq = y[8 * q2 + e] * bq[e];
+                    const float tp = tq * eq[e];
+                    ph[e] = (__bf16)tp;
+                    pl[e] = (__bf16)(tp - (float)ph[e]);
+                    qh[e] = (__bf16)tq;
+                    ql[e] = (__bf16)(tq - (float)qh[e]);
+                }
+                lds_st(lds, P_TPH + tr_off(l, q), ph);
+                lds_st(lds, P_TPL + tr_off(l, q), pl);
+                lds_st(lds, P_TQH + tr_off(l, q), qh);
+                lds_st(lds, P_TQL + tr_off(l, q), ql);
+            }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // Wave w: W^T = K^T T'^T for dk rows [32w, 32w + 32) (stored as W rows,
-    // token-major), and U = T'' V for value columns [32w, 32w + 32) (fp32, in
-    // the pieces of slice w). Rows past the chunk's end come out zero.
-    uint16_t *wt = reinterpret_cast<uint16_t *>(tile_at(p, s, h));
-    float *ut = reinterpret_cast<float *>(tile_at(p, s, h) + T_U);
+        // Wave w: W^T = K^T T'^T for dk rows [32w, 32w + 32) (stored as W rows,
+        // token-major), and U = T'' V for value columns [32w, 32w + 32) (fp32, in
+        // the pieces of slice w). Rows past the chunk's end come out zero.
+        uint16_t *wt = reinterpret_cast<uint16_t *>(tile_at(p, s, h));
+        float *ut = reinterpret_cast<float *>(tile_at(p, s, h) + T_U);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        f32x16 aw = {}, au = {};
+        for (int nt = 0; nt < 2; ++nt) {
+            f32x16 aw = {}, au = {};
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const bf16x8 kt = lds_ld<bf16x8>(lds, P_KT + tr_off(32 * w + ln, 2 * st + lh));
-            const bf16x8 vt = lds_ld<bf16x8>(lds, P_VT + tr_off(32 * w + ln, 2 * st + lh));
-            const int ti = 32 * nt + ln;
-            aw = mfma(kt, lds_ld<bf16x8>(lds, P_TPH + tr_off(ti, 2 * st + lh)), aw);
-            aw = mfma(kt, lds_ld<bf16x8>(lds, P_TPL + tr_off(ti, 2 * st + lh)), aw);
-            au = mfma(lds_ld<bf16x8>(lds, P_TQH + tr_off(ti, 2 * st + lh)), vt, au);
-            au = mfma(lds_ld<bf16x8>(lds, P_TQL + tr_off(ti, 2 * st + lh)), vt, au);
+            for (int st = 0; st < 4; ++st) {
+                const bf16x8 kt = lds_ld<bf16x8>(lds, P_KT + tr_off(32 * w + ln, 2 * st + lh));
+                const bf16x8 vt = lds_ld<bf16x8>(lds, P_VT + tr_off(32 * w + ln, 2 * st + lh));
+                const int ti = 32 * nt + ln;
+                aw = mfma(kt, lds_ld<bf16x8>(lds, P_TPH + tr_off(ti, 2 * st + lh)), aw);
+                aw = mfma(kt, lds_ld<bf16x8>(lds, P_TPL + tr_off(ti, 2 * st + lh)), aw);
+                au = mfma(lds_ld<bf16x8>(lds, P_TQH + tr_off(ti, 2 * st + lh)), vt, au);
+                au = mfma(lds_ld<bf16x8>(lds, P_TQL + tr_off(ti, 2 * st + lh)), vt, au);
+            }
+            const int i = 32 * nt + ln;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const u32x2 pw = {pack_f32(aw[4 * g4], aw[4 * g4 + 1]), pack_f32(aw[4 * g4 + 2], aw[4 * g4 + 3])};
+                *reinterpret_cast<u32x2 *>(wt + i * D + 32 * w + 8 * g4 + 4 * lh) = pw;
+                *reinterpret_cast<float4 *>(ut + ((w * 8 + 4 * nt + g4) * 64 + l) * 4) =
+                    make_float4(au[4 * g4], au[4 * g4 + 1], au[4 * g4 + 2], au[4 * g4 + 3]);
+            }
         }
-        const int i = 32 * nt + ln;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-            const u32x2 pw = {pack_f32(aw[4 * g4], aw[4 * g4 + 1]), pack_f32(aw[4 * g4 + 2], aw[4 * g4 + 3])};
-            *reinterpret_cast<u32x2 *>(wt + i * D + 32 * w + 8 * g4 + 4 * lh) = pw;
-            *reinterpret_cast<float4 *>(ut + ((w * 8 + 4 * nt + g4) * 64 + l) * 4) =
-                make_float4(au[4 * g4], au[4 * g4 + 1], au[4 * g4 + 2], au[4 * g4 + 3]);
-        }
-    }
-    __syncthreads();  // LDS is free for the next item
+        __syncthreads();  // LDS is free for the next item
     }
 }
 
