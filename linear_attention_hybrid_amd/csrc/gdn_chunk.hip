@@ -178,34 +178,34 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
         if (n <= 0) continue;
         __syncthreads();
 
-        // A[i][m] = beta_i (k_i . k_m) exp(G_i - G_m) for i > m, else 0, row-major.
-        // K K^T is symmetric; with the m block as the A operand each lane holds
-        // one row i and four consecutive m per group. Waves 0-2 take the tiles
-        // (i block, m block) = (0,0), (1,0), (1,1); the tile with every i < m is
-        // never read.
-        if (w < 3) {
-            const int ib = w == 0 ? 0 : 1;
-            const int mb = w == 2 ? 1 : 0;
-            const int i = 32 * ib + ln;
-            const int mr = 32 * mb + ln;
-            f32x16 acc = {};
+        // A[i][m] = beta_i (k_i . k_m) exp(G_i - G_m) for i > m, else 0, row-major,
+        // as the ten 16 x 16 blocks (I, J), J <= I, spread over the four waves
+        // (the blocks with J > I are never read). K K^T is symmetric; with the m
+        // block as the A operand each lane holds one row i and four consecutive
+        // m.
+        {
+            const int lc = l & 15;
+            const int g = l >> 4;
+            for (int bi = w; bi < 10; bi += 4) {
+                const int I = bi >= 6 ? 3 : bi >= 3 ? 2 : bi >= 1 ? 1 : 0;
+                const int J = bi - I * (I + 1) / 2;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const bf16x8 a = lds_ld<bf16x8>(lds, P_K + row_off(mr, 2 * st + lh));
-                const bf16x8 b = lds_ld<bf16x8>(lds, P_K + row_off(i, 2 * st + lh));
-                acc = mfma(a, b, acc);
-            }
-            const float Gi = lds_ld<float>(lds, P_G + 4 * i);
-            const float bi = lds_ld<float>(lds, P_B + 4 * i);
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-                const int m0 = 32 * mb + 8 * g4 + 4 * lh;
+                for (int ks = 0; ks < 4; ++ks) {
+                    const bf16x8 a = lds_ld<bf16x8>(lds, P_K + row_off(16 * J + lc, 4 * ks + g));
+                    const bf16x8 b = lds_ld<bf16x8>(lds, P_K + row_off(16 * I + lc, 4 * ks + g));
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+                }
+                const int i = 16 * I + lc;
+                const int m0 = 16 * J + 4 * g;
+                const float Gi = lds_ld<float>(lds, P_G + 4 * i);
+                const float bti = lds_ld<float>(lds, P_B + 4 * i);
                 const float4 Gm = lds_ld<float4>(lds, P_G + 4 * m0);
                 const float gm[4] = {Gm.x, Gm.y, Gm.z, Gm.w};
                 float a[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    a[r] = (i > m0 + r) ? bi * acc[4 * g4 + r] * __expf(Gi - gm[r]) : 0.f;
+                    a[r] = (i > m0 + r) ? bti * acc[r] * __expf(Gi - gm[r]) : 0.f;
                 lds_st(lds, P_A + i * A_ROW + 4 * m0, make_float4(a[0], a[1], a[2], a[3]));
             }
         }
