@@ -291,8 +291,8 @@ sgla_status sgla_out_norm_gate(const void *o, const void *z, const float *weight
  *
  * Arguments: as sgla_chunk_fwd, plus
  *   beta   [B, T, H] fp32 (packed [T, H] with cu_seqlens), 4-byte aligned.
- * Only dtype SGLA_BF16 with Dk = Dv = 128 is supported (SGLA_ERR_UNSUPPORTED
- * otherwise).
+ * Only dtype SGLA_BF16 with Dk = Dv = 128 and B * H <= 2^28 - 8 (B the
+ * number of sequences) is supported (SGLA_ERR_UNSUPPORTED otherwise).
  *
  * Memory: the call takes a device workspace from HIP's stream-ordered
  * allocator on `stream` of (T / 64 + B + 1) * H * 64 KiB (per chunk and head

@@ -115,12 +115,12 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
     u32x4 kr[2][2], vr[2][2];
     float gv, bv;
     int fn;  // the fetched item's token count
-    auto fetch = [&](int item) {
+    auto fetch = [&](int64_t item) {
         int n = 0, hh = 0;
         int64_t tok0 = 0;
         if (item < nitems) {
-            const int s = item / H;
-            hh = item - s * H;
+            const int s = (int)(item / H);
+            hh = (int)(item - (int64_t)s * H);
             const SegEntry se = seg_at(p.c, s);
             n = se.len;
             tok0 = se.tok0;
@@ -143,9 +143,10 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
     };
 
     fetch(blockIdx.x);
-    for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-        const int s = item / H;
-        const int h = item - s * H;
+    // 64-bit, so that item + gridDim.x cannot wrap for item counts near 2^31.
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const int s = (int)(item / H);
+        const int h = (int)(item - (int64_t)s * H);
         const int n = fn;  // <= 64
         if (n > 0) {
             const float G = wave_prefix_sum(gv);

@@ -293,6 +293,9 @@ sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
     const int64_t ttot = cu_seqlens ? (int64_t)T : (int64_t)B * T;
     if (ttot > ((int64_t)1 << 62) / ((int64_t)H * 128)) return SGLA_ERR_INVALID_ARG;
     if ((int64_t)B * H > (int64_t)1 << 30) return SGLA_ERR_INVALID_ARG;
+    // The chain kernel runs eight workgroups per (sequence, head), their count
+    // rounded up to a multiple of 64; the grid must stay below 2^31.
+    if ((int64_t)B * H > ((int64_t)1 << 28) - 8) return SGLA_ERR_UNSUPPORTED;
     if (ttot > 0 && (!q || !k || !v || !g || !beta || !out)) return SGLA_ERR_INVALID_ARG;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) ||
         misaligned(beta, 4) || misaligned(out) || misaligned(initial_state) ||

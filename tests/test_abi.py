@@ -233,6 +233,7 @@ def test_gdn_validation(lib):
     assert gdn_chunk(lib, beta=A + 4) == 0     # fp32 alignment is enough
     assert gdn_chunk(lib, cu=A + 4) == 1
     assert gdn_chunk(lib, B=1, T=1, H=2**16 + 1) == 2
+    assert gdn_chunk(lib, B=2**26, T=1, H=5) == 2    # the chain's grid would pass 2^31
     assert gdn_step(lib) == 0
     assert gdn_step(lib, Dk=64, Dv=64, dtype=0) == 0
     assert gdn_step(lib, Dk=96) == 2
