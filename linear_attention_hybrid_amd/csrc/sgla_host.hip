@@ -139,7 +139,9 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
     const bool table = cu_seqlens != nullptr;
     const int64_t nps64 = T == 0 ? 1 : ((int64_t)T + seg_len - 1) / seg_len;
     const int64_t nseg_max64 = table ? ttot / seg_len + B + 1 : (int64_t)B * nps64;
-    if (nseg_max64 * H > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+    // The vector-ALU kernels run one workgroup per 32 value columns of each
+    // (segment, head); every grid must stay below 2^31.
+    if (nseg_max64 * H * ((Dv + 31) / 32) > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
     const int nseg_max = (int)nseg_max64;
     // Sequences that fit in one segment need no segment states and no scan.
     const bool split = table || nps64 > 1;

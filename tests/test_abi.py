@@ -84,6 +84,9 @@ def test_chunk_fwd_validation(lib):
     assert chunk(lib, cu=A + 4) == 1
     assert chunk(lib, B=2**28, T=2**31 - 1, H=1, Dk=128, Dv=128) == 1  # B*T*H*D past 2^62
     assert chunk(lib, B=1, T=1, H=2**16 + 1) == 2                      # beyond the head limit
+    # 2^30 one-segment (sequence, head) units: the vector-ALU grid (four
+    # workgroups per unit at Dv = 128) would pass 2^31
+    assert chunk(lib, B=2**24, T=64, H=64, Dk=128, Dv=128) == 2
 
 
 @pytest.mark.skipif("not _no_gpu()", reason="could reach a launch if validation were wrong")
