@@ -371,7 +371,7 @@ constexpr int H_XL = H_XH + 2048;     // low part
 constexpr int H_E = H_XL + 2048;      // exp(G_last - G)[64], one copy per compute wave
 constexpr int H_CW = 2;               // compute waves
 constexpr int H_BYTES = H_E + H_CW * 256;
-constexpr int H_MOVERS = 4;           // waves that move data (after the two compute waves)
+constexpr int H_MOVERS = 4;           // waves that move data (after the compute waves)
 constexpr int H_THREADS = 64 * (H_CW + H_MOVERS);
 // Mover roles: every mover takes 16 / H_MOVERS of the W and of the k pieces;
 // movers 0..3 one U token tile each; H_SMOV.. H_SMOV + 3 one quarter of the
