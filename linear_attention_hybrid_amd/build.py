@@ -50,7 +50,9 @@ def build(verbose: bool = False) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIBRARY + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
+    # -z defs: an unresolved symbol (such as a kernel launch stub the host
+    # pass failed to emit) fails the link instead of the first load.
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-Wl,-z,defs", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))

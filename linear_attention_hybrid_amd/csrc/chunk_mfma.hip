@@ -25,8 +25,9 @@
 //
 // A workgroup is 4 waves; wave w owns value columns [32w, 32w+32) of the state
 // and of the output. Per chunk the workgroup streams q, k, v (16 KiB each) and
-// g from HBM with 16-byte loads, one chunk ahead of the compute (registers),
-// and stages them in LDS: Q and K row-major with 16-byte chunks XOR-swizzled by
+// g from HBM with 16-byte buffer loads, one chunk ahead of the compute
+// (registers); the buffer range check zeroes the rows past the end of a ragged
+// chunk and drops their output stores. It stages the tiles in LDS: Q and K row-major with 16-byte chunks XOR-swizzled by
 // row, K*exp(G_last-G) and V transposed (token-contiguous) with a swizzle that
 // keeps both the transposing writes and the MFMA operand reads spread over the
 // banks. LDS: 72 KiB for the output phase, so two workgroups fit on a CU.
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
 
     // Each thread moves two row pairs of 16-byte chunks per tile:
     // pair pr = (tid >> 4) + 16 * it, rows 2pr and 2pr+1, chunk cidx.
-    u32x4 qr[2][2], kr[2][2], vr[2][2];
+    u32x4 qr[2][2] = {}, kr[2][2] = {}, vr[2][2] = {};
     float gr = 0.f;
     // Byte offset of this thread's 16-byte piece of row r inside a chunk, the
     // same for q, k, v and out ([T, H, 128] rows of 256 bytes): 32-bit per
@@ -159,28 +160,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
     auto piece = [&](int r, int tv) -> uint32_t {
         return (uint32_t)(r * H) * (uint32_t)(D * 2) + (uint32_t)(tv & 15) * 16u;
     };
+    // Bytes from a chunk's first row to the end of its row n - 1 in q, k, v
+    // and out: the range of the chunk's buffer resources, so that rows past
+    // the end read as zeros and are not written (< 2^31 for H <= 65536).
+    auto rows_bytes = [&](int n) -> int { return (n - 1) * H * (D * 2) + D * 2; };
     auto issue = [&](int64_t t0, int n) {
         // Opaque copy of the thread index: the per-lane offsets are rebuilt
-        // here rather than kept as twelve 64-bit pointers across the loop.
+        // here rather than kept across the loop.
         int tv = tid;
         asm volatile("" : "+v"(tv));
         const int64_t base = (t0 * H + h) * D;
-        const char *qb = reinterpret_cast<const char *>(qg + base);
-        const char *kb = reinterpret_cast<const char *>(kg + base);
-        const char *vb = reinterpret_cast<const char *>(vg + base);
+        const int nb = rows_bytes(n);
+        const buf_t rq = buf_rsrc(qg + base, nb);
+        const buf_t rk = buf_rsrc(kg + base, nb);
+        const buf_t rv = buf_rsrc(vg + base, nb);
+        gr = buf_ld_f32(buf_rsrc(p.g + t0 * H + h, (n - 1) * H * 4 + 4), (tv & 63) * H * 4);
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
-                const int r = 2 * (((tv >> 4) & 15) + 16 * it) + rr;
-                const uint32_t off = piece(r, tv);
-                const bool ok = r < n;
-                kr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(kb + off) : u32x4{0, 0, 0, 0};
-                vr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(vb + off) : u32x4{0, 0, 0, 0};
-                if (!STATE_ONLY)
-                    qr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(qb + off) : u32x4{0, 0, 0, 0};
+                const uint32_t off = piece(2 * (((tv >> 4) & 15) + 16 * it) + rr, tv);
+                kr[it][rr] = buf_ld16(rk, off);
+                vr[it][rr] = buf_ld16(rv, off);
+                if (!STATE_ONLY) qr[it][rr] = buf_ld16(rq, off);
             }
-        gr = (tv & 63) < n ? p.g[(t0 + (tv & 63)) * H + h] : 0.f;
     };
 
     // Prologue tables, and the position of the segment's first token.
@@ -205,6 +208,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
 
     const int len = se.len;
     if (len > 0) issue(se.tok0, min(64, len));
+    // Everything loaded so far completes before the loop. The loop's own waits
+    // then cover only the next chunk's loads, and the output stores issued
+    // after them stay in flight across the loop's back edge.
+    settle(gr);
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            settle(kr[it][rr]);
+            settle(vr[it][rr]);
+            if (!STATE_ONLY) settle(qr[it][rr]);
+        }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) settle(S[b][v]);
     float gam_acc = 0.f;
 
     for (int c0 = 0; c0 < len; c0 += 64) {
@@ -414,16 +433,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
 
         if (!STATE_ONLY) {
             __syncthreads();  // O staging rows complete
+            const buf_t ro = buf_rsrc(og + (t0 * H + h) * D, rows_bytes(n));
 #pragma unroll
             for (int it = 0; it < 2; ++it)
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr) {
                     const int r = 2 * (prb + 16 * it) + rr;
-                    if (r < n) {
-                        const u32x4 o = lds_ld<u32x4>(lds, OFF_K + row_off(r, cidx));
-                        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(og + (t0 * H + h) * D) +
-                                                   piece(r, tidv)) = o;
-                    }
+                    buf_st16(ro, piece(r, tidv), lds_ld<u32x4>(lds, OFF_K + row_off(r, cidx)));
                 }
         }
     }

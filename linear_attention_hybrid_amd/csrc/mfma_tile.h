@@ -121,6 +121,32 @@ __device__ __forceinline__ void wait_vm_n(int n) {
     }
 }
 
+// A raw buffer resource over [base, base + bytes): the hardware's range check
+// makes loads past the end return zeros and drops stores past the end, so a
+// ragged tile needs no branch around its loads and stores. Word 3 selects
+// 32-bit data, which the untyped loads and stores of gfx9-family chips need.
+// bytes < 2^31; offsets are unsigned 32-bit.
+typedef __amdgpu_buffer_rsrc_t buf_t;
+__device__ __forceinline__ buf_t buf_rsrc(const void *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(buf_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ float buf_ld_f32(buf_t r, uint32_t off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_st16(buf_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+
+// A use of x that the compiler cannot see through, so it waits for x's load
+// here. Used before a loop so that the loop's own waits need not cover loads
+// from before it. x is a scalar or a 16-byte vector (the host pass parses the
+// constraint too).
+template <typename T>
+__device__ __forceinline__ void settle(const T &x) { asm volatile("" ::"v"(x)); }
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
 // i % 4 of the 8 bytes named by lane 4k + i / 4, for k = 0..3. With lane m of
 // the group naming row r0 + m / 4, columns c0 + 4 (m % 4) .. + 3 of a
