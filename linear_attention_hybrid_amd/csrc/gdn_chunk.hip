@@ -108,7 +108,6 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
     const int lh = l >> 5;
     const int cidx = tid & 15;
     const int prb = (tid >> 4) & 15;
-    const int64_t row_stride = (int64_t)H * D;
 
     // An item's k and v rows (each thread two row pairs of 16-byte pieces;
     // zero past the chunk's end), g and beta.
@@ -125,58 +124,75 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
             n = se.len;
             tok0 = se.tok0;
         }
+        // Buffer resources over the item's n rows: rows past the end (all of
+        // them past the last item) read as zeros, with no branch around the
+        // loads (< 2^31 bytes for H <= 65536).
         const int64_t base = (tok0 * H + hh) * D;
-        const uint16_t *kg = static_cast<const uint16_t *>(p.c.k) + base;
-        const uint16_t *vg = static_cast<const uint16_t *>(p.c.v) + base;
+        const int nb = n > 0 ? (n - 1) * H * (D * 2) + D * 2 : 0;
+        const buf_t rk = buf_rsrc(static_cast<const uint16_t *>(p.c.k) + base, nb);
+        const buf_t rv = buf_rsrc(static_cast<const uint16_t *>(p.c.v) + base, nb);
 #pragma unroll
         for (int it = 0; it < 2; ++it)
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
-                const int r = 2 * (prb + 16 * it) + rr;
-                const bool ok = r < n;
-                kr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(kg + r * row_stride + 8 * cidx) : u32x4{0, 0, 0, 0};
-                vr[it][rr] = ok ? *reinterpret_cast<const u32x4 *>(vg + r * row_stride + 8 * cidx) : u32x4{0, 0, 0, 0};
+                const uint32_t off = (uint32_t)((2 * (prb + 16 * it) + rr) * H) * (uint32_t)(D * 2) +
+                                     16u * (uint32_t)cidx;
+                kr[it][rr] = buf_ld16(rk, off);
+                vr[it][rr] = buf_ld16(rv, off);
             }
-        gv = l < n ? p.c.g[(tok0 + l) * H + hh] : 0.f;
-        bv = l < n ? p.beta[(tok0 + l) * H + hh] : 0.f;
+        const int gb = n > 0 ? (n - 1) * H * 4 + 4 : 0;
+        gv = buf_ld_f32(buf_rsrc(p.c.g + tok0 * H + hh, gb), (uint32_t)(l * H * 4));
+        bv = buf_ld_f32(buf_rsrc(p.beta + tok0 * H + hh, gb), (uint32_t)(l * H * 4));
         fn = __builtin_amdgcn_readfirstlane(n);
     };
 
     fetch(blockIdx.x);
+    // The first item's loads complete before the loop, so that the loop's own
+    // waits cover only the next item's loads and not the W and U stores
+    // issued after them.
+    settle(gv);
+    settle(bv);
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            settle(kr[it][rr]);
+            settle(vr[it][rr]);
+        }
     // 64-bit, so that item + gridDim.x cannot wrap for item counts near 2^31.
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
         const int s = (int)(item / H);
         const int h = (int)(item - (int64_t)s * H);
         const int n = fn;  // <= 64
-        if (n > 0) {
-            const float G = wave_prefix_sum(gv);
-            if (w == 0) {
-                lds_st(lds, P_G + 4 * l, G);
-                lds_st(lds, P_B + 4 * l, bv);
-            } else if (w == 1) {
-                lds_st(lds, P_E + 4 * l, __expf(G));
-            }
+        // Empty items (past the last one, or an empty table row) run the same
+        // code on zeros, and their stores are dropped, so that every path
+        // back to the loop top issues the same memory operations.
+        const float G = wave_prefix_sum(gv);
+        if (w == 0) {
+            lds_st(lds, P_G + 4 * l, G);
+            lds_st(lds, P_B + 4 * l, bv);
+        } else if (w == 1) {
+            lds_st(lds, P_E + 4 * l, __expf(G));
+        }
 #pragma unroll
-            for (int it = 0; it < 2; ++it) {
+        for (int it = 0; it < 2; ++it) {
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr)
-                    lds_st(lds, P_K + row_off(2 * (prb + 16 * it) + rr, cidx), kr[it][rr]);
-                const int r0 = 2 * (prb + 16 * it);
-                const int cb = (r0 & 7) * 2;  // byte offset of the token pair inside its 8-token piece
+            for (int rr = 0; rr < 2; ++rr)
+                lds_st(lds, P_K + row_off(2 * (prb + 16 * it) + rr, cidx), kr[it][rr]);
+            const int r0 = 2 * (prb + 16 * it);
+            const int cb = (r0 & 7) * 2;  // byte offset of the token pair inside its 8-token piece
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const int d = 8 * cidx + 2 * e2;
-                    const uint32_t k0 = kr[it][0][e2], k1 = kr[it][1][e2];
-                    const uint32_t v0 = vr[it][0][e2], v1 = vr[it][1][e2];
-                    lds_st(lds, P_KT + tr_off(d, r0 >> 3) + cb, pack_lo(k0, k1));
-                    lds_st(lds, P_KT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(k0, k1));
-                    lds_st(lds, P_VT + tr_off(d, r0 >> 3) + cb, pack_lo(v0, v1));
-                    lds_st(lds, P_VT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(v0, v1));
-                }
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const int d = 8 * cidx + 2 * e2;
+                const uint32_t k0 = kr[it][0][e2], k1 = kr[it][1][e2];
+                const uint32_t v0 = vr[it][0][e2], v1 = vr[it][1][e2];
+                lds_st(lds, P_KT + tr_off(d, r0 >> 3) + cb, pack_lo(k0, k1));
+                lds_st(lds, P_KT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(k0, k1));
+                lds_st(lds, P_VT + tr_off(d, r0 >> 3) + cb, pack_lo(v0, v1));
+                lds_st(lds, P_VT + tr_off(d + 1, r0 >> 3) + cb, pack_hi(v0, v1));
             }
         }
         fetch(item + gridDim.x);
-        if (n <= 0) continue;
         __syncthreads();
 
         // A[i][m] = beta_i (k_i . k_m) exp(G_i - G_m) for i > m, else 0, row-major,
@@ -322,8 +338,7 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
         // Wave w: W^T = K^T T'^T for dk rows [32w, 32w + 32) (stored as W rows,
         // token-major), and U = T'' V for value columns [32w, 32w + 32) (fp32, in
         // the pieces of slice w). Rows past the chunk's end come out zero.
-        uint16_t *wt = reinterpret_cast<uint16_t *>(tile_at(p, s, h));
-        float *ut = reinterpret_cast<float *>(tile_at(p, s, h) + T_U);
+        const buf_t rt = buf_rsrc(tile_at(p, s, h), n > 0 ? TILE_BYTES : 0);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             f32x16 aw = {}, au = {};
@@ -341,9 +356,10 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const u32x2 pw = {pack_f32(aw[4 * g4], aw[4 * g4 + 1]), pack_f32(aw[4 * g4 + 2], aw[4 * g4 + 3])};
-                *reinterpret_cast<u32x2 *>(wt + i * D + 32 * w + 8 * g4 + 4 * lh) = pw;
-                *reinterpret_cast<float4 *>(ut + ((w * 8 + 4 * nt + g4) * 64 + l) * 4) =
-                    make_float4(au[4 * g4], au[4 * g4 + 1], au[4 * g4 + 2], au[4 * g4 + 3]);
+                buf_st8(rt, 2 * (i * D + 32 * w + 8 * g4 + 4 * lh), pw);
+                const u32x4 pu = {__float_as_uint(au[4 * g4]), __float_as_uint(au[4 * g4 + 1]),
+                                  __float_as_uint(au[4 * g4 + 2]), __float_as_uint(au[4 * g4 + 3])};
+                buf_st16(rt, T_U + 16 * ((w * 8 + 4 * nt + g4) * 64 + l), pu);
             }
         }
         __syncthreads();  // LDS is free for the next item

@@ -139,6 +139,9 @@ __device__ __forceinline__ float buf_ld_f32(buf_t r, uint32_t off) {
 __device__ __forceinline__ void buf_st16(buf_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void buf_st8(buf_t r, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
 
 // A use of x that the compiler cannot see through, so it waits for x's load
 // here. Used before a loop so that the loop's own waits need not cover loads
