@@ -439,7 +439,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
 #pragma unroll
                 for (int rr = 0; rr < 2; ++rr) {
                     const int r = 2 * (prb + 16 * it) + rr;
-                    buf_st16(ro, piece(r, tidv), lds_ld<u32x4>(lds, OFF_K + row_off(r, cidx)));
+                    buf_st16_nt(ro, piece(r, tidv), lds_ld<u32x4>(lds, OFF_K + row_off(r, cidx)));
                 }
         }
     }

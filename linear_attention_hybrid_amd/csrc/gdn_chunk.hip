@@ -517,8 +517,11 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
         if (more) issue_w(jn);
         __syncthreads();  // the state operands are staged
         if (s_copy) {
+            // Non-temporal (as the new_v image below): the images are read only
+            // by the output kernel, and kept out of L2 they leave it to the W
+            // and k rows the head's other column blocks still read.
             const bf16x8 x = lds_ld<bf16x8>(lds, H_SS + 16 * sp);
-            *reinterpret_cast<bf16x8 *>(tile_at(p, c.first + j, h) + slice + s_img) = x;
+            __builtin_nontemporal_store(x, reinterpret_cast<bf16x8 *>(tile_at(p, c.first + j, h) + slice + s_img));
             ++issued;
         }
         if (more) issue_k(jn);
@@ -527,7 +530,8 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
         const int mark2 = issued;
         if (mv < 2) {
             const bf16x8 x = lds_ld<bf16x8>(lds, H_SN + 16 * np);
-            *reinterpret_cast<bf16x8 *>(p.nvimg + ((int64_t)(c.first + j) * H + h) * NV_BYTES + n_img) = x;
+            __builtin_nontemporal_store(
+                x, reinterpret_cast<bf16x8 *>(p.nvimg + ((int64_t)(c.first + j) * H + h) * NV_BYTES + n_img));
             ++issued;
         }
         mark[0] = mark[1];
@@ -836,8 +840,9 @@ __global__ __launch_bounds__(NT) void gdn_output_kernel(GdnParams p) {
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
             const int r = 2 * (prb + 16 * it) + rr;
-            if (r < n)
-                *reinterpret_cast<u32x4 *>(og + r * rs + 8 * cidx) = lds_ld<u32x4>(lds, O_K + row_off(r, cidx));
+            if (r < n)  // non-temporal: nothing in the call reads the output again
+                __builtin_nontemporal_store(lds_ld<u32x4>(lds, O_K + row_off(r, cidx)),
+                                            reinterpret_cast<u32x4 *>(og + r * rs + 8 * cidx));
         }
 }
 

@@ -139,6 +139,12 @@ __device__ __forceinline__ float buf_ld_f32(buf_t r, uint32_t off) {
 __device__ __forceinline__ void buf_st16(buf_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
+// Non-temporal store (the nt bit): for outputs that nothing in the same call
+// reads again, so that they do not push the call's re-read data out of the
+// caches.
+__device__ __forceinline__ void buf_st16_nt(buf_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 2);
+}
 __device__ __forceinline__ void buf_st8(buf_t r, uint32_t off, u32x2 v) {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
 }

@@ -50,12 +50,13 @@ __device__ __forceinline__ void store8<uint16_t>(uint16_t *p, const float v[8]) 
         const __bf16 a = (__bf16)v[2 * j], b = (__bf16)v[2 * j + 1];
         r[j] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
     }
-    *reinterpret_cast<u32x4 *>(p) = r;
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x4 *>(p));  // not read again here
 }
 template <>
 __device__ __forceinline__ void store8<float>(float *p, const float v[8]) {
-    reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-    reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(f32x4v{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4v *>(p));
+    __builtin_nontemporal_store(f32x4v{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4v *>(p) + 1);
 }
 
 template <typename T>
