@@ -208,21 +208,34 @@ def decode_bytes(N, H, Dk, Dv, elem=2, state_elem=4):
     return N * H * (2 * Dk * Dv * state_elem + (2 * Dk + Dv) * elem + 4 + Dv * elem)
 
 
-def time_calls(fn, steps, warmup, torch):
+def time_calls(fn, steps, warmup, torch, single_reps=20):
+    """Time `steps` back-to-back calls between two events on the current
+    stream (the stream the library launches on). Returns the host wall time,
+    the region's event time (ms) and, from a separate short pass with events
+    around each call, single-call times. Events around every call would add
+    host time to each step, so the timed region has none."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region = a.elapsed_time(b)
+    n1 = min(steps, single_reps)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n1)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n1)]
+    for i in range(n1):
         starts[i].record()
         fn()
         ends[i].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    region = starts[0].elapsed_time(ends[-1])
+    per = [e0.elapsed_time(e1) for e0, e1 in zip(starts, ends)]
     return wall, region, per
 
 
@@ -335,7 +348,7 @@ def main():
 
         wall, region, per = time_calls(step, args.steps, args.warmup, torch)
         ms_step = region / args.steps
-        per_avg = sum(per) / len(per)
+        per_avg = ms_step
         nbytes = prefill_bytes(B, T, H, Dk, Dv)
         flops = prefill_flops(B, T, H, Dk, Dv)
         achieved = nbytes / (per_avg * 1e-3) / 1e9
@@ -356,7 +369,7 @@ def main():
                      BF16_DENSE_PEAK_TFLOPS,
                      "dense_tile_flops_per_launch": flops},
             "wall_s_timed": wall,
-            "per_call_ms": {"mean": per_avg, "median": median(per), "min": min(per)},
+            "per_call_ms": {"mean": per_avg, "median_single": median(per), "min_single": min(per)},
         })
         if args.flushed_reps > 0:
             fl = time_flushed(step, args.flushed_reps, torch, dev)
@@ -387,7 +400,7 @@ def main():
 
         n_timed = steps * args.decode_passes
         wall, region, per = time_calls(dstep, n_timed, steps, torch)
-        per_avg = sum(per) / len(per)
+        per_avg = region / n_timed
         nb = decode_bytes(N, H, Dk, Dv)
         gbs = nb / (per_avg * 1e-3) / 1e9
         dec = {"workload": DECODE, "steps_timed": n_timed, "ms_per_step": region / n_timed,
@@ -451,12 +464,12 @@ def bench_gdn(args, torch, sgla, W, dev):
                            scale=inp["scale"], out=o, final_state=fs)
 
     _, region, per = time_calls(step, args.steps, args.warmup, torch)
-    per_avg = sum(per) / len(per)
+    per_avg = region / args.steps
     nbytes = prefill_bytes(1, 8192, 32, 128, 128) + 8192 * 32 * 4
     gbs = nbytes / (per_avg * 1e-3) / 1e9
     out["prefill"] = {"workload": GDN_PREFILL, "ms_per_call": region / args.steps,
                       "tokens_per_s": 8192 / (region / args.steps * 1e-3),
-                      "per_call_ms": {"mean": per_avg, "median": median(per), "min": min(per)},
+                      "per_call_ms": {"mean": per_avg, "median_single": median(per), "min_single": min(per)},
                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                                    "traffic": recorded_traffic(GDN_PREFILL),
@@ -478,7 +491,7 @@ def bench_gdn(args, torch, sgla, W, dev):
 
     n_timed = 64 * args.decode_passes
     _, region, per = time_calls(dstep, n_timed, 64, torch)
-    per_avg = sum(per) / len(per)
+    per_avg = region / n_timed
     nb = decode_bytes(256, 32, 128, 128) + 256 * 32 * 4
     gbs = nb / (per_avg * 1e-3) / 1e9
     out["decode"] = {"workload": GDN_DECODE, "ms_per_step": region / n_timed,
@@ -512,7 +525,7 @@ def bench_bf16_state(args, torch, sgla, W, dev):
 
     n_timed = steps * args.decode_passes
     _, region, per = time_calls(dstep, n_timed, steps, torch)
-    per_avg = sum(per) / len(per)
+    per_avg = region / n_timed
     nb = decode_bytes(N, H, Dk, Dv, state_elem=2)
     gbs = nb / (per_avg * 1e-3) / 1e9
     del d, state, out
@@ -536,13 +549,13 @@ def bench_epilogue(args, torch, sgla, W, dev):
         sgla.out_norm_gate(inp["o"], inp["z"], inp["weight"], out=out)
 
     _, region, per = time_calls(step, args.steps, args.warmup, torch)
-    per_avg = sum(per) / len(per)
+    per_avg = region / args.steps
     nbytes = 3 * rows * width * 2 + width * 4
     gbs = nbytes / (per_avg * 1e-3) / 1e9
     del inp, out
     return {"workload": "out_norm_gate bf16 %d tokens x %d (32 heads x 128)" % (rows, width),
             "ms_per_call": region / args.steps, "tokens_per_s": rows / (region / args.steps * 1e-3),
-            "per_call_ms": {"mean": per_avg, "median": median(per), "min": min(per)},
+            "per_call_ms": {"mean": per_avg, "median_single": median(per), "min_single": min(per)},
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(EPILOGUE),
                          "kernel": "sgla_out_norm_gate",
@@ -564,12 +577,12 @@ def bench_prologue(args, torch, sgla, W, dev):
                                     scale=inp["scale"], out=o, final_state=fs)
 
     _, region, per = time_calls(step, args.steps, args.warmup, torch)
-    per_avg = sum(per) / len(per)
+    per_avg = region / args.steps
     nbytes = prefill_bytes(1, 8192, 32, 128, 128) + 2 * 128 * 4
     gbs = nbytes / (per_avg * 1e-3) / 1e9
     out["prefill"] = {"workload": PREFILL + " with raw q/k", "ms_per_call": region / args.steps,
                       "tokens_per_s": 8192 / (region / args.steps * 1e-3),
-                      "per_call_ms": {"mean": per_avg, "median": median(per), "min": min(per)},
+                      "per_call_ms": {"mean": per_avg, "median_single": median(per), "min_single": min(per)},
                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                                    "traffic": recorded_traffic(PREFILL_PRO),
@@ -590,7 +603,7 @@ def bench_prologue(args, torch, sgla, W, dev):
 
     n_timed = 64 * args.decode_passes
     _, region, per = time_calls(dstep, n_timed, 64, torch)
-    per_avg = sum(per) / len(per)
+    per_avg = region / n_timed
     nb = decode_bytes(256, 32, 128, 128) + 256 * 4 + 2 * 128 * 4
     gbs = nb / (per_avg * 1e-3) / 1e9
     out["decode"] = {"workload": DECODE + " with raw q/k", "ms_per_step": region / n_timed,
