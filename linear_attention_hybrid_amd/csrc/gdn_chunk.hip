@@ -138,7 +138,7 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
                 const uint32_t off = (uint32_t)((2 * (prb + 16 * it) + rr) * H) * (uint32_t)(D * 2) +
                                      16u * (uint32_t)cidx;
                 kr[it][rr] = buf_ld16(rk, off);
-                vr[it][rr] = buf_ld16(rv, off);
+                vr[it][rr] = buf_ld16_nt(rv, off);  // v: read only here
             }
         const int gb = n > 0 ? (n - 1) * H * 4 + 4 : 0;
         gv = buf_ld_f32(buf_rsrc(p.c.g + tok0 * H + hh, gb), (uint32_t)(l * H * 4));
@@ -482,8 +482,9 @@ __device__ __forceinline__ void chain_mover(const GdnParams &p, int seq, int h, 
         if (mv >= 4) return;
         const char *buf = lds + (j % H_RING) * H_BUF;
         const int rho = 4 * mv + (l >> 4);
-        gll16(tile_at(p, c.first + j, h) + slice + image_off(cb, rho >> 1, rho & 1, m16),
-              buf + HB_U + 1024 * mv);
+        // Non-temporal: each U piece is read once, by this workgroup.
+        gll16_nt(tile_at(p, c.first + j, h) + slice + image_off(cb, rho >> 1, rho & 1, m16),
+                 buf + HB_U + 1024 * mv);
         ++issued;
     };
 
@@ -745,13 +746,14 @@ __global__ __launch_bounds__(NT) void gdn_output_kernel(GdnParams p) {
     const float gv = l < n ? p.c.g[(se.tok0 + l) * H + h] : 0.f;
     const char *img = tile_at(p, s, h) + IMG_S;
     const char *nimg = p.nvimg + ((int64_t)s * H + h) * NV_BYTES;
+    // Non-temporal: each image is read once, here.
     bf16x8 sb[8], nvop[4];
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-        sb[k] = *reinterpret_cast<const bf16x8 *>(img + ((w * 8 + k) * 64 + l) * 16);
+        sb[k] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(img + ((w * 8 + k) * 64 + l) * 16));
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        nvop[k] = *reinterpret_cast<const bf16x8 *>(nimg + ((w * 4 + k) * 64 + l) * 16);
+        nvop[k] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(nimg + ((w * 4 + k) * 64 + l) * 16));
 
     const float G = wave_prefix_sum(gv);
 #pragma unroll

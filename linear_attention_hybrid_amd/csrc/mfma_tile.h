@@ -97,6 +97,12 @@ __device__ __forceinline__ void gll16(const void *src, const char *lds_dst) {
                  :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_dst))), "v"(src)
                  : "memory", "m0");
 }
+// The same with the non-temporal hint, for data read once.
+__device__ __forceinline__ void gll16_nt(const void *src, const char *lds_dst) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_dst))), "v"(src)
+                 : "memory", "m0");
+}
 __device__ __forceinline__ void gll4(const void *src, const char *lds_dst) {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                  :: "s"(__builtin_amdgcn_readfirstlane(lds_addr(lds_dst))), "v"(src)
@@ -132,6 +138,10 @@ __device__ __forceinline__ buf_t buf_rsrc(const void *base, int bytes) {
 }
 __device__ __forceinline__ u32x4 buf_ld16(buf_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+// Non-temporal load (the nt bit), for data that nothing reads again.
+__device__ __forceinline__ u32x4 buf_ld16_nt(buf_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
 }
 __device__ __forceinline__ float buf_ld_f32(buf_t r, uint32_t off) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
