@@ -224,6 +224,23 @@ def test_workload_varlen_512k():
             starts=[int(c) for c in cu[:-1]])
 
 
+@pytest.mark.parametrize("seg_len", [None, 64])
+def test_most_heads_ragged_chunk(seg_len):
+    """H = 65536, the most heads a call takes, and T = 70 (a full chunk and a
+    ragged one of 6 tokens). The row stride is H * 256 bytes, so the chunk
+    kernels' per-chunk byte ranges and row offsets are at their largest (about
+    2^30). With 64-token segments the segment-state and scan kernels run too."""
+    if seg_len:
+        os.environ["SGLA_SEG_LEN"] = str(seg_len)
+    say("chunk_fwd bf16 B=1 T=70 H=65536 D=128 seed=77 seg_len", seg_len, "(4 sampled heads)")
+    inp = W.make_prefill(1, 70, 65536, 128, 128, "bf16", "lightning", seed=77, device="cuda",
+                         init="normal")
+    o, S = run_gpu(inp)
+    compare(inp, o, S, "bf16", "H=65536 T=70", heads=[0, 1, 40961, 65535])
+    del inp, o, S
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("T", [65, 700])
 def test_vector_alu_path_for_bf16_128(T):
     """bf16 with 128-wide heads normally runs on the matrix cores; the vector

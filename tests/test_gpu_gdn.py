@@ -215,6 +215,25 @@ def test_gdn_chunk_prefill_workload_sampled():
     check(host(S[:, heads]), rS, "bf16", "gdn prefill state", bf16_out=False)
 
 
+def test_gdn_chunk_most_heads():
+    """H = 65536, the most heads a call takes, and T = 70 (a full chunk and a
+    ragged one): the prep kernel's per-item byte ranges and row offsets are at
+    their largest (about 2^30), and the chain runs 2^19 workgroups."""
+    say("gdn_chunk_fwd bf16 B=1 T=70 H=65536 D=128 seed=78 (4 sampled heads)")
+    inp = W.make_prefill(1, 70, 65536, 128, 128, "bf16", "gdn", seed=78, device="cuda",
+                         init="normal", with_beta=True)
+    o, S = sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                              initial_state=inp["initial_state"],
+                              out=nan_like((1, 70, 65536, 128), torch.bfloat16))
+    torch.cuda.synchronize()
+    heads = [0, 1, 40961, 65535]
+    ro, rS = oracle_gdn(inp, heads=heads)
+    check(host(o[:, :, heads]), ro, "bf16", "gdn H=65536 o")
+    check(host(S[:, heads]), rS, "bf16", "gdn H=65536 final state", bf16_out=False)
+    del inp, o, S
+    torch.cuda.empty_cache()
+
+
 def _sample_heads(H, n, seed):
     return np.sort(np.random.default_rng(seed).choice(H, size=n, replace=False))
 
