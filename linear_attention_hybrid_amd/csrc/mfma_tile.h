@@ -1,6 +1,8 @@
 // Matrix-core tile helpers shared by the chunked kernels: bf16 32x32x16 MFMA
-// with fp32 accumulation, swizzled LDS tile layouts, bf16 packing and the
-// wave prefix sum of the gate. Internal; not part of the ABI.
+// with fp32 accumulation, swizzled LDS tile layouts, bf16 packing, the wave
+// prefix sum of the gate, direct global-to-LDS loads with their waits,
+// range-checked buffer loads and stores, and the transposing LDS read.
+// Internal; not part of the ABI.
 //
 // MFMA 32x32x16 register layout (v_mfma_f32_32x32x16_bf16): for D = A B + C,
 // lane l supplies A[l % 32][8 (l / 32) .. + 7] and B[8 (l / 32) .. + 7][l % 32]
