@@ -226,7 +226,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
         for (int v = 0; v < 16; ++v) settle(S[b][v]);
     float gam_acc = 0.f;
 
+    // Two output workgroups share each CU, one from each half of the grid when
+    // the grid fills the chip once, and when both have a wave ready the SIMD
+    // picks the older one: left alone, the first-dispatched workgroup ends its
+    // loop about 6 us before the other. Alternating a raised wave priority
+    // between the two halves chunk by chunk lets each lead in turn.
+    const int half = blockIdx.x >= gridDim.x / 2 ? 1 : 0;
     for (int c0 = 0; c0 < len; c0 += 64) {
+        if (!STATE_ONLY) {
+            if (((c0 >> 6) + half) & 1) __builtin_amdgcn_s_setprio(1);
+            else __builtin_amdgcn_s_setprio(0);
+        }
         const int n = min(64, len - c0);
         const int64_t t0 = se.tok0 + c0;
         // The swizzled LDS addresses depend on the lane; rebuilding them from
