@@ -1,0 +1,395 @@
+// Chunked Simple GLA output pass over value-column halves: bf16 operands,
+// fp32 accumulation, Dk = Dv = 128, chunks of 64 tokens.
+//
+// Per chunk with inclusive cumulative gate sums G (page "Formulas and code for
+// adapting inference to GDN/KDA linear modules", section 1.2, reduced to Simple
+// GLA: no delta-rule terms, new_v = v; the diagonal is included because the
+// query reads the state after the token's own update, blueprint page, section
+// "B2 lightning-attn (Simple GLA)"):
+//
+//   A   = scale * (Q K^T) * exp(G_i - G_j) for j <= i, else 0
+//   O   = scale * diag(exp(G)) Q S + A V
+//   S   = exp(G_last) * S + K^T (diag(exp(G_last - G)) V)
+//
+// One workgroup owns one output segment of one head and one half of the value
+// columns (64 of 128), so a head's segment is split over two workgroups that
+// share the q and k rows through their XCD's L2. It is four waves, and two
+// workgroups share a compute unit, so that one's memory and LDS latency hides
+// behind the other's work. Each thread loads its share of the next chunk's q
+// and k rows, the half's v rows and g into registers with range-checked buffer
+// loads while the current chunk is computed, and writes them into the LDS
+// tiles at the top of the next iteration; rows past a ragged end read as
+// zeros. Wave (cc, t) owns value columns 32cc .. 32cc+31 of the half; for the
+// output it takes token half t (tokens 32t .. 32t+31), and of the fp32 state
+// it holds key rows 64t .. 64t+63 in MFMA accumulators. The two waves of one
+// column block exchange their halves of the state as bf16 operands through
+// LDS once per chunk, so each can form Q S over all 128 key rows.
+//
+// The products are 32x32x16 bf16 MFMAs, each written so that its result is
+// already in the register layout the next consumes (see mfma_tile.h): the
+// state accumulators convert to the A operand of S^T Q^T; A^T = K Q^T leaves
+// each lane one query column, stored as A[i][j] rows for the B operand of
+// V^T A^T. K^T and V^T operands come from the row-major tiles through the
+// transposing LDS read, and the decay exp(G_last - G) scales the V operand of
+// the update (one bf16 rounding, as scaling K would be). Output rows go
+// through an LDS staging tile, so each row's 128 bytes are stored as one line.
+//
+// The start state of a segment is the initial state, or, when the sequence
+// spans several output segments, the state the scan kernel left in the
+// segment-state buffer.
+#include "mfma_tile.h"
+
+namespace sgla {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int NTH = 256;              // four waves
+// LDS map (bytes); two workgroups share a compute unit.
+constexpr int L_Q = 0;                // Q rows [64][256 B], swizzled as qk_off
+constexpr int L_K = 16384;            // K rows, same layout
+constexpr int L_V = 32768;            // the half's V rows [64][128 B], swizzled as v_off
+constexpr int L_G = 40960;            // g [64] fp32
+constexpr int L_A = 41216;            // scores A[64 i][128 B] bf16, swizzled as tr_off
+constexpr int L_SX = L_A + 8192;      // bf16 state operands [block cc 2][dk tile 4][step 2][lane 64] x 16 B
+constexpr int L_O = L_SX + 16384;     // output staging [64 rows][128 B], swizzled as o_off
+constexpr int L_F = L_O + 8192;       // per wave: G[64] and exp(G_last - G)[64], fp32
+constexpr int L_BYTES = L_F + 4 * 512;
+static_assert(2 * L_BYTES <= 160 * 1024, "two workgroups must fit one compute unit's LDS");
+
+// Q and K tiles (64 rows of 256 bytes): 16-byte chunk c of row r sits at
+// chunk c ^ qk_sw(r), and the two 8-byte halves of every chunk of a row with
+// bit 4 set trade places. Sixteen consecutive rows then put one chunk in 16
+// different bank groups (the scores' row reads), rows r and r + 16 put one
+// 8-byte half in different banks (the 8-byte reads of Q S), and the four rows
+// of a transposing read put an aligned group of four chunks in 16 different
+// bank groups (the K^T reads of the update). Every read names 8-byte halves
+// at their place, so each operand keeps the logical order of its k values.
+__device__ __forceinline__ int qk_sw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int qk_off(int r, int c) { return r * 256 + ((c ^ qk_sw(r)) << 4); }
+__device__ __forceinline__ int qk_half(int r, int hf) { return 8 * (hf ^ ((r >> 4) & 1)); }
+// Transposing-read address (rows r0 .. r0+3, columns c0 .. c0+15; r0 a
+// multiple of 4, c0 a multiple of 16) for lane m of a 16-lane group.
+__device__ __forceinline__ int qk_tr_src(int r0, int c0, int m) {
+    const int r = r0 + (m >> 2);
+    return qk_off(r, (c0 >> 3) + ((m & 3) >> 1)) + qk_half(r, m & 1);
+}
+__device__ __forceinline__ u32x4 swap_halves(u32x4 x) { return u32x4{x[2], x[3], x[0], x[1]}; }
+
+// V half tile: 16-byte piece p of row r. Rows r and r + 2 differ in bit 2 of
+// the swizzle, so the four rows of one transposing read fill 16 different
+// bank groups.
+__device__ __forceinline__ int v_off(int r, int p) { return r * 128 + ((p ^ (((r >> 1) & 1) << 2)) << 4); }
+// Byte offset of the 8 bytes lane m of a 16-lane group names for the
+// transposing read of rows r0 .. r0+3, columns c0 .. c0+15 of the V tile
+// (r0 a multiple of 4, c0 a multiple of 16).
+__device__ __forceinline__ int vtr_src(int r0, int c0, int m) {
+    return v_off(r0 + (m >> 2), (c0 >> 3) + ((m & 3) >> 1)) + 8 * (m & 1);
+}
+// Output staging tile (64 rows of 128 bytes): piece p of row r at piece
+// p ^ ((r >> 1) & 7), halves traded in rows with bit 4 set, so that the
+// 8-byte writes of 32 consecutive rows fill all banks once.
+__device__ __forceinline__ int o_off(int r, int p) { return r * 128 + ((p ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ int sx_off(int cc, int b, int s2, int l) {
+    return L_SX + (((cc * 4 + b) * 2 + s2) * 64 + l) * 16;
+}
+
+// Output segment s of the call (arithmetic without a table, as seg_at).
+__device__ __forceinline__ SegEntry oseg_at(const HalvesParams &hp, int s) {
+    if (hp.osegs) return hp.osegs[s];
+    SegEntry e;
+    const int n = s / hp.onps;
+    const int j = s - n * hp.onps;
+    e.seq = n;
+    e.p = j;
+    e.nseg = hp.onps;
+    e.tok0 = (int64_t)n * hp.c.T + (int64_t)j * hp.oseg_len;
+    const int rem = hp.c.T - j * hp.oseg_len;
+    e.len = rem < hp.oseg_len ? rem : hp.oseg_len;
+    e.pad0 = 0;
+    e.pad1 = 0;
+    return e;
+}
+
+template <int TH>
+__device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, int half, char *lds) {
+    const ChunkParams &p = hp.c;
+    const int H = p.H;
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int l = tid & 63;
+    const int cc = w >> 1;   // 32-column block of the half
+    constexpr int t = TH;    // token half of the output, key-row half of the state
+    const int lh = l >> 5;
+    const int ln = l & 31;
+    const int m16 = l & 15;
+    const int gi = l >> 4;
+    const int col = half * 64 + 32 * cc + ln;  // this lane's value column
+    const int len = se.len;
+    const int nch = (len + 63) >> 6;
+    const bool last = se.p == se.nseg - 1;
+    const int64_t sl = (int64_t)D * D;
+    const uint16_t *__restrict__ qg = static_cast<const uint16_t *>(p.q);
+    const uint16_t *__restrict__ kg = static_cast<const uint16_t *>(p.k);
+    const uint16_t *__restrict__ vg = static_cast<const uint16_t *>(p.v);
+    char *og = static_cast<char *>(p.out);
+
+    // This thread's share of a chunk: q and k pieces (tid & 15) of rows
+    // (tid >> 4) + 16 i, v piece (tid & 7) of rows (tid >> 3) + 32 i, and for
+    // the first wave g of token l; a per-chunk buffer resource whose range
+    // ends at the chunk's last row, so rows past a ragged end read as zeros.
+    u32x4 qr[4], kr[4], vr[2];
+    float gr = 0.f;
+    // Bytes from a chunk's first row to the end of its row n - 1 (< 2^31
+    // for H <= 65536).
+    auto rows_bytes = [&](int n) -> int { return (n - 1) * H * (D * 2) + D * 2; };
+    auto issue = [&](int c) {
+        int tv = tid;
+        asm volatile("" : "+v"(tv));
+        const int n = min(64, len - 64 * c);
+        const int64_t t0 = se.tok0 + 64 * (int64_t)c;
+        const int64_t base = (t0 * H + h) * D;
+        const int nb = rows_bytes(n);
+        const buf_t rq = buf_rsrc(qg + base, nb);
+        const buf_t rk = buf_rsrc(kg + base, nb);
+        const buf_t rv = buf_rsrc(vg + base + half * 64, nb - 128);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t off = (uint32_t)((tv >> 4) + 16 * i) * (uint32_t)(H * D * 2) + (tv & 15) * 16u;
+            qr[i] = buf_ld16(rq, off);
+            kr[i] = buf_ld16(rk, off);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t off = (uint32_t)((tv >> 3) + 32 * i) * (uint32_t)(H * D * 2) + (tv & 7) * 16u;
+            vr[i] = buf_ld16(rv, off);
+        }
+        if (w == 0) gr = buf_ld_f32(buf_rsrc(p.g + t0 * H + h, (n - 1) * H * 4 + 4), (uint32_t)(tv & 63) * H * 4);
+    };
+    auto store_o = [&](int c) {
+        int tv = tid;
+        asm volatile("" : "+v"(tv));
+        const int n = min(64, len - 64 * c);
+        const int64_t t0 = se.tok0 + 64 * (int64_t)c;
+        const buf_t ro = buf_rsrc(og + (t0 * H + h) * (D * 2) + half * 128, (n - 1) * H * (D * 2) + 128);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = (tv >> 3) + 32 * i;
+            const int pc = tv & 7;
+            const u32x4 x = lds_ld<u32x4>(lds, L_O + o_off(r, pc));
+            buf_st16_nt(ro, (uint32_t)r * (uint32_t)(H * D * 2) + pc * 16u, ((r >> 4) & 1) ? swap_halves(x) : x);
+        }
+    };
+
+    // The start state, key tiles 2t and 2t + 1 of this column block.
+    f32x16 S[2];
+    {
+        const float *src;
+        if (se.nseg == 1) {
+            src = p.s0 ? p.s0 + ((int64_t)se.seq * H + h) * sl : nullptr;
+        } else {
+            // Clamped into the buffer, so that offsets that break the
+            // documented rule cannot send the read past it.
+            const int slot = min(seq_at(p, se.seq).first + p.rsub * se.p, p.nseg_max - 1);
+            src = p.buf + ((int64_t)slot * H + h) * sl;
+        }
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int dk = 32 * (2 * t + bi) + 8 * (v >> 2) + 4 * lh + (v & 3);
+                S[bi][v] = src ? src[dk * D + col] : 0.f;
+            }
+    }
+    if (nch > 0) issue(0);
+    // This wave's state tiles as bf16 A operands of S^T Q^T, kept in
+    // registers and staged for the other wave of the column block.
+    bf16x8 sown[2][2];
+    auto stage_state = [&]() {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                bf16x8 x;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = (__bf16)S[bi][8 * s2 + e];
+                sown[bi][s2] = x;
+                lds_st(lds, sx_off(cc, 2 * t + bi, s2, l), x);
+            }
+    };
+    stage_state();
+
+    char *ft = lds + L_F + 512 * w;  // this wave's G[64], then exp(G_last - G)[64]
+    const int i = 32 * t + ln;        // this lane's query row of the output
+    for (int c = 0; c < nch; ++c) {
+        const int n = min(64, len - 64 * c);
+        __syncthreads();  // the previous chunk's tiles and staging are read
+        if (c > 0) store_o(c - 1);
+        {
+            int tv = tid;
+            asm volatile("" : "+v"(tv));
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int r = (tv >> 4) + 16 * i4;
+                const bool sw = (r >> 4) & 1;
+                lds_st(lds, L_Q + qk_off(r, tv & 15), sw ? swap_halves(qr[i4]) : qr[i4]);
+                lds_st(lds, L_K + qk_off(r, tv & 15), sw ? swap_halves(kr[i4]) : kr[i4]);
+            }
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) lds_st(lds, L_V + v_off((tv >> 3) + 32 * i2, tv & 7), vr[i2]);
+            if (w == 0) lds_st(lds, L_G + 4 * l, gr);
+        }
+        __syncthreads();  // chunk c's tiles are in LDS
+        if (c + 1 < nch) issue(c + 1);
+
+        // Gate prefix sum, one lane per token (rows past the end read as 0).
+        const float G = wave_prefix_sum(lds_ld<float>(lds, L_G + 4 * l));
+        const float Gl = lane_value(G, 63);
+        lds_st(ft, 4 * l, G);
+        lds_st(ft, 256 + 4 * l, l < n ? __expf(Gl - G) : 0.f);
+
+        // O^T = S^T Q^T over all key rows, then the rows scaled by
+        // scale * exp(G_i).
+        f32x16 acc = {};
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const bf16x8 sa = (b >> 1) == t ? sown[b & 1][s2] : lds_ld<bf16x8>(lds, sx_off(cc, b, s2, l));
+                const int cq = 4 * b + 2 * s2;
+                const bf16x4 x0 = lds_ld<bf16x4>(lds, L_Q + qk_off(i, cq) + qk_half(i, lh));
+                const bf16x4 x1 = lds_ld<bf16x4>(lds, L_Q + qk_off(i, cq + 1) + qk_half(i, lh));
+                acc = mfma(sa, cat4(x0, x1), acc);
+            }
+        {
+            const float f = p.scale * __expf(lds_ld<float>(ft, 4 * i));
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] *= f;
+        }
+
+        // Scores: wave 0 -> (keys 0-31, queries 0-31), 1 -> (0-31, 32-63),
+        // 3 -> (32-63, 32-63); the fourth quadrant is masked out.
+        if (w != 2) {
+            const int jb = w == 3 ? 1 : 0;
+            const int ib = w == 0 ? 0 : 1;
+            const int j = 32 * jb + ln;
+            const int iq = 32 * ib + ln;
+            f32x16 sc = {};
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) {
+                // Both halves of the chunk in their logical order: one MFMA
+                // pairs rows and columns that differ in bit 4.
+                const int cj = L_K + qk_off(j, 2 * s8 + lh), ci = L_Q + qk_off(iq, 2 * s8 + lh);
+                const bf16x8 a = cat4(lds_ld<bf16x4>(lds, cj + qk_half(j, 0)), lds_ld<bf16x4>(lds, cj + qk_half(j, 1)));
+                const bf16x8 bq = cat4(lds_ld<bf16x4>(lds, ci + qk_half(iq, 0)), lds_ld<bf16x4>(lds, ci + qk_half(iq, 1)));
+                sc = mfma(a, bq, sc);
+            }
+            const float Gi = lds_ld<float>(ft, 4 * iq);
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const int jr = 32 * jb + 8 * g4 + 4 * lh;
+                const float4 Gj = lds_ld<float4>(ft, 4 * jr);
+                const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
+                float val[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    val[r] = (jr + r <= iq) ? p.scale * __expf(Gi - gj[r]) * sc[4 * g4 + r] : 0.f;
+                const u32x2 pk = {pack_f32(val[0], val[1]), pack_f32(val[2], val[3])};
+                lds_st(lds, L_A + tr_off(iq, 4 * jb + g4) + 8 * lh, pk);
+            }
+        }
+
+        // V^T operands (lane: value column 32cc + ln, tokens 16s + 8lh .. + 7),
+        // shared by V^T A^T and the update.
+        bf16x8 vop[4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const int c0 = 32 * cc + 16 * (gi & 1);
+            vop[s4] = cat4(lds_tr(lds, L_V + vtr_src(16 * s4 + 8 * lh, c0, m16)),
+                           lds_tr(lds, L_V + vtr_src(16 * s4 + 8 * lh + 4, c0, m16)));
+        }
+        __syncthreads();  // the scores are staged
+
+        // O^T += V^T A^T over the keys up to this token half.
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            if (s4 < 2 * t + 2) {
+                const bf16x8 ba = lds_ld<bf16x8>(lds, L_A + tr_off(i, 2 * s4 + lh));
+                acc = mfma(vop[s4], ba, acc);
+            }
+        }
+        // Output rows into the staging tile (stored at the next iteration).
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const u32x2 pk = {pack_f32(acc[4 * g4], acc[4 * g4 + 1]), pack_f32(acc[4 * g4 + 2], acc[4 * g4 + 3])};
+            lds_st(lds, L_O + o_off(i, 4 * cc + g4) + qk_half(i, lh), pk);
+        }
+
+        // S = exp(G_last) S + K^T (exp(G_last - G) V) on this wave's key rows.
+        if (c + 1 < nch || (last && p.sfin)) {
+            const float a = __expf(Gl);
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[bi][v] *= a;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const float4 f0 = lds_ld<float4>(ft, 256 + 4 * (16 * s4 + 8 * lh));
+                const float4 f1 = lds_ld<float4>(ft, 256 + 4 * (16 * s4 + 8 * lh) + 16);
+                const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                bf16x8 vs;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) vs[e] = (__bf16)((float)vop[s4][e] * fe[e]);
+#pragma unroll
+                for (int bi = 0; bi < 2; ++bi) {
+                    const int c0 = 32 * (2 * t + bi) + 16 * (gi & 1);
+                    const bf16x8 kt = cat4(lds_tr(lds, L_K + qk_tr_src(16 * s4 + 8 * lh, c0, m16)),
+                                           lds_tr(lds, L_K + qk_tr_src(16 * s4 + 8 * lh + 4, c0, m16)));
+                    S[bi] = mfma(kt, vs, S[bi]);
+                }
+            }
+            stage_state();
+        }
+    }
+    __syncthreads();  // the last chunk's output rows are staged
+    if (nch > 0) store_o(nch - 1);
+
+    if (last && p.sfin) {
+        float *dst = p.sfin + ((int64_t)se.seq * H + h) * sl;
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int dk = 32 * (2 * t + bi) + 8 * (v >> 2) + 4 * lh + (v & 3);
+                dst[dk * D + col] = S[bi][v];
+            }
+    }
+}
+
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(2))) void chunk_halves_kernel(HalvesParams hp) {
+    int unit, half;
+    xcd_unit_map(blockIdx.x, 2, unit, half);
+    const int H = hp.c.H;
+    const int s = unit / H;
+    const int h = unit - s * H;
+    if (s >= hp.onseg_max) return;
+    const SegEntry se = oseg_at(hp, s);
+    if (se.len < 0) return;
+    __shared__ __attribute__((aligned(16))) char lds[L_BYTES];
+    if ((threadIdx.x >> 6) & 1) halves_wave<1>(hp, se, h, half, lds);
+    else halves_wave<0>(hp, se, h, half, lds);
+}
+
+}  // namespace
+
+hipError_t launch_chunk_halves(const HalvesParams &hp, hipStream_t st) {
+    if (hp.onseg_max == 0) return hipSuccess;
+    // Two workgroups per (segment, head), laid out by xcd_unit_map: the grid
+    // covers every unit when it is a multiple of 16.
+    const int64_t units = (int64_t)hp.onseg_max * hp.c.H;
+    const int64_t grid = (2 * units + 15) / 16 * 16;
+    hipLaunchKernelGGL(chunk_halves_kernel, dim3((unsigned)grid), dim3(NTH), 0, st, hp);
+    return hipGetLastError();
+}
+
+}  // namespace sgla

@@ -111,7 +111,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
     const SegEntry se = seg_at(p, s);
     if (se.len < 0) return;
     const bool last = se.p == se.nseg - 1;
-    if (STATE_ONLY && last) return;
+    // The state pass skips the segments of each sequence's last output
+    // segment (rsub of them): nothing after them needs their states.
+    if (STATE_ONLY && se.p >= p.rsub * ((se.nseg + p.rsub - 1) / p.rsub - 1)) return;
 
     constexpr int kBase = STATE_ONLY ? LDS_STATE : LDS_OUT;
     __shared__ __attribute__((aligned(16))) char lds[kBase + (PRO ? PRO_BYTES : 0)];

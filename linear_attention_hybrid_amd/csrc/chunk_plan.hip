@@ -101,12 +101,13 @@ __global__ __launch_bounds__(256) void plan_kernel(const int64_t *__restrict__ c
 
 // One thread owns four consecutive state elements of one (sequence, head) and
 // walks the sequence's segments in order. In place: the slot of segment j
-// holds dS_j on entry and S_in(j) on exit. Segments go in batches with three
-// separate phases: all loads, then the combines in registers, then the
-// stores. Keeping branches out of the first two phases lets a batch cost one
-// memory latency; a store between two loads would make every later wait
-// count it, and a branch between them makes the compiler wait for all of
-// them.
+// holds dS_j on entry, and on exit S_in(j) for every j that starts an output
+// segment (j a multiple of rsub); the other slots are left as they are.
+// Segments go in batches with three separate phases: all loads, then the
+// combines in registers, then the stores. Keeping branches out of the first
+// two phases lets a batch cost one memory latency; a store between two loads
+// would make every later wait count it, and a branch between them makes the
+// compiler wait for all of them.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void scan_kernel(ChunkParams p) {
     constexpr int kBatch = 16;
@@ -114,21 +115,24 @@ __global__ __launch_bounds__(256) void scan_kernel(ChunkParams p) {
     const int n = nh / p.H;
     const int h = nh - n * p.H;
     const SeqEntry se = seq_at(p, n);
-    if (se.nseg <= 1) return;
+    const int R = p.rsub;
+    const int nout = (se.nseg + R - 1) / R;  // output segments of the sequence
+    if (nout <= 1) return;
+    const int nj = R * (nout - 1);  // segment states combined; S_in(nj) is the last one stored
     const int64_t e = ((int64_t)blockIdx.y * 256 + threadIdx.x) * 4;
     const int64_t stride = (int64_t)p.H * DK * DV;  // floats between segment slots
     float *slot0 = p.buf + ((int64_t)se.first * p.H + h) * DK * DV + e;
     const float *gam0 = p.gam + (int64_t)se.first * p.H + h;
     float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p.s0) S = *reinterpret_cast<const float4 *>(p.s0 + ((int64_t)n * p.H + h) * DK * DV + e);
-    for (int j0 = 0; j0 < se.nseg; j0 += kBatch) {
+    for (int j0 = 0; j0 <= nj; j0 += kBatch) {
         // Slots past the last segment state are clamped to a valid one; the
         // states they produce are never stored.
         float4 d[kBatch];
         float lg[kBatch];
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
-            const int j = min(j0 + b, se.nseg - 2);
+            const int j = min(j0 + b, nj - 1);
             d[b] = *reinterpret_cast<const float4 *>(slot0 + j * stride);
             lg[b] = gam0[(int64_t)j * p.H];
         }
@@ -142,10 +146,11 @@ __global__ __launch_bounds__(256) void scan_kernel(ChunkParams p) {
             S.z = fmaf(a, S.z, d[b].z);
             S.w = fmaf(a, S.w, d[b].w);
         }
-        const int nb = min(kBatch, se.nseg - j0);
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b)
-            if (b < nb) *reinterpret_cast<float4 *>(slot0 + (j0 + b) * stride) = o[b];
+        for (int b = 0; b < kBatch; ++b) {
+            const int j = j0 + b;
+            if (j <= nj && j % R == 0) *reinterpret_cast<float4 *>(slot0 + j * stride) = o[b];
+        }
     }
 }
 

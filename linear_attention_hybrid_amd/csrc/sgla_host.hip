@@ -41,6 +41,37 @@ int choose_seg_len(int64_t ttot, int B, int H) {
     return (int)len;
 }
 
+// Output segments of the value-half kernel (bf16, 128-wide heads): long
+// enough that two workgroups per compute unit cover the call, two per
+// (segment, head), and at least 512 tokens.
+int choose_out_len(int64_t ttot, int H) {
+    const char *env = getenv("SGLA_OUT_SEG_LEN");
+    if (env) {
+        long v = strtol(env, nullptr, 10);
+        if (v >= kChunk && v % kChunk == 0 && v <= (1 << 24)) return (int)v;
+    }
+    const int64_t target_wgs = 512;
+    int64_t len = (ttot * H * 2 + target_wgs - 1) / target_wgs;
+    if (len < 512) len = 512;
+    if (len > (1 << 24)) len = 1 << 24;
+    return (int)((len + kChunk - 1) / kChunk * kChunk);
+}
+
+// Sub-segments per output segment for the state pass: split until the pass
+// has about 384 (segment, head) workgroups, keeping sub-segments of at least
+// 512 tokens and whole chunks. pre_units = (segment, head) pairs whose state
+// is needed when each output segment is one sub-segment.
+int choose_rsub(int out_len, int64_t pre_units) {
+    const char *env = getenv("SGLA_RSUB");
+    if (env) {
+        long v = strtol(env, nullptr, 10);
+        if (v >= 1 && v <= out_len / kChunk && (out_len / kChunk) % v == 0) return (int)v;
+    }
+    int r = 1;
+    while (out_len / (2 * r) >= 512 && (out_len / kChunk) % (2 * r) == 0 && pre_units * r < 384) r *= 2;
+    return r;
+}
+
 sgla_status hip_status(hipError_t e) { return e == hipSuccess ? SGLA_OK : SGLA_ERR_HIP; }
 
 // Arguments of the q/k prologue (RMSNorm, RoPE) as the entry points get them.
@@ -66,6 +97,10 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
                       const float *initial_state, void *out, float *final_state,
                       const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv, float scale,
                       sgla_dtype dtype, void *stream, const ProArgs *pro);
+sgla_status chunk_fwd_halves(const void *q, const void *k, const void *v, const float *g,
+                             const float *initial_state, void *out, float *final_state,
+                             const int64_t *cu_seqlens, int B, int T, int H, float scale,
+                             void *stream);
 
 }  // namespace
 
@@ -132,6 +167,19 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
     if (ttot == 0 && !final_state) return SGLA_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
+    // bf16 with 128-wide heads and no prologue: equal-length batches run on
+    // the value-half kernels (less state traffic; as fast on 8K-token
+    // sequences and faster on long ones). Packed sequences of mixed lengths
+    // stay on the one-level kernels, whose shorter segments balance better:
+    // there the per-chunk work bounds the call, and the value halves repeat
+    // the scores. SGLA_VALUE_HALVES / SGLA_ONE_LEVEL force either path.
+    const bool bf16 = dtype == SGLA_BF16;
+    const bool halves = cu_seqlens ? getenv("SGLA_VALUE_HALVES") != nullptr
+                                   : getenv("SGLA_ONE_LEVEL") == nullptr;
+    if (bf16 && Dk == 128 && Dv == 128 && !pro && !getenv("SGLA_FORCE_VALU") && halves)
+        return chunk_fwd_halves(q, k, v, g, initial_state, out, final_state, cu_seqlens, B, T, H,
+                                scale, stream);
+
     const int seg_len = choose_seg_len(ttot, B, H);
     // Without cu_seqlens every sequence has T tokens and the same number of
     // segments, so no table is built; with it, a device-side plan kernel lays
@@ -183,7 +231,7 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
     p.pos_off = pro ? pro->pos : nullptr;
     p.theta = pro ? pro->theta : 0.f;
     p.eps = pro ? pro->eps : 0.f;
-    const bool bf16 = dtype == SGLA_BF16;
+    p.rsub = 1;
 
     // bf16 with 128-wide heads runs on the matrix cores; every other
     // combination on the vector ALUs.
@@ -198,6 +246,96 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
     if (e == hipSuccess && split) e = phase(/*state_phase=*/true);
     if (e == hipSuccess && split) e = launch_scan(p, Dk, Dv, st);
     if (e == hipSuccess) e = phase(/*state_phase=*/false);
+    if (ws) {
+        const hipError_t ef = hipFreeAsync(ws, st);
+        if (e == hipSuccess) e = ef;
+    }
+    return hip_status(e);
+}
+
+// bf16, Dk = Dv = 128, no prologue: output segments of oseg_len tokens over
+// value-column halves (chunk_halves.hip). When a sequence spans several
+// output segments, the state kernel first computes the zero-start state of
+// every sub-segment (oseg_len / rsub tokens) that precedes its last output
+// segment, and the scan turns them into the start state of each output
+// segment. Arguments are checked by chunk_fwd.
+sgla_status chunk_fwd_halves(const void *q, const void *k, const void *v, const float *g,
+                             const float *initial_state, void *out, float *final_state,
+                             const int64_t *cu_seqlens, int B, int T, int H, float scale,
+                             void *stream) {
+    constexpr int D = 128;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool table = cu_seqlens != nullptr;
+    const int64_t ttot = table ? (int64_t)T : (int64_t)B * T;
+    const int oseg_len = choose_out_len(ttot, H);
+    const int64_t onps64 = T == 0 ? 1 : ((int64_t)T + oseg_len - 1) / oseg_len;
+    const int64_t onseg64 = table ? ttot / oseg_len + B + 1 : (int64_t)B * onps64;
+    if (onseg64 * H * 2 > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+    const bool split = table || onps64 > 1;
+    const int64_t pre_units = table ? (ttot / oseg_len) * H : (onps64 - 1) * B * H;
+    const int rsub = split ? choose_rsub(oseg_len, pre_units) : 1;
+    const int sub_len = oseg_len / rsub;
+    const int64_t nps64 = T == 0 ? 1 : ((int64_t)T + sub_len - 1) / sub_len;
+    const int64_t nseg64 = !split ? 0 : table ? ttot / sub_len + B + 1 : (int64_t)B * nps64;
+    if (nseg64 * H > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+
+    // Workspace: output-segment table, sub-segment tables, log-decays, states.
+    auto r256 = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t osegs_b = table ? r256((size_t)onseg64 * sizeof(SegEntry)) : 0;
+    const size_t oseqs_b = table ? r256((size_t)B * sizeof(SeqEntry)) : 0;
+    const size_t segs_b = table ? r256((size_t)nseg64 * sizeof(SegEntry)) : 0;
+    const size_t seqs_b = table ? r256((size_t)B * sizeof(SeqEntry)) : 0;
+    const size_t gam_b = split ? r256((size_t)nseg64 * H * sizeof(float)) : 0;
+    const size_t buf_b = split ? (size_t)nseg64 * H * D * D * sizeof(float) : 0;
+    const size_t ws_b = osegs_b + oseqs_b + segs_b + seqs_b + gam_b + buf_b;
+    char *ws = nullptr;
+    hipError_t e = hipSuccess;
+    if (ws_b) {
+        e = hipMallocAsync(reinterpret_cast<void **>(&ws), ws_b, st);
+        if (e != hipSuccess) return SGLA_ERR_HIP;
+    }
+    char *wp = ws;
+    auto take = [&](size_t b) { char *r = b ? wp : nullptr; wp += b; return r; };
+    SegEntry *osegs = reinterpret_cast<SegEntry *>(take(osegs_b));
+    SeqEntry *oseqs = reinterpret_cast<SeqEntry *>(take(oseqs_b));
+    SegEntry *segs = reinterpret_cast<SegEntry *>(take(segs_b));
+    SeqEntry *seqs = reinterpret_cast<SeqEntry *>(take(seqs_b));
+    float *gam = reinterpret_cast<float *>(take(gam_b));
+    float *buf = reinterpret_cast<float *>(take(buf_b));
+
+    HalvesParams hp{};
+    ChunkParams &p = hp.c;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.s0 = initial_state;
+    p.out = out;
+    p.sfin = final_state;
+    p.buf = buf;
+    p.gam = gam;
+    p.segs = segs;
+    p.seqs = seqs;
+    p.H = H;
+    p.nseg_max = (int)nseg64;
+    p.N = B;
+    p.scale = scale;
+    p.T = T;
+    p.seg_len = sub_len;
+    p.nps = (int)nps64;
+    p.rsub = rsub;
+    hp.osegs = osegs;
+    hp.onseg_max = (int)onseg64;
+    hp.onps = (int)onps64;
+    hp.oseg_len = oseg_len;
+
+    if (table) {
+        e = launch_plan(cu_seqlens, B, T, oseg_len, (int)onseg64, osegs, oseqs, st);
+        if (e == hipSuccess) e = launch_plan(cu_seqlens, B, T, sub_len, (int)nseg64, segs, seqs, st);
+    }
+    if (e == hipSuccess && split) e = launch_chunk_mfma(p, /*phase_state=*/true, st);
+    if (e == hipSuccess && split) e = launch_scan(p, D, D, st);
+    if (e == hipSuccess) e = launch_chunk_halves(hp, st);
     if (ws) {
         const hipError_t ef = hipFreeAsync(ws, st);
         if (e == hipSuccess) e = ef;

@@ -53,6 +53,22 @@ struct ChunkParams {
     const int32_t *pos_off;  // [N] position of each sequence's first token, or nullptr (0)
     float theta;             // RoPE base
     float eps;               // RMSNorm epsilon
+    // Sub-segments per output segment: the state and scan kernels work on
+    // segments of seg_len tokens, and an output pass over segments rsub times
+    // longer starts output segment j of a sequence from the state the scan
+    // leaves in slot first + rsub * j. 1 when both passes use the same segments.
+    int rsub;
+};
+
+// Arguments of the value-half output kernel (chunk_halves.hip): the output
+// segments (oseg_len tokens each, from `osegs` or arithmetic), and in `c` the
+// sub-segment tables, the state buffer and the tensors.
+struct HalvesParams {
+    ChunkParams c;
+    const SegEntry *osegs;  // [onseg_max], or nullptr for B equal rows
+    int onseg_max;
+    int onps;               // output segments per sequence when osegs == nullptr
+    int oseg_len;           // tokens per output segment (a multiple of the chunk size)
 };
 
 // Segment s of the call. Without a table (no cu_seqlens) every sequence has
@@ -144,6 +160,7 @@ hipError_t launch_scan(const ChunkParams &p, int Dk, int Dv, hipStream_t st);
 hipError_t launch_chunk_valu(const ChunkParams &p, bool bf16, int Dk, int Dv, bool phase_state,
                              hipStream_t st);
 hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t st);
+hipError_t launch_chunk_halves(const HalvesParams &hp, hipStream_t st);
 hipError_t launch_out_norm_gate(const void *o, const void *z, const float *w, void *out,
                                 int64_t rows, int width, float eps, bool bf16, hipStream_t st);
 // Decode-step prologue arguments; qw == nullptr: none.

@@ -19,13 +19,28 @@ pytestmark = pytest.mark.gpu
 DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
+SEG_ENV = ("SGLA_SEG_LEN", "SGLA_OUT_SEG_LEN", "SGLA_RSUB", "SGLA_ONE_LEVEL", "SGLA_VALUE_HALVES")
+
+
 @pytest.fixture(autouse=True)
 def _seg_len_env():
-    old = os.environ.pop("SGLA_SEG_LEN", None)
+    old = {k: os.environ.pop(k, None) for k in SEG_ENV}
     yield
-    os.environ.pop("SGLA_SEG_LEN", None)
-    if old is not None:
-        os.environ["SGLA_SEG_LEN"] = old
+    for k in SEG_ENV:
+        os.environ.pop(k, None)
+        if old[k] is not None:
+            os.environ[k] = old[k]
+
+
+def set_segments(seg_len, rsub=None):
+    """Segment lengths for both prefill paths: SGLA_SEG_LEN for the one-level
+    kernels (fp32, 64-wide heads, the prologue), SGLA_OUT_SEG_LEN (and the
+    number of state-pass sub-segments per output segment, SGLA_RSUB) for the
+    bf16 value-half kernel."""
+    os.environ["SGLA_SEG_LEN"] = str(seg_len)
+    os.environ["SGLA_OUT_SEG_LEN"] = str(seg_len)
+    if rsub is not None:
+        os.environ["SGLA_RSUB"] = str(rsub)
 
 
 def run_gpu(inp, poison=True, final=True):
@@ -86,7 +101,7 @@ def test_multi_segment_state_passing(dtype, seg_len):
     """Force short segments so sequences span several workgroups and the
     carried state goes through the segment scan."""
     say("chunk_fwd segments", dtype, "seg_len", seg_len)
-    os.environ["SGLA_SEG_LEN"] = str(seg_len)
+    set_segments(seg_len)
     T = 1000
     inp = W.make_prefill(2, T, 3, 128, 128, dtype, "lightning", seed=seg_len, device="cuda",
                          init="normal")
@@ -95,15 +110,37 @@ def test_multi_segment_state_passing(dtype, seg_len):
     ro, rS = compare(inp, o, S, dtype, "segments %d" % seg_len, starts=starts)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_varlen_packed_matches_oracle_and_separate_runs(dtype):
+@pytest.mark.parametrize("oseg,rsub", [(128, 1), (128, 2), (256, 4), (512, 2), (1024, 4),
+                                       (640, 5)])
+def test_value_half_segments_and_sub_segments(oseg, rsub):
+    """The bf16 value-half path with a sequence over several output segments:
+    the state pass runs over rsub sub-segments per output segment and the
+    scan keeps only the output segments' start states."""
+    say("chunk_fwd value halves oseg", oseg, "rsub", rsub, "B=2 T=1700 H=3 S0")
+    set_segments(oseg, rsub)
+    T = 1700
+    inp = W.make_prefill(2, T, 3, 128, 128, "bf16", "lightning", seed=oseg + rsub, device="cuda",
+                         init="normal")
+    o, S = run_gpu(inp)
+    compare(inp, o, S, "bf16", "halves %d/%d" % (oseg, rsub),
+            starts=[0] + list(range(oseg, T, oseg)))
+
+
+@pytest.mark.parametrize("dtype,path", [("f32", None), ("bf16", "one_level"), ("bf16", "halves")])
+def test_varlen_packed_matches_oracle_and_separate_runs(dtype, path):
+    """Packed sequences on each bf16 path: the one-level kernels (the default
+    with cu_seqlens) and the value-half kernels (the default without)."""
+    if path == "halves":
+        os.environ["SGLA_VALUE_HALVES"] = "1"
+    else:
+        os.environ["SGLA_ONE_LEVEL"] = "1"
     lengths = [0, 1, 63, 64, 65, 200, 0, 700, 129]
     cu = W.cu_from_lengths(lengths)
     T = int(cu[-1])
     say("chunk_fwd varlen", dtype, lengths)
     inp = W.make_prefill(1, T, 4, 128, 128, dtype, "lightning", seed=3, device="cuda",
                          cu_seqlens=cu, init="normal")
-    os.environ["SGLA_SEG_LEN"] = "128"
+    set_segments(128)
     o, S = run_gpu(inp)
     compare(inp, o, S, dtype, "varlen", starts=[int(c) for c in cu[:-1]])
     # Packed equals separate runs, bit for bit (same segment length).
@@ -123,7 +160,7 @@ def test_varlen_packed_matches_oracle_and_separate_runs(dtype):
 
 def test_no_final_state_and_in_place_state():
     say("chunk_fwd final_state None / in place")
-    os.environ["SGLA_SEG_LEN"] = "128"
+    set_segments(128)
     inp = W.make_prefill(2, 700, 2, 64, 64, "bf16", "lightning", seed=9, device="cuda",
                          init="normal")
     o1, S1 = run_gpu(inp)
@@ -214,8 +251,11 @@ def test_workload_prefill_64k_continuation_and_split():
     check_windows(oc[0], ro[0], [t], "bf16", "64k split")
 
 
-def test_workload_varlen_512k():
-    say("chunk_fwd workload varlen bf16 8 seqs 524288 tokens H=32 D=128 seed=5 (4 heads)")
+@pytest.mark.parametrize("path", ["one_level", "halves"])
+def test_workload_varlen_512k(path):
+    if path == "halves":
+        os.environ["SGLA_VALUE_HALVES"] = "1"
+    say("chunk_fwd workload varlen bf16 8 seqs 524288 tokens H=32 D=128 seed=5 (4 heads)", path)
     inp = W.make_workload("varlen_bf16_h32_d128_8seq_512k", seed=5, device="cuda")
     o, S = run_gpu(inp)
     heads = _sample_heads(32, 4, 5)
@@ -231,7 +271,7 @@ def test_most_heads_ragged_chunk(seg_len):
     kernels' per-chunk byte ranges and row offsets are at their largest (about
     2^30). With 64-token segments the segment-state and scan kernels run too."""
     if seg_len:
-        os.environ["SGLA_SEG_LEN"] = str(seg_len)
+        set_segments(seg_len)
     say("chunk_fwd bf16 B=1 T=70 H=65536 D=128 seed=77 seg_len", seg_len, "(4 sampled heads)")
     inp = W.make_prefill(1, 70, 65536, 128, 128, "bf16", "lightning", seed=77, device="cuda",
                          init="normal")
