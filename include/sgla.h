@@ -34,11 +34,14 @@
  *     reported synchronously, before anything is enqueued. Launch failures map
  *     to SGLA_ERR_HIP. Faults inside kernels surface at the caller's next
  *     synchronisation, as usual in HIP.
- *   - The library is re-entrant: it keeps no global mutable state.
+ *   - The library is re-entrant: it keeps no global mutable state, and it
+ *     allocates no memory: scratch space comes from a caller-owned workspace
+ *     (the *_ex entry points, sized by the *_workspace_size queries).
  */
 #ifndef SGLA_H_
 #define SGLA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -49,7 +52,9 @@ typedef enum {
     SGLA_OK = 0,
     SGLA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad enum      */
     SGLA_ERR_UNSUPPORTED = 2, /* a size or combination this build does not handle */
-    SGLA_ERR_HIP = 3          /* a HIP runtime call or a launch failed              */
+    SGLA_ERR_HIP = 3,         /* a HIP runtime call or a launch failed              */
+    SGLA_ERR_WORKSPACE = 4    /* the call needs a (larger) caller workspace: see the
+                                 *_workspace_size queries and the *_ex entry points */
 } sgla_status;
 
 typedef enum {
@@ -95,10 +100,11 @@ typedef enum {
  *   dtype         element type of q, k, v, out.
  *   stream        hipStream_t, or NULL.
  *
- * Memory: the call takes a temporary device workspace from HIP's
- * stream-ordered allocator (hipMallocAsync/hipFreeAsync on `stream`) when a
- * sequence is long enough to be split across workgroups; its size is at most
- * (T / 256 + B + 1) * H * Dk * Dv * 4 bytes plus a small table.
+ * Memory: allocates nothing and takes no workspace. Every sequence is one
+ * segment: one workgroup per (sequence, head), or per (sequence, head, half
+ * of the value columns) for bf16 with Dk = Dv = 128. That is the fastest plan
+ * when B * H fills the chip; with few long sequences, sgla_chunk_fwd_ex with a
+ * workspace splits each sequence across many workgroups.
  * out must not alias q, k, v or g.
  *
  * Returns SGLA_OK, or SGLA_ERR_INVALID_ARG (null required pointer, negative
@@ -109,6 +115,67 @@ sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const fl
                            const float *initial_state, void *out, float *final_state,
                            const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv,
                            float scale, sgla_dtype dtype, void *stream);
+
+/*
+ * sgla_chunk_fwd_workspace_size — bytes of device workspace sgla_chunk_fwd_ex
+ * uses for these sizes (0 when the call needs none).
+ *
+ *   varlen    0: B sequences of T tokens; 1: packed sequences (cu_seqlens),
+ *             T the packed total. The size is a bound over every cu_seqlens
+ *             with that B and T.
+ *   prologue  0 or 1: whether q_weight will be given (the q/k prologue).
+ * Other arguments as sgla_chunk_fwd. Writes *bytes (0 on error) and returns
+ * SGLA_OK, SGLA_ERR_INVALID_ARG or SGLA_ERR_UNSUPPORTED under the rules of
+ * sgla_chunk_fwd.
+ */
+sgla_status sgla_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, sgla_dtype dtype,
+                                          int varlen, int prologue, size_t *bytes);
+
+/*
+ * sgla_chunk_fwd_ex — sgla_chunk_fwd with every option: the q/k prologue
+ * (q_weight != NULL; see sgla_chunk_fwd_qk_norm_rope below for its arguments
+ * and conditions) and a caller-owned workspace that lets long sequences be
+ * split across workgroups.
+ *
+ * With a workspace each sequence is cut into segments. A first pass computes
+ * every segment's state contribution from a zero state, a scan combines them
+ * in order into the state each segment starts from (the recurrence regrouped:
+ * the decayed initial state plus the decayed sum of outer products, blueprint
+ * page, section "Why Linear Attention Loses Information"), and the output
+ * pass runs all segments at once. With packed sequences, device-side tables
+ * lay the segments out from cu_seqlens.
+ *
+ *   workspace        device memory, 256-byte aligned, owned by the caller,
+ *                    or NULL (then the call plans as sgla_chunk_fwd and needs
+ *                    none). Its contents need no initialisation and are
+ *                    meaningless after the call, except word 0 (int32) when
+ *                    the environment sets SGLA_VALIDATE: the cu_seqlens check
+ *                    of sgla_validate_cu_seqlens. Calls that overlap in time
+ *                    must use different workspaces.
+ *   workspace_bytes  its size; at least what sgla_chunk_fwd_workspace_size
+ *                    reports for these sizes, or the call returns
+ *                    SGLA_ERR_WORKSPACE without enqueuing anything.
+ * All other arguments and the return codes are those of sgla_chunk_fwd.
+ */
+sgla_status sgla_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g,
+                              const float *initial_state, void *out, float *final_state,
+                              const int64_t *cu_seqlens, const float *q_weight,
+                              const float *k_weight, const int32_t *pos_offset, float theta,
+                              float eps, int B, int T, int H, int Dk, int Dv, float scale,
+                              sgla_dtype dtype, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/*
+ * sgla_validate_cu_seqlens — checks packed-sequence offsets on the device
+ * (the rules under sgla_chunk_fwd: cu[0] = 0, non-decreasing, cu[B] = T) and
+ * writes to *status (device int32, 4-byte aligned) the sum of the rules
+ * broken: 1 cu[0] != 0, 2 some cu[i] > cu[i+1], 4 cu[B] != T; 0 if none.
+ * cu_seqlens holds B + 1 int64 values, 8-byte aligned, never NULL. Enqueued
+ * on `stream`; read *status after synchronising. Returns SGLA_OK,
+ * SGLA_ERR_INVALID_ARG or SGLA_ERR_HIP. Allocates nothing.
+ */
+sgla_status sgla_validate_cu_seqlens(const int64_t *cu_seqlens, int B, int T, int32_t *status,
+                                     void *stream);
 
 /*
  * sgla_recurrent_step — one decode token per row, state updated in place.
@@ -174,8 +241,9 @@ sgla_status sgla_recurrent_step(const void *q, const void *k, const void *v, con
  *               sequence continued from an earlier call passes the number of
  *               tokens already processed.
  *   theta, eps  RoPE base (10000 on the page) and RMSNorm epsilon.
- * All other arguments, the workspace and the return codes are those of
- * sgla_chunk_fwd.
+ * All other arguments and the return codes are those of sgla_chunk_fwd; it
+ * allocates nothing and takes no workspace (sgla_chunk_fwd_ex with q_weight
+ * takes one).
  */
 sgla_status sgla_chunk_fwd_qk_norm_rope(const void *q, const void *k, const void *v,
                                         const float *g, const float *initial_state, void *out,
@@ -294,16 +362,39 @@ sgla_status sgla_out_norm_gate(const void *o, const void *z, const float *weight
  * Only dtype SGLA_BF16 with Dk = Dv = 128 and B * H <= 2^28 - 8 (B the
  * number of sequences) is supported (SGLA_ERR_UNSUPPORTED otherwise).
  *
- * Memory: the call takes a device workspace from HIP's stream-ordered
- * allocator on `stream` of (T / 64 + B + 1) * H * 64 KiB (per chunk and head
- * W and new_v in bf16, U in fp32; B * ceil(T / 64) * H * 64 KiB without
- * cu_seqlens) plus a small table, and frees it on the same stream. Returns as
- * sgla_chunk_fwd.
+ * Memory: the chunkwise form keeps, per chunk and head, W and new_v in bf16
+ * and U in fp32 (64 KiB) in device memory between its kernels, so the call
+ * needs a caller workspace: sgla_gdn_chunk_fwd returns SGLA_ERR_WORKSPACE
+ * whenever there are tokens to process (use sgla_gdn_chunk_fwd_ex), and
+ * otherwise (B = 0, or T = 0 with the final state copied) succeeds without
+ * one. Returns as sgla_chunk_fwd.
  */
 sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                                const float *beta, const float *initial_state, void *out,
                                float *final_state, const int64_t *cu_seqlens, int B, int T, int H,
                                int Dk, int Dv, float scale, sgla_dtype dtype, void *stream);
+
+/*
+ * sgla_gdn_chunk_fwd_workspace_size — bytes of workspace sgla_gdn_chunk_fwd_ex
+ * needs: 256 + (tables with varlen) + (chunks * H) * 64 KiB, where chunks is
+ * B * ceil(T / 64), or T / 64 + B + 1 with varlen (a bound over every
+ * cu_seqlens). Arguments and return codes as sgla_chunk_fwd_workspace_size.
+ */
+sgla_status sgla_gdn_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                              sgla_dtype dtype, int varlen, size_t *bytes);
+
+/*
+ * sgla_gdn_chunk_fwd_ex — sgla_gdn_chunk_fwd with a caller-owned workspace
+ * (256-byte aligned, workspace_bytes at least the size query's answer, or
+ * SGLA_ERR_WORKSPACE; contents need no initialisation; overlapping calls need
+ * different workspaces; word 0 receives the cu_seqlens check under
+ * SGLA_VALIDATE as for sgla_chunk_fwd_ex). Allocates nothing.
+ */
+sgla_status sgla_gdn_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, const float *initial_state, void *out,
+                                  float *final_state, const int64_t *cu_seqlens, int B, int T,
+                                  int H, int Dk, int Dv, float scale, sgla_dtype dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * sgla_gdn_recurrent_step — one GDN decode token per row, state updated in

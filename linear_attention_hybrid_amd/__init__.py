@@ -38,13 +38,14 @@ import torch
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_qk_norm_rope", "recurrent_step_qk_norm_rope",
            "recurrent_step_ex", "out_norm_gate", "gdn_chunk_fwd", "gdn_recurrent_step",
+           "chunk_workspace_size", "gdn_workspace_size", "validate_cu_seqlens",
            "status_string", "library", "library_path", "exported_symbols", "SglaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libsgla.so")
 header_path = os.path.join(os.path.dirname(_HERE), "include", "sgla.h")
 
-SGLA_OK, SGLA_ERR_INVALID_ARG, SGLA_ERR_UNSUPPORTED, SGLA_ERR_HIP = 0, 1, 2, 3
+SGLA_OK, SGLA_ERR_INVALID_ARG, SGLA_ERR_UNSUPPORTED, SGLA_ERR_HIP, SGLA_ERR_WORKSPACE = 0, 1, 2, 3, 4
 SGLA_F32, SGLA_BF16 = 0, 1
 _DTYPE = {torch.float32: SGLA_F32, torch.bfloat16: SGLA_BF16}
 
@@ -90,6 +91,19 @@ def library():
         lib.sgla_gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf,
                                                 ci, vp]
         lib.sgla_gdn_recurrent_step.restype = ci
+        zp = ctypes.POINTER(ctypes.c_size_t)
+        lib.sgla_chunk_fwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, zp]
+        lib.sgla_chunk_fwd_workspace_size.restype = ci
+        lib.sgla_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, cf, ci,
+                                          ci, ci, ci, ci, cf, ci, vp, ctypes.c_size_t, vp]
+        lib.sgla_chunk_fwd_ex.restype = ci
+        lib.sgla_validate_cu_seqlens.argtypes = [vp, ci, ci, vp, vp]
+        lib.sgla_validate_cu_seqlens.restype = ci
+        lib.sgla_gdn_chunk_fwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, zp]
+        lib.sgla_gdn_chunk_fwd_workspace_size.restype = ci
+        lib.sgla_gdn_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci,
+                                              ci, cf, ci, vp, ctypes.c_size_t, vp]
+        lib.sgla_gdn_chunk_fwd_ex.restype = ci
         lib.sgla_status_string.argtypes = [ci]
         lib.sgla_status_string.restype = ctypes.c_char_p
         lib.sgla_version.argtypes = []
@@ -172,8 +186,64 @@ def _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
                 sizes=(Barg, T, H, Dk, Dv), scale=float(scale))
 
 
+def chunk_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16, varlen=False, prologue=False):
+    """Bytes of workspace ``sgla_chunk_fwd_ex`` takes for these sizes (B is the
+    number of sequences; with ``varlen`` T is the packed total)."""
+    n = ctypes.c_size_t(0)
+    st = library().sgla_chunk_fwd_workspace_size(int(B), int(T), int(H), int(Dk), int(Dv),
+                                                  _DTYPE[dtype], int(bool(varlen)),
+                                                  int(bool(prologue)), ctypes.byref(n))
+    if st != SGLA_OK:
+        raise SglaError("sgla_chunk_fwd_workspace_size", st)
+    return int(n.value)
+
+
+def gdn_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16, varlen=False):
+    """Bytes of workspace ``sgla_gdn_chunk_fwd_ex`` takes for these sizes."""
+    n = ctypes.c_size_t(0)
+    st = library().sgla_gdn_chunk_fwd_workspace_size(int(B), int(T), int(H), int(Dk), int(Dv),
+                                                      _DTYPE[dtype], int(bool(varlen)),
+                                                      ctypes.byref(n))
+    if st != SGLA_OK:
+        raise SglaError("sgla_gdn_chunk_fwd_workspace_size", st)
+    return int(n.value)
+
+
+def _workspace(workspace, nbytes, device):
+    """The workspace pointer and size to pass: "auto" takes a byte tensor from
+    torch's allocator, None passes none, a uint8 tensor is used as given."""
+    if workspace is None:
+        return None, 0, None
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+        if nbytes == 0:
+            return None, 0, None
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % device)
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), workspace
+
+
+def validate_cu_seqlens(cu_seqlens, T):
+    """Check packed-sequence offsets on the GPU (sgla_validate_cu_seqlens) and
+    return the bits of the rules they break: 1 cu[0] != 0, 2 decreasing, 4
+    cu[-1] != T; 0 when valid. Synchronises with the device."""
+    device = cu_seqlens.device
+    _check(cu_seqlens, "cu_seqlens", torch.int64, (cu_seqlens.numel(),), device)
+    status = torch.full((1,), -1, dtype=torch.int32, device=device)
+    with torch.cuda.device(device):
+        st = library().sgla_validate_cu_seqlens(_ptr(cu_seqlens), cu_seqlens.numel() - 1, int(T),
+                                                _ptr(status), _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_validate_cu_seqlens", st)
+    return int(status.item())
+
+
 def chunk_fwd(q, k, v, g, initial_state=None, cu_seqlens=None, scale=None, out=None,
-              final_state=None, output_final_state=True):
+              final_state=None, output_final_state=True, workspace="auto"):
     """Chunked Simple GLA prefill.
 
     q, k [B, T, H, Dk], v [B, T, H, Dv] (fp32 or bf16, same dtype, on one GPU),
@@ -183,16 +253,24 @@ def chunk_fwd(q, k, v, g, initial_state=None, cu_seqlens=None, scale=None, out=N
     1/sqrt(Dk). Returns (o [B, T, H, Dv] in v's dtype, final_state [N, H, Dk,
     Dv] fp32, or None when output_final_state is False and none was given).
     ``final_state`` may be passed in (also the same tensor as initial_state).
+    ``workspace``: "auto" (a workspace from torch's allocator, so long
+    sequences are split across workgroups), None (no workspace: one segment
+    per sequence), or a uint8 tensor of at least ``chunk_workspace_size``
+    bytes.
     """
     a = _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
                     output_final_state)
     device = a["device"]
     with torch.cuda.device(device):
-        st = library().sgla_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state),
-                                      _ptr(a["out"]), _ptr(a["final_state"]), _ptr(cu_seqlens),
-                                      *a["sizes"], a["scale"], _DTYPE[q.dtype], _stream(device))
+        nb = chunk_workspace_size(*a["sizes"], dtype=q.dtype, varlen=cu_seqlens is not None) \
+            if isinstance(workspace, str) else 0
+        wp, wn, _keep = _workspace(workspace, nb, device)
+        st = library().sgla_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state),
+                                         _ptr(a["out"]), _ptr(a["final_state"]), _ptr(cu_seqlens),
+                                         None, None, None, 0.0, 0.0, *a["sizes"], a["scale"],
+                                         _DTYPE[q.dtype], wp, wn, _stream(device))
     if st != SGLA_OK:
-        raise SglaError("sgla_chunk_fwd", st)
+        raise SglaError("sgla_chunk_fwd_ex", st)
     return a["out"], a["final_state"]
 
 
@@ -203,12 +281,13 @@ def _prologue_args(q_weight, k_weight, Dk, device):
 
 def chunk_fwd_qk_norm_rope(q, k, v, g, q_weight, k_weight, pos_offset=None, theta=10000.0,
                            eps=1e-6, initial_state=None, cu_seqlens=None, scale=None, out=None,
-                           final_state=None, output_final_state=True):
+                           final_state=None, output_final_state=True, workspace="auto"):
     """``chunk_fwd`` with q and k given before the per-head RMSNorm (weights
     q_weight, k_weight: fp32 [Dk], shared by all heads) and the rotate-half
     RoPE with base ``theta``, both applied inside the kernels (bf16, Dk = Dv =
     128 only). ``pos_offset`` (int32 [N] or None for zeros) is the position of
-    each sequence's first token; the others follow one by one.
+    each sequence's first token; the others follow one by one. ``workspace``
+    as for ``chunk_fwd``.
     """
     a = _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
                     output_final_state)
@@ -217,13 +296,16 @@ def chunk_fwd_qk_norm_rope(q, k, v, g, q_weight, k_weight, pos_offset=None, thet
     if pos_offset is not None:
         _check(pos_offset, "pos_offset", torch.int32, (a["N"],), device)
     with torch.cuda.device(device):
-        st = library().sgla_chunk_fwd_qk_norm_rope(
+        nb = chunk_workspace_size(*a["sizes"], dtype=q.dtype, varlen=cu_seqlens is not None,
+                                  prologue=True) if isinstance(workspace, str) else 0
+        wp, wn, _keep = _workspace(workspace, nb, device)
+        st = library().sgla_chunk_fwd_ex(
             _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(initial_state), _ptr(a["out"]),
             _ptr(a["final_state"]), _ptr(cu_seqlens), _ptr(q_weight), _ptr(k_weight),
             _ptr(pos_offset), float(theta), float(eps), *a["sizes"], a["scale"],
-            _DTYPE[q.dtype], _stream(device))
+            _DTYPE[q.dtype], wp, wn, _stream(device))
     if st != SGLA_OK:
-        raise SglaError("sgla_chunk_fwd_qk_norm_rope", st)
+        raise SglaError("sgla_chunk_fwd_ex", st)
     return a["out"], a["final_state"]
 
 
@@ -353,21 +435,28 @@ def recurrent_step_ex(q, k, v, g, state, state_indices=None, q_weight=None, k_we
 
 
 def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None, out=None,
-                  final_state=None, output_final_state=True):
+                  final_state=None, output_final_state=True, workspace="auto"):
     """Chunked prefill of the gated delta rule: arguments and results as
     ``chunk_fwd``, plus ``beta`` [B, T, H] fp32, the write strength of each
-    token and head. bf16 with Dk = Dv = 128 only."""
+    token and head. bf16 with Dk = Dv = 128 only. The chunkwise form keeps
+    per-chunk tiles between its kernels, so ``workspace`` ("auto" or a uint8
+    tensor of ``gdn_workspace_size`` bytes) is required when there are tokens.
+    """
     a = _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
                     output_final_state)
     device = a["device"]
     _check(beta, "beta", torch.float32, tuple(g.shape), device)
     with torch.cuda.device(device):
-        st = library().sgla_gdn_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                          _ptr(initial_state), _ptr(a["out"]),
-                                          _ptr(a["final_state"]), _ptr(cu_seqlens), *a["sizes"],
-                                          a["scale"], _DTYPE[q.dtype], _stream(device))
+        nb = gdn_workspace_size(*a["sizes"], dtype=q.dtype, varlen=cu_seqlens is not None) \
+            if isinstance(workspace, str) else 0
+        wp, wn, _keep = _workspace(workspace, nb, device)
+        st = library().sgla_gdn_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                             _ptr(initial_state), _ptr(a["out"]),
+                                             _ptr(a["final_state"]), _ptr(cu_seqlens),
+                                             *a["sizes"], a["scale"], _DTYPE[q.dtype], wp, wn,
+                                             _stream(device))
     if st != SGLA_OK:
-        raise SglaError("sgla_gdn_chunk_fwd", st)
+        raise SglaError("sgla_gdn_chunk_fwd_ex", st)
     return a["out"], a["final_state"]
 
 

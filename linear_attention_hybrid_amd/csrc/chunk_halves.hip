@@ -94,9 +94,10 @@ __device__ __forceinline__ int sx_off(int cc, int b, int s2, int l) {
     return L_SX + (((cc * 4 + b) * 2 + s2) * 64 + l) * 16;
 }
 
-// Output segment s of the call (arithmetic without a table, as seg_at).
+// Output segment s of the call (without a table as seg_at).
 __device__ __forceinline__ SegEntry oseg_at(const HalvesParams &hp, int s) {
     if (hp.osegs) return hp.osegs[s];
+    if (hp.c.cu) return seg_from_cu(hp.c.cu, s, hp.c.T);
     SegEntry e;
     const int n = s / hp.onps;
     const int j = s - n * hp.onps;

@@ -154,6 +154,30 @@ __global__ __launch_bounds__(256) void scan_kernel(ChunkParams p) {
     }
 }
 
+// One workgroup checks the offsets' rules and writes the bits of the broken
+// ones (see launch_validate_cu).
+__global__ __launch_bounds__(256) void validate_cu_kernel(const int64_t *__restrict__ cu, int B, int T,
+                                                          int32_t *__restrict__ status) {
+    __shared__ int32_t bits;
+    if (threadIdx.x == 0) bits = 0;
+    __syncthreads();
+    int32_t mine = 0;
+    for (int i = threadIdx.x; i < B; i += blockDim.x)
+        if (cu[i] > cu[i + 1]) mine |= 2;
+    if (threadIdx.x == 0) {
+        if (cu[0] != 0) mine |= 1;
+        if (cu[B] != (int64_t)T) mine |= 4;
+    }
+    if (mine) atomicOr(&bits, mine);
+    __syncthreads();
+    if (threadIdx.x == 0) *status = bits;
+}
+
+hipError_t launch_validate_cu(const int64_t *cu, int B, int T, int32_t *status, hipStream_t st) {
+    hipLaunchKernelGGL(validate_cu_kernel, dim3(1), dim3(256), 0, st, cu, B, T, status);
+    return hipGetLastError();
+}
+
 hipError_t launch_plan(const int64_t *cu, int B, int T, int seg_len, int nseg_max,
                        SegEntry *segs, SeqEntry *seqs, hipStream_t st) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, st, cu, B, T, seg_len, nseg_max, segs,

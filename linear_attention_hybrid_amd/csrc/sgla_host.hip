@@ -93,14 +93,34 @@ sgla_status check_prologue(const ProArgs &a) {
     return SGLA_OK;
 }
 
+// The plan of one chunked Simple GLA call: which kernels run, how sequences
+// are cut into segments, and where the tables and states sit in the caller's
+// workspace (a 256-byte header first: word 0 receives the cu_seqlens check
+// when SGLA_VALIDATE is set). Computed the same way for the workspace-size
+// query and for the call.
+struct ChunkPlan {
+    bool halves = false;   // value-half output kernel (bf16, 128-wide heads, no prologue)
+    bool mfma = false;     // one-level kernels on the matrix cores (else the vector ALUs)
+    bool table = false;    // segment tables built on the device from cu_seqlens
+    bool split = false;    // state pass and scan (some sequence spans several segments)
+    int seg_len = 0;       // one-level segments, or the state pass's sub-segments
+    int64_t nps = 1;       // segments per sequence without a table
+    int64_t nseg = 0;      // table rows (segments) of the one-level or state pass
+    int rsub = 1;          // sub-segments per output segment (value halves)
+    int oseg_len = 0;      // value-half output segments
+    int64_t onps = 1;
+    int64_t onseg = 0;
+    size_t off_osegs = 0, off_oseqs = 0, off_segs = 0, off_seqs = 0, off_gam = 0, off_buf = 0;
+    size_t bytes = 0;      // workspace bytes (0: none)
+};
+
+sgla_status make_plan(int B, int T, int H, int Dk, int Dv, sgla_dtype dtype, bool varlen, bool pro,
+                      bool split_ok, ChunkPlan &pl);
 sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *g,
                       const float *initial_state, void *out, float *final_state,
                       const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv, float scale,
-                      sgla_dtype dtype, void *stream, const ProArgs *pro);
-sgla_status chunk_fwd_halves(const void *q, const void *k, const void *v, const float *g,
-                             const float *initial_state, void *out, float *final_state,
-                             const int64_t *cu_seqlens, int B, int T, int H, float scale,
-                             void *stream);
+                      sgla_dtype dtype, void *stream, const ProArgs *pro, void *workspace,
+                      size_t workspace_bytes);
 
 }  // namespace
 
@@ -112,6 +132,7 @@ const char *sgla_status_string(sgla_status s) {
         case SGLA_ERR_INVALID_ARG: return "SGLA_ERR_INVALID_ARG";
         case SGLA_ERR_UNSUPPORTED: return "SGLA_ERR_UNSUPPORTED";
         case SGLA_ERR_HIP: return "SGLA_ERR_HIP";
+        case SGLA_ERR_WORKSPACE: return "SGLA_ERR_WORKSPACE";
     }
     return "SGLA_ERR_UNKNOWN";
 }
@@ -123,7 +144,44 @@ sgla_status sgla_chunk_fwd(const void *q, const void *k, const void *v, const fl
                            const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv,
                            float scale, sgla_dtype dtype, void *stream) {
     return chunk_fwd(q, k, v, g, initial_state, out, final_state, cu_seqlens, B, T, H, Dk, Dv,
-                     scale, dtype, stream, nullptr);
+                     scale, dtype, stream, nullptr, nullptr, 0);
+}
+
+sgla_status sgla_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, sgla_dtype dtype,
+                                          int varlen, int prologue, size_t *bytes) {
+    if (!bytes) return SGLA_ERR_INVALID_ARG;
+    *bytes = 0;
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
+    if (!head_size_ok(Dk) || !head_size_ok(Dv) || H > kMaxHeads) return SGLA_ERR_UNSUPPORTED;
+    if (prologue && (dtype != SGLA_BF16 || Dk != 128 || Dv != 128)) return SGLA_ERR_UNSUPPORTED;
+    const int64_t ttot = varlen ? (int64_t)T : (int64_t)B * T;
+    if (ttot > ((int64_t)1 << 62) / ((int64_t)H * 128)) return SGLA_ERR_INVALID_ARG;
+    if ((int64_t)B * H > (int64_t)1 << 30) return SGLA_ERR_INVALID_ARG;
+    if (B == 0) return SGLA_OK;
+    ChunkPlan pl;
+    const sgla_status st = make_plan(B, T, H, Dk, Dv, dtype, varlen != 0, prologue != 0, true, pl);
+    if (st == SGLA_OK) *bytes = pl.bytes;
+    return st;
+}
+
+sgla_status sgla_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g,
+                              const float *initial_state, void *out, float *final_state,
+                              const int64_t *cu_seqlens, const float *q_weight,
+                              const float *k_weight, const int32_t *pos_offset, float theta,
+                              float eps, int B, int T, int H, int Dk, int Dv, float scale,
+                              sgla_dtype dtype, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    const ProArgs pro{q_weight, k_weight, pos_offset, theta, eps};
+    return chunk_fwd(q, k, v, g, initial_state, out, final_state, cu_seqlens, B, T, H, Dk, Dv,
+                     scale, dtype, stream, q_weight ? &pro : nullptr, workspace, workspace_bytes);
+}
+
+sgla_status sgla_validate_cu_seqlens(const int64_t *cu_seqlens, int B, int T, int32_t *status,
+                                     void *stream) {
+    if (B < 0 || T < 0 || !status || !cu_seqlens) return SGLA_ERR_INVALID_ARG;
+    if (misaligned(cu_seqlens, 8) || misaligned(status, 4)) return SGLA_ERR_INVALID_ARG;
+    return hip_status(launch_validate_cu(cu_seqlens, B, T, status, static_cast<hipStream_t>(stream)));
 }
 
 sgla_status sgla_chunk_fwd_qk_norm_rope(const void *q, const void *k, const void *v,
@@ -135,17 +193,83 @@ sgla_status sgla_chunk_fwd_qk_norm_rope(const void *q, const void *k, const void
                                         sgla_dtype dtype, void *stream) {
     const ProArgs pro{q_weight, k_weight, pos_offset, theta, eps};
     return chunk_fwd(q, k, v, g, initial_state, out, final_state, cu_seqlens, B, T, H, Dk, Dv,
-                     scale, dtype, stream, &pro);
+                     scale, dtype, stream, &pro, nullptr, 0);
 }
 
 }  // extern "C"
 
 namespace {
 
-sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *g,
-                      const float *initial_state, void *out, float *final_state,
-                      const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv, float scale,
-                      sgla_dtype dtype, void *stream, const ProArgs *pro) {
+constexpr size_t kWsHeader = 256;
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// split_ok: a workspace may be used. Without one, every sequence is one
+// segment (one workgroup per sequence and head, or per sequence, head and
+// value half), which needs no tables and no states.
+sgla_status make_plan(int B, int T, int H, int Dk, int Dv, sgla_dtype dtype, bool varlen, bool pro,
+                      bool split_ok, ChunkPlan &pl) {
+    const int64_t ttot = varlen ? (int64_t)T : (int64_t)B * T;
+    const bool bf16 = dtype == SGLA_BF16;
+    // bf16 with 128-wide heads and no prologue: equal-length batches run on
+    // the value-half kernels (less state traffic; as fast on 8K-token
+    // sequences and faster on long ones). Packed sequences of mixed lengths
+    // stay on the one-level kernels, whose shorter segments balance better:
+    // there the per-chunk work bounds the call, and the value halves repeat
+    // the scores. Without a workspace (one segment per sequence) the value
+    // halves give twice the workgroups. SGLA_VALUE_HALVES / SGLA_ONE_LEVEL
+    // force either path.
+    const bool mfma_ok = bf16 && Dk == 128 && Dv == 128 && !getenv("SGLA_FORCE_VALU");
+    const bool want_halves = getenv("SGLA_ONE_LEVEL") ? false
+                             : getenv("SGLA_VALUE_HALVES") ? true
+                             : !varlen || !split_ok;
+    pl.halves = mfma_ok && !pro && want_halves;
+    pl.mfma = bf16 && Dk == 128 && Dv == 128 && (pro || !getenv("SGLA_FORCE_VALU"));
+    const int whole = T <= 0 ? kChunk : (int)(((int64_t)T + kChunk - 1) / kChunk * kChunk);
+    size_t off = kWsHeader;
+    if (pl.halves) {
+        pl.oseg_len = split_ok ? choose_out_len(ttot, H) : whole;
+        pl.onps = T == 0 ? 1 : ((int64_t)T + pl.oseg_len - 1) / pl.oseg_len;
+        pl.table = varlen && split_ok;
+        pl.onseg = varlen ? (pl.table ? ttot / pl.oseg_len + B + 1 : B) : (int64_t)B * pl.onps;
+        if (pl.onseg * H * 2 > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+        pl.split = pl.table || pl.onps > 1;
+        const int64_t pre_units = varlen ? (ttot / pl.oseg_len) * H : (pl.onps - 1) * B * H;
+        pl.rsub = pl.split ? choose_rsub(pl.oseg_len, pre_units) : 1;
+        pl.seg_len = pl.oseg_len / pl.rsub;
+        pl.nps = T == 0 ? 1 : ((int64_t)T + pl.seg_len - 1) / pl.seg_len;
+        pl.nseg = !pl.split ? 0 : pl.table ? ttot / pl.seg_len + B + 1 : (int64_t)B * pl.nps;
+        if (pl.nseg * H > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+        if (pl.table) {
+            pl.off_osegs = off; off += round256((size_t)pl.onseg * sizeof(SegEntry));
+            pl.off_oseqs = off; off += round256((size_t)B * sizeof(SeqEntry));
+        }
+    } else {
+        pl.seg_len = split_ok ? choose_seg_len(ttot, B, H) : whole;
+        pl.nps = T == 0 ? 1 : ((int64_t)T + pl.seg_len - 1) / pl.seg_len;
+        pl.table = varlen && split_ok;
+        pl.nseg = varlen ? (pl.table ? ttot / pl.seg_len + B + 1 : B) : (int64_t)B * pl.nps;
+        // The vector-ALU kernels run one workgroup per 32 value columns of
+        // each (segment, head); every grid must stay below 2^31.
+        if (pl.nseg * H * ((Dv + 31) / 32) > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+        pl.split = pl.table || pl.nps > 1;
+    }
+    if (pl.table) {
+        pl.off_segs = off; off += round256((size_t)pl.nseg * sizeof(SegEntry));
+        pl.off_seqs = off; off += round256((size_t)B * sizeof(SeqEntry));
+    }
+    if (pl.split) {
+        pl.off_gam = off; off += round256((size_t)pl.nseg * H * sizeof(float));
+        pl.off_buf = off; off += (size_t)pl.nseg * H * Dk * Dv * sizeof(float);
+    }
+    pl.bytes = (pl.table || pl.split) ? off : 0;
+    return SGLA_OK;
+}
+
+sgla_status check_chunk_args(const void *q, const void *k, const void *v, const float *g,
+                             const float *initial_state, const void *out, const float *final_state,
+                             const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv,
+                             sgla_dtype dtype, const ProArgs *pro) {
     if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
     if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
@@ -163,51 +287,32 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) || misaligned(out) ||
         misaligned(initial_state) || misaligned(final_state) || misaligned(cu_seqlens, 8))
         return SGLA_ERR_INVALID_ARG;
+    return SGLA_OK;
+}
+
+sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                      const float *initial_state, void *out, float *final_state,
+                      const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv, float scale,
+                      sgla_dtype dtype, void *stream, const ProArgs *pro, void *workspace,
+                      size_t workspace_bytes) {
+    sgla_status stt = check_chunk_args(q, k, v, g, initial_state, out, final_state, cu_seqlens, B,
+                                       T, H, Dk, Dv, dtype, pro);
+    if (stt != SGLA_OK) return stt;
+    if (misaligned(workspace, 256)) return SGLA_ERR_INVALID_ARG;
+    const int64_t ttot = cu_seqlens ? (int64_t)T : (int64_t)B * T;
     if (B == 0) return SGLA_OK;
     if (ttot == 0 && !final_state) return SGLA_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    // bf16 with 128-wide heads and no prologue: equal-length batches run on
-    // the value-half kernels (less state traffic; as fast on 8K-token
-    // sequences and faster on long ones). Packed sequences of mixed lengths
-    // stay on the one-level kernels, whose shorter segments balance better:
-    // there the per-chunk work bounds the call, and the value halves repeat
-    // the scores. SGLA_VALUE_HALVES / SGLA_ONE_LEVEL force either path.
-    const bool bf16 = dtype == SGLA_BF16;
-    const bool halves = cu_seqlens ? getenv("SGLA_VALUE_HALVES") != nullptr
-                                   : getenv("SGLA_ONE_LEVEL") == nullptr;
-    if (bf16 && Dk == 128 && Dv == 128 && !pro && !getenv("SGLA_FORCE_VALU") && halves)
-        return chunk_fwd_halves(q, k, v, g, initial_state, out, final_state, cu_seqlens, B, T, H,
-                                scale, stream);
+    ChunkPlan pl;
+    stt = make_plan(B, T, H, Dk, Dv, dtype, cu_seqlens != nullptr, pro != nullptr,
+                    workspace != nullptr, pl);
+    if (stt != SGLA_OK) return stt;
+    if (pl.bytes > workspace_bytes) return SGLA_ERR_WORKSPACE;
+    char *ws = static_cast<char *>(workspace);
+    auto at = [&](size_t off) -> char * { return ws ? ws + off : nullptr; };
 
-    const int seg_len = choose_seg_len(ttot, B, H);
-    // Without cu_seqlens every sequence has T tokens and the same number of
-    // segments, so no table is built; with it, a device-side plan kernel lays
-    // the segments out (the host never reads the offsets).
-    const bool table = cu_seqlens != nullptr;
-    const int64_t nps64 = T == 0 ? 1 : ((int64_t)T + seg_len - 1) / seg_len;
-    const int64_t nseg_max64 = table ? ttot / seg_len + B + 1 : (int64_t)B * nps64;
-    // The vector-ALU kernels run one workgroup per 32 value columns of each
-    // (segment, head); every grid must stay below 2^31.
-    if (nseg_max64 * H * ((Dv + 31) / 32) > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
-    const int nseg_max = (int)nseg_max64;
-    // Sequences that fit in one segment need no segment states and no scan.
-    const bool split = table || nps64 > 1;
-
-    // Workspace: segment table, sequence table, per-segment log-decays, states.
-    const size_t segs_b = table ? (size_t)nseg_max * sizeof(SegEntry) : 0;
-    const size_t seqs_b = table ? ((size_t)B * sizeof(SeqEntry) + 255) / 256 * 256 : 0;
-    const size_t gam_b = split ? ((size_t)nseg_max * H * sizeof(float) + 255) / 256 * 256 : 0;
-    const size_t buf_b = split ? (size_t)nseg_max * H * Dk * Dv * sizeof(float) : 0;
-    const size_t ws_b = segs_b + seqs_b + gam_b + buf_b;
-    char *ws = nullptr;
-    hipError_t e = hipSuccess;
-    if (ws_b) {
-        e = hipMallocAsync(reinterpret_cast<void **>(&ws), ws_b, st);
-        if (e != hipSuccess) return SGLA_ERR_HIP;
-    }
-
-    ChunkParams p;
+    ChunkParams p{};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -215,131 +320,61 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
     p.s0 = initial_state;
     p.out = out;
     p.sfin = final_state;
-    p.segs = table ? reinterpret_cast<SegEntry *>(ws) : nullptr;
-    p.seqs = table ? reinterpret_cast<SeqEntry *>(ws + segs_b) : nullptr;
-    p.gam = split ? reinterpret_cast<float *>(ws + segs_b + seqs_b) : nullptr;
-    p.buf = split ? reinterpret_cast<float *>(ws + segs_b + seqs_b + gam_b) : nullptr;
+    p.cu = pl.table ? nullptr : cu_seqlens;
+    p.segs = pl.table ? reinterpret_cast<SegEntry *>(at(pl.off_segs)) : nullptr;
+    p.seqs = pl.table ? reinterpret_cast<SeqEntry *>(at(pl.off_seqs)) : nullptr;
+    p.gam = pl.split ? reinterpret_cast<float *>(at(pl.off_gam)) : nullptr;
+    p.buf = pl.split ? reinterpret_cast<float *>(at(pl.off_buf)) : nullptr;
     p.H = H;
-    p.nseg_max = nseg_max;
+    p.nseg_max = (int)pl.nseg;
     p.N = B;
     p.scale = scale;
     p.T = T;
-    p.seg_len = seg_len;
-    p.nps = (int)nps64;
+    p.seg_len = pl.seg_len;
+    p.nps = (int)pl.nps;
     p.qw = pro ? pro->qw : nullptr;
     p.kw = pro ? pro->kw : nullptr;
     p.pos_off = pro ? pro->pos : nullptr;
     p.theta = pro ? pro->theta : 0.f;
     p.eps = pro ? pro->eps : 0.f;
-    p.rsub = 1;
+    p.rsub = pl.rsub;
+    const bool bf16 = dtype == SGLA_BF16;
 
-    // bf16 with 128-wide heads runs on the matrix cores; every other
-    // combination on the vector ALUs.
-    const bool mfma = bf16 && Dk == 128 && Dv == 128 && (pro || !getenv("SGLA_FORCE_VALU"));
-    auto phase = [&](bool state_phase) {
-        return mfma ? launch_chunk_mfma(p, state_phase, st)
-                    : launch_chunk_valu(p, bf16, Dk, Dv, state_phase, st);
-    };
-    if (table)
-        e = launch_plan(cu_seqlens, B, T, seg_len, nseg_max, reinterpret_cast<SegEntry *>(ws),
-                        reinterpret_cast<SeqEntry *>(ws + segs_b), st);
-    if (e == hipSuccess && split) e = phase(/*state_phase=*/true);
-    if (e == hipSuccess && split) e = launch_scan(p, Dk, Dv, st);
-    if (e == hipSuccess) e = phase(/*state_phase=*/false);
-    if (ws) {
-        const hipError_t ef = hipFreeAsync(ws, st);
-        if (e == hipSuccess) e = ef;
-    }
-    return hip_status(e);
-}
-
-// bf16, Dk = Dv = 128, no prologue: output segments of oseg_len tokens over
-// value-column halves (chunk_halves.hip). When a sequence spans several
-// output segments, the state kernel first computes the zero-start state of
-// every sub-segment (oseg_len / rsub tokens) that precedes its last output
-// segment, and the scan turns them into the start state of each output
-// segment. Arguments are checked by chunk_fwd.
-sgla_status chunk_fwd_halves(const void *q, const void *k, const void *v, const float *g,
-                             const float *initial_state, void *out, float *final_state,
-                             const int64_t *cu_seqlens, int B, int T, int H, float scale,
-                             void *stream) {
-    constexpr int D = 128;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const bool table = cu_seqlens != nullptr;
-    const int64_t ttot = table ? (int64_t)T : (int64_t)B * T;
-    const int oseg_len = choose_out_len(ttot, H);
-    const int64_t onps64 = T == 0 ? 1 : ((int64_t)T + oseg_len - 1) / oseg_len;
-    const int64_t onseg64 = table ? ttot / oseg_len + B + 1 : (int64_t)B * onps64;
-    if (onseg64 * H * 2 > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
-    const bool split = table || onps64 > 1;
-    const int64_t pre_units = table ? (ttot / oseg_len) * H : (onps64 - 1) * B * H;
-    const int rsub = split ? choose_rsub(oseg_len, pre_units) : 1;
-    const int sub_len = oseg_len / rsub;
-    const int64_t nps64 = T == 0 ? 1 : ((int64_t)T + sub_len - 1) / sub_len;
-    const int64_t nseg64 = !split ? 0 : table ? ttot / sub_len + B + 1 : (int64_t)B * nps64;
-    if (nseg64 * H > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
-
-    // Workspace: output-segment table, sub-segment tables, log-decays, states.
-    auto r256 = [](size_t b) { return (b + 255) / 256 * 256; };
-    const size_t osegs_b = table ? r256((size_t)onseg64 * sizeof(SegEntry)) : 0;
-    const size_t oseqs_b = table ? r256((size_t)B * sizeof(SeqEntry)) : 0;
-    const size_t segs_b = table ? r256((size_t)nseg64 * sizeof(SegEntry)) : 0;
-    const size_t seqs_b = table ? r256((size_t)B * sizeof(SeqEntry)) : 0;
-    const size_t gam_b = split ? r256((size_t)nseg64 * H * sizeof(float)) : 0;
-    const size_t buf_b = split ? (size_t)nseg64 * H * D * D * sizeof(float) : 0;
-    const size_t ws_b = osegs_b + oseqs_b + segs_b + seqs_b + gam_b + buf_b;
-    char *ws = nullptr;
     hipError_t e = hipSuccess;
-    if (ws_b) {
-        e = hipMallocAsync(reinterpret_cast<void **>(&ws), ws_b, st);
-        if (e != hipSuccess) return SGLA_ERR_HIP;
+    if (cu_seqlens && ws && getenv("SGLA_VALIDATE"))
+        e = launch_validate_cu(cu_seqlens, B, T, reinterpret_cast<int32_t *>(ws), st);
+    if (pl.halves) {
+        HalvesParams hp{};
+        hp.c = p;
+        hp.osegs = pl.table ? reinterpret_cast<SegEntry *>(at(pl.off_osegs)) : nullptr;
+        hp.onseg_max = (int)pl.onseg;
+        hp.onps = (int)pl.onps;
+        hp.oseg_len = pl.oseg_len;
+        if (e == hipSuccess && pl.table) {
+            e = launch_plan(cu_seqlens, B, T, pl.oseg_len, (int)pl.onseg,
+                            reinterpret_cast<SegEntry *>(at(pl.off_osegs)),
+                            reinterpret_cast<SeqEntry *>(at(pl.off_oseqs)), st);
+            if (e == hipSuccess)
+                e = launch_plan(cu_seqlens, B, T, pl.seg_len, (int)pl.nseg,
+                                reinterpret_cast<SegEntry *>(at(pl.off_segs)),
+                                reinterpret_cast<SeqEntry *>(at(pl.off_seqs)), st);
+        }
+        if (e == hipSuccess && pl.split) e = launch_chunk_mfma(p, /*phase_state=*/true, st);
+        if (e == hipSuccess && pl.split) e = launch_scan(p, 128, 128, st);
+        if (e == hipSuccess) e = launch_chunk_halves(hp, st);
+        return hip_status(e);
     }
-    char *wp = ws;
-    auto take = [&](size_t b) { char *r = b ? wp : nullptr; wp += b; return r; };
-    SegEntry *osegs = reinterpret_cast<SegEntry *>(take(osegs_b));
-    SeqEntry *oseqs = reinterpret_cast<SeqEntry *>(take(oseqs_b));
-    SegEntry *segs = reinterpret_cast<SegEntry *>(take(segs_b));
-    SeqEntry *seqs = reinterpret_cast<SeqEntry *>(take(seqs_b));
-    float *gam = reinterpret_cast<float *>(take(gam_b));
-    float *buf = reinterpret_cast<float *>(take(buf_b));
-
-    HalvesParams hp{};
-    ChunkParams &p = hp.c;
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.g = g;
-    p.s0 = initial_state;
-    p.out = out;
-    p.sfin = final_state;
-    p.buf = buf;
-    p.gam = gam;
-    p.segs = segs;
-    p.seqs = seqs;
-    p.H = H;
-    p.nseg_max = (int)nseg64;
-    p.N = B;
-    p.scale = scale;
-    p.T = T;
-    p.seg_len = sub_len;
-    p.nps = (int)nps64;
-    p.rsub = rsub;
-    hp.osegs = osegs;
-    hp.onseg_max = (int)onseg64;
-    hp.onps = (int)onps64;
-    hp.oseg_len = oseg_len;
-
-    if (table) {
-        e = launch_plan(cu_seqlens, B, T, oseg_len, (int)onseg64, osegs, oseqs, st);
-        if (e == hipSuccess) e = launch_plan(cu_seqlens, B, T, sub_len, (int)nseg64, segs, seqs, st);
-    }
-    if (e == hipSuccess && split) e = launch_chunk_mfma(p, /*phase_state=*/true, st);
-    if (e == hipSuccess && split) e = launch_scan(p, D, D, st);
-    if (e == hipSuccess) e = launch_chunk_halves(hp, st);
-    if (ws) {
-        const hipError_t ef = hipFreeAsync(ws, st);
-        if (e == hipSuccess) e = ef;
-    }
+    auto phase = [&](bool state_phase) {
+        return pl.mfma ? launch_chunk_mfma(p, state_phase, st)
+                       : launch_chunk_valu(p, bf16, Dk, Dv, state_phase, st);
+    };
+    if (e == hipSuccess && pl.table)
+        e = launch_plan(cu_seqlens, B, T, pl.seg_len, (int)pl.nseg,
+                        reinterpret_cast<SegEntry *>(at(pl.off_segs)),
+                        reinterpret_cast<SeqEntry *>(at(pl.off_seqs)), st);
+    if (e == hipSuccess && pl.split) e = phase(/*state_phase=*/true);
+    if (e == hipSuccess && pl.split) e = launch_scan(p, Dk, Dv, st);
+    if (e == hipSuccess) e = phase(/*state_phase=*/false);
     return hip_status(e);
 }
 
@@ -421,10 +456,42 @@ sgla_status sgla_out_norm_gate(const void *o, const void *z, const float *weight
                                            dtype == SGLA_BF16, static_cast<hipStream_t>(stream)));
 }
 
-sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
-                               const float *beta, const float *initial_state, void *out,
-                               float *final_state, const int64_t *cu_seqlens, int B, int T, int H,
-                               int Dk, int Dv, float scale, sgla_dtype dtype, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Workspace layout of the chunked gated delta rule: a 256-byte header, the
+// chunk tables (with cu_seqlens), then per (chunk, head) the W/U tile and the
+// new_v image.
+struct GdnPlan {
+    bool table = false;
+    int64_t nps = 1, nch = 0;
+    size_t off_segs = 0, off_seqs = 0, off_tiles = 0, off_nv = 0, bytes = 0;
+};
+
+sgla_status gdn_plan(int B, int T, int H, bool varlen, GdnPlan &pl) {
+    const int64_t ttot = varlen ? (int64_t)T : (int64_t)B * T;
+    pl.table = varlen;
+    pl.nps = T == 0 ? 1 : ((int64_t)T + kChunk - 1) / kChunk;
+    pl.nch = varlen ? ttot / kChunk + B + 1 : (int64_t)B * pl.nps;
+    if (pl.nch * H > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+    size_t off = kWsHeader;
+    if (pl.table) {
+        pl.off_segs = off; off += round256((size_t)pl.nch * sizeof(SegEntry));
+        pl.off_seqs = off; off += round256((size_t)B * sizeof(SeqEntry));
+    }
+    // Per chunk and head: W (64 x 128 bf16) and U (64 x 128 fp32), then
+    // new_v (64 x 128 bf16) for the output kernel.
+    pl.off_tiles = off; off += (size_t)pl.nch * H * kChunk * 128 * (sizeof(uint16_t) + sizeof(float));
+    pl.off_nv = off; off += (size_t)pl.nch * H * kChunk * 128 * sizeof(uint16_t);
+    pl.bytes = off;
+    return SGLA_OK;
+}
+
+sgla_status check_gdn_args(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *initial_state, const void *out,
+                           const float *final_state, const int64_t *cu_seqlens, int B, int T,
+                           int H, int Dk, int Dv, sgla_dtype dtype) {
     if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
     if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
     // The delta rule runs on the bf16 matrix-core kernels with 128-wide heads.
@@ -441,28 +508,27 @@ sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
         misaligned(beta, 4) || misaligned(out) || misaligned(initial_state) ||
         misaligned(final_state) || misaligned(cu_seqlens, 8))
         return SGLA_ERR_INVALID_ARG;
+    return SGLA_OK;
+}
+
+sgla_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, void *out,
+                          float *final_state, const int64_t *cu_seqlens, int B, int T, int H,
+                          int Dk, int Dv, float scale, sgla_dtype dtype, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    sgla_status stt = check_gdn_args(q, k, v, g, beta, initial_state, out, final_state, cu_seqlens,
+                                     B, T, H, Dk, Dv, dtype);
+    if (stt != SGLA_OK) return stt;
+    if (misaligned(workspace, 256)) return SGLA_ERR_INVALID_ARG;
+    const int64_t ttot = cu_seqlens ? (int64_t)T : (int64_t)B * T;
     if (B == 0) return SGLA_OK;
     if (ttot == 0 && !final_state) return SGLA_OK;
+    GdnPlan pl;
+    stt = gdn_plan(B, T, H, cu_seqlens != nullptr, pl);
+    if (stt != SGLA_OK) return stt;
+    if (!workspace || pl.bytes > workspace_bytes) return SGLA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
-
-    // One table row per chunk: without cu_seqlens the rows are arithmetic,
-    // with it the plan kernel lays them out on the device.
-    const bool table = cu_seqlens != nullptr;
-    const int64_t nps64 = T == 0 ? 1 : ((int64_t)T + kChunk - 1) / kChunk;
-    const int64_t nch64 = table ? ttot / kChunk + B + 1 : (int64_t)B * nps64;
-    if (nch64 * H > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
-    const int nch = (int)nch64;
-
-    const size_t segs_b = table ? (size_t)nch * sizeof(SegEntry) : 0;
-    const size_t seqs_b = table ? ((size_t)B * sizeof(SeqEntry) + 255) / 256 * 256 : 0;
-    // Per chunk and head: W (64 x 128 bf16) and U (64 x 128 fp32), then
-    // new_v (64 x 128 bf16) for the output kernel.
-    const size_t tiles_b = (size_t)nch * H * kChunk * 128 * (sizeof(uint16_t) + sizeof(float));
-    const size_t nv_b = (size_t)nch * H * kChunk * 128 * sizeof(uint16_t);
-    const size_t ws_b = segs_b + seqs_b + tiles_b + nv_b;
-    char *ws = nullptr;
-    hipError_t e = hipMallocAsync(reinterpret_cast<void **>(&ws), ws_b, st);
-    if (e != hipSuccess) return SGLA_ERR_HIP;
+    char *ws = static_cast<char *>(workspace);
 
     GdnParams p{};
     p.c.q = q;
@@ -472,25 +538,66 @@ sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, cons
     p.c.s0 = initial_state;
     p.c.out = out;
     p.c.sfin = final_state;
-    p.c.segs = table ? reinterpret_cast<SegEntry *>(ws) : nullptr;
-    p.c.seqs = table ? reinterpret_cast<SeqEntry *>(ws + segs_b) : nullptr;
+    p.c.segs = pl.table ? reinterpret_cast<SegEntry *>(ws + pl.off_segs) : nullptr;
+    p.c.seqs = pl.table ? reinterpret_cast<SeqEntry *>(ws + pl.off_seqs) : nullptr;
     p.c.H = H;
-    p.c.nseg_max = nch;
+    p.c.nseg_max = (int)pl.nch;
     p.c.N = B;
     p.c.scale = scale;
     p.c.T = T;
     p.c.seg_len = kChunk;
-    p.c.nps = (int)nps64;
+    p.c.nps = (int)pl.nps;
+    p.c.rsub = 1;
     p.beta = beta;
-    p.tiles = ws + segs_b + seqs_b;
-    p.nvimg = ws + segs_b + seqs_b + tiles_b;
-    if (table)
-        e = launch_plan(cu_seqlens, B, T, kChunk, nch, reinterpret_cast<SegEntry *>(ws),
-                        reinterpret_cast<SeqEntry *>(ws + segs_b), st);
+    p.tiles = ws + pl.off_tiles;
+    p.nvimg = ws + pl.off_nv;
+    hipError_t e = hipSuccess;
+    if (cu_seqlens && getenv("SGLA_VALIDATE"))
+        e = launch_validate_cu(cu_seqlens, B, T, reinterpret_cast<int32_t *>(ws), st);
+    if (e == hipSuccess && pl.table)
+        e = launch_plan(cu_seqlens, B, T, kChunk, (int)pl.nch,
+                        reinterpret_cast<SegEntry *>(ws + pl.off_segs),
+                        reinterpret_cast<SeqEntry *>(ws + pl.off_seqs), st);
     if (e == hipSuccess) e = launch_gdn_chunk(p, st);
-    const hipError_t ef = hipFreeAsync(ws, st);
-    if (e == hipSuccess) e = ef;
     return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+sgla_status sgla_gdn_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                              sgla_dtype dtype, int varlen, size_t *bytes) {
+    if (!bytes) return SGLA_ERR_INVALID_ARG;
+    *bytes = 0;
+    sgla_status st = check_gdn_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                    nullptr, nullptr, B, 0, H, Dk, Dv, dtype);
+    if (st != SGLA_OK) return st;
+    if (T < 0) return SGLA_ERR_INVALID_ARG;
+    const int64_t ttot = varlen ? (int64_t)T : (int64_t)B * T;
+    if (ttot > ((int64_t)1 << 62) / ((int64_t)H * 128)) return SGLA_ERR_INVALID_ARG;
+    if (B == 0) return SGLA_OK;
+    GdnPlan pl;
+    st = gdn_plan(B, T, H, varlen != 0, pl);
+    if (st == SGLA_OK) *bytes = pl.bytes;
+    return st;
+}
+
+sgla_status sgla_gdn_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, const float *initial_state, void *out,
+                                  float *final_state, const int64_t *cu_seqlens, int B, int T,
+                                  int H, int Dk, int Dv, float scale, sgla_dtype dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    return gdn_chunk_fwd(q, k, v, g, beta, initial_state, out, final_state, cu_seqlens, B, T, H,
+                         Dk, Dv, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+sgla_status sgla_gdn_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *initial_state, void *out,
+                               float *final_state, const int64_t *cu_seqlens, int B, int T, int H,
+                               int Dk, int Dv, float scale, sgla_dtype dtype, void *stream) {
+    return gdn_chunk_fwd(q, k, v, g, beta, initial_state, out, final_state, cu_seqlens, B, T, H,
+                         Dk, Dv, scale, dtype, nullptr, 0, stream);
 }
 
 sgla_status sgla_gdn_recurrent_step(const void *q, const void *k, const void *v, const float *g,

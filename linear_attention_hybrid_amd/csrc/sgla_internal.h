@@ -37,8 +37,11 @@ struct ChunkParams {
     float *sfin;          // [N,H,Dk,Dv] or nullptr
     float *buf;           // [nseg_max,H,Dk,Dv]: segment states, then carried-in states
     float *gam;           // [nseg_max,H]: total log-decay of each segment
-    const SegEntry *segs;  // [nseg_max], or nullptr for B equal rows (see seg_at)
+    const SegEntry *segs;  // [nseg_max], or nullptr: arithmetic segments (see seg_at)
     const SeqEntry *seqs;  // [N], or nullptr likewise
+    // Packed sequences without a table: one segment per sequence, read from
+    // the offsets (segs == nullptr; nps == 1; T is the packed total).
+    const int64_t *cu;
     int H;
     int nseg_max;
     int N;
@@ -71,10 +74,29 @@ struct HalvesParams {
     int oseg_len;           // tokens per output segment (a multiple of the chunk size)
 };
 
-// Segment s of the call. Without a table (no cu_seqlens) every sequence has
-// the same T tokens and nps segments, so the entry is arithmetic.
+// Sequence n of a packed call as one segment, straight from the offsets;
+// offsets that break the documented rule are clamped into [0, T].
+__device__ __forceinline__ SegEntry seg_from_cu(const int64_t *cu, int n, int T) {
+    int64_t a = cu[n], b = cu[n + 1];
+    a = a < 0 ? 0 : (a > T ? T : a);
+    b = b < a ? a : (b > T ? T : b);
+    SegEntry e;
+    e.tok0 = a;
+    e.len = (int32_t)(b - a);
+    e.seq = n;
+    e.p = 0;
+    e.nseg = 1;
+    e.pad0 = 0;
+    e.pad1 = 0;
+    return e;
+}
+
+// Segment s of the call. Without a table every sequence has the same T
+// tokens and nps segments, so the entry is arithmetic (or, for packed
+// sequences, the whole sequence s).
 __device__ __forceinline__ SegEntry seg_at(const ChunkParams &p, int s) {
     if (p.segs) return p.segs[s];
+    if (p.cu) return seg_from_cu(p.cu, s, p.T);
     SegEntry e;
     const int n = s / p.nps;
     const int j = s - n * p.nps;
@@ -91,6 +113,7 @@ __device__ __forceinline__ SegEntry seg_at(const ChunkParams &p, int s) {
 
 __device__ __forceinline__ SeqEntry seq_at(const ChunkParams &p, int n) {
     if (p.seqs) return p.seqs[n];
+    if (p.cu) return SeqEntry{n, 1};
     SeqEntry e;
     e.first = n * p.nps;
     e.nseg = p.nps;
@@ -157,6 +180,9 @@ struct GdnParams {
 hipError_t launch_plan(const int64_t *cu, int B, int T, int seg_len, int nseg_max,
                        SegEntry *segs, SeqEntry *seqs, hipStream_t st);
 hipError_t launch_scan(const ChunkParams &p, int Dk, int Dv, hipStream_t st);
+// Writes to *status the bits of the rules cu_seqlens breaks (0: none):
+// 1 cu[0] != 0, 2 some cu[i] > cu[i+1], 4 cu[B] != T.
+hipError_t launch_validate_cu(const int64_t *cu, int B, int T, int32_t *status, hipStream_t st);
 hipError_t launch_chunk_valu(const ChunkParams &p, bool bf16, int Dk, int Dv, bool phase_state,
                              hipStream_t st);
 hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t st);

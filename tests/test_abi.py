@@ -251,3 +251,63 @@ def test_gdn_pointer_checks(lib):
     assert gdn_step(lib, N=1, beta=None) == 1
     assert gdn_step(lib, N=1, beta=A + 2) == 1
     assert gdn_step(lib, N=1, state=A + 4) == 1
+
+
+def chunk_ex(lib, q=A, k=A, v=A, g=A, s0=None, out=A, sf=None, cu=None, qw=None, kw=None,
+             pos=None, theta=0.0, eps=0.0, B=0, T=0, H=1, Dk=64, Dv=64, scale=1.0, dtype=0,
+             ws=None, wsb=0):
+    return lib.sgla_chunk_fwd_ex(q, k, v, g, s0, out, sf, cu, qw, kw, pos, theta, eps, B, T, H,
+                                 Dk, Dv, scale, dtype, ws, wsb, None)
+
+
+def ws_size(lib, B, T, H, Dk, Dv, dtype, varlen=0, prologue=0, gdn=False):
+    n = ctypes.c_size_t(12345)
+    if gdn:
+        st = lib.sgla_gdn_chunk_fwd_workspace_size(B, T, H, Dk, Dv, dtype, varlen, ctypes.byref(n))
+    else:
+        st = lib.sgla_chunk_fwd_workspace_size(B, T, H, Dk, Dv, dtype, varlen, prologue,
+                                               ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_queries(lib):
+    # Sequences short enough to be one segment need no workspace.
+    assert ws_size(lib, 4, 256, 8, 128, 128, 1) == (0, 0)
+    assert ws_size(lib, 0, 8192, 32, 128, 128, 1) == (0, 0)
+    # The lightning prefill shape splits: states, log-decays and a header.
+    st, n = ws_size(lib, 1, 8192, 32, 128, 128, 1)
+    assert st == 0 and n > 32 * 128 * 128 * 4 and n % 256 == 0
+    # A bound over every cu_seqlens is at least the equal-length size of the
+    # same total, and it grows with T.
+    assert ws_size(lib, 1, 8192, 32, 128, 128, 1, varlen=1)[1] >= n
+    assert ws_size(lib, 1, 65536, 32, 128, 128, 1)[1] >= n
+    # fp32, the prologue and 64-wide heads take the one-level kernels.
+    assert ws_size(lib, 1, 8192, 4, 64, 64, 0)[0] == 0
+    assert ws_size(lib, 1, 8192, 32, 128, 128, 1, prologue=1)[0] == 0
+    # Errors: bad dtype, unsupported sizes, the prologue outside bf16 / 128, no output.
+    assert ws_size(lib, 1, 64, 1, 128, 128, 7)[0] == 1
+    assert ws_size(lib, 1, 64, 1, 96, 128, 1)[0] == 2
+    assert ws_size(lib, 1, 64, 1, 128, 128, 0, prologue=1)[0] == 2
+    assert ws_size(lib, -1, 64, 1, 128, 128, 1)[0] == 1
+    assert lib.sgla_chunk_fwd_workspace_size(1, 64, 1, 128, 128, 1, 0, 0, None) == 1
+    # The gated delta rule keeps 64 KiB per chunk and head, plus the header.
+    st, n = ws_size(lib, 2, 100, 3, 128, 128, 1, gdn=True)
+    assert st == 0 and n == 256 + 2 * 2 * 3 * 65536
+    assert ws_size(lib, 2, 100, 3, 128, 128, 0, gdn=True)[0] == 2
+    assert ws_size(lib, 0, 100, 3, 128, 128, 1, gdn=True) == (0, 0)
+
+
+def test_workspace_checks_before_any_launch(lib):
+    big = dict(B=1, T=8192, H=32, Dk=128, Dv=128, dtype=1)
+    n = ws_size(lib, 1, 8192, 32, 128, 128, 1)[1]
+    assert chunk_ex(lib, ws=A, wsb=n - 1, **big) == 4        # too small: SGLA_ERR_WORKSPACE
+    assert chunk_ex(lib, ws=A + 128, wsb=n, **big) == 1      # not 256-byte aligned
+    assert sgla.status_string(4) == "SGLA_ERR_WORKSPACE"
+    # The plain GDN entry point has no workspace: with tokens it says so.
+    assert gdn_chunk(lib, B=1, T=64, H=1) == 4
+    assert lib.sgla_gdn_chunk_fwd_ex(A, A, A, A, A, None, A, None, None, 1, 64, 1, 128, 128, 1.0,
+                                     1, A, 1024, None) == 4
+    # The offsets check needs its pointers.
+    assert lib.sgla_validate_cu_seqlens(None, 2, 10, A, None) == 1
+    assert lib.sgla_validate_cu_seqlens(A, 2, 10, None, None) == 1
+    assert lib.sgla_validate_cu_seqlens(A + 4, 2, 10, A, None) == 1

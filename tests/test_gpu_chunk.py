@@ -294,3 +294,69 @@ def test_vector_alu_path_for_bf16_128(T):
     finally:
         os.environ.pop("SGLA_FORCE_VALU", None)
     compare(inp, o, S, "bf16", "forced VALU T=%d" % T)
+
+
+@pytest.mark.parametrize("dtype,dk,varlen", [("bf16", 128, False), ("bf16", 128, True),
+                                              ("f32", 64, False), ("f32", 64, True)])
+def test_without_workspace_one_segment_per_sequence(dtype, dk, varlen):
+    """sgla_chunk_fwd (no workspace): every sequence is one segment, packed
+    sequences read straight from cu_seqlens; same results as the oracle."""
+    say("chunk_fwd without workspace", dtype, dk, "varlen" if varlen else "B=2")
+    if varlen:
+        lengths = [0, 70, 1, 300, 64]
+        cu = W.cu_from_lengths(lengths)
+        inp = W.make_prefill(1, int(cu[-1]), 3, dk, dk, dtype, "lightning", seed=21,
+                             device="cuda", cu_seqlens=cu, init="normal")
+        starts = [int(c) for c in cu[:-1]]
+    else:
+        inp = W.make_prefill(2, 700, 3, dk, dk, dtype, "lightning", seed=22, device="cuda",
+                             init="normal")
+        starts = [0]
+    o, S = sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["initial_state"],
+                          inp["cu_seqlens"], inp["scale"], workspace=None)
+    torch.cuda.synchronize()
+    compare(inp, o, S, dtype, "no workspace", starts=starts)
+
+
+def test_explicit_workspace_tensor_and_reuse():
+    say("chunk_fwd explicit workspace B=1 T=3000 H=4")
+    inp = W.make_prefill(1, 3000, 4, 128, 128, "bf16", "lightning", seed=23, device="cuda",
+                         init="normal")
+    set_segments(1024, 2)
+    n = sgla.chunk_workspace_size(1, 3000, 4, 128, 128, torch.bfloat16)
+    assert n > 0
+    ws = torch.full((n,), 0xAB, dtype=torch.uint8, device="cuda")
+    o1, S1 = sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["initial_state"],
+                            scale=inp["scale"], workspace=ws)
+    o2, S2 = sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["initial_state"],
+                            scale=inp["scale"], workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    compare(inp, o1, S1, "bf16", "explicit workspace", starts=[0, 1024, 2048])
+    with pytest.raises(sgla.SglaError):
+        sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], workspace=ws[: n - 256])
+
+
+def test_validate_cu_seqlens():
+    say("validate_cu_seqlens")
+    good = torch.tensor([0, 3, 3, 10], dtype=torch.int64, device="cuda")
+    assert sgla.validate_cu_seqlens(good, 10) == 0
+    assert sgla.validate_cu_seqlens(good, 11) == 4
+    assert sgla.validate_cu_seqlens(torch.tensor([1, 3, 2, 10], dtype=torch.int64,
+                                                 device="cuda"), 10) == 3
+    big = torch.arange(0, 5001, dtype=torch.int64, device="cuda")
+    big[2500] = 9999
+    assert sgla.validate_cu_seqlens(big, 5000) == 2
+    # The check lands in word 0 of the workspace when SGLA_VALIDATE is set.
+    inp = W.make_prefill(1, 300, 2, 128, 128, "bf16", "lightning", seed=24, device="cuda",
+                         cu_seqlens=W.cu_from_lengths([100, 200]), init="normal")
+    os.environ["SGLA_VALIDATE"] = "1"
+    try:
+        n = sgla.chunk_workspace_size(2, 300, 2, 128, 128, torch.bfloat16, varlen=True)
+        ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+        sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], cu_seqlens=inp["cu_seqlens"],
+                       workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 0
+    finally:
+        os.environ.pop("SGLA_VALIDATE", None)
