@@ -166,6 +166,28 @@ sgla_status sgla_chunk_fwd_ex(const void *q, const void *k, const void *v, const
                               void *stream);
 
 /*
+ * sgla_chunk_fwd_noalloc — for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): sgla_chunk_fwd_ex's split plan, with a scratch array the
+ * library holds on each GPU in place of the caller's workspace. Arguments and
+ * results as sgla_chunk_fwd (no prologue). It calls no allocator.
+ *
+ * The scratch holds at most 64 MiB per GPU (enough for the split plan of
+ * B = 1, H = 32, Dk = Dv = 128 up to T = 65536); a call whose plan
+ * (sgla_chunk_fwd_workspace_size) needs more returns SGLA_ERR_WORKSPACE
+ * without enqueuing anything. The array is part of the library's device code
+ * and is held on every GPU the library runs on until the process ends; the
+ * first call on a GPU looks up its address there, with that GPU current.
+ * Every call on one GPU uses the same array: calls that overlap in time on
+ * one GPU (other streams, other host threads) race and must be serialised by
+ * the caller. Nothing in it needs clearing between calls.
+ */
+sgla_status sgla_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                   const float *initial_state, void *out, float *final_state,
+                                   const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv,
+                                   float scale, sgla_dtype dtype, void *stream);
+
+/*
  * sgla_validate_cu_seqlens — checks packed-sequence offsets on the device
  * (the rules under sgla_chunk_fwd: cu[0] = 0, non-decreasing, cu[B] = T) and
  * writes to *status (device int32, 4-byte aligned) the sum of the rules

@@ -97,6 +97,9 @@ def library():
         lib.sgla_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, cf, cf, ci,
                                           ci, ci, ci, ci, cf, ci, vp, ctypes.c_size_t, vp]
         lib.sgla_chunk_fwd_ex.restype = ci
+        lib.sgla_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
+                                               cf, ci, vp]
+        lib.sgla_chunk_fwd_noalloc.restype = ci
         lib.sgla_validate_cu_seqlens.argtypes = [vp, ci, ci, vp, vp]
         lib.sgla_validate_cu_seqlens.restype = ci
         lib.sgla_gdn_chunk_fwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, zp]

@@ -2,6 +2,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/sgla.h"
 #include "sgla_internal.h"
 
@@ -378,6 +380,33 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
     return hip_status(e);
 }
 
+// Scratch space of sgla_chunk_fwd_noalloc: one array per GPU, in the code
+// object's device memory, held until the process ends. Host code must not use
+// the array's name as an address (it names a host-side stand-in): the device
+// address of each GPU's copy comes from hipGetSymbolAddress, once per device,
+// with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::once_flag scratch_once[kMaxDevices];
+void *scratch_ptr[kMaxDevices];
+hipError_t scratch_err[kMaxDevices];
+
+hipError_t scratch_of_current_device(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(scratch_once[dev], [dev] {
+        void *p = nullptr;
+        scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        scratch_ptr[dev] = p;
+    });
+    if (scratch_err[dev] != hipSuccess) return scratch_err[dev];
+    *out = scratch_ptr[dev];
+    return hipSuccess;
+}
+
 sgla_status recurrent_step(const void *q, const void *k, const void *v, const float *g,
                            void *state, sgla_dtype state_dtype, const int32_t *state_indices,
                            void *out, int N, int H, int Dk, int Dv, float scale, sgla_dtype dtype,
@@ -409,6 +438,19 @@ sgla_status recurrent_step(const void *q, const void *k, const void *v, const fl
 }  // namespace
 
 extern "C" {
+
+sgla_status sgla_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                   const float *initial_state, void *out, float *final_state,
+                                   const int64_t *cu_seqlens, int B, int T, int H, int Dk, int Dv,
+                                   float scale, sgla_dtype dtype, void *stream) {
+    const sgla_status st = check_chunk_args(q, k, v, g, initial_state, out, final_state,
+                                            cu_seqlens, B, T, H, Dk, Dv, dtype, nullptr);
+    if (st != SGLA_OK) return st;
+    void *ws = nullptr;
+    if (scratch_of_current_device(&ws) != hipSuccess) return SGLA_ERR_HIP;
+    return chunk_fwd(q, k, v, g, initial_state, out, final_state, cu_seqlens, B, T, H, Dk, Dv,
+                     scale, dtype, stream, nullptr, ws, kScratchBytes);
+}
 
 sgla_status sgla_recurrent_step(const void *q, const void *k, const void *v, const float *g,
                                 float *state, const int32_t *state_indices, void *out, int N,
