@@ -2,15 +2,21 @@
 """Benchmark of the Simple GLA hot path on one MI355X.
 
 One step = one chunked prefill of a lightning layer (B=1, H=32, T=8192,
-Dk=Dv=128, bf16 in, fp32 state out) through ``sgla_chunk_fwd``. K timed steps
-run back to back after W warm-up steps, bracketed by device synchronisation;
-``value`` is prefill tokens/s. Each call is also bracketed by HIP events on the
-stream it runs on, which gives the per-call duration used for the roofline.
+Dk=Dv=128, bf16 in, fp32 state out) through ``sgla_chunk_fwd_ex`` with a
+caller workspace. The headline times each of K calls on its own, after a pass
+that reads a 1 GiB buffer so that q, k, v come from HBM and not from the
+memory-side cache (read, not written: a written buffer would leave dirty lines
+whose write-back lands inside the timed call); ``value`` is prefill tokens/s
+over those calls. The same calls back to back are reported in
+``back_to_back``.
 
-The fused decode step (256 sequences x 32 heads, Dk=Dv=128, fp32 state in HBM,
-64 successive steps) is timed the same way and reported in ``decode``.
-``prologue`` reports both again through the entry points that take q and k
-before the per-head RMSNorm and RoPE and apply them as the tiles load.
+Also reported, each with its own roofline object: a stream copy on the same
+GPU (``stream_copy``), the 65,536-token continuation with an initial state and
+its split at 32,768 as two chained calls (``long``), the 524,288-token packed
+varlen prefill (``varlen``), the fused decode step (256 sequences x 32 heads,
+64 successive steps, ``decode``), a cache-resident prefill that measures the
+kernels' compute rate (``mfma.cache_resident``), and the prologue, bf16-state,
+epilogue and gated-delta-rule entry points.
 
 ``cpu_baseline`` times the oracle (plain C, fp64, OpenMP over (sequence, head)
 units) on the same prefill workload on the host cores.
@@ -40,6 +46,8 @@ BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
+LONG = "prefill_bf16_h32_t65536_d128_cont"
+VARLEN = "varlen_bf16_h32_d128_8seq_512k"
 PREFILL_PRO = PREFILL + "+qk_norm_rope"
 DECODE_PRO = DECODE + "+qk_norm_rope"
 DECODE_BF16 = DECODE + "+bf16_state"
@@ -48,10 +56,12 @@ GDN_PREFILL = "gdn_prefill_bf16_h32_t8192_d128"
 GDN_DECODE = "gdn_decode_bf16_n256_h32_d128_x64"
 # The kernels of one call of each workload, as rocprofv3 names them.
 CALL_KERNELS = {
-    PREFILL: ["chunk_mfma_kernel<true, false>", "scan_kernel<128, 128>",
-              "chunk_mfma_kernel<false, false>"],
+    PREFILL: ["chunk_mfma_kernel<true, false>", "scan_kernel<128, 128>", "chunk_halves_kernel"],
     PREFILL_PRO: ["chunk_mfma_kernel<true, true>", "scan_kernel<128, 128>",
                   "chunk_mfma_kernel<false, true>"],
+    LONG: ["chunk_mfma_kernel<true, false>", "scan_kernel<128, 128>", "chunk_halves_kernel"],
+    VARLEN: ["plan_kernel", "chunk_mfma_kernel<true, false>", "scan_kernel<128, 128>",
+             "chunk_mfma_kernel<false, false>"],
     DECODE: ["recurrent_step_kernel<unsigned short, 128, 128, false, float>"],
     DECODE_PRO: ["recurrent_step_kernel<unsigned short, 128, 128, true, float>"],
     DECODE_BF16: ["recurrent_step_kernel<unsigned short, 128, 128, false, unsigned short>"],
@@ -64,7 +74,9 @@ CALL_KERNELS = {
 # The sources each workload's kernels are built from, besides the shared ones
 # (headers, the host code that picks launch shapes, the build flags).
 WORKLOAD_SOURCES = {
-    PREFILL: ["chunk_mfma.hip", "chunk_plan.hip"],
+    PREFILL: ["chunk_mfma.hip", "chunk_plan.hip", "chunk_halves.hip"],
+    LONG: ["chunk_mfma.hip", "chunk_plan.hip", "chunk_halves.hip"],
+    VARLEN: ["chunk_mfma.hip", "chunk_plan.hip"],
     PREFILL_PRO: ["chunk_mfma.hip", "chunk_plan.hip"],
     DECODE: ["recurrent_step.hip"],
     DECODE_PRO: ["recurrent_step.hip"],
@@ -102,6 +114,24 @@ def recorded_traffic(workload):
     return entry.get("bytes_per_call")
 
 
+MFMA_RECORD = os.path.join(ROOT, "profiles", "mfma.json")
+
+
+def recorded_mfma(workload):
+    """Matrix-core busy fraction per kernel of one call, from the committed
+    counter record (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE cycles of
+    every SIMD), or None when there is none or the kernels changed since."""
+    try:
+        with open(MFMA_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("source_hash") != kernel_source_hash(workload):
+        return None
+    return entry.get("kernels")
+
+
 def copy_calibration(torch, dev, nbytes=256 << 20, reps=3):
     """An elementwise pass of known size (fp32 negation: nbytes read, nbytes
     written, kernel name containing ``neg_kernel``), so FETCH_SIZE/WRITE_SIZE
@@ -136,7 +166,15 @@ def _per_kernel_avg(rows):
     return {name: sum(v) / len(v) for name, v in acc.items()}
 
 
-def record_traffic(fetch_dir, write_dir, calib_bytes=256 << 20):
+def _load_record(path):
+    try:
+        with open(path) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return {}
+
+
+def record_traffic(fetch_dir, write_dir, workloads=None, calib_bytes=256 << 20):
     """Turn a FETCH_SIZE run and a WRITE_SIZE run of
     ``bench.py --copy-calibration`` into HBM bytes per call.
 
@@ -144,7 +182,9 @@ def record_traffic(fetch_dir, write_dir, calib_bytes=256 << 20):
     for the fp32 negation pass of known size (calib_bytes read and written),
     averaged per kernel, and summed over the kernels of one call of each
     workload (CALL_KERNELS). Writes profiles/traffic.json keyed by workload,
-    with the hash of the kernel sources the counters were taken on."""
+    with the hash of the kernel sources the counters were taken on; with
+    ``workloads`` only those entries are replaced (the runs then hold only
+    their kernels: several workloads share kernel names)."""
     fetch_rows = _counter_rows(fetch_dir, "FETCH_SIZE")
     write_rows = _counter_rows(write_dir, "WRITE_SIZE")
 
@@ -166,9 +206,12 @@ def record_traffic(fetch_dir, write_dir, calib_bytes=256 << 20):
         names = [n for n in table if pattern in n]
         return names[0] if len(names) == 1 else None
 
-    rec = {"_calibration": {"fetch_scale": f_scale, "write_scale": w_scale,
-                            "pass": "fp32 negation, %d bytes read and written" % calib_bytes}}
+    rec = _load_record(TRAFFIC_RECORD)
+    rec["_calibration"] = {"fetch_scale": f_scale, "write_scale": w_scale,
+                           "pass": "fp32 negation, %d bytes read and written" % calib_bytes}
     for wl, parts in CALL_KERNELS.items():
+        if workloads and wl not in workloads:
+            continue
         kern = {}
         for pat in parts:
             nf, nw = find(pat, fetch), find(pat, write)
@@ -181,6 +224,42 @@ def record_traffic(fetch_dir, write_dir, calib_bytes=256 << 20):
                        "bytes_per_call": sum(v["fetch"] + v["write"] for v in kern.values())}
     os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
     with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec, indent=1, sort_keys=True))
+    return 0
+
+
+def record_mfma(pmc_dir, workloads=None, xcds=8, simds=1024):
+    """Matrix-core busy fraction of each kernel of a call, from a rocprofv3
+    --pmc run with SQ_VALU_MFMA_BUSY_CYCLES (busy cycles summed over every
+    SIMD) and GRBM_GUI_ACTIVE (active cycles summed over the XCDs):
+    busy / (active / xcds * simds). Writes profiles/mfma.json keyed by
+    workload, with the hash of the kernel sources the counters were taken on."""
+    busy = _per_kernel_avg(_counter_rows(pmc_dir, "SQ_VALU_MFMA_BUSY_CYCLES"))
+    active = _per_kernel_avg(_counter_rows(pmc_dir, "GRBM_GUI_ACTIVE"))
+
+    def find(pattern):
+        names = [n for n in busy if pattern in n and n in active]
+        return names[0] if len(names) == 1 else None
+
+    rec = _load_record(MFMA_RECORD)
+    rec["_formula"] = ("SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d XCDs * %d SIMDs)"
+                       % (xcds, simds))
+    for wl, parts in CALL_KERNELS.items():
+        if workloads and wl not in workloads:
+            continue
+        kern = {}
+        for pat in parts:
+            n = find(pat)
+            if n is None:
+                kern = None
+                break
+            kern[pat] = busy[n] / (active[n] / xcds * simds) if active[n] else 0.0
+        if kern:
+            rec[wl] = {"source_hash": kernel_source_hash(wl), "kernels": kern}
+    os.makedirs(os.path.dirname(MFMA_RECORD), exist_ok=True)
+    with open(MFMA_RECORD, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
     print(json.dumps(rec, indent=1, sort_keys=True))
@@ -240,13 +319,16 @@ def time_calls(fn, steps, warmup, torch, single_reps=20):
 
 
 def time_flushed(fn, reps, torch, dev, flush_bytes=1 << 30):
-    """Per-call times with the caches emptied before each call: a 1 GiB
-    buffer is overwritten between calls (outside the timed events), so the
-    call's inputs come from HBM rather than the 256 MB memory-side cache."""
-    flush = torch.empty(flush_bytes // 4, dtype=torch.float32, device=dev)
+    """Per-call times with the caches emptied before each call: a 1 GiB buffer
+    is read (summed) between calls, outside the timed events, so the call's
+    inputs come from HBM rather than the 256 MB memory-side cache. Reading
+    leaves the cache full of clean lines; overwriting the buffer instead would
+    leave dirty lines, and their write-back during the timed call made every
+    kernel measured that way two to three times slower."""
+    flush = torch.ones(flush_bytes // 4, dtype=torch.float32, device=dev)
     per = []
     for _ in range(reps):
-        flush.fill_(1.0)
+        sink = flush.sum()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -254,8 +336,30 @@ def time_flushed(fn, reps, torch, dev, flush_bytes=1 << 30):
         b.record()
         torch.cuda.synchronize()
         per.append(a.elapsed_time(b))
-    del flush
+    del flush, sink
     return per
+
+
+def stream_copy(torch, dev, nbytes=1 << 30, reps=20):
+    """A 1 GiB -> 1 GiB fp32 copy (torch's copy kernel), back to back: the
+    HBM rate a plain stream reaches on this GPU (2 * nbytes per copy)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    return {"bytes_per_copy": 2 * nbytes, "ms": ms, "GBs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS,
+            "kernel": "torch copy_ of 1 GiB fp32, back to back"}
 
 
 def median(xs):
@@ -295,24 +399,34 @@ def cpu_baseline(inp, W, min_seconds=10.0, max_reps=500):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50,
+                    help="timed prefill calls (each after a cache flush; also back to back)")
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-passes", type=int, default=3,
                     help="timed passes of 64 decode steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "prologue", "epilogue",
-                                       "bf16-state", "gdn"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "long", "varlen", "decode", "prologue",
+                                       "epilogue", "bf16-state", "gdn"], default="all")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB elementwise pass (for counter calibration)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: write profiles/traffic.json from two rocprofv3 --pmc "
                          "runs (FETCH_SIZE, WRITE_SIZE) of this script with --copy-calibration")
-    ap.add_argument("--flushed-reps", type=int, default=20,
-                    help="calls timed one by one after a cache flush (0: skip)")
+    ap.add_argument("--workloads", nargs="+", metavar="W",
+                    help="with --record-traffic / --record-mfma: the workloads the runs hold")
+    ap.add_argument("--no-b2b", action="store_true",
+                    help="time the prefill only after cache flushes (profiler runs)")
+    ap.add_argument("--record-mfma", metavar="PMC_DIR",
+                    help="no GPU work: write profiles/mfma.json from a rocprofv3 --pmc run with "
+                         "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE")
+    ap.add_argument("--long-steps", type=int, default=5,
+                    help="timed calls of the 65,536-token and the packed varlen workloads")
     args = ap.parse_args()
     if args.record_traffic:
-        return record_traffic(*args.record_traffic)
+        return record_traffic(*args.record_traffic, workloads=args.workloads)
+    if args.record_mfma:
+        return record_mfma(args.record_mfma, workloads=args.workloads)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d (WORLD_SIZE %d) is not "
@@ -333,56 +447,89 @@ def main():
     props = torch.cuda.get_device_properties(dev)
     result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-              "data": "synthetic (seeded; q,k unit-RMS + RoPE, v ~ N(0,1), g = log sigmoid(N(4,1)))"}
+              "data": "synthetic (seeded; q,k rows N(0,1) scaled to unit RMS, isotropic, so the "
+                      "RoPE rotation would leave their distribution unchanged and is not applied; "
+                      "v ~ N(0,1); g = log sigmoid(N(4,1)))"}
 
     if args.only in ("all", "prefill"):
+        result["stream_copy"] = stream_copy(torch, dev)
         inp = W.make_workload(PREFILL, seed=args.seed, device=dev)
         B, T, H, Dk = inp["q"].shape
         Dv = inp["v"].shape[-1]
         out = torch.empty_like(inp["v"])
         fs = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(1, sgla.chunk_workspace_size(B, T, H, Dk, Dv)), dtype=torch.uint8,
+                         device=dev)
 
         def step():
             sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], None, None, inp["scale"],
-                           out=out, final_state=fs)
+                           out=out, final_state=fs, workspace=ws)
 
-        wall, region, per = time_calls(step, args.steps, args.warmup, torch)
-        ms_step = region / args.steps
-        per_avg = ms_step
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fl = time_flushed(step, args.steps, torch, dev)
+        wall = time.perf_counter() - t0
+        ms_step = sum(fl) / len(fl)
+        if args.no_b2b:
+            region, per = float("nan"), [float("nan")]
+        else:
+            _, region, per = time_calls(step, args.steps, 0, torch)
+        b2b = region / args.steps
         nbytes = prefill_bytes(B, T, H, Dk, Dv)
         flops = prefill_flops(B, T, H, Dk, Dv)
-        achieved = nbytes / (per_avg * 1e-3) / 1e9
+        achieved = nbytes / (ms_step * 1e-3) / 1e9
+        copy_gbs = result["stream_copy"]["GBs"]
         result.update({
             "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "ms_per_step": ms_step,
             "config": {"workload": PREFILL, "B": B, "T": T, "H": H, "Dk": Dk, "Dv": Dv,
                        "chunk": 64, "scale": inp["scale"], "initial_state": "zero",
-                       "final_state": "fp32", "gpu": props.name},
+                       "final_state": "fp32", "timing": "each call after a 1 GiB read pass",
+                       "gpu": props.name},
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "frac_of_stream_copy": achieved / copy_gbs,
                          "traffic": recorded_traffic(PREFILL),
-                         "kernel": "sgla_chunk_fwd (whole call: plan, segment-state, scan and "
-                                   "output kernels)",
+                         "kernel": "sgla_chunk_fwd_ex (whole call: segment-state, scan and "
+                                   "value-half output kernels)",
                          "algorithmic_bytes_per_launch": nbytes,
-                         "avg_launch_ms": per_avg},
-            "mfma": {"useful_tflops": flops / (per_avg * 1e-3) / 1e12,
-                     "useful_frac_of_bf16_peak": flops / (per_avg * 1e-3) / 1e12 /
+                         "avg_launch_ms": ms_step},
+            "mfma": {"useful_tflops": flops / (ms_step * 1e-3) / 1e12,
+                     "useful_frac_of_bf16_peak": flops / (ms_step * 1e-3) / 1e12 /
                      BF16_DENSE_PEAK_TFLOPS,
-                     "dense_tile_flops_per_launch": flops},
+                     "dense_tile_flops_per_launch": flops,
+                     "busy": recorded_mfma(PREFILL)},
             "wall_s_timed": wall,
-            "per_call_ms": {"mean": per_avg, "median_single": median(per), "min_single": min(per)},
+            "per_call_ms": {"mean": ms_step, "median": median(fl), "min": min(fl),
+                            "max": max(fl)},
+            "back_to_back": {"note": "the same calls with no flush between them; q, k, v then "
+                                     "stay partly in the 256 MB memory-side cache",
+                             "ms_per_call": b2b, "tokens_per_s": B * T / (b2b * 1e-3),
+                             "achieved_GBs": nbytes / (b2b * 1e-3) / 1e9,
+                             "frac": nbytes / (b2b * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "median_single": median(per), "min_single": min(per)},
         })
-        if args.flushed_reps > 0:
-            fl = time_flushed(step, args.flushed_reps, torch, dev)
-            result["flushed"] = {
-                "note": "each call after a 1 GiB overwrite; inputs read from HBM",
-                "reps": len(fl), "median_ms": median(fl), "min_ms": min(fl),
-                "tokens_per_s": B * T / (median(fl) * 1e-3),
-                "achieved_GBs": nbytes / (median(fl) * 1e-3) / 1e9,
-                "frac": nbytes / (median(fl) * 1e-3) / 1e9 / HBM_PEAK_GBS}
         if not args.no_cpu:
             result["cpu_baseline"] = cpu_baseline(inp, W)
-        del inp, out, fs
+        del inp, out, fs, ws
         torch.cuda.empty_cache()
+        if args.only == "all":
+            result["mfma"]["cache_resident"] = bench_cache_resident(args, torch, sgla, W, dev)
+    if args.only in ("all", "long"):
+        result["long"] = bench_long(args, torch, sgla, W, dev)
+        if args.only == "long":
+            e = result["long"]
+            result.update({"value": e["tokens_per_s"], "unit": "tokens/s",
+                           "ms_per_step": e["ms_per_call"], "config": {"workload": LONG},
+                           "roofline": e["roofline"]})
+    if args.only in ("all", "varlen"):
+        result["varlen"] = bench_varlen(args, torch, sgla, W, dev)
+        if args.only == "varlen":
+            e = result["varlen"]
+            result.update({"value": e["tokens_per_s"], "unit": "tokens/s",
+                           "ms_per_step": e["ms_per_call"], "config": {"workload": VARLEN},
+                           "roofline": e["roofline"]})
 
     if args.only in ("all", "decode"):
         d = W.make_workload(DECODE, seed=4, device=dev)
@@ -448,6 +595,132 @@ def main():
     return 0
 
 
+def _prefill_caller(sgla, torch, inp, dev):
+    """A prefill call on a named workload's inputs with preallocated outputs
+    and workspace, and its algorithmic bytes."""
+    B, T, H, Dk = inp["q"].shape
+    Dv = inp["v"].shape[-1]
+    cu = inp["cu_seqlens"]
+    N = B if cu is None else cu.numel() - 1
+    Barg = N if cu is not None else B
+    out = torch.empty_like(inp["v"])
+    fs = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, sgla.chunk_workspace_size(Barg, T, H, Dk, Dv, varlen=cu is not None)),
+                     dtype=torch.uint8, device=dev)
+    s0 = inp["initial_state"]
+
+    def call():
+        sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], s0, cu, inp["scale"], out=out,
+                       final_state=fs, workspace=ws)
+
+    tokens = B * T * H * (2 * Dk * 2 + 2 * Dv * 2 + 4)
+    states = N * H * Dk * Dv * 4 * (2 if s0 is not None else 1)
+    return call, tokens + states, out, fs, ws
+
+
+def _region(fn, n, torch):
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def bench_long(args, torch, sgla, W, dev):
+    """The 65,536-token continuation (B=1, H=32, D=128, bf16, fp32 initial
+    state ~ N(0, 0.02^2)), and the same tokens as two chained calls split at
+    32,768 (the second starts from the first's final state). Its inputs (1.5
+    GiB) exceed the memory-side cache, so back-to-back calls read HBM."""
+    inp = W.make_workload(LONG, seed=3, device=dev)
+    call, nbytes, out, fs, ws = _prefill_caller(sgla, torch, inp, dev)
+    T = inp["q"].shape[1]
+    call()
+    torch.cuda.synchronize()
+    ms = _region(call, args.long_steps, torch)
+    res = {"workload": LONG, "ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+           "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "traffic": recorded_traffic(LONG),
+                        "kernel": "sgla_chunk_fwd_ex (whole call: segment-state, scan and "
+                                  "value-half output kernels)",
+                        "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms},
+           "mfma_busy": recorded_mfma(LONG)}
+    t = W.WORKLOADS[LONG]["split"]
+    halves = []
+    for part in ("a", "b"):
+        sl = slice(0, t) if part == "a" else slice(t, T)
+        d = {x: inp[x][:, sl].contiguous() for x in ("q", "k", "v", "g")}
+        d.update(cu_seqlens=None, scale=inp["scale"],
+                 initial_state=inp["initial_state"] if part == "a" else None)
+        halves.append(d)
+    ca, nba, _, fsa, wsa = _prefill_caller(sgla, torch, halves[0], dev)
+    halves[1]["initial_state"] = fsa
+    cb, nbb, _, _, wsb = _prefill_caller(sgla, torch, halves[1], dev)
+
+    def chained():
+        ca()
+        cb()
+
+    chained()
+    torch.cuda.synchronize()
+    ms2 = _region(chained, args.long_steps, torch)
+    res["split"] = {"at": t, "ms_per_pair": ms2, "tokens_per_s": T / (ms2 * 1e-3),
+                    "achieved_GBs": (nba + nbb) / (ms2 * 1e-3) / 1e9,
+                    "frac": (nba + nbb) / (ms2 * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del inp, out, fs, ws, halves, fsa, wsa, wsb
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_varlen(args, torch, sgla, W, dev):
+    """The packed varlen prefill: 8 sequences, 524,288 tokens in total, lengths
+    log-uniform in [4096, 262144] rescaled to the total, H=32, D=128, bf16."""
+    inp = W.make_workload(VARLEN, seed=5, device=dev)
+    call, nbytes, out, fs, ws = _prefill_caller(sgla, torch, inp, dev)
+    T = inp["q"].shape[1]
+    lengths = (inp["cu_seqlens"][1:] - inp["cu_seqlens"][:-1]).tolist()
+    call()
+    torch.cuda.synchronize()
+    ms = _region(call, args.long_steps, torch)
+    res = {"workload": VARLEN, "lengths": lengths, "ms_per_call": ms,
+           "tokens_per_s": T / (ms * 1e-3),
+           "roofline": {"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "traffic": recorded_traffic(VARLEN),
+                        "kernel": "sgla_chunk_fwd_ex (whole call: plan, segment-state, scan "
+                                  "and output kernels)",
+                        "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms},
+           "mfma_busy": recorded_mfma(VARLEN)}
+    del inp, out, fs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_cache_resident(args, torch, sgla, W, dev):
+    """The prefill kernels' compute rate: B=2, T=2048, H=32, D=128 (64 MiB of
+    q, k, v and o) back to back, so every call finds its inputs in the caches
+    and the call is bound by the kernels' own work, not by HBM. Reported as
+    dense-tile flops per second over the bf16 matrix-core peak."""
+    inp = W.make_prefill(2, 2048, 32, 128, 128, "bf16", "lightning", seed=7, device=dev)
+    call, nbytes, out, fs, ws = _prefill_caller(sgla, torch, inp, dev)
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    ms = _region(call, 50, torch)
+    flops = prefill_flops(2, 2048, 32, 128, 128)
+    del inp, out, fs, ws
+    torch.cuda.empty_cache()
+    return {"workload": "prefill B=2 T=2048 H=32 D=128 bf16, back to back (cache-resident)",
+            "ms_per_call": ms, "useful_tflops": flops / (ms * 1e-3) / 1e12,
+            "useful_frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS,
+            "achieved_GBs": nbytes / (ms * 1e-3) / 1e9}
+
+
 def bench_gdn(args, torch, sgla, W, dev):
     """The gated delta rule on the same shapes: prefill B=1, T=8192, H=32,
     Dk=Dv=128 (sgla_gdn_chunk_fwd) and the batched decode, 256 x 32 heads,
@@ -458,10 +731,11 @@ def bench_gdn(args, torch, sgla, W, dev):
                          with_beta=True)
     o = torch.empty_like(inp["v"])
     fs = torch.empty((1, 32, 128, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(sgla.gdn_workspace_size(1, 8192, 32, 128, 128), dtype=torch.uint8, device=dev)
 
     def step():
         sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
-                           scale=inp["scale"], out=o, final_state=fs)
+                           scale=inp["scale"], out=o, final_state=fs, workspace=ws)
 
     _, region, per = time_calls(step, args.steps, args.warmup, torch)
     per_avg = region / args.steps
@@ -571,10 +845,12 @@ def bench_prologue(args, torch, sgla, W, dev):
     qw, kw = W.norm_weights(128, seed=args.seed, device=dev)
     o = torch.empty_like(inp["v"])
     fs = torch.empty((1, 32, 128, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, sgla.chunk_workspace_size(1, 8192, 32, 128, 128, prologue=True)),
+                     dtype=torch.uint8, device=dev)
 
     def step():
         sgla.chunk_fwd_qk_norm_rope(inp["q"], inp["k"], inp["v"], inp["g"], qw, kw,
-                                    scale=inp["scale"], out=o, final_state=fs)
+                                    scale=inp["scale"], out=o, final_state=fs, workspace=ws)
 
     _, region, per = time_calls(step, args.steps, args.warmup, torch)
     per_avg = region / args.steps
@@ -586,7 +862,7 @@ def bench_prologue(args, torch, sgla, W, dev):
                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                                    "traffic": recorded_traffic(PREFILL_PRO),
-                                   "kernel": "sgla_chunk_fwd_qk_norm_rope (whole call)",
+                                   "kernel": "sgla_chunk_fwd_ex with the prologue (whole call)",
                                    "algorithmic_bytes_per_launch": nbytes,
                                    "avg_launch_ms": per_avg}}
     del inp, o, fs
