@@ -276,6 +276,25 @@ sgla_status sgla_chunk_fwd_qk_norm_rope(const void *q, const void *k, const void
                                         sgla_dtype dtype, void *stream);
 
 /*
+ * sgla_qk_norm_rope — the prologue alone, applied to one of q or k: the same
+ * device code the chunked entry points run as they load each 64-token chunk,
+ * so its output is, bit for bit, what they feed the recurrence.
+ *
+ *   x           [B, T, H, 128] bf16 (q or k before the prologue).
+ *   weight      [128] fp32 RMSNorm weight (q_weight or k_weight).
+ *   pos_offset  [B] int32 device, or NULL for zeros: token t of sequence b is
+ *               at position pos_offset[b] + t.
+ *   out         [B, T, H, 128] bf16; it may equal x (in place), it must not
+ *               overlap it otherwise.
+ *   theta, eps  as above.
+ * dtype must be SGLA_BF16 and Dk 128 (SGLA_ERR_UNSUPPORTED otherwise); x and
+ * out 16-byte aligned. Returns as sgla_chunk_fwd; allocates nothing.
+ */
+sgla_status sgla_qk_norm_rope(const void *x, const float *weight, const int32_t *pos_offset,
+                              void *out, int B, int T, int H, int Dk, float theta, float eps,
+                              sgla_dtype dtype, void *stream);
+
+/*
  * sgla_recurrent_step_qk_norm_rope — sgla_recurrent_step with the prologue.
  *
  *   positions   [N] int32 device, never NULL: the position of each row's

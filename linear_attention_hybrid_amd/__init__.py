@@ -38,7 +38,7 @@ import torch
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_qk_norm_rope", "recurrent_step_qk_norm_rope",
            "recurrent_step_ex", "out_norm_gate", "gdn_chunk_fwd", "gdn_recurrent_step",
-           "chunk_workspace_size", "gdn_workspace_size", "validate_cu_seqlens",
+           "chunk_workspace_size", "gdn_workspace_size", "validate_cu_seqlens", "qk_norm_rope",
            "status_string", "library", "library_path", "exported_symbols", "SglaError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -100,6 +100,8 @@ def library():
         lib.sgla_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
                                                cf, ci, vp]
         lib.sgla_chunk_fwd_noalloc.restype = ci
+        lib.sgla_qk_norm_rope.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, cf, cf, ci, vp]
+        lib.sgla_qk_norm_rope.restype = ci
         lib.sgla_validate_cu_seqlens.argtypes = [vp, ci, ci, vp, vp]
         lib.sgla_validate_cu_seqlens.restype = ci
         lib.sgla_gdn_chunk_fwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, zp]
@@ -228,6 +230,32 @@ def _workspace(workspace, nbytes, device):
     if workspace.device != device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on %s" % device)
     return ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), workspace
+
+
+def qk_norm_rope(x, weight, pos_offset=None, theta=10000.0, eps=1e-6, out=None):
+    """The q/k prologue alone (sgla_qk_norm_rope): per-head RMSNorm with
+    ``weight`` (fp32 [128]) then rotate-half RoPE, on x [B, T, H, 128] bf16;
+    token t of sequence b at position pos_offset[b] + t (int32 [B] or None).
+    Returns the bf16 result (``out`` may be x itself)."""
+    if x.dim() != 4:
+        raise ValueError("x must be [B, T, H, Dk]")
+    B, T, H, Dk = x.shape
+    device = x.device
+    _check(x, "x", torch.bfloat16, (B, T, H, Dk), device)
+    _check(weight, "weight", torch.float32, (Dk,), device)
+    if pos_offset is not None:
+        _check(pos_offset, "pos_offset", torch.int32, (B,), device)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check(out, "out", torch.bfloat16, (B, T, H, Dk), device)
+    with torch.cuda.device(device):
+        st = library().sgla_qk_norm_rope(_ptr(x), _ptr(weight), _ptr(pos_offset), _ptr(out), B, T,
+                                         H, Dk, float(theta), float(eps), SGLA_BF16,
+                                         _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_qk_norm_rope", st)
+    return out
 
 
 def validate_cu_seqlens(cu_seqlens, T):

@@ -49,17 +49,15 @@ constexpr int OFF_G = 73728;      // G[64] fp32
 constexpr int LDS_OUT = OFF_G + 256;
 constexpr int LDS_STATE = 32768;  // KT and VT only (state phase, placed at 0)
 // q/k prologue tables, after the kernel's own LDS: RMSNorm weights of q and
-// k (2 x 128 fp32), RoPE turns per position per frequency (64 fp64 and the
-// same as fp32), cos and sin of one position's and of 32 positions' turn per
-// frequency (2 x 64 x 2 fp32), and each wave's base turns of the current
-// chunk (4 x 64 fp32).
+// k (2 x 128 fp32), RoPE turns per position per frequency (64 fp64), cos and sin of one position's and of 32 positions' turn per
+// frequency (2 x 64 x 2 fp32), and each wave's turns of its four rows of the
+// current chunk (4 x 4 x 64 fp32).
 constexpr int PRO_W = 0;
 constexpr int PRO_OM = 1024;
-constexpr int PRO_OREV = 1536;
 constexpr int PRO_ROT = 1792;
 constexpr int PRO_ROT32 = 2304;
-constexpr int PRO_BASE = 2816;
-constexpr int PRO_BYTES = 3840;
+constexpr int PRO_BASE = 2816;   // per wave: turns of its 4 rows x 64 frequencies (4 x 1 KiB)
+constexpr int PRO_BYTES = PRO_BASE + 4 * 1024;
 
 // The prologue of one 16-byte piece (8 consecutive dims 8c .. 8c+7 of a
 // 128-dim row, c = lane & 15) held by each of the 16 lanes of a DPP row:
@@ -101,6 +99,100 @@ __device__ __forceinline__ u32x4 qk_prologue_piece(u32x4 raw, const char *lds, i
         r[j] = pack_f32(o[0], o[1]);
     }
     return r;
+}
+
+// The prologue tables in LDS at `base` (PRO_BYTES): the two RMSNorm weight
+// vectors (q's skipped when qw is null), the turns per position of each
+// frequency (fp64), and the cos and sin of one position's and of 32
+// positions' turn per frequency. Callers synchronise before reading them.
+__device__ __forceinline__ void prologue_tables(char *lds, int base, const float *qw,
+                                                const float *kw, float theta, int tid) {
+    if (tid < D) {
+        if (qw) lds_st(lds, base + PRO_W + 4 * tid, qw[tid]);
+        lds_st(lds, base + PRO_W + 512 + 4 * tid, kw[tid]);
+    }
+    if (tid < 64) {
+        const double om = rope_turns_per_pos(tid, D, theta);
+        lds_st(lds, base + PRO_OM + 8 * tid, om);
+        const double t = 6.283185307179586477 * (om - rint(om));
+        lds_st(lds, base + PRO_ROT + 8 * tid, make_float2((float)cos(t), (float)sin(t)));
+        const double t32 = 6.283185307179586477 * (32.0 * om - rint(32.0 * om));
+        lds_st(lds, base + PRO_ROT32 + 8 * tid, make_float2((float)cos(t32), (float)sin(t32)));
+    }
+}
+
+// The prologue of one 64-token chunk on the registers of one thread: its
+// 16-byte pieces (dims 8c .. 8c+7, c = tid & 15) of rows 2 prb + 32 it + rr
+// (prb = (tid >> 4) & 15) of k, and of q when Q. pos_chunk is the position
+// of the chunk's first token and n its valid rows (rows past it give zeros).
+// Row 2 prb takes the hardware sine and cosine of its own angle, reduced in
+// fp64 to a fraction of a turn; rows 2 prb + 1, + 32 and + 33 turn it by one,
+// 32 and 33 positions with per-frequency constants. Each row's values are
+// formed just before its pieces use them. The reduced angles of the wave's
+// four rows go through LDS at base + PRO_BASE + 1024 w (lane l computes
+// frequency l of each) and are read back by the same wave (its LDS accesses
+// complete in order).
+template <bool Q>
+__device__ __forceinline__ void prologue_chunk(u32x4 (&kr)[2][2], u32x4 (&qr)[2][2], char *lds,
+                                               int base, int64_t pos_chunk, int n, float eps,
+                                               int tidv) {
+    const int w = tidv >> 6;
+    const int cidx = tidv & 15;
+    const int prb = (tidv >> 4) & 15;  // 4 w + (lane >> 4)
+    const int wb = base + PRO_BASE + 1024 * w;
+    {
+        const double om = lds_ld<double>(lds, base + PRO_OM + 8 * (tidv & 63));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            lds_st(lds, wb + 256 * j + 4 * (tidv & 63),
+                   rope_base_turns(pos_chunk + 2 * (4 * w + j), om));
+    }
+    const int fb = 4 * 8 * (cidx & 7);
+    const int rb = wb + 256 * ((tidv >> 4) & 3);
+    const float4 b0 = lds_ld<float4>(lds, rb + fb), b1 = lds_ld<float4>(lds, rb + fb + 16);
+    // The lower half of the row turns its partner in with a minus sign:
+    // there every sine is negated (the angle is).
+    const float sg = cidx >= 8 ? 1.f : -1.f;
+    const float bt[8] = {sg * b0.x, sg * b0.y, sg * b0.z, sg * b0.w,
+                         sg * b1.x, sg * b1.y, sg * b1.z, sg * b1.w};
+    float c0[8], s0[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        c0[e] = cos_turns(bt[e]);
+        s0[e] = sin_turns(bt[e]);
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            float cs[8], sn[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float c = c0[e], sv = s0[e];
+                if (it) {
+                    const float2 r32 = lds_ld<float2>(lds, base + PRO_ROT32 + 2 * fb + 8 * e);
+                    const float rs = sg * r32.y;
+                    const float cn = fmaf(c, r32.x, -sv * rs);
+                    sv = fmaf(sv, r32.x, c * rs);
+                    c = cn;
+                }
+                if (rr) {
+                    const float2 rot = lds_ld<float2>(lds, base + PRO_ROT + 2 * fb + 8 * e);
+                    const float rs = sg * rot.y;
+                    const float cn = fmaf(c, rot.x, -sv * rs);
+                    sv = fmaf(sv, rot.x, c * rs);
+                    c = cn;
+                }
+                cs[e] = c;
+                sn[e] = sv;
+            }
+            const int r = 2 * (prb + 16 * it) + rr;
+            kr[it][rr] = qk_prologue_piece(kr[it][rr], lds, base + PRO_W + 512 + 32 * cidx, cs, sn,
+                                           r < n, eps);
+            if (Q)
+                qr[it][rr] = qk_prologue_piece(qr[it][rr], lds, base + PRO_W + 32 * cidx, cs, sn,
+                                               r < n, eps);
+        }
 }
 
 template <bool STATE_ONLY, bool PRO>
@@ -191,19 +283,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
     // Prologue tables, and the position of the segment's first token.
     int64_t pos0 = 0;
     if (PRO) {
-        if (tid < D) {
-            if (!STATE_ONLY) lds_st(lds, kBase + PRO_W + 4 * tid, p.qw[tid]);
-            lds_st(lds, kBase + PRO_W + 512 + 4 * tid, p.kw[tid]);
-        }
-        if (tid < 64) {
-            const double om = rope_turns_per_pos(tid, D, p.theta);
-            lds_st(lds, kBase + PRO_OM + 8 * tid, om);
-            lds_st(lds, kBase + PRO_OREV + 4 * tid, (float)om);
-            const double t = 6.283185307179586477 * (om - rint(om));
-            lds_st(lds, kBase + PRO_ROT + 8 * tid, make_float2((float)cos(t), (float)sin(t)));
-            const double t32 = 6.283185307179586477 * (32.0 * om - rint(32.0 * om));
-            lds_st(lds, kBase + PRO_ROT32 + 8 * tid, make_float2((float)cos(t32), (float)sin(t32)));
-        }
+        prologue_tables(lds, kBase, STATE_ONLY ? nullptr : p.qw, p.kw, p.theta, tid);
         pos0 = (p.pos_off ? (int64_t)p.pos_off[se.seq] : 0) + (int64_t)se.p * p.seg_len;
         __syncthreads();
     }
@@ -262,67 +342,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
             for (int rr = 0; rr < 2; ++rr)
                 fac[it][rr] = __expf(Gl - __shfl(G, 2 * (prb + 16 * it) + rr, 64));
 
-        if (PRO) {
-            // This wave's base turns of the chunk's first token, one lane per
-            // frequency; the wave reads them back right away (its LDS
-            // accesses complete in order).
-            const int base = kBase + PRO_BASE + 256 * w;
-            lds_st(lds, base + 4 * (tidv & 63),
-                   rope_base_turns(pos0 + c0, lds_ld<double>(lds, kBase + PRO_OM + 8 * (tidv & 63))));
-            const int fb = 4 * 8 * (cidx & 7);
-            const float4 b0 = lds_ld<float4>(lds, base + fb), b1 = lds_ld<float4>(lds, base + fb + 16);
-            const float4 f0 = lds_ld<float4>(lds, kBase + PRO_OREV + fb);
-            const float4 f1 = lds_ld<float4>(lds, kBase + PRO_OREV + fb + 16);
-            // The lower half of the row turns its partner in with a minus
-            // sign: there every sine is negated (the angle is).
-            const float sg = cidx >= 8 ? 1.f : -1.f;
-            const float bt[8] = {sg * b0.x, sg * b0.y, sg * b0.z, sg * b0.w,
-                                 sg * b1.x, sg * b1.y, sg * b1.z, sg * b1.w};
-            const float om[8] = {sg * f0.x, sg * f0.y, sg * f0.z, sg * f0.w,
-                                 sg * f1.x, sg * f1.y, sg * f1.z, sg * f1.w};
-            // Row 2prb from the hardware sine/cosine; rows 2prb + 1, + 32 and
-            // + 33 by turning it one, 32 and 33 positions further. Each row's
-            // values are formed just before its pieces use them.
-            float c0[8], s0[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float a = fmaf((float)(2 * prb), om[e], bt[e]);
-                c0[e] = cos_turns(a);
-                s0[e] = sin_turns(a);
-            }
-#pragma unroll
-            for (int it = 0; it < 2; ++it)
-#pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    float cs[8], sn[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        float c = c0[e], sv = s0[e];
-                        if (it) {
-                            const float2 r32 = lds_ld<float2>(lds, kBase + PRO_ROT32 + 2 * fb + 8 * e);
-                            const float rs = sg * r32.y;
-                            const float cn = fmaf(c, r32.x, -sv * rs);
-                            sv = fmaf(sv, r32.x, c * rs);
-                            c = cn;
-                        }
-                        if (rr) {
-                            const float2 rot = lds_ld<float2>(lds, kBase + PRO_ROT + 2 * fb + 8 * e);
-                            const float rs = sg * rot.y;
-                            const float cn = fmaf(c, rot.x, -sv * rs);
-                            sv = fmaf(sv, rot.x, c * rs);
-                            c = cn;
-                        }
-                        cs[e] = c;
-                        sn[e] = sv;
-                    }
-                    const int r = 2 * (prb + 16 * it) + rr;
-                    kr[it][rr] = qk_prologue_piece(kr[it][rr], lds, kBase + PRO_W + 512 + 32 * cidx,
-                                                   cs, sn, r < n, p.eps);
-                    if (!STATE_ONLY)
-                        qr[it][rr] = qk_prologue_piece(qr[it][rr], lds, kBase + PRO_W + 32 * cidx,
-                                                       cs, sn, r < n, p.eps);
-                }
-        }
+        if (PRO) prologue_chunk<!STATE_ONLY>(kr, qr, lds, kBase, pos0 + c0, n, p.eps, tidv);
 
         __syncthreads();  // every reader of the previous chunk's tiles is done
         if (!STATE_ONLY) {
@@ -471,7 +491,60 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
     if (STATE_ONLY && tid == 0) p.gam[(int64_t)s * H + h] = gam_acc;
 }
 
+// The prologue alone: one workgroup per (64-token chunk, head) of x [B, T,
+// H, 128] bf16, through the same loads and the same prologue_chunk as the
+// chunked kernels; token t of sequence b sits at position pos_off[b] + t.
+__global__ __launch_bounds__(NT) void qk_norm_rope_kernel(const uint16_t *__restrict__ x,
+                                                          const float *__restrict__ w,
+                                                          const int32_t *__restrict__ pos_off,
+                                                          uint16_t *out, int B, int T, int H,
+                                                          float theta, float eps) {
+    __shared__ __attribute__((aligned(16))) char lds[PRO_BYTES];
+    const int64_t unit = blockIdx.x;
+    const int h = (int)(unit % H);
+    const int64_t bc = unit / H;
+    const int nch = (T + 63) / 64;
+    const int b = (int)(bc / nch);
+    const int c = (int)(bc - (int64_t)b * nch);
+    if (b >= B) return;
+    const int tid = threadIdx.x;
+    int tidv = tid;
+    asm volatile("" : "+v"(tidv));
+    const int n = min(64, T - 64 * c);
+    const int64_t base = (((int64_t)b * T + 64 * (int64_t)c) * H + h) * D;
+    const int nb = (n - 1) * H * (D * 2) + D * 2;
+    const buf_t rx = buf_rsrc(x + base, nb);
+    const buf_t ro = buf_rsrc(out + base, nb);
+    u32x4 kr[2][2], none[2][2];
+    auto off = [&](int it, int rr) -> uint32_t {
+        const int r = 2 * (((tidv >> 4) & 15) + 16 * it) + rr;
+        return (uint32_t)(r * H) * (uint32_t)(D * 2) + (uint32_t)(tidv & 15) * 16u;
+    };
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) kr[it][rr] = buf_ld16(rx, off(it, rr));
+    prologue_tables(lds, 0, nullptr, w, theta, tid);
+    __syncthreads();
+    const int64_t pos = (pos_off ? (int64_t)pos_off[b] : 0) + 64 * (int64_t)c;
+    prologue_chunk<false>(kr, none, lds, 0, pos, n, eps, tidv);
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) buf_st16(ro, off(it, rr), kr[it][rr]);
+}
+
 }  // namespace
+
+hipError_t launch_qk_norm_rope(const void *x, const float *w, const int32_t *pos_off, void *out,
+                               int B, int T, int H, float theta, float eps, hipStream_t st) {
+    const int64_t units = (int64_t)B * ((T + 63) / 64) * H;
+    if (units == 0) return hipSuccess;
+    hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)units), dim3(NT), 0, st,
+                       static_cast<const uint16_t *>(x), w, pos_off, static_cast<uint16_t *>(out),
+                       B, T, H, theta, eps);
+    return hipGetLastError();
+}
 
 hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t st) {
     if (p.nseg_max == 0) return hipSuccess;

@@ -179,6 +179,23 @@ sgla_status sgla_chunk_fwd_ex(const void *q, const void *k, const void *v, const
                      scale, dtype, stream, q_weight ? &pro : nullptr, workspace, workspace_bytes);
 }
 
+sgla_status sgla_qk_norm_rope(const void *x, const float *weight, const int32_t *pos_offset,
+                              void *out, int B, int T, int H, int Dk, float theta, float eps,
+                              sgla_dtype dtype, void *stream) {
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 1 || Dk < 1) return SGLA_ERR_INVALID_ARG;
+    if (dtype != SGLA_BF16 || Dk != 128 || H > kMaxHeads) return SGLA_ERR_UNSUPPORTED;
+    const ProArgs pro{weight, weight, pos_offset, theta, eps};
+    const sgla_status ps = check_prologue(pro);
+    if (ps != SGLA_OK) return ps;
+    const int64_t units = (int64_t)B * ((T + 63) / 64) * H;
+    if (units > ((int64_t)1 << 31) - 1) return SGLA_ERR_UNSUPPORTED;
+    if (units == 0) return SGLA_OK;
+    if (!x || !out || misaligned(x) || misaligned(out)) return SGLA_ERR_INVALID_ARG;
+    return hip_status(launch_qk_norm_rope(x, weight, pos_offset, out, B, T, H, theta, eps,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 sgla_status sgla_validate_cu_seqlens(const int64_t *cu_seqlens, int B, int T, int32_t *status,
                                      void *stream) {
     if (B < 0 || T < 0 || !status || !cu_seqlens) return SGLA_ERR_INVALID_ARG;

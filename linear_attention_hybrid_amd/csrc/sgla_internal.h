@@ -187,6 +187,8 @@ hipError_t launch_chunk_valu(const ChunkParams &p, bool bf16, int Dk, int Dv, bo
                              hipStream_t st);
 hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t st);
 hipError_t launch_chunk_halves(const HalvesParams &hp, hipStream_t st);
+hipError_t launch_qk_norm_rope(const void *x, const float *w, const int32_t *pos_off, void *out,
+                               int B, int T, int H, float theta, float eps, hipStream_t st);
 hipError_t launch_out_norm_gate(const void *o, const void *z, const float *w, void *out,
                                 int64_t rows, int width, float eps, bool bf16, hipStream_t st);
 // Decode-step prologue arguments; qw == nullptr: none.

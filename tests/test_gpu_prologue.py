@@ -4,15 +4,23 @@ the raw q and k into the bf16 values the recurrence consumes, then the
 recurrence oracle runs on them. Same bars as the other bf16 cases.
 
 The prologue ends in two bf16 roundings. The kernels take them from fp32
-values (fp32 angles, hardware sine and cosine), the oracle from fp64 ones, so
-an element whose exact value lies within about 2^-15 of the size of its inputs
-from a midpoint between two bf16 numbers may round either way; both are
-correct. The oracle bounds what
-such an element can change (``qk_prologue(..., tie_eta)``), and three more
-runs of the recurrence oracle on absolute values bound the effect on every
-output and state element (flips in k, flips in q, both); that bound is added
-per element to the max-abs bar. Every other element keeps the plain bar, and
-rel-L2 is not relaxed.
+values, the oracle from fp64 ones, so an element whose exact value lies very
+near a midpoint between two bf16 numbers may round either way; both are
+correct. How near: the fp32 path's error relative to the size of its inputs
+is a few fp32 units (sum of squares and reciprocal square root for RMSNorm,
+about 2^-22; the angle reduced in fp64 then carried in fp32 turns, about
+2^-24; the hardware sine and cosine, about 2^-23; at most two turns by
+per-frequency constants, each a few 2^-24), together under 2^-21, so the band
+is TIE_ETA = 2^-20 times the size of the inputs, with a factor 2 to spare.
+The standalone prologue test checks that band directly: every element the
+kernels round differently from the oracle lies inside it.
+
+The oracle bounds what a flagged element can change (``qk_prologue(...,
+tie_eta)``), and three more runs of the recurrence oracle on absolute values
+bound the effect on every output and state element (flips in k, flips in q,
+both); that bound is added per element to the max-abs bar, and its median
+must stay below a tenth of the bar. Every other element keeps the plain bar,
+and rel-L2 is not relaxed.
 """
 import os
 
@@ -29,7 +37,8 @@ from tests.parity import check, host, nan_like, say
 pytestmark = pytest.mark.gpu
 
 THETA, EPS = 10000.0, 1e-6
-TIE_ETA = 2.0 ** -15
+TIE_ETA = 2.0 ** -20
+MEDIAN_CAP = 0.1  # allowance median / max-abs bar
 
 
 @pytest.fixture(autouse=True)
@@ -93,9 +102,12 @@ def run_chunk(inp, qw, kw, pos_off):
 def compare(inp, o, S, ref, what, heads=None, starts=None):
     ro, rS, ao, aS = ref
     go = host(o if heads is None else o[:, :, heads])
-    check(go, ro, "bf16", what + " o", allowance=ao)
+    m = check(go, ro, "bf16", what + " o", allowance=ao, max_allowance_median=MEDIAN_CAP)
+    say("  %s o: allowance/bar median %.3g max %.3g, over the bar %.4f" % (
+        what, m["allowance_median_over_bar"], m["allowance_max_over_bar"],
+        m["allowance_frac_over_bar"]))
     check(host(S if heads is None else S[:, heads]), rS, "bf16", what + " final state",
-          bf16_out=False, allowance=aS)
+          bf16_out=False, allowance=aS, max_allowance_median=MEDIAN_CAP)
     if starts:
         for s0 in starts:
             for w in (64, 256):
@@ -169,8 +181,9 @@ def test_split_and_continue():
     b["initial_state"] = Sa
     ob, Sb = run_chunk(b, qw, kw, torch.tensor([t], dtype=torch.int32, device="cuda"))
     go = host(torch.cat([oa, ob], dim=1))
-    check(go, ro, "bf16", "split o", allowance=ao)
-    check(host(Sb), rS, "bf16", "split state", bf16_out=False, allowance=aS)
+    check(go, ro, "bf16", "split o", allowance=ao, max_allowance_median=MEDIAN_CAP)
+    check(host(Sb), rS, "bf16", "split state", bf16_out=False, allowance=aS,
+          max_allowance_median=MEDIAN_CAP)
     for w in (64, 256):
         check(go[0, t:t + w], ro[0, t:t + w], "bf16", "split window %d" % w,
               allowance=ao[0, t:t + w])
@@ -225,9 +238,10 @@ def test_step_with_slot_map(dv):
                                              state_indices=idx, scale=d["scale"], out=out)
         torch.cuda.synchronize()
         ro, ao, aS = oracle_step_with_prologue(d, i, qw, kw, pos + i, ref_state, idx)
-        check(host(o), ro, "bf16", "step %d o" % i, allowance=ao)
+        check(host(o), ro, "bf16", "step %d o" % i, allowance=ao,
+              max_allowance_median=MEDIAN_CAP)
         check(host(state[idx.long()]), ref_state[idx.cpu().numpy()], "bf16",
-              "step %d state" % i, bf16_out=False, allowance=aS)
+              "step %d state" % i, bf16_out=False, allowance=aS, max_allowance_median=MEDIAN_CAP)
 
 
 def test_step_equals_one_token_chunk():
@@ -260,5 +274,40 @@ def test_workload_decode_one_step():
                                          kw, d["pos"][0], theta=THETA, eps=EPS)
     torch.cuda.synchronize()
     ro, ao, aS = oracle_step_with_prologue(d, 0, qw, kw, d["pos"][0], ref_state)
-    check(host(o), ro, "bf16", "decode o", allowance=ao)
-    check(host(state), ref_state, "bf16", "decode state", bf16_out=False, allowance=aS)
+    m = check(host(o), ro, "bf16", "decode o", allowance=ao, max_allowance_median=MEDIAN_CAP)
+    say("  decode o: allowance/bar median %.3g max %.3g" % (m["allowance_median_over_bar"],
+                                                          m["allowance_max_over_bar"]))
+    check(host(state), ref_state, "bf16", "decode state", bf16_out=False, allowance=aS,
+          max_allowance_median=MEDIAN_CAP)
+
+
+@pytest.mark.parametrize("B,T,H,offsets", [(1, 2048, 2, [123456]), (2, 300, 3, [0, (1 << 31) - 400]),
+                                           (1, 8192, 4, None)])
+def test_standalone_prologue_is_the_oracle_bit_for_bit_outside_the_tie_band(B, T, H, offsets):
+    """sgla_qk_norm_rope runs the chunked kernels' own prologue code. Its bf16
+    output equals the oracle's exactly, except on elements the oracle flags
+    as within TIE_ETA of a rounding midpoint (at either rounding); this is
+    the evidence for the band the other prologue tests use."""
+    say("qk_norm_rope B=%d T=%d H=%d offsets %s" % (B, T, H, offsets))
+    inp = W.make_prefill(B, T, H, 128, 128, "bf16", "raw", seed=T + H, device="cuda")
+    qw, kw = W.norm_weights(128, seed=T + H, device="cuda")
+    pos_off = None if offsets is None else torch.tensor(offsets, dtype=torch.int32, device="cuda")
+    pos = token_positions(B, T, None, pos_off)
+    total = flagged = differ = 0
+    for name, x, w in (("q", inp["q"], qw), ("k", inp["k"], kw)):
+        got = host(sgla.qk_norm_rope(x, w, pos_off, THETA, EPS))
+        torch.cuda.synchronize()
+        ref, bound = OP.qk_prologue(host(x), host(w), pos, THETA, EPS, TIE_ETA)
+        diff = got != ref
+        flag = bound > 0
+        outside = diff & ~flag
+        assert not np.any(outside), (name, int(outside.sum()), np.argwhere(outside)[:5])
+        total += got.size
+        flagged += int(flag.sum())
+        differ += int(diff.sum())
+    say("  %d elements, %d (%.3f%%) flagged near a tie, %d differ from the oracle" % (
+        total, flagged, 100.0 * flagged / total, differ))
+    # In place gives the same bits.
+    y = inp["q"].clone()
+    sgla.qk_norm_rope(y, qw, pos_off, THETA, EPS, out=y)
+    assert torch.equal(y, sgla.qk_norm_rope(inp["q"], qw, pos_off, THETA, EPS))
