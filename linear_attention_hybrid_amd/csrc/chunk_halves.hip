@@ -21,13 +21,16 @@
 // tiles at the top of the next iteration; rows past a ragged end read as
 // zeros. Wave (cc, t) owns value columns 32cc .. 32cc+31 of the half; for the
 // output it takes token half t (tokens 32t .. 32t+31), and of the fp32 state
-// it holds key rows 64t .. 64t+63 in MFMA accumulators. The two waves of one
-// column block exchange their halves of the state as bf16 operands through
-// LDS once per chunk, so each can form Q S over all 128 key rows.
+// it holds key rows 64t .. 64t+63 in MFMA accumulators. Each wave forms Q S
+// over its own 64 key rows for all 64 tokens, and the two waves of one column
+// block trade the fp32 partial sums of each other's tokens through LDS.
 //
 // The products are 32x32x16 bf16 MFMAs, each written so that its result is
 // already in the register layout the next consumes (see mfma_tile.h): the
-// state accumulators convert to the A operand of S^T Q^T; A^T = K Q^T leaves
+// state accumulators convert to the A operand of S^T Q^T, as a bf16 pair
+// hi + lo (two MFMAs), so that the state keeps about 16 bits in the output:
+// one bf16 rounding of a large, slowly decaying state would cost the outputs
+// 2^-9 of their size. A^T = K Q^T leaves
 // each lane one query column, stored as A[i][j] rows for the B operand of
 // V^T A^T. K^T and V^T operands come from the row-major tiles through the
 // transposing LDS read, and the decay exp(G_last - G) scales the V operand of
@@ -51,7 +54,7 @@ constexpr int L_K = 16384;            // K rows, same layout
 constexpr int L_V = 32768;            // the half's V rows [64][128 B], swizzled as v_off
 constexpr int L_G = 40960;            // g [64] fp32
 constexpr int L_A = 41216;            // scores A[64 i][128 B] bf16, swizzled as tr_off
-constexpr int L_SX = L_A + 8192;      // bf16 state operands [block cc 2][dk tile 4][step 2][lane 64] x 16 B
+constexpr int L_SX = L_A + 8192;      // fp32 partials of Q S [block cc 2][token half 2][4][lane 64] x 16 B
 constexpr int L_O = L_SX + 16384;     // output staging [64 rows][128 B], swizzled as o_off
 constexpr int L_F = L_O + 8192;       // per wave: G[64] and exp(G_last - G)[64], fp32
 constexpr int L_BYTES = L_F + 4 * 512;
@@ -90,8 +93,8 @@ __device__ __forceinline__ int vtr_src(int r0, int c0, int m) {
 // p ^ ((r >> 1) & 7), halves traded in rows with bit 4 set, so that the
 // 8-byte writes of 32 consecutive rows fill all banks once.
 __device__ __forceinline__ int o_off(int r, int p) { return r * 128 + ((p ^ ((r >> 1) & 7)) << 4); }
-__device__ __forceinline__ int sx_off(int cc, int b, int s2, int l) {
-    return L_SX + (((cc * 4 + b) * 2 + s2) * 64 + l) * 16;
+__device__ __forceinline__ int sx_off(int cc, int ib, int v4, int l) {
+    return L_SX + (((cc * 2 + ib) * 4 + v4) * 64 + l) * 16;
 }
 
 // Output segment s of the call (without a table as seg_at).
@@ -203,22 +206,6 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             }
     }
     if (nch > 0) issue(0);
-    // This wave's state tiles as bf16 A operands of S^T Q^T, kept in
-    // registers and staged for the other wave of the column block.
-    bf16x8 sown[2][2];
-    auto stage_state = [&]() {
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                bf16x8 x;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = (__bf16)S[bi][8 * s2 + e];
-                sown[bi][s2] = x;
-                lds_st(lds, sx_off(cc, 2 * t + bi, s2, l), x);
-            }
-    };
-    stage_state();
 
     char *ft = lds + L_F + 512 * w;  // this wave's G[64], then exp(G_last - G)[64]
     const int i = 32 * t + ln;        // this lane's query row of the output
@@ -249,24 +236,40 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
         lds_st(ft, 4 * l, G);
         lds_st(ft, 256 + 4 * l, l < n ? __expf(Gl - G) : 0.f);
 
-        // O^T = S^T Q^T over all key rows, then the rows scaled by
-        // scale * exp(G_i).
-        f32x16 acc = {};
+        // O^T = S^T Q^T over this wave's key rows for both token halves;
+        // the other half's partial sums go to the partner wave.
+        f32x16 acc = {}, oth = {};
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const bf16x8 sa = (b >> 1) == t ? sown[b & 1][s2] : lds_ld<bf16x8>(lds, sx_off(cc, b, s2, l));
-                const int cq = 4 * b + 2 * s2;
-                const bf16x4 x0 = lds_ld<bf16x4>(lds, L_Q + qk_off(i, cq) + qk_half(i, lh));
-                const bf16x4 x1 = lds_ld<bf16x4>(lds, L_Q + qk_off(i, cq + 1) + qk_half(i, lh));
-                acc = mfma(sa, cat4(x0, x1), acc);
-            }
-        {
-            const float f = p.scale * __expf(lds_ld<float>(ft, 4 * i));
+                bf16x8 sh, sl;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[v] *= f;
-        }
+                for (int e = 0; e < 8; ++e) {
+                    const float x = S[bi][8 * s2 + e];
+                    sh[e] = (__bf16)x;
+                    sl[e] = (__bf16)(x - (float)sh[e]);
+                }
+                const int cq = 4 * (2 * t + bi) + 2 * s2;
+#pragma unroll
+                for (int ib = 0; ib < 2; ++ib) {
+                    const int iq = 32 * ib + ln;
+                    const bf16x4 x0 = lds_ld<bf16x4>(lds, L_Q + qk_off(iq, cq) + qk_half(iq, lh));
+                    const bf16x4 x1 = lds_ld<bf16x4>(lds, L_Q + qk_off(iq, cq + 1) + qk_half(iq, lh));
+                    const bf16x8 bq = cat4(x0, x1);
+                    if (ib == t) {
+                        acc = mfma(sh, bq, acc);
+                        acc = mfma(sl, bq, acc);
+                    } else {
+                        oth = mfma(sh, bq, oth);
+                        oth = mfma(sl, bq, oth);
+                    }
+                }
+            }
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4)
+            lds_st(lds, sx_off(cc, 1 - t, v4, l),
+                   make_float4(oth[4 * v4], oth[4 * v4 + 1], oth[4 * v4 + 2], oth[4 * v4 + 3]));
 
         // Scores: wave 0 -> (keys 0-31, queries 0-31), 1 -> (0-31, 32-63),
         // 3 -> (32-63, 32-63); the fourth quadrant is masked out.
@@ -309,7 +312,20 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             vop[s4] = cat4(lds_tr(lds, L_V + vtr_src(16 * s4 + 8 * lh, c0, m16)),
                            lds_tr(lds, L_V + vtr_src(16 * s4 + 8 * lh + 4, c0, m16)));
         }
-        __syncthreads();  // the scores are staged
+        __syncthreads();  // the scores and the partial sums are staged
+
+        // The partner's key rows, then the rows scaled by scale * exp(G_i).
+        {
+            const float f = p.scale * __expf(lds_ld<float>(ft, 4 * i));
+#pragma unroll
+            for (int v4 = 0; v4 < 4; ++v4) {
+                const float4 y = lds_ld<float4>(lds, sx_off(cc, t, v4, l));
+                acc[4 * v4] = (acc[4 * v4] + y.x) * f;
+                acc[4 * v4 + 1] = (acc[4 * v4 + 1] + y.y) * f;
+                acc[4 * v4 + 2] = (acc[4 * v4 + 2] + y.z) * f;
+                acc[4 * v4 + 3] = (acc[4 * v4 + 3] + y.w) * f;
+            }
+        }
 
         // O^T += V^T A^T over the keys up to this token half.
 #pragma unroll
@@ -349,7 +365,6 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
                     S[bi] = mfma(kt, vs, S[bi]);
                 }
             }
-            stage_state();
         }
     }
     __syncthreads();  // the last chunk's output rows are staged

@@ -15,8 +15,11 @@
 // already in the register layout the next MFMA consumes:
 //   * the fp32 state S lives in the accumulators of the state update
 //     (32x32 tiles: lane l holds S[dk rows 8(v/4)+4(l/32)+v%4][dv column l%32]);
-//     converted to bf16 in registers it is directly the A operand of S^T Q^T,
-//     with Q read in the matching order of its dk rows;
+//     converted in registers to a bf16 pair hi + lo it is directly the A
+//     operand of S^T Q^T (two MFMAs), with Q read in the matching order of
+//     its dk rows. The pair keeps about 16 bits of the state: one bf16
+//     rounding of a large, slowly decaying state would cost the outputs 2^-9
+//     of their size;
 //   * A^T = K Q^T leaves each lane one query column i and 16 key rows j, i.e.
 //     4 consecutive j per group, written to LDS as A[i][j] with 8-byte stores,
 //     and read back as the B operand of V^T A^T;
@@ -412,37 +415,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
             }
             __syncthreads();  // A complete; K rows free for the O staging
 
+            // O^T = S^T Q^T for both token halves, each state tile converted
+            // once to the bf16 pair hi + lo.
+            f32x16 acc[2] = {};
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int i = 32 * nt + ln;
-                f32x16 acc = {};
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    bf16x8 sh, sl;
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        const int c = 4 * b + 2 * s2;
+                    for (int e = 0; e < 8; ++e) {
+                        const float x = S[b][8 * s2 + e];
+                        sh[e] = (__bf16)x;
+                        sl[e] = (__bf16)(x - (float)sh[e]);
+                    }
+                    const int c = 4 * b + 2 * s2;
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) {
+                        const int i = 32 * nt + ln;
                         const bf16x4 x0 = lds_ld<bf16x4>(lds, OFF_Q + row_off(i, c) + 8 * lh);
                         const bf16x4 x1 = lds_ld<bf16x4>(lds, OFF_Q + row_off(i, c + 1) + 8 * lh);
                         const bf16x8 bq = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
-                        // S^T as the bf16 A operand, converted from the fp32 state.
-                        bf16x8 sa;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) sa[e] = (__bf16)S[b][8 * s2 + e];
-                        acc = mfma(sa, bq, acc);
+                        acc[nt] = mfma(sh, bq, acc[nt]);
+                        acc[nt] = mfma(sl, bq, acc[nt]);
                     }
+                }
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) {
+                const int i = 32 * nt + ln;
                 const float f = p.scale * __expf(lds_ld<float>(lds, OFF_G + 4 * i));
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[v] *= f;
+                for (int v = 0; v < 16; ++v) acc[nt][v] *= f;
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
                     if (nt == 0 && st >= 2) break;
                     const bf16x8 ba = lds_ld<bf16x8>(lds, OFF_A + tr_off(i, 2 * st + lh));
-                    acc = mfma(vop[st], ba, acc);
+                    acc[nt] = mfma(vop[st], ba, acc[nt]);
                 }
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
-                    u32x2 pk = {pack_f32(acc[4 * g4], acc[4 * g4 + 1]),
-                                pack_f32(acc[4 * g4 + 2], acc[4 * g4 + 3])};
+                    u32x2 pk = {pack_f32(acc[nt][4 * g4], acc[nt][4 * g4 + 1]),
+                                pack_f32(acc[nt][4 * g4 + 2], acc[nt][4 * g4 + 3])};
                     lds_st(lds, OFF_K + row_off(i, 4 * w + g4) + 8 * lh, pk);
                 }
             }

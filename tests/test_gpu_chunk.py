@@ -223,18 +223,17 @@ def _sample_heads(H, n, seed):
 
 
 def test_workload_prefill_8k():
-    say("chunk_fwd workload prefill bf16 H=32 T=8192 D=128 seed=2 (4 sampled heads)")
+    say("chunk_fwd workload prefill bf16 H=32 T=8192 D=128 seed=2 (every head)")
     inp = W.make_workload("prefill_bf16_h32_t8192_d128", seed=2, device="cuda")
     o, S = run_gpu(inp)
-    heads = _sample_heads(32, 4, 2)
-    compare(inp, o, S, "bf16", "prefill 8k", heads=heads)
+    compare(inp, o, S, "bf16", "prefill 8k")
 
 
 def test_workload_prefill_64k_continuation_and_split():
-    say("chunk_fwd workload prefill bf16 H=32 T=65536 D=128 S0 seed=3 (3 sampled heads)")
+    say("chunk_fwd workload prefill bf16 H=32 T=65536 D=128 S0 seed=3 (every head)")
     inp = W.make_workload("prefill_bf16_h32_t65536_d128_cont", seed=3, device="cuda")
     o, S = run_gpu(inp)
-    heads = _sample_heads(32, 3, 3)
+    heads = list(range(32))
     ro, rS = compare(inp, o, S, "bf16", "prefill 64k", heads=heads, starts=[0])
     t = 32768
     a = dict(inp)
@@ -360,3 +359,119 @@ def test_validate_cu_seqlens():
         assert int(ws[:4].view(torch.int32).item()) == 0
     finally:
         os.environ.pop("SGLA_VALIDATE", None)
+
+
+
+# Per-head constant log-decays spread like the lightning layer's fixed ones
+# (page "MiniCPM-SALA - Complete Blueprint", section "B2 lightning-attn
+# (Simple GLA)": from -0.917, alpha about 0.40, the fastest forgetting, to
+# -0.0001, the slowest): geometric between the two ends. One 64-token chunk of
+# the fastest head sums to about -58.7.
+def g_gamma(H):
+    return -0.917 * (0.0001 / 0.917) ** (np.arange(H) / max(H - 1, 1))
+
+
+def constant_decay_inputs(B, T, H, D, dtype, seed, cu=None):
+    inp = W.make_prefill(B, T, H, D, D, dtype, "lightning", seed=seed, device="cuda",
+                         init="normal", cu_seqlens=cu)
+    gg = torch.tensor(g_gamma(H), dtype=torch.float32, device="cuda")
+    inp["g"] = gg.view(1, 1, H).expand_as(inp["g"]).contiguous()
+    return inp
+
+
+@pytest.mark.parametrize("path", ["halves", "one_level", "valu_bf16", "valu_f32_d64"])
+def test_per_head_constant_decay_from_0p40_to_0p9999(path):
+    """Strong and weak constant decays side by side, over several segments and
+    sub-segments, on each prefill path."""
+    dtype, D = ("f32", 64) if path == "valu_f32_d64" else ("bf16", 128)
+    if path == "one_level":
+        os.environ["SGLA_ONE_LEVEL"] = "1"
+    if path == "valu_bf16":
+        os.environ["SGLA_FORCE_VALU"] = "1"
+    set_segments(256, 2)
+    say("chunk_fwd constant per-head decay", path, "B=2 T=1100 H=8")
+    try:
+        inp = constant_decay_inputs(2, 1100, 8, D, dtype, seed=51)
+        o, S = run_gpu(inp)
+    finally:
+        os.environ.pop("SGLA_FORCE_VALU", None)
+    compare(inp, o, S, dtype, "constant decay " + path, starts=[0, 256, 512, 768, 1024])
+
+
+def test_per_head_constant_decay_varlen_without_workspace():
+    say("chunk_fwd constant per-head decay, packed, no workspace")
+    cu = W.cu_from_lengths([700, 0, 65, 300])
+    inp = constant_decay_inputs(1, int(cu[-1]), 8, 128, "bf16", seed=52, cu=cu)
+    o, S = sgla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["initial_state"],
+                          inp["cu_seqlens"], inp["scale"], workspace=None)
+    torch.cuda.synchronize()
+    compare(inp, o, S, "bf16", "constant decay packed", starts=[int(c) for c in cu[:-1]])
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("f32", 64)])
+def test_decay_table_of_the_blueprint_through_the_gpu(dtype, D):
+    """The page's "Concrete decay over distance" table (blueprint page,
+    section "Why Linear Attention Loses Information", Problem 1; fixture
+    tests/golden/decay_table.json): a one-hot outer product written at the
+    first token, zero keys after it, constant decay per head; after n more
+    tokens the written entry of the final state must print as the page's
+    value."""
+    import json
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "decay_table.json")))
+    heads = fx["heads"]
+    H = len(heads)
+    for n_str in ("1", "10", "100", "1000", "10000", "100000"):
+        n = int(n_str)
+        T = n + 1
+        say("chunk_fwd decay table", dtype, "n =", n)
+        tdt = DT[dtype]
+        q = torch.zeros((1, T, H, D), dtype=tdt, device="cuda")
+        k = torch.zeros_like(q)
+        v = torch.zeros((1, T, H, D), dtype=tdt, device="cuda")
+        i, j = 3, 5
+        k[0, 0, :, i] = 1.0
+        v[0, 0, :, j] = 1.0
+        g = torch.tensor([h["g"] for h in heads], dtype=torch.float32,
+                         device="cuda").view(1, 1, H).expand(1, T, H).contiguous()
+        _, S = sgla.chunk_fwd(q, k, v, g, scale=1.0)
+        torch.cuda.synchronize()
+        got = S[0, :, i, j].double().cpu().numpy()
+        others = S[0].clone()
+        others[:, i, j] = 0
+        assert float(others.abs().max()) == 0.0, n
+        for hh, val in zip(heads, got):
+            printed = hh["values"][n_str]
+            if float(printed) == 0.0:
+                assert abs(val) < fx["zero_bound"], (hh["label"], n, val)
+            elif dtype == "f32":
+                # The printed value carries its digits: the GPU result must
+                # round to it at that precision.
+                digits = len(printed.split("e")[0].replace(".", "").lstrip("0"))
+                assert float("%.*g" % (digits, val)) == float(printed), (hh["label"], n, val)
+            else:
+                # bf16 inputs: the update's decayed values exp(G_last - G) v
+                # are bf16 MFMA operands, one rounding of at most 2^-9 of the
+                # entry; the state and its decay between chunks stay fp32.
+                # So the entry lies within 2^-8 of the printed value plus half
+                # a unit of the printed value's last digit.
+                p = float(printed)
+                digits = len(printed.split("e")[0].replace(".", "").lstrip("0"))
+                last_unit = 10.0 ** (np.floor(np.log10(abs(p))) - digits + 1)
+                assert abs(val - p) <= 2.0 ** -8 * abs(p) + 0.5 * last_unit, (hh["label"], n, val)
+
+
+@pytest.mark.parametrize("path", ["halves", "one_level", "valu_f32_d64"])
+def test_growing_and_shrinking_gates(path):
+    """g of either sign (the interface takes any real g): per token g ~
+    U(-0.05, 0.05), so the state both decays and grows."""
+    dtype, D = ("f32", 64) if path == "valu_f32_d64" else ("bf16", 128)
+    if path == "one_level":
+        os.environ["SGLA_ONE_LEVEL"] = "1"
+    set_segments(256, 2)
+    say("chunk_fwd mixed-sign g", path)
+    inp = W.make_prefill(2, 900, 4, D, D, dtype, "lightning", seed=53, device="cuda",
+                         init="normal")
+    gen = torch.Generator(device="cuda").manual_seed(53)
+    inp["g"] = (torch.rand(inp["g"].shape, generator=gen, device="cuda") - 0.5) * 0.1
+    o, S = run_gpu(inp)
+    compare(inp, o, S, dtype, "mixed-sign g " + path, starts=[0, 256, 512, 768])

@@ -285,3 +285,32 @@ def test_gdn_varlen_sampled():
     check(host(S[:, heads]), rS, "bf16", "gdn varlen 64k states", bf16_out=False)
     check_windows(host(o[0][:, heads]), ro[0], [int(c) for c in cu[:-1]], "bf16",
                   "gdn varlen 64k o", ends=[int(c) for c in cu[1:]])
+
+
+def test_gdn_per_head_constant_decay():
+    """The gated delta rule with the lightning layer's spread of per-head
+    constant decays (blueprint page, section "B2 lightning-attn (Simple GLA)":
+    -0.917 .. -0.0001), chunked prefill and decode steps from its final state."""
+    say("gdn constant per-head decay B=2 T=700 H=8")
+    H = 8
+    inp = W.make_prefill(2, 700, H, 128, 128, "bf16", "gdn", seed=71, device="cuda",
+                         init="normal", with_beta=True)
+    gg = torch.tensor(-0.917 * (0.0001 / 0.917) ** (np.arange(H) / (H - 1)),
+                      dtype=torch.float32, device="cuda")
+    inp["g"] = gg.view(1, 1, H).expand_as(inp["g"]).contiguous()
+    o, S = sgla.gdn_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                              initial_state=inp["initial_state"])
+    torch.cuda.synchronize()
+    ro, rS = oracle_gdn(inp)
+    check(host(o), ro, "bf16", "gdn constant decay o")
+    check(host(S), rS, "bf16", "gdn constant decay state", bf16_out=False)
+    d = W.make_decode(2, H, 128, 128, 4, "bf16", "gdn", seed=72, device="cuda", with_beta=True)
+    g = gg.view(1, H).expand(2, H).contiguous()
+    state = S.clone()
+    ref = np.ascontiguousarray(rS.astype(np.float64))
+    for i in range(4):
+        od = sgla.gdn_recurrent_step(d["q"][i], d["k"][i], d["v"][i], g, d["beta"][i], state)
+        torch.cuda.synchronize()
+        ro_i = GDN.step(host(d["q"][i]), host(d["k"][i]), host(d["v"][i]), host(g),
+                        host(d["beta"][i]), ref, d["scale"])
+        check(host(od), ro_i, "bf16", "gdn constant decay step %d" % i)

@@ -53,24 +53,39 @@ def test_step_equals_one_token_chunk(dtype):
     check(host(state), host(S_chunk), dtype, "step vs chunk state", bf16_out=False)
 
 
-def test_workload_decode_sampled():
+def test_workload_decode_every_state():
     """The batched-decode workload (256 x 32 heads, 64 steps), in the launch
-    configuration the benchmark times; the oracle follows 24 sampled
-    (sequence, head) states through all 64 steps."""
-    say("recurrent_step workload N=256 H=32 D=128 64 steps seed=4 (24 sampled states)")
+    configuration the benchmark times; the oracle follows every one of the
+    8192 (sequence, head) states through all 64 steps."""
+    say("recurrent_step workload N=256 H=32 D=128 64 steps seed=4 (every state)")
     d = W.make_workload("decode_bf16_n256_h32_d128_x64", seed=4, device="cuda")
     state = d["state"]
-    rng = np.random.default_rng(4)
-    rows = rng.choice(256, size=8, replace=False)
-    heads = rng.choice(32, size=3, replace=False)
-    ref = host(state[rows][:, heads]).astype(np.float64)  # [8, 3, D, D]
-    ref = np.ascontiguousarray(ref)
+    ref = np.ascontiguousarray(host(state).astype(np.float64))  # [256, 32, D, D]
     for i in range(64):
         o = sgla.recurrent_step(d["q"][i], d["k"][i], d["v"][i], d["g"][i], state,
                                 scale=d["scale"])
-        sel = lambda t: host(t[rows][:, heads])
-        ro = oracle.step(sel(d["q"][i]), sel(d["k"][i]), sel(d["v"][i]), sel(d["g"][i]), ref,
+        ro = oracle.step(host(d["q"][i]), host(d["k"][i]), host(d["v"][i]), host(d["g"][i]), ref,
                          d["scale"])
-        check(host(o[rows][:, heads]), ro, "bf16", "decode step %d o" % i)
+        check(host(o), ro, "bf16", "decode step %d o" % i)
     torch.cuda.synchronize()
-    check(host(state[rows][:, heads]), ref, "bf16", "decode final states", bf16_out=False)
+    check(host(state), ref, "bf16", "decode final states", bf16_out=False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_step_per_head_constant_decay(dtype):
+    """The per-head constant decays of the lightning layer (blueprint page,
+    section "B2 lightning-attn (Simple GLA)": -0.917 .. -0.0001), 20 steps."""
+    say("recurrent_step constant per-head decay", dtype)
+    N, H, steps = 6, 8, 20
+    d = W.make_decode(N, H, 128, 128, steps, dtype, "lightning", seed=61, device="cuda")
+    gg = -0.917 * (0.0001 / 0.917) ** (np.arange(H) / (H - 1))
+    g = torch.tensor(gg, dtype=torch.float32, device="cuda").view(1, H).expand(N, H).contiguous()
+    state = d["state"].clone()
+    ref = np.ascontiguousarray(host(state).astype(np.float64))
+    for i in range(steps):
+        o = sgla.recurrent_step(d["q"][i], d["k"][i], d["v"][i], g, state, scale=d["scale"])
+        ro = oracle.step(host(d["q"][i]), host(d["k"][i]), host(d["v"][i]), host(g), ref,
+                         d["scale"])
+        torch.cuda.synchronize()
+        check(host(o), ro, dtype, "step %d o" % i)
+    check(host(state), ref, dtype, "constant decay states", bf16_out=False)
