@@ -58,7 +58,7 @@ constexpr int L_SX = L_A + 8192;      // fp32 partials of Q S [block cc 2][token
 constexpr int L_O = L_SX + 16384;     // output staging [64 rows][128 B], swizzled as o_off
 constexpr int L_F = L_O + 8192;       // per wave: G[64] and exp(G_last - G)[64], fp32
 constexpr int L_BYTES = L_F + 4 * 512;
-static_assert(2 * L_BYTES <= 160 * 1024, "two workgroups must fit one compute unit's LDS");
+static_assert(2 * L_BYTES <= kLdsPerCU, "two workgroups must fit one compute unit's LDS");
 
 // Q and K tiles (64 rows of 256 bytes): 16-byte chunk c of row r sits at
 // chunk c ^ qk_sw(r), and the two 8-byte halves of every chunk of a row with

@@ -61,6 +61,9 @@ constexpr int PRO_ROT = 1792;
 constexpr int PRO_ROT32 = 2304;
 constexpr int PRO_BASE = 2816;   // per wave: turns of its 4 rows x 64 frequencies (4 x 1 KiB)
 constexpr int PRO_BYTES = PRO_BASE + 4 * 1024;
+// Two workgroups per CU (amdgpu_waves_per_eu(2), four waves each).
+static_assert(2 * (LDS_OUT + PRO_BYTES) <= kLdsPerCU, "two output workgroups must fit one CU's LDS");
+static_assert(2 * (LDS_STATE + PRO_BYTES) <= kLdsPerCU, "two state workgroups must fit one CU's LDS");
 
 // The prologue of one 16-byte piece (8 consecutive dims 8c .. 8c+7 of a
 // 128-dim row, c = lane & 15) held by each of the 16 lanes of a DPP row:

@@ -24,6 +24,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int64_t *__restrict__ c
                                                    SeqEntry *__restrict__ seqs) {
     __shared__ int32_t sbuf[256];
     __shared__ int32_t carry;
+    static_assert(sizeof(sbuf) + sizeof(carry) <= kLdsPerCU, "the workgroup must fit one CU's LDS");
     const int tid = threadIdx.x;
     const int64_t ttot = cu ? (int64_t)T : (int64_t)B * T;
     if (tid == 0) carry = 0;

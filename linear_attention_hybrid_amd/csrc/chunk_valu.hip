@@ -50,6 +50,9 @@ __global__ __launch_bounds__(256) void chunk_valu_kernel(ChunkParams p) {
     __shared__ float Ss[DK][kBV + 1];
     __shared__ float Gs[kChunk], eGs[kChunk], eLs[kChunk];
     __shared__ float glast_s;
+    static_assert(sizeof(Qs) + sizeof(Ks) + sizeof(Vs) + sizeof(As) + sizeof(Ss) + 3 * sizeof(Gs) +
+                      sizeof(float) <= kLdsPerCU,
+                  "the workgroup must fit one CU's LDS");
 
     // Carried-in state of this segment.
     const int64_t sl = (int64_t)DK * DV;

@@ -59,6 +59,7 @@ constexpr int P_B = P_G + 256;
 constexpr int P_E = P_B + 256;     // exp(G) per token
 constexpr int P_X = P_E + 256;     // per-wave 16 x 16 fp32 scratch block (4 x 1280 B)
 constexpr int P_BYTES = P_X + 4 * 1280;
+static_assert(2 * P_BYTES <= kLdsPerCU, "two prep workgroups must fit one CU's LDS");
 // T in 16 x 16 fp32 blocks (I, J), I >= J, rows of 80 bytes (20 floats: the
 // 16 rows of a block start 4 banks apart), in the K rows region once K K^T
 // is done.
@@ -387,6 +388,7 @@ constexpr int H_XL = H_XH + 2048;     // low part
 constexpr int H_E = H_XL + 2048;      // exp(G_last - G)[64], one copy per compute wave
 constexpr int H_CW = 2;               // compute waves
 constexpr int H_BYTES = H_E + H_CW * 256;
+static_assert(H_BYTES <= kLdsPerCU, "the chain workgroup must fit one CU's LDS");
 constexpr int H_MOVERS = 4;           // waves that move data (after the compute waves)
 constexpr int H_THREADS = 64 * (H_CW + H_MOVERS);
 // Mover roles: every mover takes 16 / H_MOVERS of the W and of the k pieces;
@@ -704,6 +706,7 @@ constexpr int O_A = 32768;   // scores A[64 i][128 B], bf16 high part
 constexpr int O_AL = 40960;  // low part
 constexpr int O_G = 49152;   // G[64] fp32
 constexpr int O_BYTES = O_G + 256;
+static_assert(3 * O_BYTES <= kLdsPerCU, "three output workgroups must fit one CU's LDS");
 
 // One (chunk, head) per workgroup, all chunks at once:
 // O = scale ((Q * exp(G)) S + lower(Q K^T * Gamma) new_v), with S (the state

@@ -38,6 +38,8 @@ __global__ __launch_bounds__(256) void gdn_step_kernel(
 
     __shared__ float qs[DK], ks[DK], vs[DV];
     __shared__ f32x4 red_u[RG][CG], red_o[RG][CG];
+    static_assert(sizeof(qs) + sizeof(ks) + sizeof(vs) + sizeof(red_u) + sizeof(red_o) <= kLdsPerCU / 4,
+                  "four workgroups must fit one CU's LDS");
     if (tid < DK) {
         qs[tid] = load_elem(q, (int64_t)row * DK + tid);
         ks[tid] = load_elem(k, (int64_t)row * DK + tid);

@@ -88,6 +88,7 @@ __global__ __launch_bounds__(NT) void out_norm_gate_kernel(const T *o,  // may e
     }
     // Row sum: within each wave, then across the four waves through LDS.
     __shared__ float part[NT / 64];
+    static_assert(sizeof(part) <= kLdsPerCU / 8, "eight workgroups must fit one CU's LDS");
     ss = row16_sum(ss);
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);

@@ -104,6 +104,8 @@ __global__ __launch_bounds__(256) void recurrent_step_kernel(
 
     __shared__ float qs[DK], ks[DK], vs[DV];
     __shared__ float red[RG][CG][VEC];
+    static_assert(sizeof(qs) + sizeof(ks) + sizeof(vs) + sizeof(red) <= kLdsPerCU / 4,
+                  "four workgroups must fit one CU's LDS");
     if (PRO) {
         if (tid < 128) {
             const int l = tid & 63;

@@ -7,6 +7,10 @@
 namespace sgla {
 
 constexpr int kChunk = 64;  // tokens per chunk (the chunk size the pages use)
+// LDS of one gfx950 compute unit, shared by the workgroups resident on it.
+// Every kernel states its footprint against this with a static_assert, times
+// the workgroups per CU it is built to run with.
+constexpr int kLdsPerCU = 160 * 1024;
 
 // One segment of one sequence: a run of whole chunks handled by one
 // workgroup column. Built on the device from cu_seqlens (or from B x T).
