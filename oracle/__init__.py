@@ -37,13 +37,14 @@ def compile_source(src: str, out: str) -> str:
 
 def build(force: bool = True) -> str:
     """Compile ``sgla_oracle.c`` into ``oracle/libsgla_oracle.so`` (and the
-    delta-rule oracle, ``gdn_oracle.c``, beside it)."""
+    delta-rule oracles, ``gdn_oracle.c`` and ``kda_oracle.c``, beside it)."""
     if force or not os.path.exists(LIBRARY):
         compile_source(SOURCE, LIBRARY)
-    gdn_src = os.path.join(_HERE, "gdn_oracle.c")
-    gdn_lib = os.path.join(_HERE, "libgdn_oracle.so")
-    if force or not os.path.exists(gdn_lib):
-        compile_source(gdn_src, gdn_lib)
+    for name in ("gdn_oracle", "kda_oracle"):
+        src = os.path.join(_HERE, name + ".c")
+        lib = os.path.join(_HERE, "lib%s.so" % name)
+        if force or not os.path.exists(lib):
+            compile_source(src, lib)
     return LIBRARY
 
 
