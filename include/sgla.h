@@ -451,6 +451,27 @@ sgla_status sgla_gdn_recurrent_step(const void *q, const void *k, const void *v,
                                     const int32_t *state_indices, void *out, int N, int H, int Dk,
                                     int Dv, float scale, sgla_dtype dtype, void *stream);
 
+/*
+ * sgla_kda_recurrent_step — one decode token per row of the gated delta rule
+ * with one gate per key dimension (KDA; page "Formulas and code for adapting
+ * inference to GDN/KDA linear modules", section 2.1: the recurrent kernel's
+ * KDA branch loads a gate vector over the key dims and scales each state row
+ * by the exponential of its own dim's gate; the rest of the step is the GDN
+ * step above):
+ *
+ *     S[i][:] <- exp(g_t[i]) S[i][:]   (i = 0 .. Dk-1)
+ *     u = k_t^T S ;  S <- S + beta_t k_t (v_t - u)^T ;  o_t = scale q_t^T S
+ *
+ * Arguments: as sgla_gdn_recurrent_step, except
+ *   g      [N, H, Dk] fp32 (row-major, 4-byte aligned): the token's gate per
+ *          key dim (any real value; the exponential must stay in fp32 range).
+ * Returns as sgla_recurrent_step. Allocates nothing.
+ */
+sgla_status sgla_kda_recurrent_step(const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, float *state,
+                                    const int32_t *state_indices, void *out, int N, int H, int Dk,
+                                    int Dv, float scale, sgla_dtype dtype, void *stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *sgla_status_string(sgla_status s);
 

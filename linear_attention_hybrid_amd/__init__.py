@@ -26,6 +26,10 @@ The gated delta rule (GDN), with a per-token write strength beta:
 
     o, S = gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None)
     o    = gdn_recurrent_step(q, k, v, g, beta, state, state_indices=None)
+
+and with one gate per key dim (KDA: g [.., H, Dk]):
+
+    o    = kda_recurrent_step(q, k, v, g, beta, state, state_indices=None)
 """
 from __future__ import annotations
 
@@ -38,6 +42,7 @@ import torch
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_qk_norm_rope", "recurrent_step_qk_norm_rope",
            "recurrent_step_ex", "out_norm_gate", "gdn_chunk_fwd", "gdn_recurrent_step",
+           "kda_recurrent_step",
            "chunk_workspace_size", "gdn_workspace_size", "validate_cu_seqlens", "qk_norm_rope",
            "status_string", "library", "library_path", "exported_symbols", "SglaError"]
 
@@ -91,6 +96,9 @@ def library():
         lib.sgla_gdn_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf,
                                                 ci, vp]
         lib.sgla_gdn_recurrent_step.restype = ci
+        lib.sgla_kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf,
+                                                ci, vp]
+        lib.sgla_kda_recurrent_step.restype = ci
         zp = ctypes.POINTER(ctypes.c_size_t)
         lib.sgla_chunk_fwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, zp]
         lib.sgla_chunk_fwd_workspace_size.restype = ci
@@ -340,7 +348,8 @@ def chunk_fwd_qk_norm_rope(q, k, v, g, q_weight, k_weight, pos_offset=None, thet
     return a["out"], a["final_state"]
 
 
-def _step_args(q, k, v, g, state, state_indices, scale, out, allow_bf16_state=False):
+def _step_args(q, k, v, g, state, state_indices, scale, out, allow_bf16_state=False,
+               gate_per_dim=False):
     if q.dim() != 3:
         raise ValueError("q must be [N, H, Dk]")
     N, H, Dk = q.shape
@@ -353,7 +362,7 @@ def _step_args(q, k, v, g, state, state_indices, scale, out, allow_bf16_state=Fa
     _check(q, "q", q.dtype, (N, H, Dk), device)
     _check(k, "k", q.dtype, (N, H, Dk), device)
     _check(v, "v", q.dtype, (N, H, Dv), device)
-    _check(g, "g", torch.float32, (N, H), device)
+    _check(g, "g", torch.float32, (N, H, Dk) if gate_per_dim else (N, H), device)
     if state.dim() != 4:
         raise ValueError("state must be [slots, H, Dk, Dv]")
     if state.dtype not in _DTYPE or (state.dtype != torch.float32 and not allow_bf16_state):
@@ -505,4 +514,22 @@ def gdn_recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=None, 
                                                _stream(device))
     if st != SGLA_OK:
         raise SglaError("sgla_gdn_recurrent_step", st)
+    return a["out"]
+
+
+def kda_recurrent_step(q, k, v, g, beta, state, state_indices=None, scale=None, out=None):
+    """One decode step of the gated delta rule with one gate per key dim
+    (KDA), updating the fp32 ``state`` pool in place: arguments as
+    ``gdn_recurrent_step`` except g [N, H, Dk] fp32. Returns o [N, H, Dv] in
+    v's dtype."""
+    a = _step_args(q, k, v, g, state, state_indices, scale, out, gate_per_dim=True)
+    device = a["device"]
+    _check(beta, "beta", torch.float32, tuple(q.shape[:2]), device)
+    with torch.cuda.device(device):
+        st = library().sgla_kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                               _ptr(state), _ptr(state_indices), _ptr(a["out"]),
+                                               *a["sizes"], a["scale"], _DTYPE[q.dtype],
+                                               _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_kda_recurrent_step", st)
     return a["out"]

@@ -1,11 +1,15 @@
-// Fused decode step of the gated delta rule (GDN): one token per row, state
-// updated in place through the row -> slot map.
+// Fused decode step of the gated delta rule (GDN, and KDA with one gate per
+// key dim): one token per row, state updated in place through the row ->
+// slot map.
 //
 // Per (row, head) (page "Formulas and code for adapting inference to GDN/KDA
 // linear modules", section 1.1 "Recursive Formulas"; the decay is applied
 // before the memory read, as in the page's chunkwise form):
 //
 //   S <- exp(g) S ;  u = k^T S ;  S <- S + beta k (v - u)^T ;  o = scale q^T S
+//
+// With per-dim gates (section 2.1, the recurrent kernel's KDA branch) g is a
+// vector over the key dims and row i of S is scaled by exp(g[i]).
 //
 // Like the Simple GLA step this is one read and one write of the fp32 state
 // with little arithmetic, built for HBM bandwidth: one workgroup per (row,
@@ -21,7 +25,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <typename Tin, int DK, int DV>
+template <typename Tin, int DK, int DV, bool KDA>
 __global__ __launch_bounds__(256) void gdn_step_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
@@ -36,16 +40,18 @@ __global__ __launch_bounds__(256) void gdn_step_kernel(
     const int tid = threadIdx.x;
     const int64_t slot = idx ? (int64_t)idx[n] : (int64_t)n;
 
-    __shared__ float qs[DK], ks[DK], vs[DV];
+    __shared__ float qs[DK], ks[DK], vs[DV], es[KDA ? DK : 1];
     __shared__ f32x4 red_u[RG][CG], red_o[RG][CG];
-    static_assert(sizeof(qs) + sizeof(ks) + sizeof(vs) + sizeof(red_u) + sizeof(red_o) <= kLdsPerCU / 4,
+    static_assert(sizeof(qs) + sizeof(ks) + sizeof(vs) + sizeof(es) + sizeof(red_u) + sizeof(red_o) <=
+                      kLdsPerCU / 4,
                   "four workgroups must fit one CU's LDS");
     if (tid < DK) {
         qs[tid] = load_elem(q, (int64_t)row * DK + tid);
         ks[tid] = load_elem(k, (int64_t)row * DK + tid);
+        if (KDA) es[tid] = __expf(g[(int64_t)row * DK + tid]);
     }
     if (tid < DV) vs[tid] = load_elem(v, (int64_t)row * DV + tid);
-    const float alpha = __expf(g[row]);
+    const float alpha = KDA ? 1.f : __expf(g[row]);
     const float b = beta[row];
 
     const int cg = tid % CG;
@@ -59,7 +65,7 @@ __global__ __launch_bounds__(256) void gdn_step_kernel(
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int m = 0; m < RPT; ++m) {
-        reg[m] *= alpha;
+        reg[m] *= KDA ? es[rg + RG * m] : alpha;
         const float kr = ks[rg + RG * m];
         acc.x = fmaf(kr, reg[m].x, acc.x);
         acc.y = fmaf(kr, reg[m].y, acc.y);
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(256) void gdn_step_kernel(
     }
 }
 
-template <typename Tin>
+template <typename Tin, bool KDA>
 hipError_t launch_dims(const void *q, const void *k, const void *v, const float *g,
                        const float *beta, float *state, const int32_t *idx, void *out, int N,
                        int H, int Dk, int Dv, float scale, hipStream_t st) {
@@ -111,13 +117,13 @@ hipError_t launch_dims(const void *q, const void *k, const void *v, const float 
     const Tin *vp = static_cast<const Tin *>(v);
     Tin *op = static_cast<Tin *>(out);
     if (Dk == 128 && Dv == 128)
-        hipLaunchKernelGGL((gdn_step_kernel<Tin, 128, 128>), grid, block, 0, st, qp, kp, vp, g, beta, state, idx, op, H, scale);
+        hipLaunchKernelGGL((gdn_step_kernel<Tin, 128, 128, KDA>), grid, block, 0, st, qp, kp, vp, g, beta, state, idx, op, H, scale);
     else if (Dk == 128 && Dv == 64)
-        hipLaunchKernelGGL((gdn_step_kernel<Tin, 128, 64>), grid, block, 0, st, qp, kp, vp, g, beta, state, idx, op, H, scale);
+        hipLaunchKernelGGL((gdn_step_kernel<Tin, 128, 64, KDA>), grid, block, 0, st, qp, kp, vp, g, beta, state, idx, op, H, scale);
     else if (Dk == 64 && Dv == 128)
-        hipLaunchKernelGGL((gdn_step_kernel<Tin, 64, 128>), grid, block, 0, st, qp, kp, vp, g, beta, state, idx, op, H, scale);
+        hipLaunchKernelGGL((gdn_step_kernel<Tin, 64, 128, KDA>), grid, block, 0, st, qp, kp, vp, g, beta, state, idx, op, H, scale);
     else
-        hipLaunchKernelGGL((gdn_step_kernel<Tin, 64, 64>), grid, block, 0, st, qp, kp, vp, g, beta, state, idx, op, H, scale);
+        hipLaunchKernelGGL((gdn_step_kernel<Tin, 64, 64, KDA>), grid, block, 0, st, qp, kp, vp, g, beta, state, idx, op, H, scale);
     return hipGetLastError();
 }
 
@@ -125,10 +131,15 @@ hipError_t launch_dims(const void *q, const void *k, const void *v, const float 
 
 hipError_t launch_gdn_step(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *state, const int32_t *idx, void *out, int N,
-                           int H, int Dk, int Dv, float scale, bool bf16, hipStream_t st) {
+                           int H, int Dk, int Dv, float scale, bool bf16, bool per_dim_gate,
+                           hipStream_t st) {
     if (N == 0) return hipSuccess;
-    if (bf16) return launch_dims<uint16_t>(q, k, v, g, beta, state, idx, out, N, H, Dk, Dv, scale, st);
-    return launch_dims<float>(q, k, v, g, beta, state, idx, out, N, H, Dk, Dv, scale, st);
+    if (per_dim_gate) {
+        if (bf16) return launch_dims<uint16_t, true>(q, k, v, g, beta, state, idx, out, N, H, Dk, Dv, scale, st);
+        return launch_dims<float, true>(q, k, v, g, beta, state, idx, out, N, H, Dk, Dv, scale, st);
+    }
+    if (bf16) return launch_dims<uint16_t, false>(q, k, v, g, beta, state, idx, out, N, H, Dk, Dv, scale, st);
+    return launch_dims<float, false>(q, k, v, g, beta, state, idx, out, N, H, Dk, Dv, scale, st);
 }
 
 }  // namespace sgla

@@ -621,6 +621,26 @@ sgla_status gdn_chunk_fwd(const void *q, const void *k, const void *v, const flo
     return hip_status(e);
 }
 
+// One delta-rule decode token per row (GDN: g [N, H]; KDA: g [N, H, Dk]).
+sgla_status delta_step(const void *q, const void *k, const void *v, const float *g,
+                       const float *beta, float *state, const int32_t *state_indices, void *out,
+                       int N, int H, int Dk, int Dv, float scale, sgla_dtype dtype, bool kda,
+                       void *stream) {
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (N < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
+    if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
+    if ((int64_t)N * H > ((int64_t)1 << 31) - 1) return SGLA_ERR_INVALID_ARG;
+    if (N == 0) return SGLA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !out) return SGLA_ERR_INVALID_ARG;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) ||
+        misaligned(beta, 4) || misaligned(state) || misaligned(out) ||
+        misaligned(state_indices, 4))
+        return SGLA_ERR_INVALID_ARG;
+    return hip_status(launch_gdn_step(q, k, v, g, beta, state, state_indices, out, N, H, Dk, Dv,
+                                      scale, dtype == SGLA_BF16, kda,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -663,18 +683,16 @@ sgla_status sgla_gdn_recurrent_step(const void *q, const void *k, const void *v,
                                     const float *beta, float *state,
                                     const int32_t *state_indices, void *out, int N, int H, int Dk,
                                     int Dv, float scale, sgla_dtype dtype, void *stream) {
-    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
-    if (N < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
-    if (!head_size_ok(Dk) || !head_size_ok(Dv)) return SGLA_ERR_UNSUPPORTED;
-    if ((int64_t)N * H > ((int64_t)1 << 31) - 1) return SGLA_ERR_INVALID_ARG;
-    if (N == 0) return SGLA_OK;
-    if (!q || !k || !v || !g || !beta || !state || !out) return SGLA_ERR_INVALID_ARG;
-    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) ||
-        misaligned(beta, 4) || misaligned(state) || misaligned(out) ||
-        misaligned(state_indices, 4))
-        return SGLA_ERR_INVALID_ARG;
-    return hip_status(launch_gdn_step(q, k, v, g, beta, state, state_indices, out, N, H, Dk, Dv,
-                                      scale, dtype == SGLA_BF16, static_cast<hipStream_t>(stream)));
+    return delta_step(q, k, v, g, beta, state, state_indices, out, N, H, Dk, Dv, scale, dtype,
+                      false, stream);
+}
+
+sgla_status sgla_kda_recurrent_step(const void *q, const void *k, const void *v, const float *g,
+                                    const float *beta, float *state,
+                                    const int32_t *state_indices, void *out, int N, int H, int Dk,
+                                    int Dv, float scale, sgla_dtype dtype, void *stream) {
+    return delta_step(q, k, v, g, beta, state, state_indices, out, N, H, Dk, Dv, scale, dtype,
+                      true, stream);
 }
 
 }  // extern "C"

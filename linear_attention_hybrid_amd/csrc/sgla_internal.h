@@ -209,9 +209,11 @@ hipError_t launch_recurrent_step(const void *q, const void *k, const void *v, co
                                  const StepPrologue &pro, hipStream_t st);
 
 hipError_t launch_gdn_chunk(const GdnParams &p, hipStream_t st);
+// per_dim_gate: g is [N, H, Dk] (KDA), else [N, H].
 hipError_t launch_gdn_step(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *state, const int32_t *idx, void *out, int N,
-                           int H, int Dk, int Dv, float scale, bool bf16, hipStream_t st);
+                           int H, int Dk, int Dv, float scale, bool bf16, bool per_dim_gate,
+                           hipStream_t st);
 
 // Map a linear workgroup id onto (unit, sub) so that the `nsub` workgroups of
 // one unit land on the same XCD (ids are dealt to the 8 XCDs round-robin) and

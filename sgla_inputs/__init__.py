@@ -26,6 +26,9 @@ the per-head RMSNorm and RoPE, cast to bf16):
   sigmoid): q, k rows ~ N(0, 1) scaled to unit L2 norm; v ~ N(0, 1); gate
   input x ~ N(4, 1); with ``with_beta`` a write strength beta = sigmoid(b),
   b ~ N(0, 1), per token and head (fp32), drawn after everything else.
+* ``"kda"``       : as ``"gdn"``, but the gate input x, and so g, has one value
+  per key dim (the page's section 2.1: the KDA branch loads a gate vector over
+  the key dims): x ~ N(4, 1) per (token, head, dim), g [.., H, Dk].
 
 In all of them, the per-token per-head log-decay is g = log(sigmoid(x)) in fp32, so
 every decay factor exp(g) lies in (0, 1). Initial states, when present, are
@@ -115,7 +118,7 @@ def _draw_qk(shape_tokens, H, D, preset, gen, device, out_dtype):
         x = torch.randn((e - s, H, D), generator=gen, device=device, dtype=torch.float32)
         if preset == "lightning":
             x = _unit_rms(x)
-        elif preset == "gdn":
+        elif preset in ("gdn", "kda"):
             x = x * torch.rsqrt(x.pow(2).sum(dim=-1, keepdim=True) + RMS_EPS)
         elif preset == "raw":
             f = torch.randn((e - s, H, 1), generator=gen, device=device, dtype=torch.float32)
@@ -145,7 +148,7 @@ def _draw_plain(shape_tokens, inner, gen, device, out_dtype, mean=0.0, std=1.0):
 
 
 def gate_mean(preset: str) -> float:
-    return {"gaussian": 3.0, "lightning": 4.0, "raw": 4.0, "gdn": 4.0}[preset]
+    return {"gaussian": 3.0, "lightning": 4.0, "raw": 4.0, "gdn": 4.0, "kda": 4.0}[preset]
 
 
 def make_prefill(B, T, H, Dk, Dv, dtype="bf16", preset="lightning", seed=0, device="cpu",
@@ -153,7 +156,7 @@ def make_prefill(B, T, H, Dk, Dv, dtype="bf16", preset="lightning", seed=0, devi
     """Inputs for one chunked-forward call.
 
     Returns a dict with q, k [B, T, H, Dk]; v [B, T, H, Dv] (dtype); g [B, T, H]
-    fp32; initial_state [N, H, Dk, Dv] fp32 or None; cu_seqlens int64 tensor or
+    fp32 ([B, T, H, Dk] for the ``"kda"`` preset); initial_state [N, H, Dk, Dv] fp32 or None; cu_seqlens int64 tensor or
     None; scale = 1/sqrt(Dk). With ``cu_seqlens`` B must be 1 and T the total.
     ``init`` is None (zero state) or "normal" (N(0, 0.02^2)). With
     ``with_beta`` also beta [B, T, H] fp32 in (0, 1).
@@ -173,7 +176,8 @@ def make_prefill(B, T, H, Dk, Dv, dtype="bf16", preset="lightning", seed=0, devi
     q = _draw_qk(BT, H, Dk, preset, gen, device, tdt)
     k = _draw_qk(BT, H, Dk, preset, gen, device, tdt)
     v = _draw_plain(BT, (H, Dv), gen, device, tdt)
-    x = _draw_plain(BT, (H,), gen, device, torch.float32, mean=gate_mean(preset))
+    gshape = (H, Dk) if preset == "kda" else (H,)
+    x = _draw_plain(BT, gshape, gen, device, torch.float32, mean=gate_mean(preset))
     g = F.logsigmoid(x)
     S0 = None
     if init == "normal":
@@ -185,7 +189,8 @@ def make_prefill(B, T, H, Dk, Dv, dtype="bf16", preset="lightning", seed=0, devi
     if with_beta:
         beta = torch.sigmoid(_draw_plain(BT, (H,), gen, device, torch.float32)).view(B, T, H)
     return dict(
-        q=q.view(B, T, H, Dk), k=k.view(B, T, H, Dk), v=v.view(B, T, H, Dv), g=g.view(B, T, H),
+        q=q.view(B, T, H, Dk), k=k.view(B, T, H, Dk), v=v.view(B, T, H, Dv),
+        g=g.view((B, T) + gshape),
         initial_state=S0, beta=beta,
         cu_seqlens=None if cu_np is None else torch.from_numpy(cu_np).to(device),
         scale=1.0 / math.sqrt(Dk), dtype=dtype, preset=preset, seed=seed,
@@ -196,7 +201,8 @@ def make_decode(N, H, Dk, Dv, steps, dtype="bf16", preset="lightning", seed=0, d
                 pos0=100000, slots=None, with_state=True, with_beta=False):
     """Inputs for ``steps`` successive decode steps of N sequences.
 
-    Returns q, k [steps, N, H, Dk]; v [steps, N, H, Dv]; g [steps, N, H] fp32;
+    Returns q, k [steps, N, H, Dk]; v [steps, N, H, Dv]; g [steps, N, H] fp32
+    ([steps, N, H, Dk] for the ``"kda"`` preset);
     state [slots or N, H, Dk, Dv] fp32 ~ N(0, 0.02^2); scale; pos [steps, N]
     int32, step i of every sequence at position pos0 + i. With ``with_beta``
     also beta [steps, N, H] fp32 (drawn after each step's gate).
@@ -214,7 +220,8 @@ def make_decode(N, H, Dk, Dv, steps, dtype="bf16", preset="lightning", seed=0, d
         qs.append(_draw_qk(N, H, Dk, preset, gen, device, tdt))
         ks.append(_draw_qk(N, H, Dk, preset, gen, device, tdt))
         vs.append(_draw_plain(N, (H, Dv), gen, device, tdt))
-        x = _draw_plain(N, (H,), gen, device, torch.float32, mean=gate_mean(preset))
+        x = _draw_plain(N, (H, Dk) if preset == "kda" else (H,), gen, device, torch.float32,
+                        mean=gate_mean(preset))
         gs.append(F.logsigmoid(x))
         if with_beta:
             bs.append(torch.sigmoid(_draw_plain(N, (H,), gen, device, torch.float32)))
