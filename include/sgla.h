@@ -452,6 +452,67 @@ sgla_status sgla_gdn_recurrent_step(const void *q, const void *k, const void *v,
                                     int Dv, float scale, sgla_dtype dtype, void *stream);
 
 /*
+ * sgla_kda_chunk_fwd — chunked prefill of the gated delta rule with one gate
+ * per key dimension (KDA) over whole sequences (page "Formulas and code for
+ * adapting inference to GDN/KDA linear modules", section 1.2's chunkwise
+ * formulas with the gate made a vector over the key dims, as section 2.1's
+ * KDA branch does; section 2.1 for the call: chunk_kda takes q, k, v, g,
+ * beta, an initial state per sequence, returns the final state, and packs
+ * sequences by cumulative offsets). Per chunk of 64 tokens, with G[a][d] the
+ * cumulative gate sum of key dim d:
+ *
+ *     M[a][b] = sum_d k_a[d] k_b[d] exp(G[a][d] - G[b][d])  (a > b)
+ *     T = (I + diag(beta) M)^-1,  W = T (diag(beta) K * exp(G)),  U = T diag(beta) V
+ *     new_v = U - W S,  O = scale ((Q * exp(G)) S + L new_v)  (L as M with q_a, a >= b)
+ *     S = diag(exp(G_last)) S + (K * exp(G_last - G))^T new_v
+ *
+ * which equals the token-by-token recurrence of sgla_kda_recurrent_step.
+ *
+ * Arguments: as sgla_gdn_chunk_fwd, except
+ *   g      [B, T, H, Dk] fp32 (packed [T, H, Dk] with cu_seqlens), 4-byte
+ *          aligned: each token's gate per key dim. Any real values whose
+ *          partial sums inside a 64-token chunk keep exp() within fp32 range.
+ * dtype SGLA_F32 or SGLA_BF16 (q, k, v, out); Dk, Dv in {64, 128}; all
+ * arithmetic is fp32.
+ *
+ * Memory: the chunkwise form keeps per chunk and head its W, U,
+ * K * exp(G_last - G), new_v and start state in device memory between its
+ * kernels (fp32; 192.5 KiB at Dk = Dv = 128), so the call needs a caller
+ * workspace: sgla_kda_chunk_fwd returns SGLA_ERR_WORKSPACE whenever there are
+ * tokens to process (use sgla_kda_chunk_fwd_ex), and otherwise (B = 0, or
+ * T = 0 with the final state copied) succeeds without one. Returns as
+ * sgla_chunk_fwd.
+ */
+sgla_status sgla_kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *initial_state, void *out,
+                               float *final_state, const int64_t *cu_seqlens, int B, int T, int H,
+                               int Dk, int Dv, float scale, sgla_dtype dtype, void *stream);
+
+/*
+ * sgla_kda_chunk_fwd_workspace_size — bytes of workspace sgla_kda_chunk_fwd_ex
+ * needs: 256 + (tables with varlen) + (chunks * H) * (2 * 64 * Dk + 64 * Dv +
+ * Dk + 64 * Dv + Dk * Dv) * 4 bytes, each part rounded up to 256, where
+ * chunks is B * ceil(T / 64), or T / 64 + B + 1 with varlen (a bound over
+ * every cu_seqlens). Arguments and return codes as
+ * sgla_chunk_fwd_workspace_size.
+ */
+sgla_status sgla_kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                              sgla_dtype dtype, int varlen, size_t *bytes);
+
+/*
+ * sgla_kda_chunk_fwd_ex — sgla_kda_chunk_fwd with a caller-owned workspace
+ * (256-byte aligned, workspace_bytes at least the size query's answer, or
+ * SGLA_ERR_WORKSPACE; contents need no initialisation; overlapping calls need
+ * different workspaces; word 0 receives the cu_seqlens check under
+ * SGLA_VALIDATE as for sgla_chunk_fwd_ex). Allocates nothing.
+ */
+sgla_status sgla_kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, const float *initial_state, void *out,
+                                  float *final_state, const int64_t *cu_seqlens, int B, int T,
+                                  int H, int Dk, int Dv, float scale, sgla_dtype dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * sgla_kda_recurrent_step — one decode token per row of the gated delta rule
  * with one gate per key dimension (KDA; page "Formulas and code for adapting
  * inference to GDN/KDA linear modules", section 2.1: the recurrent kernel's

@@ -29,6 +29,7 @@ The gated delta rule (GDN), with a per-token write strength beta:
 
 and with one gate per key dim (KDA: g [.., H, Dk]):
 
+    o, S = kda_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None)
     o    = kda_recurrent_step(q, k, v, g, beta, state, state_indices=None)
 """
 from __future__ import annotations
@@ -42,7 +43,7 @@ import torch
 
 __all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_qk_norm_rope", "recurrent_step_qk_norm_rope",
            "recurrent_step_ex", "out_norm_gate", "gdn_chunk_fwd", "gdn_recurrent_step",
-           "kda_recurrent_step",
+           "kda_recurrent_step", "kda_chunk_fwd", "kda_workspace_size",
            "chunk_workspace_size", "gdn_workspace_size", "validate_cu_seqlens", "qk_norm_rope",
            "status_string", "library", "library_path", "exported_symbols", "SglaError"]
 
@@ -99,6 +100,9 @@ def library():
         lib.sgla_kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, cf,
                                                 ci, vp]
         lib.sgla_kda_recurrent_step.restype = ci
+        lib.sgla_kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci,
+                                           cf, ci, vp]
+        lib.sgla_kda_chunk_fwd.restype = ci
         zp = ctypes.POINTER(ctypes.c_size_t)
         lib.sgla_chunk_fwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, ci, zp]
         lib.sgla_chunk_fwd_workspace_size.restype = ci
@@ -117,6 +121,11 @@ def library():
         lib.sgla_gdn_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci,
                                               ci, cf, ci, vp, ctypes.c_size_t, vp]
         lib.sgla_gdn_chunk_fwd_ex.restype = ci
+        lib.sgla_kda_chunk_fwd_workspace_size.argtypes = [ci, ci, ci, ci, ci, ci, ci, zp]
+        lib.sgla_kda_chunk_fwd_workspace_size.restype = ci
+        lib.sgla_kda_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci,
+                                              ci, cf, ci, vp, ctypes.c_size_t, vp]
+        lib.sgla_kda_chunk_fwd_ex.restype = ci
         lib.sgla_status_string.argtypes = [ci]
         lib.sgla_status_string.restype = ctypes.c_char_p
         lib.sgla_version.argtypes = []
@@ -159,7 +168,7 @@ def _check(t, name, dtype, shape, device):
 
 
 def _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
-                output_final_state):
+                output_final_state, gate_per_dim=False):
     if q.dim() != 4:
         raise ValueError("q must be [B, T, H, Dk]")
     B, T, H, Dk = q.shape
@@ -172,7 +181,7 @@ def _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
     _check(q, "q", q.dtype, (B, T, H, Dk), device)
     _check(k, "k", q.dtype, (B, T, H, Dk), device)
     _check(v, "v", q.dtype, (B, T, H, Dv), device)
-    _check(g, "g", torch.float32, (B, T, H), device)
+    _check(g, "g", torch.float32, (B, T, H, Dk) if gate_per_dim else (B, T, H), device)
     N = B
     if cu_seqlens is not None:
         if B != 1:
@@ -219,6 +228,17 @@ def gdn_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16, varlen=False):
                                                       ctypes.byref(n))
     if st != SGLA_OK:
         raise SglaError("sgla_gdn_chunk_fwd_workspace_size", st)
+    return int(n.value)
+
+
+def kda_workspace_size(B, T, H, Dk, Dv, dtype=torch.bfloat16, varlen=False):
+    """Bytes of workspace ``sgla_kda_chunk_fwd_ex`` takes for these sizes."""
+    n = ctypes.c_size_t(0)
+    st = library().sgla_kda_chunk_fwd_workspace_size(int(B), int(T), int(H), int(Dk), int(Dv),
+                                                      _DTYPE[dtype], int(bool(varlen)),
+                                                      ctypes.byref(n))
+    if st != SGLA_OK:
+        raise SglaError("sgla_kda_chunk_fwd_workspace_size", st)
     return int(n.value)
 
 
@@ -497,6 +517,32 @@ def gdn_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=N
                                              _stream(device))
     if st != SGLA_OK:
         raise SglaError("sgla_gdn_chunk_fwd_ex", st)
+    return a["out"], a["final_state"]
+
+
+def kda_chunk_fwd(q, k, v, g, beta, initial_state=None, cu_seqlens=None, scale=None, out=None,
+                  final_state=None, output_final_state=True, workspace="auto"):
+    """Chunked prefill of the gated delta rule with one gate per key dim
+    (KDA): arguments and results as ``gdn_chunk_fwd``, except g [B, T, H, Dk]
+    fp32. fp32 or bf16 inputs, Dk and Dv in {64, 128}. ``workspace`` ("auto"
+    or a uint8 tensor of ``kda_workspace_size`` bytes) is required when there
+    are tokens.
+    """
+    a = _chunk_args(q, k, v, g, initial_state, cu_seqlens, scale, out, final_state,
+                    output_final_state, gate_per_dim=True)
+    device = a["device"]
+    _check(beta, "beta", torch.float32, tuple(g.shape[:3]), device)
+    with torch.cuda.device(device):
+        nb = kda_workspace_size(*a["sizes"], dtype=q.dtype, varlen=cu_seqlens is not None) \
+            if isinstance(workspace, str) else 0
+        wp, wn, _keep = _workspace(workspace, nb, device)
+        st = library().sgla_kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                             _ptr(initial_state), _ptr(a["out"]),
+                                             _ptr(a["final_state"]), _ptr(cu_seqlens),
+                                             *a["sizes"], a["scale"], _DTYPE[q.dtype], wp, wn,
+                                             _stream(device))
+    if st != SGLA_OK:
+        raise SglaError("sgla_kda_chunk_fwd_ex", st)
     return a["out"], a["final_state"]
 
 

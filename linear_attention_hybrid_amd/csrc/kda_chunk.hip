@@ -1,0 +1,510 @@
+// Chunked gated delta rule with one gate per key dimension (KDA), in fp32 on
+// the vector ALUs: q, k, v in fp32 or bf16, gates g [tokens, H, Dk] and write
+// strengths beta [tokens, H] in fp32, Dk and Dv in {64, 128}, chunks of 64
+// tokens, fp32 state.
+//
+// Per chunk (page "Formulas and code for adapting inference to GDN/KDA linear
+// modules", section 1.2, the chunkwise formulas, with the gate made a vector
+// over the key dims as in section 2.1's KDA branch), with G[a][d] the
+// inclusive cumulative sum of g over the chunk's tokens for key dim d:
+//
+//   M[a][b] = sum_d K[a][d] K[b][d] exp(G[a][d] - G[b][d])        (a > b)
+//   T       = (I + diag(beta) M)^-1                              (UT transform)
+//   W       = T (diag(beta) K * exp(G)),   U = T diag(beta) V
+//   new_v   = U - W S
+//   L[a][b] = sum_d Q[a][d] K[b][d] exp(G[a][d] - G[b][d])        (a >= b)
+//   O       = scale ((Q * exp(G)) S + L new_v)
+//   S       = diag(exp(G_last)) S + (K * exp(G_last - G))^T new_v
+//
+// Three kernels, as for the scalar gate: kda_prep_kernel forms W, U,
+// K * exp(G_last - G) and exp(G_last) for every (chunk, head) at once;
+// kda_chain_kernel walks each (sequence, head, block of 16 value columns)
+// through its chunks, leaving every chunk's start state and new_v behind; and
+// kda_output_kernel forms every chunk's output at once from them.
+//
+// The pairwise factors exp(G[a][d] - G[b][d]) of M and L are never formed as
+// exp(G[a]) exp(-G[b]), which overflows once a chunk's gates sum past about
+// -88. Inside each 16-token block they are taken directly; between block I
+// (queries a) and an earlier token b they are split at the block's first
+// token c, exp(G[a] - G[c]) exp(G[c] - G[b]), two factors that each lie in
+// (0, 1] when g <= 0, so every block pair costs one exponential per element
+// and token rather than per pair. T is inverted in 16 x 16 blocks: each
+// diagonal block by forward substitution, the blocks below it block row by
+// block row, T_IJ = -T_II sum_K A_IK T_KJ.
+#include "mfma_tile.h"
+
+namespace sgla {
+
+namespace {
+
+constexpr int KC = kChunk;  // tokens per chunk
+constexpr int KP = KC + 1;  // padded token stride of transposed tiles
+
+// Per chunk and head workspace tile, in floats: W [64][Dk], then
+// K * exp(G_last - G) [64][Dk], U [64][Dv], exp(G_last) [Dk].
+__host__ __device__ constexpr int64_t tile_floats(int dk, int dv) {
+    return 2 * (int64_t)KC * dk + (int64_t)KC * dv + dk;
+}
+
+__device__ __forceinline__ int64_t tile_index(const KdaParams &p, int64_t s, int h) {
+    return (s * p.c.H + h);
+}
+
+// ---- prep: one workgroup per (chunk, head).
+template <typename Tin, int DK, int DV>
+__global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
+    constexpr int NT = 512;
+    __shared__ float Kt[DK][KP];       // K^T; later (diag(beta) K * exp(G))^T
+    __shared__ float Gt[DK][KP];       // G^T
+    __shared__ float Vs[KC][DV + 1];   // diag(beta) V
+    __shared__ float Ms[KC][KP];       // A = diag(beta) M below the diagonal; partial sums above
+    __shared__ float Xs[KC][DK + 1];   // K decayed to a reference token; then T
+    __shared__ float bs[KC];
+    static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xs) + sizeof(bs) <=
+                      kLdsPerCU,
+                  "the workgroup must fit one CU's LDS");
+    const int H = p.c.H;
+    const int s = blockIdx.x / H;
+    const int h = blockIdx.x - s * H;
+    if (s >= p.c.nseg_max) return;
+    const SegEntry se = seg_at(p.c, s);
+    if (se.len < 0) return;
+    const int n = se.len;
+    const int tid = threadIdx.x;
+    const Tin *__restrict__ kg = static_cast<const Tin *>(p.c.k);
+    const Tin *__restrict__ vg = static_cast<const Tin *>(p.c.v);
+
+    // Tiles of the chunk; rows past its end are zeros (zero gate, beta, key).
+    for (int i = tid; i < KC * DK; i += NT) {
+        const int a = i / DK, d = i - a * DK;
+        float kv = 0.f, gv = 0.f;
+        if (a < n) {
+            const int64_t row = (se.tok0 + a) * H + h;
+            kv = load_elem(kg, row * DK + d);
+            gv = p.c.g[row * DK + d];
+        }
+        Kt[d][a] = kv;
+        Gt[d][a] = gv;
+    }
+    if (tid < KC) bs[tid] = tid < n ? p.beta[(se.tok0 + tid) * H + h] : 0.f;
+    __syncthreads();
+    for (int i = tid; i < KC * DV; i += NT) {
+        const int a = i / DV, j = i - a * DV;
+        Vs[a][j] = a < n ? bs[a] * load_elem(vg, ((se.tok0 + a) * H + h) * DV + j) : 0.f;
+    }
+    // G: cumulative sums over the tokens, one wave per key dim, lane = token.
+    {
+        const int w = tid >> 6, l = tid & 63;
+        for (int d = w; d < DK; d += NT / 64) Gt[d][l] = wave_prefix_sum(Gt[d][l]);
+    }
+    __syncthreads();
+
+    // A inside the diagonal 16 x 16 blocks (a > b), exponent taken directly.
+    for (int i = tid; i < 4 * 120; i += NT) {
+        const int blk = i / 120, r = i - blk * 120;
+        int ai = 1;
+        while ((ai + 1) * ai / 2 <= r) ++ai;
+        const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai - 1) / 2);
+        float acc = 0.f;
+        for (int d = 0; d < DK; ++d) acc = fmaf(Kt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
+        Ms[a][b] = bs[a] * acc;
+    }
+    // A below the diagonal blocks: block row I against tokens b < c = 16 I,
+    // split at c.
+    for (int I = 1; I < 4; ++I) {
+        const int c = 16 * I;
+        __syncthreads();  // the previous block row's products are done with Xs
+        for (int i = tid; i < (c + 16) * DK; i += NT) {
+            const int a = i / DK, d = i - a * DK;
+            const float e = a < c ? Gt[d][c] - Gt[d][a] : Gt[d][a] - Gt[d][c];
+            Xs[a][d] = Kt[d][a] * __expf(e);
+        }
+        __syncthreads();
+        for (int i = tid; i < 16 * c; i += NT) {
+            const int ai = i / c, b = i - ai * c;
+            const int a = c + ai;
+            float acc = 0.f;
+            for (int d = 0; d < DK; ++d) acc = fmaf(Xs[a][d], Xs[b][d], acc);
+            Ms[a][b] = bs[a] * acc;
+        }
+    }
+    __syncthreads();
+
+    // T = (I + A)^-1 into Xs[a][b]. Diagonal blocks: waves 0-3, one block
+    // each, lanes 0-15 the columns; row r of block w from the rows above it.
+    const int w = tid >> 6, l = tid & 63;
+    if (w < 4 && l < 16)
+        for (int i = 0; i < 16; ++i) Xs[16 * w + i][16 * w + l] = i == l ? 1.f : 0.f;
+    __syncthreads();
+    for (int i = 1; i < 16; ++i) {
+        if (w < 4 && l < i) {
+            const int r = 16 * w + i, j = 16 * w + l;
+            float acc = 0.f;
+            for (int m = j; m < r; ++m) acc = fmaf(Ms[r][m], Xs[m][j], acc);
+            Xs[r][j] = -acc;
+        }
+        __syncthreads();
+    }
+    // Blocks below the diagonal, block row by block row: P_IJ = sum_K A_IK
+    // T_KJ (K = J .. I-1) into Ms's unused upper part at (16 J + x, 16 I + y),
+    // then T_IJ = -T_II P_IJ.
+    for (int I = 1; I < 4; ++I) {
+        for (int i = tid; i < 256 * I; i += NT) {
+            const int J = i >> 8, x = (i >> 4) & 15, y = i & 15;
+            float acc = 0.f;
+            for (int m = 16 * J; m < 16 * I; ++m) acc = fmaf(Ms[16 * I + x][m], Xs[m][16 * J + y], acc);
+            Ms[16 * J + x][16 * I + y] = acc;
+        }
+        __syncthreads();
+        for (int i = tid; i < 256 * I; i += NT) {
+            const int J = i >> 8, x = (i >> 4) & 15, y = i & 15;
+            float acc = 0.f;
+            for (int z = 0; z <= x; ++z) acc = fmaf(Xs[16 * I + x][16 * I + z], Ms[16 * J + z][16 * I + y], acc);
+            Xs[16 * I + x][16 * J + y] = -acc;
+        }
+        __syncthreads();
+    }
+
+    float *tile = p.tiles + tile_index(p, s, h) * tile_floats(DK, DV);
+    // K * exp(G_last - G) and exp(G_last) for the chain (rows past the end
+    // have zero keys and gates, so G_last is the last row's G).
+    for (int i = tid; i < KC * DK; i += NT) {
+        const int a = i / DK, d = i - a * DK;
+        tile[KC * DK + i] = Kt[d][a] * __expf(Gt[d][KC - 1] - Gt[d][a]);
+    }
+    if (tid < DK) tile[2 * KC * DK + KC * DV + tid] = __expf(Gt[tid][KC - 1]);
+    __syncthreads();
+    for (int i = tid; i < KC * DK; i += NT) {
+        const int d = i / KC, a = i - d * KC;
+        Kt[d][a] *= bs[a] * __expf(Gt[d][a]);
+    }
+    __syncthreads();
+    // W = T X and U = T (diag(beta) V), 4 tokens x 4 columns per thread; T is
+    // lower triangular (its upper part in Xs holds stale values).
+    for (int i = tid; i < (KC / 4) * (DK / 4); i += NT) {
+        const int at = i / (DK / 4), a0 = 4 * at, d0 = 4 * (i - at * (DK / 4));
+        float acc[4][4] = {};
+        for (int b = 0; b <= a0 + 3; ++b) {
+            float tv[4], xv[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) tv[x] = b <= a0 + x ? Xs[a0 + x][b] : 0.f;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) xv[y] = Kt[d0 + y][b];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(tv[x], xv[y], acc[x][y]);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            *reinterpret_cast<float4 *>(tile + (a0 + x) * DK + d0) =
+                make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+    }
+    for (int i = tid; i < (KC / 4) * (DV / 4); i += NT) {
+        const int at = i / (DV / 4), a0 = 4 * at, j0 = 4 * (i - at * (DV / 4));
+        float acc[4][4] = {};
+        for (int b = 0; b <= a0 + 3; ++b) {
+            float tv[4], vv[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) tv[x] = b <= a0 + x ? Xs[a0 + x][b] : 0.f;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) vv[y] = Vs[b][j0 + y];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(tv[x], vv[y], acc[x][y]);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            *reinterpret_cast<float4 *>(tile + 2 * KC * DK + (a0 + x) * DV + j0) =
+                make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+    }
+}
+
+// ---- chain: one workgroup per (sequence, head, block of VB value columns),
+// through the sequence's chunks in order. The next chunk's W, K * exp(G_last
+// - G), U block and exp(G_last) are loaded into registers while the current
+// one is worked on.
+constexpr int VB = 16;
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void kda_chain_kernel(KdaParams p) {
+    constexpr int NT = 256;
+    constexpr int PW = KC * DK / NT;  // floats of W (and of K * exp(..)) per thread
+    __shared__ float Ws[KC][DK + 1];
+    __shared__ float Kds[KC][DK + 1];
+    __shared__ float Ss[DK][VB + 1];
+    __shared__ float Us[KC][VB + 1];  // U block, then new_v block
+    __shared__ float eg[DK];
+    static_assert(2 * (sizeof(Ws) + sizeof(Kds) + sizeof(Ss) + sizeof(Us) + sizeof(eg)) <= kLdsPerCU,
+                  "two workgroups must fit one CU's LDS");
+    constexpr int NVB = DV / VB;
+    const int H = p.c.H;
+    const int vb = blockIdx.x % NVB;
+    const int nh = blockIdx.x / NVB;
+    const int n = nh / H;
+    const int h = nh - n * H;
+    if (n >= p.c.N) return;
+    const int tid = threadIdx.x;
+    const SeqEntry sq = seq_at(p.c, n);
+    const int64_t sl = (int64_t)DK * DV;
+    for (int i = tid; i < DK * VB; i += NT) {
+        const int d = i / VB, j = i - d * VB;
+        Ss[d][j] = p.c.s0 ? p.c.s0[((int64_t)n * H + h) * sl + (int64_t)d * DV + vb * VB + j] : 0.f;
+    }
+    const int64_t tf = tile_floats(DK, DV);
+    float rw[PW], rk[PW], ru[KC * VB / NT], re = 0.f;
+    auto load = [&](int64_t s) {
+        const float *tile = p.tiles + tile_index(p, s, h) * tf;
+#pragma unroll
+        for (int m = 0; m < PW; ++m) {
+            rw[m] = tile[m * NT + tid];
+            rk[m] = tile[KC * DK + m * NT + tid];
+        }
+#pragma unroll
+        for (int m = 0; m < KC * VB / NT; ++m) {
+            const int e = m * NT + tid, a = e / VB, j = e - a * VB;
+            ru[m] = tile[2 * KC * DK + a * DV + vb * VB + j];
+        }
+        if (tid < DK) re = tile[2 * KC * DK + KC * DV + tid];
+    };
+    if (sq.nseg > 0) load(sq.first);
+    for (int c = 0; c < sq.nseg; ++c) {
+        const int64_t s = sq.first + c;
+        __syncthreads();  // the previous chunk is done with the tiles
+#pragma unroll
+        for (int m = 0; m < PW; ++m) {
+            const int e = m * NT + tid, a = e / DK, d = e - a * DK;
+            Ws[a][d] = rw[m];
+            Kds[a][d] = rk[m];
+        }
+#pragma unroll
+        for (int m = 0; m < KC * VB / NT; ++m) {
+            const int e = m * NT + tid, a = e / VB, j = e - a * VB;
+            Us[a][j] = ru[m];
+        }
+        if (tid < DK) eg[tid] = re;
+        // This chunk's start state, for the output kernel.
+        for (int i = tid; i < DK * VB; i += NT) {
+            const int d = i / VB, j = i - d * VB;
+            p.sin[tile_index(p, s, h) * sl + (int64_t)d * DV + vb * VB + j] = Ss[d][j];
+        }
+        __syncthreads();
+        if (c + 1 < sq.nseg) load(s + 1);
+        // new_v = U - W S: token a = tid / 4, columns 4 (tid % 4) .. + 3.
+        {
+            const int a = tid >> 2, j0 = 4 * (tid & 3);
+            float acc[4];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) acc[y] = Us[a][j0 + y];
+            for (int d = 0; d < DK; ++d) {
+                const float wv = Ws[a][d];
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[y] = fmaf(-wv, Ss[d][j0 + y], acc[y]);
+            }
+            float *nv = p.nv + (tile_index(p, s, h) * KC + a) * DV + vb * VB + j0;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                Us[a][j0 + y] = acc[y];
+                nv[y] = acc[y];
+            }
+        }
+        __syncthreads();
+        // S = diag(exp(G_last)) S + (K * exp(G_last - G))^T new_v.
+        {
+            constexpr int TPR = NT / DK;        // threads per state row
+            constexpr int CPT = VB / TPR;       // columns per thread
+            const int d = tid / TPR, j0 = CPT * (tid - d * TPR);
+            float acc[CPT];
+#pragma unroll
+            for (int y = 0; y < CPT; ++y) acc[y] = eg[d] * Ss[d][j0 + y];
+            for (int a = 0; a < KC; ++a) {
+                const float kv = Kds[a][d];
+#pragma unroll
+                for (int y = 0; y < CPT; ++y) acc[y] = fmaf(kv, Us[a][j0 + y], acc[y]);
+            }
+#pragma unroll
+            for (int y = 0; y < CPT; ++y) Ss[d][j0 + y] = acc[y];
+        }
+    }
+    __syncthreads();
+    if (p.c.sfin)
+        for (int i = tid; i < DK * VB; i += NT) {
+            const int d = i / VB, j = i - d * VB;
+            p.c.sfin[((int64_t)n * H + h) * sl + (int64_t)d * DV + vb * VB + j] = Ss[d][j];
+        }
+}
+
+// ---- output: one workgroup per (chunk, head).
+template <typename Tin, int DK, int DV>
+__global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p) {
+    constexpr int NT = 512;
+    // LDS map (bytes): Q^T, K^T, G^T [DK][KP]; L [64][KP]; X [64][DK + 1]
+    // (sized for the larger of Dk and Dv).
+    // Once L is formed, the start state [DK][DV] takes the K^T and G^T space
+    // and new_v [64][DV + 1] the X space.
+    constexpr int O_QT = 0;
+    constexpr int O_KT = O_QT + DK * KP * 4;
+    constexpr int O_GT = O_KT + DK * KP * 4;
+    constexpr int O_L = O_GT + DK * KP * 4;
+    constexpr int O_X = O_L + KC * KP * 4;
+    constexpr int O_BYTES = O_X + KC * ((DK > DV ? DK : DV) + 1) * 4;
+    static_assert(DK * DV * 4 <= O_L - O_KT, "the start state must fit the K^T and G^T space");
+    static_assert(KC * (DV + 1) * 4 <= O_BYTES - O_X, "new_v must fit the X space");
+    static_assert(O_BYTES <= kLdsPerCU, "the workgroup must fit one CU's LDS");
+    __shared__ __attribute__((aligned(16))) char lds[O_BYTES];
+    auto Qt = reinterpret_cast<float(*)[KP]>(lds + O_QT);
+    auto Kt = reinterpret_cast<float(*)[KP]>(lds + O_KT);
+    auto Gt = reinterpret_cast<float(*)[KP]>(lds + O_GT);
+    auto Ls = reinterpret_cast<float(*)[KP]>(lds + O_L);
+    auto Xs = reinterpret_cast<float(*)[DK + 1]>(lds + O_X);
+    auto Sv = reinterpret_cast<float(*)[DV]>(lds + O_KT);
+    auto Nv = reinterpret_cast<float(*)[DV + 1]>(lds + O_X);
+
+    const int H = p.c.H;
+    const int s = blockIdx.x / H;
+    const int h = blockIdx.x - s * H;
+    if (s >= p.c.nseg_max) return;
+    const SegEntry se = seg_at(p.c, s);
+    if (se.len <= 0) return;
+    const int n = se.len;
+    const int tid = threadIdx.x;
+    const Tin *__restrict__ qg = static_cast<const Tin *>(p.c.q);
+    const Tin *__restrict__ kg = static_cast<const Tin *>(p.c.k);
+    Tin *__restrict__ og = static_cast<Tin *>(p.c.out);
+
+    for (int i = tid; i < KC * DK; i += NT) {
+        const int a = i / DK, d = i - a * DK;
+        float qv = 0.f, kv = 0.f, gv = 0.f;
+        if (a < n) {
+            const int64_t e = ((se.tok0 + a) * H + h) * DK + d;
+            qv = load_elem(qg, e);
+            kv = load_elem(kg, e);
+            gv = p.c.g[e];
+        }
+        Qt[d][a] = qv;
+        Kt[d][a] = kv;
+        Gt[d][a] = gv;
+    }
+    __syncthreads();
+    {
+        const int w = tid >> 6, l = tid & 63;
+        for (int d = w; d < DK; d += NT / 64) Gt[d][l] = wave_prefix_sum(Gt[d][l]);
+    }
+    __syncthreads();
+
+    // L inside the diagonal blocks (a >= b), exponent taken directly.
+    for (int i = tid; i < 4 * 136; i += NT) {
+        const int blk = i / 136, r = i - blk * 136;
+        int ai = 0;
+        while ((ai + 2) * (ai + 1) / 2 <= r) ++ai;
+        const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai + 1) / 2);
+        float acc = 0.f;
+        for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
+        Ls[a][b] = acc;
+    }
+    // L below the diagonal blocks, split at the block's first token c.
+    for (int I = 1; I < 4; ++I) {
+        const int c = 16 * I;
+        __syncthreads();
+        for (int i = tid; i < (c + 16) * DK; i += NT) {
+            const int a = i / DK, d = i - a * DK;
+            Xs[a][d] = a < c ? Kt[d][a] * __expf(Gt[d][c] - Gt[d][a])
+                             : Qt[d][a] * __expf(Gt[d][a] - Gt[d][c]);
+        }
+        __syncthreads();
+        for (int i = tid; i < 16 * c; i += NT) {
+            const int ai = i / c, b = i - ai * c;
+            const int a = c + ai;
+            float acc = 0.f;
+            for (int d = 0; d < DK; ++d) acc = fmaf(Xs[a][d], Xs[b][d], acc);
+            Ls[a][b] = acc;
+        }
+    }
+    __syncthreads();
+    // Q * exp(G) in place; then the start state and new_v over K^T, G^T, X.
+    for (int i = tid; i < KC * DK; i += NT) {
+        const int d = i / KC, a = i - d * KC;
+        Qt[d][a] *= __expf(Gt[d][a]);
+    }
+    __syncthreads();
+    const int64_t ti = tile_index(p, s, h);
+    {
+        const float4 *src = reinterpret_cast<const float4 *>(p.sin + ti * DK * DV);
+        for (int i = tid; i < DK * DV / 4; i += NT) reinterpret_cast<float4 *>(&Sv[0][0])[i] = src[i];
+        const float *nv = p.nv + ti * KC * DV;
+        for (int i = tid; i < KC * DV; i += NT) {
+            const int a = i / DV, j = i - a * DV;
+            Nv[a][j] = nv[i];
+        }
+    }
+    __syncthreads();
+    // O, 4 tokens x 4 value columns per thread.
+    for (int i = tid; i < (KC / 4) * (DV / 4); i += NT) {
+        const int at = i / (DV / 4), a0 = 4 * at, j0 = 4 * (i - at * (DV / 4));
+        float acc[4][4] = {};
+        for (int d = 0; d < DK; ++d) {
+            const float4 sv = *reinterpret_cast<const float4 *>(&Sv[d][j0]);
+            const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const float qv = Qt[d][a0 + x];
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(qv, svv[y], acc[x][y]);
+            }
+        }
+        for (int b = 0; b <= a0 + 3; ++b) {
+            float lv[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) lv[x] = b <= a0 + x ? Ls[a0 + x][b] : 0.f;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const float nvv = Nv[b][j0 + y];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) acc[x][y] = fmaf(lv[x], nvv, acc[x][y]);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            if (a0 + x >= n) continue;
+            const int64_t e = ((se.tok0 + a0 + x) * H + h) * DV + j0;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) store_elem(og, e + y, p.c.scale * acc[x][y]);
+        }
+    }
+}
+
+template <typename Tin, int DK, int DV>
+hipError_t launch_dims(const KdaParams &p, hipStream_t st) {
+    const unsigned units = (unsigned)((int64_t)p.c.nseg_max * p.c.H);
+    hipLaunchKernelGGL((kda_prep_kernel<Tin, DK, DV>), dim3(units), dim3(512), 0, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned chains = (unsigned)((int64_t)p.c.N * p.c.H * (DV / VB));
+    hipLaunchKernelGGL((kda_chain_kernel<DK, DV>), dim3(chains), dim3(256), 0, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kda_output_kernel<Tin, DK, DV>), dim3(units), dim3(512), 0, st, p);
+    return hipGetLastError();
+}
+
+template <typename Tin>
+hipError_t launch_typed(const KdaParams &p, hipStream_t st) {
+    if (p.dk == 128 && p.dv == 128) return launch_dims<Tin, 128, 128>(p, st);
+    if (p.dk == 128 && p.dv == 64) return launch_dims<Tin, 128, 64>(p, st);
+    if (p.dk == 64 && p.dv == 128) return launch_dims<Tin, 64, 128>(p, st);
+    return launch_dims<Tin, 64, 64>(p, st);
+}
+
+}  // namespace
+
+size_t kda_chunk_bytes(int dk, int dv) {
+    return (size_t)(tile_floats(dk, dv) + (int64_t)KC * dv + (int64_t)dk * dv) * sizeof(float);
+}
+
+hipError_t launch_kda_chunk(const KdaParams &p, bool bf16, hipStream_t st) {
+    if (p.c.nseg_max == 0 || p.c.N == 0) return hipSuccess;
+    return bf16 ? launch_typed<uint16_t>(p, st) : launch_typed<float>(p, st);
+}
+
+}  // namespace sgla

@@ -696,3 +696,147 @@ sgla_status sgla_kda_recurrent_step(const void *q, const void *k, const void *v,
 }
 
 }  // extern "C"
+
+namespace {
+
+// Workspace layout of the chunked KDA: a 256-byte header, the chunk tables
+// (with cu_seqlens), then per (chunk, head) the prep tile, new_v and the
+// chunk's start state.
+struct KdaPlan {
+    bool table = false;
+    int64_t nps = 1, nch = 0;
+    size_t off_segs = 0, off_seqs = 0, off_tiles = 0, off_nv = 0, off_sin = 0, bytes = 0;
+};
+
+sgla_status kda_plan(int B, int T, int H, int Dk, int Dv, bool varlen, KdaPlan &pl) {
+    const int64_t ttot = varlen ? (int64_t)T : (int64_t)B * T;
+    pl.table = varlen;
+    pl.nps = T == 0 ? 1 : ((int64_t)T + kChunk - 1) / kChunk;
+    pl.nch = varlen ? ttot / kChunk + B + 1 : (int64_t)B * pl.nps;
+    if (pl.nch * H > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+    size_t off = kWsHeader;
+    if (pl.table) {
+        pl.off_segs = off; off += round256((size_t)pl.nch * sizeof(SegEntry));
+        pl.off_seqs = off; off += round256((size_t)B * sizeof(SeqEntry));
+    }
+    const size_t units = (size_t)pl.nch * H;
+    const size_t tile = (size_t)(2 * kChunk * Dk + kChunk * Dv + Dk) * sizeof(float);
+    pl.off_tiles = off; off += round256(units * tile);
+    pl.off_nv = off; off += round256(units * kChunk * Dv * sizeof(float));
+    pl.off_sin = off; off += round256(units * Dk * Dv * sizeof(float));
+    pl.bytes = off;
+    return SGLA_OK;
+}
+
+sgla_status check_kda_args(const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, const float *initial_state, const void *out,
+                           const float *final_state, const int64_t *cu_seqlens, int B, int T,
+                           int H, int Dk, int Dv, sgla_dtype dtype) {
+    if (dtype != SGLA_F32 && dtype != SGLA_BF16) return SGLA_ERR_INVALID_ARG;
+    if (B < 0 || T < 0 || H < 1 || Dk < 1 || Dv < 1) return SGLA_ERR_INVALID_ARG;
+    if (!head_size_ok(Dk) || !head_size_ok(Dv) || H > kMaxHeads) return SGLA_ERR_UNSUPPORTED;
+    const int64_t ttot = cu_seqlens ? (int64_t)T : (int64_t)B * T;
+    if (ttot > ((int64_t)1 << 62) / ((int64_t)H * 128)) return SGLA_ERR_INVALID_ARG;
+    // The chain kernel runs Dv / 16 workgroups per (sequence, head).
+    if ((int64_t)B * H * (Dv / 16) > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
+    if (ttot > 0 && (!q || !k || !v || !g || !beta || !out)) return SGLA_ERR_INVALID_ARG;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) ||
+        misaligned(beta, 4) || misaligned(out) || misaligned(initial_state) ||
+        misaligned(final_state) || misaligned(cu_seqlens, 8))
+        return SGLA_ERR_INVALID_ARG;
+    return SGLA_OK;
+}
+
+sgla_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *initial_state, void *out,
+                          float *final_state, const int64_t *cu_seqlens, int B, int T, int H,
+                          int Dk, int Dv, float scale, sgla_dtype dtype, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+    sgla_status stt = check_kda_args(q, k, v, g, beta, initial_state, out, final_state, cu_seqlens,
+                                     B, T, H, Dk, Dv, dtype);
+    if (stt != SGLA_OK) return stt;
+    if (misaligned(workspace, 256)) return SGLA_ERR_INVALID_ARG;
+    const int64_t ttot = cu_seqlens ? (int64_t)T : (int64_t)B * T;
+    if (B == 0) return SGLA_OK;
+    if (ttot == 0 && !final_state) return SGLA_OK;
+    KdaPlan pl;
+    stt = kda_plan(B, T, H, Dk, Dv, cu_seqlens != nullptr, pl);
+    if (stt != SGLA_OK) return stt;
+    if (!workspace || pl.bytes > workspace_bytes) return SGLA_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+
+    KdaParams p{};
+    p.c.q = q;
+    p.c.k = k;
+    p.c.v = v;
+    p.c.g = g;
+    p.c.s0 = initial_state;
+    p.c.out = out;
+    p.c.sfin = final_state;
+    p.c.segs = pl.table ? reinterpret_cast<SegEntry *>(ws + pl.off_segs) : nullptr;
+    p.c.seqs = pl.table ? reinterpret_cast<SeqEntry *>(ws + pl.off_seqs) : nullptr;
+    p.c.H = H;
+    p.c.nseg_max = (int)pl.nch;
+    p.c.N = B;
+    p.c.scale = scale;
+    p.c.T = T;
+    p.c.seg_len = kChunk;
+    p.c.nps = (int)pl.nps;
+    p.c.rsub = 1;
+    p.beta = beta;
+    p.tiles = reinterpret_cast<float *>(ws + pl.off_tiles);
+    p.nv = reinterpret_cast<float *>(ws + pl.off_nv);
+    p.sin = reinterpret_cast<float *>(ws + pl.off_sin);
+    p.dk = Dk;
+    p.dv = Dv;
+    hipError_t e = hipSuccess;
+    if (cu_seqlens && getenv("SGLA_VALIDATE"))
+        e = launch_validate_cu(cu_seqlens, B, T, reinterpret_cast<int32_t *>(ws), st);
+    if (e == hipSuccess && pl.table)
+        e = launch_plan(cu_seqlens, B, T, kChunk, (int)pl.nch,
+                        reinterpret_cast<SegEntry *>(ws + pl.off_segs),
+                        reinterpret_cast<SeqEntry *>(ws + pl.off_seqs), st);
+    if (e == hipSuccess) e = launch_kda_chunk(p, dtype == SGLA_BF16, st);
+    return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+sgla_status sgla_kda_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                              sgla_dtype dtype, int varlen, size_t *bytes) {
+    if (!bytes) return SGLA_ERR_INVALID_ARG;
+    *bytes = 0;
+    sgla_status st = check_kda_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                    nullptr, nullptr, B, 0, H, Dk, Dv, dtype);
+    if (st != SGLA_OK) return st;
+    if (T < 0) return SGLA_ERR_INVALID_ARG;
+    const int64_t ttot = varlen ? (int64_t)T : (int64_t)B * T;
+    if (ttot > ((int64_t)1 << 62) / ((int64_t)H * 128)) return SGLA_ERR_INVALID_ARG;
+    if (B == 0) return SGLA_OK;
+    KdaPlan pl;
+    st = kda_plan(B, T, H, Dk, Dv, varlen != 0, pl);
+    if (st == SGLA_OK) *bytes = pl.bytes;
+    return st;
+}
+
+sgla_status sgla_kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta, const float *initial_state, void *out,
+                                  float *final_state, const int64_t *cu_seqlens, int B, int T,
+                                  int H, int Dk, int Dv, float scale, sgla_dtype dtype,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+    return kda_chunk_fwd(q, k, v, g, beta, initial_state, out, final_state, cu_seqlens, B, T, H,
+                         Dk, Dv, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+sgla_status sgla_kda_chunk_fwd(const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const float *initial_state, void *out,
+                               float *final_state, const int64_t *cu_seqlens, int B, int T, int H,
+                               int Dk, int Dv, float scale, sgla_dtype dtype, void *stream) {
+    return kda_chunk_fwd(q, k, v, g, beta, initial_state, out, final_state, cu_seqlens, B, T, H,
+                         Dk, Dv, scale, dtype, nullptr, 0, stream);
+}
+
+}  // extern "C"

@@ -209,6 +209,21 @@ hipError_t launch_recurrent_step(const void *q, const void *k, const void *v, co
                                  const StepPrologue &pro, hipStream_t st);
 
 hipError_t launch_gdn_chunk(const GdnParams &p, hipStream_t st);
+
+// Arguments of the chunked KDA kernels (kda_chunk.hip): the chunk table is
+// the segment table with one chunk per segment, as for GDN; g is [tokens, H,
+// Dk].
+struct KdaParams {
+    ChunkParams c;      // q, k, v, g, s0, out, sfin, segs, seqs, H, nseg_max, N, scale, T, nps
+    const float *beta;  // [tokens, H]
+    float *tiles;       // [nseg_max, H] of 2 * 64 * Dk + 64 * Dv + Dk floats: W, K * exp(G_last - G), U, exp(G_last)
+    float *nv;          // [nseg_max, H, 64, Dv] new_v of each chunk
+    float *sin;         // [nseg_max, H, Dk, Dv] start state of each chunk
+    int dk, dv;
+};
+// Workspace bytes per (chunk, head) of the chunked KDA kernels.
+size_t kda_chunk_bytes(int dk, int dv);
+hipError_t launch_kda_chunk(const KdaParams &p, bool bf16, hipStream_t st);
 // per_dim_gate: g is [N, H, Dk] (KDA), else [N, H].
 hipError_t launch_gdn_step(const void *q, const void *k, const void *v, const float *g,
                            const float *beta, float *state, const int32_t *idx, void *out, int N,

@@ -78,3 +78,116 @@ def test_kda_decode_workload_sampled():
         check(host(o[rows]), ro, "bf16", "kda decode step %d o" % i)
     torch.cuda.synchronize()
     check(host(state[rows]), ref, "bf16", "kda decode final states", bf16_out=False)
+
+
+def oracle_kda(inp, heads=None):
+    sel = (lambda t: t) if heads is None else (lambda t: t[:, :, heads])
+    S0 = inp["initial_state"]
+    if S0 is not None:
+        S0 = host(S0 if heads is None else S0[:, heads]).astype(np.float64)
+    cu = None if inp["cu_seqlens"] is None else inp["cu_seqlens"].cpu().numpy()
+    return KDA.forward(host(sel(inp["q"])), host(sel(inp["k"])), host(sel(inp["v"])),
+                       host(sel(inp["g"])), host(sel(inp["beta"])), inp["scale"],
+                       initial_state=S0, cu_seqlens=cu)
+
+
+def run_chunk(inp, **kw):
+    out = nan_like(tuple(inp["v"].shape), inp["v"].dtype)
+    o, S = sgla.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                              initial_state=inp["initial_state"], cu_seqlens=inp["cu_seqlens"],
+                              scale=inp["scale"], out=out, **kw)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def compare_chunk(inp, o, S, dtype, what, heads=None):
+    ro, rS = oracle_kda(inp, heads)
+    sel = (lambda t: t) if heads is None else (lambda t: t[:, :, heads])
+    check(host(sel(o)), ro, dtype, what + " o")
+    check(host(S if heads is None else S[:, heads]), rS, dtype, what + " final state",
+          bf16_out=False)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200, 333])
+@pytest.mark.parametrize("init", [None, "normal"])
+def test_kda_chunk_vs_oracle(dtype, T, init):
+    say("kda_chunk_fwd B=2 H=3 D=128 T=%d %s init=%s" % (T, dtype, init))
+    inp = W.make_prefill(2, T, 3, 128, 128, dtype, "kda", seed=T + 3 * (init is not None),
+                         device="cuda", init=init, with_beta=True)
+    o, S = run_chunk(inp)
+    compare_chunk(inp, o, S, dtype, "kda T=%d" % T)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_kda_chunk_head_sizes(dtype, dk, dv):
+    say("kda_chunk_fwd B=2 H=2 T=150", dtype, dk, dv)
+    inp = W.make_prefill(2, 150, 2, dk, dv, dtype, "kda", seed=dk + dv, device="cuda",
+                         init="normal", with_beta=True)
+    o, S = run_chunk(inp)
+    compare_chunk(inp, o, S, dtype, "kda %dx%d" % (dk, dv))
+
+
+def test_kda_chunk_varlen():
+    lengths = [0, 1, 63, 64, 65, 130, 7, 200]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    say("kda_chunk_fwd varlen", lengths)
+    inp = W.make_prefill(1, int(cu[-1]), 3, 128, 128, "bf16", "kda", seed=9, device="cuda",
+                         cu_seqlens=cu, init="normal", with_beta=True)
+    o, S = run_chunk(inp)
+    compare_chunk(inp, o, S, "bf16", "kda varlen")
+
+
+def test_kda_chunk_no_tokens_copies_state():
+    say("kda_chunk_fwd T=0")
+    inp = W.make_prefill(3, 0, 2, 128, 128, "bf16", "kda", seed=1, device="cuda", init="normal",
+                         with_beta=True)
+    o, S = run_chunk(inp)
+    assert torch.equal(S, inp["initial_state"])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_kda_chunk_per_dim_rates(dtype):
+    """Per-dim gate rates from -1e-4 to -5 per token: a chunk's gate sum
+    reaches -320 in the fastest dims, where exp(G) alone underflows and
+    exp(-G) overflows fp32; the slowest dims barely forget."""
+    say("kda_chunk_fwd per-dim rates", dtype)
+    B, T, H, D = 2, 300, 2, 128
+    inp = W.make_prefill(B, T, H, D, D, dtype, "kda", seed=31, device="cuda", init="normal",
+                         with_beta=True)
+    rate = torch.tensor(10.0 ** np.linspace(-4, np.log10(5.0), D), dtype=torch.float32,
+                        device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    inp["g"] = -(rate * (0.5 + torch.rand((B, T, H, D), generator=gen, device="cuda"))).contiguous()
+    o, S = run_chunk(inp)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    compare_chunk(inp, o, S, dtype, "kda per-dim rates")
+
+
+def test_kda_chunk_split_chain_and_step():
+    """Splitting a sequence and chaining the final state gives the same
+    result, and decode steps continue a prefill."""
+    say("kda_chunk_fwd split at 100 of 230, then 3 decode steps")
+    inp = W.make_prefill(2, 230, 3, 128, 128, "bf16", "kda", seed=5, device="cuda",
+                         init="normal", with_beta=True)
+    o, S = run_chunk(inp)
+    part = lambda x, sl: x[:, sl].contiguous()
+    a = dict(inp, **{key: part(inp[key], slice(0, 100)) for key in ("q", "k", "v", "g", "beta")})
+    b = dict(inp, **{key: part(inp[key], slice(100, 230)) for key in ("q", "k", "v", "g", "beta")})
+    oa, Sa = run_chunk(a)
+    b["initial_state"] = Sa
+    ob, Sb = run_chunk(b)
+    check(host(torch.cat([oa, ob], 1)), host(o), "bf16", "split o")
+    check(host(Sb), host(S), "bf16", "split state", bf16_out=False)
+
+
+def test_kda_prefill_workload_sampled():
+    """B=1, T=8192, H=32, D=128 in bf16 (the prefill shape), four sampled
+    heads checked against the oracle."""
+    say("kda_chunk_fwd B=1 T=8192 H=32 D=128 bf16 (4 sampled heads)")
+    inp = W.make_prefill(1, 8192, 32, 128, 128, "bf16", "kda", seed=2, device="cuda",
+                         with_beta=True)
+    o, S = run_chunk(inp)
+    heads = sorted(np.random.default_rng(2).choice(32, 4, replace=False).tolist())
+    compare_chunk(inp, o, S, "bf16", "kda prefill", heads=heads)
