@@ -54,6 +54,9 @@ DECODE_BF16 = DECODE + "+bf16_state"
 EPILOGUE = "out_norm_gate_bf16_8192x4096"
 GDN_PREFILL = "gdn_prefill_bf16_h32_t8192_d128"
 GDN_DECODE = "gdn_decode_bf16_n256_h32_d128_x64"
+KDA_PREFILL = "kda_prefill_bf16_h32_t8192_d128"
+KDA_DECODE = "kda_decode_bf16_n256_h32_d128_x64"
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector ALU, vendor figure
 # The kernels of one call of each workload, as rocprofv3 names them.
 CALL_KERNELS = {
     PREFILL: ["chunk_mfma_kernel<true, false>", "scan_kernel<128, 128>", "chunk_halves_kernel"],
@@ -67,7 +70,10 @@ CALL_KERNELS = {
     DECODE_BF16: ["recurrent_step_kernel<unsigned short, 128, 128, false, unsigned short>"],
     EPILOGUE: ["out_norm_gate_kernel<unsigned short, 2>"],
     GDN_PREFILL: ["gdn_prep_kernel", "gdn_chain_kernel", "gdn_output_kernel"],
-    GDN_DECODE: ["gdn_step_kernel<unsigned short, 128, 128>"],
+    GDN_DECODE: ["gdn_step_kernel<unsigned short, 128, 128, false>"],
+    KDA_PREFILL: ["kda_prep_kernel<unsigned short, 128, 128>", "kda_chain_kernel<128, 128>",
+                  "kda_output_kernel<unsigned short, 128, 128>"],
+    KDA_DECODE: ["gdn_step_kernel<unsigned short, 128, 128, true>"],
 }
 
 
@@ -84,6 +90,8 @@ WORKLOAD_SOURCES = {
     EPILOGUE: ["out_norm_gate.hip"],
     GDN_PREFILL: ["gdn_chunk.hip"],
     GDN_DECODE: ["gdn_step.hip"],
+    KDA_PREFILL: ["kda_chunk.hip", "chunk_plan.hip"],
+    KDA_DECODE: ["gdn_step.hip"],
 }
 SHARED_SOURCES = ["sgla_internal.h", "mfma_tile.h", "sgla_host.hip", "../build.py"]
 
@@ -406,7 +414,7 @@ def main():
                     help="timed passes of 64 decode steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["all", "prefill", "long", "varlen", "decode", "prologue",
-                                       "epilogue", "bf16-state", "gdn"], default="all")
+                                       "epilogue", "bf16-state", "gdn", "kda"], default="all")
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB elementwise pass (for counter calibration)")
@@ -588,6 +596,13 @@ def main():
         result["gdn"] = bench_gdn(args, torch, sgla, W, dev)
         if args.only == "gdn":
             e = result["gdn"]["prefill"]
+            result.update({"value": e["tokens_per_s"], "unit": "tokens/s",
+                           "ms_per_step": e["ms_per_call"],
+                           "config": {"workload": e["workload"]}, "roofline": e["roofline"]})
+    if args.only in ("all", "kda"):
+        result["kda"] = bench_kda(args, torch, sgla, W, dev)
+        if args.only == "kda":
+            e = result["kda"]["prefill"]
             result.update({"value": e["tokens_per_s"], "unit": "tokens/s",
                            "ms_per_step": e["ms_per_call"],
                            "config": {"workload": e["workload"]}, "roofline": e["roofline"]})
@@ -774,6 +789,81 @@ def bench_gdn(args, torch, sgla, W, dev):
                                   "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                                   "traffic": recorded_traffic(GDN_DECODE),
                                   "kernel": "sgla_gdn_recurrent_step",
+                                  "algorithmic_bytes_per_launch": nb, "avg_launch_ms": per_avg}}
+    del d, dout
+    torch.cuda.empty_cache()
+    return out
+
+
+def kda_prefill_flops(T, H, D):
+    """Algorithmic fp32 FLOPs of the chunked KDA per call (chunks of 64, Dk =
+    Dv = D): per chunk and head the per-dim-decayed products M (63 * 64 / 2
+    pairs), L (64 * 65 / 2), the triangular W = T X and U = T V (64 * 65 / 2
+    rows each), new_v = U - W S, the state update and the inter output (64 x D
+    x D each), the intra output L new_v (64 * 65 / 2), at 2 FLOPs per
+    multiply-add; the 64 x 64 triangular solve is left out."""
+    per = 2 * D * (2016 + 4 * 2080) + 3 * 2 * 64 * D * D
+    return per * (T // 64) * H
+
+
+def bench_kda(args, torch, sgla, W, dev):
+    """The gated delta rule with one gate per key dim (KDA) on the same
+    shapes: prefill B=1, T=8192, H=32, Dk=Dv=128 (sgla_kda_chunk_fwd, fp32
+    arithmetic on the vector ALUs) and the batched decode, 256 x 32 heads, 64
+    successive steps (sgla_kda_recurrent_step); "kda" inputs (L2-normalised q
+    and k, per-dim gates, beta = sigmoid(N(0, 1)))."""
+    out = {}
+    inp = W.make_prefill(1, 8192, 32, 128, 128, "bf16", "kda", seed=args.seed, device=dev,
+                         with_beta=True)
+    o = torch.empty_like(inp["v"])
+    fs = torch.empty((1, 32, 128, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(sgla.kda_workspace_size(1, 8192, 32, 128, 128), dtype=torch.uint8, device=dev)
+
+    def step():
+        sgla.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                           scale=inp["scale"], out=o, final_state=fs, workspace=ws)
+
+    _, region, per = time_calls(step, args.steps, args.warmup, torch)
+    per_avg = region / args.steps
+    flops = kda_prefill_flops(8192, 32, 128)
+    tf = flops / (per_avg * 1e-3) / 1e12
+    # prefill_bytes counts one gate float per token and head; KDA reads 128,
+    # and beta: 128 more floats per token and head.
+    nbytes = prefill_bytes(1, 8192, 32, 128, 128) + 8192 * 32 * 128 * 4
+    out["prefill"] = {"workload": KDA_PREFILL, "ms_per_call": per_avg,
+                      "tokens_per_s": 8192 / (per_avg * 1e-3),
+                      "per_call_ms": {"mean": per_avg, "median_single": median(per), "min_single": min(per)},
+                      "achieved_GBs": nbytes / (per_avg * 1e-3) / 1e9,
+                      "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": tf / FP32_VALU_PEAK_TFLOPS,
+                                   "traffic": recorded_traffic(KDA_PREFILL),
+                                   "kernel": "sgla_kda_chunk_fwd (whole call: per-chunk UT "
+                                             "transform, state chain, per-chunk output; fp32)",
+                                   "algorithmic_flops_per_launch": flops,
+                                   "avg_launch_ms": per_avg}}
+    del inp, o, fs, ws
+    torch.cuda.empty_cache()
+    d = W.make_decode(256, 32, 128, 128, 64, "bf16", "kda", seed=4, device=dev, with_beta=True)
+    dout = torch.empty((256, 32, 128), dtype=torch.bfloat16, device=dev)
+    counter = [0]
+
+    def dstep():
+        i = counter[0] % 64
+        counter[0] += 1
+        sgla.kda_recurrent_step(d["q"][i], d["k"][i], d["v"][i], d["g"][i], d["beta"][i],
+                                d["state"], scale=d["scale"], out=dout)
+
+    n_timed = 64 * args.decode_passes
+    _, region, per = time_calls(dstep, n_timed, 64, torch)
+    per_avg = region / n_timed
+    nb = decode_bytes(256, 32, 128, 128) + 256 * 32 * 128 * 4
+    gbs = nb / (per_avg * 1e-3) / 1e9
+    out["decode"] = {"workload": KDA_DECODE, "ms_per_step": per_avg,
+                     "tokens_per_s": 256 / (per_avg * 1e-3),
+                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                  "traffic": recorded_traffic(KDA_DECODE),
+                                  "kernel": "sgla_kda_recurrent_step",
                                   "algorithmic_bytes_per_launch": nb, "avg_launch_ms": per_avg}}
     del d, dout
     torch.cuda.empty_cache()

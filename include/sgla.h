@@ -469,7 +469,7 @@ sgla_status sgla_gdn_recurrent_step(const void *q, const void *k, const void *v,
  * which equals the token-by-token recurrence of sgla_kda_recurrent_step.
  *
  * Arguments: as sgla_gdn_chunk_fwd, except
- *   g      [B, T, H, Dk] fp32 (packed [T, H, Dk] with cu_seqlens), 4-byte
+ *   g      [B, T, H, Dk] fp32 (packed [T, H, Dk] with cu_seqlens), 16-byte
  *          aligned: each token's gate per key dim. Any real values whose
  *          partial sums inside a 64-token chunk keep exp() within fp32 range.
  * dtype SGLA_F32 or SGLA_BF16 (q, k, v, out); Dk, Dv in {64, 128}; all

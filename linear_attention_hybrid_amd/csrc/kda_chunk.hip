@@ -50,6 +50,57 @@ __device__ __forceinline__ int64_t tile_index(const KdaParams &p, int64_t s, int
     return (s * p.c.H + h);
 }
 
+// 16 bytes of a row as floats: 8 bf16 or 4 fp32 values.
+template <typename Tin>
+__device__ __forceinline__ void load_piece(const Tin *src, float *out) {
+    const uint4 u = *reinterpret_cast<const uint4 *>(src);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    if constexpr (sizeof(Tin) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            out[2 * e] = __uint_as_float(w[e] << 16);
+            out[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = __uint_as_float(w[e]);
+    }
+}
+
+// A chunk's rows of a [tokens, H, W] tensor (rows past n read as zeros),
+// moved through registers into LDS as tile[col][row] (TR) or tile[row][col]:
+// every thread issues all its 16-byte loads before its first LDS store, so
+// one chunk costs one memory latency.
+template <typename Tin, int W, int NT, bool TR, int STRIDE>
+__device__ __forceinline__ void stage_rows(const Tin *base, int64_t tok0, int H, int h, int n,
+                                           float *tile, int tid) {
+    constexpr int PE = 16 / sizeof(Tin);   // elements per piece
+    constexpr int PR = W / PE;             // pieces per row
+    constexpr int PT = (KC * PR + NT - 1) / NT;
+    float r[PT][PE];
+#pragma unroll
+    for (int m = 0; m < PT; ++m) {
+        const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
+        if (idx < KC * PR && a < n) {
+            load_piece(base + ((tok0 + a) * H + h) * W + pc * PE, r[m]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < PE; ++e) r[m][e] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < PT; ++m) {
+        const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
+        if (idx >= KC * PR) continue;
+#pragma unroll
+        for (int e = 0; e < PE; ++e) {
+            const int col = pc * PE + e;
+            if (TR) tile[col * STRIDE + a] = r[m][e];
+            else tile[a * STRIDE + col] = r[m][e];
+        }
+    }
+}
+
 // ---- prep: one workgroup per (chunk, head).
 template <typename Tin, int DK, int DV>
 __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
@@ -75,22 +126,14 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     const Tin *__restrict__ vg = static_cast<const Tin *>(p.c.v);
 
     // Tiles of the chunk; rows past its end are zeros (zero gate, beta, key).
-    for (int i = tid; i < KC * DK; i += NT) {
-        const int a = i / DK, d = i - a * DK;
-        float kv = 0.f, gv = 0.f;
-        if (a < n) {
-            const int64_t row = (se.tok0 + a) * H + h;
-            kv = load_elem(kg, row * DK + d);
-            gv = p.c.g[row * DK + d];
-        }
-        Kt[d][a] = kv;
-        Gt[d][a] = gv;
-    }
     if (tid < KC) bs[tid] = tid < n ? p.beta[(se.tok0 + tid) * H + h] : 0.f;
+    stage_rows<Tin, DK, NT, true, KP>(kg, se.tok0, H, h, n, &Kt[0][0], tid);
+    stage_rows<float, DK, NT, true, KP>(p.c.g, se.tok0, H, h, n, &Gt[0][0], tid);
+    stage_rows<Tin, DV, NT, false, DV + 1>(vg, se.tok0, H, h, n, &Vs[0][0], tid);
     __syncthreads();
     for (int i = tid; i < KC * DV; i += NT) {
         const int a = i / DV, j = i - a * DV;
-        Vs[a][j] = a < n ? bs[a] * load_elem(vg, ((se.tok0 + a) * H + h) * DV + j) : 0.f;
+        Vs[a][j] *= bs[a];
     }
     // G: cumulative sums over the tokens, one wave per key dim, lane = token.
     {
@@ -230,7 +273,7 @@ constexpr int VB = 16;
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void kda_chain_kernel(KdaParams p) {
     constexpr int NT = 256;
-    constexpr int PW = KC * DK / NT;  // floats of W (and of K * exp(..)) per thread
+    constexpr int PW = KC * DK / 4 / NT;  // float4 pieces of W (and of K * exp(..)) per thread
     __shared__ float Ws[KC][DK + 1];
     __shared__ float Kds[KC][DK + 1];
     __shared__ float Ss[DK][VB + 1];
@@ -253,13 +296,14 @@ __global__ __launch_bounds__(256) void kda_chain_kernel(KdaParams p) {
         Ss[d][j] = p.c.s0 ? p.c.s0[((int64_t)n * H + h) * sl + (int64_t)d * DV + vb * VB + j] : 0.f;
     }
     const int64_t tf = tile_floats(DK, DV);
-    float rw[PW], rk[PW], ru[KC * VB / NT], re = 0.f;
+    float4 rw[PW], rk[PW];
+    float ru[KC * VB / NT], re = 0.f;
     auto load = [&](int64_t s) {
         const float *tile = p.tiles + tile_index(p, s, h) * tf;
 #pragma unroll
         for (int m = 0; m < PW; ++m) {
-            rw[m] = tile[m * NT + tid];
-            rk[m] = tile[KC * DK + m * NT + tid];
+            rw[m] = reinterpret_cast<const float4 *>(tile)[m * NT + tid];
+            rk[m] = reinterpret_cast<const float4 *>(tile + KC * DK)[m * NT + tid];
         }
 #pragma unroll
         for (int m = 0; m < KC * VB / NT; ++m) {
@@ -274,9 +318,15 @@ __global__ __launch_bounds__(256) void kda_chain_kernel(KdaParams p) {
         __syncthreads();  // the previous chunk is done with the tiles
 #pragma unroll
         for (int m = 0; m < PW; ++m) {
-            const int e = m * NT + tid, a = e / DK, d = e - a * DK;
-            Ws[a][d] = rw[m];
-            Kds[a][d] = rk[m];
+            const int e = 4 * (m * NT + tid), a = e / DK, d = e - a * DK;
+            Ws[a][d] = rw[m].x;
+            Ws[a][d + 1] = rw[m].y;
+            Ws[a][d + 2] = rw[m].z;
+            Ws[a][d + 3] = rw[m].w;
+            Kds[a][d] = rk[m].x;
+            Kds[a][d + 1] = rk[m].y;
+            Kds[a][d + 2] = rk[m].z;
+            Kds[a][d + 3] = rk[m].w;
         }
 #pragma unroll
         for (int m = 0; m < KC * VB / NT; ++m) {
@@ -373,19 +423,9 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p) {
     const Tin *__restrict__ kg = static_cast<const Tin *>(p.c.k);
     Tin *__restrict__ og = static_cast<Tin *>(p.c.out);
 
-    for (int i = tid; i < KC * DK; i += NT) {
-        const int a = i / DK, d = i - a * DK;
-        float qv = 0.f, kv = 0.f, gv = 0.f;
-        if (a < n) {
-            const int64_t e = ((se.tok0 + a) * H + h) * DK + d;
-            qv = load_elem(qg, e);
-            kv = load_elem(kg, e);
-            gv = p.c.g[e];
-        }
-        Qt[d][a] = qv;
-        Kt[d][a] = kv;
-        Gt[d][a] = gv;
-    }
+    stage_rows<Tin, DK, NT, true, KP>(qg, se.tok0, H, h, n, &Qt[0][0], tid);
+    stage_rows<Tin, DK, NT, true, KP>(kg, se.tok0, H, h, n, &Kt[0][0], tid);
+    stage_rows<float, DK, NT, true, KP>(p.c.g, se.tok0, H, h, n, &Gt[0][0], tid);
     __syncthreads();
     {
         const int w = tid >> 6, l = tid & 63;
@@ -430,12 +470,23 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p) {
     __syncthreads();
     const int64_t ti = tile_index(p, s, h);
     {
+        constexpr int SP = DK * DV / 4 / NT, NP = KC * DV / 4 / NT;
         const float4 *src = reinterpret_cast<const float4 *>(p.sin + ti * DK * DV);
-        for (int i = tid; i < DK * DV / 4; i += NT) reinterpret_cast<float4 *>(&Sv[0][0])[i] = src[i];
-        const float *nv = p.nv + ti * KC * DV;
-        for (int i = tid; i < KC * DV; i += NT) {
-            const int a = i / DV, j = i - a * DV;
-            Nv[a][j] = nv[i];
+        const float4 *nsrc = reinterpret_cast<const float4 *>(p.nv + ti * KC * DV);
+        float4 rs[SP], rn[NP];
+#pragma unroll
+        for (int m = 0; m < SP; ++m) rs[m] = src[m * NT + tid];
+#pragma unroll
+        for (int m = 0; m < NP; ++m) rn[m] = nsrc[m * NT + tid];
+#pragma unroll
+        for (int m = 0; m < SP; ++m) reinterpret_cast<float4 *>(&Sv[0][0])[m * NT + tid] = rs[m];
+#pragma unroll
+        for (int m = 0; m < NP; ++m) {
+            const int e = 4 * (m * NT + tid), a = e / DV, j = e - a * DV;
+            Nv[a][j] = rn[m].x;
+            Nv[a][j + 1] = rn[m].y;
+            Nv[a][j + 2] = rn[m].z;
+            Nv[a][j + 3] = rn[m].w;
         }
     }
     __syncthreads();

@@ -740,7 +740,7 @@ sgla_status check_kda_args(const void *q, const void *k, const void *v, const fl
     // The chain kernel runs Dv / 16 workgroups per (sequence, head).
     if ((int64_t)B * H * (Dv / 16) > ((int64_t)1 << 31) - 64) return SGLA_ERR_UNSUPPORTED;
     if (ttot > 0 && (!q || !k || !v || !g || !beta || !out)) return SGLA_ERR_INVALID_ARG;
-    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g, 4) ||
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(g) ||
         misaligned(beta, 4) || misaligned(out) || misaligned(initial_state) ||
         misaligned(final_state) || misaligned(cu_seqlens, 8))
         return SGLA_ERR_INVALID_ARG;
