@@ -207,8 +207,13 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
     }
     if (nch > 0) issue(0);
 
-    char *ft = lds + L_F + 512 * w;  // this wave's G[64], then exp(G_last - G)[64]
+    char *ft = lds + L_F + 512 * w;  // this wave's G log2(e) [64], then exp(G_last - G)[64]
     const int i = 32 * t + ln;        // this lane's query row of the output
+    // The scores' and rows' exponentials take base 2 with log2|scale| added
+    // to the exponent: |scale| exp(G_i - G_j) = exp2(G_i log2(e) +
+    // log2|scale| - G_j log2(e)); a negative scale flips the output rows.
+    const float ls = __builtin_amdgcn_logf(fabsf(p.scale));
+    const bool neg = p.scale < 0.f;
     for (int c = 0; c < nch; ++c) {
         const int n = min(64, len - 64 * c);
         __syncthreads();  // the previous chunk's tiles and staging are read
@@ -218,8 +223,9 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             asm volatile("" : "+v"(tv));
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
+                // tv < 256, so bit 4 of the row is that of 16 i4.
                 const int r = (tv >> 4) + 16 * i4;
-                const bool sw = (r >> 4) & 1;
+                const bool sw = i4 & 1;
                 lds_st(lds, L_Q + qk_off(r, tv & 15), sw ? swap_halves(qr[i4]) : qr[i4]);
                 lds_st(lds, L_K + qk_off(r, tv & 15), sw ? swap_halves(kr[i4]) : kr[i4]);
             }
@@ -233,7 +239,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
         // Gate prefix sum, one lane per token (rows past the end read as 0).
         const float G = wave_prefix_sum(lds_ld<float>(lds, L_G + 4 * l));
         const float Gl = lane_value(G, 63);
-        lds_st(ft, 4 * l, G);
+        lds_st(ft, 4 * l, G * 1.44269504088896341f);
         lds_st(ft, 256 + 4 * l, l < n ? __expf(Gl - G) : 0.f);
 
         // O^T = S^T Q^T over this wave's key rows for both token halves;
@@ -244,11 +250,11 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 bf16x8 sh, sl;
+                {
+                    float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = S[bi][8 * s2 + e];
-                    sh[e] = (__bf16)x;
-                    sl[e] = (__bf16)(x - (float)sh[e]);
+                    for (int e = 0; e < 8; ++e) x[e] = S[bi][8 * s2 + e];
+                    split_bf16x8(x, sh, sl);
                 }
                 const int cq = 4 * (2 * t + bi) + 2 * s2;
 #pragma unroll
@@ -288,7 +294,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
                 const bf16x8 bq = cat4(lds_ld<bf16x4>(lds, ci + qk_half(iq, 0)), lds_ld<bf16x4>(lds, ci + qk_half(iq, 1)));
                 sc = mfma(a, bq, sc);
             }
-            const float Gi = lds_ld<float>(ft, 4 * iq);
+            const float Gi = lds_ld<float>(ft, 4 * iq) + ls;
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int jr = 32 * jb + 8 * g4 + 4 * lh;
@@ -297,7 +303,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
                 float val[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    val[r] = (jr + r <= iq) ? p.scale * __expf(Gi - gj[r]) * sc[4 * g4 + r] : 0.f;
+                    val[r] = (jr + r <= iq) ? __builtin_amdgcn_exp2f(Gi - gj[r]) * sc[4 * g4 + r] : 0.f;
                 const u32x2 pk = {pack_f32(val[0], val[1]), pack_f32(val[2], val[3])};
                 lds_st(lds, L_A + tr_off(iq, 4 * jb + g4) + 8 * lh, pk);
             }
@@ -316,7 +322,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
 
         // The partner's key rows, then the rows scaled by scale * exp(G_i).
         {
-            const float f = p.scale * __expf(lds_ld<float>(ft, 4 * i));
+            const float f = __builtin_amdgcn_exp2f(lds_ld<float>(ft, 4 * i) + ls);
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const float4 y = lds_ld<float4>(lds, sx_off(cc, t, v4, l));
@@ -336,6 +342,9 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             }
         }
         // Output rows into the staging tile (stored at the next iteration).
+        if (neg)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] = -acc[v];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const u32x2 pk = {pack_f32(acc[4 * g4], acc[4 * g4 + 1]), pack_f32(acc[4 * g4 + 2], acc[4 * g4 + 3])};
@@ -354,9 +363,10 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
                 const float4 f0 = lds_ld<float4>(ft, 256 + 4 * (16 * s4 + 8 * lh));
                 const float4 f1 = lds_ld<float4>(ft, 256 + 4 * (16 * s4 + 8 * lh) + 16);
                 const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-                bf16x8 vs;
+                float xs[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) vs[e] = (__bf16)((float)vop[s4][e] * fe[e]);
+                for (int e = 0; e < 8; ++e) xs[e] = (float)vop[s4][e] * fe[e];
+                const bf16x8 vs = to_bf16x8(xs);
 #pragma unroll
                 for (int bi = 0; bi < 2; ++bi) {
                     const int c0 = 32 * (2 * t + bi) + 16 * (gi & 1);

@@ -426,11 +426,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2) {
                     bf16x8 sh, sl;
+                    {
+                        float x[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float x = S[b][8 * s2 + e];
-                        sh[e] = (__bf16)x;
-                        sl[e] = (__bf16)(x - (float)sh[e]);
+                        for (int e = 0; e < 8; ++e) x[e] = S[b][8 * s2 + e];
+                        split_bf16x8(x, sh, sl);
                     }
                     const int c = 4 * b + 2 * s2;
 #pragma unroll

@@ -43,6 +43,30 @@ __device__ __forceinline__ uint32_t pack_f32(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Eight floats as a bf16 pair hi + lo with |x - hi - lo| < 2^-16 |x|: hi is
+// x cut to its top 16 bits (one byte permute per two values), lo the
+// remainder, exact in fp32, rounded to bf16.
+__device__ __forceinline__ void split_bf16x8(const float *x, bf16x8 &hi, bf16x8 &lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t a = __float_as_uint(x[2 * e]), b = __float_as_uint(x[2 * e + 1]);
+        h[e] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+        l[e] = pack_f32(x[2 * e] - __uint_as_float(a & 0xffff0000u),
+                        x[2 * e + 1] - __uint_as_float(b & 0xffff0000u));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// Eight floats rounded to bf16 (nearest even), two per conversion.
+__device__ __forceinline__ bf16x8 to_bf16x8(const float *x) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = pack_f32(x[2 * e], x[2 * e + 1]);
+    return __builtin_bit_cast(bf16x8, r);
+}
+
 __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }

@@ -475,3 +475,24 @@ def test_growing_and_shrinking_gates(path):
     inp["g"] = (torch.rand(inp["g"].shape, generator=gen, device="cuda") - 0.5) * 0.1
     o, S = run_gpu(inp)
     compare(inp, o, S, dtype, "mixed-sign g " + path, starts=[0, 256, 512, 768])
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.0])
+@pytest.mark.parametrize("path", ["halves", "one_level", "valu_f32_d64"])
+def test_output_scale_of_either_sign(path, scale):
+    """The output scale is any real number: negative, zero and above one."""
+    dtype, D = ("f32", 64) if path == "valu_f32_d64" else ("bf16", 128)
+    if path == "one_level":
+        os.environ["SGLA_ONE_LEVEL"] = "1"
+    set_segments(256, 2)
+    say("chunk_fwd scale", scale, path)
+    inp = W.make_prefill(2, 600, 3, D, D, dtype, "lightning", seed=57, device="cuda",
+                         init="normal")
+    inp["scale"] = scale
+    o, S = run_gpu(inp)
+    if scale == 0.0:
+        assert float(o.float().abs().max()) == 0.0
+        ro, rS = oracle_prefill(inp)
+        check(host(S), rS, dtype, "scale 0 final state", bf16_out=False)
+        return
+    compare(inp, o, S, dtype, "scale %g %s" % (scale, path), starts=[0, 256, 512])
