@@ -28,9 +28,9 @@
 // (queries a) and an earlier token b they are split at the block's first
 // token c, exp(G[a] - G[c]) exp(G[c] - G[b]), two factors that each lie in
 // (0, 1] when g <= 0, so every block pair costs one exponential per element
-// and token rather than per pair. T is inverted in 16 x 16 blocks: each
-// diagonal block by forward substitution, the blocks below it block row by
-// block row, T_IJ = -T_II sum_K A_IK T_KJ.
+// and token rather than per pair. T is found by forward substitution on one
+// wave, each lane holding one column in registers, while the other waves form
+// the decayed keys.
 #include "mfma_tile.h"
 
 namespace sgla {
@@ -105,11 +105,12 @@ __device__ __forceinline__ void stage_rows(const Tin *base, int64_t tok0, int H,
 template <typename Tin, int DK, int DV>
 __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     constexpr int NT = 512;
+    constexpr int MP = KC + 4;         // row stride of A/T: 16-byte aligned rows
     __shared__ float Kt[DK][KP];       // K^T; later (diag(beta) K * exp(G))^T
     __shared__ float Gt[DK][KP];       // G^T
     __shared__ float Vs[KC][DV + 1];   // diag(beta) V
-    __shared__ float Ms[KC][KP];       // A = diag(beta) M below the diagonal; partial sums above
-    __shared__ float Xs[KC][DK + 1];   // K decayed to a reference token; then T
+    __shared__ __attribute__((aligned(16))) float Ms[KC][MP];  // A = diag(beta) M below the diagonal; then T
+    __shared__ float Xs[KC][DK + 1];   // K decayed to a reference token
     __shared__ float bs[KC];
     static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xs) + sizeof(bs) <=
                       kLdsPerCU,
@@ -122,6 +123,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     if (se.len < 0) return;
     const int n = se.len;
     const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63;
     const Tin *__restrict__ kg = static_cast<const Tin *>(p.c.k);
     const Tin *__restrict__ vg = static_cast<const Tin *>(p.c.v);
 
@@ -136,10 +138,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
         Vs[a][j] *= bs[a];
     }
     // G: cumulative sums over the tokens, one wave per key dim, lane = token.
-    {
-        const int w = tid >> 6, l = tid & 63;
-        for (int d = w; d < DK; d += NT / 64) Gt[d][l] = wave_prefix_sum(Gt[d][l]);
-    }
+    for (int d = w; d < DK; d += NT / 64) Gt[d][l] = wave_prefix_sum(Gt[d][l]);
     __syncthreads();
 
     // A inside the diagonal 16 x 16 blocks (a > b), exponent taken directly.
@@ -153,7 +152,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
         Ms[a][b] = bs[a] * acc;
     }
     // A below the diagonal blocks: block row I against tokens b < c = 16 I,
-    // split at c.
+    // split at c; a lane pair takes one row a and four tokens b, each lane
+    // every other key dim, and the pair's sums are added across it.
     for (int I = 1; I < 4; ++I) {
         const int c = 16 * I;
         __syncthreads();  // the previous block row's products are done with Xs
@@ -163,74 +163,78 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
             Xs[a][d] = Kt[d][a] * __expf(e);
         }
         __syncthreads();
-        for (int i = tid; i < 16 * c; i += NT) {
-            const int ai = i / c, b = i - ai * c;
+        const int q4 = c / 4;  // groups of four tokens b per row
+        if (tid < 32 * q4) {    // 32 c <= 384 threads, whole lane pairs
+            const int pr = tid >> 1, dq = tid & 1;
+            const int ai = pr / q4, b0 = 4 * (pr - ai * q4);
             const int a = c + ai;
-            float acc = 0.f;
-            for (int d = 0; d < DK; ++d) acc = fmaf(Xs[a][d], Xs[b][d], acc);
-            Ms[a][b] = bs[a] * acc;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+            for (int d = dq; d < DK; d += 2) {
+                const float xa = Xs[a][d];
+#pragma unroll
+                for (int y = 0; y < 4; ++y) acc[y] = fmaf(xa, Xs[b0 + y][d], acc[y]);
+            }
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                // quad_perm [1, 0, 3, 2]: the other lane of the pair
+                acc[y] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                                        __builtin_bit_cast(int, acc[y]), 0xb1, 0xf, 0xf, false));
+                if (dq == 0) Ms[a][b0 + y] = bs[a] * acc[y];
+            }
         }
     }
     __syncthreads();
-
-    // T = (I + A)^-1 into Xs[a][b]. Diagonal blocks: waves 0-3, one block
-    // each, lanes 0-15 the columns; row r of block w from the rows above it.
-    const int w = tid >> 6, l = tid & 63;
-    if (w < 4 && l < 16)
-        for (int i = 0; i < 16; ++i) Xs[16 * w + i][16 * w + l] = i == l ? 1.f : 0.f;
-    __syncthreads();
-    for (int i = 1; i < 16; ++i) {
-        if (w < 4 && l < i) {
-            const int r = 16 * w + i, j = 16 * w + l;
-            float acc = 0.f;
-            for (int m = j; m < r; ++m) acc = fmaf(Ms[r][m], Xs[m][j], acc);
-            Xs[r][j] = -acc;
-        }
-        __syncthreads();
-    }
-    // Blocks below the diagonal, block row by block row: P_IJ = sum_K A_IK
-    // T_KJ (K = J .. I-1) into Ms's unused upper part at (16 J + x, 16 I + y),
-    // then T_IJ = -T_II P_IJ.
-    for (int I = 1; I < 4; ++I) {
-        for (int i = tid; i < 256 * I; i += NT) {
-            const int J = i >> 8, x = (i >> 4) & 15, y = i & 15;
-            float acc = 0.f;
-            for (int m = 16 * J; m < 16 * I; ++m) acc = fmaf(Ms[16 * I + x][m], Xs[m][16 * J + y], acc);
-            Ms[16 * J + x][16 * I + y] = acc;
-        }
-        __syncthreads();
-        for (int i = tid; i < 256 * I; i += NT) {
-            const int J = i >> 8, x = (i >> 4) & 15, y = i & 15;
-            float acc = 0.f;
-            for (int z = 0; z <= x; ++z) acc = fmaf(Xs[16 * I + x][16 * I + z], Ms[16 * J + z][16 * I + y], acc);
-            Xs[16 * I + x][16 * J + y] = -acc;
-        }
-        __syncthreads();
-    }
 
     float *tile = p.tiles + tile_index(p, s, h) * tile_floats(DK, DV);
-    // K * exp(G_last - G) and exp(G_last) for the chain (rows past the end
-    // have zero keys and gates, so G_last is the last row's G).
-    for (int i = tid; i < KC * DK; i += NT) {
-        const int a = i / DK, d = i - a * DK;
-        tile[KC * DK + i] = Kt[d][a] * __expf(Gt[d][KC - 1] - Gt[d][a]);
-    }
-    if (tid < DK) tile[2 * KC * DK + KC * DV + tid] = __expf(Gt[tid][KC - 1]);
-    __syncthreads();
-    for (int i = tid; i < KC * DK; i += NT) {
-        const int d = i / KC, a = i - d * KC;
-        Kt[d][a] *= bs[a] * __expf(Gt[d][a]);
+    if (w == 0) {
+        // T = (I + A)^-1 by forward substitution on one wave: lane l holds
+        // column l of T in registers, T[i][l] = delta_il - sum_{m < i}
+        // A[i][m] T[m][l] (zero above the diagonal), and reads row i of A as
+        // 16-byte broadcasts. Written over A once every row is read.
+        float tc[KC];
+#pragma unroll
+        for (int i = 0; i < KC; ++i) {
+            // Row i of A in full first, then four independent partial sums.
+            float4 arow[KC / 4];
+#pragma unroll
+            for (int m4 = 0; m4 < (i + 3) / 4; ++m4)
+                arow[m4] = *reinterpret_cast<const float4 *>(&Ms[i][4 * m4]);
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m4 = 0; m4 < (i + 3) / 4; ++m4) {
+                const float av[4] = {arow[m4].x, arow[m4].y, arow[m4].z, arow[m4].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * m4 + e < i) acc[e] = fmaf(av[e], tc[4 * m4 + e], acc[e]);
+            }
+            const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            tc[i] = l < i ? -sum : (l == i ? 1.f : 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < KC; ++i) Ms[i][l] = tc[i];
+    } else {
+        // Meanwhile: K * exp(G_last - G) and exp(G_last) for the chain (rows
+        // past the end have zero keys and gates, so G_last is the last row's
+        // G), and X = diag(beta) K * exp(G) in place of K.
+        for (int i = tid - 64; i < KC * DK; i += NT - 64) {
+            const int a = i / DK, d = i - a * DK;
+            const float kv = Kt[d][a], gv = Gt[d][a];
+            tile[KC * DK + i] = kv * __expf(Gt[d][KC - 1] - gv);
+            Kt[d][a] = kv * bs[a] * __expf(gv);
+        }
+        if (tid - 64 < DK) tile[2 * KC * DK + KC * DV + tid - 64] = __expf(Gt[tid - 64][KC - 1]);
     }
     __syncthreads();
     // W = T X and U = T (diag(beta) V), 4 tokens x 4 columns per thread; T is
-    // lower triangular (its upper part in Xs holds stale values).
+    // lower triangular.
     for (int i = tid; i < (KC / 4) * (DK / 4); i += NT) {
         const int at = i / (DK / 4), a0 = 4 * at, d0 = 4 * (i - at * (DK / 4));
         float acc[4][4] = {};
         for (int b = 0; b <= a0 + 3; ++b) {
             float tv[4], xv[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) tv[x] = b <= a0 + x ? Xs[a0 + x][b] : 0.f;
+            for (int x = 0; x < 4; ++x) tv[x] = Ms[a0 + x][b];
 #pragma unroll
             for (int y = 0; y < 4; ++y) xv[y] = Kt[d0 + y][b];
 #pragma unroll
@@ -249,7 +253,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
         for (int b = 0; b <= a0 + 3; ++b) {
             float tv[4], vv[4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) tv[x] = b <= a0 + x ? Xs[a0 + x][b] : 0.f;
+            for (int x = 0; x < 4; ++x) tv[x] = Ms[a0 + x][b];
 #pragma unroll
             for (int y = 0; y < 4; ++y) vv[y] = Vs[b][j0 + y];
 #pragma unroll
@@ -286,8 +290,10 @@ __global__ __launch_bounds__(CHAIN_NT) void kda_chain_kernel(KdaParams p) {
                   "two workgroups must fit one CU's LDS");
     constexpr int NVB = DV / VB;
     const int H = p.c.H;
-    const int vb = blockIdx.x % NVB;
-    const int nh = blockIdx.x / NVB;
+    // The NVB column blocks of a (sequence, head) share each chunk's W and
+    // K * exp(G_last - G) tiles: they run on one XCD, through its L2.
+    int nh, vb;
+    xcd_unit_map(blockIdx.x, NVB, nh, vb);
     const int n = nh / H;
     const int h = nh - n * H;
     if (n >= p.c.N) return;
@@ -537,7 +543,9 @@ hipError_t launch_dims(const KdaParams &p, hipStream_t st) {
     hipLaunchKernelGGL((kda_prep_kernel<Tin, DK, DV>), dim3(units), dim3(512), 0, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned chains = (unsigned)((int64_t)p.c.N * p.c.H * (DV / VB));
+    // xcd_unit_map covers every (sequence, head) when the unit count is
+    // rounded up to a multiple of the 8 XCDs; the extra ids return at once.
+    const unsigned chains = (unsigned)(((int64_t)p.c.N * p.c.H + 7) / 8 * 8 * (DV / VB));
     hipLaunchKernelGGL((kda_chain_kernel<DK, DV>), dim3(chains), dim3(CHAIN_NT), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
