@@ -28,14 +28,17 @@
 // (queries a) and an earlier token b they are split at the block's first
 // token c, exp(G[a] - G[c]) exp(G[c] - G[b]), two factors that each lie in
 // (0, 1] when g <= 0, so every block pair costs one exponential per element
-// and token rather than per pair. T is found by forward substitution on one
-// wave, each lane holding one column in registers, while the other waves form
-// the decayed keys.
+// and token rather than per pair; the products between blocks run on the
+// matrix cores as bf16 high/low pairs. T is inverted in 16 x 16 blocks: each
+// diagonal block by back substitution on one wave, the blocks below it block
+// row by block row, T_IJ = -T_II sum_K A_IK T_KJ, on fp32 MFMAs.
 #include "mfma_tile.h"
 
 namespace sgla {
 
 namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KC = kChunk;  // tokens per chunk
 constexpr int KP = KC + 1;  // padded token stride of transposed tiles
@@ -65,6 +68,37 @@ __device__ __forceinline__ void load_piece(const Tin *src, float *out) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = __uint_as_float(w[e]);
     }
+}
+
+// bf16 tiles of 64 rows of DK values for the 16 x 16 x 32 MFMA operands:
+// 16-byte chunk c of row r sits at chunk c ^ (r mod chunks-per-row), so the
+// 16 rows one operand read touches fall in different banks.
+template <int DK>
+__device__ __forceinline__ int brow_off(int r, int c) {
+    constexpr int NC = DK / 8;
+    return r * (DK * 2) + ((c ^ (r & (NC - 1))) << 4);
+}
+
+// 16 x 16 block of P = X_a X_b^T over DK (rows 16 ra0 .. and 16 rb0 .. of
+// two bf16 hi/lo tile pairs), on one wave: hi hi + hi lo + lo hi, about 2^-16
+// of each product. Lane (g, lc) gets P[16 ra0 + lc][16 rb0 + 4 g + r] in
+// acc[r] (16 x 16 x 32 MFMA: both operands name row lc of their block and
+// k = 32 ks + 8 g .. + 7; the result is C[4 g + r][lc], C = B-block x A-block).
+template <int DK>
+__device__ __forceinline__ f32x4 block_product(const char *hi, const char *lo, int ra0, int rb0,
+                                               int l) {
+    const int lc = l & 15, g = l >> 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+        const int oa = brow_off<DK>(16 * ra0 + lc, 4 * ks + g), ob = brow_off<DK>(16 * rb0 + lc, 4 * ks + g);
+        const bf16x8 ah = lds_ld<bf16x8>(hi, oa), al = lds_ld<bf16x8>(lo, oa);
+        const bf16x8 bh = lds_ld<bf16x8>(hi, ob), bl = lds_ld<bf16x8>(lo, ob);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, ah, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, al, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl, ah, acc, 0, 0, 0);
+    }
+    return acc;
 }
 
 // A chunk's rows of a [tokens, H, W] tensor (rows past n read as zeros),
@@ -110,10 +144,14 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     __shared__ float Gt[DK][KP];       // G^T
     __shared__ float Vs[KC][DV + 1];   // diag(beta) V
     __shared__ __attribute__((aligned(16))) float Ms[KC][MP];  // A = diag(beta) M below the diagonal; then T
-    __shared__ float Xs[KC][DK + 1];   // K decayed to a reference token
+    // K decayed to a reference token, as bf16 high and low tiles; later the
+    // blocks of T (14 blocks of 16 rows x 20 floats).
+    constexpr int XT = 2 * KC * DK * 2, XTB = 14 * 16 * 20 * 4;
+    __shared__ __attribute__((aligned(16))) char Xb[XT > XTB ? XT : XTB];
+    char *const Xh = Xb;
+    char *const Xl = Xb + KC * DK * 2;
     __shared__ float bs[KC];
-    static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xs) + sizeof(bs) <=
-                      kLdsPerCU,
+    static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xb) + sizeof(bs) <= kLdsPerCU,
                   "the workgroup must fit one CU's LDS");
     const int H = p.c.H;
     const int s = blockIdx.x / H;
@@ -152,78 +190,121 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
         Ms[a][b] = bs[a] * acc;
     }
     // A below the diagonal blocks: block row I against tokens b < c = 16 I,
-    // split at c; a lane pair takes one row a and four tokens b, each lane
-    // every other key dim, and the pair's sums are added across it.
+    // split at c, the decayed keys as bf16 hi/lo tiles; one wave per 16 x 16
+    // block on the matrix cores.
     for (int I = 1; I < 4; ++I) {
         const int c = 16 * I;
-        __syncthreads();  // the previous block row's products are done with Xs
-        for (int i = tid; i < (c + 16) * DK; i += NT) {
-            const int a = i / DK, d = i - a * DK;
-            const float e = a < c ? Gt[d][c] - Gt[d][a] : Gt[d][a] - Gt[d][c];
-            Xs[a][d] = Kt[d][a] * __expf(e);
+        __syncthreads();  // the previous block row's products are done with the tiles
+        for (int i = tid; i < (c + 16) * DK / 2; i += NT) {
+            const int a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
+            float x[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float ex = a < c ? Gt[d + e][c] - Gt[d + e][a] : Gt[d + e][a] - Gt[d + e][c];
+                x[e] = Kt[d + e][a] * __expf(ex);
+            }
+            const uint32_t u0 = __float_as_uint(x[0]), u1 = __float_as_uint(x[1]);
+            const int off = brow_off<DK>(a, d >> 3) + 2 * (d & 7);
+            *reinterpret_cast<uint32_t *>(Xh + off) = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+            *reinterpret_cast<uint32_t *>(Xl + off) =
+                pack_f32(x[0] - __uint_as_float(u0 & 0xffff0000u), x[1] - __uint_as_float(u1 & 0xffff0000u));
         }
         __syncthreads();
-        const int q4 = c / 4;  // groups of four tokens b per row
-        if (tid < 32 * q4) {    // 32 c <= 384 threads, whole lane pairs
-            const int pr = tid >> 1, dq = tid & 1;
-            const int ai = pr / q4, b0 = 4 * (pr - ai * q4);
-            const int a = c + ai;
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int d = dq; d < DK; d += 2) {
-                const float xa = Xs[a][d];
-#pragma unroll
-                for (int y = 0; y < 4; ++y) acc[y] = fmaf(xa, Xs[b0 + y][d], acc[y]);
-            }
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                // quad_perm [1, 0, 3, 2]: the other lane of the pair
-                acc[y] += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
-                                                        __builtin_bit_cast(int, acc[y]), 0xb1, 0xf, 0xf, false));
-                if (dq == 0) Ms[a][b0 + y] = bs[a] * acc[y];
-            }
+        if (w < I) {
+            const f32x4 acc = block_product<DK>(Xh, Xl, I, w, l);
+            const int a = c + (l & 15), b0 = 16 * w + 4 * (l >> 4);
+            const float ba = bs[a];
+            *reinterpret_cast<float4 *>(&Ms[a][b0]) =
+                make_float4(ba * acc[0], ba * acc[1], ba * acc[2], ba * acc[3]);
         }
     }
     __syncthreads();
 
     float *tile = p.tiles + tile_index(p, s, h) * tile_floats(DK, DV);
-    if (w == 0) {
-        // T = (I + A)^-1 by forward substitution on one wave: lane l holds
-        // column l of T in registers, T[i][l] = delta_il - sum_{m < i}
-        // A[i][m] T[m][l] (zero above the diagonal), and reads row i of A as
-        // 16-byte broadcasts. Written over A once every row is read.
-        float tc[KC];
+    // T = (I + A)^-1 in 16 x 16 blocks, kept in the space of the bf16 tiles
+    // (free once A is formed): the ten blocks (I, J), J <= I, rows of 80 bytes
+    // (20 floats: the 16 rows of a block start 4 banks apart), then one
+    // scratch block per wave.
+    constexpr int TBR = 20;                         // floats per block row
+    constexpr int TBF = 16 * TBR;                   // floats per block
+    float *tb = reinterpret_cast<float *>(Xb);      // 10 blocks + 4 scratch = 17.5 KiB
+    static_assert(14 * TBF * 4 <= (int)sizeof(Xb), "T blocks exceed the tile space");
+    auto tbo = [](int I, int J) { return (I * (I + 1) / 2 + J) * TBF; };
+    if (w < 4 && l < 16) {
+        // Diagonal block w, row l of T_ww = (I + A_ww)^-1: y with
+        // (I + A_ww)^T y = e_l, by back substitution (once y_j is final it
+        // takes A[j][m] y_j out of every y_m, m < j; 15 dependent steps).
+        float y[16];
 #pragma unroll
-        for (int i = 0; i < KC; ++i) {
-            // Row i of A in full first, then four independent partial sums.
-            float4 arow[KC / 4];
+        for (int m = 0; m < 16; ++m) y[m] = m == l ? 1.f : 0.f;
 #pragma unroll
-            for (int m4 = 0; m4 < (i + 3) / 4; ++m4)
-                arow[m4] = *reinterpret_cast<const float4 *>(&Ms[i][4 * m4]);
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 15; j >= 1; --j) {
 #pragma unroll
-            for (int m4 = 0; m4 < (i + 3) / 4; ++m4) {
-                const float av[4] = {arow[m4].x, arow[m4].y, arow[m4].z, arow[m4].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (4 * m4 + e < i) acc[e] = fmaf(av[e], tc[4 * m4 + e], acc[e]);
+            for (int mq = 0; mq < j; mq += 4) {
+                const float4 a = *reinterpret_cast<const float4 *>(&Ms[16 * w + j][16 * w + mq]);
+                if (mq + 0 < j) y[mq + 0] = fmaf(-a.x, y[j], y[mq + 0]);
+                if (mq + 1 < j) y[mq + 1] = fmaf(-a.y, y[j], y[mq + 1]);
+                if (mq + 2 < j) y[mq + 2] = fmaf(-a.z, y[j], y[mq + 2]);
+                if (mq + 3 < j) y[mq + 3] = fmaf(-a.w, y[j], y[mq + 3]);
             }
-            const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            tc[i] = l < i ? -sum : (l == i ? 1.f : 0.f);
         }
 #pragma unroll
-        for (int i = 0; i < KC; ++i) Ms[i][l] = tc[i];
-    } else {
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4 *>(tb + tbo(w, w) + l * TBR + 4 * q) =
+                make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
+    } else if (w >= 4) {
         // Meanwhile: K * exp(G_last - G) and exp(G_last) for the chain (rows
         // past the end have zero keys and gates, so G_last is the last row's
         // G), and X = diag(beta) K * exp(G) in place of K.
-        for (int i = tid - 64; i < KC * DK; i += NT - 64) {
+        for (int i = tid - 256; i < KC * DK; i += NT - 256) {
             const int a = i / DK, d = i - a * DK;
             const float kv = Kt[d][a], gv = Gt[d][a];
             tile[KC * DK + i] = kv * __expf(Gt[d][KC - 1] - gv);
             Kt[d][a] = kv * bs[a] * __expf(gv);
         }
-        if (tid - 64 < DK) tile[2 * KC * DK + KC * DV + tid - 64] = __expf(Gt[tid - 64][KC - 1]);
+        if (tid - 256 < DK) tile[2 * KC * DK + KC * DV + tid - 256] = __expf(Gt[tid - 256][KC - 1]);
+    }
+    __syncthreads();
+    // Block rows below: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, wave J taking
+    // column block J. Each 16 x 16 x 16 product is four fp32 16 x 16 x 4
+    // MFMAs: lane l supplies L[l % 16][4k + l / 16] and R[4k + l / 16][l % 16]
+    // and receives D[4 (l / 16) + v][l % 16] in element v.
+    {
+        const int lr = l & 15, lk = l >> 4;
+        float *scr = tb + (10 + (w & 3)) * TBF;
+#pragma unroll
+        for (int I = 1; I < 4; ++I) {
+            if (w < I) {
+                const int J = w;
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+                for (int K = J; K < I; ++K)
+#pragma unroll
+                    for (int k4 = 0; k4 < 4; ++k4) {
+                        const float a = Ms[16 * I + lr][16 * K + 4 * k4 + lk];
+                        const float b = tb[tbo(K, J) + (4 * k4 + lk) * TBR + lr];
+                        x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
+                    }
+                // X to this wave's scratch block (a wave's LDS accesses take
+                // effect in order), then T_II X.
+#pragma unroll
+                for (int v = 0; v < 4; ++v) scr[(4 * lk + v) * TBR + lr] = x[v];
+                f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    const float a = tb[tbo(I, I) + lr * TBR + 4 * k4 + lk];
+                    const float b = scr[(4 * k4 + lk) * TBR + lr];
+                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t, 0, 0, 0);
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) tb[tbo(I, J) + (4 * lk + v) * TBR + lr] = -t[v];
+            }
+            __syncthreads();
+        }
+    }
+    // T back into Ms row-major, zero above the diagonal.
+    for (int i = tid; i < KC * KC; i += NT) {
+        const int a = i / KC, b = i - a * KC;
+        Ms[a][b] = b <= a ? tb[tbo(a >> 4, b >> 4) + (a & 15) * TBR + (b & 15)] : 0.f;
     }
     __syncthreads();
     // W = T X and U = T (diag(beta) V), 4 tokens x 4 columns per thread; T is
