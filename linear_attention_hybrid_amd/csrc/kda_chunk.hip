@@ -43,8 +43,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int KC = kChunk;  // tokens per chunk
 constexpr int KP = KC + 1;  // padded token stride of transposed tiles
 
-// Per chunk and head workspace tile, in floats: W [64][Dk], then
-// K * exp(G_last - G) [64][Dk], U [64][Dv], exp(G_last) [Dk].
+// Per chunk and head workspace tile, in floats: W, then K * exp(G_last - G),
+// then U, each as fp32 MFMA operand images (below), then exp(G_last) [Dk].
+//
+// The chain's products are fp32 16 x 16 x 4 MFMAs: lane l = 16 kk + r
+// supplies A[r][kk] and B[kk][r] and receives D[4 kk + v][r] in element v.
+// Four of them cover 16 k values, MFMA k4 taking k = 4 kk + k4 for lane
+// group kk, so each lane's operands for the four are one float4 and an
+// accumulator quad is already the B operand of the next product. The images
+// hold those float4s in lane order (1 KiB per 16 x 16 block):
+//   W   [tok block tt][key block b][lane]  = W[16 tt + r][16 b + 4 kk .. +3]
+//   Kd  [key block b][tok block tt][lane]  = Kd[16 tt + 4 kk .. +3][16 b + r]
+//   U   [tok block tt][col block cb][lane] = U[16 tt + 4 kk .. +3][16 cb + r]
+// and the chain leaves, per chunk, the start state and new_v likewise:
+//   S   [key block b][col block cb][lane]  = S[16 b + 4 kk .. +3][16 cb + r]
+//   nv  [tok block tt][col block cb][lane] = new_v[16 tt + 4 kk .. +3][16 cb + r]
 __host__ __device__ constexpr int64_t tile_floats(int dk, int dv) {
     return 2 * (int64_t)KC * dk + (int64_t)KC * dv + dk;
 }
@@ -256,11 +269,18 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
         // Meanwhile: K * exp(G_last - G) and exp(G_last) for the chain (rows
         // past the end have zero keys and gates, so G_last is the last row's
         // G), and X = diag(beta) K * exp(G) in place of K.
-        for (int i = tid - 256; i < KC * DK; i += NT - 256) {
-            const int a = i / DK, d = i - a * DK;
-            const float kv = Kt[d][a], gv = Gt[d][a];
-            tile[KC * DK + i] = kv * __expf(Gt[d][KC - 1] - gv);
-            Kt[d][a] = kv * bs[a] * __expf(gv);
+        for (int q = tid - 256; q < KC / 4 * DK; q += NT - 256) {
+            // float4 q of the Kd image: tokens a0 .. a0 + 3, key dim d.
+            const int d = 16 * (q >> 8) + (q & 15), a0 = 16 * ((q >> 6) & 3) + 4 * ((q >> 4) & 3);
+            const float gl = Gt[d][KC - 1];
+            float kd[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float kv = Kt[d][a0 + v], gv = Gt[d][a0 + v];
+                kd[v] = kv * __expf(gl - gv);
+                Kt[d][a0 + v] = kv * bs[a0 + v] * __expf(gv);
+            }
+            reinterpret_cast<float4 *>(tile + KC * DK)[q] = make_float4(kd[0], kd[1], kd[2], kd[3]);
         }
         if (tid - 256 < DK) tile[2 * KC * DK + KC * DV + tid - 256] = __expf(Gt[tid - 256][KC - 1]);
     }
@@ -324,9 +344,11 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
                 for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(tv[x], xv[y], acc[x][y]);
         }
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-            *reinterpret_cast<float4 *>(tile + (a0 + x) * DK + d0) =
-                make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+        for (int x = 0; x < 4; ++x) {
+            const int a = a0 + x;
+            reinterpret_cast<float4 *>(tile)[((a >> 4) * (DK / 16) + (d0 >> 4)) * 64 + 16 * ((d0 >> 2) & 3) +
+                                             (a & 15)] = make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+        }
     }
     for (int i = tid; i < (KC / 4) * (DV / 4); i += NT) {
         const int at = i / (DV / 4), a0 = 4 * at, j0 = 4 * (i - at * (DV / 4));
@@ -343,139 +365,142 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
                 for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(tv[x], vv[y], acc[x][y]);
         }
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-            *reinterpret_cast<float4 *>(tile + 2 * KC * DK + (a0 + x) * DV + j0) =
-                make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
+        for (int y = 0; y < 4; ++y) {
+            const int j = j0 + y;
+            reinterpret_cast<float4 *>(tile + 2 * KC * DK)[((a0 >> 4) * (DV / 16) + (j >> 4)) * 64 +
+                                                           16 * ((a0 >> 2) & 3) + (j & 15)] =
+                make_float4(acc[0][y], acc[1][y], acc[2][y], acc[3][y]);
+        }
     }
 }
 
-// ---- chain: one workgroup of CHAIN_NT threads per (sequence, head, block of
-// VB value columns), through the sequence's chunks in order. The next chunk's
-// W, K * exp(G_last - G), U block and exp(G_last) are loaded into registers
-// while the current one is worked on. Measured at T = 8192, H = 32, D = 128
-// (whole call): 16 columns with 512 threads 2.50 ms; with 256 threads
-// 2.62 ms; 8 columns 2.66 ms (256 threads) and 2.76 ms (512).
+// ---- chain: one workgroup of four waves per (sequence, head, block of 16
+// value columns), through the sequence's chunks in order, on fp32 MFMAs.
+// Wave w holds key rows 16 b .. 16 b + 15 of the state block, for its RB
+// row blocks b = RB w .. RB w + RB - 1, as accumulator quads. Per chunk:
+//   1. it stores them as the chunk's start state (image layout);
+//   2. new_v for token block w: U - W S over every key row, with S read from
+//      LDS where each wave left its quads (as B operands, in lane order);
+//   3. new_v goes to LDS and to the workspace;
+//   4. S <- diag(exp(G_last)) S + Kd^T new_v on its own rows, new_v read back
+//      from LDS in lane order.
+// Each wave's next-chunk operands (W after step 2, Kd after step 4) are
+// loaded into the registers that step just freed.
 constexpr int VB = 16;
-constexpr int CHAIN_NT = 512;
+constexpr int CHAIN_NT = 256;
 
 template <int DK, int DV>
 __global__ __launch_bounds__(CHAIN_NT) void kda_chain_kernel(KdaParams p) {
-    constexpr int NT = CHAIN_NT;
-    constexpr int PW = KC * DK / 4 / NT;  // float4 pieces of W (and of K * exp(..)) per thread
-    __shared__ float Ws[KC][DK + 1];
-    __shared__ float Kds[KC][DK + 1];
-    __shared__ float Ss[DK][VB + 1];
-    __shared__ float Us[KC][VB + 1];  // U block, then new_v block
-    __shared__ float eg[DK];
-    static_assert(2 * (sizeof(Ws) + sizeof(Kds) + sizeof(Ss) + sizeof(Us) + sizeof(eg)) <= kLdsPerCU,
-                  "two workgroups must fit one CU's LDS");
-    constexpr int NVB = DV / VB;
+    constexpr int NB = DK / 16;   // key blocks
+    constexpr int RB = NB / 4;    // key blocks per wave
+    constexpr int NVB = DV / VB;  // column blocks
+    __shared__ float4 sbuf[NB][64];
+    __shared__ float4 nbuf[4][64];
     const int H = p.c.H;
     // The NVB column blocks of a (sequence, head) share each chunk's W and
-    // K * exp(G_last - G) tiles: they run on one XCD, through its L2.
+    // Kd images: they run on one XCD, through its L2.
     int nh, vb;
     xcd_unit_map(blockIdx.x, NVB, nh, vb);
     const int n = nh / H;
     const int h = nh - n * H;
     if (n >= p.c.N) return;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lk = l >> 4;
     const SeqEntry sq = seq_at(p.c, n);
     const int64_t sl = (int64_t)DK * DV;
-    for (int i = tid; i < DK * VB; i += NT) {
-        const int d = i / VB, j = i - d * VB;
-        Ss[d][j] = p.c.s0 ? p.c.s0[((int64_t)n * H + h) * sl + (int64_t)d * DV + vb * VB + j] : 0.f;
-    }
     const int64_t tf = tile_floats(DK, DV);
-    float4 rw[PW], rk[PW];
-    float ru[KC * VB / NT], re = 0.f;
-    auto load = [&](int64_t s) {
-        const float *tile = p.tiles + tile_index(p, s, h) * tf;
+
+    f32x4 sacc[RB];
 #pragma unroll
-        for (int m = 0; m < PW; ++m) {
-            rw[m] = reinterpret_cast<const float4 *>(tile)[m * NT + tid];
-            rk[m] = reinterpret_cast<const float4 *>(tile + KC * DK)[m * NT + tid];
-        }
+    for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int m = 0; m < KC * VB / NT; ++m) {
-            const int e = m * NT + tid, a = e / VB, j = e - a * VB;
-            ru[m] = tile[2 * KC * DK + a * DV + vb * VB + j];
+        for (int v = 0; v < 4; ++v) {
+            const int row = 16 * (RB * w + i) + 4 * lk + v;
+            sacc[i][v] = p.c.s0 ? p.c.s0[((int64_t)n * H + h) * sl + (int64_t)row * DV + vb * VB + lr] : 0.f;
         }
-        if (tid < DK) re = tile[2 * KC * DK + KC * DV + tid];
+
+    float4 wr[NB], kr[RB][4], ur, er[RB];
+    auto tile_at = [&](int64_t s) {
+        return reinterpret_cast<const float4 *>(p.tiles + tile_index(p, s, h) * tf);
     };
-    if (sq.nseg > 0) load(sq.first);
+    auto load_w = [&](int64_t s) {
+        const float4 *t = tile_at(s);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) wr[b] = t[(w * NB + b) * 64 + l];
+        ur = t[KC * DK / 2 + (w * NVB + vb) * 64 + l];
+    };
+    auto load_k = [&](int64_t s) {
+        const float4 *t = tile_at(s);
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) kr[i][tt] = t[KC * DK / 4 + ((RB * w + i) * 4 + tt) * 64 + l];
+            er[i] = t[(2 * KC * DK + KC * DV) / 4 + 4 * (RB * w + i) + lk];
+        }
+    };
+    if (sq.nseg > 0) {
+        load_w(sq.first);
+        load_k(sq.first);
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) sbuf[RB * w + i][l] = make_float4(sacc[i][0], sacc[i][1], sacc[i][2], sacc[i][3]);
+    __syncthreads();
     for (int c = 0; c < sq.nseg; ++c) {
         const int64_t s = sq.first + c;
-        __syncthreads();  // the previous chunk is done with the tiles
+        const int64_t ti = tile_index(p, s, h);
+        f32x4 *sin4 = reinterpret_cast<f32x4 *>(p.sin + ti * sl);
 #pragma unroll
-        for (int m = 0; m < PW; ++m) {
-            const int e = 4 * (m * NT + tid), a = e / DK, d = e - a * DK;
-            Ws[a][d] = rw[m].x;
-            Ws[a][d + 1] = rw[m].y;
-            Ws[a][d + 2] = rw[m].z;
-            Ws[a][d + 3] = rw[m].w;
-            Kds[a][d] = rk[m].x;
-            Kds[a][d + 1] = rk[m].y;
-            Kds[a][d + 2] = rk[m].z;
-            Kds[a][d + 3] = rk[m].w;
+        for (int i = 0; i < RB; ++i) __builtin_nontemporal_store(sacc[i], sin4 + ((RB * w + i) * NVB + vb) * 64 + l);
+        // new_v = U - W S for tokens 16 w .. 16 w + 15 (two accumulators
+        // for two independent MFMA chains).
+        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const float4 sv = sbuf[b][l];
+            f32x4 &x = (b & 1) ? x1 : x0;
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(wr[b].x, sv.x, x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(wr[b].y, sv.y, x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(wr[b].z, sv.z, x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(wr[b].w, sv.w, x, 0, 0, 0);
         }
+        f32x4 nv;
+        nv[0] = ur.x - (x0[0] + x1[0]);
+        nv[1] = ur.y - (x0[1] + x1[1]);
+        nv[2] = ur.z - (x0[2] + x1[2]);
+        nv[3] = ur.w - (x0[3] + x1[3]);
+        nbuf[w][l] = make_float4(nv[0], nv[1], nv[2], nv[3]);
+        __builtin_nontemporal_store(nv, reinterpret_cast<f32x4 *>(p.nv + ti * KC * DV) + (w * NVB + vb) * 64 + l);
+        if (c + 1 < sq.nseg) load_w(s + 1);
+        __syncthreads();  // new_v complete
 #pragma unroll
-        for (int m = 0; m < KC * VB / NT; ++m) {
-            const int e = m * NT + tid, a = e / VB, j = e - a * VB;
-            Us[a][j] = ru[m];
-        }
-        if (tid < DK) eg[tid] = re;
-        // This chunk's start state, for the output kernel.
-        for (int i = tid; i < DK * VB; i += NT) {
-            const int d = i / VB, j = i - d * VB;
-            p.sin[tile_index(p, s, h) * sl + (int64_t)d * DV + vb * VB + j] = Ss[d][j];
-        }
-        __syncthreads();
-        if (c + 1 < sq.nseg) load(s + 1);
-        // new_v = U - W S: NV columns of one token per thread.
-        {
-            constexpr int NV = KC * VB / NT, TPN = VB / NV;
-            const int a = tid / TPN, j0 = NV * (tid - a * TPN);
-            float acc[NV];
+        for (int i = 0; i < RB; ++i) {
+            sacc[i][0] *= er[i].x;
+            sacc[i][1] *= er[i].y;
+            sacc[i][2] *= er[i].z;
+            sacc[i][3] *= er[i].w;
 #pragma unroll
-            for (int y = 0; y < NV; ++y) acc[y] = Us[a][j0 + y];
-#pragma unroll 8
-            for (int d = 0; d < DK; ++d) {
-                const float wv = Ws[a][d];
-#pragma unroll
-                for (int y = 0; y < NV; ++y) acc[y] = fmaf(-wv, Ss[d][j0 + y], acc[y]);
-            }
-            float *nv = p.nv + (tile_index(p, s, h) * KC + a) * DV + vb * VB + j0;
-#pragma unroll
-            for (int y = 0; y < NV; ++y) {
-                Us[a][j0 + y] = acc[y];
-                nv[y] = acc[y];
+            for (int tt = 0; tt < 4; ++tt) {
+                const float4 nb = nbuf[tt][l];
+                sacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i][tt].x, nb.x, sacc[i], 0, 0, 0);
+                sacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i][tt].y, nb.y, sacc[i], 0, 0, 0);
+                sacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i][tt].z, nb.z, sacc[i], 0, 0, 0);
+                sacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i][tt].w, nb.w, sacc[i], 0, 0, 0);
             }
         }
-        __syncthreads();
-        // S = diag(exp(G_last)) S + (K * exp(G_last - G))^T new_v.
-        {
-            constexpr int TPR = NT / DK;        // threads per state row
-            constexpr int CPT = VB / TPR;       // columns per thread
-            const int d = tid / TPR, j0 = CPT * (tid - d * TPR);
-            float acc[CPT];
+        if (c + 1 < sq.nseg) load_k(s + 1);
 #pragma unroll
-            for (int y = 0; y < CPT; ++y) acc[y] = eg[d] * Ss[d][j0 + y];
-#pragma unroll 8
-            for (int a = 0; a < KC; ++a) {
-                const float kv = Kds[a][d];
-#pragma unroll
-                for (int y = 0; y < CPT; ++y) acc[y] = fmaf(kv, Us[a][j0 + y], acc[y]);
-            }
-#pragma unroll
-            for (int y = 0; y < CPT; ++y) Ss[d][j0 + y] = acc[y];
-        }
+        for (int i = 0; i < RB; ++i)
+            sbuf[RB * w + i][l] = make_float4(sacc[i][0], sacc[i][1], sacc[i][2], sacc[i][3]);
+        __syncthreads();  // the state complete; every wave is done with new_v
     }
-    __syncthreads();
     if (p.c.sfin)
-        for (int i = tid; i < DK * VB; i += NT) {
-            const int d = i / VB, j = i - d * VB;
-            p.c.sfin[((int64_t)n * H + h) * sl + (int64_t)d * DV + vb * VB + j] = Ss[d][j];
-        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = 16 * (RB * w + i) + 4 * lk + v;
+                p.c.sfin[((int64_t)n * H + h) * sl + (int64_t)row * DV + vb * VB + lr] = sacc[i][v];
+            }
 }
 
 // ---- output: one workgroup per (chunk, head).
@@ -571,15 +596,26 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p) {
         for (int m = 0; m < SP; ++m) rs[m] = src[m * NT + tid];
 #pragma unroll
         for (int m = 0; m < NP; ++m) rn[m] = nsrc[m * NT + tid];
+        // Both arrive as operand images: float4 f holds rows 16 (blk / (DV /
+        // 16)) + 4 kk .. +3 of column 16 (blk % (DV / 16)) + r, with
+        // blk = f / 64 and lane f % 64 = 16 kk + r.
 #pragma unroll
-        for (int m = 0; m < SP; ++m) reinterpret_cast<float4 *>(&Sv[0][0])[m * NT + tid] = rs[m];
+        for (int m = 0; m < SP; ++m) {
+            const int f = m * NT + tid, blk = f >> 6, ln = f & 63;
+            const int r0 = 16 * (blk / (DV / 16)) + 4 * (ln >> 4), j = 16 * (blk % (DV / 16)) + (ln & 15);
+            Sv[r0][j] = rs[m].x;
+            Sv[r0 + 1][j] = rs[m].y;
+            Sv[r0 + 2][j] = rs[m].z;
+            Sv[r0 + 3][j] = rs[m].w;
+        }
 #pragma unroll
         for (int m = 0; m < NP; ++m) {
-            const int e = 4 * (m * NT + tid), a = e / DV, j = e - a * DV;
-            Nv[a][j] = rn[m].x;
-            Nv[a][j + 1] = rn[m].y;
-            Nv[a][j + 2] = rn[m].z;
-            Nv[a][j + 3] = rn[m].w;
+            const int f = m * NT + tid, blk = f >> 6, ln = f & 63;
+            const int r0 = 16 * (blk / (DV / 16)) + 4 * (ln >> 4), j = 16 * (blk % (DV / 16)) + (ln & 15);
+            Nv[r0][j] = rn[m].x;
+            Nv[r0 + 1][j] = rn[m].y;
+            Nv[r0 + 2][j] = rn[m].z;
+            Nv[r0 + 3][j] = rn[m].w;
         }
     }
     __syncthreads();
