@@ -68,8 +68,7 @@ __device__ __forceinline__ int64_t tile_index(const KdaParams &p, int64_t s, int
 
 // 16 bytes of a row as floats: 8 bf16 or 4 fp32 values.
 template <typename Tin>
-__device__ __forceinline__ void load_piece(const Tin *src, float *out) {
-    const uint4 u = *reinterpret_cast<const uint4 *>(src);
+__device__ __forceinline__ void load_piece(const uint4 u, float *out) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
     if constexpr (sizeof(Tin) == 2) {
 #pragma unroll
@@ -114,43 +113,68 @@ __device__ __forceinline__ f32x4 block_product(const char *hi, const char *lo, i
     return acc;
 }
 
-// A chunk's rows of a [tokens, H, W] tensor (rows past n read as zeros),
-// moved through registers into LDS as tile[col][row] (TR) or tile[row][col]:
-// every thread issues all its 16-byte loads before its first LDS store, so
-// one chunk costs one memory latency.
-template <typename Tin, int W, int NT, bool TR, int STRIDE>
-__device__ __forceinline__ void stage_rows(const Tin *base, int64_t tok0, int H, int h, int n,
-                                           float *tile, int tid) {
-    constexpr int PE = 16 / sizeof(Tin);   // elements per piece
-    constexpr int PR = W / PE;             // pieces per row
-    constexpr int PT = (KC * PR + NT - 1) / NT;
-    float r[PT][PE];
+// A chunk's rows of a [tokens, H, W] tensor, held in registers as raw
+// 16-byte pieces (PT per thread; rows past n are zeros): load() issues the
+// loads and returns at once, store() converts to fp32 and writes the tile to
+// LDS as tile[col][row] (TR) or tile[row][col]. The persistent kernels load
+// the next item's rows while they work on the current one.
+template <typename Tin, int W, int NT>
+struct Rows {
+    static constexpr int PE = 16 / sizeof(Tin);  // elements per piece
+    static constexpr int PR = W / PE;            // pieces per row
+    static constexpr int PT = (KC * PR + NT - 1) / NT;
+    uint4 r[PT];
+    __device__ __forceinline__ void load(const Tin *base, int64_t tok0, int H, int h, int n, int tid) {
 #pragma unroll
-    for (int m = 0; m < PT; ++m) {
-        const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
-        if (idx < KC * PR && a < n) {
-            load_piece(base + ((tok0 + a) * H + h) * W + pc * PE, r[m]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < PE; ++e) r[m][e] = 0.f;
+        for (int m = 0; m < PT; ++m) {
+            const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
+            r[m] = make_uint4(0u, 0u, 0u, 0u);
+            if (idx < KC * PR && a < n)
+                r[m] = *reinterpret_cast<const uint4 *>(base + ((tok0 + a) * H + h) * W + pc * PE);
         }
     }
+    template <bool TR, int STRIDE>
+    __device__ __forceinline__ void store(float *tile, int tid) const {
 #pragma unroll
-    for (int m = 0; m < PT; ++m) {
-        const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
-        if (idx >= KC * PR) continue;
+        for (int m = 0; m < PT; ++m) {
+            const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
+            if (idx >= KC * PR) continue;
+            float f[PE];
+            load_piece<Tin>(r[m], f);
 #pragma unroll
-        for (int e = 0; e < PE; ++e) {
-            const int col = pc * PE + e;
-            if (TR) tile[col * STRIDE + a] = r[m][e];
-            else tile[a * STRIDE + col] = r[m][e];
+            for (int e = 0; e < PE; ++e) {
+                const int col = pc * PE + e;
+                if (TR) tile[col * STRIDE + a] = f[e];
+                else tile[a * STRIDE + col] = f[e];
+            }
         }
     }
+};
+
+// A (chunk, head) item of the persistent kernels: item = s H + h.
+// len < 0 marks a table row with no segment; past the last item len is -1.
+struct Item {
+    int s, h, n, len;
+    int64_t tok0;
+};
+__device__ __forceinline__ Item item_at(const KdaParams &p, int64_t item, int64_t nitems) {
+    Item it{0, 0, 0, -1, 0};
+    if (item < nitems) {
+        it.s = (int)(item / p.c.H);
+        it.h = (int)(item - (int64_t)it.s * p.c.H);
+        const SegEntry se = seg_at(p.c, it.s);
+        it.len = se.len;
+        it.n = se.len > 0 ? se.len : 0;
+        it.tok0 = se.tok0;
+    }
+    return it;
 }
 
-// ---- prep: one workgroup per (chunk, head).
+// ---- prep: persistent over the (chunk, head) items, one workgroup per CU;
+// the next item's k, g, v rows and beta load into registers while the
+// current one is worked on.
 template <typename Tin, int DK, int DV>
-__global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
+__global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nitems) {
     constexpr int NT = 512;
     constexpr int MP = KC + 4;         // row stride of A/T: 16-byte aligned rows
     __shared__ float Kt[DK][KP];       // K^T; later (diag(beta) K * exp(G))^T
@@ -167,22 +191,36 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
     static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xb) + sizeof(bs) <= kLdsPerCU,
                   "the workgroup must fit one CU's LDS");
     const int H = p.c.H;
-    const int s = blockIdx.x / H;
-    const int h = blockIdx.x - s * H;
-    if (s >= p.c.nseg_max) return;
-    const SegEntry se = seg_at(p.c, s);
-    if (se.len < 0) return;
-    const int n = se.len;
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63;
     const Tin *__restrict__ kg = static_cast<const Tin *>(p.c.k);
     const Tin *__restrict__ vg = static_cast<const Tin *>(p.c.v);
 
-    // Tiles of the chunk; rows past its end are zeros (zero gate, beta, key).
-    if (tid < KC) bs[tid] = tid < n ? p.beta[(se.tok0 + tid) * H + h] : 0.f;
-    stage_rows<Tin, DK, NT, true, KP>(kg, se.tok0, H, h, n, &Kt[0][0], tid);
-    stage_rows<float, DK, NT, true, KP>(p.c.g, se.tok0, H, h, n, &Gt[0][0], tid);
-    stage_rows<Tin, DV, NT, false, DV + 1>(vg, se.tok0, H, h, n, &Vs[0][0], tid);
+    // Rows past a chunk's end are zeros (zero gate, beta, key).
+    Rows<Tin, DK, NT> rk;
+    Rows<float, DK, NT> rg;
+    Rows<Tin, DV, NT> rv;
+    float rb = 0.f;
+    auto fetch = [&](int64_t item) {
+        const Item it = item_at(p, item, nitems);
+        rk.load(kg, it.tok0, H, it.h, it.n, tid);
+        rg.load(p.c.g, it.tok0, H, it.h, it.n, tid);
+        rv.load(vg, it.tok0, H, it.h, it.n, tid);
+        rb = tid < it.n ? p.beta[(it.tok0 + tid) * H + it.h] : 0.f;
+    };
+    fetch(blockIdx.x);
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const Item it = item_at(p, item, nitems);
+    if (it.len < 0) {
+        fetch(item + gridDim.x);
+        continue;
+    }
+    const int s = it.s, h = it.h;
+    if (tid < KC) bs[tid] = rb;
+    rk.template store<true, KP>(&Kt[0][0], tid);
+    rg.template store<true, KP>(&Gt[0][0], tid);
+    rv.template store<false, DV + 1>(&Vs[0][0], tid);
+    fetch(item + gridDim.x);
     __syncthreads();
     for (int i = tid; i < KC * DV; i += NT) {
         const int a = i / DV, j = i - a * DV;
@@ -372,6 +410,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p) {
                 make_float4(acc[0][y], acc[1][y], acc[2][y], acc[3][y]);
         }
     }
+    __syncthreads();  // the next item's tiles overwrite these
+    }
 }
 
 // ---- chain: one workgroup of four waves per (sequence, head, block of 16
@@ -503,161 +543,175 @@ __global__ __launch_bounds__(CHAIN_NT) void kda_chain_kernel(KdaParams p) {
             }
 }
 
-// ---- output: one workgroup per (chunk, head).
+// ---- output: one workgroup per (chunk, head). L inside the diagonal 16 x 16
+// blocks on the vector ALUs (exponents taken directly), below them as bf16
+// hi/lo products on the matrix cores (split at the block's first token);
+// then O = scale ((Q * exp(G)) S + L new_v) on fp32 16 x 16 x 4 MFMAs, whose
+// B operands are the chain's start-state and new_v images as loaded. Wave w
+// takes column block w mod (Dv / 16) and TPW token blocks. Persistent over
+// the (chunk, head) items, one workgroup per CU: the next item's q, k, g rows
+// load into registers once the current ones are in LDS, and its images once
+// the current output is formed.
 template <typename Tin, int DK, int DV>
-__global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p) {
+__global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t nitems) {
     constexpr int NT = 512;
-    // LDS map (bytes): Q^T, K^T, G^T [DK][KP]; L [64][KP]; X [64][DK + 1]
-    // (sized for the larger of Dk and Dv).
-    // Once L is formed, the start state [DK][DV] takes the K^T and G^T space
-    // and new_v [64][DV + 1] the X space.
-    constexpr int O_QT = 0;
-    constexpr int O_KT = O_QT + DK * KP * 4;
-    constexpr int O_GT = O_KT + DK * KP * 4;
-    constexpr int O_L = O_GT + DK * KP * 4;
-    constexpr int O_X = O_L + KC * KP * 4;
-    constexpr int O_BYTES = O_X + KC * ((DK > DV ? DK : DV) + 1) * 4;
-    static_assert(DK * DV * 4 <= O_L - O_KT, "the start state must fit the K^T and G^T space");
-    static_assert(KC * (DV + 1) * 4 <= O_BYTES - O_X, "new_v must fit the X space");
-    static_assert(O_BYTES <= kLdsPerCU, "the workgroup must fit one CU's LDS");
-    __shared__ __attribute__((aligned(16))) char lds[O_BYTES];
-    auto Qt = reinterpret_cast<float(*)[KP]>(lds + O_QT);
-    auto Kt = reinterpret_cast<float(*)[KP]>(lds + O_KT);
-    auto Gt = reinterpret_cast<float(*)[KP]>(lds + O_GT);
-    auto Ls = reinterpret_cast<float(*)[KP]>(lds + O_L);
-    auto Xs = reinterpret_cast<float(*)[DK + 1]>(lds + O_X);
-    auto Sv = reinterpret_cast<float(*)[DV]>(lds + O_KT);
-    auto Nv = reinterpret_cast<float(*)[DV + 1]>(lds + O_X);
+    constexpr int NB = DK / 16;        // key blocks
+    constexpr int NCB = DV / 16;       // column blocks
+    constexpr int TPW = NCB / 2;       // token blocks per wave
+    constexpr int LP = KC + 4;         // row stride of L: 16-byte aligned rows
+    __shared__ float Qt[DK][KP];       // Q^T, then (Q * exp(G))^T
+    __shared__ float Kt[DK][KP];
+    __shared__ float Gt[DK][KP];
+    __shared__ __attribute__((aligned(16))) float Ls[KC][LP];
+    __shared__ __attribute__((aligned(16))) char Xb[2 * KC * DK * 2];  // bf16 hi and lo tiles
+    static_assert(sizeof(Qt) + sizeof(Kt) + sizeof(Gt) + sizeof(Ls) + sizeof(Xb) <= kLdsPerCU,
+                  "the workgroup must fit one CU's LDS");
+    char *const Xh = Xb;
+    char *const Xl = Xb + KC * DK * 2;
 
     const int H = p.c.H;
-    const int s = blockIdx.x / H;
-    const int h = blockIdx.x - s * H;
-    if (s >= p.c.nseg_max) return;
-    const SegEntry se = seg_at(p.c, s);
-    if (se.len <= 0) return;
-    const int n = se.len;
     const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63;
+    const int lr = l & 15, lk = l >> 4;
+    const int cb = w % NCB, tt0 = (w / NCB) * TPW;
     const Tin *__restrict__ qg = static_cast<const Tin *>(p.c.q);
     const Tin *__restrict__ kg = static_cast<const Tin *>(p.c.k);
     Tin *__restrict__ og = static_cast<Tin *>(p.c.out);
 
-    stage_rows<Tin, DK, NT, true, KP>(qg, se.tok0, H, h, n, &Qt[0][0], tid);
-    stage_rows<Tin, DK, NT, true, KP>(kg, se.tok0, H, h, n, &Kt[0][0], tid);
-    stage_rows<float, DK, NT, true, KP>(p.c.g, se.tok0, H, h, n, &Gt[0][0], tid);
-    __syncthreads();
-    {
-        const int w = tid >> 6, l = tid & 63;
-        for (int d = w; d < DK; d += NT / 64) Gt[d][l] = wave_prefix_sum(Gt[d][l]);
+    Rows<Tin, DK, NT> rq, rk;
+    Rows<float, DK, NT> rg;
+    auto fetch_rows = [&](int64_t item) {
+        const Item it = item_at(p, item, nitems);
+        rq.load(qg, it.tok0, H, it.h, it.n, tid);
+        rk.load(kg, it.tok0, H, it.h, it.n, tid);
+        rg.load(p.c.g, it.tok0, H, it.h, it.n, tid);
+    };
+    // The B operands: start-state blocks (b, cb) and new_v blocks (tt, cb).
+    f32x4 sb[NB], nb[4];
+    auto fetch_ops = [&](int64_t item) {
+        const Item it = item_at(p, item, nitems);
+        if (it.len <= 0) return;
+        const int64_t ti = tile_index(p, it.s, it.h);
+        const f32x4 *simg = reinterpret_cast<const f32x4 *>(p.sin + ti * DK * DV);
+        const f32x4 *nimg = reinterpret_cast<const f32x4 *>(p.nv + ti * KC * DV);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) sb[b] = __builtin_nontemporal_load(simg + (b * NCB + cb) * 64 + l);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) nb[t] = __builtin_nontemporal_load(nimg + (t * NCB + cb) * 64 + l);
+    };
+    fetch_rows(blockIdx.x);
+    fetch_ops(blockIdx.x);
+    for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const Item it = item_at(p, item, nitems);
+    const int64_t next = item + gridDim.x;
+    if (it.len <= 0) {
+        fetch_rows(next);
+        fetch_ops(next);
+        continue;
     }
+    const int h = it.h, n = it.n;
+    rq.template store<true, KP>(&Qt[0][0], tid);
+    rk.template store<true, KP>(&Kt[0][0], tid);
+    rg.template store<true, KP>(&Gt[0][0], tid);
+    fetch_rows(next);
+    __syncthreads();
+    for (int d = w; d < DK; d += NT / 64) Gt[d][l] = wave_prefix_sum(Gt[d][l]);
     __syncthreads();
 
-    // L inside the diagonal blocks (a >= b), exponent taken directly.
-    for (int i = tid; i < 4 * 136; i += NT) {
-        const int blk = i / 136, r = i - blk * 136;
-        int ai = 0;
-        while ((ai + 2) * (ai + 1) / 2 <= r) ++ai;
-        const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai + 1) / 2);
+    // L inside the diagonal blocks: one pair (a > b) per thread, the
+    // diagonal itself (no decay) on the rest, zeros above it.
+    if (tid < 4 * 120) {
+        const int blk = tid / 120, r = tid - blk * 120;
+        int ai = 1;
+        while ((ai + 1) * ai / 2 <= r) ++ai;
+        const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai - 1) / 2);
         float acc = 0.f;
         for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
         Ls[a][b] = acc;
+        Ls[b][a] = 0.f;
+    } else {
+        for (int a = tid - 4 * 120; a < KC; a += NT - 4 * 120) {
+            float acc = 0.f;
+            for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a], Kt[d][a], acc);
+            Ls[a][a] = acc;
+        }
     }
-    // L below the diagonal blocks, split at the block's first token c.
+    // L below the diagonal blocks: block row I against tokens b < c = 16 I,
+    // queries as Q exp(G - G_c) and keys as K exp(G_c - G), bf16 hi/lo.
     for (int I = 1; I < 4; ++I) {
         const int c = 16 * I;
-        __syncthreads();
-        for (int i = tid; i < (c + 16) * DK; i += NT) {
-            const int a = i / DK, d = i - a * DK;
-            Xs[a][d] = a < c ? Kt[d][a] * __expf(Gt[d][c] - Gt[d][a])
-                             : Qt[d][a] * __expf(Gt[d][a] - Gt[d][c]);
+        __syncthreads();  // the previous block row's products are done with the tiles
+        for (int i = tid; i < (c + 16) * DK / 2; i += NT) {
+            const int a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
+            float x[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                x[e] = a < c ? Kt[d + e][a] * __expf(Gt[d + e][c] - Gt[d + e][a])
+                             : Qt[d + e][a] * __expf(Gt[d + e][a] - Gt[d + e][c]);
+            const uint32_t u0 = __float_as_uint(x[0]), u1 = __float_as_uint(x[1]);
+            const int off = brow_off<DK>(a, d >> 3) + 2 * (d & 7);
+            *reinterpret_cast<uint32_t *>(Xh + off) = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+            *reinterpret_cast<uint32_t *>(Xl + off) =
+                pack_f32(x[0] - __uint_as_float(u0 & 0xffff0000u), x[1] - __uint_as_float(u1 & 0xffff0000u));
         }
         __syncthreads();
-        for (int i = tid; i < 16 * c; i += NT) {
-            const int ai = i / c, b = i - ai * c;
-            const int a = c + ai;
-            float acc = 0.f;
-            for (int d = 0; d < DK; ++d) acc = fmaf(Xs[a][d], Xs[b][d], acc);
-            Ls[a][b] = acc;
+        if (w < I) {
+            const f32x4 acc = block_product<DK>(Xh, Xl, I, w, l);
+            *reinterpret_cast<float4 *>(&Ls[c + lr][16 * w + 4 * lk]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
-    __syncthreads();
-    // Q * exp(G) in place; then the start state and new_v over K^T, G^T, X.
+    // Q * exp(G) in place.
     for (int i = tid; i < KC * DK; i += NT) {
         const int d = i / KC, a = i - d * KC;
         Qt[d][a] *= __expf(Gt[d][a]);
     }
     __syncthreads();
-    const int64_t ti = tile_index(p, s, h);
-    {
-        constexpr int SP = DK * DV / 4 / NT, NP = KC * DV / 4 / NT;
-        const float4 *src = reinterpret_cast<const float4 *>(p.sin + ti * DK * DV);
-        const float4 *nsrc = reinterpret_cast<const float4 *>(p.nv + ti * KC * DV);
-        float4 rs[SP], rn[NP];
+
+    // O blocks (tt, cb): A = (Q exp G)[16 tt + r][16 b + 4 kk + k4] against the
+    // start-state image, then L[16 tt + r][16 t + 4 kk + k4] against new_v.
 #pragma unroll
-        for (int m = 0; m < SP; ++m) rs[m] = src[m * NT + tid];
+    for (int j = 0; j < TPW; ++j) {
+        const int tt = tt0 + j;
+        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int m = 0; m < NP; ++m) rn[m] = nsrc[m * NT + tid];
-        // Both arrive as operand images: float4 f holds rows 16 (blk / (DV /
-        // 16)) + 4 kk .. +3 of column 16 (blk % (DV / 16)) + r, with
-        // blk = f / 64 and lane f % 64 = 16 kk + r.
+        for (int b = 0; b < NB; ++b) {
+            f32x4 &x = (b & 1) ? x1 : x0;
 #pragma unroll
-        for (int m = 0; m < SP; ++m) {
-            const int f = m * NT + tid, blk = f >> 6, ln = f & 63;
-            const int r0 = 16 * (blk / (DV / 16)) + 4 * (ln >> 4), j = 16 * (blk % (DV / 16)) + (ln & 15);
-            Sv[r0][j] = rs[m].x;
-            Sv[r0 + 1][j] = rs[m].y;
-            Sv[r0 + 2][j] = rs[m].z;
-            Sv[r0 + 3][j] = rs[m].w;
+            for (int k4 = 0; k4 < 4; ++k4)
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(Qt[16 * b + 4 * lk + k4][16 * tt + lr], sb[b][k4], x, 0, 0, 0);
         }
 #pragma unroll
-        for (int m = 0; m < NP; ++m) {
-            const int f = m * NT + tid, blk = f >> 6, ln = f & 63;
-            const int r0 = 16 * (blk / (DV / 16)) + 4 * (ln >> 4), j = 16 * (blk % (DV / 16)) + (ln & 15);
-            Nv[r0][j] = rn[m].x;
-            Nv[r0 + 1][j] = rn[m].y;
-            Nv[r0 + 2][j] = rn[m].z;
-            Nv[r0 + 3][j] = rn[m].w;
+        for (int t = 0; t < 4; ++t) {
+            if (t > tt) break;
+            const float4 lv = *reinterpret_cast<const float4 *>(&Ls[16 * tt + lr][16 * t + 4 * lk]);
+            f32x4 &x = (t & 1) ? x1 : x0;
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.x, nb[t][0], x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.y, nb[t][1], x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.z, nb[t][2], x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.w, nb[t][3], x, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int a = 16 * tt + 4 * lk + v;
+            if (a < n) store_elem(og, ((it.tok0 + a) * H + h) * DV + 16 * cb + lr, p.c.scale * (x0[v] + x1[v]));
         }
     }
-    __syncthreads();
-    // O, 4 tokens x 4 value columns per thread.
-    for (int i = tid; i < (KC / 4) * (DV / 4); i += NT) {
-        const int at = i / (DV / 4), a0 = 4 * at, j0 = 4 * (i - at * (DV / 4));
-        float acc[4][4] = {};
-        for (int d = 0; d < DK; ++d) {
-            const float4 sv = *reinterpret_cast<const float4 *>(&Sv[d][j0]);
-            const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const float qv = Qt[d][a0 + x];
-#pragma unroll
-                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(qv, svv[y], acc[x][y]);
-            }
-        }
-        for (int b = 0; b <= a0 + 3; ++b) {
-            float lv[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) lv[x] = b <= a0 + x ? Ls[a0 + x][b] : 0.f;
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                const float nvv = Nv[b][j0 + y];
-#pragma unroll
-                for (int x = 0; x < 4; ++x) acc[x][y] = fmaf(lv[x], nvv, acc[x][y]);
-            }
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            if (a0 + x >= n) continue;
-            const int64_t e = ((se.tok0 + a0 + x) * H + h) * DV + j0;
-#pragma unroll
-            for (int y = 0; y < 4; ++y) store_elem(og, e + y, p.c.scale * acc[x][y]);
-        }
+    fetch_ops(next);
+    __syncthreads();  // the next item's tiles overwrite these
     }
 }
 
 template <typename Tin, int DK, int DV>
 hipError_t launch_dims(const KdaParams &p, hipStream_t st) {
-    const unsigned units = (unsigned)((int64_t)p.c.nseg_max * p.c.H);
-    hipLaunchKernelGGL((kda_prep_kernel<Tin, DK, DV>), dim3(units), dim3(512), 0, st, p);
+    // The prep and output kernels are persistent, one workgroup per CU (each
+    // takes most of a CU's LDS).
+    const int64_t nitems = (int64_t)p.c.nseg_max * p.c.H;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    const unsigned wgs = (unsigned)std::min<int64_t>(nitems, cus);
+    hipLaunchKernelGGL((kda_prep_kernel<Tin, DK, DV>), dim3(wgs), dim3(512), 0, st, p, nitems);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // xcd_unit_map covers every (sequence, head) when the unit count is
@@ -666,7 +720,7 @@ hipError_t launch_dims(const KdaParams &p, hipStream_t st) {
     hipLaunchKernelGGL((kda_chain_kernel<DK, DV>), dim3(chains), dim3(CHAIN_NT), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_output_kernel<Tin, DK, DV>), dim3(units), dim3(512), 0, st, p);
+    hipLaunchKernelGGL((kda_output_kernel<Tin, DK, DV>), dim3(wgs), dim3(512), 0, st, p, nitems);
     return hipGetLastError();
 }
 
