@@ -365,49 +365,45 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
         Ms[a][b] = b <= a ? tb[tbo(a >> 4, b >> 4) + (a & 15) * TBR + (b & 15)] : 0.f;
     }
     __syncthreads();
-    // W = T X and U = T (diag(beta) V), 4 tokens x 4 columns per thread; T is
-    // lower triangular.
-    for (int i = tid; i < (KC / 4) * (DK / 4); i += NT) {
-        const int at = i / (DK / 4), a0 = 4 * at, d0 = 4 * (i - at * (DK / 4));
-        float acc[4][4] = {};
-        for (int b = 0; b <= a0 + 3; ++b) {
-            float tv[4], xv[4];
+    // W = T X and U = T (diag(beta) V) on fp32 16 x 16 x 4 MFMAs, straight
+    // into the chain's operand images. W comes out transposed, W^T = X^T T^T,
+    // so that each accumulator quad is one W image float4 (4 key dims of a
+    // token); U's quads are U image float4s as they stand. T is lower
+    // triangular with zeros above the diagonal, so block (tt, .) sums over
+    // token blocks kb <= tt only. A job is one column block of W or of U
+    // (all four token blocks); wave w takes jobs w, w + 8, ...
+    {
+        const int lr = l & 15, lk = l >> 4;
+        constexpr int NBK = DK / 16, NBV = DV / 16;
+        for (int job = w; job < NBK + NBV; job += NT / 64) {
+            const bool isw = job < NBK;
+            const int cb = isw ? job : job - NBK;
+            // The operand that is not T, for token blocks kb = 0..3: X^T
+            // [16 cb + r][16 kb + 4 kk + k4] or (beta V)[16 kb + 4 kk + k4][16 cb + r].
+            float o[4][4];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) tv[x] = Ms[a0 + x][b];
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int y = 0; y < 4; ++y) xv[y] = Kt[d0 + y][b];
+                for (int k4 = 0; k4 < 4; ++k4)
+                    o[kb][k4] = isw ? Kt[16 * cb + lr][16 * kb + 4 * lk + k4] : Vs[16 * kb + 4 * lk + k4][16 * cb + lr];
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int tt = 0; tt < 4; ++tt) {
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(tv[x], xv[y], acc[x][y]);
-        }
+                for (int kb = 0; kb <= tt; ++kb) {
+                    const float4 t4 = *reinterpret_cast<const float4 *>(&Ms[16 * tt + lr][16 * kb + 4 * lk]);
+                    const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int a = a0 + x;
-            reinterpret_cast<float4 *>(tile)[((a >> 4) * (DK / 16) + (d0 >> 4)) * 64 + 16 * ((d0 >> 2) & 3) +
-                                             (a & 15)] = make_float4(acc[x][0], acc[x][1], acc[x][2], acc[x][3]);
-        }
-    }
-    for (int i = tid; i < (KC / 4) * (DV / 4); i += NT) {
-        const int at = i / (DV / 4), a0 = 4 * at, j0 = 4 * (i - at * (DV / 4));
-        float acc[4][4] = {};
-        for (int b = 0; b <= a0 + 3; ++b) {
-            float tv[4], vv[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) tv[x] = Ms[a0 + x][b];
-#pragma unroll
-            for (int y = 0; y < 4; ++y) vv[y] = Vs[b][j0 + y];
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int y = 0; y < 4; ++y) acc[x][y] = fmaf(tv[x], vv[y], acc[x][y]);
-        }
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int j = j0 + y;
-            reinterpret_cast<float4 *>(tile + 2 * KC * DK)[((a0 >> 4) * (DV / 16) + (j >> 4)) * 64 +
-                                                           16 * ((a0 >> 2) & 3) + (j & 15)] =
-                make_float4(acc[0][y], acc[1][y], acc[2][y], acc[3][y]);
+                    for (int k4 = 0; k4 < 4; ++k4)
+                        x = isw ? __builtin_amdgcn_mfma_f32_16x16x4f32(o[kb][k4], tv[k4], x, 0, 0, 0)
+                                : __builtin_amdgcn_mfma_f32_16x16x4f32(tv[k4], o[kb][k4], x, 0, 0, 0);
+                }
+                const float4 r = make_float4(x[0], x[1], x[2], x[3]);
+                if (isw)
+                    reinterpret_cast<float4 *>(tile)[(tt * NBK + cb) * 64 + l] = r;
+                else
+                    reinterpret_cast<float4 *>(tile + 2 * KC * DK)[(tt * NBV + cb) * 64 + l] = r;
+            }
         }
     }
     __syncthreads();  // the next item's tiles overwrite these
