@@ -114,23 +114,28 @@ __device__ __forceinline__ f32x4 block_product(const char *hi, const char *lo, i
 }
 
 // A chunk's rows of a [tokens, H, W] tensor, held in registers as raw
-// 16-byte pieces (PT per thread; rows past n are zeros): load() issues the
-// loads and returns at once, store() converts to fp32 and writes the tile to
-// LDS as tile[col][row] (TR) or tile[row][col]. The persistent kernels load
-// the next item's rows while they work on the current one.
+// 16-byte pieces (PT per thread): load() issues the loads and returns at
+// once, store() converts to fp32 and writes the tile to LDS as
+// tile[col][row] (TR) or tile[row][col]. The persistent kernels load the next
+// item's rows while they work on the current one. The loads go through a
+// buffer resource whose range ends at row n, so rows past it read as zeros
+// with no branch, and every path issues the same loads (which keeps the
+// compiler's waits on them exact). Offsets stay below 2^31 bytes for
+// H <= 65536 and W <= 128 fp32.
 template <typename Tin, int W, int NT>
 struct Rows {
     static constexpr int PE = 16 / sizeof(Tin);  // elements per piece
     static constexpr int PR = W / PE;            // pieces per row
-    static constexpr int PT = (KC * PR + NT - 1) / NT;
-    uint4 r[PT];
+    static constexpr int PT = KC * PR / NT;
+    static_assert(KC * PR % NT == 0, "whole pieces per thread");
+    u32x4 r[PT];
     __device__ __forceinline__ void load(const Tin *base, int64_t tok0, int H, int h, int n, int tid) {
+        const int bytes = n > 0 ? ((n - 1) * H * W + W) * (int)sizeof(Tin) : 0;
+        const buf_t rs = buf_rsrc(base + (tok0 * H + h) * W, bytes);
 #pragma unroll
         for (int m = 0; m < PT; ++m) {
             const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
-            r[m] = make_uint4(0u, 0u, 0u, 0u);
-            if (idx < KC * PR && a < n)
-                r[m] = *reinterpret_cast<const uint4 *>(base + ((tok0 + a) * H + h) * W + pc * PE);
+            r[m] = buf_ld16(rs, (uint32_t)((a * H * W + pc * PE) * (int)sizeof(Tin)));
         }
     }
     template <bool TR, int STRIDE>
@@ -138,9 +143,8 @@ struct Rows {
 #pragma unroll
         for (int m = 0; m < PT; ++m) {
             const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
-            if (idx >= KC * PR) continue;
             float f[PE];
-            load_piece<Tin>(r[m], f);
+            load_piece<Tin>(make_uint4(r[m][0], r[m][1], r[m][2], r[m][3]), f);
 #pragma unroll
             for (int e = 0; e < PE; ++e) {
                 const int col = pc * PE + e;
@@ -206,7 +210,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
         rk.load(kg, it.tok0, H, it.h, it.n, tid);
         rg.load(p.c.g, it.tok0, H, it.h, it.n, tid);
         rv.load(vg, it.tok0, H, it.h, it.n, tid);
-        rb = tid < it.n ? p.beta[(it.tok0 + tid) * H + it.h] : 0.f;
+        rb = buf_ld_f32(buf_rsrc(p.beta + it.tok0 * H + it.h, it.n > 0 ? (it.n - 1) * H * 4 + 4 : 0),
+                        (uint32_t)(tid * H * 4));
     };
     fetch(blockIdx.x);
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
@@ -455,17 +460,21 @@ __global__ __launch_bounds__(CHAIN_NT) void kda_chain_kernel(KdaParams p) {
             sacc[i][v] = p.c.s0 ? p.c.s0[((int64_t)n * H + h) * sl + (int64_t)row * DV + vb * VB + lr] : 0.f;
         }
 
-    float4 wr[NB], kr[RB][4], ur, er[RB];
+    // The operands are double-buffered: chunk c's sit in buffer c mod 2 and
+    // are replaced by chunk c + 2's once used, so their loads have two
+    // chunks' time to land (the first of a head's column blocks to ask for a
+    // chunk's W and Kd fetches them from HBM).
+    float4 wr0[NB], wr1[NB], ur0, ur1, kr0[RB][4], kr1[RB][4], er0[RB], er1[RB];
     auto tile_at = [&](int64_t s) {
         return reinterpret_cast<const float4 *>(p.tiles + tile_index(p, s, h) * tf);
     };
-    auto load_w = [&](int64_t s) {
+    auto load_w = [&](int64_t s, float4 (&wr)[NB], float4 &ur) {
         const float4 *t = tile_at(s);
 #pragma unroll
         for (int b = 0; b < NB; ++b) wr[b] = t[(w * NB + b) * 64 + l];
         ur = t[KC * DK / 2 + (w * NVB + vb) * 64 + l];
     };
-    auto load_k = [&](int64_t s) {
+    auto load_k = [&](int64_t s, float4 (&kr)[RB][4], float4 (&er)[RB]) {
         const float4 *t = tile_at(s);
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
@@ -474,14 +483,20 @@ __global__ __launch_bounds__(CHAIN_NT) void kda_chain_kernel(KdaParams p) {
             er[i] = t[(2 * KC * DK + KC * DV) / 4 + 4 * (RB * w + i) + lk];
         }
     };
+    // Prefetches past the sequence's last chunk reload that chunk (unused):
+    // the loads are unconditional, so every path issues the same ones.
+    const int64_t last = sq.first + sq.nseg - 1;
+    auto clampc = [&](int64_t s) { return s < last ? s : last; };
     if (sq.nseg > 0) {
-        load_w(sq.first);
-        load_k(sq.first);
+        load_w(sq.first, wr0, ur0);
+        load_k(sq.first, kr0, er0);
+        load_w(clampc(sq.first + 1), wr1, ur1);
+        load_k(clampc(sq.first + 1), kr1, er1);
     }
 #pragma unroll
     for (int i = 0; i < RB; ++i) sbuf[RB * w + i][l] = make_float4(sacc[i][0], sacc[i][1], sacc[i][2], sacc[i][3]);
     __syncthreads();
-    for (int c = 0; c < sq.nseg; ++c) {
+    auto step = [&](int c, float4 (&wr)[NB], float4 &ur, float4 (&kr)[RB][4], float4 (&er)[RB]) {
         const int64_t s = sq.first + c;
         const int64_t ti = tile_index(p, s, h);
         f32x4 *sin4 = reinterpret_cast<f32x4 *>(p.sin + ti * sl);
@@ -506,7 +521,7 @@ __global__ __launch_bounds__(CHAIN_NT) void kda_chain_kernel(KdaParams p) {
         nv[3] = ur.w - (x0[3] + x1[3]);
         nbuf[w][l] = make_float4(nv[0], nv[1], nv[2], nv[3]);
         __builtin_nontemporal_store(nv, reinterpret_cast<f32x4 *>(p.nv + ti * KC * DV) + (w * NVB + vb) * 64 + l);
-        if (c + 1 < sq.nseg) load_w(s + 1);
+        load_w(clampc(s + 2), wr, ur);
         __syncthreads();  // new_v complete
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
@@ -523,11 +538,15 @@ __global__ __launch_bounds__(CHAIN_NT) void kda_chain_kernel(KdaParams p) {
                 sacc[i] = __builtin_amdgcn_mfma_f32_16x16x4f32(kr[i][tt].w, nb.w, sacc[i], 0, 0, 0);
             }
         }
-        if (c + 1 < sq.nseg) load_k(s + 1);
+        load_k(clampc(s + 2), kr, er);
 #pragma unroll
         for (int i = 0; i < RB; ++i)
             sbuf[RB * w + i][l] = make_float4(sacc[i][0], sacc[i][1], sacc[i][2], sacc[i][3]);
         __syncthreads();  // the state complete; every wave is done with new_v
+    };
+    for (int c = 0; c < sq.nseg; c += 2) {
+        step(c, wr0, ur0, kr0, er0);
+        if (c + 1 < sq.nseg) step(c + 1, wr1, ur1, kr1, er1);
     }
     if (p.c.sfin)
 #pragma unroll
@@ -584,9 +603,10 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
     };
     // The B operands: start-state blocks (b, cb) and new_v blocks (tt, cb).
     f32x4 sb[NB], nb[4];
+    // Loaded for every item, also those with no tokens (their images hold
+    // anything, and go unused), so that every path issues the same loads.
     auto fetch_ops = [&](int64_t item) {
         const Item it = item_at(p, item, nitems);
-        if (it.len <= 0) return;
         const int64_t ti = tile_index(p, it.s, it.h);
         const f32x4 *simg = reinterpret_cast<const f32x4 *>(p.sin + ti * DK * DV);
         const f32x4 *nimg = reinterpret_cast<const f32x4 *>(p.nv + ti * KC * DV);
