@@ -56,7 +56,7 @@ GDN_PREFILL = "gdn_prefill_bf16_h32_t8192_d128"
 GDN_DECODE = "gdn_decode_bf16_n256_h32_d128_x64"
 KDA_PREFILL = "kda_prefill_bf16_h32_t8192_d128"
 KDA_DECODE = "kda_decode_bf16_n256_h32_d128_x64"
-FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector ALU, vendor figure
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32, vendor figure: dense matrix cores and vector ALUs alike
 # The kernels of one call of each workload, as rocprofv3 names them.
 CALL_KERNELS = {
     PREFILL: ["chunk_mfma_kernel<true, false>", "scan_kernel<128, 128>", "chunk_halves_kernel"],
@@ -809,7 +809,8 @@ def kda_prefill_flops(T, H, D):
 def bench_kda(args, torch, sgla, W, dev):
     """The gated delta rule with one gate per key dim (KDA) on the same
     shapes: prefill B=1, T=8192, H=32, Dk=Dv=128 (sgla_kda_chunk_fwd, fp32
-    arithmetic on the vector ALUs) and the batched decode, 256 x 32 heads, 64
+    contractions on the matrix cores, the pairwise decay factors on the
+    vector ALUs) and the batched decode, 256 x 32 heads, 64
     successive steps (sgla_kda_recurrent_step); "kda" inputs (L2-normalised q
     and k, per-dim gates, beta = sigmoid(N(0, 1)))."""
     out = {}
@@ -834,8 +835,8 @@ def bench_kda(args, torch, sgla, W, dev):
                       "tokens_per_s": 8192 / (per_avg * 1e-3),
                       "per_call_ms": {"mean": per_avg, "median_single": median(per), "min_single": min(per)},
                       "achieved_GBs": nbytes / (per_avg * 1e-3) / 1e9,
-                      "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS,
-                                   "unit": "TFLOP/s", "frac": tf / FP32_VALU_PEAK_TFLOPS,
+                      "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": tf / FP32_PEAK_TFLOPS,
                                    "traffic": recorded_traffic(KDA_PREFILL),
                                    "kernel": "sgla_kda_chunk_fwd (whole call: per-chunk UT "
                                              "transform, state chain, per-chunk output; fp32)",
