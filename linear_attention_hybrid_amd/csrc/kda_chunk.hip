@@ -676,25 +676,72 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
             *reinterpret_cast<float4 *>(&Ls[c + lr][16 * w + 4 * lk]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
         }
     }
-    // Q * exp(G) in place.
-    for (int i = tid; i < KC * DK; i += NT) {
-        const int d = i / KC, a = i - d * KC;
-        Qt[d][a] *= __expf(Gt[d][a]);
+    // Q * exp(G): for fp32 inputs in place, for the fp32 products below; for
+    // bf16 inputs as bf16 hi/lo tiles in the space of the L tiles (free once
+    // the last block row's products are done), laid out as the A operands of
+    // 16 x 16 x 32 MFMAs: 16-byte chunk c = 4 ks + kk of token row a holds
+    // the key dims 32 ks + 4 kk .. +3 and 32 ks + 16 + 4 kk .. +3, the k
+    // order in which a lane of the start-state image holds its two blocks.
+    constexpr bool HILO = sizeof(Tin) == 2;
+    if constexpr (HILO) {
+        __syncthreads();
+        for (int i = tid; i < KC * DK / 2; i += NT) {
+            const int a = i & (KC - 1), pr = i >> 6;  // token a; dim pair pr of its row
+            const int c = pr >> 2, jp = pr & 3;       // chunk c = 4 ks + kk; pair jp in it
+            const int d = 32 * (c >> 2) + (jp >= 2 ? 16 : 0) + 4 * (c & 3) + 2 * (jp & 1);
+            const float x0 = Qt[d][a] * __expf(Gt[d][a]), x1 = Qt[d + 1][a] * __expf(Gt[d + 1][a]);
+            const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
+            const int off = brow_off<DK>(a, c) + 4 * jp;
+            *reinterpret_cast<uint32_t *>(Xh + off) = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+            *reinterpret_cast<uint32_t *>(Xl + off) =
+                pack_f32(x0 - __uint_as_float(u0 & 0xffff0000u), x1 - __uint_as_float(u1 & 0xffff0000u));
+        }
+    } else {
+        for (int i = tid; i < KC * DK; i += NT) {
+            const int d = i / KC, a = i - d * KC;
+            Qt[d][a] *= __expf(Gt[d][a]);
+        }
     }
     __syncthreads();
 
-    // O blocks (tt, cb): A = (Q exp G)[16 tt + r][16 b + 4 kk + k4] against the
-    // start-state image, then L[16 tt + r][16 t + 4 kk + k4] against new_v.
+    // O blocks (tt, cb): (Q exp G) S_in, then L[16 tt + r][16 t + 4 kk + k4]
+    // against new_v on fp32 MFMAs. For bf16 inputs the first product takes
+    // the start-state blocks 2 ks and 2 ks + 1 of each lane as one 8-value
+    // k slice, split into bf16 hi/lo (hi hi + hi lo + lo hi, about 2^-16 of
+    // each term); for fp32 inputs it is fp32 16 x 16 x 4 MFMAs, A =
+    // (Q exp G)[16 tt + r][16 b + 4 kk + k4]. Both leave O[16 tt + 4 kk + v]
+    // [16 cb + r] in element v.
+    [[maybe_unused]] bf16x8 sh[HILO ? DK / 32 : 1], sl[HILO ? DK / 32 : 1];
+    if constexpr (HILO) {
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) {
+            const float f[8] = {sb[2 * ks][0], sb[2 * ks][1], sb[2 * ks][2], sb[2 * ks][3],
+                                sb[2 * ks + 1][0], sb[2 * ks + 1][1], sb[2 * ks + 1][2], sb[2 * ks + 1][3]};
+            split_bf16x8(f, sh[ks], sl[ks]);
+        }
+    }
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
         const int tt = tt0 + j;
         f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (HILO) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            f32x4 &x = (b & 1) ? x1 : x0;
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                f32x4 &x = (ks & 1) ? x1 : x0;
+                const int off = brow_off<DK>(16 * tt + lr, 4 * ks + lk);
+                const bf16x8 ah = lds_ld<bf16x8>(Xh, off), al = lds_ld<bf16x8>(Xl, off);
+                x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sh[ks], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sl[ks], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, sh[ks], x, 0, 0, 0);
+            }
+        } else {
 #pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4)
-                x = __builtin_amdgcn_mfma_f32_16x16x4f32(Qt[16 * b + 4 * lk + k4][16 * tt + lr], sb[b][k4], x, 0, 0, 0);
+            for (int b = 0; b < NB; ++b) {
+                f32x4 &x = (b & 1) ? x1 : x0;
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4)
+                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(Qt[16 * b + 4 * lk + k4][16 * tt + lr], sb[b][k4], x, 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
