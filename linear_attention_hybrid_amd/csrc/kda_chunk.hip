@@ -1,7 +1,9 @@
-// Chunked gated delta rule with one gate per key dimension (KDA), in fp32 on
-// the vector ALUs: q, k, v in fp32 or bf16, gates g [tokens, H, Dk] and write
-// strengths beta [tokens, H] in fp32, Dk and Dv in {64, 128}, chunks of 64
-// tokens, fp32 state.
+// Chunked gated delta rule with one gate per key dimension (KDA): q, k, v in
+// fp32 or bf16, gates g [tokens, H, Dk] and write strengths beta [tokens, H]
+// in fp32, Dk and Dv in {64, 128}, chunks of 64 tokens, fp32 state. The
+// contractions run on the matrix cores in fp32 (fp32 16 x 16 x 4 MFMAs, or
+// bf16 high/low pairs where noted, about 2^-16 of each term); the pairwise
+// decay factors are exponentials on the vector ALUs.
 //
 // Per chunk (page "Formulas and code for adapting inference to GDN/KDA linear
 // modules", section 1.2, the chunkwise formulas, with the gate made a vector
@@ -20,7 +22,9 @@
 // K * exp(G_last - G) and exp(G_last) for every (chunk, head) at once;
 // kda_chain_kernel walks each (sequence, head, block of 16 value columns)
 // through its chunks, leaving every chunk's start state and new_v behind; and
-// kda_output_kernel forms every chunk's output at once from them.
+// kda_output_kernel forms every chunk's output at once from them. The prep and
+// output kernels are persistent, one workgroup per CU over the (chunk, head)
+// items, each loading the next item's rows while it works on the current one.
 //
 // The pairwise factors exp(G[a][d] - G[b][d]) of M and L are never formed as
 // exp(G[a]) exp(-G[b]), which overflows once a chunk's gates sum past about
