@@ -548,10 +548,15 @@ __global__ __launch_bounds__(CHAIN_NT) void kda_chain_kernel(KdaParams p) {
             sbuf[RB * w + i][l] = make_float4(sacc[i][0], sacc[i][1], sacc[i][2], sacc[i][3]);
         __syncthreads();  // the state complete; every wave is done with new_v
     };
-    for (int c = 0; c < sq.nseg; c += 2) {
+    // Chunk pairs, then a last odd chunk on its own: with both steps of the
+    // loop unconditional, every path back to its top has issued the same
+    // memory operations, and the compiler's waits there count them exactly.
+    int c = 0;
+    for (; c + 1 < sq.nseg; c += 2) {
         step(c, wr0, ur0, kr0, er0);
-        if (c + 1 < sq.nseg) step(c + 1, wr1, ur1, kr1, er1);
+        step(c + 1, wr1, ur1, kr1, er1);
     }
+    if (c < sq.nseg) step(c, wr0, ur0, kr0, er0);
     if (p.c.sfin)
 #pragma unroll
         for (int i = 0; i < RB; ++i)
