@@ -145,8 +145,11 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
     u32x4 qr[4], kr[4], vr[2];
     float gr = 0.f;
     // Bytes from a chunk's first row to the end of its row n - 1 (< 2^31
-    // for H <= 65536).
-    auto rows_bytes = [&](int n) -> int { return (n - 1) * H * (D * 2) + D * 2; };
+    // for H <= 65536); 0 for a chunk past the end (n <= 0), whose loads then
+    // read zeros and whose stores are dropped. The loop issues the same loads
+    // and stores on every path (a chunk past the end, every wave's g), so the
+    // compiler's waits count exactly and the output stores stay in flight.
+    auto rows_bytes = [&](int n) -> int { return n > 0 ? (n - 1) * H * (D * 2) + D * 2 : 0; };
     auto issue = [&](int c) {
         int tv = tid;
         asm volatile("" : "+v"(tv));
@@ -156,7 +159,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
         const int nb = rows_bytes(n);
         const buf_t rq = buf_rsrc(qg + base, nb);
         const buf_t rk = buf_rsrc(kg + base, nb);
-        const buf_t rv = buf_rsrc(vg + base + half * 64, nb - 128);
+        const buf_t rv = buf_rsrc(vg + base + half * 64, nb > 0 ? nb - 128 : 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const uint32_t off = (uint32_t)((tv >> 4) + 16 * i) * (uint32_t)(H * D * 2) + (tv & 15) * 16u;
@@ -168,14 +171,16 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             const uint32_t off = (uint32_t)((tv >> 3) + 32 * i) * (uint32_t)(H * D * 2) + (tv & 7) * 16u;
             vr[i] = buf_ld16(rv, off);
         }
-        if (w == 0) gr = buf_ld_f32(buf_rsrc(p.g + t0 * H + h, (n - 1) * H * 4 + 4), (uint32_t)(tv & 63) * H * 4);
+        gr = buf_ld_f32(buf_rsrc(p.g + t0 * H + h, n > 0 ? (n - 1) * H * 4 + 4 : 0), (uint32_t)(tv & 63) * H * 4);
     };
-    auto store_o = [&](int c) {
+    // Chunk c's output rows from the staging tile; with ok false (before the
+    // first chunk) the same stores go out with an empty range and are dropped.
+    auto store_o = [&](int c, bool ok) {
         int tv = tid;
         asm volatile("" : "+v"(tv));
         const int n = min(64, len - 64 * c);
         const int64_t t0 = se.tok0 + 64 * (int64_t)c;
-        const buf_t ro = buf_rsrc(og + (t0 * H + h) * (D * 2) + half * 128, (n - 1) * H * (D * 2) + 128);
+        const buf_t ro = buf_rsrc(og + (t0 * H + h) * (D * 2) + half * 128, ok ? (n - 1) * H * (D * 2) + 128 : 0);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int r = (tv >> 3) + 32 * i;
@@ -217,7 +222,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
     for (int c = 0; c < nch; ++c) {
         const int n = min(64, len - 64 * c);
         __syncthreads();  // the previous chunk's tiles and staging are read
-        if (c > 0) store_o(c - 1);
+        store_o(c - 1, c > 0);
         {
             int tv = tid;
             asm volatile("" : "+v"(tv));
@@ -234,7 +239,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             if (w == 0) lds_st(lds, L_G + 4 * l, gr);
         }
         __syncthreads();  // chunk c's tiles are in LDS
-        if (c + 1 < nch) issue(c + 1);
+        issue(c + 1);
 
         // Gate prefix sum, one lane per token (rows past the end read as 0).
         const float G = wave_prefix_sum(lds_ld<float>(lds, L_G + 4 * l));
@@ -378,7 +383,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
         }
     }
     __syncthreads();  // the last chunk's output rows are staged
-    if (nch > 0) store_o(nch - 1);
+    if (nch > 0) store_o(nch - 1, true);
 
     if (last && p.sfin) {
         float *dst = p.sfin + ((int64_t)se.seq * H + h) * sl;
