@@ -44,6 +44,22 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+template <bool B>
+struct Tag {
+    static constexpr bool value = B;
+};
+
+// Stores through a buffer resource: past its range (an empty range included)
+// they are dropped. The prep kernel gives every path through an item the same
+// stores this way, so that the compiler's waits on the next item's loads count
+// them exactly instead of waiting for every store in flight.
+__device__ __forceinline__ void st_f4(buf_t r, uint32_t off, float4 v) {
+    buf_st16(r, off, u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)});
+}
+__device__ __forceinline__ void st_f1(buf_t r, uint32_t off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)off, 0, 0);
+}
+
 constexpr int KC = kChunk;  // tokens per chunk
 constexpr int KP = KC + 1;  // padded token stride of transposed tiles
 
@@ -161,16 +177,29 @@ struct Rows {
 
 // A (chunk, head) item of the persistent kernels: item = s H + h.
 // len < 0 marks a table row with no segment; past the last item len is -1.
+// TAB: the segments come from the device table (packed sequences); without
+// it they are arithmetic (B sequences of T tokens) and decoding an item loads
+// nothing, which leaves the compiler's waits in the item loop exact (a table
+// load merged into the loop would make it wait for every store in flight).
 struct Item {
     int s, h, n, len;
     int64_t tok0;
 };
+template <bool TAB>
 __device__ __forceinline__ Item item_at(const KdaParams &p, int64_t item, int64_t nitems) {
     Item it{0, 0, 0, -1, 0};
     if (item < nitems) {
         it.s = (int)(item / p.c.H);
         it.h = (int)(item - (int64_t)it.s * p.c.H);
-        const SegEntry se = seg_at(p.c, it.s);
+        SegEntry se;
+        if constexpr (TAB) {
+            se = seg_at(p.c, it.s);
+        } else {
+            const int n = it.s / p.c.nps, j = it.s - n * p.c.nps;
+            const int rem = p.c.T - j * kChunk;
+            se.tok0 = (int64_t)n * p.c.T + (int64_t)j * kChunk;
+            se.len = rem < kChunk ? rem : kChunk;
+        }
         it.len = se.len;
         it.n = se.len > 0 ? se.len : 0;
         it.tok0 = se.tok0;
@@ -181,7 +210,7 @@ __device__ __forceinline__ Item item_at(const KdaParams &p, int64_t item, int64_
 // ---- prep: persistent over the (chunk, head) items, one workgroup per CU;
 // the next item's k, g, v rows and beta load into registers while the
 // current one is worked on.
-template <typename Tin, int DK, int DV>
+template <typename Tin, int DK, int DV, bool TAB>
 __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nitems) {
     constexpr int NT = 512;
     constexpr int MP = KC + 4;         // row stride of A/T: 16-byte aligned rows
@@ -200,7 +229,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
                   "the workgroup must fit one CU's LDS");
     const int H = p.c.H;
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;  // w: one value per wave
     const Tin *__restrict__ kg = static_cast<const Tin *>(p.c.k);
     const Tin *__restrict__ vg = static_cast<const Tin *>(p.c.v);
 
@@ -210,22 +239,34 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     Rows<Tin, DV, NT> rv;
     float rb = 0.f;
     auto fetch = [&](int64_t item) {
-        const Item it = item_at(p, item, nitems);
+        const Item it = item_at<TAB>(p, item, nitems);
         rk.load(kg, it.tok0, H, it.h, it.n, tid);
         rg.load(p.c.g, it.tok0, H, it.h, it.n, tid);
         rv.load(vg, it.tok0, H, it.h, it.n, tid);
         rb = buf_ld_f32(buf_rsrc(p.beta + it.tok0 * H + it.h, it.n > 0 ? (it.n - 1) * H * 4 + 4 : 0),
-                        (uint32_t)(tid * H * 4));
+                        (uint32_t)((tid & (KC - 1)) * H * 4));
     };
     fetch(blockIdx.x);
+    // The first item's loads complete before the loop, so that the waits at
+    // its top count only the next item's loads and the stores issued after
+    // them (and never wait for the stores).
+#pragma unroll
+    for (int m = 0; m < rk.PT; ++m) settle(rk.r[m]);
+#pragma unroll
+    for (int m = 0; m < rg.PT; ++m) settle(rg.r[m]);
+#pragma unroll
+    for (int m = 0; m < rv.PT; ++m) settle(rv.r[m]);
+    settle(rb);
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const Item it = item_at(p, item, nitems);
-    if (it.len < 0) {
+    const Item it = item_at<TAB>(p, item, nitems);
+    // Without the table every item has a segment (len >= 0; T = 0 gives an
+    // empty one whose tile the chain still reads).
+    if (TAB && it.len < 0) {
         fetch(item + gridDim.x);
         continue;
     }
     const int s = it.s, h = it.h;
-    if (tid < KC) bs[tid] = rb;
+    bs[tid & (KC - 1)] = rb;  // eight threads per token write the same value
     rk.template store<true, KP>(&Kt[0][0], tid);
     rg.template store<true, KP>(&Gt[0][0], tid);
     rv.template store<false, DV + 1>(&Vs[0][0], tid);
@@ -290,7 +331,13 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     float *tb = reinterpret_cast<float *>(Xb);      // 10 blocks + 4 scratch = 17.5 KiB
     static_assert(14 * TBF * 4 <= (int)sizeof(Xb), "T blocks exceed the tile space");
     auto tbo = [](int I, int J) { return (I * (I + 1) / 2 + J) * TBF; };
-    if (w < 4 && l < 16) {
+    // The item's tile as a buffer (bytes), and an empty one for the stores
+    // that only balance the paths.
+    const buf_t rtile = buf_rsrc(tile, (int)(tile_floats(DK, DV) * 4));
+    const buf_t rnone = buf_rsrc(tile, 0);
+    constexpr int KDQ = KC / 4 * DK / (NT - 256);  // Kd image float4s per thread of waves 4..7
+    if (w < 4) {
+    if (l < 16) {
         // Diagonal block w, row l of T_ww = (I + A_ww)^-1: y with
         // (I + A_ww)^T y = e_l, by back substitution (once y_j is final it
         // takes A[j][m] y_j out of every y_m, m < j; 15 dependent steps).
@@ -312,11 +359,18 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
         for (int q = 0; q < 4; ++q)
             *reinterpret_cast<float4 *>(tb + tbo(w, w) + l * TBR + 4 * q) =
                 make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3]);
-    } else if (w >= 4) {
+    }
+        // Distinct offsets, so that the compiler keeps every one of them.
+#pragma unroll
+        for (int m = 0; m < KDQ; ++m) st_f4(rnone, 16u * m, make_float4(0.f, 0.f, 0.f, 0.f));
+        st_f1(rnone, 16u * KDQ, 0.f);
+    } else {
         // Meanwhile: K * exp(G_last - G) and exp(G_last) for the chain (rows
         // past the end have zero keys and gates, so G_last is the last row's
         // G), and X = diag(beta) K * exp(G) in place of K.
-        for (int q = tid - 256; q < KC / 4 * DK; q += NT - 256) {
+#pragma unroll
+        for (int m = 0; m < KDQ; ++m) {
+            const int q = m * (NT - 256) + tid - 256;
             // float4 q of the Kd image: tokens a0 .. a0 + 3, key dim d.
             const int d = 16 * (q >> 8) + (q & 15), a0 = 16 * ((q >> 6) & 3) + 4 * ((q >> 4) & 3);
             const float gl = Gt[d][KC - 1];
@@ -327,9 +381,11 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
                 kd[v] = kv * __expf(gl - gv);
                 Kt[d][a0 + v] = kv * bs[a0 + v] * __expf(gv);
             }
-            reinterpret_cast<float4 *>(tile + KC * DK)[q] = make_float4(kd[0], kd[1], kd[2], kd[3]);
+            st_f4(rtile, (uint32_t)(KC * DK + 4 * q) * 4u, make_float4(kd[0], kd[1], kd[2], kd[3]));
         }
-        if (tid - 256 < DK) tile[2 * KC * DK + KC * DV + tid - 256] = __expf(Gt[tid - 256][KC - 1]);
+        // exp(G_last) of key dim tid - 256; threads past Dk store out of range.
+        const int dl = tid - 256 < DK ? tid - 256 : DK - 1;
+        st_f1(buf_rsrc(tile + 2 * KC * DK + KC * DV, DK * 4), (uint32_t)(tid - 256) * 4u, __expf(Gt[dl][KC - 1]));
     }
     __syncthreads();
     // Block rows below: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, wave J taking
@@ -384,35 +440,46 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     {
         const int lr = l & 15, lk = l >> 4;
         constexpr int NBK = DK / 16, NBV = DV / 16;
-        for (int job = w; job < NBK + NBV; job += NT / 64) {
-            const bool isw = job < NBK;
-            const int cb = isw ? job : job - NBK;
-            // The operand that is not T, for token blocks kb = 0..3: X^T
-            // [16 cb + r][16 kb + 4 kk + k4] or (beta V)[16 kb + 4 kk + k4][16 cb + r].
-            float o[4][4];
+        // Jobs w, w + 8, ...; a wave with fewer real jobs runs job 0 again
+        // with its stores dropped.
+        constexpr int NJ = NBK + NBV, JPW = (NJ + NT / 64 - 1) / (NT / 64);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+        for (int m = 0; m < JPW; ++m) {
+            const int jr = w + m * (NT / 64);
+            const bool real = jr < NJ;
+            const int job = real ? jr : 0;
+            // W's jobs (W^T = X^T T^T) and U's (U = T (beta V)) as separate
+            // code, chosen once per job (the choice is the same for the wave).
+            auto job4 = [&](auto wside) {
+                constexpr bool ISW = decltype(wside)::value;
+                const int cb = ISW ? job : job - NBK;
+                // The operand that is not T, for token blocks kb = 0..3: X^T
+                // [16 cb + r][16 kb + 4 kk + k4] or (beta V)[16 kb + 4 kk + k4][16 cb + r].
+                float o[4][4];
 #pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4)
-                    o[kb][k4] = isw ? Kt[16 * cb + lr][16 * kb + 4 * lk + k4] : Vs[16 * kb + 4 * lk + k4][16 * cb + lr];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kb = 0; kb <= tt; ++kb) {
-                    const float4 t4 = *reinterpret_cast<const float4 *>(&Ms[16 * tt + lr][16 * kb + 4 * lk]);
-                    const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+                for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                     for (int k4 = 0; k4 < 4; ++k4)
-                        x = isw ? __builtin_amdgcn_mfma_f32_16x16x4f32(o[kb][k4], tv[k4], x, 0, 0, 0)
-                                : __builtin_amdgcn_mfma_f32_16x16x4f32(tv[k4], o[kb][k4], x, 0, 0, 0);
+                        o[kb][k4] = ISW ? Kt[16 * cb + lr][16 * kb + 4 * lk + k4] : Vs[16 * kb + 4 * lk + k4][16 * cb + lr];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb <= tt; ++kb) {
+                        const float4 t4 = *reinterpret_cast<const float4 *>(&Ms[16 * tt + lr][16 * kb + 4 * lk]);
+                        const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+                        for (int k4 = 0; k4 < 4; ++k4)
+                            x = ISW ? __builtin_amdgcn_mfma_f32_16x16x4f32(o[kb][k4], tv[k4], x, 0, 0, 0)
+                                    : __builtin_amdgcn_mfma_f32_16x16x4f32(tv[k4], o[kb][k4], x, 0, 0, 0);
+                    }
+                    const uint32_t off = ISW ? (uint32_t)((tt * NBK + cb) * 64 + l) * 16u
+                                             : (uint32_t)(2 * KC * DK) * 4u + (uint32_t)((tt * NBV + cb) * 64 + l) * 16u;
+                    st_f4(real ? rtile : rnone, off, make_float4(x[0], x[1], x[2], x[3]));
                 }
-                const float4 r = make_float4(x[0], x[1], x[2], x[3]);
-                if (isw)
-                    reinterpret_cast<float4 *>(tile)[(tt * NBK + cb) * 64 + l] = r;
-                else
-                    reinterpret_cast<float4 *>(tile + 2 * KC * DK)[(tt * NBV + cb) * 64 + l] = r;
-            }
+            };
+            if (job < NBK) job4(Tag<true>{});
+            else job4(Tag<false>{});
         }
     }
     __syncthreads();  // the next item's tiles overwrite these
@@ -576,7 +643,7 @@ __global__ __launch_bounds__(CHAIN_NT) void kda_chain_kernel(KdaParams p) {
 // the (chunk, head) items, one workgroup per CU: the next item's q, k, g rows
 // load into registers once the current ones are in LDS, and its images once
 // the current output is formed.
-template <typename Tin, int DK, int DV>
+template <typename Tin, int DK, int DV, bool TAB>
 __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t nitems) {
     constexpr int NT = 512;
     constexpr int NB = DK / 16;        // key blocks
@@ -605,7 +672,7 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
     Rows<Tin, DK, NT> rq, rk;
     Rows<float, DK, NT> rg;
     auto fetch_rows = [&](int64_t item) {
-        const Item it = item_at(p, item, nitems);
+        const Item it = item_at<TAB>(p, item, nitems);
         rq.load(qg, it.tok0, H, it.h, it.n, tid);
         rk.load(kg, it.tok0, H, it.h, it.n, tid);
         rg.load(p.c.g, it.tok0, H, it.h, it.n, tid);
@@ -615,7 +682,7 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
     // Loaded for every item, also those with no tokens (their images hold
     // anything, and go unused), so that every path issues the same loads.
     auto fetch_ops = [&](int64_t item) {
-        const Item it = item_at(p, item, nitems);
+        const Item it = item_at<TAB>(p, item, nitems);
         const int64_t ti = tile_index(p, it.s, it.h);
         const f32x4 *simg = reinterpret_cast<const f32x4 *>(p.sin + ti * DK * DV);
         const f32x4 *nimg = reinterpret_cast<const f32x4 *>(p.nv + ti * KC * DV);
@@ -627,7 +694,7 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
     fetch_rows(blockIdx.x);
     fetch_ops(blockIdx.x);
     for (int64_t item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const Item it = item_at(p, item, nitems);
+    const Item it = item_at<TAB>(p, item, nitems);
     const int64_t next = item + gridDim.x;
     if (it.len <= 0) {
         fetch_rows(next);
@@ -783,7 +850,11 @@ hipError_t launch_dims(const KdaParams &p, hipStream_t st) {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
     const unsigned wgs = (unsigned)std::min<int64_t>(nitems, cus);
-    hipLaunchKernelGGL((kda_prep_kernel<Tin, DK, DV>), dim3(wgs), dim3(512), 0, st, p, nitems);
+    const bool tab = p.c.segs != nullptr || p.c.cu != nullptr;
+    if (tab)
+        hipLaunchKernelGGL((kda_prep_kernel<Tin, DK, DV, true>), dim3(wgs), dim3(512), 0, st, p, nitems);
+    else
+        hipLaunchKernelGGL((kda_prep_kernel<Tin, DK, DV, false>), dim3(wgs), dim3(512), 0, st, p, nitems);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // xcd_unit_map covers every (sequence, head) when the unit count is
@@ -792,7 +863,10 @@ hipError_t launch_dims(const KdaParams &p, hipStream_t st) {
     hipLaunchKernelGGL((kda_chain_kernel<DK, DV>), dim3(chains), dim3(CHAIN_NT), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_output_kernel<Tin, DK, DV>), dim3(wgs), dim3(512), 0, st, p, nitems);
+    if (tab)
+        hipLaunchKernelGGL((kda_output_kernel<Tin, DK, DV, true>), dim3(wgs), dim3(512), 0, st, p, nitems);
+    else
+        hipLaunchKernelGGL((kda_output_kernel<Tin, DK, DV, false>), dim3(wgs), dim3(512), 0, st, p, nitems);
     return hipGetLastError();
 }
 
