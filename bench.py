@@ -71,8 +71,8 @@ CALL_KERNELS = {
     EPILOGUE: ["out_norm_gate_kernel<unsigned short, 2>"],
     GDN_PREFILL: ["gdn_prep_kernel", "gdn_chain_kernel", "gdn_output_kernel"],
     GDN_DECODE: ["gdn_step_kernel<unsigned short, 128, 128, false>"],
-    KDA_PREFILL: ["kda_prep_kernel<unsigned short, 128, 128>", "kda_chain_kernel<128, 128>",
-                  "kda_output_kernel<unsigned short, 128, 128>"],
+    KDA_PREFILL: ["kda_prep_kernel<unsigned short, 128, 128, false>", "kda_chain_kernel<128, 128>",
+                  "kda_output_kernel<unsigned short, 128, 128, false>"],
     KDA_DECODE: ["gdn_step_kernel<unsigned short, 128, 128, true>"],
 }
 
