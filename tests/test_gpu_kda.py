@@ -129,14 +129,18 @@ def test_kda_chunk_head_sizes(dtype, dk, dv):
     compare_chunk(inp, o, S, dtype, "kda %dx%d" % (dk, dv))
 
 
-def test_kda_chunk_varlen():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128)])
+def test_kda_chunk_varlen(dtype, dk, dv):
+    """Packed sequences go through the segment table (its own kernel
+    variants): empty, ragged and whole-chunk sequences in one call."""
     lengths = [0, 1, 63, 64, 65, 130, 7, 200]
     cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
-    say("kda_chunk_fwd varlen", lengths)
-    inp = W.make_prefill(1, int(cu[-1]), 3, 128, 128, "bf16", "kda", seed=9, device="cuda",
+    say("kda_chunk_fwd varlen", dtype, dk, dv, lengths)
+    inp = W.make_prefill(1, int(cu[-1]), 3, dk, dv, dtype, "kda", seed=9 + dk, device="cuda",
                          cu_seqlens=cu, init="normal", with_beta=True)
     o, S = run_chunk(inp)
-    compare_chunk(inp, o, S, "bf16", "kda varlen")
+    compare_chunk(inp, o, S, dtype, "kda varlen")
 
 
 def test_kda_chunk_no_tokens_copies_state():
