@@ -140,6 +140,21 @@ def recorded_mfma(workload):
     return entry.get("kernels")
 
 
+def recorded_issued(workload):
+    """Matrix-core flops one call issues (bf16 and fp32), from the committed
+    counter record (SQ_INSTS_VALU_MFMA_MOPS_* x 512 summed over the call's
+    kernels), or None when there is none or the kernels changed since."""
+    try:
+        with open(MFMA_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("source_hash") != kernel_source_hash(workload) or "issued" not in entry:
+        return None
+    return entry["issued"]
+
+
 def copy_calibration(torch, dev, nbytes=256 << 20, reps=3):
     """An elementwise pass of known size (fp32 negation: nbytes read, nbytes
     written, kernel name containing ``neg_kernel``), so FETCH_SIZE/WRITE_SIZE
@@ -238,6 +253,54 @@ def record_traffic(fetch_dir, write_dir, workloads=None, calib_bytes=256 << 20):
     return 0
 
 
+def _update_entry(rec, wl, fields):
+    """Merge fields into a workload's entry; an entry taken on other kernel
+    sources is dropped first."""
+    h = kernel_source_hash(wl)
+    entry = rec.get(wl)
+    if not entry or entry.get("source_hash") != h:
+        entry = {"source_hash": h}
+    entry.update(fields)
+    rec[wl] = entry
+
+
+def record_mops(pmc_dir, workloads=None):
+    """Matrix-core flops issued by each kernel of a call, from a rocprofv3
+    --pmc run with SQ_INSTS_VALU_MFMA_MOPS_BF16 and SQ_INSTS_VALU_MFMA_MOPS_F32
+    (units of 512 flops), averaged per kernel and summed over the call.
+    Merged into profiles/mfma.json beside the busy fractions."""
+    bf = _per_kernel_avg(_counter_rows(pmc_dir, "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+    f32 = _per_kernel_avg(_counter_rows(pmc_dir, "SQ_INSTS_VALU_MFMA_MOPS_F32"))
+
+    def find(pattern):
+        names = [n for n in bf if pattern in n and n in f32]
+        return names[0] if len(names) == 1 else None
+
+    rec = _load_record(MFMA_RECORD)
+    rec["_issued"] = "SQ_INSTS_VALU_MFMA_MOPS_BF16 and _F32 x 512 flops, per kernel and per call"
+    for wl, parts in CALL_KERNELS.items():
+        if workloads and wl not in workloads:
+            continue
+        kern = {}
+        for pat in parts:
+            n = find(pat)
+            if n is None:
+                kern = None
+                break
+            kern[pat] = {"bf16": bf[n] * 512.0, "f32": f32[n] * 512.0}
+        if kern:
+            _update_entry(rec, wl, {"issued": {
+                "kernels": kern,
+                "bf16_per_call": sum(v["bf16"] for v in kern.values()),
+                "f32_per_call": sum(v["f32"] for v in kern.values())}})
+    os.makedirs(os.path.dirname(MFMA_RECORD), exist_ok=True)
+    with open(MFMA_RECORD, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec, indent=1, sort_keys=True))
+    return 0
+
+
 def record_mfma(pmc_dir, workloads=None, xcds=8, simds=1024):
     """Matrix-core busy fraction of each kernel of a call, from a rocprofv3
     --pmc run with SQ_VALU_MFMA_BUSY_CYCLES (busy cycles summed over every
@@ -265,13 +328,25 @@ def record_mfma(pmc_dir, workloads=None, xcds=8, simds=1024):
                 break
             kern[pat] = busy[n] / (active[n] / xcds * simds) if active[n] else 0.0
         if kern:
-            rec[wl] = {"source_hash": kernel_source_hash(wl), "kernels": kern}
+            _update_entry(rec, wl, {"kernels": kern})
     os.makedirs(os.path.dirname(MFMA_RECORD), exist_ok=True)
     with open(MFMA_RECORD, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
     print(json.dumps(rec, indent=1, sort_keys=True))
     return 0
+
+
+def issued_reading(issued, dense_flops, ms):
+    """The matrix-core flops a call issues (counter record) as a rate, a
+    fraction of the bf16 dense peak, and a multiple of the dense-tile
+    algorithmic flops (what the kernels recompute or split into hi/lo pairs)."""
+    if not issued:
+        return None
+    fl = issued["bf16_per_call"]
+    return {"bf16_flops_per_call": fl, "tflops": fl / (ms * 1e-3) / 1e12,
+            "frac_of_bf16_peak": fl / (ms * 1e-3) / 1e12 / BF16_DENSE_PEAK_TFLOPS,
+            "recompute_factor": fl / dense_flops}
 
 
 def prefill_bytes(B, T, H, Dk, Dv, elem=2, with_s0=False):
@@ -425,9 +500,15 @@ def main():
                     help="with --record-traffic / --record-mfma: the workloads the runs hold")
     ap.add_argument("--no-b2b", action="store_true",
                     help="time the prefill only after cache flushes (profiler runs)")
+    ap.add_argument("--record-mops", metavar="PMC_DIR",
+                    help="write the matrix-core flops issued per call into profiles/mfma.json from a "
+                         "rocprofv3 --pmc run with SQ_INSTS_VALU_MFMA_MOPS_BF16 and _F32")
     ap.add_argument("--record-mfma", metavar="PMC_DIR",
                     help="no GPU work: write profiles/mfma.json from a rocprofv3 --pmc run with "
                          "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the 65,536-token workload's split (two chained calls), so that a "
+                         "profiler's per-kernel averages hold whole calls only")
     ap.add_argument("--long-steps", type=int, default=5,
                     help="timed calls of the 65,536-token and the packed varlen workloads")
     args = ap.parse_args()
@@ -435,6 +516,8 @@ def main():
         return record_traffic(*args.record_traffic, workloads=args.workloads)
     if args.record_mfma:
         return record_mfma(args.record_mfma, workloads=args.workloads)
+    if args.record_mops:
+        return record_mops(args.record_mops, workloads=args.workloads)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on one GPU only; --gpus %d (WORLD_SIZE %d) is not "
@@ -507,7 +590,8 @@ def main():
                      "useful_frac_of_bf16_peak": flops / (ms_step * 1e-3) / 1e12 /
                      BF16_DENSE_PEAK_TFLOPS,
                      "dense_tile_flops_per_launch": flops,
-                     "busy": recorded_mfma(PREFILL)},
+                     "busy": recorded_mfma(PREFILL),
+                     "issued": issued_reading(recorded_issued(PREFILL), flops, ms_step)},
             "wall_s_timed": wall,
             "per_call_ms": {"mean": ms_step, "median": median(fl), "min": min(fl),
                             "max": max(fl)},
@@ -663,7 +747,13 @@ def bench_long(args, torch, sgla, W, dev):
                         "kernel": "sgla_chunk_fwd_ex (whole call: segment-state, scan and "
                                   "value-half output kernels)",
                         "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms},
-           "mfma_busy": recorded_mfma(LONG)}
+           "mfma_busy": recorded_mfma(LONG),
+           "mfma_issued": issued_reading(recorded_issued(LONG),
+                                         prefill_flops(1, T, 32, 128, 128), ms)}
+    if args.no_split:
+        del inp, out, fs, ws
+        torch.cuda.empty_cache()
+        return res
     t = W.WORKLOADS[LONG]["split"]
     halves = []
     for part in ("a", "b"):
@@ -842,6 +932,13 @@ def bench_kda(args, torch, sgla, W, dev):
                                              "transform, state chain, per-chunk output; fp32)",
                                    "algorithmic_flops_per_launch": flops,
                                    "avg_launch_ms": per_avg}}
+    iss = recorded_issued(KDA_PREFILL)
+    out["prefill"]["mfma"] = {
+        "busy": recorded_mfma(KDA_PREFILL),
+        "issued": None if not iss else {
+            "f32_flops_per_call": iss["f32_per_call"], "bf16_flops_per_call": iss["bf16_per_call"],
+            "f32_tflops": iss["f32_per_call"] / (per_avg * 1e-3) / 1e12,
+            "f32_frac_of_peak": iss["f32_per_call"] / (per_avg * 1e-3) / 1e12 / FP32_PEAK_TFLOPS}}
     del inp, o, fs, ws
     torch.cuda.empty_cache()
     d = W.make_decode(256, 32, 128, 128, 64, "bf16", "kda", seed=4, device=dev, with_beta=True)
