@@ -61,8 +61,14 @@ int choose_out_len(int64_t ttot, int H) {
 
 // Sub-segments per output segment for the state pass: split until the pass
 // has about 384 (segment, head) workgroups, keeping sub-segments of at least
-// 512 tokens and whole chunks. pre_units = (segment, head) pairs whose state
-// is needed when each output segment is one sub-segment.
+// 1024 tokens (16 chunks) and whole chunks. pre_units = (segment, head) pairs
+// whose state is needed when each output segment is one sub-segment.
+// Measured on the 8192-token call (1024-token output segments): one
+// sub-segment each, 111.9 us flushed, against 114.3 us with two of 512
+// tokens (shorter workgroups spend more of their time waiting for their
+// first chunk, and the scan moves twice the states); on the 65,536-token call
+// two 4096-token sub-segments stay best (732 us, against 758 us with one or
+// four).
 int choose_rsub(int out_len, int64_t pre_units) {
     const char *env = getenv("SGLA_RSUB");
     if (env) {
@@ -70,7 +76,7 @@ int choose_rsub(int out_len, int64_t pre_units) {
         if (v >= 1 && v <= out_len / kChunk && (out_len / kChunk) % v == 0) return (int)v;
     }
     int r = 1;
-    while (out_len / (2 * r) >= 512 && (out_len / kChunk) % (2 * r) == 0 && pre_units * r < 384) r *= 2;
+    while (out_len / (2 * r) >= 1024 && (out_len / kChunk) % (2 * r) == 0 && pre_units * r < 384) r *= 2;
     return r;
 }
 
