@@ -120,7 +120,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
     const ChunkParams &p = hp.c;
     const int H = p.H;
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int l = tid & 63;
     const int cc = w >> 1;   // 32-column block of the half
     constexpr int t = TH;    // token half of the output, key-row half of the state
@@ -181,12 +181,16 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
         const int n = min(64, len - 64 * c);
         const int64_t t0 = se.tok0 + 64 * (int64_t)c;
         const buf_t ro = buf_rsrc(og + (t0 * H + h) * (D * 2) + half * 128, ok ? (n - 1) * H * (D * 2) + 128 : 0);
+        // Bit 4 of this thread's rows is bit 1 of its wave index (tv >> 3
+        // < 32), so whether the halves of its pieces trade places is the
+        // same for the whole wave.
+        u32x4 x[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) x[i] = lds_ld<u32x4>(lds, L_O + o_off((tv >> 3) + 32 * i, tv & 7));
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int r = (tv >> 3) + 32 * i;
-            const int pc = tv & 7;
-            const u32x4 x = lds_ld<u32x4>(lds, L_O + o_off(r, pc));
-            buf_st16_nt(ro, (uint32_t)r * (uint32_t)(H * D * 2) + pc * 16u, ((r >> 4) & 1) ? swap_halves(x) : x);
+            buf_st16_nt(ro, (uint32_t)r * (uint32_t)(H * D * 2) + (tv & 7) * 16u, (w & 2) ? swap_halves(x[i]) : x[i]);
         }
     };
 
@@ -219,6 +223,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
     // log2|scale| - G_j log2(e)); a negative scale flips the output rows.
     const float ls = __builtin_amdgcn_logf(fabsf(p.scale));
     const bool neg = p.scale < 0.f;
+    const uint32_t sgn2 = neg ? 0x80008000u : 0u;  // sign bits of a bf16 pair
     for (int c = 0; c < nch; ++c) {
         const int n = min(64, len - 64 * c);
         __syncthreads();  // the previous chunk's tiles and staging are read
@@ -300,6 +305,11 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
                 sc = mfma(a, bq, sc);
             }
             const float Gi = lds_ld<float>(ft, 4 * iq) + ls;
+            // Keys past the query are cleared after packing, by a mask on
+            // each bf16 of a pair: no branch, and an infinite or NaN product
+            // there (exp of a positive gate sum) is cleared as well. Wave 1
+            // pairs keys 0-31 with queries 32-63 and keeps every key. A
+            // negative scale flips the sign bits.
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const int jr = 32 * jb + 8 * g4 + 4 * lh;
@@ -307,9 +317,13 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
                 const float gj[4] = {Gj.x, Gj.y, Gj.z, Gj.w};
                 float val[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    val[r] = (jr + r <= iq) ? __builtin_amdgcn_exp2f(Gi - gj[r]) * sc[4 * g4 + r] : 0.f;
-                const u32x2 pk = {pack_f32(val[0], val[1]), pack_f32(val[2], val[3])};
+                for (int r = 0; r < 4; ++r) val[r] = __builtin_amdgcn_exp2f(Gi - gj[r]) * sc[4 * g4 + r];
+                u32x2 pk = {pack_f32(val[0], val[1]), pack_f32(val[2], val[3])};
+                const int d = w == 1 ? 64 : iq - jr;  // key jr + r is kept when r <= d
+                pk[0] &= (d >= 1 ? 0xffffffffu : 0u) | (d >= 0 ? 0x0000ffffu : 0u);
+                pk[1] &= (d >= 3 ? 0xffffffffu : 0u) | (d >= 2 ? 0x0000ffffu : 0u);
+                pk[0] ^= sgn2;
+                pk[1] ^= sgn2;
                 lds_st(lds, L_A + tr_off(iq, 4 * jb + g4) + 8 * lh, pk);
             }
         }
@@ -327,7 +341,8 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
 
         // The partner's key rows, then the rows scaled by scale * exp(G_i).
         {
-            const float f = __builtin_amdgcn_exp2f(lds_ld<float>(ft, 4 * i) + ls);
+            const float fa = __builtin_amdgcn_exp2f(lds_ld<float>(ft, 4 * i) + ls);
+            const float f = neg ? -fa : fa;
 #pragma unroll
             for (int v4 = 0; v4 < 4; ++v4) {
                 const float4 y = lds_ld<float4>(lds, sx_off(cc, t, v4, l));
@@ -347,9 +362,6 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             }
         }
         // Output rows into the staging tile (stored at the next iteration).
-        if (neg)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[v] = -acc[v];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const u32x2 pk = {pack_f32(acc[4 * g4], acc[4 * g4 + 1]), pack_f32(acc[4 * g4 + 2], acc[4 * g4 + 3])};
