@@ -61,21 +61,30 @@ constexpr int L_BYTES = L_F + 4 * 512;
 static_assert(2 * L_BYTES <= kLdsPerCU, "two workgroups must fit one compute unit's LDS");
 
 // Q and K tiles (64 rows of 256 bytes): 16-byte chunk c of row r sits at
-// chunk c ^ qk_sw(r), and the two 8-byte halves of every chunk of a row with
-// bit 4 set trade places. Sixteen consecutive rows then put one chunk in 16
-// different bank groups (the scores' row reads), rows r and r + 16 put one
-// 8-byte half in different banks (the 8-byte reads of Q S), and the four rows
-// of a transposing read put an aligned group of four chunks in 16 different
-// bank groups (the K^T reads of the update). Every read names 8-byte halves
-// at their place, so each operand keeps the logical order of its k values.
+// chunk c ^ qk_sw(r). Sixteen consecutive rows then put one chunk in 16
+// different bank groups, so the 16-byte operand reads of the scores and of
+// Q S, one row per lane, are free of bank conflicts, and the four rows of a
+// transposing read put an aligned group of four chunks in 16 different bank
+// groups (the K^T reads of the update).
 __device__ __forceinline__ int qk_sw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 __device__ __forceinline__ int qk_off(int r, int c) { return r * 256 + ((c ^ qk_sw(r)) << 4); }
-__device__ __forceinline__ int qk_half(int r, int hf) { return 8 * (hf ^ ((r >> 4) & 1)); }
 // Transposing-read address (rows r0 .. r0+3, columns c0 .. c0+15; r0 a
-// multiple of 4, c0 a multiple of 16) for lane m of a 16-lane group.
+// multiple of 4, c0 a multiple of 16) for lane m of a 16-lane group. Lane m
+// names 4-column piece kPiece[m % 4], so lane i of the group receives column
+// c0 + sigma(i), sigma = (0-3, 8-11, 4-7, 12-15). The update's K^T operand
+// then leaves state row rho of each 32-row block holding key dim sigma(rho)
+// of it (sigma applied to each 16-row half), and the eight k values a lane
+// gives Q S (state rows 4lh + 0..3 and 8 + 4lh + 0..3 of a 16-row group)
+// are the eight consecutive dims 8lh .. 8lh + 7: one 16-byte Q read.
 __device__ __forceinline__ int qk_tr_src(int r0, int c0, int m) {
     const int r = r0 + (m >> 2);
-    return qk_off(r, (c0 >> 3) + ((m & 3) >> 1)) + qk_half(r, m & 1);
+    const int pc = ((m & 1) << 1) | ((m >> 1) & 1);  // kPiece = (0, 2, 1, 3)
+    return qk_off(r, (c0 >> 3) + (pc >> 1)) + 8 * (pc & 1);
+}
+// Key dim, within the state block of key rows 32 b .. 32 b + 31, of the state
+// value a lane (half lh of the wave) holds in accumulator element v.
+__device__ __forceinline__ int state_dim(int v, int lh) {
+    return 16 * (v >> 3) + 4 * ((v >> 2) & 1) + 8 * lh + (v & 3);
 }
 __device__ __forceinline__ u32x4 swap_halves(u32x4 x) { return u32x4{x[2], x[3], x[0], x[1]}; }
 
@@ -93,6 +102,7 @@ __device__ __forceinline__ int vtr_src(int r0, int c0, int m) {
 // p ^ ((r >> 1) & 7), halves traded in rows with bit 4 set, so that the
 // 8-byte writes of 32 consecutive rows fill all banks once.
 __device__ __forceinline__ int o_off(int r, int p) { return r * 128 + ((p ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ int o_half(int r, int hf) { return 8 * (hf ^ ((r >> 4) & 1)); }
 __device__ __forceinline__ int sx_off(int cc, int ib, int v4, int l) {
     return L_SX + (((cc * 2 + ib) * 4 + v4) * 64 + l) * 16;
 }
@@ -210,7 +220,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * (2 * t + bi) + 8 * (v >> 2) + 4 * lh + (v & 3);
+                const int dk = 32 * (2 * t + bi) + state_dim(v, lh);
                 S[bi][v] = src ? src[dk * D + col] : 0.f;
             }
     }
@@ -233,11 +243,9 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             asm volatile("" : "+v"(tv));
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-                // tv < 256, so bit 4 of the row is that of 16 i4.
                 const int r = (tv >> 4) + 16 * i4;
-                const bool sw = i4 & 1;
-                lds_st(lds, L_Q + qk_off(r, tv & 15), sw ? swap_halves(qr[i4]) : qr[i4]);
-                lds_st(lds, L_K + qk_off(r, tv & 15), sw ? swap_halves(kr[i4]) : kr[i4]);
+                lds_st(lds, L_Q + qk_off(r, tv & 15), qr[i4]);
+                lds_st(lds, L_K + qk_off(r, tv & 15), kr[i4]);
             }
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2) lds_st(lds, L_V + v_off((tv >> 3) + 32 * i2, tv & 7), vr[i2]);
@@ -266,13 +274,11 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
                     for (int e = 0; e < 8; ++e) x[e] = S[bi][8 * s2 + e];
                     split_bf16x8(x, sh, sl);
                 }
-                const int cq = 4 * (2 * t + bi) + 2 * s2;
+                const int cq = 4 * (2 * t + bi) + 2 * s2 + lh;
 #pragma unroll
                 for (int ib = 0; ib < 2; ++ib) {
                     const int iq = 32 * ib + ln;
-                    const bf16x4 x0 = lds_ld<bf16x4>(lds, L_Q + qk_off(iq, cq) + qk_half(iq, lh));
-                    const bf16x4 x1 = lds_ld<bf16x4>(lds, L_Q + qk_off(iq, cq + 1) + qk_half(iq, lh));
-                    const bf16x8 bq = cat4(x0, x1);
+                    const bf16x8 bq = lds_ld<bf16x8>(lds, L_Q + qk_off(iq, cq));
                     if (ib == t) {
                         acc = mfma(sh, bq, acc);
                         acc = mfma(sl, bq, acc);
@@ -297,11 +303,8 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             f32x16 sc = {};
 #pragma unroll
             for (int s8 = 0; s8 < 8; ++s8) {
-                // Both halves of the chunk in their logical order: one MFMA
-                // pairs rows and columns that differ in bit 4.
-                const int cj = L_K + qk_off(j, 2 * s8 + lh), ci = L_Q + qk_off(iq, 2 * s8 + lh);
-                const bf16x8 a = cat4(lds_ld<bf16x4>(lds, cj + qk_half(j, 0)), lds_ld<bf16x4>(lds, cj + qk_half(j, 1)));
-                const bf16x8 bq = cat4(lds_ld<bf16x4>(lds, ci + qk_half(iq, 0)), lds_ld<bf16x4>(lds, ci + qk_half(iq, 1)));
+                const bf16x8 a = lds_ld<bf16x8>(lds, L_K + qk_off(j, 2 * s8 + lh));
+                const bf16x8 bq = lds_ld<bf16x8>(lds, L_Q + qk_off(iq, 2 * s8 + lh));
                 sc = mfma(a, bq, sc);
             }
             const float Gi = lds_ld<float>(ft, 4 * iq) + ls;
@@ -365,7 +368,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const u32x2 pk = {pack_f32(acc[4 * g4], acc[4 * g4 + 1]), pack_f32(acc[4 * g4 + 2], acc[4 * g4 + 3])};
-            lds_st(lds, L_O + o_off(i, 4 * cc + g4) + qk_half(i, lh), pk);
+            lds_st(lds, L_O + o_off(i, 4 * cc + g4) + o_half(i, lh), pk);
         }
 
         // S = exp(G_last) S + K^T (exp(G_last - G) V) on this wave's key rows.
@@ -403,7 +406,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
         for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * (2 * t + bi) + 8 * (v >> 2) + 4 * lh + (v & 3);
+                const int dk = 32 * (2 * t + bi) + state_dim(v, lh);
                 dst[dk * D + col] = S[bi][v];
             }
     }
