@@ -507,6 +507,152 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ch
     if (STATE_ONLY && tid == 0) p.gam[(int64_t)s * H + h] = gam_acc;
 }
 
+// The segment-state pass over value-column halves (inputs without the q/k
+// prologue): the state-only pass above, with one workgroup per (sub-segment,
+// head, half of the value columns), laid out by xcd_unit_map so that the two
+// halves of a sub-segment run on one XCD and read its k rows through that
+// XCD's L2. Twice the workgroups of the one-level pass, each with half its
+// MFMA and vector work per chunk: about two workgroups per compute unit, so
+// that one's load latency hides behind the other's work. Wave w holds key
+// rows 64 (w >> 1) .. + 63 and value columns 32 (w & 1) .. + 31 of the half,
+// as two 32x32 accumulator tiles. The result, the sub-segment's state from a
+// zero start and its total log-decay, goes where the scan reads it, as from
+// the one-level pass.
+constexpr int SH_KT = 0;       // (K * exp(G_last - G))^T [128 dk][128 B]
+constexpr int SH_VT = 16384;   // V^T of the half [64 dv][128 B]
+constexpr int SH_BYTES = 24576;
+static_assert(2 * SH_BYTES <= kLdsPerCU, "two state workgroups must fit one CU's LDS");
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void state_halves_kernel(ChunkParams p) {
+    int unit, half;
+    xcd_unit_map(blockIdx.x, 2, unit, half);
+    const int H = p.H;
+    const int s = unit / H;
+    const int h = unit - s * H;
+    if (s >= p.nseg_max) return;
+    const SegEntry se = seg_at(p, s);
+    if (se.len < 0) return;
+    // The last output segment of a sequence needs no carried-out state.
+    if (se.p >= p.rsub * ((se.nseg + p.rsub - 1) / p.rsub - 1)) return;
+    __shared__ __attribute__((aligned(16))) char lds[SH_BYTES];
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int cb = w & 1, kb = w >> 1;
+    const uint16_t *__restrict__ kg = static_cast<const uint16_t *>(p.k);
+    const uint16_t *__restrict__ vg = static_cast<const uint16_t *>(p.v);
+    const int64_t sl = (int64_t)D * D;
+
+    // This thread's share of a chunk: k pieces (tid & 15) of rows
+    // 2 (((tid >> 4) & 15) + 16 it) + rr, v pieces (tid & 7) of the half of
+    // rows 2 ((tid >> 3) & 31) + rr, and g of token (tid & 63); a buffer
+    // range ending at the chunk's last row zeroes the rows past a ragged end.
+    u32x4 kr[2][2], vr[2];
+    float gr;
+    auto rows_bytes = [&](int n) -> int { return (n - 1) * H * (D * 2) + D * 2; };
+    auto issue = [&](int64_t t0, int n) {
+        int tv = tid;
+        asm volatile("" : "+v"(tv));
+        const int64_t base = (t0 * H + h) * D;
+        const int nb = rows_bytes(n);
+        const buf_t rk = buf_rsrc(kg + base, nb);
+        const buf_t rv = buf_rsrc(vg + base + 64 * half, nb - 128);
+        gr = buf_ld_f32(buf_rsrc(p.g + t0 * H + h, (n - 1) * H * 4 + 4), (tv & 63) * H * 4);
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int r = 2 * (((tv >> 4) & 15) + 16 * it) + rr;
+                kr[it][rr] = buf_ld16(rk, (uint32_t)(r * H) * (uint32_t)(D * 2) + (uint32_t)(tv & 15) * 16u);
+            }
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int r = 2 * ((tv >> 3) & 31) + rr;
+            vr[rr] = buf_ld16(rv, (uint32_t)(r * H) * (uint32_t)(D * 2) + (uint32_t)(tv & 7) * 16u);
+        }
+    };
+
+    f32x16 S[2] = {};
+    float gam_acc = 0.f;
+    const int len = se.len;
+    if (len > 0) issue(se.tok0, min(64, len));
+    for (int c0 = 0; c0 < len; c0 += 64) {
+        const int64_t t0 = se.tok0 + c0;
+        int tidv = tid;
+        asm volatile("" : "+v"(tidv));
+        const int ln = tidv & 31;
+        const int lh = (tidv >> 5) & 1;
+        const int cidx = tidv & 15;
+        const int prb = (tidv >> 4) & 15;
+
+        const float G = wave_prefix_sum(gr);
+        const float Gl = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 63));
+        gam_acc += Gl;
+        float fac[2][2];
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr)
+                fac[it][rr] = __expf(Gl - __shfl(G, 2 * (prb + 16 * it) + rr, 64));
+
+        __syncthreads();  // every reader of the previous chunk's tiles is done
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+            const int r0 = 2 * (prb + 16 * it);
+            const int bo = (r0 & 7) * 2;  // byte offset of the token pair inside its chunk
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const uint32_t k0 = kr[it][0][e2], k1 = kr[it][1][e2];
+                const int d = 8 * cidx + 2 * e2;
+                lds_st(lds, SH_KT + tr_off(d, r0 >> 3) + bo,
+                       pack_f32(lo_bf16(k0) * fac[it][0], lo_bf16(k1) * fac[it][1]));
+                lds_st(lds, SH_KT + tr_off(d + 1, r0 >> 3) + bo,
+                       pack_f32(hi_bf16(k0) * fac[it][0], hi_bf16(k1) * fac[it][1]));
+            }
+        }
+        {
+            const int r0 = 2 * ((tidv >> 3) & 31);
+            const int bo = (r0 & 7) * 2;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                const uint32_t a0 = vr[0][e2], a1 = vr[1][e2];
+                const int d = 8 * (tidv & 7) + 2 * e2;
+                lds_st(lds, SH_VT + tr_off(d, r0 >> 3) + bo, pack_lo(a0, a1));
+                lds_st(lds, SH_VT + tr_off(d + 1, r0 >> 3) + bo, pack_hi(a0, a1));
+            }
+        }
+        __syncthreads();  // tiles of this chunk are in LDS
+
+        if (c0 + 64 < len) issue(t0 + 64, min(64, len - c0 - 64));
+
+        bf16x8 vop[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) vop[st] = lds_ld<bf16x8>(lds, SH_VT + tr_off(32 * cb + ln, 2 * st + lh));
+        const float a = __expf(Gl);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) S[b][v] *= a;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const bf16x8 ka = lds_ld<bf16x8>(lds, SH_KT + tr_off(64 * kb + 32 * b + ln, 2 * st + lh));
+                S[b] = mfma(ka, vop[st], S[b]);
+            }
+        }
+    }
+
+    float *dst = p.buf + ((int64_t)s * H + h) * sl;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int dk = 64 * kb + 32 * b + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+            dst[dk * D + 64 * half + 32 * cb + (l & 31)] = S[b][v];
+        }
+    if (half == 0 && tid == 0) p.gam[(int64_t)s * H + h] = gam_acc;
+}
+
 // The prologue alone: one workgroup per (64-token chunk, head) of x [B, T,
 // H, 128] bf16, through the same loads and the same prologue_chunk as the
 // chunked kernels; token t of sequence b sits at position pos_off[b] + t.
@@ -569,8 +715,15 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t
         if (phase_state) hipLaunchKernelGGL((chunk_mfma_kernel<true, true>), grid, dim3(NT), 0, st, p);
         else hipLaunchKernelGGL((chunk_mfma_kernel<false, true>), grid, dim3(NT), 0, st, p);
     } else {
-        if (phase_state) hipLaunchKernelGGL((chunk_mfma_kernel<true, false>), grid, dim3(NT), 0, st, p);
-        else hipLaunchKernelGGL((chunk_mfma_kernel<false, false>), grid, dim3(NT), 0, st, p);
+        if (phase_state) {
+            // Two workgroups per (sub-segment, head), laid out by
+            // xcd_unit_map: the grid covers every unit when it is a multiple
+            // of 16.
+            const int64_t units = (int64_t)p.nseg_max * p.H;
+            hipLaunchKernelGGL(state_halves_kernel, dim3((unsigned)((2 * units + 15) / 16 * 16)), dim3(NT), 0, st, p);
+        } else {
+            hipLaunchKernelGGL((chunk_mfma_kernel<false, false>), grid, dim3(NT), 0, st, p);
+        }
     }
     return hipGetLastError();
 }
