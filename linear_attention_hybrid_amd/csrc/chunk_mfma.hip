@@ -715,12 +715,14 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, bool phase_state, hipStream_t
         if (phase_state) hipLaunchKernelGGL((chunk_mfma_kernel<true, true>), grid, dim3(NT), 0, st, p);
         else hipLaunchKernelGGL((chunk_mfma_kernel<false, true>), grid, dim3(NT), 0, st, p);
     } else {
-        if (phase_state) {
+        if (phase_state && p.state_halves) {
             // Two workgroups per (sub-segment, head), laid out by
             // xcd_unit_map: the grid covers every unit when it is a multiple
             // of 16.
             const int64_t units = (int64_t)p.nseg_max * p.H;
             hipLaunchKernelGGL(state_halves_kernel, dim3((unsigned)((2 * units + 15) / 16 * 16)), dim3(NT), 0, st, p);
+        } else if (phase_state) {
+            hipLaunchKernelGGL((chunk_mfma_kernel<true, false>), grid, dim3(NT), 0, st, p);
         } else {
             hipLaunchKernelGGL((chunk_mfma_kernel<false, false>), grid, dim3(NT), 0, st, p);
         }

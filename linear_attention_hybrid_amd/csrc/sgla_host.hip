@@ -46,6 +46,10 @@ int choose_seg_len(int64_t ttot, int B, int H) {
 // Output segments of the value-half kernel (bf16, 128-wide heads): long
 // enough that two workgroups per compute unit cover the call, two per
 // (segment, head), and at least 512 tokens.
+// Below this many (sub-segment, head) units the state pass runs over value
+// halves: the compute units of one MI355X.
+constexpr int64_t kStateHalvesUnits = 256;
+
 int choose_out_len(int64_t ttot, int H) {
     const char *env = getenv("SGLA_OUT_SEG_LEN");
     if (env) {
@@ -115,6 +119,7 @@ struct ChunkPlan {
     int64_t nps = 1;       // segments per sequence without a table
     int64_t nseg = 0;      // table rows (segments) of the one-level or state pass
     int rsub = 1;          // sub-segments per output segment (value halves)
+    bool state_halves = false;  // state pass over value-column halves (see below)
     int oseg_len = 0;      // value-half output segments
     int64_t onps = 1;
     int64_t onseg = 0;
@@ -261,6 +266,12 @@ sgla_status make_plan(int B, int T, int H, int Dk, int Dv, sgla_dtype dtype, boo
         pl.split = pl.table || pl.onps > 1;
         const int64_t pre_units = varlen ? (ttot / pl.oseg_len) * H : (pl.onps - 1) * B * H;
         pl.rsub = pl.split ? choose_rsub(pl.oseg_len, pre_units) : 1;
+        // The state pass over value-column halves, when one workgroup per
+        // (sub-segment, head) would leave compute units idle. Measured: on
+        // the 8192-token call (224 units) 108.3 against 109.5 us flushed;
+        // on the 65,536-token call (448 units) 756 against 712 us and on
+        // the 524,288-token varlen call 6.19 against 5.94 ms, so not there.
+        pl.state_halves = pl.split && pre_units * pl.rsub < kStateHalvesUnits;
         pl.seg_len = pl.oseg_len / pl.rsub;
         pl.nps = T == 0 ? 1 : ((int64_t)T + pl.seg_len - 1) / pl.seg_len;
         pl.nseg = !pl.split ? 0 : pl.table ? ttot / pl.seg_len + B + 1 : (int64_t)B * pl.nps;
@@ -363,6 +374,7 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
     p.theta = pro ? pro->theta : 0.f;
     p.eps = pro ? pro->eps : 0.f;
     p.rsub = pl.rsub;
+    p.state_halves = pl.state_halves ? 1 : 0;
     const bool bf16 = dtype == SGLA_BF16;
 
     hipError_t e = hipSuccess;

@@ -65,6 +65,10 @@ struct ChunkParams {
     // longer starts output segment j of a sequence from the state the scan
     // leaves in slot first + rsub * j. 1 when both passes use the same segments.
     int rsub;
+    // Nonzero: the state pass (without the prologue) runs one workgroup per
+    // (sub-segment, head, half of the value columns) instead of one per
+    // (sub-segment, head).
+    int state_halves;
 };
 
 // Arguments of the value-half output kernel (chunk_halves.hip): the output
