@@ -52,8 +52,7 @@ constexpr int NTH = 256;              // four waves
 constexpr int L_Q = 0;                // Q rows [64][256 B], swizzled as qk_off
 constexpr int L_K = 16384;            // K rows, same layout
 constexpr int L_V = 32768;            // the half's V rows [64][128 B], swizzled as v_off
-constexpr int L_G = 40960;            // g [64] fp32
-constexpr int L_A = 41216;            // scores A[64 i][128 B] bf16, swizzled as tr_off
+constexpr int L_A = 40960;            // scores A[64 i][128 B] bf16, swizzled as tr_off
 constexpr int L_SX = L_A + 8192;      // fp32 partials of Q S [block cc 2][token half 2][4][lane 64] x 16 B
 constexpr int L_O = L_SX + 16384;     // output staging [64 rows][128 B], swizzled as o_off
 constexpr int L_F = L_O + 8192;       // per wave: G[64] and exp(G_last - G)[64], fp32
@@ -249,16 +248,18 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             }
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2) lds_st(lds, L_V + v_off((tv >> 3) + 32 * i2, tv & 7), vr[i2]);
-            if (w == 0) lds_st(lds, L_G + 4 * l, gr);
         }
-        __syncthreads();  // chunk c's tiles are in LDS
-        issue(c + 1);
-
-        // Gate prefix sum, one lane per token (rows past the end read as 0).
-        const float G = wave_prefix_sum(lds_ld<float>(lds, L_G + 4 * l));
+        // Gate prefix sum over this wave's own copy of g, one lane per token
+        // (rows past the end read as 0), and the wave's gate table, before
+        // the barrier: the table is the wave's own, and its reads of the
+        // previous chunk's values came first (a wave's LDS accesses complete
+        // in order).
+        const float G = wave_prefix_sum(gr);
         const float Gl = lane_value(G, 63);
         lds_st(ft, 4 * l, G * 1.44269504088896341f);
         lds_st(ft, 256 + 4 * l, l < n ? __expf(Gl - G) : 0.f);
+        __syncthreads();  // chunk c's tiles are in LDS
+        issue(c + 1);
 
         // O^T = S^T Q^T over this wave's key rows for both token halves;
         // the other half's partial sums go to the partner wave.
