@@ -54,7 +54,7 @@ constexpr int L_K = 16384;            // K rows, same layout
 constexpr int L_V = 32768;            // the half's V rows [64][128 B], swizzled as v_off
 constexpr int L_A = 40960;            // scores A[64 i][128 B] bf16, swizzled as tr_off
 constexpr int L_SX = L_A + 8192;      // fp32 partials of Q S [block cc 2][token half 2][4][lane 64] x 16 B
-constexpr int L_O = L_SX + 16384;     // output staging [64 rows][128 B], swizzled as o_off
+constexpr int L_O = L_SX + 16384;     // output staging [64 rows][128 B], swizzled as o_off; first the update's V operand halves passed between partner waves
 constexpr int L_F = L_O + 8192;       // per wave: G[64] and exp(G_last - G)[64], fp32
 constexpr int L_BYTES = L_F + 4 * 512;
 static_assert(2 * L_BYTES <= kLdsPerCU, "two workgroups must fit one compute unit's LDS");
@@ -341,7 +341,29 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             vop[s4] = cat4(lds_tr(lds, L_V + vtr_src(16 * s4 + 8 * lh, c0, m16)),
                            lds_tr(lds, L_V + vtr_src(16 * s4 + 8 * lh + 4, c0, m16)));
         }
-        __syncthreads();  // the scores and the partial sums are staged
+        // The update's V operand, exp(G_last - G) V: this wave forms tokens
+        // 32t .. 32t+31 (s4 = 2t, 2t+1), which its partner (cc, 1-t) needs as
+        // well, and hands them over in the partner's own output-staging
+        // slots (rows 32(1-t) .., pieces 4cc ..), unused until the partner
+        // stages its output after reading them; it takes the other two from
+        // its own slots after the barrier.
+        const bool upd = c + 1 < nch || (last && p.sfin);
+        bf16x8 vs[4];
+        if (upd) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int s4 = 2 * t + k;
+                const float4 f0 = lds_ld<float4>(ft, 256 + 4 * (16 * s4 + 8 * lh));
+                const float4 f1 = lds_ld<float4>(ft, 256 + 4 * (16 * s4 + 8 * lh) + 16);
+                const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+                float xs[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xs[e] = (float)vop[s4][e] * fe[e];
+                vs[s4] = to_bf16x8(xs);
+                lds_st(lds, L_O + o_off(32 * (1 - t) + ln, 4 * cc + 2 * k + lh), vs[s4]);
+            }
+        }
+        __syncthreads();  // the scores, the partial sums and the V operand halves are staged
 
         // The partner's key rows, then the rows scaled by scale * exp(G_i).
         {
@@ -365,6 +387,12 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
                 acc = mfma(vop[s4], ba, acc);
             }
         }
+        // The partner's half of the V operand, read before this wave's
+        // output rows overwrite those slots.
+        if (upd) {
+#pragma unroll
+            for (int k = 0; k < 2; ++k) vs[2 * (1 - t) + k] = lds_ld<bf16x8>(lds, L_O + o_off(32 * t + ln, 4 * cc + 2 * k + lh));
+        }
         // Output rows into the staging tile (stored at the next iteration).
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
@@ -373,7 +401,7 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
         }
 
         // S = exp(G_last) S + K^T (exp(G_last - G) V) on this wave's key rows.
-        if (c + 1 < nch || (last && p.sfin)) {
+        if (upd) {
             const float a = __expf(Gl);
 #pragma unroll
             for (int bi = 0; bi < 2; ++bi)
@@ -381,19 +409,12 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
                 for (int v = 0; v < 16; ++v) S[bi][v] *= a;
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
-                const float4 f0 = lds_ld<float4>(ft, 256 + 4 * (16 * s4 + 8 * lh));
-                const float4 f1 = lds_ld<float4>(ft, 256 + 4 * (16 * s4 + 8 * lh) + 16);
-                const float fe[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-                float xs[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xs[e] = (float)vop[s4][e] * fe[e];
-                const bf16x8 vs = to_bf16x8(xs);
 #pragma unroll
                 for (int bi = 0; bi < 2; ++bi) {
                     const int c0 = 32 * (2 * t + bi) + 16 * (gi & 1);
                     const bf16x8 kt = cat4(lds_tr(lds, L_K + qk_tr_src(16 * s4 + 8 * lh, c0, m16)),
                                            lds_tr(lds, L_K + qk_tr_src(16 * s4 + 8 * lh + 4, c0, m16)));
-                    S[bi] = mfma(kt, vs, S[bi]);
+                    S[bi] = mfma(kt, vs[s4], S[bi]);
                 }
             }
         }
