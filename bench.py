@@ -59,10 +59,10 @@ KDA_DECODE = "kda_decode_bf16_n256_h32_d128_x64"
 FP32_PEAK_TFLOPS = 157.3  # MI355X fp32, vendor figure: dense matrix cores and vector ALUs alike
 # The kernels of one call of each workload, as rocprofv3 names them.
 CALL_KERNELS = {
-    PREFILL: ["state_halves_kernel", "scan_kernel<128, 128>", "chunk_halves_kernel"],
+    PREFILL: ["state_halves_kernel", "chunk_halves_kernel"],
     PREFILL_PRO: ["chunk_mfma_kernel<true, true>", "scan_kernel<128, 128>",
                   "chunk_mfma_kernel<false, true>"],
-    LONG: ["chunk_mfma_kernel<true, false>", "scan_kernel<128, 128>", "chunk_halves_kernel"],
+    LONG: ["chunk_mfma_kernel<true, false>", "chunk_halves_kernel"],
     VARLEN: ["plan_kernel", "chunk_mfma_kernel<true, false>", "scan_kernel<128, 128>",
              "chunk_mfma_kernel<false, false>"],
     DECODE: ["recurrent_step_kernel<unsigned short, 128, 128, false, float>"],

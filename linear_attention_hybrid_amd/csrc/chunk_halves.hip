@@ -38,8 +38,9 @@
 // through an LDS staging tile, so each row's 128 bytes are stored as one line.
 //
 // The start state of a segment is the initial state, or, when the sequence
-// spans several output segments, the state the scan kernel left in the
-// segment-state buffer.
+// spans several output segments, the initial state and the states of the
+// sub-segments before it (from the state pass), combined at the start of the
+// workgroup: this path needs no scan kernel.
 #include "mfma_tile.h"
 
 namespace sgla {
@@ -203,25 +204,72 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
         }
     };
 
-    // The start state, key tiles 2t and 2t + 1 of this column block.
-    f32x16 S[2];
+    // The start state, key tiles 2t and 2t + 1 of this column block: the
+    // initial state decayed over the sub-segments before this output
+    // segment, plus each of their zero-start states (left by the state pass
+    // with its total log-decay) decayed over the sub-segments after it: the
+    // recurrence regrouped. The weights come from running sums of the
+    // log-decays, taken from the nearest sub-segment back, so every load is
+    // independent of the others. The first chunk's loads follow, so that
+    // their registers are free here.
+    f32x16 S[2] = {};
     {
-        const float *src;
-        if (se.nseg == 1) {
-            src = p.s0 ? p.s0 + ((int64_t)se.seq * H + h) * sl : nullptr;
-        } else {
-            // Clamped into the buffer, so that offsets that break the
-            // documented rule cannot send the read past it.
-            const int slot = min(seq_at(p, se.seq).first + p.rsub * se.p, p.nseg_max - 1);
-            src = p.buf + ((int64_t)slot * H + h) * sl;
+        const int nj = se.nseg == 1 ? 0 : p.rsub * se.p;  // sub-segments before this segment
+        const int first = nj > 0 ? seq_at(p, se.seq).first : 0;
+        // This lane's 32 values of the state at `src`, all loads issued
+        // before any is used: the opaque step needs every value, so the
+        // compiler cannot interleave each load with its use.
+        auto fetch = [&](const float *src, float (&x)[32]) {
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) x[16 * bi + v] = src[(32 * (2 * t + bi) + state_dim(v, lh)) * D + col];
+        };
+        auto settle32 = [](float (&x)[32]) {
+            asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]),
+                         "+v"(x[6]), "+v"(x[7]), "+v"(x[8]), "+v"(x[9]), "+v"(x[10]), "+v"(x[11]),
+                         "+v"(x[12]), "+v"(x[13]), "+v"(x[14]), "+v"(x[15]));
+            asm volatile("" : "+v"(x[16]), "+v"(x[17]), "+v"(x[18]), "+v"(x[19]), "+v"(x[20]), "+v"(x[21]),
+                         "+v"(x[22]), "+v"(x[23]), "+v"(x[24]), "+v"(x[25]), "+v"(x[26]), "+v"(x[27]),
+                         "+v"(x[28]), "+v"(x[29]), "+v"(x[30]), "+v"(x[31]));
+        };
+        auto add = [&](float wgt, const float (&x)[32]) {
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) S[bi][v] = fmaf(wgt, x[16 * bi + v], S[bi][v]);
+        };
+        // Clamped into the buffer, so that offsets that break the documented
+        // rule cannot send a read past it.
+        auto slot_of = [&](int i) { return min(first + i, p.nseg_max - 1); };
+        auto dstate = [&](int i) { return p.buf + ((int64_t)slot_of(i) * H + h) * sl; };
+        auto lgam = [&](int i) { return p.gam[(int64_t)slot_of(i) * H + h]; };
+        float tail = 0.f;  // log-decay of the sub-segments after i, up to this segment
+        int i = nj - 1;
+        for (; i >= 1; i -= 2) {  // two sub-segment states in flight at a time
+            float x0[32], x1[32];
+            fetch(dstate(i), x0);
+            fetch(dstate(i - 1), x1);
+            settle32(x0);
+            settle32(x1);
+            add(__expf(tail), x0);
+            tail += lgam(i);
+            add(__expf(tail), x1);
+            tail += lgam(i - 1);
         }
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int dk = 32 * (2 * t + bi) + state_dim(v, lh);
-                S[bi][v] = src ? src[dk * D + col] : 0.f;
-            }
+        if (i == 0) {
+            float x0[32];
+            fetch(dstate(0), x0);
+            settle32(x0);
+            add(__expf(tail), x0);
+            tail += lgam(0);
+        }
+        if (p.s0) {
+            float x0[32];
+            fetch(p.s0 + ((int64_t)se.seq * H + h) * sl, x0);
+            settle32(x0);
+            add(__expf(tail), x0);
+        }
     }
     if (nch > 0) issue(0);
 

@@ -396,8 +396,8 @@ sgla_status chunk_fwd(const void *q, const void *k, const void *v, const float *
                                 reinterpret_cast<SegEntry *>(at(pl.off_segs)),
                                 reinterpret_cast<SeqEntry *>(at(pl.off_seqs)), st);
         }
+        // The output kernel combines the sub-segment states itself (no scan).
         if (e == hipSuccess && pl.split) e = launch_chunk_mfma(p, /*phase_state=*/true, st);
-        if (e == hipSuccess && pl.split) e = launch_scan(p, 128, 128, st);
         if (e == hipSuccess) e = launch_chunk_halves(hp, st);
         return hip_status(e);
     }
