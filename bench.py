@@ -582,7 +582,7 @@ def main():
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "frac_of_stream_copy": achieved / copy_gbs,
                          "traffic": recorded_traffic(PREFILL),
-                         "kernel": "sgla_chunk_fwd_ex (whole call: segment-state, scan and "
+                         "kernel": "sgla_chunk_fwd_ex (whole call: segment-state and "
                                    "value-half output kernels)",
                          "algorithmic_bytes_per_launch": nbytes,
                          "avg_launch_ms": ms_step},
@@ -744,7 +744,7 @@ def bench_long(args, torch, sgla, W, dev):
                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "traffic": recorded_traffic(LONG),
-                        "kernel": "sgla_chunk_fwd_ex (whole call: segment-state, scan and "
+                        "kernel": "sgla_chunk_fwd_ex (whole call: segment-state and "
                                   "value-half output kernels)",
                         "algorithmic_bytes_per_launch": nbytes, "avg_launch_ms": ms},
            "mfma_busy": recorded_mfma(LONG),
