@@ -138,11 +138,12 @@ sgla_status sgla_chunk_fwd_workspace_size(int B, int T, int H, int Dk, int Dv, s
  * split across workgroups.
  *
  * With a workspace each sequence is cut into segments. A first pass computes
- * every segment's state contribution from a zero state, a scan combines them
- * in order into the state each segment starts from (the recurrence regrouped:
+ * every segment's state contribution from a zero state; these are combined in
+ * order into the state each segment starts from (the recurrence regrouped:
  * the decayed initial state plus the decayed sum of outer products, blueprint
- * page, section "Why Linear Attention Loses Information"), and the output
- * pass runs all segments at once. With packed sequences, device-side tables
+ * page, section "Why Linear Attention Loses Information"), by a scan pass or
+ * by the output workgroups as they start, and the output pass runs all
+ * segments at once. With packed sequences, device-side tables
  * lay the segments out from cu_seqlens.
  *
  *   workspace        device memory, 256-byte aligned, owned by the caller,

@@ -68,11 +68,11 @@ int choose_out_len(int64_t ttot, int H) {
 // 1024 tokens (16 chunks) and whole chunks. pre_units = (segment, head) pairs
 // whose state is needed when each output segment is one sub-segment.
 // Measured on the 8192-token call (1024-token output segments): one
-// sub-segment each, 111.9 us flushed, against 114.3 us with two of 512
-// tokens (shorter workgroups spend more of their time waiting for their
-// first chunk, and the scan moves twice the states); on the 65,536-token call
-// two 4096-token sub-segments stay best (732 us, against 758 us with one or
-// four).
+// sub-segment each, 104.1 us flushed, against 111.2 us with two of 512
+// tokens and 140.0 us with four (shorter workgroups spend more of their time
+// waiting for their first chunk, and the output workgroups combine twice the
+// states); on the 65,536-token call two 4096-token sub-segments stay best
+// (707.6 us flushed, against 737.7 us with one and 755.5 us with four).
 int choose_rsub(int out_len, int64_t pre_units) {
     const char *env = getenv("SGLA_RSUB");
     if (env) {
