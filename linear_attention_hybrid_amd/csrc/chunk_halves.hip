@@ -210,8 +210,10 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
     // with its total log-decay) decayed over the sub-segments after it: the
     // recurrence regrouped. The weights come from running sums of the
     // log-decays, taken from the nearest sub-segment back, so every load is
-    // independent of the others. The first chunk's loads follow, so that
-    // their registers are free here.
+    // independent of the others. The first chunk's loads go first, so that
+    // they land while the states are read; one state is in flight at a time,
+    // which leaves registers for them.
+    if (nch > 0) issue(0);
     f32x16 S[2] = {};
     {
         const int nj = se.nseg == 1 ? 0 : p.rsub * se.p;  // sub-segments before this segment
@@ -245,24 +247,12 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
         auto dstate = [&](int i) { return p.buf + ((int64_t)slot_of(i) * H + h) * sl; };
         auto lgam = [&](int i) { return p.gam[(int64_t)slot_of(i) * H + h]; };
         float tail = 0.f;  // log-decay of the sub-segments after i, up to this segment
-        int i = nj - 1;
-        for (; i >= 1; i -= 2) {  // two sub-segment states in flight at a time
-            float x0[32], x1[32];
+        for (int i = nj - 1; i >= 0; --i) {
+            float x0[32];
             fetch(dstate(i), x0);
-            fetch(dstate(i - 1), x1);
             settle32(x0);
-            settle32(x1);
             add(__expf(tail), x0);
             tail += lgam(i);
-            add(__expf(tail), x1);
-            tail += lgam(i - 1);
-        }
-        if (i == 0) {
-            float x0[32];
-            fetch(dstate(0), x0);
-            settle32(x0);
-            add(__expf(tail), x0);
-            tail += lgam(0);
         }
         if (p.s0) {
             float x0[32];
@@ -271,7 +261,6 @@ __device__ void halves_wave(const HalvesParams &hp, const SegEntry &se, int h, i
             add(__expf(tail), x0);
         }
     }
-    if (nch > 0) issue(0);
 
     char *ft = lds + L_F + 512 * w;  // this wave's G log2(e) [64], then exp(G_last - G)[64]
     const int i = 32 * t + ln;        // this lane's query row of the output
