@@ -28,12 +28,15 @@
 //
 // The pairwise factors exp(G[a][d] - G[b][d]) of M and L are never formed as
 // exp(G[a]) exp(-G[b]), which overflows once a chunk's gates sum past about
-// -88. Inside each 16-token block they are taken directly; between block I
-// (queries a) and an earlier token b they are split at the block's first
-// token c, exp(G[a] - G[c]) exp(G[c] - G[b]), two factors that each lie in
-// (0, 1] when g <= 0, so every block pair costs one exponential per element
-// and token rather than per pair; the products between blocks run on the
-// matrix cores as bf16 high/low pairs. T is inverted in 16 x 16 blocks: each
+// -88. Between block I (queries a) and an earlier token b they are split at
+// the block's first token c, exp(G[a] - G[c]) exp(G[c] - G[b]), two factors
+// that each lie in (0, 1] when g <= 0, so every block pair costs one
+// exponential per element and token rather than per pair; the products run
+// on the matrix cores as bf16 high/low pairs. Inside block I the same split
+// gives a factor exp(G[c] - G[b]) >= 1 for its own keys b >= c, which is
+// safe while the gates of the block span little (kSplitSpan); the diagonal
+// blocks then run the same way, and a chunk where some block spans more
+// takes their pairwise factors directly instead. T is inverted in 16 x 16 blocks: each
 // diagonal block by back substitution on one wave, the blocks below it block
 // row by block row, T_IJ = -T_II sum_K A_IK T_KJ, on fp32 MFMAs.
 #include "mfma_tile.h"
@@ -62,6 +65,28 @@ __device__ __forceinline__ void st_f1(buf_t r, uint32_t off, float v) {
 
 constexpr int KC = kChunk;  // tokens per chunk
 constexpr int KP = KC + 1;  // padded token stride of transposed tiles
+constexpr int XR = KC + 16; // rows of the bf16 high/low tiles of decayed rows
+
+// The diagonal 16 x 16 blocks of M and L are split at their first token c
+// when every |G[t][d] - G[c][d]| over the block's tokens t stays within this
+// span: each factor then lies within exp(+-40), finite and normal in fp32 and
+// bf16, and each product term keeps about 2^-16 of its value as between
+// blocks. A chunk where some block spans more takes the diagonal blocks'
+// exponents pair by pair.
+constexpr float kSplitSpan = 40.f;
+
+// G: inclusive cumulative sums over a chunk's tokens, one wave per key dim
+// (lane = token), for the tile Gt[DK][KP] of the chunk's gates. Sets *wide
+// when some token's G leaves its 16-token block's first value by more than
+// kSplitSpan (the writes race benignly: all store 1).
+template <int DK, int NT>
+__device__ __forceinline__ void gate_prefix(float (*Gt)[KP], int w, int l, int *wide) {
+    for (int d = w; d < DK; d += NT / 64) {
+        const float x = wave_prefix_sum(Gt[d][l]);
+        Gt[d][l] = x;
+        if (fabsf(x - __shfl(x, l & 48, 64)) > kSplitSpan) *wide = 1;
+    }
+}
 
 // Per chunk and head workspace tile, in floats: W, then K * exp(G_last - G),
 // then U, each as fp32 MFMA operand images (below), then exp(G_last) [Dk].
@@ -218,14 +243,16 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     __shared__ float Gt[DK][KP];       // G^T
     __shared__ float Vs[KC][DV + 1];   // diag(beta) V
     __shared__ __attribute__((aligned(16))) float Ms[KC][MP];  // A = diag(beta) M below the diagonal; then T
-    // K decayed to a reference token, as bf16 high and low tiles; later the
-    // blocks of T (14 blocks of 16 rows x 20 floats).
-    constexpr int XT = 2 * KC * DK * 2, XTB = 14 * 16 * 20 * 4;
+    // K decayed to a reference token, as bf16 high and low tiles of XR rows;
+    // later the blocks of T (14 blocks of 16 rows x 20 floats).
+    constexpr int XT = 2 * XR * DK * 2, XTB = 14 * 16 * 20 * 4;
     __shared__ __attribute__((aligned(16))) char Xb[XT > XTB ? XT : XTB];
     char *const Xh = Xb;
-    char *const Xl = Xb + KC * DK * 2;
+    char *const Xl = Xb + XR * DK * 2;
     __shared__ float bs[KC];
-    static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xb) + sizeof(bs) <= kLdsPerCU,
+    __shared__ int wide;  // some diagonal block's gates span more than kSplitSpan
+    static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xb) + sizeof(bs) + sizeof(wide) <=
+                      kLdsPerCU,
                   "the workgroup must fit one CU's LDS");
     const int H = p.c.H;
     const int tid = threadIdx.x;
@@ -266,6 +293,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
         continue;
     }
     const int s = it.s, h = it.h;
+    if (tid == 0) wide = 0;   // the last item read it before its final barrier
     bs[tid & (KC - 1)] = rb;  // eight threads per token write the same value
     rk.template store<true, KP>(&Kt[0][0], tid);
     rg.template store<true, KP>(&Gt[0][0], tid);
@@ -276,33 +304,42 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
         const int a = i / DV, j = i - a * DV;
         Vs[a][j] *= bs[a];
     }
-    // G: cumulative sums over the tokens, one wave per key dim, lane = token.
-    for (int d = w; d < DK; d += NT / 64) Gt[d][l] = wave_prefix_sum(Gt[d][l]);
+    gate_prefix<DK, NT>(Gt, w, l, &wide);
     __syncthreads();
 
-    // A inside the diagonal 16 x 16 blocks (a > b), exponent taken directly.
-    for (int i = tid; i < 4 * 120; i += NT) {
-        const int blk = i / 120, r = i - blk * 120;
-        int ai = 1;
-        while ((ai + 1) * ai / 2 <= r) ++ai;
-        const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai - 1) / 2);
-        float acc = 0.f;
-        for (int d = 0; d < DK; ++d) acc = fmaf(Kt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
-        Ms[a][b] = bs[a] * acc;
+    // A inside the diagonal 16 x 16 blocks (a > b): split at the block's
+    // first token with the blocks below (when the gates allow), else here,
+    // one pair per thread with its exponent taken directly.
+    const bool split = __builtin_amdgcn_readfirstlane(wide) == 0;
+    if (!split) {
+        for (int i = tid; i < 4 * 120; i += NT) {
+            const int blk = i / 120, r = i - blk * 120;
+            int ai = 1;
+            while ((ai + 1) * ai / 2 <= r) ++ai;
+            const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai - 1) / 2);
+            float acc = 0.f;
+            for (int d = 0; d < DK; ++d) acc = fmaf(Kt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
+            Ms[a][b] = bs[a] * acc;
+        }
     }
-    // A below the diagonal blocks: block row I against tokens b < c = 16 I,
-    // split at c, the decayed keys as bf16 hi/lo tiles; one wave per 16 x 16
-    // block on the matrix cores.
-    for (int I = 1; I < 4; ++I) {
-        const int c = 16 * I;
+    // A by block row I: tokens b < c = 16 I, and with the split block I's own
+    // tokens, against block I's, split at c. The decayed keys go to bf16
+    // hi/lo tiles: rows below c hold K exp(G_c - G) (keys b = row), rows
+    // c .. c + 15 K exp(G - G_c) (block I as a), rows c + 16 .. c + 31 K
+    // exp(G_c - G) (block I as b = row - 16); one wave per 16 x 16 block on
+    // the matrix cores.
+    for (int I = split ? 0 : 1; I < 4; ++I) {
+        const int c = 16 * I, nr = c + (split ? 32 : 16);
         __syncthreads();  // the previous block row's products are done with the tiles
-        for (int i = tid; i < (c + 16) * DK / 2; i += NT) {
+        for (int i = tid; i < nr * DK / 2; i += NT) {
             const int a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
+            const bool qry = a >= c && a < c + 16;
+            const int t = a < c + 16 ? a : a - 16;
             float x[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const float ex = a < c ? Gt[d + e][c] - Gt[d + e][a] : Gt[d + e][a] - Gt[d + e][c];
-                x[e] = Kt[d + e][a] * __expf(ex);
+                const float ex = qry ? Gt[d + e][t] - Gt[d + e][c] : Gt[d + e][c] - Gt[d + e][t];
+                x[e] = Kt[d + e][t] * __expf(ex);
             }
             const uint32_t u0 = __float_as_uint(x[0]), u1 = __float_as_uint(x[1]);
             const int off = brow_off<DK>(a, d >> 3) + 2 * (d & 7);
@@ -311,12 +348,19 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
                 pack_f32(x[0] - __uint_as_float(u0 & 0xffff0000u), x[1] - __uint_as_float(u1 & 0xffff0000u));
         }
         __syncthreads();
+        const int lc = l & 15, g4 = 4 * (l >> 4), a = c + lc;
         if (w < I) {
             const f32x4 acc = block_product<DK>(Xh, Xl, I, w, l);
-            const int a = c + (l & 15), b0 = 16 * w + 4 * (l >> 4);
             const float ba = bs[a];
-            *reinterpret_cast<float4 *>(&Ms[a][b0]) =
+            *reinterpret_cast<float4 *>(&Ms[a][16 * w + g4]) =
                 make_float4(ba * acc[0], ba * acc[1], ba * acc[2], ba * acc[3]);
+        } else if (split && w == I) {
+            // Keys b = c + g4 + r of the block itself; A keeps b < a.
+            const f32x4 acc = block_product<DK>(Xh, Xl, I, I + 1, l);
+            const float ba = bs[a];
+            *reinterpret_cast<float4 *>(&Ms[a][c + g4]) =
+                make_float4(g4 < lc ? ba * acc[0] : 0.f, g4 + 1 < lc ? ba * acc[1] : 0.f,
+                            g4 + 2 < lc ? ba * acc[2] : 0.f, g4 + 3 < lc ? ba * acc[3] : 0.f);
         }
     }
     __syncthreads();
@@ -654,11 +698,12 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
     __shared__ float Kt[DK][KP];
     __shared__ float Gt[DK][KP];
     __shared__ __attribute__((aligned(16))) float Ls[KC][LP];
-    __shared__ __attribute__((aligned(16))) char Xb[2 * KC * DK * 2];  // bf16 hi and lo tiles
-    static_assert(sizeof(Qt) + sizeof(Kt) + sizeof(Gt) + sizeof(Ls) + sizeof(Xb) <= kLdsPerCU,
+    __shared__ __attribute__((aligned(16))) char Xb[2 * XR * DK * 2];  // bf16 hi and lo tiles
+    __shared__ int wide;  // some diagonal block's gates span more than kSplitSpan
+    static_assert(sizeof(Qt) + sizeof(Kt) + sizeof(Gt) + sizeof(Ls) + sizeof(Xb) + sizeof(wide) <= kLdsPerCU,
                   "the workgroup must fit one CU's LDS");
     char *const Xh = Xb;
-    char *const Xl = Xb + KC * DK * 2;
+    char *const Xl = Xb + XR * DK * 2;
 
     const int H = p.c.H;
     const int tid = threadIdx.x;
@@ -702,44 +747,56 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
         continue;
     }
     const int h = it.h, n = it.n;
+    if (tid == 0) wide = 0;  // the last item read it before its final barrier
     rq.template store<true, KP>(&Qt[0][0], tid);
     rk.template store<true, KP>(&Kt[0][0], tid);
     rg.template store<true, KP>(&Gt[0][0], tid);
     fetch_rows(next);
     __syncthreads();
-    for (int d = w; d < DK; d += NT / 64) Gt[d][l] = wave_prefix_sum(Gt[d][l]);
+    gate_prefix<DK, NT>(Gt, w, l, &wide);
     __syncthreads();
 
-    // L inside the diagonal blocks: one pair (a > b) per thread, the
-    // diagonal itself (no decay) on the rest, zeros above it.
-    if (tid < 4 * 120) {
-        const int blk = tid / 120, r = tid - blk * 120;
-        int ai = 1;
-        while ((ai + 1) * ai / 2 <= r) ++ai;
-        const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai - 1) / 2);
-        float acc = 0.f;
-        for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
-        Ls[a][b] = acc;
-        Ls[b][a] = 0.f;
-    } else {
-        for (int a = tid - 4 * 120; a < KC; a += NT - 4 * 120) {
+    // L inside the diagonal blocks: split at the block's first token with
+    // the blocks below (when the gates allow), else here, one pair (a > b)
+    // per thread with its exponent taken directly, the diagonal itself (no
+    // decay) on the rest, zeros above it.
+    const bool split = __builtin_amdgcn_readfirstlane(wide) == 0;
+    if (!split) {
+        if (tid < 4 * 120) {
+            const int blk = tid / 120, r = tid - blk * 120;
+            int ai = 1;
+            while ((ai + 1) * ai / 2 <= r) ++ai;
+            const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai - 1) / 2);
             float acc = 0.f;
-            for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a], Kt[d][a], acc);
-            Ls[a][a] = acc;
+            for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
+            Ls[a][b] = acc;
+            Ls[b][a] = 0.f;
+        } else {
+            for (int a = tid - 4 * 120; a < KC; a += NT - 4 * 120) {
+                float acc = 0.f;
+                for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a], Kt[d][a], acc);
+                Ls[a][a] = acc;
+            }
         }
     }
-    // L below the diagonal blocks: block row I against tokens b < c = 16 I,
-    // queries as Q exp(G - G_c) and keys as K exp(G_c - G), bf16 hi/lo.
-    for (int I = 1; I < 4; ++I) {
-        const int c = 16 * I;
+    // L by block row I: tokens b < c = 16 I, and with the split block I's own
+    // tokens, against block I's queries, as bf16 hi/lo tiles: rows below c
+    // hold K exp(G_c - G) (keys b = row), rows c .. c + 15 Q exp(G - G_c)
+    // (queries), rows c + 16 .. c + 31 K exp(G_c - G) (keys b = row - 16).
+    for (int I = split ? 0 : 1; I < 4; ++I) {
+        const int c = 16 * I, nr = c + (split ? 32 : 16);
         __syncthreads();  // the previous block row's products are done with the tiles
-        for (int i = tid; i < (c + 16) * DK / 2; i += NT) {
+        for (int i = tid; i < nr * DK / 2; i += NT) {
             const int a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
+            const bool qry = a >= c && a < c + 16;
+            const int t = a < c + 16 ? a : a - 16;
+            const float *src = qry ? &Qt[0][0] : &Kt[0][0];
             float x[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e)
-                x[e] = a < c ? Kt[d + e][a] * __expf(Gt[d + e][c] - Gt[d + e][a])
-                             : Qt[d + e][a] * __expf(Gt[d + e][a] - Gt[d + e][c]);
+            for (int e = 0; e < 2; ++e) {
+                const float ex = qry ? Gt[d + e][t] - Gt[d + e][c] : Gt[d + e][c] - Gt[d + e][t];
+                x[e] = src[(d + e) * KP + t] * __expf(ex);
+            }
             const uint32_t u0 = __float_as_uint(x[0]), u1 = __float_as_uint(x[1]);
             const int off = brow_off<DK>(a, d >> 3) + 2 * (d & 7);
             *reinterpret_cast<uint32_t *>(Xh + off) = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
@@ -750,6 +807,13 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
         if (w < I) {
             const f32x4 acc = block_product<DK>(Xh, Xl, I, w, l);
             *reinterpret_cast<float4 *>(&Ls[c + lr][16 * w + 4 * lk]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        } else if (split && w == I) {
+            // Keys b = c + 4 lk + v of the block itself; L keeps b <= a = c + lr.
+            const f32x4 acc = block_product<DK>(Xh, Xl, I, I + 1, l);
+            const int b0 = 4 * lk;
+            *reinterpret_cast<float4 *>(&Ls[c + lr][c + b0]) =
+                make_float4(b0 <= lr ? acc[0] : 0.f, b0 + 1 <= lr ? acc[1] : 0.f, b0 + 2 <= lr ? acc[2] : 0.f,
+                            b0 + 3 <= lr ? acc[3] : 0.f);
         }
     }
     // Q * exp(G): for fp32 inputs in place, for the fp32 products below; for
@@ -780,20 +844,29 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
     }
     __syncthreads();
 
-    // O blocks (tt, cb): (Q exp G) S_in, then L[16 tt + r][16 t + 4 kk + k4]
-    // against new_v on fp32 MFMAs. For bf16 inputs the first product takes
-    // the start-state blocks 2 ks and 2 ks + 1 of each lane as one 8-value
-    // k slice, split into bf16 hi/lo (hi hi + hi lo + lo hi, about 2^-16 of
-    // each term); for fp32 inputs it is fp32 16 x 16 x 4 MFMAs, A =
-    // (Q exp G)[16 tt + r][16 b + 4 kk + k4]. Both leave O[16 tt + 4 kk + v]
-    // [16 cb + r] in element v.
+    // O blocks (tt, cb): (Q exp G) S_in, then L new_v. For bf16 inputs both
+    // run on 16 x 16 x 32 MFMAs as bf16 hi/lo (hi hi + hi lo + lo hi, about
+    // 2^-16 of each term): the first takes the start-state blocks 2 ks and
+    // 2 ks + 1 of each lane as one 8-value k slice, the second the new_v
+    // blocks 2 u and 2 u + 1 likewise, against L[16 tt + r][32 u + 4 kk .. +3]
+    // and L[16 tt + r][32 u + 16 + 4 kk .. +3] (zeros past block tt). For
+    // fp32 inputs they are fp32 16 x 16 x 4 MFMAs, A = (Q exp G)[16 tt + r]
+    // [16 b + 4 kk + k4] and L[16 tt + r][16 t + 4 kk + k4]. All leave
+    // O[16 tt + 4 kk + v][16 cb + r] in element v.
     [[maybe_unused]] bf16x8 sh[HILO ? DK / 32 : 1], sl[HILO ? DK / 32 : 1];
+    [[maybe_unused]] bf16x8 nh[2], nl[2];
     if constexpr (HILO) {
 #pragma unroll
         for (int ks = 0; ks < DK / 32; ++ks) {
             const float f[8] = {sb[2 * ks][0], sb[2 * ks][1], sb[2 * ks][2], sb[2 * ks][3],
                                 sb[2 * ks + 1][0], sb[2 * ks + 1][1], sb[2 * ks + 1][2], sb[2 * ks + 1][3]};
             split_bf16x8(f, sh[ks], sl[ks]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const float f[8] = {nb[2 * u][0], nb[2 * u][1], nb[2 * u][2], nb[2 * u][3],
+                                nb[2 * u + 1][0], nb[2 * u + 1][1], nb[2 * u + 1][2], nb[2 * u + 1][3]};
+            split_bf16x8(f, nh[u], nl[u]);
         }
     }
 #pragma unroll
@@ -819,15 +892,32 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
                     x = __builtin_amdgcn_mfma_f32_16x16x4f32(Qt[16 * b + 4 * lk + k4][16 * tt + lr], sb[b][k4], x, 0, 0, 0);
             }
         }
+        if constexpr (HILO) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (t > tt) break;
-            const float4 lv = *reinterpret_cast<const float4 *>(&Ls[16 * tt + lr][16 * t + 4 * lk]);
-            f32x4 &x = (t & 1) ? x1 : x0;
-            x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.x, nb[t][0], x, 0, 0, 0);
-            x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.y, nb[t][1], x, 0, 0, 0);
-            x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.z, nb[t][2], x, 0, 0, 0);
-            x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.w, nb[t][3], x, 0, 0, 0);
+            for (int u = 0; u < 2; ++u) {
+                if (2 * u > tt) break;
+                const float4 l0 = *reinterpret_cast<const float4 *>(&Ls[16 * tt + lr][32 * u + 4 * lk]);
+                const float4 l1 = 2 * u + 1 > tt ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                                 : *reinterpret_cast<const float4 *>(&Ls[16 * tt + lr][32 * u + 16 + 4 * lk]);
+                const float f[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+                bf16x8 ah, al;
+                split_bf16x8(f, ah, al);
+                f32x4 &x = u ? x1 : x0;
+                x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, nh[u], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, nl[u], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, nh[u], x, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                if (t > tt) break;
+                const float4 lv = *reinterpret_cast<const float4 *>(&Ls[16 * tt + lr][16 * t + 4 * lk]);
+                f32x4 &x = (t & 1) ? x1 : x0;
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.x, nb[t][0], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.y, nb[t][1], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.z, nb[t][2], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(lv.w, nb[t][3], x, 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
