@@ -78,14 +78,27 @@ constexpr float kSplitSpan = 40.f;
 // G: inclusive cumulative sums over a chunk's tokens, one wave per key dim
 // (lane = token), for the tile Gt[DK][KP] of the chunk's gates. Sets *wide
 // when some token's G leaves its 16-token block's first value by more than
-// kSplitSpan (the writes race benignly: all store 1).
+// kSplitSpan, and *far when some token's G leaves the chunk's middle value
+// G[KC / 2] by more (the writes race benignly: all store 1). Wave w takes
+// key dims w, w + NT / 64, ...: all its columns are read first, so that
+// their independent scans interleave.
 template <int DK, int NT>
-__device__ __forceinline__ void gate_prefix(float (*Gt)[KP], int w, int l, int *wide) {
-    for (int d = w; d < DK; d += NT / 64) {
-        const float x = wave_prefix_sum(Gt[d][l]);
-        Gt[d][l] = x;
-        if (fabsf(x - __shfl(x, l & 48, 64)) > kSplitSpan) *wide = 1;
+__device__ __forceinline__ void gate_prefix(float (*Gt)[KP], int w, int l, int *wide, int *far) {
+    constexpr int NW = NT / 64, ND = DK / NW;
+    float x[ND];
+#pragma unroll
+    for (int i = 0; i < ND; ++i) x[i] = Gt[w + NW * i][l];
+    bool big = false, span = false;
+#pragma unroll
+    for (int i = 0; i < ND; ++i) {
+        x[i] = wave_prefix_sum(x[i]);
+        big |= fabsf(x[i] - __shfl(x[i], l & 48, 64)) > kSplitSpan;
+        span |= fabsf(x[i] - lane_value(x[i], KC / 2)) > kSplitSpan;
     }
+#pragma unroll
+    for (int i = 0; i < ND; ++i) Gt[w + NW * i][l] = x[i];
+    if (big) *wide = 1;
+    if (span) *far = 1;
 }
 
 // Per chunk and head workspace tile, in floats: W, then K * exp(G_last - G),
@@ -142,20 +155,106 @@ __device__ __forceinline__ int brow_off(int r, int c) {
 // acc[r] (16 x 16 x 32 MFMA: both operands name row lc of their block and
 // k = 32 ks + 8 g .. + 7; the result is C[4 g + r][lc], C = B-block x A-block).
 template <int DK>
-__device__ __forceinline__ f32x4 block_product(const char *hi, const char *lo, int ra0, int rb0,
-                                               int l) {
+__device__ __forceinline__ f32x4 block_product(const char *ahi, const char *alo, int ra0, const char *bhi,
+                                               const char *blo, int rb0, int l) {
     const int lc = l & 15, g = l >> 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) {
         const int oa = brow_off<DK>(16 * ra0 + lc, 4 * ks + g), ob = brow_off<DK>(16 * rb0 + lc, 4 * ks + g);
-        const bf16x8 ah = lds_ld<bf16x8>(hi, oa), al = lds_ld<bf16x8>(lo, oa);
-        const bf16x8 bh = lds_ld<bf16x8>(hi, ob), bl = lds_ld<bf16x8>(lo, ob);
+        const bf16x8 ah = lds_ld<bf16x8>(ahi, oa), al = lds_ld<bf16x8>(alo, oa);
+        const bf16x8 bh = lds_ld<bf16x8>(bhi, ob), bl = lds_ld<bf16x8>(blo, ob);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, ah, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh, al, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl, ah, acc, 0, 0, 0);
     }
     return acc;
+}
+// Both blocks from one tile pair.
+template <int DK>
+__device__ __forceinline__ f32x4 block_product(const char *hi, const char *lo, int ra0, int rb0, int l) {
+    return block_product<DK>(hi, lo, ra0, hi, lo, rb0, l);
+}
+
+// Two floats as bf16 high parts (truncated) and low parts (the rounded
+// remainders), each pair packed into one word, element 0 in the low half.
+__device__ __forceinline__ void hilo2(const float *x, uint32_t &hi, uint32_t &lo) {
+    const uint32_t u0 = __float_as_uint(x[0]), u1 = __float_as_uint(x[1]);
+    hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+    lo = pack_f32(x[0] - __uint_as_float(u0 & 0xffff0000u), x[1] - __uint_as_float(u1 & 0xffff0000u));
+}
+
+// The value, opaque to the compiler: index math derived from it inside an
+// item loop is formed there, instead of being hoisted out of the loop and
+// spilled (the persistent kernels keep the next item's rows and operand
+// images live across their loops).
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// fp32 tiles of rows of DK values: 16-byte chunk c of row r sits at chunk
+// c ^ (r mod 16), so the 16 rows one operand read touches fall in different
+// banks.
+template <int DK>
+__device__ __forceinline__ int frow_off(int r, int c) {
+    return r * (DK * 4) + ((c ^ (r & 15)) << 4);
+}
+
+// NR rows of decayed queries or keys for the pairwise products. For bf16
+// inputs (HL) a bf16 high tile and, NR * DK * 2 bytes on, a low tile, whose
+// products (block_product) keep about 2^-16 of each term; for fp32 inputs
+// one fp32 tile, whose products run on fp32 16 x 16 x 4 MFMAs and round only
+// in the accumulation. In the bf16 tiles 16-byte chunk c = 4 ks + kk of a
+// row holds the values 32 ks + 4 kk .. +3 and 32 ks + 16 + 4 kk .. +3: the
+// k order in which a lane of the start-state image holds its blocks 2 ks and
+// 2 ks + 1, so that a tile of queries is also the A operand of (Q exp G) S_in
+// (and every product of two tiles sums over the same k).
+template <int DK, bool HL, int NR>
+struct DecayTile {
+    static constexpr int BYTES = HL ? 2 * NR * DK * 2 : NR * DK * 4;
+    char *t;
+    // Values d and d + 1 (d even) of row r.
+    __device__ __forceinline__ void put2(int r, int d, const float *x) const {
+        if constexpr (HL) {
+            uint32_t hi, lo;
+            hilo2(x, hi, lo);
+            const int c = 4 * (d >> 5) + ((d >> 2) & 3), e = 4 * ((d >> 4) & 1) + (d & 3);
+            const int off = brow_off<DK>(r, c) + 2 * e;
+            *reinterpret_cast<uint32_t *>(t + off) = hi;
+            *reinterpret_cast<uint32_t *>(t + NR * DK * 2 + off) = lo;
+        } else {
+            *reinterpret_cast<float2 *>(t + frow_off<DK>(r, d >> 2) + 4 * (d & 3)) = make_float2(x[0], x[1]);
+        }
+    }
+};
+
+// The 16 x 16 block P[16 ra0 + i][16 rb0 + j] = sum_d A[16 ra0 + i][d]
+// B[16 rb0 + j][d] on one wave: lane (g, lc) gets P[16 ra0 + lc][16 rb0 +
+// 4 g + r] in acc[r]. For fp32 tiles the k order of MFMA k4 of 16-value
+// step j is 16 j + 4 g + k4 for lane group g (one float4 per operand and
+// step); lane 16 g + lc supplies key row lc as A and query row lc as B, and
+// receives D[4 g + r][lc].
+template <int DK, bool HL, int NA, int NB>
+__device__ __forceinline__ f32x4 tile_block(const DecayTile<DK, HL, NA> &A, int ra0, const DecayTile<DK, HL, NB> &B,
+                                            int rb0, int l) {
+    if constexpr (HL) {
+        return block_product<DK>(A.t, A.t + NA * DK * 2, ra0, B.t, B.t + NB * DK * 2, rb0, l);
+    } else {
+        const int lc = l & 15, g = l >> 4;
+        f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < DK / 16; ++j) {
+            const float4 a = lds_ld<float4>(A.t, frow_off<DK>(16 * ra0 + lc, 4 * j + g));
+            const float4 b = lds_ld<float4>(B.t, frow_off<DK>(16 * rb0 + lc, 4 * j + g));
+            f32x4 &x = (j & 1) ? x1 : x0;
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(b.x, a.x, x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(b.y, a.y, x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(b.z, a.z, x, 0, 0, 0);
+            x = __builtin_amdgcn_mfma_f32_16x16x4f32(b.w, a.w, x, 0, 0, 0);
+        }
+        return x0 + x1;
+    }
 }
 
 // A chunk's rows of a [tokens, H, W] tensor, held in registers as raw
@@ -247,11 +346,12 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     // later the blocks of T (14 blocks of 16 rows x 20 floats).
     constexpr int XT = 2 * XR * DK * 2, XTB = 14 * 16 * 20 * 4;
     __shared__ __attribute__((aligned(16))) char Xb[XT > XTB ? XT : XTB];
-    char *const Xh = Xb;
-    char *const Xl = Xb + XR * DK * 2;
+    constexpr bool HL = sizeof(Tin) == 2;
+    const DecayTile<DK, HL, XR> X{Xb};
+    static_assert(X.BYTES <= (int)sizeof(Xb), "the decayed rows fit their space");
     __shared__ float bs[KC];
-    __shared__ int wide;  // some diagonal block's gates span more than kSplitSpan
-    static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xb) + sizeof(bs) + sizeof(wide) <=
+    __shared__ int wide, far;  // gate spans past kSplitSpan (gate_prefix)
+    static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xb) + sizeof(bs) + 2 * sizeof(int) <=
                       kLdsPerCU,
                   "the workgroup must fit one CU's LDS");
     const int H = p.c.H;
@@ -293,7 +393,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
         continue;
     }
     const int s = it.s, h = it.h;
-    if (tid == 0) wide = 0;   // the last item read it before its final barrier
+    if (tid == 0) wide = far = 0;  // the last item read them before its final barrier
     bs[tid & (KC - 1)] = rb;  // eight threads per token write the same value
     rk.template store<true, KP>(&Kt[0][0], tid);
     rg.template store<true, KP>(&Gt[0][0], tid);
@@ -304,7 +404,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
         const int a = i / DV, j = i - a * DV;
         Vs[a][j] *= bs[a];
     }
-    gate_prefix<DK, NT>(Gt, w, l, &wide);
+    gate_prefix<DK, NT>(Gt, w, l, &wide, &far);
     __syncthreads();
 
     // A inside the diagonal 16 x 16 blocks (a > b): split at the block's
@@ -323,11 +423,11 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
         }
     }
     // A by block row I: tokens b < c = 16 I, and with the split block I's own
-    // tokens, against block I's, split at c. The decayed keys go to bf16
-    // hi/lo tiles: rows below c hold K exp(G_c - G) (keys b = row), rows
-    // c .. c + 15 K exp(G - G_c) (block I as a), rows c + 16 .. c + 31 K
-    // exp(G_c - G) (block I as b = row - 16); one wave per 16 x 16 block on
-    // the matrix cores.
+    // tokens, against block I's, split at c. The decayed keys go to the rows
+    // of X: rows below c hold K exp(G_c - G) (keys b = row), rows c .. c + 15
+    // K exp(G - G_c) (block I as a), rows c + 16 .. c + 31 K exp(G_c - G)
+    // (block I as b = row - 16); one wave per 16 x 16 block on the matrix
+    // cores.
     for (int I = split ? 0 : 1; I < 4; ++I) {
         const int c = 16 * I, nr = c + (split ? 32 : 16);
         __syncthreads();  // the previous block row's products are done with the tiles
@@ -341,22 +441,18 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
                 const float ex = qry ? Gt[d + e][t] - Gt[d + e][c] : Gt[d + e][c] - Gt[d + e][t];
                 x[e] = Kt[d + e][t] * __expf(ex);
             }
-            const uint32_t u0 = __float_as_uint(x[0]), u1 = __float_as_uint(x[1]);
-            const int off = brow_off<DK>(a, d >> 3) + 2 * (d & 7);
-            *reinterpret_cast<uint32_t *>(Xh + off) = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-            *reinterpret_cast<uint32_t *>(Xl + off) =
-                pack_f32(x[0] - __uint_as_float(u0 & 0xffff0000u), x[1] - __uint_as_float(u1 & 0xffff0000u));
+            X.put2(a, d, x);
         }
         __syncthreads();
         const int lc = l & 15, g4 = 4 * (l >> 4), a = c + lc;
         if (w < I) {
-            const f32x4 acc = block_product<DK>(Xh, Xl, I, w, l);
+            const f32x4 acc = tile_block(X, I, X, w, l);
             const float ba = bs[a];
             *reinterpret_cast<float4 *>(&Ms[a][16 * w + g4]) =
                 make_float4(ba * acc[0], ba * acc[1], ba * acc[2], ba * acc[3]);
         } else if (split && w == I) {
             // Keys b = c + g4 + r of the block itself; A keeps b < a.
-            const f32x4 acc = block_product<DK>(Xh, Xl, I, I + 1, l);
+            const f32x4 acc = tile_block(X, I, X, I + 1, l);
             const float ba = bs[a];
             *reinterpret_cast<float4 *>(&Ms[a][c + g4]) =
                 make_float4(g4 < lc ? ba * acc[0] : 0.f, g4 + 1 < lc ? ba * acc[1] : 0.f,
@@ -694,16 +790,22 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
     constexpr int NCB = DV / 16;       // column blocks
     constexpr int TPW = NCB / 2;       // token blocks per wave
     constexpr int LP = KC + 4;         // row stride of L: 16-byte aligned rows
-    __shared__ float Qt[DK][KP];       // Q^T, then (Q * exp(G))^T
+    __shared__ __attribute__((aligned(16))) float Qt[DK][KP];  // Q^T; then decayed keys (one reference)
     __shared__ float Kt[DK][KP];
     __shared__ float Gt[DK][KP];
     __shared__ __attribute__((aligned(16))) float Ls[KC][LP];
-    __shared__ __attribute__((aligned(16))) char Xb[2 * XR * DK * 2];  // bf16 hi and lo tiles
-    __shared__ int wide;  // some diagonal block's gates span more than kSplitSpan
-    static_assert(sizeof(Qt) + sizeof(Kt) + sizeof(Gt) + sizeof(Ls) + sizeof(Xb) + sizeof(wide) <= kLdsPerCU,
+    __shared__ __attribute__((aligned(16))) char Xb[2 * XR * DK * 2];  // decayed rows
+    __shared__ __attribute__((aligned(16))) float eR[DK];  // exp(G_r) or 1 (below)
+    __shared__ int wide, far;  // gate spans past kSplitSpan (gate_prefix)
+    static_assert(sizeof(Qt) + sizeof(Kt) + sizeof(Gt) + sizeof(Ls) + sizeof(Xb) + sizeof(eR) + 2 * sizeof(int) <=
+                      kLdsPerCU,
                   "the workgroup must fit one CU's LDS");
-    char *const Xh = Xb;
-    char *const Xl = Xb + XR * DK * 2;
+    constexpr bool HILO = sizeof(Tin) == 2;
+    // The A operands of (Q exp G) S_in: queries decayed to a reference token
+    // r (G_r = 0 without one), tokens in rows.
+    const DecayTile<DK, HILO, KC> Xq{Xb};
+    static_assert(DecayTile<DK, HILO, XR>::BYTES <= (int)sizeof(Xb), "the decayed rows fit their space");
+    static_assert(Xq.BYTES <= (int)sizeof(Qt), "the decayed keys fit in the space of Q^T");
 
     const int H = p.c.H;
     const int tid = threadIdx.x;
@@ -747,112 +849,147 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
         continue;
     }
     const int h = it.h, n = it.n;
-    if (tid == 0) wide = 0;  // the last item read it before its final barrier
+    if (tid == 0) wide = far = 0;  // the last item read them before its final barrier
     rq.template store<true, KP>(&Qt[0][0], tid);
     rk.template store<true, KP>(&Kt[0][0], tid);
     rg.template store<true, KP>(&Gt[0][0], tid);
     fetch_rows(next);
     __syncthreads();
-    gate_prefix<DK, NT>(Gt, w, l, &wide);
+    gate_prefix<DK, NT>(Gt, w, l, &wide, &far);
     __syncthreads();
+    const int tix = opaque(tid);
 
-    // L inside the diagonal blocks: split at the block's first token with
-    // the blocks below (when the gates allow), else here, one pair (a > b)
-    // per thread with its exponent taken directly, the diagonal itself (no
-    // decay) on the rest, zeros above it.
-    const bool split = __builtin_amdgcn_readfirstlane(wide) == 0;
-    if (!split) {
-        if (tid < 4 * 120) {
-            const int blk = tid / 120, r = tid - blk * 120;
-            int ai = 1;
-            while ((ai + 1) * ai / 2 <= r) ++ai;
-            const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai - 1) / 2);
-            float acc = 0.f;
-            for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
-            Ls[a][b] = acc;
-            Ls[b][a] = 0.f;
-        } else {
-            for (int a = tid - 4 * 120; a < KC; a += NT - 4 * 120) {
-                float acc = 0.f;
-                for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a], Kt[d][a], acc);
-                Ls[a][a] = acc;
-            }
-        }
-    }
-    // L by block row I: tokens b < c = 16 I, and with the split block I's own
-    // tokens, against block I's queries, as bf16 hi/lo tiles: rows below c
-    // hold K exp(G_c - G) (keys b = row), rows c .. c + 15 Q exp(G - G_c)
-    // (queries), rows c + 16 .. c + 31 K exp(G_c - G) (keys b = row - 16).
-    for (int I = split ? 0 : 1; I < 4; ++I) {
-        const int c = 16 * I, nr = c + (split ? 32 : 16);
-        __syncthreads();  // the previous block row's products are done with the tiles
-        for (int i = tid; i < nr * DK / 2; i += NT) {
-            const int a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
-            const bool qry = a >= c && a < c + 16;
-            const int t = a < c + 16 ? a : a - 16;
-            const float *src = qry ? &Qt[0][0] : &Kt[0][0];
+    // L from one reference token r = KC / 2 for the whole chunk, when every
+    // |G[t][d] - G[r][d]| stays within kSplitSpan: queries Q exp(G - G_r) in
+    // Xq (which (Q exp G) S_in then takes as its A operand, with exp(G_r)
+    // moved into the start state's rows), keys K exp(G_r - G) in the space of
+    // Q^T once every wave is done with it, and the 10 blocks on or below the
+    // diagonal in one pass, wave w taking blocks w and w + 8 (block
+    // I (I + 1) / 2 + J is (I, J)). Each thread forms the dim pair d of rows
+    // w, w + 8, ... (d = 2 (tid mod DK / 2) for DK = 128).
+    const bool one_ref = __builtin_amdgcn_readfirstlane(far) == 0;
+    if (one_ref) {
+        constexpr int RP = KC * DK / 2 / NT;  // dim pairs of each row kind per thread
+        constexpr int R = KC / 2;
+        const DecayTile<DK, HILO, KC> Xk{reinterpret_cast<char *>(&Qt[0][0])};
+#pragma unroll
+        for (int m = 0; m < RP; ++m) {
+            const int i = m * NT + tix, a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
             float x[2];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float ex = qry ? Gt[d + e][t] - Gt[d + e][c] : Gt[d + e][c] - Gt[d + e][t];
-                x[e] = src[(d + e) * KP + t] * __expf(ex);
-            }
-            const uint32_t u0 = __float_as_uint(x[0]), u1 = __float_as_uint(x[1]);
-            const int off = brow_off<DK>(a, d >> 3) + 2 * (d & 7);
-            *reinterpret_cast<uint32_t *>(Xh + off) = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-            *reinterpret_cast<uint32_t *>(Xl + off) =
-                pack_f32(x[0] - __uint_as_float(u0 & 0xffff0000u), x[1] - __uint_as_float(u1 & 0xffff0000u));
+            for (int e = 0; e < 2; ++e) x[e] = Qt[d + e][a] * __expf(Gt[d + e][a] - Gt[d + e][R]);
+            Xq.put2(a, d, x);
+        }
+        if (tix < DK) eR[tix] = __expf(Gt[tix][R]);
+        __syncthreads();  // every wave is done reading Q^T
+#pragma unroll
+        for (int m = 0; m < RP; ++m) {
+            const int i = m * NT + tix, a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
+            float x[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) x[e] = Kt[d + e][a] * __expf(Gt[d + e][R] - Gt[d + e][a]);
+            Xk.put2(a, d, x);
         }
         __syncthreads();
-        if (w < I) {
-            const f32x4 acc = block_product<DK>(Xh, Xl, I, w, l);
-            *reinterpret_cast<float4 *>(&Ls[c + lr][16 * w + 4 * lk]) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        } else if (split && w == I) {
-            // Keys b = c + 4 lk + v of the block itself; L keeps b <= a = c + lr.
-            const f32x4 acc = block_product<DK>(Xh, Xl, I, I + 1, l);
+        for (int bi = w; bi < 10; bi += NT / 64) {
+            const int I = bi < 1 ? 0 : bi < 3 ? 1 : bi < 6 ? 2 : 3, J = bi - I * (I + 1) / 2;
+            const f32x4 acc = tile_block(Xq, I, Xk, J, l);
+            // On the diagonal L keeps b = 16 J + 4 lk + v <= a = 16 I + lr.
             const int b0 = 4 * lk;
-            *reinterpret_cast<float4 *>(&Ls[c + lr][c + b0]) =
-                make_float4(b0 <= lr ? acc[0] : 0.f, b0 + 1 <= lr ? acc[1] : 0.f, b0 + 2 <= lr ? acc[2] : 0.f,
-                            b0 + 3 <= lr ? acc[3] : 0.f);
-        }
-    }
-    // Q * exp(G): for fp32 inputs in place, for the fp32 products below; for
-    // bf16 inputs as bf16 hi/lo tiles in the space of the L tiles (free once
-    // the last block row's products are done), laid out as the A operands of
-    // 16 x 16 x 32 MFMAs: 16-byte chunk c = 4 ks + kk of token row a holds
-    // the key dims 32 ks + 4 kk .. +3 and 32 ks + 16 + 4 kk .. +3, the k
-    // order in which a lane of the start-state image holds its two blocks.
-    constexpr bool HILO = sizeof(Tin) == 2;
-    if constexpr (HILO) {
-        __syncthreads();
-        for (int i = tid; i < KC * DK / 2; i += NT) {
-            const int a = i & (KC - 1), pr = i >> 6;  // token a; dim pair pr of its row
-            const int c = pr >> 2, jp = pr & 3;       // chunk c = 4 ks + kk; pair jp in it
-            const int d = 32 * (c >> 2) + (jp >= 2 ? 16 : 0) + 4 * (c & 3) + 2 * (jp & 1);
-            const float x0 = Qt[d][a] * __expf(Gt[d][a]), x1 = Qt[d + 1][a] * __expf(Gt[d + 1][a]);
-            const uint32_t u0 = __float_as_uint(x0), u1 = __float_as_uint(x1);
-            const int off = brow_off<DK>(a, c) + 4 * jp;
-            *reinterpret_cast<uint32_t *>(Xh + off) = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-            *reinterpret_cast<uint32_t *>(Xl + off) =
-                pack_f32(x0 - __uint_as_float(u0 & 0xffff0000u), x1 - __uint_as_float(u1 & 0xffff0000u));
+            const bool dg = I == J;
+            *reinterpret_cast<float4 *>(&Ls[16 * I + lr][16 * J + b0]) =
+                make_float4(!dg || b0 <= lr ? acc[0] : 0.f, !dg || b0 + 1 <= lr ? acc[1] : 0.f,
+                            !dg || b0 + 2 <= lr ? acc[2] : 0.f, !dg || b0 + 3 <= lr ? acc[3] : 0.f);
         }
     } else {
-        for (int i = tid; i < KC * DK; i += NT) {
-            const int d = i / KC, a = i - d * KC;
-            Qt[d][a] *= __expf(Gt[d][a]);
+        // L inside the diagonal blocks: split at the block's first token with
+        // the blocks below (when the gates allow), else here, one pair (a > b)
+        // per thread with its exponent taken directly, the diagonal itself (no
+        // decay) on the rest, zeros above it.
+        const bool split = __builtin_amdgcn_readfirstlane(wide) == 0;
+        if (!split) {
+            if (tid < 4 * 120) {
+                const int blk = tid / 120, r = tid - blk * 120;
+                int ai = 1;
+                while ((ai + 1) * ai / 2 <= r) ++ai;
+                const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai - 1) / 2);
+                float acc = 0.f;
+                for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
+                Ls[a][b] = acc;
+                Ls[b][a] = 0.f;
+            } else {
+                for (int a = tid - 4 * 120; a < KC; a += NT - 4 * 120) {
+                    float acc = 0.f;
+                    for (int d = 0; d < DK; ++d) acc = fmaf(Qt[d][a], Kt[d][a], acc);
+                    Ls[a][a] = acc;
+                }
+            }
         }
+        // L by block row I: tokens b < c = 16 I, and with the split block I's own
+        // tokens, against block I's queries, in the rows of X: rows below c
+        // hold K exp(G_c - G) (keys b = row), rows c .. c + 15 Q exp(G - G_c)
+        // (queries), rows c + 16 .. c + 31 K exp(G_c - G) (keys b = row - 16).
+        const DecayTile<DK, HILO, XR> X{Xb};
+        for (int I = split ? 0 : 1; I < 4; ++I) {
+            const int c = 16 * I, nr = c + (split ? 32 : 16);
+            __syncthreads();  // the previous block row's products are done with the tiles
+            for (int i = tix; i < nr * DK / 2; i += NT) {
+                const int a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
+                const bool qry = a >= c && a < c + 16;
+                const int t = a < c + 16 ? a : a - 16;
+                const float *src = qry ? &Qt[0][0] : &Kt[0][0];
+                float x[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float ex = qry ? Gt[d + e][t] - Gt[d + e][c] : Gt[d + e][c] - Gt[d + e][t];
+                    x[e] = src[(d + e) * KP + t] * __expf(ex);
+                }
+                X.put2(a, d, x);
+            }
+            __syncthreads();
+            if (w < I) {
+                const f32x4 acc = tile_block(X, I, X, w, l);
+                *reinterpret_cast<float4 *>(&Ls[c + lr][16 * w + 4 * lk]) =
+                    make_float4(acc[0], acc[1], acc[2], acc[3]);
+            } else if (split && w == I) {
+                // Keys b = c + 4 lk + v of the block itself; L keeps b <= a = c + lr.
+                const f32x4 acc = tile_block(X, I, X, I + 1, l);
+                const int b0 = 4 * lk;
+                *reinterpret_cast<float4 *>(&Ls[c + lr][c + b0]) =
+                    make_float4(b0 <= lr ? acc[0] : 0.f, b0 + 1 <= lr ? acc[1] : 0.f, b0 + 2 <= lr ? acc[2] : 0.f,
+                                b0 + 3 <= lr ? acc[3] : 0.f);
+            }
+        }
+        // Q * exp(G) (no reference token) in the space of the decayed rows,
+        // free once the last block row's products are done.
+        __syncthreads();
+        for (int i = tix; i < KC * DK / 2; i += NT) {
+            const int a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
+            const float x[2] = {Qt[d][a] * __expf(Gt[d][a]), Qt[d + 1][a] * __expf(Gt[d + 1][a])};
+            Xq.put2(a, d, x);
+        }
+        if (tix < DK) eR[tix] = 1.f;
     }
     __syncthreads();
 
-    // O blocks (tt, cb): (Q exp G) S_in, then L new_v. For bf16 inputs both
-    // run on 16 x 16 x 32 MFMAs as bf16 hi/lo (hi hi + hi lo + lo hi, about
-    // 2^-16 of each term): the first takes the start-state blocks 2 ks and
-    // 2 ks + 1 of each lane as one 8-value k slice, the second the new_v
-    // blocks 2 u and 2 u + 1 likewise, against L[16 tt + r][32 u + 4 kk .. +3]
-    // and L[16 tt + r][32 u + 16 + 4 kk .. +3] (zeros past block tt). For
-    // fp32 inputs they are fp32 16 x 16 x 4 MFMAs, A = (Q exp G)[16 tt + r]
-    // [16 b + 4 kk + k4] and L[16 tt + r][16 t + 4 kk + k4]. All leave
-    // O[16 tt + 4 kk + v][16 cb + r] in element v.
+    // O blocks (tt, cb): (Q exp(G - G_r)) (diag(exp(G_r)) S_in), then L new_v.
+    // For bf16 inputs both run on 16 x 16 x 32 MFMAs as bf16 hi/lo (hi hi +
+    // hi lo + lo hi, about 2^-16 of each term): the first takes the
+    // start-state blocks 2 ks and 2 ks + 1 of each lane as one 8-value k
+    // slice (Xq's k order), the second the new_v blocks 2 u and 2 u + 1
+    // likewise, against L[16 tt + r][32 u + 4 kk .. +3] and L[16 tt + r]
+    // [32 u + 16 + 4 kk .. +3] (zeros past block tt). For fp32 inputs they are
+    // fp32 16 x 16 x 4 MFMAs, A = Xq[16 tt + r][16 b + 4 kk + k4] and
+    // L[16 tt + r][16 t + 4 kk + k4]. All leave O[16 tt + 4 kk + v][16 cb + r]
+    // in element v.
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const float4 e = *reinterpret_cast<const float4 *>(&eR[16 * b + 4 * lk]);
+        sb[b][0] *= e.x;
+        sb[b][1] *= e.y;
+        sb[b][2] *= e.z;
+        sb[b][3] *= e.w;
+    }
     [[maybe_unused]] bf16x8 sh[HILO ? DK / 32 : 1], sl[HILO ? DK / 32 : 1];
     [[maybe_unused]] bf16x8 nh[2], nl[2];
     if constexpr (HILO) {
@@ -878,7 +1015,7 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
             for (int ks = 0; ks < DK / 32; ++ks) {
                 f32x4 &x = (ks & 1) ? x1 : x0;
                 const int off = brow_off<DK>(16 * tt + lr, 4 * ks + lk);
-                const bf16x8 ah = lds_ld<bf16x8>(Xh, off), al = lds_ld<bf16x8>(Xl, off);
+                const bf16x8 ah = lds_ld<bf16x8>(Xq.t, off), al = lds_ld<bf16x8>(Xq.t + KC * DK * 2, off);
                 x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sh[ks], x, 0, 0, 0);
                 x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sl[ks], x, 0, 0, 0);
                 x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, sh[ks], x, 0, 0, 0);
@@ -887,9 +1024,11 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
                 f32x4 &x = (b & 1) ? x1 : x0;
-#pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4)
-                    x = __builtin_amdgcn_mfma_f32_16x16x4f32(Qt[16 * b + 4 * lk + k4][16 * tt + lr], sb[b][k4], x, 0, 0, 0);
+                const float4 av = lds_ld<float4>(Xq.t, frow_off<DK>(16 * tt + lr, 4 * b + lk));
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, sb[b][0], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, sb[b][1], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, sb[b][2], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, sb[b][3], x, 0, 0, 0);
             }
         }
         if constexpr (HILO) {
@@ -897,8 +1036,9 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
             for (int u = 0; u < 2; ++u) {
                 if (2 * u > tt) break;
                 const float4 l0 = *reinterpret_cast<const float4 *>(&Ls[16 * tt + lr][32 * u + 4 * lk]);
-                const float4 l1 = 2 * u + 1 > tt ? make_float4(0.f, 0.f, 0.f, 0.f)
-                                                 : *reinterpret_cast<const float4 *>(&Ls[16 * tt + lr][32 * u + 16 + 4 * lk]);
+                const float4 l1 = 2 * u + 1 > tt
+                                      ? make_float4(0.f, 0.f, 0.f, 0.f)
+                                      : *reinterpret_cast<const float4 *>(&Ls[16 * tt + lr][32 * u + 16 + 4 * lk]);
                 const float f[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
                 bf16x8 ah, al;
                 split_bf16x8(f, ah, al);

@@ -169,6 +169,37 @@ def test_kda_chunk_per_dim_rates(dtype):
     compare_chunk(inp, o, S, dtype, "kda per-dim rates")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_kda_chunk_gate_regimes(dtype):
+    """Chunks whose gates put them on each way of forming the pairwise decay
+    factors: within +-40 of the chunk's middle gate sum (one reference for
+    the chunk), within 40 inside each 16-token block but not of the middle
+    (one reference per block row), and wider inside a block (exponents pair
+    by pair); the last chunk is ragged. Per-token gates per chunk of 64:
+    -0.02 (1 +- 0.5), -1.5 (1 +- 0.125), -8 (1 +- 0.5), -0.02 (1 +- 0.5)."""
+    say("kda_chunk_fwd gate regimes", dtype)
+    B, T, H, D = 2, 250, 2, 128
+    inp = W.make_prefill(B, T, H, D, D, dtype, "kda", seed=41, device="cuda", init="normal",
+                         with_beta=True)
+    gen = torch.Generator(device="cuda").manual_seed(41)
+    u = torch.rand((B, T, H, D), generator=gen, device="cuda") - 0.5
+    rate = torch.tensor([0.02, 1.5, 8.0, 0.02], dtype=torch.float32, device="cuda")
+    spread = torch.tensor([1.0, 0.25, 1.0, 1.0], dtype=torch.float32, device="cuda")
+    ch = torch.arange(T, device="cuda") // 64
+    r = rate[ch].view(1, T, 1, 1)
+    sp = spread[ch].view(1, T, 1, 1)
+    inp["g"] = (-r * (1.0 + sp * u)).contiguous()
+    o, S = run_chunk(inp)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    compare_chunk(inp, o, S, dtype, "kda gate regimes")
+    # Each chunk's output on its own, so that one regime cannot hide behind
+    # the others' magnitudes.
+    ro, _ = oracle_kda(inp)
+    for c in range(4):
+        sl = slice(64 * c, min(T, 64 * c + 64))
+        check(host(o)[:, sl], ro[:, sl], dtype, "kda gate regimes chunk %d" % c)
+
+
 def test_kda_chunk_split_chain_and_step():
     """Splitting a sequence and chaining the final state gives the same
     result, and decode steps continue a prefill."""
