@@ -282,6 +282,19 @@ struct Rows {
             r[m] = buf_ld16(rs, (uint32_t)((a * H * W + pc * PE) * (int)sizeof(Tin)));
         }
     }
+    // As store<false, STRIDE>, row a multiplied by scale[a] (one rounding).
+    template <int STRIDE>
+    __device__ __forceinline__ void store_scaled(float *tile, int tid, const float *scale) const {
+#pragma unroll
+        for (int m = 0; m < PT; ++m) {
+            const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
+            float f[PE];
+            load_piece<Tin>(make_uint4(r[m][0], r[m][1], r[m][2], r[m][3]), f);
+            const float sa = scale[a];
+#pragma unroll
+            for (int e = 0; e < PE; ++e) tile[a * STRIDE + pc * PE + e] = f[e] * sa;
+        }
+    }
     template <bool TR, int STRIDE>
     __device__ __forceinline__ void store(float *tile, int tid) const {
 #pragma unroll
@@ -340,7 +353,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     constexpr int MP = KC + 4;         // row stride of A/T: 16-byte aligned rows
     __shared__ float Kt[DK][KP];       // K^T; later (diag(beta) K * exp(G))^T
     __shared__ float Gt[DK][KP];       // G^T
-    __shared__ float Vs[KC][DV + 1];   // diag(beta) V
+    // diag(beta) V, staged once A is formed (before, the space of decayed keys)
+    __shared__ __attribute__((aligned(16))) float Vs[KC][DV + 1];
     __shared__ __attribute__((aligned(16))) float Ms[KC][MP];  // A = diag(beta) M below the diagonal; then T
     // K decayed to a reference token, as bf16 high and low tiles of XR rows;
     // later the blocks of T (14 blocks of 16 rows x 20 floats).
@@ -349,6 +363,9 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     constexpr bool HL = sizeof(Tin) == 2;
     const DecayTile<DK, HL, XR> X{Xb};
     static_assert(X.BYTES <= (int)sizeof(Xb), "the decayed rows fit their space");
+    // One reference token per chunk needs a second tile of KC rows: the space
+    // of diag(beta) V, where it fits (not at Dk = 128 with Dv = 64).
+    constexpr bool kOneRef = DecayTile<DK, HL, KC>::BYTES <= (int)sizeof(Vs);
     __shared__ float bs[KC];
     __shared__ int wide, far;  // gate spans past kSplitSpan (gate_prefix)
     static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xb) + sizeof(bs) + 2 * sizeof(int) <=
@@ -365,15 +382,21 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     Rows<float, DK, NT> rg;
     Rows<Tin, DV, NT> rv;
     float rb = 0.f;
-    auto fetch = [&](int64_t item) {
+    // k, g and beta rows are staged at the item's top; v rows once A is
+    // formed, so their loads follow later.
+    auto fetch_kg = [&](int64_t item) {
         const Item it = item_at<TAB>(p, item, nitems);
         rk.load(kg, it.tok0, H, it.h, it.n, tid);
         rg.load(p.c.g, it.tok0, H, it.h, it.n, tid);
-        rv.load(vg, it.tok0, H, it.h, it.n, tid);
         rb = buf_ld_f32(buf_rsrc(p.beta + it.tok0 * H + it.h, it.n > 0 ? (it.n - 1) * H * 4 + 4 : 0),
                         (uint32_t)((tid & (KC - 1)) * H * 4));
     };
-    fetch(blockIdx.x);
+    auto fetch_v = [&](int64_t item) {
+        const Item it = item_at<TAB>(p, item, nitems);
+        rv.load(vg, it.tok0, H, it.h, it.n, tid);
+    };
+    fetch_kg(blockIdx.x);
+    fetch_v(blockIdx.x);
     // The first item's loads complete before the loop, so that the waits at
     // its top count only the next item's loads and the stores issued after
     // them (and never wait for the stores).
@@ -389,7 +412,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     // Without the table every item has a segment (len >= 0; T = 0 gives an
     // empty one whose tile the chain still reads).
     if (TAB && it.len < 0) {
-        fetch(item + gridDim.x);
+        fetch_kg(item + gridDim.x);
+        fetch_v(item + gridDim.x);
         continue;
     }
     const int s = it.s, h = it.h;
@@ -397,69 +421,107 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     bs[tid & (KC - 1)] = rb;  // eight threads per token write the same value
     rk.template store<true, KP>(&Kt[0][0], tid);
     rg.template store<true, KP>(&Gt[0][0], tid);
-    rv.template store<false, DV + 1>(&Vs[0][0], tid);
-    fetch(item + gridDim.x);
+    fetch_kg(item + gridDim.x);
     __syncthreads();
-    for (int i = tid; i < KC * DV; i += NT) {
-        const int a = i / DV, j = i - a * DV;
-        Vs[a][j] *= bs[a];
-    }
     gate_prefix<DK, NT>(Gt, w, l, &wide, &far);
     __syncthreads();
+    const int tix = opaque(tid);
 
-    // A inside the diagonal 16 x 16 blocks (a > b): split at the block's
-    // first token with the blocks below (when the gates allow), else here,
-    // one pair per thread with its exponent taken directly.
-    const bool split = __builtin_amdgcn_readfirstlane(wide) == 0;
-    if (!split) {
-        for (int i = tid; i < 4 * 120; i += NT) {
-            const int blk = i / 120, r = i - blk * 120;
-            int ai = 1;
-            while ((ai + 1) * ai / 2 <= r) ++ai;
-            const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai - 1) / 2);
-            float acc = 0.f;
-            for (int d = 0; d < DK; ++d) acc = fmaf(Kt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
-            Ms[a][b] = bs[a] * acc;
-        }
-    }
-    // A by block row I: tokens b < c = 16 I, and with the split block I's own
-    // tokens, against block I's, split at c. The decayed keys go to the rows
-    // of X: rows below c hold K exp(G_c - G) (keys b = row), rows c .. c + 15
-    // K exp(G - G_c) (block I as a), rows c + 16 .. c + 31 K exp(G_c - G)
-    // (block I as b = row - 16); one wave per 16 x 16 block on the matrix
-    // cores.
-    for (int I = split ? 0 : 1; I < 4; ++I) {
-        const int c = 16 * I, nr = c + (split ? 32 : 16);
-        __syncthreads();  // the previous block row's products are done with the tiles
-        for (int i = tid; i < nr * DK / 2; i += NT) {
-            const int a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
-            const bool qry = a >= c && a < c + 16;
-            const int t = a < c + 16 ? a : a - 16;
-            float x[2];
+    // A from one reference token r = KC / 2 for the whole chunk, when every
+    // |G[t][d] - G[r][d]| stays within kSplitSpan: K exp(G - G_r) (tokens as
+    // a) in Xb, K exp(G_r - G) (tokens as b) in the space of diag(beta) V,
+    // and the 10 blocks on or below the diagonal in one pass, wave w taking
+    // blocks w and w + 8 (block I (I + 1) / 2 + J is (I, J)).
+    bool one_ref = false;
+    if constexpr (kOneRef) one_ref = __builtin_amdgcn_readfirstlane(far) == 0;
+    if (one_ref) {
+        constexpr int RP = KC * DK / 2 / NT;  // dim pairs per thread
+        constexpr int R = KC / 2;
+        const DecayTile<DK, HL, KC> Xa{Xb}, Xc{reinterpret_cast<char *>(&Vs[0][0])};
+#pragma unroll
+        for (int m = 0; m < RP; ++m) {
+            const int i = m * NT + tix, a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
+            float xa[2], xc[2];
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                const float ex = qry ? Gt[d + e][t] - Gt[d + e][c] : Gt[d + e][c] - Gt[d + e][t];
-                x[e] = Kt[d + e][t] * __expf(ex);
+                const float kv = Kt[d + e][a], ex = Gt[d + e][a] - Gt[d + e][R];
+                xa[e] = kv * __expf(ex);
+                xc[e] = kv * __expf(-ex);
             }
-            X.put2(a, d, x);
+            Xa.put2(a, d, xa);
+            Xc.put2(a, d, xc);
         }
         __syncthreads();
-        const int lc = l & 15, g4 = 4 * (l >> 4), a = c + lc;
-        if (w < I) {
-            const f32x4 acc = tile_block(X, I, X, w, l);
+        for (int bi = w; bi < 10; bi += NT / 64) {
+            const int I = bi < 1 ? 0 : bi < 3 ? 1 : bi < 6 ? 2 : 3, J = bi - I * (I + 1) / 2;
+            const f32x4 acc = tile_block(Xa, I, Xc, J, l);
+            // On the diagonal A keeps b = 16 J + g4 + v < a = 16 I + lc.
+            const int lc = l & 15, g4 = 4 * (l >> 4), a = 16 * I + lc;
+            const bool dg = I == J;
             const float ba = bs[a];
-            *reinterpret_cast<float4 *>(&Ms[a][16 * w + g4]) =
-                make_float4(ba * acc[0], ba * acc[1], ba * acc[2], ba * acc[3]);
-        } else if (split && w == I) {
-            // Keys b = c + g4 + r of the block itself; A keeps b < a.
-            const f32x4 acc = tile_block(X, I, X, I + 1, l);
-            const float ba = bs[a];
-            *reinterpret_cast<float4 *>(&Ms[a][c + g4]) =
-                make_float4(g4 < lc ? ba * acc[0] : 0.f, g4 + 1 < lc ? ba * acc[1] : 0.f,
-                            g4 + 2 < lc ? ba * acc[2] : 0.f, g4 + 3 < lc ? ba * acc[3] : 0.f);
+            *reinterpret_cast<float4 *>(&Ms[a][16 * J + g4]) =
+                make_float4(!dg || g4 < lc ? ba * acc[0] : 0.f, !dg || g4 + 1 < lc ? ba * acc[1] : 0.f,
+                            !dg || g4 + 2 < lc ? ba * acc[2] : 0.f, !dg || g4 + 3 < lc ? ba * acc[3] : 0.f);
+        }
+    } else {
+        // A inside the diagonal 16 x 16 blocks (a > b): split at the block's
+        // first token with the blocks below (when the gates allow), else here,
+        // one pair per thread with its exponent taken directly.
+        const bool split = __builtin_amdgcn_readfirstlane(wide) == 0;
+        if (!split) {
+            for (int i = tix; i < 4 * 120; i += NT) {
+                const int blk = i / 120, r = i - blk * 120;
+                int ai = 1;
+                while ((ai + 1) * ai / 2 <= r) ++ai;
+                const int a = 16 * blk + ai, b = 16 * blk + (r - ai * (ai - 1) / 2);
+                float acc = 0.f;
+                for (int d = 0; d < DK; ++d) acc = fmaf(Kt[d][a] * Kt[d][b], __expf(Gt[d][a] - Gt[d][b]), acc);
+                Ms[a][b] = bs[a] * acc;
+            }
+        }
+        // A by block row I: tokens b < c = 16 I, and with the split block I's own
+        // tokens, against block I's, split at c. The decayed keys go to the rows
+        // of X: rows below c hold K exp(G_c - G) (keys b = row), rows c .. c + 15
+        // K exp(G - G_c) (block I as a), rows c + 16 .. c + 31 K exp(G_c - G)
+        // (block I as b = row - 16); one wave per 16 x 16 block on the matrix
+        // cores.
+        for (int I = split ? 0 : 1; I < 4; ++I) {
+            const int c = 16 * I, nr = c + (split ? 32 : 16);
+            __syncthreads();  // the previous block row's products are done with the tiles
+            for (int i = tix; i < nr * DK / 2; i += NT) {
+                const int a = i / (DK / 2), d = 2 * (i - a * (DK / 2));
+                const bool qry = a >= c && a < c + 16;
+                const int t = a < c + 16 ? a : a - 16;
+                float x[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float ex = qry ? Gt[d + e][t] - Gt[d + e][c] : Gt[d + e][c] - Gt[d + e][t];
+                    x[e] = Kt[d + e][t] * __expf(ex);
+                }
+                X.put2(a, d, x);
+            }
+            __syncthreads();
+            const int lc = l & 15, g4 = 4 * (l >> 4), a = c + lc;
+            if (w < I) {
+                const f32x4 acc = tile_block(X, I, X, w, l);
+                const float ba = bs[a];
+                *reinterpret_cast<float4 *>(&Ms[a][16 * w + g4]) =
+                    make_float4(ba * acc[0], ba * acc[1], ba * acc[2], ba * acc[3]);
+            } else if (split && w == I) {
+                // Keys b = c + g4 + r of the block itself; A keeps b < a.
+                const f32x4 acc = tile_block(X, I, X, I + 1, l);
+                const float ba = bs[a];
+                *reinterpret_cast<float4 *>(&Ms[a][c + g4]) =
+                    make_float4(g4 < lc ? ba * acc[0] : 0.f, g4 + 1 < lc ? ba * acc[1] : 0.f,
+                                g4 + 2 < lc ? ba * acc[2] : 0.f, g4 + 3 < lc ? ba * acc[3] : 0.f);
+            }
         }
     }
     __syncthreads();
+    // diag(beta) V, in the space of the decayed keys now that A is formed;
+    // then the next item's v rows.
+    rv.template store_scaled<DV + 1>(&Vs[0][0], tid, bs);
+    fetch_v(item + gridDim.x);
 
     float *tile = p.tiles + tile_index(p, s, h) * tile_floats(DK, DV);
     // T = (I + A)^-1 in 16 x 16 blocks, kept in the space of the bf16 tiles
