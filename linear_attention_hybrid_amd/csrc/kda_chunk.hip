@@ -32,11 +32,14 @@
 // the block's first token c, exp(G[a] - G[c]) exp(G[c] - G[b]), two factors
 // that each lie in (0, 1] when g <= 0, so every block pair costs one
 // exponential per element and token rather than per pair; the products run
-// on the matrix cores as bf16 high/low pairs. Inside block I the same split
-// gives a factor exp(G[c] - G[b]) >= 1 for its own keys b >= c, which is
-// safe while the gates of the block span little (kSplitSpan); the diagonal
-// blocks then run the same way, and a chunk where some block spans more
-// takes their pairwise factors directly instead. T is inverted in 16 x 16 blocks: each
+// on the matrix cores (bf16 high/low pairs for bf16 inputs, fp32 for fp32).
+// Inside block I the same split gives a factor exp(G[c] - G[b]) >= 1 for its
+// own keys b >= c, which is safe while the gates of the block span little
+// (kSplitSpan); the diagonal blocks then run the same way, and a chunk where
+// some block spans more takes their pairwise factors directly instead. When
+// the whole chunk's gates stay within kSplitSpan of its middle token r, one
+// split at r serves every pair: 64 decayed rows of each kind per chunk, and
+// all ten blocks on or below the diagonal in one pass. T is inverted in 16 x 16 blocks: each
 // diagonal block by back substitution on one wave, the blocks below it block
 // row by block row, T_IJ = -T_II sum_K A_IK T_KJ, on fp32 MFMAs.
 #include "mfma_tile.h"
@@ -345,8 +348,11 @@ __device__ __forceinline__ Item item_at(const KdaParams &p, int64_t item, int64_
 }
 
 // ---- prep: persistent over the (chunk, head) items, one workgroup per CU;
-// the next item's k, g, v rows and beta load into registers while the
-// current one is worked on.
+// the next item's k, g rows and beta load into registers while the current
+// one is worked on, and its v rows once the current A is formed. A comes from
+// decayed-key tiles on the matrix cores: split at the chunk's middle token
+// when its gates allow, else block row by block row (with the diagonal
+// blocks pair by pair when a block's gates span too far).
 template <typename Tin, int DK, int DV, bool TAB>
 __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nitems) {
     constexpr int NT = 512;
@@ -836,10 +842,10 @@ __global__ __launch_bounds__(CHAIN_NT) void kda_chain_kernel(KdaParams p) {
             }
 }
 
-// ---- output: one workgroup per (chunk, head). L inside the diagonal 16 x 16
-// blocks on the vector ALUs (exponents taken directly), below them as bf16
-// hi/lo products on the matrix cores (split at the block's first token);
-// then O = scale ((Q * exp(G)) S + L new_v) on fp32 16 x 16 x 4 MFMAs, whose
+// ---- output: L from decayed query and key tiles on the matrix cores (split
+// at the chunk's middle token when its gates allow, else block row by block
+// row, with the diagonal blocks pair by pair when a block's gates span too
+// far); then O = scale ((Q * exp(G)) S + L new_v) on the matrix cores, whose
 // B operands are the chain's start-state and new_v images as loaded. Wave w
 // takes column block w mod (Dv / 16) and TPW token blocks. Persistent over
 // the (chunk, head) items, one workgroup per CU: the next item's q, k, g rows
