@@ -79,29 +79,41 @@ constexpr int XR = KC + 16; // rows of the bf16 high/low tiles of decayed rows
 constexpr float kSplitSpan = 40.f;
 
 // G: inclusive cumulative sums over a chunk's tokens, one wave per key dim
-// (lane = token), for the tile Gt[DK][KP] of the chunk's gates. Sets *wide
-// when some token's G leaves its 16-token block's first value by more than
-// kSplitSpan, and *far when some token's G leaves the chunk's middle value
-// G[KC / 2] by more (the writes race benignly: all store 1). Wave w takes
-// key dims w, w + NT / 64, ...: all its columns are read first, so that
-// their independent scans interleave.
+// (lane = token), for the tile Gt[DK][KP] of the chunk's gates. Sets *far
+// when some token's G leaves the chunk's middle value G[KC / 2] by more than
+// kSplitSpan (the writes race benignly: all store 1). Wave w takes key dims
+// w, w + NT / 64, ...: all its columns are read first, so that their
+// independent scans interleave.
 template <int DK, int NT>
-__device__ __forceinline__ void gate_prefix(float (*Gt)[KP], int w, int l, int *wide, int *far) {
+__device__ __forceinline__ void gate_prefix(float (*Gt)[KP], int w, int l, int *far) {
     constexpr int NW = NT / 64, ND = DK / NW;
     float x[ND];
 #pragma unroll
     for (int i = 0; i < ND; ++i) x[i] = Gt[w + NW * i][l];
-    bool big = false, span = false;
+    bool span = false;
 #pragma unroll
     for (int i = 0; i < ND; ++i) {
         x[i] = wave_prefix_sum(x[i]);
-        big |= fabsf(x[i] - __shfl(x[i], l & 48, 64)) > kSplitSpan;
         span |= fabsf(x[i] - lane_value(x[i], KC / 2)) > kSplitSpan;
     }
 #pragma unroll
     for (int i = 0; i < ND; ++i) Gt[w + NW * i][l] = x[i];
-    if (big) *wide = 1;
     if (span) *far = 1;
+}
+
+// Sets *wide when some token's G leaves its 16-token block's first value by
+// more than kSplitSpan (read from the tile Gt after gate_prefix; thread i of
+// NT takes elements i, i + NT, ...). Only chunks that are not split at one
+// reference token need it.
+template <int DK, int NT>
+__device__ __forceinline__ void block_spans(const float (*Gt)[KP], int tid, int *wide) {
+    bool big = false;
+#pragma unroll 4
+    for (int i = tid; i < DK * KC; i += NT) {
+        const int d = i / KC, t = i - d * KC;
+        big |= fabsf(Gt[d][t] - Gt[d][t & ~15]) > kSplitSpan;
+    }
+    if (big) *wide = 1;
 }
 
 // Per chunk and head workspace tile, in floats: W, then K * exp(G_last - G),
@@ -373,7 +385,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     // of diag(beta) V, where it fits (not at Dk = 128 with Dv = 64).
     constexpr bool kOneRef = DecayTile<DK, HL, KC>::BYTES <= (int)sizeof(Vs);
     __shared__ float bs[KC];
-    __shared__ int wide, far;  // gate spans past kSplitSpan (gate_prefix)
+    __shared__ int wide, far;  // gate spans past kSplitSpan (block_spans, gate_prefix)
     static_assert(sizeof(Kt) + sizeof(Gt) + sizeof(Vs) + sizeof(Ms) + sizeof(Xb) + sizeof(bs) + 2 * sizeof(int) <=
                       kLdsPerCU,
                   "the workgroup must fit one CU's LDS");
@@ -429,7 +441,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     rg.template store<true, KP>(&Gt[0][0], tid);
     fetch_kg(item + gridDim.x);
     __syncthreads();
-    gate_prefix<DK, NT>(Gt, w, l, &wide, &far);
+    gate_prefix<DK, NT>(Gt, w, l, &far);
     __syncthreads();
     const int tix = opaque(tid);
 
@@ -473,6 +485,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
         // A inside the diagonal 16 x 16 blocks (a > b): split at the block's
         // first token with the blocks below (when the gates allow), else here,
         // one pair per thread with its exponent taken directly.
+        block_spans<DK, NT>(Gt, tix, &wide);
+        __syncthreads();
         const bool split = __builtin_amdgcn_readfirstlane(wide) == 0;
         if (!split) {
             for (int i = tix; i < 4 * 120; i += NT) {
@@ -864,7 +878,7 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
     __shared__ __attribute__((aligned(16))) float Ls[KC][LP];
     __shared__ __attribute__((aligned(16))) char Xb[2 * XR * DK * 2];  // decayed rows
     __shared__ __attribute__((aligned(16))) float eR[DK];  // exp(G_r) or 1 (below)
-    __shared__ int wide, far;  // gate spans past kSplitSpan (gate_prefix)
+    __shared__ int wide, far;  // gate spans past kSplitSpan (block_spans, gate_prefix)
     static_assert(sizeof(Qt) + sizeof(Kt) + sizeof(Gt) + sizeof(Ls) + sizeof(Xb) + sizeof(eR) + 2 * sizeof(int) <=
                       kLdsPerCU,
                   "the workgroup must fit one CU's LDS");
@@ -923,7 +937,7 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
     rg.template store<true, KP>(&Gt[0][0], tid);
     fetch_rows(next);
     __syncthreads();
-    gate_prefix<DK, NT>(Gt, w, l, &wide, &far);
+    gate_prefix<DK, NT>(Gt, w, l, &far);
     __syncthreads();
     const int tix = opaque(tid);
 
@@ -974,6 +988,8 @@ __global__ __launch_bounds__(512) void kda_output_kernel(KdaParams p, int64_t ni
         // the blocks below (when the gates allow), else here, one pair (a > b)
         // per thread with its exponent taken directly, the diagonal itself (no
         // decay) on the rest, zeros above it.
+        block_spans<DK, NT>(Gt, tix, &wide);
+        __syncthreads();
         const bool split = __builtin_amdgcn_readfirstlane(wide) == 0;
         if (!split) {
             if (tid < 4 * 120) {
