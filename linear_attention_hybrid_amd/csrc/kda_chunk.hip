@@ -287,13 +287,26 @@ struct Rows {
     static constexpr int PR = W / PE;            // pieces per row
     static constexpr int PT = KC * PR / NT;
     static_assert(KC * PR % NT == 0, "whole pieces per thread");
+    // A wave's 64 pieces cover PE rows of 64 / PE pieces each: element e of
+    // lane (row i, piece j) then lands in LDS word (PE j + e) * S + i or
+    // i * S + PE j + e, S = 1 mod 64, whose bank PE j + i + e differs across
+    // the wave's lanes; the global reads stay whole runs of 64 / PE pieces.
+    static constexpr int PW = 64 / PE;  // pieces per wave row
+    static constexpr int RG = KC / PE;  // row groups
+    static_assert(PR % PW == 0 && KC % PE == 0, "whole wave blocks");
+    __device__ __forceinline__ static void piece(int idx, int &a, int &pc) {
+        const int wv = idx >> 6, lane = idx & 63;
+        a = PE * (wv % RG) + lane / PW;
+        pc = PW * (wv / RG) + lane % PW;
+    }
     u32x4 r[PT];
     __device__ __forceinline__ void load(const Tin *base, int64_t tok0, int H, int h, int n, int tid) {
         const int bytes = n > 0 ? ((n - 1) * H * W + W) * (int)sizeof(Tin) : 0;
         const buf_t rs = buf_rsrc(base + (tok0 * H + h) * W, bytes);
 #pragma unroll
         for (int m = 0; m < PT; ++m) {
-            const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
+            int a, pc;
+            piece(m * NT + tid, a, pc);
             r[m] = buf_ld16(rs, (uint32_t)((a * H * W + pc * PE) * (int)sizeof(Tin)));
         }
     }
@@ -302,7 +315,8 @@ struct Rows {
     __device__ __forceinline__ void store_scaled(float *tile, int tid, const float *scale) const {
 #pragma unroll
         for (int m = 0; m < PT; ++m) {
-            const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
+            int a, pc;
+            piece(m * NT + tid, a, pc);
             float f[PE];
             load_piece<Tin>(make_uint4(r[m][0], r[m][1], r[m][2], r[m][3]), f);
             const float sa = scale[a];
@@ -314,7 +328,8 @@ struct Rows {
     __device__ __forceinline__ void store(float *tile, int tid) const {
 #pragma unroll
         for (int m = 0; m < PT; ++m) {
-            const int idx = m * NT + tid, a = idx / PR, pc = idx - a * PR;
+            int a, pc;
+            piece(m * NT + tid, a, pc);
             float f[PE];
             load_piece<Tin>(make_uint4(r[m][0], r[m][1], r[m][2], r[m][3]), f);
 #pragma unroll
