@@ -68,7 +68,7 @@ __device__ __forceinline__ void st_f1(buf_t r, uint32_t off, float v) {
 
 constexpr int KC = kChunk;  // tokens per chunk
 constexpr int KP = KC + 1;  // padded token stride of transposed tiles
-constexpr int XR = KC + 16; // rows of the bf16 high/low tiles of decayed rows
+constexpr int XR = KC + 16; // rows of decayed queries and keys per block row (DecayTile)
 
 // The diagonal 16 x 16 blocks of M and L are split at their first token c
 // when every |G[t][d] - G[c][d]| over the block's tokens t stays within this
@@ -155,7 +155,7 @@ __device__ __forceinline__ void load_piece(const uint4 u, float *out) {
     }
 }
 
-// bf16 tiles of 64 rows of DK values for the 16 x 16 x 32 MFMA operands:
+// bf16 tiles of rows of DK values for the 16 x 16 x 32 MFMA operands:
 // 16-byte chunk c of row r sits at chunk c ^ (r mod chunks-per-row), so the
 // 16 rows one operand read touches fall in different banks.
 template <int DK>
@@ -389,8 +389,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     // diag(beta) V, staged once A is formed (before, the space of decayed keys)
     __shared__ __attribute__((aligned(16))) float Vs[KC][DV + 1];
     __shared__ __attribute__((aligned(16))) float Ms[KC][MP];  // A = diag(beta) M below the diagonal; then T
-    // K decayed to a reference token, as bf16 high and low tiles of XR rows;
-    // later the blocks of T (14 blocks of 16 rows x 20 floats).
+    // K decayed to a reference token, XR rows of a DecayTile; later the
+    // blocks of T (14 blocks of 16 rows x 20 floats).
     constexpr int XT = 2 * XR * DK * 2, XTB = 14 * 16 * 20 * 4;
     __shared__ __attribute__((aligned(16))) char Xb[XT > XTB ? XT : XTB];
     constexpr bool HL = sizeof(Tin) == 2;
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     fetch_v(item + gridDim.x);
 
     float *tile = p.tiles + tile_index(p, s, h) * tile_floats(DK, DV);
-    // T = (I + A)^-1 in 16 x 16 blocks, kept in the space of the bf16 tiles
+    // T = (I + A)^-1 in 16 x 16 blocks, kept in the space of the decayed rows
     // (free once A is formed): the ten blocks (I, J), J <= I, rows of 80 bytes
     // (20 floats: the 16 rows of a block start 4 banks apart), then one
     // scratch block per wave.
