@@ -13,7 +13,7 @@ itself is the recurrence): for each row's state S (bf16 values),
     o  = scale * q S'
     S <- bf16(S')                    (stored back, round to nearest even)
 
-Reading where the page is silent (listed in the design doc as well): the query
+Reading where the page is silent: the query
 reads the updated state before it is rounded for storage, as a kernel that
 keeps the state in registers between the update and the store does. The
 arithmetic is fp64 except that one rounding.

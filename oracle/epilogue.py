@@ -15,7 +15,7 @@ concatenated to one row of width H * Dv (4096 on the page), goes through
    layer input (an input here);
 3. out = y * z, elementwise.
 
-Readings where the page is silent (listed in the design doc as well): with bf16
+Readings where the page is silent: with bf16
 tensors every step's result is stored in bf16 (y, the gate and the product),
 the dtype the module outputs have; with fp32 tensors nothing is rounded; eps
 is an argument.

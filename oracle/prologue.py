@@ -15,7 +15,7 @@ the recurrence): each head's 128-vector of q and of k goes through
    fp32 values and stored back to bf16 (the page's ``q.float()`` ...
    ``.bf16()``).
 
-Readings where the page is silent (listed in the design doc as well):
+Readings where the page is silent:
 * RoPE pairs dimension i with i + Dk/2 ("rotate half"), rotating the pair by
   angle pos * theta^(-2i/Dk), i < Dk/2, in the positive sense:
   (a, b) -> (a cos - b sin, b cos + a sin);
