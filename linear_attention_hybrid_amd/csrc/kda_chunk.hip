@@ -388,10 +388,10 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     __shared__ float Gt[DK][KP];       // G^T
     // diag(beta) V, staged once A is formed (before, the space of decayed keys)
     __shared__ __attribute__((aligned(16))) float Vs[KC][DV + 1];
-    __shared__ __attribute__((aligned(16))) float Ms[KC][MP];  // A = diag(beta) M below the diagonal; then T
+    __shared__ __attribute__((aligned(16))) float Ms[KC][MP];  // A = diag(beta) M below the diagonal
     // K decayed to a reference token, XR rows of a DecayTile; later the
-    // blocks of T (14 blocks of 16 rows x 20 floats).
-    constexpr int XT = 2 * XR * DK * 2, XTB = 14 * 16 * 20 * 4;
+    // blocks of T (10 blocks of 16 rows x 20 floats).
+    constexpr int XT = 2 * XR * DK * 2, XTB = 10 * 16 * 20 * 4;
     __shared__ __attribute__((aligned(16))) char Xb[XT > XTB ? XT : XTB];
     constexpr bool HL = sizeof(Tin) == 2;
     const DecayTile<DK, HL, XR> X{Xb};
@@ -561,12 +561,12 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     float *tile = p.tiles + tile_index(p, s, h) * tile_floats(DK, DV);
     // T = (I + A)^-1 in 16 x 16 blocks, kept in the space of the decayed rows
     // (free once A is formed): the ten blocks (I, J), J <= I, rows of 80 bytes
-    // (20 floats: the 16 rows of a block start 4 banks apart), then one
-    // scratch block per wave.
+    // (20 floats: the 16 rows of a block start 4 banks apart). W and U read
+    // them there.
     constexpr int TBR = 20;                         // floats per block row
     constexpr int TBF = 16 * TBR;                   // floats per block
-    float *tb = reinterpret_cast<float *>(Xb);      // 10 blocks + 4 scratch = 17.5 KiB
-    static_assert(14 * TBF * 4 <= (int)sizeof(Xb), "T blocks exceed the tile space");
+    float *tb = reinterpret_cast<float *>(Xb);      // 10 blocks = 12.5 KiB
+    static_assert(10 * TBF * 4 <= (int)sizeof(Xb), "T blocks exceed the tile space");
     auto tbo = [](int I, int J) { return (I * (I + 1) / 2 + J) * TBF; };
     // The item's tile as a buffer (bytes), and an empty one for the stores
     // that only balance the paths.
@@ -627,11 +627,12 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
     __syncthreads();
     // Block rows below: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ, wave J taking
     // column block J. Each 16 x 16 x 16 product is four fp32 16 x 16 x 4
-    // MFMAs: lane l supplies L[l % 16][4k + l / 16] and R[4k + l / 16][l % 16]
-    // and receives D[4 (l / 16) + v][l % 16] in element v.
+    // MFMAs: lane l supplies L[l % 16][k] and R[k][l % 16] and receives
+    // D[4 (l / 16) + v][l % 16] in element v, with k = 4 k4 + l / 16 in MFMA
+    // k4 of the first product, and k = 4 (l / 16) + k4 in the second, whose
+    // R is then X = sum_K A_IK T_KJ as the first left it in the lane.
     {
         const int lr = l & 15, lk = l >> 4;
-        float *scr = tb + (10 + (w & 3)) * TBF;
 #pragma unroll
         for (int I = 1; I < 4; ++I) {
             if (w < I) {
@@ -644,16 +645,11 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
                         const float b = tb[tbo(K, J) + (4 * k4 + lk) * TBR + lr];
                         x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
                     }
-                // X to this wave's scratch block (a wave's LDS accesses take
-                // effect in order), then T_II X.
-#pragma unroll
-                for (int v = 0; v < 4; ++v) scr[(4 * lk + v) * TBR + lr] = x[v];
                 f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int k4 = 0; k4 < 4; ++k4) {
-                    const float a = tb[tbo(I, I) + lr * TBR + 4 * k4 + lk];
-                    const float b = scr[(4 * k4 + lk) * TBR + lr];
-                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t, 0, 0, 0);
+                    const float a = tb[tbo(I, I) + lr * TBR + 4 * lk + k4];
+                    t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, x[k4], t, 0, 0, 0);
                 }
 #pragma unroll
                 for (int v = 0; v < 4; ++v) tb[tbo(I, J) + (4 * lk + v) * TBR + lr] = -t[v];
@@ -661,12 +657,6 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
             __syncthreads();
         }
     }
-    // T back into Ms row-major, zero above the diagonal.
-    for (int i = tid; i < KC * KC; i += NT) {
-        const int a = i / KC, b = i - a * KC;
-        Ms[a][b] = b <= a ? tb[tbo(a >> 4, b >> 4) + (a & 15) * TBR + (b & 15)] : 0.f;
-    }
-    __syncthreads();
     // W = T X and U = T (diag(beta) V) on fp32 16 x 16 x 4 MFMAs, straight
     // into the chain's operand images. W comes out transposed, W^T = X^T T^T,
     // so that each accumulator quad is one W image float4 (4 key dims of a
@@ -703,7 +693,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaParams p, int64_t nite
                     f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb <= tt; ++kb) {
-                        const float4 t4 = *reinterpret_cast<const float4 *>(&Ms[16 * tt + lr][16 * kb + 4 * lk]);
+                        const float4 t4 = *reinterpret_cast<const float4 *>(tb + tbo(tt, kb) + lr * TBR + 4 * lk);
                         const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
                         for (int k4 = 0; k4 < 4; ++k4)
