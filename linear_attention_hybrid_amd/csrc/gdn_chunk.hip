@@ -57,8 +57,7 @@ constexpr int A_ROW = 68 * 4;      // padded row (16-byte aligned, rows start 4 
 constexpr int P_G = P_A + 64 * A_ROW;
 constexpr int P_B = P_G + 256;
 constexpr int P_E = P_B + 256;     // exp(G) per token
-constexpr int P_X = P_E + 256;     // per-wave 16 x 16 fp32 scratch block (4 x 1280 B)
-constexpr int P_BYTES = P_X + 4 * 1280;
+constexpr int P_BYTES = P_E + 256;
 static_assert(2 * P_BYTES <= kLdsPerCU, "two prep workgroups must fit one CU's LDS");
 // T in 16 x 16 fp32 blocks (I, J), I >= J, rows of 80 bytes (20 floats: the
 // 16 rows of a block start 4 banks apart), in the K rows region once K K^T
@@ -257,8 +256,10 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
         // Then block row by block row: T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ,
         // wave J taking column block J (waves J >= I wait at this level). Each
         // 16 x 16 x 16 product is four fp32 16 x 16 x 4 MFMAs: lane l supplies
-        // L[l % 16][4k + l / 16] and R[4k + l / 16][l % 16] and receives
-        // D[4 (l / 16) + v][l % 16] in element v.
+        // L[l % 16][k] and R[k][l % 16] and receives D[4 (l / 16) + v][l % 16]
+        // in element v, with k = 4 k4 + l / 16 in MFMA k4 of the first product,
+        // and k = 4 (l / 16) + k4 in the second, whose R is then X =
+        // sum_K A_IK T_KJ as the first left it in the lane.
         {
             const int lr = l & 15;
             const int lk = l >> 4;
@@ -274,16 +275,11 @@ __global__ __launch_bounds__(NT) void gdn_prep_kernel(GdnParams p, int nitems) {
                             const float b = lds_ld<float>(lds, tb_off(K, J) + (4 * k4 + lk) * TB_ROW + 4 * lr);
                             x = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, x, 0, 0, 0);
                         }
-                    // X to this wave's scratch block, row-major (a wave's LDS
-                    // accesses take effect in order), then T_II X.
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) lds_st(lds, P_X + 1280 * w + (4 * lk + v) * TB_ROW + 4 * lr, x[v]);
                     f32x4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int k4 = 0; k4 < 4; ++k4) {
-                        const float a = lds_ld<float>(lds, tb_off(I, I) + lr * TB_ROW + 4 * (4 * k4 + lk));
-                        const float b = lds_ld<float>(lds, P_X + 1280 * w + (4 * k4 + lk) * TB_ROW + 4 * lr);
-                        t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, t, 0, 0, 0);
+                        const float a = lds_ld<float>(lds, tb_off(I, I) + lr * TB_ROW + 4 * (4 * lk + k4));
+                        t = __builtin_amdgcn_mfma_f32_16x16x4f32(a, x[k4], t, 0, 0, 0);
                     }
 #pragma unroll
                     for (int v = 0; v < 4; ++v) lds_st(lds, tb_off(I, J) + (4 * lk + v) * TB_ROW + 4 * lr, -t[v]);
